@@ -1,0 +1,599 @@
+/*
+ * oracle.c -- plain, slow CPU reference for the SageSLA attention path.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h). Built with gcc -O2
+ * -ffp-contract=off and no fast-math, so every fp32 expression below is
+ * evaluated exactly as written (IEEE round-to-nearest-even, no reassociation,
+ * no fused multiply-add unless fmaf is called).
+ *
+ * Source of the method: the TurboDiffusion pages, page 5 "Four Technical
+ * Pillars" (Pillar One: SageAttention quantizes attention to INT8 and smooths
+ * outliers; Pillar Two: SLA keeps the important block interactions, about 10%
+ * of them, and covers the rest with a light global linear attention; the two
+ * stack as "SageSLA") and page 5 "Hands-On Tutorial" (--attention_type
+ * sagesla, --sla_topk = fraction of connections kept). Where the pages are
+ * silent the concrete reading is stated at each function.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdatomic.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* block counts                                                              */
+
+int64_t orc_nqb(int64_t N) { return (N + ORC_QBLK - 1) / ORC_QBLK; }
+int64_t orc_nkb(int64_t N) { return (N + ORC_KBLK - 1) / ORC_KBLK; }
+
+/* --sla_topk is the fraction of key blocks kept (page 5, "Hands-On Tutorial":
+ * 0.1 sets 90% sparsity). Reading: round half up, at least one block. */
+int64_t orc_keep(int64_t N, double topk) {
+    int64_t nkb = orc_nkb(N);
+    int64_t kb = (int64_t)floor(topk * (double)nkb + 0.5);
+    if (kb < 1) kb = 1;
+    if (kb > nkb) kb = nkb;
+    return kb;
+}
+
+/* ------------------------------------------------------------------------ */
+/* bf16                                                                      */
+
+float orc_bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round a double to the nearest bf16 value (8 significant bits, exponent range
+ * of fp32, subnormal spacing 2^-133), ties to even. Written from the format's
+ * definition: scale so the kept bits are the integer part, rint, scale back. */
+double orc_round_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    frexp(x, &e);            /* |x| = f * 2^e, f in [0.5, 1) */
+    int q = e - 8;           /* weight of the last kept bit */
+    if (q < -133) q = -133;  /* bf16 subnormals */
+    double r = nearbyint(ldexp(x, -q)); /* default mode: ties to even */
+    return ldexp(r, q);
+}
+
+uint16_t orc_f32_to_bf16(float x) {
+    double r = orc_round_bf16((double)x);
+    float f = (float)r; /* exact: r is a bf16 value (or inf) */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------------ */
+/* a tiny parallel for (dynamic schedule)                                    */
+
+typedef void (*orc_task)(void* ctx, int64_t idx);
+typedef struct {
+    orc_task fn;
+    void* ctx;
+    int64_t n;
+    atomic_llong next;
+} orc_pool_t;
+
+static void* orc_worker(void* arg) {
+    orc_pool_t* p = (orc_pool_t*)arg;
+    for (;;) {
+        int64_t i = atomic_fetch_add(&p->next, 1);
+        if (i >= p->n) break;
+        p->fn(p->ctx, i);
+    }
+    return NULL;
+}
+
+static void orc_parallel_for(int64_t n, int nthreads, orc_task fn, void* ctx) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (n < nthreads) nthreads = (int)(n > 0 ? n : 1);
+    orc_pool_t p;
+    p.fn = fn;
+    p.ctx = ctx;
+    p.n = n;
+    atomic_init(&p.next, 0);
+    if (nthreads == 1) {
+        orc_worker(&p);
+        return;
+    }
+    pthread_t th[256];
+    int started = 0;
+    for (int t = 0; t < nthreads - 1; ++t)
+        if (pthread_create(&th[t], NULL, orc_worker, &p) == 0) ++started;
+    orc_worker(&p);
+    for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+}
+
+/* ------------------------------------------------------------------------ */
+/* K smoothing (page 5, Pillar One: "smoothing" of outliers). Reading: the   */
+/* mean of K over all N tokens of the head, per channel, subtracted from K.  */
+/* Every score of a query row then shifts by the same q.mu, so softmax is    */
+/* unchanged. The fp32 summation order is pinned: per 64-token block in      */
+/* token order, then over blocks in block order.                             */
+
+void orc_k_mean(const uint16_t* k, int64_t BH, int64_t N, int64_t D, float* mu) {
+    int64_t nkb = orc_nkb(N);
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const uint16_t* kh = k + bh * N * D;
+        for (int64_t d = 0; d < D; ++d) {
+            float tot = 0.0f;
+            for (int64_t j = 0; j < nkb; ++j) {
+                float part = 0.0f;
+                int64_t t1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
+                for (int64_t t = j * ORC_KBLK; t < t1; ++t) part += orc_bf16_to_f32(kh[t * D + d]);
+                tot += part;
+            }
+            mu[bh * D + d] = tot / (float)N;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-block INT8 quantization (page 5, Pillar One: attention in 8-bit      */
+/* integers). Reading: one fp32 scale per (head, block) over all channels,  */
+/* scale = amax/127, q = rint(x/scale) with ties to even, symmetric range.  */
+
+typedef struct {
+    const uint16_t* x;
+    const float* mu;
+    int64_t N, D, blk, nb;
+    int8_t* xq;
+    float* scale;
+} quant_ctx;
+
+static void quant_task(void* vctx, int64_t idx) {
+    quant_ctx* c = (quant_ctx*)vctx;
+    int64_t bh = idx / c->nb, b = idx % c->nb;
+    int64_t D = c->D, N = c->N;
+    int64_t t0 = b * c->blk, t1 = t0 + c->blk < N ? t0 + c->blk : N;
+    const uint16_t* xh = c->x + bh * N * D;
+    const float* mu = c->mu ? c->mu + bh * D : NULL;
+    float amax = 0.0f;
+    for (int64_t t = t0; t < t1; ++t)
+        for (int64_t d = 0; d < D; ++d) {
+            float v = orc_bf16_to_f32(xh[t * D + d]);
+            if (mu) v = v - mu[d];
+            float a = fabsf(v);
+            if (a > amax) amax = a;
+        }
+    float s = amax / 127.0f;
+    c->scale[bh * c->nb + b] = s;
+    for (int64_t t = t0; t < t1; ++t)
+        for (int64_t d = 0; d < D; ++d) {
+            float v = orc_bf16_to_f32(xh[t * D + d]);
+            if (mu) v = v - mu[d];
+            int8_t q = 0;
+            if (s > 0.0f) {
+                float r = rintf(v / s);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                q = (int8_t)r;
+            }
+            c->xq[(bh * N + t) * D + d] = q;
+        }
+}
+
+void orc_quant(const uint16_t* x, const float* mu, int64_t BH, int64_t N, int64_t D,
+               int64_t blk, int8_t* xq, float* scale, int nthreads) {
+    quant_ctx c = {x, mu, N, D, blk, (N + blk - 1) / blk, xq, scale};
+    orc_parallel_for(BH * c.nb, nthreads, quant_task, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* int32 scores of one (query block, key block) tile                        */
+
+void orc_qk_tile(const int8_t* q_i8, const int8_t* k_i8, int64_t N, int64_t D,
+                 int64_t bh, int64_t i, int64_t j, int32_t* tile) {
+    for (int64_t r = 0; r < ORC_QBLK; ++r)
+        for (int64_t c = 0; c < ORC_KBLK; ++c) {
+            int64_t t = i * ORC_QBLK + r, u = j * ORC_KBLK + c;
+            int32_t acc = 0;
+            if (t < N && u < N) {
+                const int8_t* qr = q_i8 + (bh * N + t) * D;
+                const int8_t* kr = k_i8 + (bh * N + u) * D;
+                for (int64_t d = 0; d < D; ++d) acc += (int32_t)qr[d] * (int32_t)kr[d];
+            }
+            tile[r * ORC_KBLK + c] = acc;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* SLA block mask (page 5, Pillar Two: only the most important interactions, */
+/* 10% of them at --sla_topk 0.1). Reading: blocks are scored by the dot     */
+/* product of the mean-pooled raw Q block and raw K block; each query block */
+/* keeps its top `keep` key blocks, ties going to the lower key block.      */
+
+void orc_pool(const uint16_t* x, int64_t N, int64_t D, int64_t bh, int64_t blk, float* out) {
+    int64_t nb = (N + blk - 1) / blk;
+    const uint16_t* xh = x + bh * N * D;
+    for (int64_t b = 0; b < nb; ++b) {
+        int64_t t0 = b * blk, t1 = t0 + blk < N ? t0 + blk : N;
+        for (int64_t d = 0; d < D; ++d) {
+            float s = 0.0f;
+            for (int64_t t = t0; t < t1; ++t) s += orc_bf16_to_f32(xh[t * D + d]);
+            out[b * D + d] = s / (float)(t1 - t0);
+        }
+    }
+}
+
+void orc_block_scores(const float* qbar, const float* kbar, int64_t Nkb, int64_t D,
+                      const int64_t* qblocks, int64_t R, float* score) {
+    for (int64_t r = 0; r < R; ++r) {
+        const float* qb = qbar + qblocks[r] * D;
+        for (int64_t j = 0; j < Nkb; ++j) {
+            const float* kb = kbar + j * D;
+            float acc = 0.0f;
+            for (int64_t d = 0; d < D; ++d) acc = fmaf(qb[d], kb[d], acc);
+            score[r * Nkb + j] = acc;
+        }
+    }
+}
+
+typedef struct {
+    float s;
+    int32_t j;
+} scored_t;
+
+/* (score descending, j ascending); -0.0 and +0.0 compare equal. */
+static int cmp_scored(const void* a, const void* b) {
+    const scored_t* x = (const scored_t*)a;
+    const scored_t* y = (const scored_t*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+static int cmp_i32(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+void orc_topk(const float* score, int64_t R, int64_t Nkb, int64_t keep, int32_t* kidx,
+              uint8_t* mask) {
+    scored_t* tmp = (scored_t*)malloc(sizeof(scored_t) * (size_t)Nkb);
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t j = 0; j < Nkb; ++j) {
+            tmp[j].s = score[r * Nkb + j];
+            tmp[j].j = (int32_t)j;
+        }
+        qsort(tmp, (size_t)Nkb, sizeof(scored_t), cmp_scored);
+        int32_t* out = kidx + r * keep;
+        for (int64_t c = 0; c < keep; ++c) out[c] = tmp[c].j;
+        qsort(out, (size_t)keep, sizeof(int32_t), cmp_i32);
+        if (mask) {
+            memset(mask + r * Nkb, 0, (size_t)Nkb);
+            for (int64_t c = 0; c < keep; ++c) mask[r * Nkb + out[c]] = 1;
+        }
+    }
+    free(tmp);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sparse softmax branch over the kept blocks (page 5, Pillar One + Two).    */
+/*                                                                           */
+/* Declared numerics (o_decl). With sm the softmax scale:                    */
+/*   K32 = fl32(sm * log2 e); c_j = fl32(fl32(sq * sk_j) * K32)              */
+/*   x_u = fl32(S_u * c_j)                 (base-2 logit of key u)           */
+/*   m   = ceil(max_u x_u)                 (integer normalizer)              */
+/*   p_u = bf16(2^(S_u * c_j - m))         (exact exponent, one rounding)    */
+/*   o   = sum_u p_u v_u / sum_u p_u       (exact)                           */
+/* Because m is an integer, p_u does not depend on the order in which a GPU  */
+/* visits the blocks (rescaling by powers of two is exact), and the row sum  */
+/* uses the same rounded p_u the PV product sees.                            */
+
+typedef struct {
+    const int8_t* q_i8;
+    const float* q_scale;
+    const int8_t* k_i8;
+    const float* k_scale;
+    const uint16_t* v;
+    int64_t N, D, bh, nqb, nkb, keep;
+    const int32_t* kidx;
+    float sm;
+    float K32;
+    const int64_t* tokens;
+    double *o_decl, *o_exact, *amb;
+} sparse_ctx;
+
+static void sparse_task(void* vctx, int64_t r) {
+    sparse_ctx* c = (sparse_ctx*)vctx;
+    int64_t N = c->N, D = c->D, t = c->tokens[r];
+    int64_t i = t / ORC_QBLK;
+    int64_t nsel = c->kidx ? c->keep : c->nkb;
+    int64_t cap = nsel * ORC_KBLK;
+    int32_t* S = (int32_t*)malloc(sizeof(int32_t) * (size_t)cap);
+    int64_t* U = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+    float* C = (float*)malloc(sizeof(float) * (size_t)cap);
+    double* se = (double*)malloc(sizeof(double) * (size_t)cap);
+    double* acc = (double*)calloc((size_t)D, sizeof(double));
+    double* acc2 = (double*)calloc((size_t)D, sizeof(double));
+    const int8_t* qr = c->q_i8 + (c->bh * N + t) * D;
+    float sq = c->q_scale[c->bh * c->nqb + i];
+    int64_t n = 0;
+    for (int64_t jj = 0; jj < nsel; ++jj) {
+        int64_t j = c->kidx ? c->kidx[i * c->keep + jj] : jj;
+        float sk = c->k_scale[c->bh * c->nkb + j];
+        float cj = (sq * sk) * c->K32;
+        int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
+        for (int64_t u = j * ORC_KBLK; u < u1; ++u) {
+            const int8_t* kr = c->k_i8 + (c->bh * N + u) * D;
+            int32_t s = 0;
+            for (int64_t d = 0; d < D; ++d) s += (int32_t)qr[d] * (int32_t)kr[d];
+            S[n] = s;
+            U[n] = u;
+            C[n] = cj;
+            se[n] = (double)s * (double)sq * (double)sk * (double)c->sm;
+            ++n;
+        }
+    }
+    const uint16_t* vh = c->v + c->bh * N * D;
+    /* declared numerics */
+    float xmax = -INFINITY;
+    for (int64_t a = 0; a < n; ++a) {
+        float x = (float)S[a] * C[a];
+        if (x > xmax) xmax = x;
+    }
+    float m = ceilf(xmax);
+    double l = 0.0;
+    double* pd = (double*)malloc(sizeof(double) * (size_t)n);
+    double* pe = (double*)malloc(sizeof(double) * (size_t)n);
+    for (int64_t a = 0; a < n; ++a) {
+        double y = (double)S[a] * (double)C[a] - (double)m;
+        pe[a] = exp2(y);
+        pd[a] = orc_round_bf16(pe[a]);
+        l += pd[a];
+        const uint16_t* vr = vh + U[a] * D;
+        for (int64_t e = 0; e < D; ++e) acc[e] += pd[a] * (double)orc_bf16_to_f32(vr[e]);
+    }
+    if (c->o_decl)
+        for (int64_t e = 0; e < D; ++e) c->o_decl[r * D + e] = acc[e] / l;
+    if (c->amb) {
+        /* A GPU evaluates the exponent in fp32 (fma against a running integer
+         * normalizer) and 2^y with a hardware approximation. Both roundings of
+         * p are legitimate when 2^y lies within that evaluation error of a
+         * bf16 rounding midpoint. Error window, relative to p: 2^-20 for the
+         * exponential plus 2^-23 * (|x| + max|x| + 2) for the fp32 exponent. */
+        double xabs_max = 0.0;
+        for (int64_t a = 0; a < n; ++a) {
+            double xa = fabs((double)((float)S[a] * C[a]));
+            if (xa > xabs_max) xabs_max = xa;
+        }
+        double bound = 0.0;
+        for (int64_t a = 0; a < n; ++a) {
+            double p = pe[a];
+            if (p < 0x1p-126) continue;
+            int ex;
+            frexp(p, &ex);
+            double ulp = ldexp(1.0, ex - 8);
+            double k = p / ulp;
+            double dist = fabs(k - floor(k) - 0.5) * ulp;
+            double xa = fabs((double)((float)S[a] * C[a]));
+            double win = p * (0x1p-20 + 0x1p-23 * (xa + xabs_max + fabs((double)m) + 2.0));
+            if (dist <= win) {
+                const uint16_t* vr = vh + U[a] * D;
+                double dv = 0.0;
+                for (int64_t e = 0; e < D; ++e) {
+                    double dd = fabs((double)orc_bf16_to_f32(vr[e]) - acc[e] / l);
+                    if (dd > dv) dv = dd;
+                }
+                bound += ulp * dv / l;
+            }
+        }
+        c->amb[r] = bound;
+    }
+    /* exact arithmetic */
+    if (c->o_exact) {
+        double smax = -INFINITY;
+        for (int64_t a = 0; a < n; ++a)
+            if (se[a] > smax) smax = se[a];
+        double l2 = 0.0;
+        for (int64_t a = 0; a < n; ++a) {
+            double p = exp(se[a] - smax);
+            l2 += p;
+            const uint16_t* vr = vh + U[a] * D;
+            for (int64_t e = 0; e < D; ++e) acc2[e] += p * (double)orc_bf16_to_f32(vr[e]);
+        }
+        for (int64_t e = 0; e < D; ++e) c->o_exact[r * D + e] = acc2[e] / l2;
+    }
+    free(pd);
+    free(pe);
+    free(S);
+    free(U);
+    free(C);
+    free(se);
+    free(acc);
+    free(acc2);
+}
+
+static float default_sm(float sm, int64_t D) {
+    return sm > 0.0f ? sm : (float)(1.0 / sqrt((double)D));
+}
+
+void orc_sparse_rows(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                     const float* k_scale, const uint16_t* v, int64_t N, int64_t D,
+                     int64_t bh, const int32_t* kidx_head, int64_t keep, float sm_scale,
+                     const int64_t* tokens, int64_t R, double* o_decl, double* o_exact,
+                     double* amb, int nthreads) {
+    sparse_ctx c;
+    c.q_i8 = q_i8;
+    c.q_scale = q_scale;
+    c.k_i8 = k_i8;
+    c.k_scale = k_scale;
+    c.v = v;
+    c.N = N;
+    c.D = D;
+    c.bh = bh;
+    c.nqb = orc_nqb(N);
+    c.nkb = orc_nkb(N);
+    c.keep = keep;
+    c.kidx = kidx_head;
+    c.sm = default_sm(sm_scale, D);
+    c.K32 = (float)((double)c.sm * 1.4426950408889634074);
+    c.tokens = tokens;
+    c.o_decl = o_decl;
+    c.o_exact = o_exact;
+    c.amb = amb;
+    orc_parallel_for(R, nthreads, sparse_task, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Linear branch (page 5, Pillar Two: "a lightweight global linear attention */
+/* component" for the interactions the sparse part skips). Reading: feature  */
+/* map phi = elu + 1, no softmax scale, no learned projection; for a query   */
+/* block the states are summed over exactly the key blocks it did not keep. */
+
+static double phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+typedef struct {
+    const uint16_t *k, *v;
+    int64_t N, D, bh;
+    double *h, *z;
+} lstate_ctx;
+
+static void lstate_task(void* vctx, int64_t j) {
+    lstate_ctx* c = (lstate_ctx*)vctx;
+    int64_t N = c->N, D = c->D;
+    double* hj = c->h + j * D * D;
+    double* zj = c->z + j * D;
+    memset(hj, 0, sizeof(double) * (size_t)(D * D));
+    memset(zj, 0, sizeof(double) * (size_t)D);
+    int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
+    for (int64_t u = j * ORC_KBLK; u < u1; ++u) {
+        const uint16_t* kr = c->k + (c->bh * N + u) * D;
+        const uint16_t* vr = c->v + (c->bh * N + u) * D;
+        for (int64_t d = 0; d < D; ++d) {
+            double f = phi((double)orc_bf16_to_f32(kr[d]));
+            zj[d] += f;
+            for (int64_t e = 0; e < D; ++e) hj[d * D + e] += f * (double)orc_bf16_to_f32(vr[e]);
+        }
+    }
+}
+
+void orc_linear_states(const uint16_t* k, const uint16_t* v, int64_t N, int64_t D,
+                       int64_t bh, double* h, double* z, int nthreads) {
+    lstate_ctx c = {k, v, N, D, bh, h, z};
+    orc_parallel_for(orc_nkb(N), nthreads, lstate_task, &c);
+}
+
+typedef struct {
+    const uint16_t* q;
+    int64_t N, D, bh, nkb, keep;
+    const double *h, *z;
+    const int32_t* kidx;
+    const int64_t* tokens;
+    int64_t R;
+    const int64_t* blocks; /* distinct query blocks */
+    double* o;
+} lrows_ctx;
+
+static void lrows_task(void* vctx, int64_t bi) {
+    lrows_ctx* c = (lrows_ctx*)vctx;
+    int64_t D = c->D, N = c->N, i = c->blocks[bi];
+    if (!c->kidx || c->keep >= c->nkb) {
+        for (int64_t r = 0; r < c->R; ++r)
+            if (c->tokens[r] / ORC_QBLK == i)
+                for (int64_t e = 0; e < D; ++e) c->o[r * D + e] = 0.0;
+        return;
+    }
+    uint8_t* kept = (uint8_t*)calloc((size_t)c->nkb, 1);
+    for (int64_t a = 0; a < c->keep; ++a) kept[c->kidx[i * c->keep + a]] = 1;
+    double* H = (double*)calloc((size_t)(D * D), sizeof(double));
+    double* zc = (double*)calloc((size_t)D, sizeof(double));
+    for (int64_t j = 0; j < c->nkb; ++j) {
+        if (kept[j]) continue;
+        const double* hj = c->h + j * D * D;
+        for (int64_t x = 0; x < D * D; ++x) H[x] += hj[x];
+        for (int64_t d = 0; d < D; ++d) zc[d] += c->z[j * D + d];
+    }
+    double* fq = (double*)malloc(sizeof(double) * (size_t)D);
+    for (int64_t r = 0; r < c->R; ++r) {
+        int64_t t = c->tokens[r];
+        if (t / ORC_QBLK != i) continue;
+        const uint16_t* qr = c->q + (c->bh * N + t) * D;
+        for (int64_t d = 0; d < D; ++d) fq[d] = phi((double)orc_bf16_to_f32(qr[d]));
+        double den = 0.0;
+        for (int64_t d = 0; d < D; ++d) den += fq[d] * zc[d];
+        for (int64_t e = 0; e < D; ++e) {
+            double num = 0.0;
+            for (int64_t d = 0; d < D; ++d) num += fq[d] * H[d * D + e];
+            c->o[r * D + e] = num / den;
+        }
+    }
+    free(fq);
+    free(H);
+    free(zc);
+    free(kept);
+}
+
+void orc_linear_rows(const uint16_t* q, int64_t N, int64_t D, int64_t bh,
+                     const double* h, const double* z, const int32_t* kidx_head,
+                     int64_t keep, const int64_t* tokens, int64_t R, double* o_lin,
+                     int nthreads) {
+    int64_t nqb = orc_nqb(N);
+    uint8_t* seen = (uint8_t*)calloc((size_t)nqb, 1);
+    int64_t* blocks = (int64_t*)malloc(sizeof(int64_t) * (size_t)(R > 0 ? R : 1));
+    int64_t nb = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t i = tokens[r] / ORC_QBLK;
+        if (!seen[i]) {
+            seen[i] = 1;
+            blocks[nb++] = i;
+        }
+    }
+    lrows_ctx c = {q, N, D, bh, orc_nkb(N), keep, h, z, kidx_head, tokens, R, blocks, o_lin};
+    orc_parallel_for(nb, nthreads, lrows_task, &c);
+    free(seen);
+    free(blocks);
+}
+
+/* ------------------------------------------------------------------------ */
+/* fp64 dense softmax attention on the unquantized inputs                   */
+
+typedef struct {
+    const uint16_t *q, *k, *v;
+    int64_t N, D, bh;
+    double sm;
+    const int64_t* tokens;
+    double* out;
+} dense_ctx;
+
+static void dense_task(void* vctx, int64_t r) {
+    dense_ctx* c = (dense_ctx*)vctx;
+    int64_t N = c->N, D = c->D, t = c->tokens[r];
+    const uint16_t* qr = c->q + (c->bh * N + t) * D;
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    double* acc = (double*)calloc((size_t)D, sizeof(double));
+    double smax = -INFINITY;
+    for (int64_t u = 0; u < N; ++u) {
+        const uint16_t* kr = c->k + (c->bh * N + u) * D;
+        double a = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            a += (double)orc_bf16_to_f32(qr[d]) * (double)orc_bf16_to_f32(kr[d]);
+        s[u] = a * c->sm;
+        if (s[u] > smax) smax = s[u];
+    }
+    double l = 0.0;
+    for (int64_t u = 0; u < N; ++u) {
+        double p = exp(s[u] - smax);
+        l += p;
+        const uint16_t* vr = c->v + (c->bh * N + u) * D;
+        for (int64_t e = 0; e < D; ++e) acc[e] += p * (double)orc_bf16_to_f32(vr[e]);
+    }
+    for (int64_t e = 0; e < D; ++e) c->out[r * D + e] = acc[e] / l;
+    free(s);
+    free(acc);
+}
+
+void orc_dense_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t N,
+                    int64_t D, int64_t bh, float sm_scale, const int64_t* tokens, int64_t R,
+                    double* out, int nthreads) {
+    dense_ctx c = {q, k, v, N, D, bh, (double)default_sm(sm_scale, D), tokens, out};
+    orc_parallel_for(R, nthreads, dense_task, &c);
+}

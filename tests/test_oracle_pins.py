@@ -1,0 +1,519 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+closed forms, exact rational arithmetic, brute force on tiny inputs, library
+routines for special cases, and hand-derived values under tests/golden/.
+
+The method is the one on the TurboDiffusion pages (page 5, "Four Technical
+Pillars", Pillars One and Two; "Hands-On Tutorial" flags --attention_type
+sagesla and --sla_topk).
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from bit_sparse_attention_amd.workloads import bf16_bits, make_qkv
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bits(t):
+    return bf16_bits(t.to(torch.bfloat16))
+
+
+def _f(bits):
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+
+
+def round_rational(fr: Fraction, mant_bits: int, emin: int) -> Fraction:
+    """Exact round-to-nearest-even of a rational to a binary format with
+    `mant_bits` significant bits and smallest exponent of the last bit `emin`."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length() - mant_bits
+    while a / Fraction(2) ** e >= 2 ** mant_bits:
+        e += 1
+    while a / Fraction(2) ** e < 2 ** (mant_bits - 1):
+        e -= 1
+    e = max(e, emin)
+    m = a / Fraction(2) ** e
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * Fraction(n) * Fraction(2) ** e
+
+
+def f32_of(fr: Fraction) -> float:
+    return float(round_rational(fr, 24, -149))
+
+
+# --------------------------------------------------------------------------
+# block counts and keep (page 5, "Hands-On Tutorial": --sla_topk 0.1 keeps 10%)
+
+def test_keep_blocks(orc):
+    assert orc.nqb(32760) == 256 and orc.nkb(32760) == 512
+    assert orc.nqb(75600) == 591 and orc.nkb(75600) == 1182
+    assert orc.nqb(269280) == 2104 and orc.nkb(269280) == 4208
+    assert orc.keep_blocks(32760, 0.1) == 51
+    assert orc.keep_blocks(75600, 0.1) == 118
+    assert orc.keep_blocks(269280, 0.05) == 210
+    assert orc.keep_blocks(1024, 0.0) == 1
+    assert orc.keep_blocks(1024, 1.0) == 16
+    assert orc.keep_blocks(1024, 0.5) == 8
+    assert orc.keep_blocks(1024, 0.15) == 2  # 2.4 -> 2
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding helpers, against torch's conversion and exact rationals
+
+def test_bf16_rounding_matches_torch(orc):
+    rng = np.random.default_rng(1)
+    vals = list(rng.standard_normal(2000).astype(np.float32) * 10 ** rng.uniform(-40, 38, 2000))
+    # exact ties: lower 16 bits = 0x8000 with even and odd kept lsb
+    for hi in (0x3F80, 0x3F81, 0xBF80, 0xBF81, 0x0001, 0x0002, 0x7F7E, 0x7F7F):
+        for lo in (0x8000, 0x7FFF, 0x8001):
+            vals.append(np.array([(hi << 16) | lo], np.uint32).view(np.float32)[0])
+    vals += [np.float32(1e-45), np.float32(-3e-39), np.float32(0.0), np.float32(-0.0)]
+    x = np.array(vals, np.float32)
+    x = x[np.isfinite(x)]
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([orc.f32_to_bf16_bits(float(v)) for v in x], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_round_bf16_double_exact(orc):
+    rng = np.random.default_rng(2)
+    xs = list(rng.uniform(0, 1, 500)) + list(2.0 ** rng.uniform(-140, -120, 100))
+    xs += [1 + 2 ** -8, 1 + 3 * 2 ** -8, 0.5 + 2 ** -9, 2 ** -126 * (1 + 2 ** -8)]
+    for x in xs:
+        want = float(round_rational(Fraction(x), 8, -133))
+        assert orc.round_bf16(x) == want, x
+
+
+# --------------------------------------------------------------------------
+# K smoothing mean (page 5, Pillar One: "smoothing" of outliers)
+
+def test_k_mean_close_to_fp64(orc):
+    q, k, v = make_qkv(1, 2, 1000, 128, seed=3)
+    kb = _bits(k).reshape(2, 1000, 128)
+    mu = orc.k_mean(kb)
+    ref = _f(kb).astype(np.float64).mean(axis=1)
+    assert np.all(np.abs(mu - ref) <= 1e-6 * (np.abs(ref) + 1))
+
+
+def test_k_mean_exact_on_integers(orc):
+    rng = np.random.default_rng(4)
+    N, D = 300, 128  # ragged: 4 full key blocks + 44 tokens
+    ki = rng.integers(-20, 21, size=(1, N, D)).astype(np.float32)
+    kb = _bits(torch.from_numpy(ki))
+    mu = orc.k_mean(kb)
+    # every partial sum is an exact small integer, so mu = fl32(sum / N)
+    want = (ki.sum(axis=1, dtype=np.float64)).astype(np.float32) / np.float32(N)
+    assert np.array_equal(mu, want)
+
+
+def test_smoothing_reading_is_softmax_invariant():
+    # The reading behind smoothing: subtracting a per-channel mean mu from every
+    # key shifts all scores of a query row by q.mu, which softmax ignores.
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((7, 16))
+    k = rng.standard_normal((33, 16)) + 3 * rng.standard_normal(16)
+    v = rng.standard_normal((33, 16))
+    mu = rng.standard_normal(16) * 5
+
+    def attn(kk):
+        s = q @ kk.T
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        return (p / p.sum(axis=1, keepdims=True)) @ v
+
+    assert np.max(np.abs(attn(k) - attn(k - mu))) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# INT8 quantization (page 5, Pillar One)
+
+def _check_quant_invariants(x, xq, sc, blk):
+    BH, N, D = x.shape
+    for bh in range(BH):
+        for b in range(sc.shape[1]):
+            t0, t1 = b * blk, min(N, (b + 1) * blk)
+            xb = x[bh, t0:t1].astype(np.float64)
+            qb = xq[bh, t0:t1].astype(np.int64)
+            s = float(sc[bh, b])
+            amax = np.abs(xb).max()
+            assert s == np.float32(np.float32(amax) / np.float32(127.0))
+            assert np.all(np.abs(qb) <= 127)
+            if amax == 0:
+                assert s == 0 and np.all(qb == 0)
+                continue
+            assert np.abs(qb).max() == 127
+            # rint acts on fl32(x/s), whose rounding (<= 2^-17 at |x/s| <= 127)
+            # can move a value just past a half-integer: |x - q s| <= s (1/2 + 2^-17)
+            assert np.all(np.abs(xb - qb * s) <= s / 2 * (1 + 2 ** -15))
+
+
+def test_quant_invariants_q_and_k(orc):
+    q, k, v = make_qkv(1, 2, 1000, 128, seed=6)
+    qb, kb = _bits(q).reshape(2, 1000, 128), _bits(k).reshape(2, 1000, 128)
+    qi, qs, ki, ks, mu = orc.quant_qk(qb, kb)
+    assert qs.shape == (2, 8) and ks.shape == (2, 16)
+    _check_quant_invariants(_f(qb), qi, qs, 128)
+    kp = (_f(kb) - mu[:, None, :]).astype(np.float32)  # one fp32 subtraction
+    _check_quant_invariants(kp, ki, ks, 64)
+
+
+def test_quant_golden_ties(orc):
+    g = _golden("quant_ties.json")
+    x = np.zeros((1, 128, 128), np.float32)
+    x[0, 0, : len(g["x"])] = g["x"]
+    xb = _bits(torch.from_numpy(x))
+    assert np.array_equal(_f(xb), x)  # all values are exact in bf16
+    qi, qs = orc.quant(xb, None, 128)
+    assert qs[0, 0] == 1.0
+    assert list(qi[0, 0, : len(g["q"])]) == g["q"]
+    # K path: rows in +/- pairs give a zero channel mean, so K' = K exactly
+    kx = np.zeros((1, 64, 128), np.float32)
+    kx[0, 0, : len(g["x"])] = g["x"]
+    kx[0, 1, : len(g["x"])] = [-a for a in g["x"]]
+    kb = _bits(torch.from_numpy(kx))
+    mu = orc.k_mean(kb)
+    assert np.all(mu == 0)
+    ki, ks = orc.quant(kb, mu, 64)
+    assert ks[0, 0] == 1.0
+    assert list(ki[0, 0, : len(g["q"])]) == g["q"]
+    assert list(ki[0, 1, : len(g["q"])]) == [-a for a in g["q"]]
+
+
+def test_quant_block_boundaries(orc):
+    # one large value moves only the scale of the block that holds it
+    N = 300
+    for blk, pos, want_block in ((128, 127, 0), (128, 128, 1), (128, 299, 2), (64, 63, 0),
+                                 (64, 64, 1), (64, 299, 4)):
+        x = np.full((1, N, 128), 0.25, np.float32)
+        x[0, pos, 5] = 100.0
+        xb = _bits(torch.from_numpy(x))
+        xq, sc = orc.quant(xb, None, blk)
+        big = np.float32(np.float32(100.0) / np.float32(127.0))
+        small = np.float32(np.float32(0.25) / np.float32(127.0))
+        for b in range(sc.shape[1]):
+            assert sc[0, b] == (big if b == want_block else small), (blk, pos, b)
+
+
+def test_quant_zero_block(orc):
+    x = np.zeros((1, 200, 128), np.float32)
+    x[0, 150:, :] = 1.0
+    xq, sc = orc.quant(_bits(torch.from_numpy(x)), None, 128)
+    assert sc[0, 0] == 0 and np.all(xq[0, :128] == 0)
+    assert sc[0, 1] == np.float32(1.0) / np.float32(127.0) and np.all(xq[0, 150:] == 127)
+
+
+# --------------------------------------------------------------------------
+# int32 scores
+
+def test_qk_tile_matches_int64_matmul(orc):
+    rng = np.random.default_rng(7)
+    N, D = 200, 128
+    qi = rng.integers(-127, 128, size=(2, N, D), dtype=np.int8)
+    ki = rng.integers(-127, 128, size=(2, N, D), dtype=np.int8)
+    qi[0, 0, :] = 127
+    ki[0, 0, :] = 127  # extreme value 128 * 127^2 fits int32
+    for bh, i, j in ((0, 0, 0), (1, 1, 2), (0, 1, 3), (1, 0, 3)):
+        tile = orc.qk_tile(qi, ki, bh, i, j)
+        ref = np.zeros((128, 64), np.int64)
+        t0, u0 = i * 128, j * 64
+        qa = qi[bh, t0:min(N, t0 + 128)].astype(np.int64)
+        ka = ki[bh, u0:min(N, u0 + 64)].astype(np.int64)
+        ref[: qa.shape[0], : ka.shape[0]] = qa @ ka.T
+        assert np.array_equal(tile, ref)
+
+
+# --------------------------------------------------------------------------
+# block mask (page 5, Pillar Two; --sla_topk = fraction kept)
+
+def test_pool_means(orc):
+    q, k, v = make_qkv(1, 1, 300, 128, seed=8)
+    qb = _bits(q).reshape(1, 300, 128)
+    p = orc.pool(qb, 0, 128)
+    x = _f(qb)[0].astype(np.float64)
+    ref = np.stack([x[0:128].mean(0), x[128:256].mean(0), x[256:300].mean(0)])
+    assert np.all(np.abs(p - ref) <= 1e-6 * (np.abs(ref) + 1))
+    # exact on small integers: fl32(sum / n) with the tail's valid count
+    xi = np.random.default_rng(9).integers(-5, 6, size=(1, 300, 128)).astype(np.float32)
+    p = orc.pool(_bits(torch.from_numpy(xi)), 0, 64)
+    for b, (t0, t1) in enumerate(((0, 64), (64, 128), (128, 192), (192, 256), (256, 300))):
+        want = xi[0, t0:t1].sum(0).astype(np.float32) / np.float32(t1 - t0)
+        assert np.array_equal(p[b], want)
+
+
+def test_block_scores_are_an_exact_fma_chain(orc):
+    rng = np.random.default_rng(10)
+    D = 24
+    qbar = rng.standard_normal((3, D)).astype(np.float32)
+    kbar = (rng.standard_normal((5, D)) * 3).astype(np.float32)
+    sc = orc.block_scores(qbar, kbar, [0, 1, 2])
+    for r in range(3):
+        for j in range(5):
+            acc = Fraction(0)
+            for d in range(D):  # one rounding per fused multiply-add
+                acc = Fraction(f32_of(Fraction(float(qbar[r, d])) * Fraction(float(kbar[j, d]))
+                                      + acc))
+            assert sc[r, j] == np.float32(float(acc))
+            assert abs(float(sc[r, j]) - float(qbar[r] @ kbar[j].astype(np.float64))) < 1e-4
+
+
+def _brute_topk(s, keep):
+    """Unique kept set under the order (score desc, index asc), by enumeration."""
+    n = len(s)
+    found = []
+    for sub in itertools.combinations(range(n), keep):
+        subset = set(sub)
+        ok = all((s[a] > s[b]) or (s[a] == s[b] and a < b)
+                 for a in subset for b in range(n) if b not in subset)
+        if ok:
+            found.append(sub)
+    return found
+
+
+def test_topk_bruteforce_with_ties(orc):
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        n = int(rng.integers(1, 13))
+        keep = int(rng.integers(1, n + 1))
+        s = rng.integers(-3, 4, size=n).astype(np.float32)  # many ties
+        if trial % 3 == 0:
+            s[s == 0] = np.where(rng.random((s == 0).sum()) < 0.5, -0.0, 0.0)
+        kidx, mask = orc.topk(s[None, :], keep)
+        found = _brute_topk([float(a) for a in s], keep)
+        assert len(found) == 1
+        assert list(kidx[0]) == list(found[0])
+        assert mask[0].sum() == keep and all(mask[0][list(found[0])] == 1)
+
+
+def test_topk_nested_and_full(orc):
+    rng = np.random.default_rng(12)
+    s = rng.standard_normal((4, 40)).astype(np.float32)
+    prev = None
+    for keep in range(1, 41):
+        kidx, _ = orc.topk(s, keep)
+        assert np.all(np.diff(kidx, axis=1) > 0)
+        if prev is not None:
+            for r in range(4):
+                assert set(prev[r]) <= set(kidx[r])
+        prev = kidx
+    assert np.array_equal(prev, np.tile(np.arange(40), (4, 1)))
+
+
+def test_mask_from_raw_k_matches_smoothed_k_when_separated(orc):
+    # q.mu is the same for every key block of a query row, so ranking with raw
+    # K or with K - mu agrees (exactly in exact arithmetic; checked here on
+    # well separated scores).
+    q, k, v = make_qkv(1, 1, 2048, 128, seed=13)
+    qb, kb = _bits(q).reshape(1, 2048, 128), _bits(k).reshape(1, 2048, 128)
+    qbar, kbar = orc.pool(qb, 0, 128), orc.pool(kb, 0, 64)
+    mu = kbar.astype(np.float64).mean(0)
+    s_raw = qbar.astype(np.float64) @ kbar.astype(np.float64).T
+    s_sm = qbar.astype(np.float64) @ (kbar.astype(np.float64) - mu).T
+    kidx, _ = orc.topk(orc.block_scores(qbar, kbar, range(16)), 5)
+    for i in range(16):
+        order = np.argsort(-s_sm[i], kind="stable")
+        gap = np.sort(s_raw[i])[::-1]
+        if gap[4] - gap[5] > 1e-4:
+            assert sorted(order[:5]) == list(kidx[i])
+
+
+# --------------------------------------------------------------------------
+# sparse softmax branch (page 5, Pillars One and Two)
+
+def test_sparse_golden_small(orc):
+    g = _golden("sparse_decl_small.json")
+    N, D = 3, 128
+    qi = np.zeros((1, N, D), np.int8)
+    qi[0, :, 0] = 1
+    ki = np.zeros((1, N, D), np.int8)
+    ki[0, :, 0] = g["S"]
+    v = np.zeros((1, N, D), np.float32)
+    for u in range(3):
+        v[0, u, u] = 1.0
+    vb = _bits(torch.from_numpy(v))
+    sm = float(np.float32(math.log(2.0)))
+    assert np.float32(sm * 1.4426950408889634) == 1.0
+    res = orc.sparse_rows(qi, np.ones((1, 1), np.float32), ki,
+                          np.full((1, 1), g["k_scale"], np.float32), vb, 0, [0], sm_scale=sm)
+    assert np.allclose(res["decl"][0, :3], g["o"], rtol=0, atol=1e-15)
+    assert np.all(res["decl"][0, 3:] == 0)
+    # exact arithmetic: p = exp((S*0.5) * ln2 - max) = 2^((S-3)/2) up to fl32(ln 2)
+    pe = 2.0 ** ((np.array(g["S"]) - 3) / 2.0)
+    assert np.allclose(res["exact"][0, :3], pe / pe.sum(), rtol=1e-7)
+
+
+def test_sparse_uniform_when_q_is_zero(orc):
+    # q = 0 gives every score 0: both numerics reduce to the plain mean of V
+    # over the valid tokens of the kept blocks.
+    q, k, v = make_qkv(1, 1, 300, 128, seed=14)
+    qb, kb, vb = (_bits(t).reshape(1, 300, 128) for t in (torch.zeros_like(q), k, v))
+    qi, qs, ki, ks, mu = orc.quant_qk(qb, kb)
+    kidx = np.array([[0, 4], [1, 2], [3, 4]], np.int32)  # block 4 is the 44-token tail
+    toks = [0, 130, 299]
+    res = orc.sparse_rows(qi, qs, ki, ks, vb, 0, toks, kidx_head=kidx)
+    vf = _f(vb)[0].astype(np.float64)
+    for r, t in enumerate(toks):
+        sel = np.concatenate([np.arange(j * 64, min(300, j * 64 + 64)) for j in kidx[t // 128]])
+        want = vf[sel].mean(0)
+        assert np.allclose(res["decl"][r], want, atol=1e-12)
+        assert np.allclose(res["exact"][r], want, atol=1e-12)
+
+
+def test_sparse_equals_dense_on_gathered_blocks(orc):
+    # The sparse branch over kept blocks equals the dense branch run on a
+    # problem whose keys are exactly those blocks (same int8 rows and scales).
+    q, k, v = make_qkv(1, 1, 1000, 128, seed=15)
+    qb, kb, vb = (_bits(t).reshape(1, 1000, 128) for t in (q, k, v))
+    qi, qs, ki, ks, mu = orc.quant_qk(qb, kb)
+    kidx = np.array([[1, 5, 15]] * 8, np.int32)  # block 15 = tokens 960..999 (tail)
+    toks = [3, 500, 999]
+    res = orc.sparse_rows(qi, qs, ki, ks, vb, 0, toks, kidx_head=kidx)
+    sel = np.concatenate([np.arange(64, 128), np.arange(320, 384), np.arange(960, 1000)])
+    ks2 = ks[:, [1, 5, 15]].copy()
+    for r, t in enumerate(toks):
+        # a problem of exactly the 168 gathered keys (blocks of 64, 64, 40),
+        # with the query row placed at its token 0 and run densely
+        q3 = np.zeros((1, len(sel), 128), np.int8)
+        q3[0, 0] = qi[0, t]
+        res3 = orc.sparse_rows(q3, np.full((1, 2), qs[0, t // 128], np.float32),
+                               ki[:, sel].copy(), ks2, vb[:, sel].copy(), 0, [0])
+        assert np.allclose(res["decl"][r], res3["decl"][0], rtol=0, atol=1e-15)
+        assert np.allclose(res["exact"][r], res3["exact"][0], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("N", [256, 1000])
+def test_full_density_close_to_fp64_dense_attention(orc, N):
+    # BASELINE pin: at 100% block density with the linear branch off, both
+    # numerics stay within cosine 0.999 of fp64 softmax attention on the
+    # unquantized inputs.
+    q, k, v = make_qkv(1, 2, N, 128, seed=16)
+    qb, kb, vb = (_bits(t).reshape(2, N, 128) for t in (q, k, v))
+    qi, qs, ki, ks, mu = orc.quant_qk(qb, kb)
+    toks = np.arange(N)
+    for bh in range(2):
+        res = orc.sparse_rows(qi, qs, ki, ks, vb, bh, toks)
+        ref = orc.dense_rows(qb, kb, vb, bh, toks)
+        for key in ("decl", "exact"):
+            a, b = res[key].ravel(), ref.ravel()
+            cos = a @ b / np.linalg.norm(a) / np.linalg.norm(b)
+            assert cos >= 0.999, (key, cos)
+
+
+def test_smoothing_reduces_quantization_error(orc):
+    # With outlier channels in K, quantizing K - mean is more accurate than
+    # quantizing K itself (the purpose of the smoothing on page 5, Pillar One).
+    N = 512
+    q, k, v = make_qkv(1, 1, N, 128, seed=17, offset_std=8.0)
+    qb, kb, vb = (_bits(t).reshape(1, N, 128) for t in (q, k, v))
+    qi, qs, ki, ks, mu = orc.quant_qk(qb, kb)
+    ki0, ks0 = orc.quant(kb, np.zeros_like(mu), 64)
+    toks = np.arange(0, N, 3)
+    ref = orc.dense_rows(qb, kb, vb, 0, toks)
+    e_sm = np.linalg.norm(orc.sparse_rows(qi, qs, ki, ks, vb, 0, toks)["exact"] - ref)
+    e_raw = np.linalg.norm(orc.sparse_rows(qi, qs, ki0, ks0, vb, 0, toks)["exact"] - ref)
+    assert e_sm < 0.5 * e_raw, (e_sm, e_raw)
+
+
+def test_dense_fp64_matches_torch_sdpa(orc):
+    q, k, v = make_qkv(1, 1, 200, 128, seed=18)
+    qb, kb, vb = (_bits(t).reshape(1, 200, 128) for t in (q, k, v))
+    toks = np.arange(200)
+    got = orc.dense_rows(qb, kb, vb, 0, toks)
+    qd, kd, vd = (t.reshape(1, 1, 200, 128).double() for t in (q, k, v))
+    sm = float(np.float32(1.0 / math.sqrt(128)))  # the oracle's default scale is fp32
+    want = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, scale=sm)[0, 0].numpy()
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_amb_flags_a_near_midpoint(orc):
+    # c chosen so that 2^(c - 1) sits within 2^-24 of the bf16 midpoint
+    # 200.5/256: that p may round either way on a GPU, so amb > 0; a row whose
+    # p are exact powers of two has amb = 0.
+    N, D = 2, 128
+    qi = np.zeros((1, N, D), np.int8)
+    qi[0, :, 0] = 1
+    ki = np.zeros((1, N, D), np.int8)
+    ki[0, 0, 0] = 1
+    ki[0, 1, 0] = 0
+    v = np.zeros((1, N, D), np.float32)
+    v[0, 0, 0] = 1.0
+    vb = _bits(torch.from_numpy(v))
+    sm = float(np.float32(math.log(2.0)))
+    c = np.float32(1.0 + math.log2(200.5 / 256))
+    res = orc.sparse_rows(qi, np.ones((1, 1), np.float32), ki, np.full((1, 1), c, np.float32),
+                          vb, 0, [0], sm_scale=sm)
+    assert res["amb"][0] > 0
+    res = orc.sparse_rows(qi, np.ones((1, 1), np.float32), ki, np.ones((1, 1), np.float32),
+                          vb, 0, [0], sm_scale=sm)
+    assert res["amb"][0] == 0
+
+
+# --------------------------------------------------------------------------
+# linear branch (page 5, Pillar Two: light global linear attention)
+
+def _phi(x):
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def test_phi_values():
+    assert _phi(np.array([0.0]))[0] == 1.0 and _phi(np.array([1.0]))[0] == 2.0
+    assert abs(_phi(np.array([-1.0]))[0] - math.exp(-1)) < 1e-16
+
+
+def test_linear_branch_equals_token_level_linear_attention(orc):
+    N = 700  # 11 key blocks, the last one 60 tokens; 6 query blocks
+    q, k, v = make_qkv(1, 2, N, 128, seed=19)
+    qb, kb, vb = (_bits(t).reshape(2, N, 128) for t in (q, k, v))
+    keep = 3
+    kidx, _ = orc.block_mask(qb, kb, keep)
+    toks = np.array([0, 1, 127, 128, 400, 650, 699])
+    for bh in range(2):
+        h, z = orc.linear_states(kb, vb, bh)
+        got = orc.linear_rows(qb, h, z, bh, toks, kidx[bh])
+        qf, kf, vf = (_f(x)[bh].astype(np.float64) for x in (qb, kb, vb))
+        for r, t in enumerate(toks):
+            kept = set(kidx[bh][t // 128])
+            comp = [u for u in range(N) if (u // 64) not in kept]
+            w = _phi(kf[comp]) @ _phi(qf[t])  # phi(q).phi(k_u) per complement token
+            want = (w[:, None] * vf[comp]).sum(0) / w.sum()
+            assert np.max(np.abs(got[r] - want)) < 1e-12 * (1 + np.max(np.abs(want)))
+
+
+def test_linear_branch_zero_when_everything_kept(orc):
+    N = 300
+    q, k, v = make_qkv(1, 1, N, 128, seed=20)
+    qb, kb, vb = (_bits(t).reshape(1, N, 128) for t in (q, k, v))
+    h, z = orc.linear_states(kb, vb, 0)
+    kidx = np.tile(np.arange(5, dtype=np.int32), (3, 1))
+    got = orc.linear_rows(qb, h, z, 0, [0, 200, 299], kidx)
+    assert np.all(got == 0)
+    got = orc.linear_rows(qb, h, z, 0, [0, 200], None)
+    assert np.all(got == 0)
+
+
+def test_linear_states_sum_to_global_linear_attention(orc):
+    # With no block kept the branch is global linear attention over all keys.
+    N = 260
+    q, k, v = make_qkv(1, 1, N, 128, seed=21)
+    qb, kb, vb = (_bits(t).reshape(1, N, 128) for t in (q, k, v))
+    h, z = orc.linear_states(kb, vb, 0)
+    qf, kf, vf = (_f(x)[0].astype(np.float64) for x in (qb, kb, vb))
+    fk = _phi(kf)
+    assert np.allclose(h.sum(0), fk.T @ vf, rtol=1e-13, atol=1e-10)
+    assert np.allclose(z.sum(0), fk.sum(0), rtol=1e-13)
