@@ -1,0 +1,384 @@
+// api.hip -- the C ABI (include/ssa.h): argument validation, workspace layout
+// and kernel launches. Validation runs before any HIP call, so every argument
+// error returns with nothing enqueued.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/ssa.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace ssa;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ssa_status fail(ssa_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+ssa_status hip_fail(hipError_t e, const char* what) {
+    return fail(SSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Dims {
+    int64_t BH, N, nqb, nkb, nkbp, ngroups;
+};
+
+ssa_status check_shape(const ssa_shape& s, Dims* d) {
+    if (s.B < 1 || s.H < 1 || s.N < 1 || s.D < 1)
+        return fail(SSA_ERR_INVALID, "shape must be positive (B=%lld H=%lld N=%lld D=%lld)",
+                    (long long)s.B, (long long)s.H, (long long)s.N, (long long)s.D);
+    if (s.D != SSA_HEAD_DIM) return fail(SSA_ERR_UNSUPPORTED, "head dim %lld != 128", (long long)s.D);
+    if (s.N > SSA_MAX_N)
+        return fail(SSA_ERR_UNSUPPORTED, "N=%lld exceeds %d", (long long)s.N, SSA_MAX_N);
+    if (s.B > (1 << 20) || s.H > (1 << 20) || s.B * s.H > (1 << 20))
+        return fail(SSA_ERR_UNSUPPORTED, "B*H too large");
+    d->BH = s.B * s.H;
+    d->N = s.N;
+    d->nqb = (s.N + QBLK - 1) / QBLK;
+    d->nkb = (s.N + KBLK - 1) / KBLK;
+    d->nkbp = (d->nkb + 31) / 32 * 32;
+    d->ngroups = (d->nkb + LIN_GROUP - 1) / LIN_GROUP;
+    return SSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+ssa_status need_ptr(const void* p, size_t align, const char* name) {
+    if (!p) return fail(SSA_ERR_INVALID, "%s is NULL", name);
+    if (!aligned(p, align)) return fail(SSA_ERR_INVALID, "%s is not %zu-byte aligned", name, align);
+    return SSA_OK;
+}
+
+struct Range {
+    const void* p;
+    size_t n;
+    const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// every output against every input and every other output
+ssa_status check_alias(const Range* outs, int no, const Range* ins, int ni) {
+    for (int x = 0; x < no; ++x) {
+        for (int y = 0; y < ni; ++y)
+            if (overlap(outs[x], ins[y]))
+                return fail(SSA_ERR_INVALID, "output %s overlaps input %s", outs[x].name, ins[y].name);
+        for (int y = x + 1; y < no; ++y)
+            if (overlap(outs[x], outs[y]))
+                return fail(SSA_ERR_INVALID, "output %s overlaps output %s", outs[x].name,
+                            outs[y].name);
+    }
+    return SSA_OK;
+}
+
+// gfx950 check, once per device
+std::atomic<int> g_dev_ok[64];
+
+ssa_status check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(SSA_ERR_UNSUPPORTED, "device index %d", dev);
+    int st = g_dev_ok[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+        st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_dev_ok[dev].store(st, std::memory_order_release);
+    }
+    if (st != 1) return fail(SSA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return SSA_OK;
+}
+
+// workspace layouts ----------------------------------------------------------
+
+size_t ws_quant(const Dims& d) { return align256((size_t)d.BH * d.nkb * HD * 4); }
+
+struct MaskWs {
+    size_t qbar, kbarT, total;
+    int64_t ldk;
+};
+MaskWs ws_mask(const Dims& d) {
+    MaskWs w;
+    w.ldk = (d.nkb + 15) / 16 * 16;
+    w.qbar = 0;
+    w.kbarT = align256((size_t)d.BH * d.nqb * HD * 4);
+    w.total = w.kbarT + align256((size_t)d.BH * HD * w.ldk * 4);
+    return w;
+}
+
+struct AttnWs {
+    size_t vt, hs, hpart, htot, msel, hnon, total;
+};
+AttnWs ws_attn(const Dims& d, bool linear) {
+    AttnWs w{};
+    size_t off = 0;
+    w.vt = off;
+    off += align256((size_t)d.BH * d.nkb * HD * KBLK * 2);
+    if (linear) {
+        w.hs = off;
+        off += align256((size_t)d.BH * d.nkb * HS_ROW * 2);
+        w.hpart = off;
+        off += align256((size_t)d.BH * d.ngroups * HS_ROW * 4);
+        w.htot = off;
+        off += align256((size_t)d.BH * HS_ROW * 4);
+        w.msel = off;
+        off += align256((size_t)d.BH * d.nqb * d.nkbp * 2);
+        w.hnon = off;
+        off += align256((size_t)d.BH * d.nqb * HS_ROW * 4);
+    }
+    w.total = off;
+    return w;
+}
+
+ssa_status check_ws(void* ws, size_t have, size_t need) {
+    if (need == 0) return SSA_OK;
+    if (!ws) return fail(SSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(ws, 256)) return fail(SSA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (have < need) return fail(SSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+    return SSA_OK;
+}
+
+#define TRY(x)                          \
+    do {                                \
+        ssa_status _st = (x);           \
+        if (_st != SSA_OK) return _st;  \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int64_t ssa_num_q_blocks(int64_t N) { return N < 1 ? 0 : (N + QBLK - 1) / QBLK; }
+int64_t ssa_num_k_blocks(int64_t N) { return N < 1 ? 0 : (N + KBLK - 1) / KBLK; }
+
+int64_t ssa_keep_blocks(int64_t N, double topk) {
+    const int64_t nkb = ssa_num_k_blocks(N);
+    if (nkb < 1) return 0;
+    if (!(topk == topk)) return 1;  // NaN
+    double x = std::floor(topk * (double)nkb + 0.5);
+    if (x < 1.0) return 1;
+    if (x > (double)nkb) return nkb;
+    return (int64_t)x;
+}
+
+size_t ssa_workspace_bytes(int op, ssa_shape s, int64_t keep, int branches) {
+    Dims d;
+    if (check_shape(s, &d) != SSA_OK) return 0;
+    switch (op) {
+        case SSA_OP_QUANT: return ws_quant(d);
+        case SSA_OP_MASK: return ws_mask(d).total;
+        case SSA_OP_ATTN: {
+            const bool linear = (branches & SSA_BRANCH_LINEAR) && keep >= 1 && keep < d.nkb;
+            return ws_attn(d, linear).total;
+        }
+        default: return 0;
+    }
+}
+
+const char* ssa_status_str(ssa_status st) {
+    switch (st) {
+        case SSA_OK: return "ok";
+        case SSA_ERR_INVALID: return "invalid argument";
+        case SSA_ERR_UNSUPPORTED: return "unsupported";
+        case SSA_ERR_WORKSPACE: return "workspace too small";
+        case SSA_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* ssa_last_error(void) { return g_err; }
+
+ssa_status sage_quant_qk(const uint16_t* q, const uint16_t* k, ssa_shape s, int8_t* q_i8,
+                         float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, void* ws,
+                         size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    Dims d;
+    TRY(check_shape(s, &d));
+    TRY(need_ptr(q, 16, "q"));
+    TRY(need_ptr(k, 16, "k"));
+    TRY(need_ptr(q_i8, 16, "q_i8"));
+    TRY(need_ptr(k_i8, 16, "k_i8"));
+    TRY(need_ptr(q_scale, 4, "q_scale"));
+    TRY(need_ptr(k_scale, 4, "k_scale"));
+    TRY(need_ptr(k_mean, 4, "k_mean"));
+    const size_t nel = (size_t)d.BH * d.N * HD;
+    const Range ins[] = {{q, nel * 2, "q"}, {k, nel * 2, "k"}};
+    const Range outs[] = {{q_i8, nel, "q_i8"},
+                          {k_i8, nel, "k_i8"},
+                          {q_scale, (size_t)d.BH * d.nqb * 4, "q_scale"},
+                          {k_scale, (size_t)d.BH * d.nkb * 4, "k_scale"},
+                          {k_mean, (size_t)d.BH * HD * 4, "k_mean"},
+                          {ws, ws_bytes, "workspace"}};
+    TRY(check_alias(outs, 6, ins, 2));
+    TRY(check_ws(ws, ws_bytes, ws_quant(d)));
+    TRY(check_device());
+    hipError_t e = launch_quant_qk(q, k, d.BH, (int)d.N, q_i8, q_scale, k_i8, k_scale, k_mean,
+                                   (float*)ws, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sage_quant_qk launch");
+    return SSA_OK;
+}
+
+ssa_status sla_block_mask(const uint16_t* q, const uint16_t* k, ssa_shape s, int64_t keep,
+                          int32_t* kidx, uint8_t* mask, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    Dims d;
+    TRY(check_shape(s, &d));
+    if (keep < 1 || keep > d.nkb)
+        return fail(SSA_ERR_INVALID, "keep=%lld outside [1, %lld]", (long long)keep,
+                    (long long)d.nkb);
+    TRY(need_ptr(q, 16, "q"));
+    TRY(need_ptr(k, 16, "k"));
+    TRY(need_ptr(kidx, 4, "kidx"));
+    if (mask && !aligned(mask, 1)) return fail(SSA_ERR_INVALID, "mask misaligned");
+    const size_t nel = (size_t)d.BH * d.N * HD;
+    const Range ins[] = {{q, nel * 2, "q"}, {k, nel * 2, "k"}};
+    const Range outs[] = {{kidx, (size_t)d.BH * d.nqb * keep * 4, "kidx"},
+                          {mask, mask ? (size_t)d.BH * d.nqb * d.nkb : 0, "mask"},
+                          {ws, ws_bytes, "workspace"}};
+    TRY(check_alias(outs, 3, ins, 2));
+    const MaskWs w = ws_mask(d);
+    TRY(check_ws(ws, ws_bytes, w.total));
+    TRY(check_device());
+    char* base = (char*)ws;
+    float* qbar = (float*)(base + w.qbar);
+    float* kbarT = (float*)(base + w.kbarT);
+    hipError_t e = launch_pool(q, k, d.BH, (int)d.N, qbar, kbarT, (int)w.ldk, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = launch_score_topk(qbar, kbarT, (int)w.ldk, d.BH, (int)d.nqb, (int)d.nkb, (int)keep, kidx,
+                              mask, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sla_block_mask launch");
+    return SSA_OK;
+}
+
+ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, ssa_shape s,
+                             const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                             const float* k_scale, const int32_t* kidx, int64_t keep, int branches,
+                             float sm_scale, uint16_t* out, float* out_f32, void* ws,
+                             size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    Dims d;
+    TRY(check_shape(s, &d));
+    if (branches < 1 || branches > 3)
+        return fail(SSA_ERR_INVALID, "branches=%d must be SPARSE, LINEAR or both", branches);
+    if (keep < 1 || keep > d.nkb)
+        return fail(SSA_ERR_INVALID, "keep=%lld outside [1, %lld]", (long long)keep,
+                    (long long)d.nkb);
+    if (!kidx && keep != d.nkb)
+        return fail(SSA_ERR_INVALID, "dense call (kidx NULL) needs keep == Nkb (%lld)",
+                    (long long)d.nkb);
+    if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
+        return fail(SSA_ERR_INVALID, "sm_scale is not finite");
+    const bool sparse = branches & SSA_BRANCH_SPARSE;
+    const bool linear = (branches & SSA_BRANCH_LINEAR) && kidx && keep < d.nkb;
+    TRY(need_ptr(v, 16, "v"));
+    TRY(need_ptr(q_i8, 16, "q_i8"));
+    TRY(need_ptr(k_i8, 16, "k_i8"));
+    TRY(need_ptr(q_scale, 4, "q_scale"));
+    TRY(need_ptr(k_scale, 4, "k_scale"));
+    TRY(need_ptr(out, 16, "out"));
+    if (out_f32) TRY(need_ptr(out_f32, 16, "out_f32"));
+    if (kidx) TRY(need_ptr(kidx, 4, "kidx"));
+    if (linear) {
+        TRY(need_ptr(q, 16, "q"));
+        TRY(need_ptr(k, 16, "k"));
+    }
+    const size_t nel = (size_t)d.BH * d.N * HD;
+    const Range ins[] = {{q, nel * 2, "q"},
+                         {k, nel * 2, "k"},
+                         {v, nel * 2, "v"},
+                         {q_i8, nel, "q_i8"},
+                         {k_i8, nel, "k_i8"},
+                         {q_scale, (size_t)d.BH * d.nqb * 4, "q_scale"},
+                         {k_scale, (size_t)d.BH * d.nkb * 4, "k_scale"},
+                         {kidx, kidx ? (size_t)d.BH * d.nqb * keep * 4 : 0, "kidx"}};
+    const Range outs[] = {{out, nel * 2, "out"},
+                          {out_f32, out_f32 ? nel * 4 : 0, "out_f32"},
+                          {ws, ws_bytes, "workspace"}};
+    TRY(check_alias(outs, 3, ins, 8));
+    const AttnWs w = ws_attn(d, linear);
+    TRY(check_ws(ws, ws_bytes, w.total));
+    TRY(check_device());
+
+    const float sm = sm_scale > 0.f ? sm_scale : (float)(1.0 / std::sqrt((double)HD));
+    hipStream_t st = (hipStream_t)stream;
+    char* base = (char*)ws;
+    uint16_t* vt = (uint16_t*)(base + w.vt);
+    hipError_t e;
+    float* hnon = nullptr;
+    if (linear) {
+        uint16_t* hs = (uint16_t*)(base + w.hs);
+        float* hpart = (float*)(base + w.hpart);
+        float* htot = (float*)(base + w.htot);
+        uint16_t* msel = (uint16_t*)(base + w.msel);
+        hnon = (float*)(base + w.hnon);
+        e = launch_linear_states(k, v, d.BH, (int)d.N, vt, hs, hpart, htot, st);
+        if (e == hipSuccess)
+            e = launch_complement(kidx, (int)keep, hs, htot, d.BH, (int)d.N, msel, hnon, st);
+    } else {
+        e = launch_vt_only(v, d.BH, (int)d.N, vt, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_fwd launch (linear / V layout)");
+    AttnArgs a;
+    a.q_i8 = q_i8;
+    a.q_scale = q_scale;
+    a.k_i8 = k_i8;
+    a.k_scale = k_scale;
+    a.vt = vt;
+    a.kidx = kidx;
+    a.keep = (int)keep;
+    a.N = (int)d.N;
+    a.nqb = (int)d.nqb;
+    a.nkb = (int)d.nkb;
+    a.BH = d.BH;
+    a.K32 = (float)((double)sm * 1.4426950408889634074);
+    a.do_sparse = sparse ? 1 : 0;
+    a.q = q;
+    a.hnon = hnon;
+    a.out = out;
+    a.out32 = out_f32;
+    e = launch_attn(a, st);
+    if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_fwd launch");
+    return SSA_OK;
+}
+
+ssa_status sage_qk_int32_tiles(const int8_t* q_i8, const int8_t* k_i8, ssa_shape s,
+                               const int32_t* tiles, int64_t T, int32_t* out, void* stream) {
+    g_err[0] = 0;
+    Dims d;
+    TRY(check_shape(s, &d));
+    if (T < 1 || T > (1 << 24)) return fail(SSA_ERR_INVALID, "T=%lld out of range", (long long)T);
+    TRY(need_ptr(q_i8, 16, "q_i8"));
+    TRY(need_ptr(k_i8, 16, "k_i8"));
+    TRY(need_ptr(tiles, 4, "tiles"));
+    TRY(need_ptr(out, 16, "out"));
+    const size_t nel = (size_t)d.BH * d.N * HD;
+    const Range ins[] = {{q_i8, nel, "q_i8"}, {k_i8, nel, "k_i8"}, {tiles, (size_t)T * 12, "tiles"}};
+    const Range outs[] = {{out, (size_t)T * QBLK * KBLK * 4, "out"}};
+    TRY(check_alias(outs, 1, ins, 3));
+    TRY(check_device());
+    hipError_t e = launch_qk_tiles(q_i8, k_i8, d.BH, (int)d.N, tiles, T, out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sage_qk_int32_tiles launch");
+    return SSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// common.hpp -- shared device helpers for the gfx950 SageSLA kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssa {
+
+constexpr int HD = 128;    // head dimension
+constexpr int QBLK = 128;  // query block (tokens)
+constexpr int KBLK = 64;   // key block (tokens)
+constexpr int HS_ROW = HD * HD + HD;  // one linear state: h^T [e][d] then z [d]
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 honours the RNE mode).
+__device__ __forceinline__ uint16_t f2bf(float x) {
+    __bf16 h = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ i32x16 mfma_i8_32x32x32(i32x4 a, i32x4 b, i32x16 c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Output layout of the 32x32 MFMA families: lane l, accumulator r holds
+// column (l & 31) and row 8*(r/4) + 4*(l/32) + (r%4).
+__device__ __forceinline__ int mfma32_row(int lane, int r) {
+    return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// Split an fp32 value into bf16 hi + bf16 lo (hi + lo carries ~16 bits).
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Workgroup id -> logical work item so that consecutive items run on the same
+// XCD. Workgroups are dispatched round-robin over the 8 XCDs; each XCD gets a
+// contiguous range of items, processed in order, so neighbouring items (which
+// share K/V or GEMM operand tiles) meet in that XCD's L2.
+__device__ __forceinline__ int64_t xcd_item(int64_t wg, int64_t total) {
+    const int64_t per = (total + 7) / 8;
+    return (wg & 7) * per + (wg >> 3);
+}
+
+}  // namespace ssa

@@ -1,0 +1,49 @@
+// kernels.hpp -- launchers of the gfx950 kernels (internal, not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssa {
+
+// quant.hip
+hipError_t launch_quant_qk(const uint16_t* q, const uint16_t* k, int64_t BH, int N, int8_t* q_i8,
+                           float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                           float* ws_part, hipStream_t st);
+hipError_t launch_pool(const uint16_t* q, const uint16_t* k, int64_t BH, int N, float* qbar,
+                       float* kbarT, int ldk, hipStream_t st);
+// mask.hip
+hipError_t launch_score_topk(const float* qbar, const float* kbarT, int ldk, int64_t BH, int nqb,
+                             int nkb, int keep, int32_t* kidx, uint8_t* mask, hipStream_t st);
+
+// linear.hip
+constexpr int LIN_GROUP = 16;  // key blocks per linear-states workgroup
+hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH, int N,
+                                uint16_t* vt, uint16_t* hs, float* hpart, float* htot,
+                                hipStream_t st);
+hipError_t launch_vt_only(const uint16_t* v, int64_t BH, int N, uint16_t* vt, hipStream_t st);
+hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, const float* htot,
+                             int64_t BH, int N, uint16_t* msel, float* hnon, hipStream_t st);
+
+// attn.hip
+struct AttnArgs {
+    const int8_t* q_i8;
+    const float* q_scale;
+    const int8_t* k_i8;
+    const float* k_scale;
+    const uint16_t* vt;    // [BH][nkb][128 dv][64 permuted keys]
+    const int32_t* kidx;   // [BH][nqb][keep] or null (dense)
+    int keep;
+    int N, nqb, nkb;
+    int64_t BH;
+    float K32;             // fl32(sm * log2 e)
+    int do_sparse;
+    const uint16_t* q;     // raw bf16 Q (linear branch)
+    const float* hnon;     // [BH][nqb][HS_ROW] complement states, or null
+    uint16_t* out;
+    float* out32;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+hipError_t launch_qk_tiles(const int8_t* q_i8, const int8_t* k_i8, int64_t BH, int N,
+                           const int32_t* tiles, int64_t T, int32_t* out, hipStream_t st);
+
+}  // namespace ssa

@@ -1,0 +1,264 @@
+// linear.hip -- the linear-attention branch of SageSLA, and the V re-layout
+// the sparse kernel reads.
+//
+// TurboDiffusion pages, page 5 "Four Technical Pillars", Pillar Two: the
+// block interactions the sparse part skips are covered by a light global
+// linear-attention term. With phi = elu + 1 on raw K, each 64-token key block
+// j contributes the state h_j = sum_u phi(k_u) v_u^T (128 x 128) and
+// z_j = sum_u phi(k_u). A query block needs the sums over the key blocks it did
+// NOT keep. They are formed as H_i = H_total - sum_{j kept} h_j: H_total in
+// fp32, the kept-block sum as a dense 0/1 x bf16 matrix-core GEMM, so the bf16
+// rounding of h_j only touches the kept ~10% of the blocks.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssa {
+
+constexpr int TP = KBLK + 8;  // LDS pitch (bf16) of a [channel][token] tile: 144 B
+
+// Position p (0..63) of a re-laid V tile row holds key 16*(p/16) + kperm(p%16):
+// the order in which one lane of the 32x32 MFMA output holds its keys, so the
+// sparse kernel feeds its P registers to the PV product without shuffles.
+//   positions 0-3 -> keys 0-3, 4-7 -> 8-11, 8-11 -> 4-7, 12-15 -> 12-15.
+
+// Per 64-token key block: V^T re-laid for the sparse kernel, and (STATES)
+// the linear states h_j^T [e][d] (bf16, for the GEMM), z_j, and an fp32 running
+// sum over the workgroup's LIN_GROUP key blocks.
+template <bool STATES>
+__global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __restrict__ k,
+                                                            const uint16_t* __restrict__ v, int N,
+                                                            int nkb, int ngroups,
+                                                            uint16_t* __restrict__ vt,
+                                                            uint16_t* __restrict__ hs,
+                                                            float* __restrict__ hpart) {
+    __shared__ __attribute__((aligned(16))) uint16_t vtl[HD * TP];
+    __shared__ __attribute__((aligned(16))) uint16_t fkh[STATES ? HD * TP : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t fkl[STATES ? HD * TP : 8];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
+              hi = lane >> 5;
+    const int64_t bh = blockIdx.y;
+    const int g = blockIdx.x;
+    const int G = STATES ? LIN_GROUP : 1;
+    f32x16 tot[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) tot[dt] = f32x16{};
+    float ztot = 0.f;
+    for (int jb = 0; jb < G; ++jb) {
+        const int j = g * G + jb;
+        if (j >= nkb) break;
+        // token-major global loads, channel-major LDS stores (u fastest: conflict free)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int c = tid + 256 * it;
+            const int u = c & 63, ch = c >> 6;
+            const int tok = j * KBLK + u;
+            const bool ok = tok < N;
+            const int64_t off = (bh * N + tok) * HD + 8 * ch;
+            u16x8 vv = ok ? *(const u16x8*)(v + off) : u16x8{};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vtl[(8 * ch + e) * TP + u] = vv[e];
+            if (STATES) {
+                u16x8 kk = ok ? *(const u16x8*)(k + off) : u16x8{};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = bf2f(kk[e]);
+                    const float ph = ok ? (f > 0.f ? f + 1.f : __expf(f)) : 0.f;
+                    __bf16 h, l;
+                    split_bf16(ph, h, l);
+                    fkh[(8 * ch + e) * TP + u] = __builtin_bit_cast(uint16_t, h);
+                    fkl[(8 * ch + e) * TP + u] = __builtin_bit_cast(uint16_t, l);
+                }
+            }
+        }
+        __syncthreads();
+        // V^T tile in the sparse kernel's key order: 128 rows x 8 chunks of 16 B
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int c = tid + 256 * it;
+            const int dv = c >> 3, pc = c & 7, cc = pc >> 1, h2 = pc & 1;
+            const u16x4 a = *(const u16x4*)(vtl + dv * TP + 16 * cc + 4 * h2);
+            const u16x4 b = *(const u16x4*)(vtl + dv * TP + 16 * cc + 8 + 4 * h2);
+            *(u16x8*)(vt + ((bh * nkb + j) * HD + dv) * KBLK + 8 * pc) =
+                u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        }
+        if (STATES) {
+            // h_j^T[e][d] = sum_u V[u][e] phi(K)[u][d]: A = V^T rows e, B = phi(K) cols d,
+            // phi(K) = hi + lo (two bf16 products, fp32 accumulation)
+            f32x16 acc[4];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+#pragma unroll
+            for (int uc = 0; uc < 4; ++uc) {
+                const bf16x8 a = *(const bf16x8*)(vtl + (32 * wave + l32) * TP + 16 * uc + 8 * hi);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x8 bh8 = *(const bf16x8*)(fkh + (32 * dt + l32) * TP + 16 * uc + 8 * hi);
+                    const bf16x8 bl8 = *(const bf16x8*)(fkl + (32 * dt + l32) * TP + 16 * uc + 8 * hi);
+                    acc[dt] = mfma_bf16_32x32x16(a, bh8, acc[dt]);
+                    acc[dt] = mfma_bf16_32x32x16(a, bl8, acc[dt]);
+                }
+            }
+            uint16_t* hrow = hs + (bh * nkb + j) * HS_ROW;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int e = 32 * wave + mfma32_row(lane, r), d = 32 * dt + l32;
+                    hrow[e * HD + d] = f2bf(acc[dt][r]);
+                    tot[dt][r] += acc[dt][r];
+                }
+            if (tid < HD) {
+                float z = 0.f;
+                for (int u = 0; u < KBLK; ++u)
+                    z += bf2f(fkh[tid * TP + u]) + bf2f(fkl[tid * TP + u]);
+                hrow[HD * HD + tid] = f2bf(z);
+                ztot += z;
+            }
+        }
+        __syncthreads();
+    }
+    if (STATES) {
+        float* prow = hpart + (bh * ngroups + g) * HS_ROW;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int e = 32 * wave + mfma32_row(lane, r), d = 32 * dt + l32;
+                prow[e * HD + d] = tot[dt][r];
+            }
+        if (tid < HD) prow[HD * HD + tid] = ztot;
+    }
+}
+
+// H_total[bh][n] = sum over groups, in group order, of the fp32 partials.
+__global__ __launch_bounds__(256) void htot_kernel(const float* __restrict__ hpart, int ngroups,
+                                                   float* __restrict__ htot) {
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    const int64_t bh = blockIdx.y;
+    if (n >= HS_ROW) return;
+    float s = 0.f;
+    for (int g = 0; g < ngroups; ++g) s += hpart[(bh * ngroups + g) * HS_ROW + n];
+    htot[bh * HS_ROW + n] = s;
+}
+
+// msel[bh][i][j] = 1 (bf16) if key block j is kept by query block i, else 0;
+// j runs to nkbp (a multiple of 32) so the GEMM reads whole K steps.
+__global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ kidx, int keep,
+                                                   int nqb, int nkbp, uint16_t* __restrict__ msel) {
+    extern __shared__ int krow[];
+    const int64_t bh = blockIdx.y;
+    const int i = blockIdx.x;
+    const int32_t* src = kidx + (bh * nqb + i) * (int64_t)keep;
+    for (int a = threadIdx.x; a < keep; a += 256) krow[a] = src[a];
+    __syncthreads();
+    uint16_t* dst = msel + (bh * nqb + i) * (int64_t)nkbp;
+    for (int j = threadIdx.x; j < nkbp; j += 256) {
+        int lo = 0, hi = keep;  // kept blocks are ascending
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (krow[mid] < j) lo = mid + 1; else hi = mid;
+        }
+        dst[j] = (lo < keep && krow[lo] == j) ? (uint16_t)0x3F80 : (uint16_t)0;
+    }
+}
+
+constexpr int GP = 32 + 8;  // LDS pitch (bf16) of a [row][32] GEMM operand tile: 80 B
+
+// hnon[bh][i][n] = htot[bh][n] - sum_j msel[bh][i][j] * hs[bh][j][n]
+// Workgroup tile 128 (i) x 128 (n), K step 32 key blocks, 4 waves of 32 rows.
+__global__ __launch_bounds__(256) void complement_gemm_kernel(
+    const uint16_t* __restrict__ msel, const uint16_t* __restrict__ hs, const float* __restrict__ htot,
+    int64_t BH, int nqb, int nkb, int nkbp, float* __restrict__ hnon) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[128 * GP];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * GP];
+    const int nnt = HS_ROW / 128, nmt = (nqb + 127) / 128;
+    const int64_t total = BH * nnt * nmt;
+    const int64_t item = xcd_item(blockIdx.x, total);
+    if (item >= total) return;
+    const int mt = (int)(item % nmt);
+    const int64_t rest = item / nmt;
+    const int nt = (int)(rest % nnt);
+    const int64_t bh = rest / nnt;
+    const int i0 = mt * 128, n0 = nt * 128;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
+              hi = lane >> 5;
+    f32x16 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
+    for (int j0 = 0; j0 < nkbp; j0 += 32) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int c = tid + 256 * p;
+            const int row = c >> 2, q = c & 3;
+            u16x8 a = (i0 + row < nqb)
+                          ? *(const u16x8*)(msel + (bh * nqb + i0 + row) * (int64_t)nkbp + j0 + 8 * q)
+                          : u16x8{};
+            *(u16x8*)(As + row * GP + 8 * q) = a;
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int c = tid + 256 * p;
+            const int jj = c & 31, q = c >> 5;
+            u16x8 b = (j0 + jj < nkb)
+                          ? *(const u16x8*)(hs + (bh * nkb + j0 + jj) * (int64_t)HS_ROW + n0 + 8 * q)
+                          : u16x8{};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Bs[(8 * q + e) * GP + jj] = b[e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+            const bf16x8 a = *(const bf16x8*)(As + (32 * wave + l32) * GP + 16 * ch + 8 * hi);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bf16x8 b = *(const bf16x8*)(Bs + (32 * t + l32) * GP + 16 * ch + 8 * hi);
+                acc[t] = mfma_bf16_32x32x16(a, b, acc[t]);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = i0 + 32 * wave + mfma32_row(lane, r);
+            const int n = n0 + 32 * t + l32;
+            if (i < nqb) hnon[(bh * nqb + i) * HS_ROW + n] = htot[bh * HS_ROW + n] - acc[t][r];
+        }
+}
+
+// ---------------------------------------------------------------------------
+
+hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH, int N,
+                                uint16_t* vt, uint16_t* hs, float* hpart, float* htot,
+                                hipStream_t st) {
+    const int nkb = (N + KBLK - 1) / KBLK;
+    const int ngroups = (nkb + LIN_GROUP - 1) / LIN_GROUP;
+    hipLaunchKernelGGL((linear_states_kernel<true>), dim3(ngroups, BH), dim3(256), 0, st, k, v, N,
+                       nkb, ngroups, vt, hs, hpart);
+    hipLaunchKernelGGL(htot_kernel, dim3((HS_ROW + 255) / 256, BH), dim3(256), 0, st, hpart, ngroups,
+                       htot);
+    return hipGetLastError();
+}
+
+hipError_t launch_vt_only(const uint16_t* v, int64_t BH, int N, uint16_t* vt, hipStream_t st) {
+    const int nkb = (N + KBLK - 1) / KBLK;
+    hipLaunchKernelGGL((linear_states_kernel<false>), dim3(nkb, BH), dim3(256), 0, st, nullptr, v, N,
+                       nkb, nkb, vt, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, const float* htot,
+                             int64_t BH, int N, uint16_t* msel, float* hnon, hipStream_t st) {
+    const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
+    const int nkbp = (nkb + 31) / 32 * 32;
+    hipLaunchKernelGGL(msel_kernel, dim3(nqb, BH), dim3(256), keep * sizeof(int), st, kidx, keep, nqb,
+                       nkbp, msel);
+    const int64_t total = BH * (HS_ROW / 128) * ((nqb + 127) / 128);
+    const int64_t grid = (total + 7) / 8 * 8;
+    hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel, hs, htot,
+                       BH, nqb, nkb, nkbp, hnon);
+    return hipGetLastError();
+}
+
+}  // namespace ssa

@@ -1,0 +1,189 @@
+// quant.hip -- K smoothing mean, per-block INT8 quantization, and the
+// block column sums the block mask pools with.
+//
+// TurboDiffusion pages, page 5 "Four Technical Pillars", Pillar One:
+// attention inputs quantized to 8-bit integers, with smoothing for outliers.
+// Every fp32 operation here is bit-reproducible: sums run in token order
+// (then block order), divisions are IEEE (this file is compiled with
+// -ffp-contract=off), and round-half-even comes from v_rndne_f32.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssa {
+
+// Per-block column sums of a bf16 [BH][N][128] tensor.
+// One workgroup covers NB consecutive blocks of BLK tokens; thread
+// (blk = tid/16, g = tid%16) owns channels 8g..8g+7 of its block and adds the
+// block's valid tokens in token order, starting from 0.
+//   MODE 0: out[bh][b][d] = sum                    (K mean partials)
+//   MODE 1: out[bh][b][d] = sum / valid            (pooled means)
+//   MODE 2: out[bh][d][b] = sum / valid, row pitch ld (pooled means, transposed)
+template <int BLK, int MODE>
+__global__ __launch_bounds__((1024 / BLK) * 16)
+void colsum_kernel(const uint16_t* __restrict__ x, int N, int nb, int ld, float* __restrict__ out) {
+    constexpr int NB = 1024 / BLK;
+    __shared__ float stage[MODE == 2 ? NB * HD : 1];
+    const int tid = threadIdx.x;
+    const int bl = tid >> 4, g = tid & 15;
+    const int64_t bh = blockIdx.y;
+    const int b = blockIdx.x * NB + bl;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int valid = 0;
+    if (b < nb) {
+        const int t0 = b * BLK;
+        valid = min(BLK, N - t0);
+        const uint16_t* p = x + (bh * N + t0) * HD + 8 * g;
+        int t = 0;
+        for (; t + 4 <= valid; t += 4) {
+            u16x8 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *(const u16x8*)(p + (int64_t)(t + u) * HD);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += bf2f(v[u][e]);
+        }
+        for (; t < valid; ++t) {
+            u16x8 v = *(const u16x8*)(p + (int64_t)t * HD);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += bf2f(v[e]);
+        }
+    }
+    if (MODE == 0 || MODE == 1) {
+        if (b < nb) {
+            float r[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r[e] = MODE == 1 ? acc[e] / (float)valid : acc[e];
+            float* o = out + ((bh * nb + b) * HD + 8 * g);
+            *(f32x4*)o = f32x4{r[0], r[1], r[2], r[3]};
+            *(f32x4*)(o + 4) = f32x4{r[4], r[5], r[6], r[7]};
+        }
+    } else {
+        if (b < nb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) stage[bl * HD + 8 * g + e] = acc[e] / (float)valid;
+        __syncthreads();
+        // transpose: NB*HD values, written as runs of NB consecutive blocks per channel
+        for (int idx = tid; idx < NB * HD; idx += NB * 16) {
+            const int d = idx / NB, bb = idx % NB;
+            const int b2 = blockIdx.x * NB + bb;
+            if (b2 < nb) out[(bh * HD + d) * ld + b2] = stage[bb * HD + d];
+        }
+    }
+}
+
+// mu[bh][d] = (sum over key blocks j in order of part[bh][j][d]) / N.
+__global__ __launch_bounds__(128) void kmean_final_kernel(const float* __restrict__ part, int nkb,
+                                                           int N, float* __restrict__ mu) {
+    const int d = threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    const float* p = part + bh * nkb * HD + d;
+    float tot = 0.f;
+    int j = 0;
+    for (; j + 8 <= nkb; j += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(j + u) * HD];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tot += v[u];
+    }
+    for (; j < nkb; ++j) tot += p[(int64_t)j * HD];
+    mu[bh * HD + d] = tot / (float)N;
+}
+
+// Per-block INT8 quantization of one (head, block): scale = amax/127 over the
+// block's valid tokens and all channels, q = clamp(rint(x/scale), +-127).
+// SMOOTH subtracts the K mean first (one fp32 subtraction).
+template <int BLK, bool SMOOTH>
+__global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ x,
+                                                    const float* __restrict__ mu, int N, int nb,
+                                                    int8_t* __restrict__ xq,
+                                                    float* __restrict__ scale) {
+    constexpr int IT = BLK * 16 / 256;  // 16-byte chunks per thread
+    __shared__ float wmax[4];
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int b = blockIdx.x;
+    const int t0 = b * BLK;
+    const int valid = min(BLK, N - t0);
+    const int g = tid & 15;
+    float m8[8];
+    if (SMOOTH) {
+        const float* mp = mu + bh * HD + 8 * g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m8[e] = mp[e];
+    }
+    float v[IT][8];
+    float amax = 0.f;
+    const uint16_t* base = x + (bh * N + t0) * HD;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int row = (tid >> 4) + 16 * it;
+        if (row < valid) {
+            u16x8 r = *(const u16x8*)(base + (int64_t)row * HD + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float f = bf2f(r[e]);
+                if (SMOOTH) f = f - m8[e];
+                v[it][e] = f;
+                amax = fmaxf(amax, fabsf(f));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[it][e] = 0.f;
+        }
+    }
+    amax = wave_max_f32(amax);
+    if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float s = amax / 127.0f;
+    if (tid == 0) scale[bh * nb + b] = s;
+    int8_t* qbase = xq + (bh * N + t0) * HD;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int row = (tid >> 4) + 16 * it;
+        if (row < valid) {
+            uint32_t w[2] = {0u, 0u};
+            if (s > 0.f) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float r = __builtin_rintf(v[it][e] / s);
+                    r = fminf(fmaxf(r, -127.f), 127.f);
+                    const uint32_t byte = (uint32_t)(uint8_t)(int8_t)(int)r;
+                    w[e >> 2] |= byte << (8 * (e & 3));
+                }
+            }
+            *(u32x2*)(qbase + (int64_t)row * HD + 8 * g) = u32x2{w[0], w[1]};
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+hipError_t launch_quant_qk(const uint16_t* q, const uint16_t* k, int64_t BH, int N,
+                           int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                           float* k_mean, float* ws_part, hipStream_t st) {
+    const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
+    hipLaunchKernelGGL((colsum_kernel<KBLK, 0>), dim3((nkb + 15) / 16, BH), dim3(256), 0, st, k, N,
+                       nkb, 0, ws_part);
+    hipLaunchKernelGGL(kmean_final_kernel, dim3(BH), dim3(128), 0, st, ws_part, nkb, N, k_mean);
+    hipLaunchKernelGGL((quant_kernel<QBLK, false>), dim3(nqb, BH), dim3(256), 0, st, q, nullptr, N,
+                       nqb, q_i8, q_scale);
+    hipLaunchKernelGGL((quant_kernel<KBLK, true>), dim3(nkb, BH), dim3(256), 0, st, k, k_mean, N,
+                       nkb, k_i8, k_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool(const uint16_t* q, const uint16_t* k, int64_t BH, int N, float* qbar,
+                       float* kbarT, int ldk, hipStream_t st) {
+    const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
+    hipLaunchKernelGGL((colsum_kernel<QBLK, 1>), dim3((nqb + 7) / 8, BH), dim3(128), 0, st, q, N, nqb,
+                       0, qbar);
+    hipLaunchKernelGGL((colsum_kernel<KBLK, 2>), dim3((nkb + 15) / 16, BH), dim3(256), 0, st, k, N,
+                       nkb, ldk, kbarT);
+    return hipGetLastError();
+}
+
+}  // namespace ssa

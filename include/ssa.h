@@ -1,0 +1,164 @@
+/*
+ * ssa.h -- C ABI of the SageSLA attention library for AMD MI355X (gfx950).
+ *
+ * The method: TurboDiffusion pages, page 5, "Four Technical Pillars".
+ *   Pillar One (SageAttention): attention computed in 8-bit integers, with a
+ *   smoothing step that tames outliers.
+ *   Pillar Two (SLA): only the most important block interactions are computed
+ *   exactly (about 10% of them), a light global linear-attention term covers
+ *   the rest; the two stack as "SageSLA".
+ *   "Hands-On Tutorial": --attention_type sagesla selects it, --sla_topk is the
+ *   fraction of connections kept (0.1 -> 90% sparsity).
+ * The concrete numerics (block sizes, scale formula, rounding, block scoring,
+ * feature map) are not printed on the pages; the readings used are stated at
+ * each entry point below.
+ *
+ * Conventions shared by every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major [B,H,N,D]
+ *     arrays (D fastest), 16-byte aligned; fp32/int32 arrays are 4-byte
+ *     aligned. D must be 128. 1 <= N <= SSA_MAX_N, B,H >= 1.
+ *   - Query blocks are 128 tokens (Nqb = ceil(N/128)), key blocks 64 tokens
+ *     (Nkb = ceil(N/64)); the last block of each may be partial.
+ *   - Ownership: the caller owns every buffer, including the workspace whose
+ *     size ssa_workspace_bytes() reports. The library never allocates device
+ *     memory, keeps no per-call state and never synchronizes: every call only
+ *     enqueues work on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Errors: argument problems are reported synchronously with nothing
+ *     enqueued (SSA_ERR_INVALID / SSA_ERR_UNSUPPORTED / SSA_ERR_WORKSPACE). A
+ *     failed HIP launch returns SSA_ERR_HIP. Device faults surface at the
+ *     caller's next synchronization. ssa_last_error() gives a message for the
+ *     last failing call on the calling thread. Nothing is printed.
+ *   - Outputs must not overlap inputs (checked).
+ */
+#ifndef SSA_H
+#define SSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssa_status {
+    SSA_OK = 0,
+    SSA_ERR_INVALID = 1,     /* null / misaligned pointer, bad size, aliasing */
+    SSA_ERR_UNSUPPORTED = 2, /* D != 128, N too large, device is not gfx950 */
+    SSA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+    SSA_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} ssa_status;
+
+typedef struct ssa_shape {
+    int64_t B, H, N, D;
+} ssa_shape;
+
+enum { SSA_OP_QUANT = 0, SSA_OP_MASK = 1, SSA_OP_ATTN = 2 };
+enum { SSA_BRANCH_SPARSE = 1, SSA_BRANCH_LINEAR = 2 };
+
+#define SSA_HEAD_DIM 128
+#define SSA_QBLK 128
+#define SSA_KBLK 64
+#define SSA_MAX_N (1 << 19)
+
+int64_t ssa_num_q_blocks(int64_t N); /* ceil(N/128) */
+int64_t ssa_num_k_blocks(int64_t N); /* ceil(N/64) */
+
+/* Key blocks kept per query block for a kept fraction `topk` (the meaning of
+ * --sla_topk, page 5 "Hands-On Tutorial"): clamp(floor(topk*Nkb + 0.5), 1, Nkb). */
+int64_t ssa_keep_blocks(int64_t N, double topk);
+
+/* Bytes of device workspace the entry point `op` needs for shape s (keep and
+ * branches only matter for SSA_OP_ATTN; pass keep = Nkb for dense). Returns 0
+ * for an invalid shape. */
+size_t ssa_workspace_bytes(int op, ssa_shape s, int64_t keep, int branches);
+
+const char* ssa_status_str(ssa_status st);
+const char* ssa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * sage_quant_qk -- K smoothing and per-block INT8 quantization.
+ * Page 5, Pillar One (INT8 attention, "smoothing" for outliers).
+ * Readings: mu[b,h,d] = mean over all N tokens of K[b,h,:,d], summed in fp32
+ * per 64-token block in token order, then over blocks in block order, divided
+ * by N (IEEE fp32). K' = fp32(K) - mu. Q in 128-token blocks of raw Q, K' in
+ * 64-token blocks; one fp32 scale per (b,h,block) = max|x| / 127 over the
+ * block's valid tokens and all channels; q = clamp(rint(x/scale), -127, 127)
+ * with the division in IEEE fp32 and ties to even; an all-zero block gets
+ * scale 0 and q = 0.
+ *   q, k     in : bf16 [B,H,N,D]
+ *   q_i8     out: int8 [B,H,N,D]      q_scale out: fp32 [B,H,Nqb]
+ *   k_i8     out: int8 [B,H,N,D]      k_scale out: fp32 [B,H,Nkb]
+ *   k_mean   out: fp32 [B,H,D]
+ *   ws: ssa_workspace_bytes(SSA_OP_QUANT, s, 0, 0) bytes, 256-byte aligned.
+ */
+ssa_status sage_quant_qk(const uint16_t* q, const uint16_t* k, ssa_shape s, int8_t* q_i8,
+                         float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sla_block_mask -- the SLA critical-block selection.
+ * Page 5, Pillar Two (only the most important interactions are computed) and
+ * "Hands-On Tutorial" (--sla_topk = fraction kept).
+ * Readings: qbar_i = fp32 mean of raw bf16 Q over the valid tokens of query
+ * block i (sequential sum in token order, IEEE division by the valid count);
+ * kbar_j likewise for raw K; score_ij = fmaf chain over d = 0..127 from 0;
+ * each query block keeps its `keep` best key blocks under (score descending,
+ * j ascending), -0.0 equal to +0.0.
+ *   kidx out: int32 [B,H,Nqb,keep], kept key blocks in ascending order
+ *   mask out: uint8 [B,H,Nqb,Nkb] (1 = kept) or NULL
+ *   ws: ssa_workspace_bytes(SSA_OP_MASK, s, keep, 0) bytes.
+ */
+ssa_status sla_block_mask(const uint16_t* q, const uint16_t* k, ssa_shape s, int64_t keep,
+                          int32_t* kidx, uint8_t* mask, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sage_sla_attn_fwd -- SageSLA forward: sparse INT8 softmax attention over the
+ * kept blocks plus the elu+1 linear branch over the other blocks.
+ * Page 5, Pillars One and Two, "SageSLA".
+ * Sparse branch (branches & SSA_BRANCH_SPARSE): for each query token, over the
+ * valid keys u of its kept blocks, S_u = int32 q_i8 . k_i8 (exact);
+ * K32 = fl32(sm * log2 e); c = fl32(fl32(q_scale * k_scale) * K32);
+ * m = ceil(max_u fl32(S_u * c)) (an integer normalizer); p_u = bf16 of
+ * 2^(S_u*c - m); o_s = sum p_u v_u / sum p_u with fp32 accumulation (P in
+ * bf16 against bf16 V on the matrix cores).
+ * Linear branch (branches & SSA_BRANCH_LINEAR): phi(x) = x + 1 (x > 0) or e^x,
+ * on raw bf16 Q and K; for query block i, H_i = sum over key blocks j NOT kept
+ * of sum_{u in j} phi(k_u) v_u^T and z_i = sum phi(k_u) likewise;
+ * o_l = phi(q)^T H_i / phi(q)^T z_i, or 0 when every block is kept.
+ * Output: out = o_s + o_l (either term dropped when its branch is off).
+ *   q, k, v      in : bf16 [B,H,N,D] (q, k only read by the linear branch)
+ *   q_i8..k_scale in : as produced by sage_quant_qk
+ *   kidx         in : int32 [B,H,Nqb,keep] ascending, as produced by
+ *                     sla_block_mask; NULL = dense (keep must equal Nkb).
+ *                     Entries are clamped into [0, Nkb) on the device, so a
+ *                     malformed kidx yields wrong values, never a stray access.
+ *   sm_scale     in : softmax scale; <= 0 selects 1/sqrt(D) rounded to fp32
+ *   out          out: bf16 [B,H,N,D] (round to nearest even of the fp32 result)
+ *   out_f32      out: fp32 [B,H,N,D] copy of the result before rounding, or NULL
+ *   ws: ssa_workspace_bytes(SSA_OP_ATTN, s, keep, branches) bytes.
+ */
+ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             ssa_shape s, const int8_t* q_i8, const float* q_scale,
+                             const int8_t* k_i8, const float* k_scale, const int32_t* kidx,
+                             int64_t keep, int branches, float sm_scale, uint16_t* out,
+                             float* out_f32, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sage_qk_int32_tiles -- test export of raw int32 score tiles computed by the
+ * same device routine the attention kernel uses (INT8 matrix-core product
+ * with int32 accumulation, page 5 Pillar One).
+ *   tiles in : int32 [T,3] device array of (b*H + h, query block i, key block j)
+ *   out   out: int32 [T,128,64]; out[t][r][c] = sum_d q_i8[128i+r][d]*k_i8[64j+c][d],
+ *              0 where the row or column is past N.
+ * Tile indices are validated on the device: an out-of-range triple yields an
+ * all-zero tile.
+ */
+ssa_status sage_qk_int32_tiles(const int8_t* q_i8, const int8_t* k_i8, ssa_shape s,
+                               const int32_t* tiles, int64_t T, int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

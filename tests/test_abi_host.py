@@ -1,0 +1,154 @@
+"""Host-side checks of the C-ABI library: it loads without a GPU, exports every
+function include/ssa.h declares, and rejects bad arguments before any HIP call
+(so these run on a CPU-only machine)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import bit_sparse_attention_amd as ssa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssa.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\**\s+\**([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("sage_quant_qk", "sla_block_mask", "sage_sla_attn_fwd", "sage_qk_int32_tiles",
+              "ssa_workspace_bytes", "ssa_keep_blocks", "ssa_status_str", "ssa_last_error",
+              "ssa_num_q_blocks", "ssa_num_k_blocks"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.CDLL(ssa.lib_path())
+    for n in _declared_functions():
+        assert hasattr(L, n), f"libssa.so does not export {n}"
+
+
+def test_block_counts_and_keep():
+    assert ssa.num_q_blocks(75600) == 591 and ssa.num_k_blocks(75600) == 1182
+    assert ssa.keep_blocks(75600, 0.1) == 118
+    assert ssa.keep_blocks(32760, 0.1) == 51
+    assert ssa.keep_blocks(269280, 0.05) == 210
+    assert ssa.keep_blocks(1024, 0.0) == 1 and ssa.keep_blocks(1024, 5.0) == 16
+    assert ssa.keep_blocks(0, 0.1) == 0
+
+
+def test_keep_matches_oracle(orc):
+    for N in (1, 63, 64, 65, 1000, 32760, 75600, 269280):
+        for topk in (0.0, 0.05, 0.1, 0.15, 0.5, 1.0):
+            assert ssa.keep_blocks(N, topk) == orc.keep_blocks(N, topk)
+
+
+def test_workspace_sizes():
+    s = (1, 40, 75600, 128)
+    assert ssa.workspace_bytes(ssa.OP_QUANT, s) >= 40 * 1182 * 128 * 4
+    dense = ssa.workspace_bytes(ssa.OP_ATTN, s, 1182, ssa.SPARSE | ssa.LINEAR)
+    sparse = ssa.workspace_bytes(ssa.OP_ATTN, s, 118, ssa.SPARSE)
+    lin = ssa.workspace_bytes(ssa.OP_ATTN, s, 118, ssa.SPARSE | ssa.LINEAR)
+    assert dense == sparse < lin  # all blocks kept: no linear states needed
+    assert ssa.workspace_bytes(ssa.OP_ATTN, (1, 1, 100, 64), 1, 1) == 0  # D != 128
+    assert ssa.workspace_bytes(7, s) == 0
+
+
+def _L():
+    return ssa._load()
+
+
+def _shape(B=1, H=1, N=1000, D=128):
+    return ssa.Shape(B, H, N, D)
+
+
+# Fake, never dereferenced device addresses: validation must reject each call
+# before it touches the GPU.
+A = 1 << 40
+
+
+def _p(off=0):
+    return C.c_void_p(A + off)
+
+
+def test_quant_rejects_bad_arguments():
+    L = _L()
+    GB = 1 << 30
+    ok = [_p(0), _p(GB), _shape(), _p(2 * GB), _p(3 * GB), _p(4 * GB), _p(5 * GB), _p(6 * GB),
+          _p(7 * GB), 1 << 24, None]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["q", "k", "s", "q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "ws", "n", "st"]
+        for k_, v_ in kw.items():
+            args[names.index(k_)] = v_
+        return L.sage_quant_qk(*args)
+
+    assert call(q=None) == 1
+    assert call(q=_p(8)) == 1  # misaligned
+    assert call(s=_shape(D=64)) == 2
+    assert call(s=_shape(N=0)) == 1
+    assert call(s=_shape(N=(1 << 19) + 1)) == 2
+    assert call(ws=None) == 3
+    assert call(n=16) == 3
+    assert call(ws=_p(7 * GB + 16)) == 3  # workspace misaligned
+    assert call(q_i8=_p(0)) == 1  # output aliases input q
+    assert call(k_mean=_p(2 * GB + 64)) == 1  # two outputs overlap
+    assert b"overlap" in L.ssa_last_error()
+
+
+def test_mask_rejects_bad_keep():
+    L = _L()
+    GB = 1 << 30
+    s = _shape(N=1000)  # 16 key blocks
+    for keep, want in ((0, 1), (17, 1), (16, 3)):
+        st = L.sla_block_mask(_p(0), _p(GB), s, keep, _p(2 * GB), None, None, 0, None)
+        assert st == want, (keep, st)
+
+
+def test_attn_rejects_bad_arguments():
+    L = _L()
+    GB = 1 << 30
+    s = _shape(N=1000)
+
+    def call(kidx=_p(6 * GB), keep=4, branches=3, sm=0.0, out=_p(7 * GB), ws=None, n=0):
+        return L.sage_sla_attn_fwd(_p(0), _p(GB), _p(2 * GB), s, _p(3 * GB), _p(4 * GB),
+                                   _p(5 * GB), _p(5 * GB + (1 << 20)), kidx, keep, branches,
+                                   sm, out, None, ws, n, None)
+
+    assert call(branches=0) == 1
+    assert call(branches=4) == 1
+    assert call(keep=0) == 1
+    assert call(kidx=None, keep=4) == 1  # dense needs keep == Nkb
+    assert call(sm=float("nan")) == 1
+    assert call(out=_p(2 * GB)) == 1  # out aliases v
+    assert call() == 3  # workspace missing
+    assert b"workspace" in L.ssa_last_error()
+
+
+def test_tiles_reject_bad_count():
+    L = _L()
+    GB = 1 << 30
+    assert L.sage_qk_int32_tiles(_p(0), _p(GB), _shape(), _p(2 * GB), 0, _p(3 * GB), None) == 1
+
+
+def test_status_strings():
+    L = _L()
+    for st in range(5):
+        assert L.ssa_status_str(st)
+    assert L.ssa_status_str(99) == b"unknown status"
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        ssa.sage_quant_qk(q, q)
