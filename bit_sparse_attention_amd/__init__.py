@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "sage_quant_qk", "sla_block_mask", "sage_sla_attn_fwd", "sage_qk_int32_tiles", "sagesla",
-    "SageSLAPlan", "keep_blocks", "num_q_blocks", "num_k_blocks", "workspace_bytes", "lib_path",
+    "SageSLAPlan", "KernelTimer", "keep_blocks", "num_q_blocks", "num_k_blocks", "workspace_bytes", "lib_path",
     "SPARSE", "LINEAR", "OP_QUANT", "OP_MASK", "OP_ATTN",
 ]
 
@@ -74,6 +74,9 @@ def _load():
         "sage_sla_attn_fwd": (i32, [_p, _p, _p, Shape, _p, _p, _p, _p, _p, i64, i32, C.c_float,
                                     _p, _p, _p, sz, _p]),
         "sage_qk_int32_tiles": (i32, [_p, _p, Shape, _p, i64, _p, _p]),
+        "ssa_kernel_timer_start": (i32, [i32]),
+        "ssa_kernel_timer_read": (i32, [C.POINTER(C.c_float), i32]),
+        "ssa_kernel_timer_stop": (None, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -235,6 +238,27 @@ def sagesla(q, k, v, topk: float | None = 0.1, linear: bool = True, sm_scale: fl
     br = SPARSE | (LINEAR if linear else 0)
     return sage_sla_attn_fwd(q, k, v, q_i8, q_scale, k_i8, k_scale, kidx, keep, br, sm_scale,
                              return_f32)
+
+
+class KernelTimer:
+    """HIP-event durations of the sparse-attention kernel launches made while
+    the timer is active (see ssa_kernel_timer_start in include/ssa.h)."""
+
+    def __init__(self, max_launches: int):
+        self.n = int(max_launches)
+
+    def __enter__(self):
+        _check("ssa_kernel_timer_start", _load().ssa_kernel_timer_start(self.n))
+        return self
+
+    def read(self):
+        buf = (C.c_float * self.n)()
+        got = _load().ssa_kernel_timer_read(buf, self.n)
+        return [float(buf[x]) for x in range(got)]
+
+    def __exit__(self, *exc):
+        _load().ssa_kernel_timer_stop()
+        return False
 
 
 class SageSLAPlan:

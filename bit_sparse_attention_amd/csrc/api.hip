@@ -5,6 +5,8 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -156,6 +158,26 @@ ssa_status check_ws(void* ws, size_t have, size_t need) {
     if (!aligned(ws, 256)) return fail(SSA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
     if (have < need) return fail(SSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
     return SSA_OK;
+}
+
+// kernel timer (benchmark hook): event pairs around the sparse-attention launch
+std::mutex g_tm;
+std::vector<hipEvent_t> g_ev0, g_ev1;
+int g_tcount = 0;
+
+void timer_destroy_locked() {
+    for (auto e : g_ev0) (void)hipEventDestroy(e);
+    for (auto e : g_ev1) (void)hipEventDestroy(e);
+    g_ev0.clear();
+    g_ev1.clear();
+    g_tcount = 0;
+}
+
+// index of the event pair for the next launch, or -1 when the timer is off/full
+int timer_slot() {
+    std::lock_guard<std::mutex> lk(g_tm);
+    if (g_tcount >= (int)g_ev0.size()) return -1;
+    return g_tcount++;
 }
 
 #define TRY(x)                          \
@@ -356,7 +378,10 @@ ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
     a.hnon = hnon;
     a.out = out;
     a.out32 = out_f32;
+    const int slot = timer_slot();
+    if (slot >= 0) (void)hipEventRecord(g_ev0[slot], st);
     e = launch_attn(a, st);
+    if (slot >= 0) (void)hipEventRecord(g_ev1[slot], st);
     if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_fwd launch");
     return SSA_OK;
 }
@@ -379,6 +404,42 @@ ssa_status sage_qk_int32_tiles(const int8_t* q_i8, const int8_t* k_i8, ssa_shape
     hipError_t e = launch_qk_tiles(q_i8, k_i8, d.BH, (int)d.N, tiles, T, out, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sage_qk_int32_tiles launch");
     return SSA_OK;
+}
+
+ssa_status ssa_kernel_timer_start(int max_launches) {
+    g_err[0] = 0;
+    if (max_launches < 1 || max_launches > (1 << 16))
+        return fail(SSA_ERR_INVALID, "max_launches=%d outside [1, 65536]", max_launches);
+    std::lock_guard<std::mutex> lk(g_tm);
+    timer_destroy_locked();
+    for (int x = 0; x < max_launches; ++x) {
+        hipEvent_t a, b;
+        hipError_t e = hipEventCreate(&a);
+        if (e == hipSuccess) e = hipEventCreate(&b);
+        if (e != hipSuccess) {
+            timer_destroy_locked();
+            return hip_fail(e, "hipEventCreate");
+        }
+        g_ev0.push_back(a);
+        g_ev1.push_back(b);
+    }
+    return SSA_OK;
+}
+
+int ssa_kernel_timer_read(float* ms, int cap) {
+    std::lock_guard<std::mutex> lk(g_tm);
+    const int n = g_tcount < cap ? g_tcount : cap;
+    for (int x = 0; x < n; ++x) {
+        if (hipEventSynchronize(g_ev1[x]) != hipSuccess ||
+            hipEventElapsedTime(&ms[x], g_ev0[x], g_ev1[x]) != hipSuccess)
+            ms[x] = -1.f;
+    }
+    return n;
+}
+
+void ssa_kernel_timer_stop(void) {
+    std::lock_guard<std::mutex> lk(g_tm);
+    timer_destroy_locked();
 }
 
 }  // extern "C"

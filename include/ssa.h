@@ -158,6 +158,20 @@ ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
 ssa_status sage_qk_int32_tiles(const int8_t* q_i8, const int8_t* k_i8, ssa_shape s,
                                const int32_t* tiles, int64_t T, int32_t* out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Kernel timer (for benchmarks). After ssa_kernel_timer_start(n), each of the
+ * next n sage_sla_attn_fwd calls records a pair of HIP events on its stream
+ * immediately around its sparse-attention kernel launch (after the linear
+ * states / V re-layout launches). ssa_kernel_timer_read waits for the recorded
+ * events and writes up to `cap` per-launch durations in milliseconds (-1 for a
+ * failed read), returning how many it wrote. ssa_kernel_timer_stop releases
+ * the events. The events are host-side runtime objects; no device memory is
+ * allocated. The timer is process-wide and guarded by a mutex.
+ */
+ssa_status ssa_kernel_timer_start(int max_launches);
+int ssa_kernel_timer_read(float* ms, int cap);
+void ssa_kernel_timer_stop(void);
+
 #ifdef __cplusplus
 }
 #endif
