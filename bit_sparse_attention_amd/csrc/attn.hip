@@ -5,17 +5,27 @@
 // (only the kept block interactions are computed exactly; a linear-attention
 // term covers the rest), stacked as SageSLA.
 //
-// One workgroup = one 128-token query block of one head, 4 waves x 32 query
-// rows. For each kept 64-token key block (ascending):
+// One workgroup = one 128-token query block of one head: 2 waves, each with
+// 64 query rows as two 32-row groups that share every K and V fragment read
+// from LDS. For each kept 64-token key block j (ascending):
 //   S^T = K_j . Q^T        v_mfma_i32_32x32x32_i8, exact int32
 //   x = S * c_ij           c_ij = fl32(fl32(sq*sk) * fl32(sm*log2 e))
-//   m = running integer max of ceil(x); rescale by exact powers of two
-//   p = bf16(2^(S*c - m)), l += p
+//   m = integer normalizer (raised only when a tile's max exceeds it by more
+//       than HEADROOM); rescaling by 2^k is exact, so p = bf16(2^(S*c - m))
+//       and the final output do not depend on the tile order
+//   p = bf16(2^(S*c - m)), l += p (v_dot2 on packed pairs)
 //   O^T += V_j^T . P^T     v_mfma_f32_32x32x16_bf16, fp32 accumulation
-// Computing S^T (keys as MFMA rows) puts one query per lane column, so the
-// row max and row sum stay inside a lane pair, and the int32 accumulator
-// order is exactly the bf16 B-operand order of the PV product: P never
-// leaves registers. V arrives pre-transposed in that key order (linear.hip).
+// S^T puts one query per lane column: row max and row sum stay in a lane
+// pair, and the int32 accumulator order is the bf16 B-operand order of the
+// PV product, so P never leaves registers. V arrives pre-transposed in that
+// key order (linear.hip).
+//
+// Software pipeline (per iteration j): global loads of K(j+2) and V(j+1) are
+// issued first and land in LDS at the end of the iteration; QK(j+1) and
+// PV(j) go to the matrix cores, and the softmax of tile j+1 runs on the VALU
+// underneath PV(j). One wave per SIMD (up to 512 registers) carries the
+// 64-row accumulators, two score tiles and the prefetch registers.
+//
 // The linear branch is applied in the epilogue from the complement states
 // (phi(Q) . H_i / phi(Q) . z_i, split-bf16 MFMA) and added to the output.
 #include "common.hpp"
@@ -23,26 +33,111 @@
 
 namespace ssa {
 
-constexpr int KP = 144;  // LDS row pitch in bytes of the K (int8) and V^T (bf16) tiles
+// Query groups (32 rows each) per wave: 1 -> 4 waves per query block, two
+// waves per SIMD; 2 -> 2 waves of 64 rows sharing every LDS fragment.
+#ifndef SSA_ATTN_GROUPS
+#define SSA_ATTN_GROUPS 1
+#endif
+constexpr int G = SSA_ATTN_GROUPS;
+constexpr int WAVES = 4 / G;
+constexpr int ATTN_THREADS = 64 * WAVES;
+constexpr int NSTAGE = 3;            // LDS buffers per operand
+constexpr int KTILE = KBLK * HD;     // bytes of an int8 K tile
+constexpr int VTILE = HD * KBLK * 2; // bytes of a bf16 V^T tile
 
-// K tile of key block j -> LDS rows [64][KP], int8, zero past N.
-__device__ __forceinline__ void load_k_regs(const int8_t* __restrict__ k_i8, int64_t bh, int N,
-                                            int j, int tid, i32x4 (&kr)[2]) {
+// Headroom of the integer normalizer: m is raised only when a tile's max
+// exceeds it by more than this (log2 units). Any integer m gives the same
+// result (rescaling by 2^k is exact and rounding commutes with it), so this
+// only bounds p <= 2^HEADROOM (far from the fp32 / bf16 range limit of
+// 2^127 even after summing 2^20 keys) and keeps rescales rare.
+constexpr float HEADROOM = 64.0f;
+
+// ---- tile staging: global -> LDS DMA, 128 threads ---------------------------
+// Both tiles are 128-byte rows (K: 64 rows of int8 channels; V^T: 128 rows of
+// 64 bf16 keys) stored with the 16-byte chunk c of row r at slot
+// c ^ swz(r): reads of 8 or 16 consecutive rows at one chunk then hit
+// distinct banks. global_load_lds_dwordx4 writes lane l's 16 bytes at
+// M0 + 16*l, so each lane fetches the chunk its slot must hold. The DMA is
+// issued from inline asm: the compiler then neither tracks it nor inserts
+// vmcnt waits before LDS reads; the pipeline waits explicitly (wait_vm).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+    // the tile base is wave-uniform: move it to SGPRs for the saddr form
+    const uint64_t b = (uint64_t)base;
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const void* sbase = (const void*)sb;
+    // No "memory" clobber: a DMA only writes an LDS buffer that no wave reads
+    // in the same iteration (ordering across iterations comes from the
+    // barrier), and a clobber would turn the read-only kidx / k_scale loads
+    // into vector loads whose vmcnt(0) waits would drain the pipeline.
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1\n\ts_nop 0" ::"v"(voff),
+                 "s"(sbase), "s"(lds_addr));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    // s_waitcnt vmcnt(N), expcnt and lgkmcnt left unconstrained (gfx9 encoding)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Two wave-uniform 32-bit loads through the scalar cache, completed inside
+// the asm block. They stay off the vector-memory counter, so fetching the
+// next kept-block index and scale never waits for the tile DMAs in flight.
+__device__ __forceinline__ void sload2(const void* p1, const void* p2, int& v1, int& v2) {
+    const uint64_t a = (uint64_t)p1, b = (uint64_t)p2;
+    const uint64_t sa = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile(
+        "s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+        : "=s"(v1), "=s"(v2)
+        : "s"((const void*)sa), "s"((const void*)sb));
+}
+
+// Per-lane byte offset inside a tile: DMA p of wave w fills rows
+// r0 = rows_per_wave*w + 8p .. +7; lane l fetches the chunk its slot holds.
+__device__ __forceinline__ uint32_t tile_voff(int rows_per_wave, int wave, int p, int lane) {
+    const int row = rows_per_wave * wave + 8 * p + (lane >> 3);
+    return row * 128 + 16 * ((lane & 7) ^ swz(row));
+}
+
+// K tile of key block j into LDS at lds_base (8/WAVES DMAs per wave). koff
+// holds the loop-invariant lane offsets. In the ragged last block, rows past
+// N are fetched from row N-1 (those keys are masked out of every use).
+__device__ __forceinline__ void dma_k_tile(const int8_t* __restrict__ k_i8, int64_t bh, int N, int j,
+                                           uint32_t lds_base, int wave, int lane,
+                                           const uint32_t (&koff)[8 / WAVES]) {
+    const int8_t* base = k_i8 + (bh * N + (int64_t)j * KBLK) * HD;
+    const bool ragged = (j + 1) * KBLK > N;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int row = (tid >> 3) + 32 * p;
-        const int tok = j * KBLK + row;
-        kr[p] = tok < N ? *(const i32x4*)(k_i8 + (bh * N + tok) * HD + 16 * (tid & 7)) : i32x4{};
+    for (int p = 0; p < 8 / WAVES; ++p) {
+        uint32_t off = koff[p];
+        if (ragged) {
+            const int row = (64 / WAVES) * wave + 8 * p + (lane >> 3);
+            const int rr = min(row, N - 1 - j * KBLK);
+            off = rr * 128 + 16 * ((lane & 7) ^ swz(row));
+        }
+        dma16(base, off, __builtin_amdgcn_readfirstlane(lds_base + ((64 / WAVES) * wave + 8 * p) * 128));
     }
 }
 
-__device__ __forceinline__ void store_k_lds(uint8_t* ks, int tid, const i32x4 (&kr)[2]) {
+// V^T tile (128 rows of 64 keys, zero past N) into LDS (16/WAVES DMAs per wave).
+__device__ __forceinline__ void dma_v_tile(const uint16_t* __restrict__ vtile, uint32_t lds_base,
+                                           int wave, const uint32_t (&voff)[16 / WAVES]) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) *(i32x4*)(ks + ((tid >> 3) + 32 * p) * KP + 16 * (tid & 7)) = kr[p];
+    for (int p = 0; p < 16 / WAVES; ++p)
+        dma16(vtile, voff[p], __builtin_amdgcn_readfirstlane(lds_base + ((128 / WAVES) * wave + 8 * p) * 128));
 }
 
-// Q operand of one wave: lane supplies query (lane & 31), channels
-// 32c + 16*(lane>>5) .. +15 for c = 0..3.
+// Q operand of one 32-row group: lane supplies query (lane & 31), channels
+// 32c + 16*(lane>>5) .. +15 for c = 0..3 (zero past N).
 __device__ __forceinline__ void load_q_operand(const int8_t* __restrict__ q_i8, int64_t bh, int N,
                                                int t, int hi, i32x4 (&qop)[4]) {
     const bool ok = t < N;
@@ -51,218 +146,327 @@ __device__ __forceinline__ void load_q_operand(const int8_t* __restrict__ q_i8, 
     for (int c = 0; c < 4; ++c) qop[c] = ok ? *(const i32x4*)(qp + 32 * c + 16 * hi) : i32x4{};
 }
 
-// The shared QK^T routine: S^T for keys 0..31 (s0) and 32..63 (s1) of the LDS
-// K tile against the wave's 32 queries. Lane (l32, hi), register r of s0 holds
-// key 8*(r/4) + 4*hi + r%4 for query l32 (32 + that for s1).
-__device__ __forceinline__ void qk_tile_mfma(const uint8_t* ks, const i32x4 (&qop)[4], int l32,
-                                             int hi, i32x16& s0, i32x16& s1) {
-    s0 = i32x16{};
-    s1 = i32x16{};
+// The shared QK^T routine: S^T of the LDS K tile against the wave's two
+// 32-query groups. Lane (l32, hi), register r of s[g][0] holds key
+// 8*(r/4) + 4*hi + r%4 for query l32 of group g (s[g][1]: that key + 32).
+__device__ __forceinline__ void qk_tile_mfma(const uint8_t* ks, const i32x4 (&qop)[G][4], int l32,
+                                             int hi, i32x16 (&s)[G][2]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g][0] = s[g][1] = i32x16{};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const i32x4 a0 = *(const i32x4*)(ks + l32 * KP + 32 * c + 16 * hi);
-        const i32x4 a1 = *(const i32x4*)(ks + (32 + l32) * KP + 32 * c + 16 * hi);
-        s0 = mfma_i8_32x32x32(a0, qop[c], s0);
-        s1 = mfma_i8_32x32x32(a1, qop[c], s1);
+        const int slot = ((2 * c + hi) ^ swz(l32)) * 16;
+        const i32x4 a0 = *(const i32x4*)(ks + l32 * 128 + slot);
+        const i32x4 a1 = *(const i32x4*)(ks + (32 + l32) * 128 + slot);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            s[g][0] = mfma_i8_32x32x32(a0, qop[g][c], s[g][0]);
+            s[g][1] = mfma_i8_32x32x32(a1, qop[g][c], s[g][1]);
+        }
     }
 }
 
+// Row max of one group's S^T tile (the lane pair holds a query's 64 keys).
+// In the ragged last key block the rows past N hold copies of row N-1, a key
+// of the same block, so the max over all 64 columns is the max over the valid
+// ones.
+__device__ __forceinline__ int tile_rowmax(const i32x16& s0, const i32x16& s1) {
+    int smax = max(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) smax = max(smax, max(s0[r], s1[r]));
+    return max(smax, __shfl_xor(smax, 32, 64));
+}
+
+// p = bf16(2^(S*c - m)) for one group's tile, packed as the PV B operand
+// (chunk cc holds keys 16cc + 8*(s/4) + 4*hi + s%4); returns the sum of the
+// rounded p.
+__device__ __forceinline__ float tile_p(const i32x16& s0, const i32x16& s1, float c, float nm,
+                                        bf16x8 (&pb)[4]) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float acc = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+        for (int s = 0; s < 8; s += 2) {
+            const int r = 8 * (cc & 1) + s;
+            const int sa = (cc < 2) ? s0[r] : s1[r];
+            const int sb = (cc < 2) ? s0[r + 1] : s1[r + 1];
+            const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sa, c, nm));
+            const float pz = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sb, c, nm));
+            const bf16x2 pr = __builtin_convertvector(f32x2{pa, pz}, bf16x2);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+            pb[cc][s] = pr[0];
+            pb[cc][s + 1] = pr[1];
+        }
+    }
+    return acc;
+}
+
+// Ragged last key block: zero p of the keys >= kval and return the new sum.
+__device__ __forceinline__ float mask_p(int kval, int hi, bf16x8 (&pb)[4]) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float acc = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+        for (int s = 0; s < 8; s += 2) {
+            const int key = 16 * cc + 8 * (s >> 2) + 4 * hi + (s & 3);
+            if (key >= kval) pb[cc][s] = (__bf16)0.0f;
+            if (key + 1 >= kval) pb[cc][s + 1] = (__bf16)0.0f;
+            const bf16x2 pr = {pb[cc][s], pb[cc][s + 1]};
+            acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+        }
+    }
+    return acc;
+}
+
+// Softmax of a fresh S tile for every group. The fast part computes P with
+// the current normalizer; when some query's tile max exceeds it by more than
+// HEADROOM (always on the first tile, rarely after), O and l are rescaled by
+// exact powers of two and P is recomputed. kval < 64 marks the ragged last
+// key block.
+__device__ __forceinline__ void tile_softmax(const i32x16 (&s)[G][2], float c, int kval, int hi,
+                                             float (&m_run)[G], float (&l_run)[G],
+                                             f32x16 (&o)[G][4], bf16x8 (&pb)[G][4]) {
+    float mt[G], lsum[G];
+    bool need[G], any = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        lsum[g] = tile_p(s[g][0], s[g][1], c, -m_run[g], pb[g]);
+        mt[g] = ceilf((float)tile_rowmax(s[g][0], s[g][1]) * c);  // c > 0, rounding monotone
+        need[g] = mt[g] > m_run[g] + HEADROOM;
+        any = any || need[g];
+        // keep the common-case P above the rare branch below, in the same
+        // block as the PV products it overlaps with
+        asm volatile("" ::"v"(pb[g][0]), "v"(pb[g][1]), "v"(pb[g][2]), "v"(pb[g][3]), "v"(lsum[g]));
+    }
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float alpha =
+                need[g] ? ((m_run[g] == -INFINITY)
+                               ? 0.f
+                               : __builtin_amdgcn_ldexpf(1.0f, (int)(m_run[g] - mt[g])))
+                        : 1.0f;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[g][dt] *= alpha;
+            l_run[g] *= alpha;
+            m_run[g] = need[g] ? mt[g] : m_run[g];
+            lsum[g] = tile_p(s[g][0], s[g][1], c, -m_run[g], pb[g]);
+        }
+    }
+    if (kval < KBLK) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) lsum[g] = mask_p(kval, hi, pb[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) l_run[g] += lsum[g];
+}
+
+// O^T += V^T . P^T for both groups; each V fragment feeds two MFMAs.
+__device__ __forceinline__ void tile_pv(const uint8_t* vs, const bf16x8 (&pb)[G][4], int l32,
+                                        int hi, f32x16 (&o)[G][4]) {
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const bf16x8 va =
+                *(const bf16x8*)(vs + (32 * dt + l32) * 128 + ((2 * cc + hi) ^ swz(l32)) * 16);
+#pragma unroll
+            for (int g = 0; g < G; ++g) o[g][dt] = mfma_bf16_32x32x16(va, pb[g][cc], o[g][dt]);
+        }
+}
+
 template <bool LIN>
-__global__ __launch_bounds__(256, 2) void sagesla_attn_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t ks[2][KBLK * KP];
-    __shared__ __attribute__((aligned(16))) uint8_t vs[2][HD * KP];
+__global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ks[NSTAGE][KTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t vs[NSTAGE][VTILE];
     const int64_t total = a.BH * a.nqb;
-    const int64_t item = xcd_item(blockIdx.x, total);
+    const int64_t item = blockIdx.x;
     if (item >= total) return;
     const int64_t bh = item / a.nqb;
     const int i = (int)(item % a.nqb);
     const int N = a.N, nkb = a.nkb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
               hi = lane >> 5;
-    const int t = i * QBLK + wave * 32 + l32;  // this lane's query token
-
-    f32x16 o[4];
+    int tq[G];  // this lane's query token in each group
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int g = 0; g < G; ++g) tq[g] = i * QBLK + 32 * G * wave + 32 * g + l32;
+
+    f32x16 o[G][4];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[g][dt] = f32x16{};
+    float m_run[G], l_run[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) m_run[g] = -INFINITY, l_run[g] = 0.f;
 
     if (a.do_sparse) {
-        i32x4 qop[4];
-        load_q_operand(a.q_i8, bh, N, t, hi, qop);
         const float sq = a.q_scale[bh * a.nqb + i];
+        const float* ksc = a.k_scale + bh * nkb;
         const int nsel = a.kidx ? a.keep : nkb;
         const int32_t* krow = a.kidx ? a.kidx + (bh * a.nqb + i) * (int64_t)a.keep : nullptr;
         const uint16_t* vtb = a.vt + bh * (int64_t)nkb * HD * KBLK;
-
-        i32x4 kr[2], vr[4];
-        auto gload = [&](int j) {
-            load_k_regs(a.k_i8, bh, N, j, tid, kr);
-            const uint16_t* vp = vtb + (int64_t)j * HD * KBLK;
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                vr[p] = *(const i32x4*)(vp + ((tid >> 3) + 32 * p) * KBLK + 8 * (tid & 7));
-        };
-        auto lstore = [&](int buf) {
-            store_k_lds(ks[buf], tid, kr);
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                *(i32x4*)(vs[buf] + ((tid >> 3) + 32 * p) * KP + 16 * (tid & 7)) = vr[p];
-        };
-
         // kept block indices are clamped into [0, nkb): a malformed kidx can
         // give wrong values but never an access outside K or V
         auto blk = [&](int jj) { return krow ? min(max(krow[jj], 0), nkb - 1) : jj; };
-        int j = blk(0);
-        gload(j);
-        lstore(0);
+        uint32_t koff[8 / WAVES], voff[16 / WAVES];
+#pragma unroll
+        for (int p = 0; p < 8 / WAVES; ++p) koff[p] = tile_voff(64 / WAVES, wave, p, lane);
+#pragma unroll
+        for (int p = 0; p < 16 / WAVES; ++p) voff[p] = tile_voff(128 / WAVES, wave, p, lane);
+        auto kdma = [&](int j, int stage) {
+            dma_k_tile(a.k_i8, bh, N, j, lds_u32(ks[stage]), wave, lane, koff);
+        };
+        auto vdma = [&](int j, int stage) {
+            dma_v_tile(vtb + (int64_t)j * HD * KBLK, lds_u32(vs[stage]), wave, voff);
+        };
+
+        // prologue: K(0), V(0), K(1) resident; K(2), V(1) in flight
+        const int j0 = blk(0);
+        int jn1 = nsel > 1 ? blk(1) : 0, jn2 = nsel > 2 ? blk(2) : 0, jn3 = nsel > 3 ? blk(3) : 0;
+        float ksc1 = ksc[jn1];
+        kdma(j0, 0);
+        vdma(j0, 0);
+        if (nsel > 1) kdma(jn1, 1);
+        i32x4 qop[G][4];
+#pragma unroll
+        for (int g = 0; g < G; ++g) load_q_operand(a.q_i8, bh, N, tq[g], hi, qop[g]);
+        const float c0 = (sq * ksc[j0]) * a.K32;
+        wait_vm<0>();
         __syncthreads();
-        for (int jj = 0; jj < nsel; ++jj) {
-            const int cur = jj & 1;
-            const int jn = (jj + 1 < nsel) ? blk(jj + 1) : -1;
-            if (jn >= 0) gload(jn);
+        if (nsel > 2) kdma(jn2, 2);
+        if (nsel > 1) vdma(jn1, 1);
 
-            i32x16 s0, s1;
-            qk_tile_mfma(ks[cur], qop, l32, hi, s0, s1);
+        bf16x8 pb[G][4];
+        {
+            i32x16 s[G][2];
+            qk_tile_mfma(ks[0], qop, l32, hi, s);
+            tile_softmax(s, c0, min(KBLK, N - j0 * KBLK), hi, m_run, l_run, o, pb);
+        }
 
-            // softmax statistics on the int32 scores (c > 0 is uniform per tile)
-            const int kval = min(KBLK, N - j * KBLK);
-            int smax = INT_MIN;
-            if (kval == KBLK) {
+        for (int jj = 0; jj + 1 < nsel; ++jj) {
+            // resident: K(jj+1), V(jj); in flight: K(jj+2), V(jj+1); pb = P(jj)
+            // jn1..jn3 = kept blocks jj+1..jj+3; ksc1 = k_scale of jn1
+            if (jj + 3 < nsel) kdma(jn3, (jj + 3) % NSTAGE);
+            if (jj + 2 < nsel) vdma(jn2, (jj + 2) % NSTAGE);
+            const float c = (sq * ksc1) * a.K32;
+            // QK(jj+1) and PV(jj) on the matrix cores; the softmax of tile jj+1
+            // (VALU) is independent of PV(jj) and interleaves with it
+            i32x16 s[G][2];
+            qk_tile_mfma(ks[(jj + 1) % NSTAGE], qop, l32, hi, s);
+            tile_pv(vs[jj % NSTAGE], pb, l32, hi, o);
+            tile_softmax(s, c, min(KBLK, N - jn1 * KBLK), hi, m_run, l_run, o, pb);
+            // next kept block (jj+4) and the scale of jn2 via the scalar cache
+            int nxt = 0, kscb = 0;
+            const int32_t* kp = krow ? krow + min(jj + 4, nsel - 1) : (const int32_t*)ksc;
+            sload2(kp, ksc + jn2, nxt, kscb);
+            const int jn4 = krow ? min(max(nxt, 0), nkb - 1) : min(jj + 4, nkb - 1);
+            // K(jj+2) and V(jj+1) must land; this iteration's DMAs may stay in flight
+            constexpr int KD = 8 / WAVES, VD = 16 / WAVES;  // DMAs per wave per tile
+            if (jj + 3 < nsel)
+                wait_vm<KD + VD>();
+            else if (jj + 2 < nsel)
+                wait_vm<VD>();
+            else
+                wait_vm<0>();
+            __syncthreads();
+            jn1 = jn2;
+            jn2 = jn3;
+            jn3 = jn4;
+            ksc1 = __int_as_float(kscb);
+        }
+        tile_pv(vs[(nsel - 1) % NSTAGE], pb, l32, hi, o);
+    }
+
+    float inv[G];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) smax = max(smax, max(s0[r], s1[r]));
-            } else {
+    for (int g = 0; g < G; ++g) {
+        const float lt = l_run[g] + __shfl_xor(l_run[g], 32, 64);
+        inv[g] = a.do_sparse ? 1.0f / lt : 0.f;
+    }
+
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = mfma32_row(lane, r);
-                    if (key < kval) smax = max(smax, s0[r]);
-                    if (key + 32 < kval) smax = max(smax, s1[r]);
+    for (int g = 0; g < G; ++g) {
+        const int t = tq[g];
+        f32x16 ol[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) ol[dt] = f32x16{};
+        float linv = 0.f;
+        if (LIN) {
+            const float* hp = a.hnon + (bh * a.nqb + i) * (int64_t)HS_ROW;
+            const bool ok = t < N;
+            const uint16_t* qr = a.q + (bh * N + (ok ? t : 0)) * HD;
+            float den = 0.f;
+#pragma unroll 2
+            for (int cd = 0; cd < 8; ++cd) {
+                const int d0 = 16 * cd + 8 * hi;
+                const u16x8 qv = ok ? *(const u16x8*)(qr + d0) : u16x8{};
+                const f32x4 z0 = *(const f32x4*)(hp + HD * HD + d0);
+                const f32x4 z1 = *(const f32x4*)(hp + HD * HD + d0 + 4);
+                bf16x8 bqh, bql;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = bf2f(qv[e]);
+                    const float ph = f > 0.f ? f + 1.f : __expf(f);
+                    __bf16 x, y;
+                    split_bf16(ph, x, y);
+                    bqh[e] = x;
+                    bql[e] = y;
+                    den = __builtin_fmaf(ph, e < 4 ? z0[e] : z1[e - 4], den);
                 }
-            }
-            smax = max(smax, __shfl_xor(smax, 32, 64));
-            const float sk = a.k_scale[bh * nkb + j];
-            const float c = (sq * sk) * a.K32;
-            const float mt = ceilf((float)smax * c);
-            if (mt > m_run) {
-                const float alpha =
-                    (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_ldexpf(1.0f, (int)(m_run - mt));
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-                l_run *= alpha;
-                m_run = mt;
-            }
-            const float nm = -m_run;
-            bf16x8 pb[4];
-            float lsum = 0.f;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const int r = 8 * (cc & 1) + s;
-                    const int sv = (cc < 2) ? s0[r] : s1[r];
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sv, c, nm));
-                    if (kval < KBLK) {
-                        const int key = 16 * cc + 8 * (s >> 2) + 4 * hi + (s & 3);
-                        if (key >= kval) p = 0.f;
-                    }
-                    const __bf16 pbv = (__bf16)p;
-                    pb[cc][s] = pbv;
-                    lsum += (float)pbv;
-                }
-            }
-            l_run += lsum;
-
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
-                    const bf16x8 va =
-                        *(const bf16x8*)(vs[cur] + (32 * dt + l32) * KP + (16 * cc + 8 * hi) * 2);
-                    o[dt] = mfma_bf16_32x32x16(va, pb[cc], o[dt]);
+                    const float* hr = hp + (32 * dt + l32) * HD + d0;
+                    const f32x4 h0 = *(const f32x4*)hr, h1 = *(const f32x4*)(hr + 4);
+                    bf16x8 ah, al;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        __bf16 x, y;
+                        split_bf16(e < 4 ? h0[e] : h1[e - 4], x, y);
+                        ah[e] = x;
+                        al[e] = y;
+                    }
+                    ol[dt] = mfma_bf16_32x32x16(ah, bqh, ol[dt]);
+                    ol[dt] = mfma_bf16_32x32x16(ah, bql, ol[dt]);
+                    ol[dt] = mfma_bf16_32x32x16(al, bqh, ol[dt]);
                 }
-
-            if (jn >= 0) lstore(cur ^ 1);
-            __syncthreads();
-            j = jn;
+            }
+            den += __shfl_xor(den, 32, 64);
+            linv = 1.0f / den;
         }
-    }
-
-    const float lt = l_run + __shfl_xor(l_run, 32, 64);
-    const float inv = a.do_sparse ? 1.0f / lt : 0.f;
-
-    f32x16 ol[4];
+        if (t < N) {
+            uint16_t* orow = a.out + (bh * N + t) * HD;
+            float* orow32 = a.out32 ? a.out32 + (bh * N + t) * HD : nullptr;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) ol[dt] = f32x16{};
-    float linv = 0.f;
-    if (LIN) {
-        const float* hp = a.hnon + (bh * a.nqb + i) * (int64_t)HS_ROW;
-        const bool ok = t < N;
-        const uint16_t* qr = a.q + (bh * N + (ok ? t : 0)) * HD;
-        float den = 0.f;
-#pragma unroll 2
-        for (int cd = 0; cd < 8; ++cd) {
-            const int d0 = 16 * cd + 8 * hi;
-            const u16x8 qv = ok ? *(const u16x8*)(qr + d0) : u16x8{};
-            const f32x4 z0 = *(const f32x4*)(hp + HD * HD + d0);
-            const f32x4 z1 = *(const f32x4*)(hp + HD * HD + d0 + 4);
-            bf16x8 bqh, bql;
+            for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const float f = bf2f(qv[s]);
-                const float ph = f > 0.f ? f + 1.f : __expf(f);
-                __bf16 h, l;
-                split_bf16(ph, h, l);
-                bqh[s] = h;
-                bql[s] = l;
-                den = __builtin_fmaf(ph, s < 4 ? z0[s] : z1[s - 4], den);
-            }
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int dv = 32 * dt + 8 * q4 + 4 * hi;
+                    float r4[4];
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const float* hr = hp + (32 * dt + l32) * HD + d0;
-                const f32x4 h0 = *(const f32x4*)hr, h1 = *(const f32x4*)(hr + 4);
-                bf16x8 ah, al;
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    __bf16 x, y;
-                    split_bf16(s < 4 ? h0[s] : h1[s - 4], x, y);
-                    ah[s] = x;
-                    al[s] = y;
+                    for (int u = 0; u < 4; ++u) {
+                        float val = o[g][dt][4 * q4 + u] * inv[g];
+                        if (LIN) val += ol[dt][4 * q4 + u] * linv;
+                        r4[u] = val;
+                    }
+                    *(u16x4*)(orow + dv) =
+                        u16x4{f2bf(r4[0]), f2bf(r4[1]), f2bf(r4[2]), f2bf(r4[3])};
+                    if (orow32) *(f32x4*)(orow32 + dv) = f32x4{r4[0], r4[1], r4[2], r4[3]};
                 }
-                ol[dt] = mfma_bf16_32x32x16(ah, bqh, ol[dt]);
-                ol[dt] = mfma_bf16_32x32x16(ah, bql, ol[dt]);
-                ol[dt] = mfma_bf16_32x32x16(al, bqh, ol[dt]);
-            }
         }
-        den += __shfl_xor(den, 32, 64);
-        linv = 1.0f / den;
-    }
-
-    if (t < N) {
-        uint16_t* orow = a.out + (bh * N + t) * HD;
-        float* orow32 = a.out32 ? a.out32 + (bh * N + t) * HD : nullptr;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int dv = 32 * dt + 8 * g + 4 * hi;
-                float r4[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    float val = o[dt][4 * g + u] * inv;
-                    if (LIN) val += ol[dt][4 * g + u] * linv;
-                    r4[u] = val;
-                }
-                *(u16x4*)(orow + dv) = u16x4{f2bf(r4[0]), f2bf(r4[1]), f2bf(r4[2]), f2bf(r4[3])};
-                if (orow32) *(f32x4*)(orow32 + dv) = f32x4{r4[0], r4[1], r4[2], r4[3]};
-            }
     }
 }
 
-// Raw int32 tiles through the same LDS staging and qk_tile_mfma routine.
-__global__ __launch_bounds__(256) void qk_tiles_kernel(const int8_t* __restrict__ q_i8,
-                                                       const int8_t* __restrict__ k_i8, int64_t BH,
-                                                       int N, const int32_t* __restrict__ tiles,
-                                                       int32_t* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint8_t ks[KBLK * KP];
+// Raw int32 tiles through the same LDS staging and qk_tile_mfma routine as
+// the attention kernel (128 threads: 2 waves x 2 groups of 32 query rows).
+__global__ __launch_bounds__(ATTN_THREADS) void qk_tiles_kernel(const int8_t* __restrict__ q_i8,
+                                                                const int8_t* __restrict__ k_i8,
+                                                                int64_t BH, int N,
+                                                                const int32_t* __restrict__ tiles,
+                                                                int32_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ks[KTILE];
     const int64_t tix = blockIdx.x;
     const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
     const int64_t bh = tiles[3 * tix];
@@ -272,41 +476,50 @@ __global__ __launch_bounds__(256) void qk_tiles_kernel(const int8_t* __restrict_
               hi = lane >> 5;
     int32_t* ot = out + tix * QBLK * KBLK;
     if (!valid) {
-        for (int x = tid; x < QBLK * KBLK; x += 256) ot[x] = 0;
+        for (int x = tid; x < QBLK * KBLK; x += ATTN_THREADS) ot[x] = 0;
         return;
     }
-    i32x4 kr[2];
-    load_k_regs(k_i8, bh, N, j, tid, kr);
-    store_k_lds(ks, tid, kr);
-    __syncthreads();
-    i32x4 qop[4];
-    const int t = i * QBLK + wave * 32 + l32;
-    load_q_operand(q_i8, bh, N, t, hi, qop);
-    i32x16 s0, s1;
-    qk_tile_mfma(ks, qop, l32, hi, s0, s1);
-    const int row = wave * 32 + l32;
+    uint32_t koff[8 / WAVES];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int key = mfma32_row(lane, r);
-        ot[row * KBLK + key] = s0[r];
-        ot[row * KBLK + key + 32] = s1[r];
+    for (int p = 0; p < 8 / WAVES; ++p) koff[p] = tile_voff(64 / WAVES, wave, p, lane);
+    dma_k_tile(k_i8, bh, N, j, lds_u32(ks), wave, lane, koff);
+    wait_vm<0>();
+    __syncthreads();
+    i32x4 qop[G][4];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        load_q_operand(q_i8, bh, N, i * QBLK + 32 * G * wave + 32 * g + l32, hi, qop[g]);
+    i32x16 s[G][2];
+    qk_tile_mfma(ks, qop, l32, hi, s);
+    const int kval = min(KBLK, N - j * KBLK);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int row = 32 * G * wave + 32 * g + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = mfma32_row(lane, r);
+            // keys past N were staged from row N-1; the export reports them as 0
+            ot[row * KBLK + key] = key < kval ? s[g][0][r] : 0;
+            ot[row * KBLK + key + 32] = key + 32 < kval ? s[g][1][r] : 0;
+        }
     }
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     const int64_t total = a.BH * a.nqb;
-    const int64_t grid = (total + 7) / 8 * 8;
     if (a.hnon)
-        hipLaunchKernelGGL((sagesla_attn_kernel<true>), dim3((unsigned)grid), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((sagesla_attn_kernel<true>), dim3((unsigned)total), dim3(ATTN_THREADS), 0,
+                           st, a);
     else
-        hipLaunchKernelGGL((sagesla_attn_kernel<false>), dim3((unsigned)grid), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((sagesla_attn_kernel<false>), dim3((unsigned)total), dim3(ATTN_THREADS),
+                           0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_qk_tiles(const int8_t* q_i8, const int8_t* k_i8, int64_t BH, int N,
                            const int32_t* tiles, int64_t T, int32_t* out, hipStream_t st) {
-    hipLaunchKernelGGL(qk_tiles_kernel, dim3((unsigned)T), dim3(256), 0, st, q_i8, k_i8, BH, N,
-                       tiles, out);
+    hipLaunchKernelGGL(qk_tiles_kernel, dim3((unsigned)T), dim3(ATTN_THREADS), 0, st, q_i8, k_i8, BH,
+                       N, tiles, out);
     return hipGetLastError();
 }
 
