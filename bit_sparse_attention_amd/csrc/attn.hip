@@ -56,35 +56,9 @@ constexpr float HEADROOM = 64.0f;
 // Both tiles are 128-byte rows (K: 64 rows of int8 channels; V^T: 128 rows of
 // 64 bf16 keys) stored with the 16-byte chunk c of row r at slot
 // c ^ swz(r): reads of 8 or 16 consecutive rows at one chunk then hit
-// distinct banks. global_load_lds_dwordx4 writes lane l's 16 bytes at
-// M0 + 16*l, so each lane fetches the chunk its slot must hold. The DMA is
-// issued from inline asm: the compiler then neither tracks it nor inserts
-// vmcnt waits before LDS reads; the pipeline waits explicitly (wait_vm).
+// distinct banks. Tiles arrive by LDS DMA (dma16): each lane fetches the
+// chunk its slot must hold; the pipeline waits explicitly (wait_vm).
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
-    // the tile base is wave-uniform: move it to SGPRs for the saddr form
-    const uint64_t b = (uint64_t)base;
-    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-    const void* sbase = (const void*)sb;
-    // No "memory" clobber: a DMA only writes an LDS buffer that no wave reads
-    // in the same iteration (ordering across iterations comes from the
-    // barrier), and a clobber would turn the read-only kidx / k_scale loads
-    // into vector loads whose vmcnt(0) waits would drain the pipeline.
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1\n\ts_nop 0" ::"v"(voff),
-                 "s"(sbase), "s"(lds_addr));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    // s_waitcnt vmcnt(N), expcnt and lgkmcnt left unconstrained (gfx9 encoding)
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // Two wave-uniform 32-bit loads through the scalar cache, completed inside
 // the asm block. They stay off the vector-memory counter, so fetching the

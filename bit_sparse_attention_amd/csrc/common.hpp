@@ -70,4 +70,39 @@ __device__ __forceinline__ int64_t xcd_item(int64_t wg, int64_t total) {
     return (wg & 7) * per + (wg >> 3);
 }
 
+// ---- asynchronous global -> LDS copies (gfx950 LDS DMA) -------------------
+// global_load_lds_dwordx4 writes lane l's 16 bytes at M0 + 16*l. It is issued
+// from inline asm so the compiler neither tracks it nor inserts vmcnt waits
+// before LDS reads; callers wait with wait_vm<N>() and a barrier. No "memory"
+// clobber: callers only target LDS buffers nobody reads in the same pipeline
+// step (a clobber would also demote read-only scalar loads to vector loads,
+// whose vmcnt(0) waits would drain the pipeline).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+    const uint64_t b = (uint64_t)base;
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const void* sbase = (const void*)sb;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1\n\ts_nop 0" ::"v"(voff),
+                 "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr)));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    // s_waitcnt vmcnt(N); expcnt and lgkmcnt left unconstrained (gfx9 encoding)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane g
+// points at 4 contiguous 16-bit elements (row g of a 16 x 4 block) and lane i
+// receives, as element k, row 4k + i/4 at column i%4.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(uintptr_t)lds_u32(p));
+}
+
 }  // namespace ssa

@@ -162,69 +162,126 @@ __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ k
     }
 }
 
-constexpr int GP = 32 + 8;  // LDS pitch (bf16) of a [row][32] GEMM operand tile: 80 B
+// Complement GEMM: hnon[bh][i][n] = htot[bh][n] - sum_j msel[bh][i][j] * hs[bh][j][n]
+// (i < nqb query blocks, n < HS_ROW state entries, j < nkbp key blocks; msel
+// is 0/1). bf16 operands, fp32 accumulation.
+// Workgroup tile 128 (i) x 128 (n), K step 32, 2 x 2 waves of 64 x 64, each a
+// 2 x 2 grid of 32x32x16 bf16 MFMAs. Operand tiles arrive by LDS DMA into a
+// 3-stage ring:
+//   A [128 i][32 j]: 64-byte rows, 16-byte chunk c of row r at slot
+//     c ^ ((r >> 1) & 3) (conflict-free row reads);
+//   B [32 j][128 n]: 256-byte rows kept j-major as in memory, 8-byte unit u of
+//     row r at u ^ 4*(r & 3), read with transposing loads (lds_read_tr16) so
+//     each lane gets 4 consecutive j of one column n.
+constexpr int GTM = 128, GTN = 128, GTK = 32, GSTAGE = 3;
+constexpr int GA_BYTES = GTM * GTK * 2, GB_BYTES = GTK * GTN * 2;
 
-// hnon[bh][i][n] = htot[bh][n] - sum_j msel[bh][i][j] * hs[bh][j][n]
-// Workgroup tile 128 (i) x 128 (n), K step 32 key blocks, 4 waves of 32 rows.
-__global__ __launch_bounds__(256) void complement_gemm_kernel(
+__global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     const uint16_t* __restrict__ msel, const uint16_t* __restrict__ hs, const float* __restrict__ htot,
     int64_t BH, int nqb, int nkb, int nkbp, float* __restrict__ hnon) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[128 * GP];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * GP];
-    const int nnt = HS_ROW / 128, nmt = (nqb + 127) / 128;
+    __shared__ __attribute__((aligned(1024))) uint8_t As[GSTAGE][GA_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t Bs[GSTAGE][GB_BYTES];
+    const int nnt = HS_ROW / GTN, nmt = (nqb + GTM - 1) / GTM;
     const int64_t total = BH * nnt * nmt;
-    const int64_t item = xcd_item(blockIdx.x, total);
+    const int64_t item = xcd_item(blockIdx.x, total);  // m fastest: B tiles shared in L2
     if (item >= total) return;
     const int mt = (int)(item % nmt);
     const int64_t rest = item / nmt;
     const int nt = (int)(rest % nnt);
     const int64_t bh = rest / nnt;
-    const int i0 = mt * 128, n0 = nt * 128;
+    const int i0 = mt * GTM, n0 = nt * GTN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
-              hi = lane >> 5;
-    f32x16 acc[4];
+              h = lane >> 5, wm = wave >> 1, wn = wave & 1;
+
+    // loop-invariant DMA lane offsets: wave w fills A rows 32w..32w+31 and
+    // B rows 8w..8w+7, two 1 KB blocks each
+    uint32_t aoff[2], boff[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
-    for (int j0 = 0; j0 < nkbp; j0 += 32) {
+    for (int p = 0; p < 2; ++p) {
+        const int ra = 32 * wave + 16 * p + (lane >> 2);
+        const int ca = (lane & 3) ^ ((ra >> 1) & 3);
+        aoff[p] = (uint32_t)(min(i0 + ra, nqb - 1) * nkbp * 2 + ca * 16);
+        const int rb = 8 * wave + 4 * p + (lane >> 4);
+        const int cb = (lane & 15) ^ (2 * (rb & 3));
+        boff[p] = (uint32_t)(rb * HS_ROW * 2 + cb * 16);
+    }
+    const uint16_t* abase = msel + (bh * nqb) * (int64_t)nkbp;
+    const uint16_t* bbase = hs + (bh * nkb) * (int64_t)HS_ROW + n0;
+    auto issue = [&](int ks) {
+        const int j0 = ks * GTK, st = ks % GSTAGE;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            dma16(abase + j0, aoff[p], lds_u32(As[st] + (32 * wave + 16 * p) * 64));
+        const bool ragged = j0 + GTK > nkb;  // rows past nkb: msel is 0 there, fetch row nkb-1
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int c = tid + 256 * p;
-            const int row = c >> 2, q = c & 3;
-            u16x8 a = (i0 + row < nqb)
-                          ? *(const u16x8*)(msel + (bh * nqb + i0 + row) * (int64_t)nkbp + j0 + 8 * q)
-                          : u16x8{};
-            *(u16x8*)(As + row * GP + 8 * q) = a;
-        }
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int c = tid + 256 * p;
-            const int jj = c & 31, q = c >> 5;
-            u16x8 b = (j0 + jj < nkb)
-                          ? *(const u16x8*)(hs + (bh * nkb + j0 + jj) * (int64_t)HS_ROW + n0 + 8 * q)
-                          : u16x8{};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Bs[(8 * q + e) * GP + jj] = b[e];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-            const bf16x8 a = *(const bf16x8*)(As + (32 * wave + l32) * GP + 16 * ch + 8 * hi);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bf16x8 b = *(const bf16x8*)(Bs + (32 * t + l32) * GP + 16 * ch + 8 * hi);
-                acc[t] = mfma_bf16_32x32x16(a, b, acc[t]);
+            uint32_t off = boff[p];
+            if (ragged) {
+                const int rb = 8 * wave + 4 * p + (lane >> 4);
+                const int cb = (lane & 15) ^ (2 * (rb & 3));
+                off = (uint32_t)(min(rb, nkb - 1 - j0) * HS_ROW * 2 + cb * 16);
             }
+            dma16(bbase + (int64_t)j0 * HS_ROW, off, lds_u32(Bs[st] + (8 * wave + 4 * p) * 256));
         }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+    const int nks = nkbp / GTK;
+    issue(0);
+    if (nks > 1) issue(1);
+    if (nks > 1) wait_vm<4>(); else wait_vm<0>();
+    __syncthreads();
+    for (int ks = 0; ks < nks; ++ks) {
+        if (ks + 2 < nks) issue(ks + 2);
+        const uint8_t* A = As[ks % GSTAGE];
+        const uint8_t* B = Bs[ks % GSTAGE];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            bf16x8 af[2], bfr[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const int row = 64 * wm + 32 * a + l32;
+                const int slot = (2 * kc + h) ^ ((row >> 1) & 3);
+                af[a] = *(const bf16x8*)(A + row * 64 + slot * 16);
+            }
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int col = 64 * wn + 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                i16x4 part[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int row = 16 * kc + 8 * h + 4 * t + ((lane & 15) >> 2);
+                    const int unit = (col >> 2) ^ (4 * (row & 3));
+                    part[t] = lds_read_tr16(B + row * 256 + unit * 8);
+                }
+                // k-slots 0-3 from the first read, 4-7 from the second (whole dwords)
+                const u32x2 w0 = __builtin_bit_cast(u32x2, part[0]);
+                const u32x2 w1 = __builtin_bit_cast(u32x2, part[1]);
+                bfr[b] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc[a][b] = mfma_bf16_32x32x16(af[a], bfr[b], acc[a][b]);
+        }
+        if (ks + 2 < nks) wait_vm<4>(); else wait_vm<0>();
         __syncthreads();
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = i0 + 32 * wave + mfma32_row(lane, r);
-            const int n = n0 + 32 * t + l32;
-            if (i < nqb) hnon[(bh * nqb + i) * HS_ROW + n] = htot[bh * HS_ROW + n] - acc[t][r];
-        }
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = i0 + 64 * wm + 32 * a + mfma32_row(lane, r);
+                const int n = n0 + 64 * wn + 32 * b + l32;
+                if (i < nqb) hnon[(bh * nqb + i) * HS_ROW + n] = htot[bh * HS_ROW + n] - acc[a][b][r];
+            }
 }
 
 // ---------------------------------------------------------------------------
