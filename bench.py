@@ -10,8 +10,11 @@ timed region. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -93,6 +96,104 @@ def cpu_baseline(q, k, v, w, keep, kidx_np, budget_blocks=128):
     }
 
 
+# Sources that define the sparse attention kernel; an HBM-traffic record taken
+# with rocprofv3 counters is valid only while these are unchanged.
+ATTN_SOURCES = ("bit_sparse_attention_amd/csrc/attn.hip", "bit_sparse_attention_amd/csrc/common.hpp")
+ATTN_KERNEL = "sagesla_attn_kernel"
+COPY_KERNEL = "copyBuffer"
+
+
+def attn_sources_sha256():
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_record_path(workload):
+    return os.path.join(ROOT, "profiles", f"attn_kernel_hbm_traffic_{workload}.md")
+
+
+def traffic_from_record(workload):
+    """HBM bytes per attention-kernel launch from the committed counter record,
+    or None when there is none or the kernel sources changed since."""
+    path = traffic_record_path(workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("attn_sources_sha256") != attn_sources_sha256():
+        return None
+    k = rec["kernels"].get(ATTN_KERNEL)
+    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
+
+
+def _pmc_per_kernel(path, counter):
+    """Mean counter value per dispatch for each kernel in a rocprofv3
+    counter_collection.csv (values summed over the counter's instances)."""
+    per_dispatch = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per_dispatch.items():
+        out.setdefault(name, []).append(v)
+    return {name: (len(v), sum(v) / len(v)) for name, v in out.items()}
+
+
+def pmc_summary(fetch_csv, write_csv, copy_mib, workload, command):
+    """Markdown record of HBM traffic per launch from a FETCH_SIZE run and a
+    WRITE_SIZE run, each scaled by what the same counter reads for a plain
+    device copy of copy_mib MiB (which moves exactly that much each way)."""
+    fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    cf = [v for n, (_, v) in fetch.items() if COPY_KERNEL in n]
+    cw = [v for n, (_, v) in write.items() if COPY_KERNEL in n]
+    if not cf or not cw:
+        raise SystemExit("no copy-kernel dispatch in the counter files")
+    sf, sw = copy_kib / max(cf), copy_kib / max(cw)
+    lines = [f"# HBM traffic per launch, {workload}", "",
+             "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over instances), "
+             "each from its own rocprofv3 --pmc run, scaled by the factor that makes the same "
+             f"counter read exactly {copy_mib} MiB for a device-to-device copy of {copy_mib} MiB "
+             "in the same run.", "",
+             f"Scale: FETCH x{sf:.4f}, WRITE x{sw:.4f}", "", "Commands:", ""]
+    lines += [f"    {c}" for c in command]
+    lines += ["", "| kernel | dispatches | FETCH KiB | WRITE KiB | scaled read MB | scaled write MB |",
+              "|---|---|---|---|---|---|"]
+    rec = {"workload": workload, "copy_mib": copy_mib, "fetch_scale": sf, "write_scale": sw,
+           "attn_sources_sha256": attn_sources_sha256(), "kernels": {}}
+    for name in sorted(fetch, key=lambda n: -fetch[n][1]):
+        n, f = fetch[name]
+        w = write.get(name, (0, float("nan")))[1]
+        short = re.sub(r"\(.*", "", name)
+        lines.append(f"| `{short}` | {n} | {f:.0f} | {w:.0f} | {f * sf * 1024 / 1e6:.1f} | "
+                     f"{w * sw * 1024 / 1e6:.1f} |")
+        if ATTN_KERNEL in name:
+            rec["kernels"][ATTN_KERNEL] = {"fetch_bytes": f * sf * 1024, "write_bytes": w * sw * 1024}
+    lines += ["", "```json", json.dumps(rec), "```", ""]
+    return "\n".join(lines)
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of `mib` MiB, three times, for scaling
+    HBM byte counters."""
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"# copy calibration: 3 x {mib} MiB device copies", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,7 +202,18 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also time each ABI call on its own")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run a plain MIB-MiB device copy (for counter scaling)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic record from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="command line recorded in the --pmc-summary output")
     args = ap.parse_args()
+    if args.pmc_summary:
+        from bit_sparse_attention_amd.workloads import BENCH_WORKLOAD
+        print(pmc_summary(*args.pmc_summary, args.copy_calibration or 1024,
+                          args.workload or BENCH_WORKLOAD, args.pmc_command))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the SageSLA path is "
               "per-head independent and this build measures one GPU's share; no multi-GPU "
@@ -135,6 +247,9 @@ def main():
         kern_ms = timer.read()
     ms_step = (t1 - t0) * 1e3 / K
     print(f"# timed {K} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
 
     stages = None
     if args.stages:
@@ -173,7 +288,8 @@ def main():
         "attn_kernel_tops": k_tops,
         "effective_ops": ops,
         "roofline": {"bound": "mfma", "achieved": k_tops, "peak": INT8_PEAK_TOPS,
-                     "unit": "TOP/s", "frac": k_tops / INT8_PEAK_TOPS, "traffic": None},
+                     "unit": "TOP/s", "frac": k_tops / INT8_PEAK_TOPS, "traffic": traffic_from_record(w.name),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled)"},
     }
     if stages is not None:
         line["stages_ms"] = stages

@@ -5,9 +5,9 @@
 // (only the kept block interactions are computed exactly; a linear-attention
 // term covers the rest), stacked as SageSLA.
 //
-// One workgroup = one 128-token query block of one head: 2 waves, each with
-// 64 query rows as two 32-row groups that share every K and V fragment read
-// from LDS. For each kept 64-token key block j (ascending):
+// One workgroup = one 128-token query block of one head: 4 waves of 32 query
+// rows, two workgroups per CU (two waves per SIMD). For each kept 64-token
+// key block j (ascending):
 //   S^T = K_j . Q^T        v_mfma_i32_32x32x32_i8, exact int32
 //   x = S * c_ij           c_ij = fl32(fl32(sq*sk) * fl32(sm*log2 e))
 //   m = integer normalizer (raised only when a tile's max exceeds it by more
@@ -20,11 +20,11 @@
 // PV product, so P never leaves registers. V arrives pre-transposed in that
 // key order (linear.hip).
 //
-// Software pipeline (per iteration j): global loads of K(j+2) and V(j+1) are
-// issued first and land in LDS at the end of the iteration; QK(j+1) and
-// PV(j) go to the matrix cores, and the softmax of tile j+1 runs on the VALU
-// underneath PV(j). One wave per SIMD (up to 512 registers) carries the
-// 64-row accumulators, two score tiles and the prefetch registers.
+// Software pipeline: K and V tiles stream through 3-deep LDS rings by LDS
+// DMA, K three blocks ahead and V two ahead, with one workgroup barrier per
+// block. Each step issues QK(j+1) and PV(j) to the matrix cores in a fixed
+// order, reading every LDS fragment ~8 MFMAs before its use, and runs the
+// softmax of tile j+1 in slices between the PV MFMAs.
 //
 // The linear branch is applied in the epilogue from the complement states
 // (phi(Q) . H_i / phi(Q) . z_i, split-bf16 MFMA) and added to the output.
@@ -151,12 +151,18 @@ __device__ __forceinline__ int tile_rowmax(const i32x16& s0, const i32x16& s1) {
     return max(smax, __shfl_xor(smax, 32, 64));
 }
 
+// Adds the two rounded p of a packed bf16 pair to a running sum (one v_dot2
+// with ones: fewer VALU cycles than widening both halves and adding).
+__device__ __forceinline__ void add_pair(bf16x2 pr, float& acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+}
+
 // p = bf16(2^(S*c - m)) for one group's tile, packed as the PV B operand
 // (chunk cc holds keys 16cc + 8*(s/4) + 4*hi + s%4); returns the sum of the
 // rounded p.
 __device__ __forceinline__ float tile_p(const i32x16& s0, const i32x16& s1, float c, float nm,
                                         bf16x8 (&pb)[4]) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float acc = 0.f;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
@@ -168,7 +174,7 @@ __device__ __forceinline__ float tile_p(const i32x16& s0, const i32x16& s1, floa
             const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sa, c, nm));
             const float pz = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sb, c, nm));
             const bf16x2 pr = __builtin_convertvector(f32x2{pa, pz}, bf16x2);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+            add_pair(pr, acc);
             pb[cc][s] = pr[0];
             pb[cc][s + 1] = pr[1];
         }
@@ -178,7 +184,6 @@ __device__ __forceinline__ float tile_p(const i32x16& s0, const i32x16& s1, floa
 
 // Ragged last key block: zero p of the keys >= kval and return the new sum.
 __device__ __forceinline__ float mask_p(int kval, int hi, bf16x8 (&pb)[4]) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float acc = 0.f;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
@@ -187,33 +192,36 @@ __device__ __forceinline__ float mask_p(int kval, int hi, bf16x8 (&pb)[4]) {
             const int key = 16 * cc + 8 * (s >> 2) + 4 * hi + (s & 3);
             if (key >= kval) pb[cc][s] = (__bf16)0.0f;
             if (key + 1 >= kval) pb[cc][s + 1] = (__bf16)0.0f;
-            const bf16x2 pr = {pb[cc][s], pb[cc][s + 1]};
-            acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+            add_pair(bf16x2{pb[cc][s], pb[cc][s + 1]}, acc);
         }
     }
     return acc;
 }
 
-// Softmax of a fresh S tile for every group. The fast part computes P with
-// the current normalizer; when some query's tile max exceeds it by more than
-// HEADROOM (always on the first tile, rarely after), O and l are rescaled by
-// exact powers of two and P is recomputed. kval < 64 marks the ragged last
-// key block.
-__device__ __forceinline__ void tile_softmax(const i32x16 (&s)[G][2], float c, int kval, int hi,
-                                             float (&m_run)[G], float (&l_run)[G],
-                                             f32x16 (&o)[G][4], bf16x8 (&pb)[G][4]) {
-    float mt[G], lsum[G];
-    bool need[G], any = false;
+// Softmax of a fresh S tile for every group, in two parts. The fast part
+// computes P with the current normalizer and flags the queries whose tile max
+// exceeds it by more than HEADROOM (always on the first tile, rarely after).
+// The rare part then rescales O and l by exact powers of two and recomputes
+// P; it also zeroes the keys past N of the ragged last key block (kval < 64).
+__device__ __forceinline__ bool softmax_fast(const i32x16 (&s)[G][2], float c,
+                                             const float (&m_run)[G], bf16x8 (&pb)[G][4],
+                                             float (&lsum)[G], float (&mt)[G], bool (&need)[G]) {
+    bool any = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         lsum[g] = tile_p(s[g][0], s[g][1], c, -m_run[g], pb[g]);
         mt[g] = ceilf((float)tile_rowmax(s[g][0], s[g][1]) * c);  // c > 0, rounding monotone
         need[g] = mt[g] > m_run[g] + HEADROOM;
         any = any || need[g];
-        // keep the common-case P above the rare branch below, in the same
-        // block as the PV products it overlaps with
-        asm volatile("" ::"v"(pb[g][0]), "v"(pb[g][1]), "v"(pb[g][2]), "v"(pb[g][3]), "v"(lsum[g]));
     }
+    return any;
+}
+
+__device__ __forceinline__ void softmax_rare(bool any, const i32x16 (&s)[G][2], float c, int kval,
+                                             int hi, const float (&mt)[G], const bool (&need)[G],
+                                             float (&m_run)[G], float (&l_run)[G],
+                                             f32x16 (&o)[G][4], bf16x8 (&pb)[G][4],
+                                             float (&lsum)[G]) {
     if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -237,6 +245,15 @@ __device__ __forceinline__ void tile_softmax(const i32x16 (&s)[G][2], float c, i
     for (int g = 0; g < G; ++g) l_run[g] += lsum[g];
 }
 
+__device__ __forceinline__ void tile_softmax(const i32x16 (&s)[G][2], float c, int kval, int hi,
+                                             float (&m_run)[G], float (&l_run)[G],
+                                             f32x16 (&o)[G][4], bf16x8 (&pb)[G][4]) {
+    float mt[G], lsum[G];
+    bool need[G];
+    const bool any = softmax_fast(s, c, m_run, pb, lsum, mt, need);
+    softmax_rare(any, s, c, kval, hi, mt, need, m_run, l_run, o, pb, lsum);
+}
+
 // O^T += V^T . P^T for both groups; each V fragment feeds two MFMAs.
 __device__ __forceinline__ void tile_pv(const uint8_t* vs, const bf16x8 (&pb)[G][4], int l32,
                                         int hi, f32x16 (&o)[G][4]) {
@@ -249,6 +266,72 @@ __device__ __forceinline__ void tile_pv(const uint8_t* vs, const bf16x8 (&pb)[G]
 #pragma unroll
             for (int g = 0; g < G; ++g) o[g][dt] = mfma_bf16_32x32x16(va, pb[g][cc], o[g][dt]);
         }
+}
+
+// One pipeline step for a 32-row group (G == 1), written in issue order with
+// scheduling fences between the pieces: the 8 K fragment reads; QK(next)
+// MFMAs, each followed by one V fragment read; PV(current) MFMAs, the first 8
+// each followed by the next V read (a fragment is read ~8 MFMAs before use)
+// and, from the third on, each followed by one slice of the fresh tile's
+// softmax (2 keys: convert, scale, exp2, round to bf16, sum, max), which runs
+// on the VALU while the MFMA executes.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+__device__ __forceinline__ void softmax_slice(int p, const i32x16 (&s)[2], float c, float nm,
+                                              bf16x8 (&pn)[4], float& acc, int& smax) {
+    const int cc = p >> 2, e = 2 * (p & 3), r = 8 * (cc & 1) + e;
+    const int sa = s[cc >> 1][r], sb = s[cc >> 1][r + 1];
+    const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sa, c, nm));
+    const float pz = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sb, c, nm));
+    const bf16x2 pr = __builtin_convertvector(f32x2{pa, pz}, bf16x2);
+    add_pair(pr, acc);
+    pn[cc][e] = pr[0];
+    pn[cc][e + 1] = pr[1];
+    smax = max(smax, max(sa, sb));
+}
+
+__device__ __forceinline__ void pipeline_step(const uint8_t* ks, const uint8_t* vs,
+                                              const i32x4 (&qop)[4], int l32, int hi,
+                                              const bf16x8 (&pb)[4], f32x16 (&o)[4], float c,
+                                              float nm, i32x16 (&s)[2], bf16x8 (&pn)[4],
+                                              float& lsum, int& smax) {
+    const int sl = swz(l32);
+    auto vread = [&](int i) {  // fragment i = 4*cc + dt of V^T
+        const int cc = i >> 2, dt = i & 3;
+        return *(const bf16x8*)(vs + (32 * dt + l32) * 128 + ((2 * cc + hi) ^ sl) * 16);
+    };
+    i32x4 ka[8];
+    bf16x8 va[16];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+        const int slot = ((2 * c4 + hi) ^ sl) * 16;
+        ka[2 * c4] = *(const i32x4*)(ks + l32 * 128 + slot);
+        ka[2 * c4 + 1] = *(const i32x4*)(ks + (32 + l32) * 128 + slot);
+    }
+    fence();
+    s[0] = s[1] = i32x16{};
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            s[h] = mfma_i8_32x32x32(ka[2 * c4 + h], qop[c4], s[h]);
+            va[2 * c4 + h] = vread(2 * c4 + h);
+            fence();
+        }
+    }
+    float acc = 0.f;
+    int mx = INT_MIN;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        o[i & 3] = mfma_bf16_32x32x16(va[i], pb[i >> 2], o[i & 3]);
+        if (i < 8) va[i + 8] = vread(i + 8);
+        if (i >= 2) softmax_slice(i - 2, s, c, nm, pn, acc, mx);
+        fence();
+    }
+    softmax_slice(14, s, c, nm, pn, acc, mx);
+    softmax_slice(15, s, c, nm, pn, acc, mx);
+    lsum = acc;
+    smax = max(mx, __shfl_xor(mx, 32, 64));
 }
 
 template <bool LIN>
@@ -329,9 +412,30 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
             // QK(jj+1) and PV(jj) on the matrix cores; the softmax of tile jj+1
             // (VALU) is independent of PV(jj) and interleaves with it
             i32x16 s[G][2];
-            qk_tile_mfma(ks[(jj + 1) % NSTAGE], qop, l32, hi, s);
-            tile_pv(vs[jj % NSTAGE], pb, l32, hi, o);
-            tile_softmax(s, c, min(KBLK, N - jn1 * KBLK), hi, m_run, l_run, o, pb);
+            bf16x8 pn[G][4];
+            float mt[G], lsum[G];
+            bool need[G];
+            static_assert(G == 1, "the scheduled pipeline step handles one 32-row group");
+            bool any;
+            {
+                int smax;
+                pipeline_step(ks[(jj + 1) % NSTAGE], vs[jj % NSTAGE], qop[0], l32, hi, pb[0], o[0],
+                              c, -m_run[0], s[0], pn[0], lsum[0], smax);
+                mt[0] = ceilf((float)smax * c);  // c > 0, rounding monotone
+                need[0] = mt[0] > m_run[0] + HEADROOM;
+                any = need[0];
+            }
+            // keep the common-case P in this block, above the rare branch
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                asm volatile("" ::"v"(pn[g][0]), "v"(pn[g][1]), "v"(pn[g][2]), "v"(pn[g][3]),
+                             "v"(lsum[g]));
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) pb[g][cc] = pn[g][cc];
+            softmax_rare(any, s, c, min(KBLK, N - jn1 * KBLK), hi, mt, need, m_run, l_run, o, pb,
+                         lsum);
             // next kept block (jj+4) and the scale of jn2 via the scalar cache
             int nxt = 0, kscb = 0;
             const int32_t* kp = krow ? krow + min(jj + 4, nsel - 1) : (const int32_t*)ksc;

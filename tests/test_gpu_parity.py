@@ -100,11 +100,13 @@ ATTN_CASES = [(1, 1, 1024, None), (1, 2, 1000, 0.25), (1, 1, 4100, 0.1), (2, 1, 
               (1, 1, 200, 0.5), (1, 1, 64, None), (1, 1, 1, None)]
 
 
-@pytest.mark.parametrize("B,H,N,topk", ATTN_CASES)
-@pytest.mark.parametrize("branches", [1, 2, 3])
+# dense attention (topk None) has no linear branch: only branches == 1
+ATTN_PARAMS = [(B, H, N, topk, br) for (B, H, N, topk) in ATTN_CASES for br in (1, 2, 3)
+               if topk is not None or br == 1]
+
+
+@pytest.mark.parametrize("B,H,N,topk,branches", ATTN_PARAMS)
 def test_attn_parity(orc, B, H, N, topk, branches):
-    if topk is None and branches != 1:
-        pytest.skip("dense runs the sparse branch only")
     q, k, v = make_qkv(B, H, N, 128, seed=7 * N + branches)
     qd, kd, vd = _gpu(q, k, v)
     label = f"B{B}H{H}N{N} topk={topk} branches={branches}"
