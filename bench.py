@@ -42,57 +42,58 @@ def effective_ops(kidx, N, nqb, nkb, dense):
     return 4.0 * HEAD_DIM * tot, None
 
 
-def cpu_baseline(q, k, v, w, keep, kidx_np, budget_blocks=128):
-    """Oracle timed on the host: head 0, full quantization / linear states of
-    that head and `budget_blocks` query blocks of mask + attention rows,
-    extrapolated to the whole workload."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline(q, k, v, w, keep, kidx_np):
+    """The oracle timed on the host's cores over heads 0 and H-1 of the
+    workload (quantization, block mask, linear states, sparse + linear
+    attention rows of every query block), extrapolated over the heads (all
+    heads do the same work up to the mask's tail-block choices)."""
     import oracle
     from bit_sparse_attention_amd.workloads import bf16_bits
 
     nthreads = min(16, os.cpu_count() or 1)
     N, H, B = w.N, w.H, w.B
     nqb, nkb = (N + 127) // 128, (N + 63) // 64
-    qb = bf16_bits(q[0, :1]).reshape(1, N, 128)
-    kb = bf16_bits(k[0, :1]).reshape(1, N, 128)
-    vb = bf16_bits(v[0, :1]).reshape(1, N, 128)
-    t0 = time.perf_counter()
-    quant = oracle.quant_qk(qb, kb, nthreads)
-    t_quant = time.perf_counter() - t0
-    rng = np.random.default_rng(0)
-    blocks = np.sort(rng.choice(nqb, size=min(budget_blocks, nqb), replace=False))
-    t0 = time.perf_counter()
-    if w.dense:
+    heads = sorted({0, B * H - 1})
+    t_heads = 0.0
+    for bh in heads:
+        b, h = divmod(bh, H)
+        qb = bf16_bits(q[b, h:h + 1]).reshape(1, N, 128)
+        kb = bf16_bits(k[b, h:h + 1]).reshape(1, N, 128)
+        vb = bf16_bits(v[b, h:h + 1]).reshape(1, N, 128)
+        t0 = time.perf_counter()
+        quant = oracle.quant_qk(qb, kb, nthreads)
         kh = None
-    else:
-        kh_rows, _ = oracle.block_mask_head(qb, kb, 0, keep, blocks)
-        kh = np.zeros((nqb, keep), np.int32)
-        kh[blocks] = kh_rows
-    t_mask = time.perf_counter() - t0
-    toks = np.concatenate([np.arange(b * 128, min(N, b * 128 + 128)) for b in blocks])
-    t0 = time.perf_counter()
-    h = z = None
-    if not w.dense:
-        h, z = oracle.linear_states(kb, vb, 0, nthreads)
-    t_states = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.sparse_rows(*quant[:4], vb, 0, toks, kh, want=("decl",), nthreads=nthreads)
-    if not w.dense:
-        oracle.linear_rows(qb, h, z, 0, toks, kh, nthreads)
-    t_rows = time.perf_counter() - t0
-    frac = nqb / len(blocks)
-    t_head = t_quant + t_states + (t_mask + t_rows) * frac
-    t_full = t_head * B * H
+        if not w.dense:
+            kh, _ = oracle.block_mask_head(qb, kb, 0, keep, np.arange(nqb))
+        hs = zs = None
+        if not w.dense:
+            hs, zs = oracle.linear_states(kb, vb, 0, nthreads)
+        toks = np.arange(N)
+        oracle.sparse_rows(*quant[:4], vb, 0, toks, kh, want=("decl",), nthreads=nthreads)
+        if not w.dense:
+            oracle.linear_rows(qb, hs, zs, 0, toks, kh, nthreads)
+        t_heads += time.perf_counter() - t0
+    t_full = t_heads / len(heads) * B * H
     ops_full, _ = effective_ops(kidx_np, N, nqb, nkb, w.dense)
-    sample_s = t_quant + t_mask + t_states + t_rows
     return {
         "value": ops_full / t_full / 1e12,
         "unit": "TOPS",
         "cores": nthreads,
         "kind": "oracle",
-        "sample": (f"head 0 of {B * H}: full quantization and linear states, {len(blocks)} of "
-                   f"{nqb} query blocks of mask + attention rows ({sample_s:.1f} s of CPU work), "
-                   f"extrapolated x{frac:.1f} over blocks and x{B * H} over heads; "
-                   f"full-workload oracle time {t_full:.0f} s"),
+        "sample": (f"heads {heads} of {B * H} in full (quantization, block mask, linear states, "
+                   f"sparse and linear attention rows of all {nqb} query blocks): {t_heads:.1f} s "
+                   f"on {nthreads} threads of {_cpu_model()}, extrapolated x{B * H / len(heads):g} "
+                   f"over heads to {t_full:.0f} s for the workload"),
     }
 
 
@@ -133,8 +134,8 @@ def traffic_from_record(workload):
 
 
 def _pmc_per_kernel(path, counter):
-    """Mean counter value per dispatch for each kernel in a rocprofv3
-    counter_collection.csv (values summed over the counter's instances)."""
+    """Per-dispatch values of a counter for each kernel in a rocprofv3
+    counter_collection.csv (each value summed over the counter's instances)."""
     per_dispatch = {}
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
@@ -144,7 +145,7 @@ def _pmc_per_kernel(path, counter):
     out = {}
     for (name, _), v in per_dispatch.items():
         out.setdefault(name, []).append(v)
-    return {name: (len(v), sum(v) / len(v)) for name, v in out.items()}
+    return out
 
 
 def pmc_summary(fetch_csv, write_csv, copy_mib, workload, command):
@@ -154,17 +155,22 @@ def pmc_summary(fetch_csv, write_csv, copy_mib, workload, command):
     fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
     write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
     copy_kib = copy_mib * 1024.0
-    cf = [v for n, (_, v) in fetch.items() if COPY_KERNEL in n]
-    cw = [v for n, (_, v) in write.items() if COPY_KERNEL in n]
+    # the calibration copies are the largest copy dispatches of the run
+    cf = [max(v) for n, v in fetch.items() if COPY_KERNEL in n]
+    cw = [max(v) for n, v in write.items() if COPY_KERNEL in n]
     if not cf or not cw:
         raise SystemExit("no copy-kernel dispatch in the counter files")
     sf, sw = copy_kib / max(cf), copy_kib / max(cw)
+    fetch = {n: (len(v), sum(v) / len(v)) for n, v in fetch.items() if COPY_KERNEL not in n}
+    write = {n: (len(v), sum(v) / len(v)) for n, v in write.items() if COPY_KERNEL not in n}
     lines = [f"# HBM traffic per launch, {workload}", "",
              "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over instances), "
              "each from its own rocprofv3 --pmc run, scaled by the factor that makes the same "
              f"counter read exactly {copy_mib} MiB for a device-to-device copy of {copy_mib} MiB "
              "in the same run.", "",
-             f"Scale: FETCH x{sf:.4f}, WRITE x{sw:.4f}", "", "Commands:", ""]
+             f"Scale: FETCH x{sf:.4f}, WRITE x{sw:.4f} (the largest copy dispatch read "
+             f"{max(cf):.0f} KiB and wrote {max(cw):.0f} KiB for {copy_kib:.0f} KiB moved).", "",
+             "Commands:", ""]
     lines += [f"    {c}" for c in command]
     lines += ["", "| kernel | dispatches | FETCH KiB | WRITE KiB | scaled read MB | scaled write MB |",
               "|---|---|---|---|---|---|"]
@@ -180,6 +186,42 @@ def pmc_summary(fetch_csv, write_csv, copy_mib, workload, command):
             rec["kernels"][ATTN_KERNEL] = {"fetch_bytes": f * sf * 1024, "write_bytes": w * sw * 1024}
     lines += ["", "```json", json.dumps(rec), "```", ""]
     return "\n".join(lines)
+
+
+def trace_summary(stats_csv, workload, command):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# Kernel time per launch, {workload}", "", "Command:", ""]
+    lines += [f"    {c}" for c in command]
+    lines += ["", "| kernel | calls | avg us | min us | max us | % of GPU time |",
+              "|---|---|---|---|---|---|"]
+    for r in rows:
+        short = re.sub(r"\(.*", "", r["Name"])
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+def pmc_table(csvs, workload, command, kernel_filter):
+    """Markdown table: mean value per dispatch of every counter in the given
+    rocprofv3 counter_collection.csv files, for kernels matching the filter."""
+    vals = {}
+    for path in csvs:
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if kernel_filter not in r["Kernel_Name"]:
+                continue
+            key = (re.sub(r"\(.*", "", r["Kernel_Name"]), r["Counter_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (kern, ctr, _), v in per.items():
+            vals.setdefault((kern, ctr), []).append(v)
+    lines = [f"# Counters per dispatch, {workload}", "", "Commands:", ""]
+    lines += [f"    {c}" for c in command]
+    lines += ["", "| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
+    for (kern, ctr), v in sorted(vals.items()):
+        lines.append(f"| `{kern}` | {ctr} | {len(v)} | {sum(v) / len(v):.6g} |")
+    return "\n".join(lines) + "\n"
 
 
 def copy_calibration(mib):
@@ -206,13 +248,23 @@ def main():
                     help="after the timed steps, run a plain MIB-MiB device copy (for counter scaling)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM traffic record from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--trace-summary", metavar="KERNEL_STATS_CSV",
+                    help="print a kernel-time table from a rocprofv3 --stats run and exit")
+    ap.add_argument("--pmc-table", nargs="+", metavar="COUNTER_CSV",
+                    help="print a per-dispatch counter table for the attention kernel and exit")
     ap.add_argument("--pmc-command", action="append", default=[],
-                    help="command line recorded in the --pmc-summary output")
+                    help="command line recorded in the summary outputs")
     args = ap.parse_args()
-    if args.pmc_summary:
+    if args.pmc_summary or args.trace_summary or args.pmc_table:
         from bit_sparse_attention_amd.workloads import BENCH_WORKLOAD
-        print(pmc_summary(*args.pmc_summary, args.copy_calibration or 1024,
-                          args.workload or BENCH_WORKLOAD, args.pmc_command))
+        wl = args.workload or BENCH_WORKLOAD
+        if args.pmc_summary:
+            print(pmc_summary(*args.pmc_summary, args.copy_calibration or 1024, wl,
+                              args.pmc_command))
+        elif args.trace_summary:
+            print(trace_summary(args.trace_summary, wl, args.pmc_command))
+        else:
+            print(pmc_table(args.pmc_table, wl, args.pmc_command, ATTN_KERNEL))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the SageSLA path is "
@@ -267,6 +319,8 @@ def main():
     kidx_np = None if plan.dense else plan.kidx.cpu().numpy()
     ops, _ = effective_ops(kidx_np, w.N, plan.nqb, plan.nkb, plan.dense)
     k_ms = float(np.mean(kern_ms)) if kern_ms else float("nan")
+    k_pct = ({f"p{p}": float(np.percentile(kern_ms, p)) for p in (10, 50, 90)}
+             if kern_ms else None)
     k_tops = ops / (k_ms * 1e-3) / 1e12
     line = {
         "metric": "SageSLA attn ms/call + effective INT8 TOPS (% MFMA peak), 14B-720p shape, 1 GPU",
@@ -285,6 +339,7 @@ def main():
                    "topk": w.topk, "keep": plan.keep, "branches": "sparse+linear"
                    if plan.branches == 3 else "sparse", "spikes": w.spikes},
         "attn_kernel_ms": k_ms,
+        "attn_kernel_ms_pct": k_pct,
         "attn_kernel_tops": k_tops,
         "effective_ops": ops,
         "roofline": {"bound": "mfma", "achieved": k_tops, "peak": INT8_PEAK_TOPS,
