@@ -28,6 +28,8 @@
 //
 // The linear branch is applied in the epilogue from the complement states
 // (phi(Q) . H_i / phi(Q) . z_i, split-bf16 MFMA) and added to the output.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -83,23 +85,27 @@ __device__ __forceinline__ uint32_t tile_voff(int rows_per_wave, int wave, int p
 }
 
 // K tile of key block j into LDS at lds_base (8/WAVES DMAs per wave). koff
-// holds the loop-invariant lane offsets. In the ragged last block, rows past
-// N are fetched from row N-1 (those keys are masked out of every use).
+// holds the loop-invariant lane offsets, krag those of the ragged last block,
+// whose rows past N are fetched from row N-1 (those keys are masked out of
+// every use).
 __device__ __forceinline__ void dma_k_tile(const int8_t* __restrict__ k_i8, int64_t bh, int N, int j,
-                                           uint32_t lds_base, int wave, int lane,
-                                           const uint32_t (&koff)[8 / WAVES]) {
+                                           uint32_t lds_base, int wave,
+                                           const uint32_t (&koff)[8 / WAVES],
+                                           const uint32_t (&krag)[8 / WAVES]) {
     const int8_t* base = k_i8 + (bh * N + (int64_t)j * KBLK) * HD;
     const bool ragged = (j + 1) * KBLK > N;
 #pragma unroll
-    for (int p = 0; p < 8 / WAVES; ++p) {
-        uint32_t off = koff[p];
-        if (ragged) {
-            const int row = (64 / WAVES) * wave + 8 * p + (lane >> 3);
-            const int rr = min(row, N - 1 - j * KBLK);
-            off = rr * 128 + 16 * ((lane & 7) ^ swz(row));
-        }
-        dma16(base, off, __builtin_amdgcn_readfirstlane(lds_base + ((64 / WAVES) * wave + 8 * p) * 128));
-    }
+    for (int p = 0; p < 8 / WAVES; ++p)
+        dma16(base, ragged ? krag[p] : koff[p],
+              __builtin_amdgcn_readfirstlane(lds_base + ((64 / WAVES) * wave + 8 * p) * 128));
+}
+
+// Lane offsets of the ragged last key block (valid rows = nval < 64): row r
+// is fetched from row min(r, nval - 1), into the slot that row r occupies.
+__device__ __forceinline__ uint32_t tile_voff_ragged(int wave, int p, int lane, int nval) {
+    const int row = (64 / WAVES) * wave + 8 * p + (lane >> 3);
+    const int rr = min(row, nval - 1);
+    return rr * 128 + 16 * ((lane & 7) ^ swz(row));
 }
 
 // V^T tile (128 rows of 64 keys, zero past N) into LDS (16/WAVES DMAs per wave).
@@ -199,41 +205,45 @@ __device__ __forceinline__ float mask_p(int kval, int hi, bf16x8 (&pb)[4]) {
 }
 
 // Softmax of a fresh S tile for every group, in two parts. The fast part
-// computes P with the current normalizer and flags the queries whose tile max
-// exceeds it by more than HEADROOM (always on the first tile, rarely after).
-// The rare part then rescales O and l by exact powers of two and recomputes
-// P; it also zeroes the keys past N of the ragged last key block (kval < 64).
+// computes P with the current normalizer and its sum. The tile's row max is
+// not needed there: if some query's max exceeds the normalizer by more than
+// HEADROOM, one of its p is >= 2^HEADROOM, so the lane holding it sees a sum
+// above 2^(HEADROOM-1) (the first tile, with m = -inf, always does). Only then
+// does the rare part compute the exact max, rescale O and l by exact powers of
+// two where it is exceeded and recompute P. The rare part also zeroes the keys
+// past N of the ragged last key block (kval < 64).
+constexpr float RESCALE_TRIGGER = 0x1p63f;  // 2^(HEADROOM - 1)
+
 __device__ __forceinline__ bool softmax_fast(const i32x16 (&s)[G][2], float c,
                                              const float (&m_run)[G], bf16x8 (&pb)[G][4],
-                                             float (&lsum)[G], float (&mt)[G], bool (&need)[G]) {
-    bool any = false;
+                                             float (&lsum)[G]) {
+    bool trig = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         lsum[g] = tile_p(s[g][0], s[g][1], c, -m_run[g], pb[g]);
-        mt[g] = ceilf((float)tile_rowmax(s[g][0], s[g][1]) * c);  // c > 0, rounding monotone
-        need[g] = mt[g] > m_run[g] + HEADROOM;
-        any = any || need[g];
+        trig = trig || !(lsum[g] <= RESCALE_TRIGGER);
     }
-    return any;
+    return trig;
 }
 
-__device__ __forceinline__ void softmax_rare(bool any, const i32x16 (&s)[G][2], float c, int kval,
-                                             int hi, const float (&mt)[G], const bool (&need)[G],
-                                             float (&m_run)[G], float (&l_run)[G],
+__device__ __forceinline__ void softmax_rare(bool trig, const i32x16 (&s)[G][2], float c, int kval,
+                                             int hi, float (&m_run)[G], float (&l_run)[G],
                                              f32x16 (&o)[G][4], bf16x8 (&pb)[G][4],
                                              float (&lsum)[G]) {
-    if (__builtin_amdgcn_ballot_w64(any)) {
+    if (__builtin_amdgcn_ballot_w64(trig)) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
+            const float mt = ceilf((float)tile_rowmax(s[g][0], s[g][1]) * c);  // c > 0
+            const bool need = mt > m_run[g] + HEADROOM;
             const float alpha =
-                need[g] ? ((m_run[g] == -INFINITY)
-                               ? 0.f
-                               : __builtin_amdgcn_ldexpf(1.0f, (int)(m_run[g] - mt[g])))
-                        : 1.0f;
+                need ? ((m_run[g] == -INFINITY)
+                            ? 0.f
+                            : __builtin_amdgcn_ldexpf(1.0f, (int)(m_run[g] - mt)))
+                     : 1.0f;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) o[g][dt] *= alpha;
             l_run[g] *= alpha;
-            m_run[g] = need[g] ? mt[g] : m_run[g];
+            m_run[g] = need ? mt : m_run[g];
             lsum[g] = tile_p(s[g][0], s[g][1], c, -m_run[g], pb[g]);
         }
     }
@@ -248,10 +258,9 @@ __device__ __forceinline__ void softmax_rare(bool any, const i32x16 (&s)[G][2], 
 __device__ __forceinline__ void tile_softmax(const i32x16 (&s)[G][2], float c, int kval, int hi,
                                              float (&m_run)[G], float (&l_run)[G],
                                              f32x16 (&o)[G][4], bf16x8 (&pb)[G][4]) {
-    float mt[G], lsum[G];
-    bool need[G];
-    const bool any = softmax_fast(s, c, m_run, pb, lsum, mt, need);
-    softmax_rare(any, s, c, kval, hi, mt, need, m_run, l_run, o, pb, lsum);
+    float lsum[G];
+    const bool trig = softmax_fast(s, c, m_run, pb, lsum);
+    softmax_rare(trig, s, c, kval, hi, m_run, l_run, o, pb, lsum);
 }
 
 // O^T += V^T . P^T for both groups; each V fragment feeds two MFMAs.
@@ -273,12 +282,12 @@ __device__ __forceinline__ void tile_pv(const uint8_t* vs, const bf16x8 (&pb)[G]
 // MFMAs, each followed by one V fragment read; PV(current) MFMAs, the first 8
 // each followed by the next V read (a fragment is read ~8 MFMAs before use)
 // and, from the third on, each followed by one slice of the fresh tile's
-// softmax (2 keys: convert, scale, exp2, round to bf16, sum, max), which runs
-// on the VALU while the MFMA executes.
+// softmax (2 keys: convert, scale, exp2, round to bf16, sum), which runs on
+// the VALU while the MFMA executes.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ void softmax_slice(int p, const i32x16 (&s)[2], float c, float nm,
-                                              bf16x8 (&pn)[4], float& acc, int& smax) {
+                                              bf16x8 (&pn)[4], float& acc) {
     const int cc = p >> 2, e = 2 * (p & 3), r = 8 * (cc & 1) + e;
     const int sa = s[cc >> 1][r], sb = s[cc >> 1][r + 1];
     const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sa, c, nm));
@@ -287,14 +296,13 @@ __device__ __forceinline__ void softmax_slice(int p, const i32x16 (&s)[2], float
     add_pair(pr, acc);
     pn[cc][e] = pr[0];
     pn[cc][e + 1] = pr[1];
-    smax = max(smax, max(sa, sb));
 }
 
 __device__ __forceinline__ void pipeline_step(const uint8_t* ks, const uint8_t* vs,
                                               const i32x4 (&qop)[4], int l32, int hi,
                                               const bf16x8 (&pb)[4], f32x16 (&o)[4], float c,
                                               float nm, i32x16 (&s)[2], bf16x8 (&pn)[4],
-                                              float& lsum, int& smax) {
+                                              float& lsum) {
     const int sl = swz(l32);
     auto vread = [&](int i) {  // fragment i = 4*cc + dt of V^T
         const int cc = i >> 2, dt = i & 3;
@@ -320,18 +328,16 @@ __device__ __forceinline__ void pipeline_step(const uint8_t* ks, const uint8_t* 
         }
     }
     float acc = 0.f;
-    int mx = INT_MIN;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         o[i & 3] = mfma_bf16_32x32x16(va[i], pb[i >> 2], o[i & 3]);
         if (i < 8) va[i + 8] = vread(i + 8);
-        if (i >= 2) softmax_slice(i - 2, s, c, nm, pn, acc, mx);
+        if (i >= 2) softmax_slice(i - 2, s, c, nm, pn, acc);
         fence();
     }
-    softmax_slice(14, s, c, nm, pn, acc, mx);
-    softmax_slice(15, s, c, nm, pn, acc, mx);
+    softmax_slice(14, s, c, nm, pn, acc);
+    softmax_slice(15, s, c, nm, pn, acc);
     lsum = acc;
-    smax = max(mx, __shfl_xor(mx, 32, 64));
 }
 
 template <bool LIN>
@@ -368,13 +374,17 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
         // kept block indices are clamped into [0, nkb): a malformed kidx can
         // give wrong values but never an access outside K or V
         auto blk = [&](int jj) { return krow ? min(max(krow[jj], 0), nkb - 1) : jj; };
-        uint32_t koff[8 / WAVES], voff[16 / WAVES];
+        uint32_t koff[8 / WAVES], krag[8 / WAVES], voff[16 / WAVES];
+        const int nlast = N - (nkb - 1) * KBLK;  // valid keys of the last key block
 #pragma unroll
-        for (int p = 0; p < 8 / WAVES; ++p) koff[p] = tile_voff(64 / WAVES, wave, p, lane);
+        for (int p = 0; p < 8 / WAVES; ++p) {
+            koff[p] = tile_voff(64 / WAVES, wave, p, lane);
+            krag[p] = tile_voff_ragged(wave, p, lane, nlast);
+        }
 #pragma unroll
         for (int p = 0; p < 16 / WAVES; ++p) voff[p] = tile_voff(128 / WAVES, wave, p, lane);
         auto kdma = [&](int j, int stage) {
-            dma_k_tile(a.k_i8, bh, N, j, lds_u32(ks[stage]), wave, lane, koff);
+            dma_k_tile(a.k_i8, bh, N, j, lds_u32(ks[stage]), wave, koff, krag);
         };
         auto vdma = [&](int j, int stage) {
             dma_v_tile(vtb + (int64_t)j * HD * KBLK, lds_u32(vs[stage]), wave, voff);
@@ -403,28 +413,24 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
             tile_softmax(s, c0, min(KBLK, N - j0 * KBLK), hi, m_run, l_run, o, pb);
         }
 
-        for (int jj = 0; jj + 1 < nsel; ++jj) {
-            // resident: K(jj+1), V(jj); in flight: K(jj+2), V(jj+1); pb = P(jj)
-            // jn1..jn3 = kept blocks jj+1..jj+3; ksc1 = k_scale of jn1
-            if (jj + 3 < nsel) kdma(jn3, (jj + 3) % NSTAGE);
-            if (jj + 2 < nsel) vdma(jn2, (jj + 2) % NSTAGE);
+        // Step jj (ring stage R = jj % NSTAGE, a compile-time constant so every
+        // LDS address is an immediate offset): resident K(jj+1), V(jj); in
+        // flight K(jj+2), V(jj+1); pb = P(jj); jn1..jn3 = kept blocks jj+1..jj+3
+        // and ksc1 = the k_scale of jn1.
+        auto step = [&](int jj, auto stage) {
+            constexpr int R = decltype(stage)::value;
+            if (jj + 3 < nsel) kdma(jn3, R);
+            if (jj + 2 < nsel) vdma(jn2, (R + 2) % NSTAGE);
             const float c = (sq * ksc1) * a.K32;
-            // QK(jj+1) and PV(jj) on the matrix cores; the softmax of tile jj+1
-            // (VALU) is independent of PV(jj) and interleaves with it
+            // QK(jj+1) and PV(jj) on the matrix cores, the softmax of tile jj+1
+            // on the VALU between the PV MFMAs
             i32x16 s[G][2];
             bf16x8 pn[G][4];
-            float mt[G], lsum[G];
-            bool need[G];
+            float lsum[G];
             static_assert(G == 1, "the scheduled pipeline step handles one 32-row group");
-            bool any;
-            {
-                int smax;
-                pipeline_step(ks[(jj + 1) % NSTAGE], vs[jj % NSTAGE], qop[0], l32, hi, pb[0], o[0],
-                              c, -m_run[0], s[0], pn[0], lsum[0], smax);
-                mt[0] = ceilf((float)smax * c);  // c > 0, rounding monotone
-                need[0] = mt[0] > m_run[0] + HEADROOM;
-                any = need[0];
-            }
+            pipeline_step(ks[(R + 1) % NSTAGE], vs[R], qop[0], l32, hi, pb[0], o[0], c, -m_run[0],
+                          s[0], pn[0], lsum[0]);
+            const bool trig = !(lsum[0] <= RESCALE_TRIGGER);
             // keep the common-case P in this block, above the rare branch
 #pragma unroll
             for (int g = 0; g < G; ++g)
@@ -434,14 +440,13 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
             for (int g = 0; g < G; ++g)
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) pb[g][cc] = pn[g][cc];
-            softmax_rare(any, s, c, min(KBLK, N - jn1 * KBLK), hi, mt, need, m_run, l_run, o, pb,
-                         lsum);
+            softmax_rare(trig, s, c, min(KBLK, N - jn1 * KBLK), hi, m_run, l_run, o, pb, lsum);
             // next kept block (jj+4) and the scale of jn2 via the scalar cache
             int nxt = 0, kscb = 0;
             const int32_t* kp = krow ? krow + min(jj + 4, nsel - 1) : (const int32_t*)ksc;
             sload2(kp, ksc + jn2, nxt, kscb);
             const int jn4 = krow ? min(max(nxt, 0), nkb - 1) : min(jj + 4, nkb - 1);
-            // K(jj+2) and V(jj+1) must land; this iteration's DMAs may stay in flight
+            // K(jj+2) and V(jj+1) must land; this step's DMAs may stay in flight
             constexpr int KD = 8 / WAVES, VD = 16 / WAVES;  // DMAs per wave per tile
             if (jj + 3 < nsel)
                 wait_vm<KD + VD>();
@@ -454,7 +459,20 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
             jn2 = jn3;
             jn3 = jn4;
             ksc1 = __int_as_float(kscb);
+        };
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        static_assert(NSTAGE == 3, "the step loop is unrolled by the ring depth");
+        const int steps = nsel - 1;
+        int jj = 0;
+        for (; jj + 3 <= steps; jj += 3) {
+            step(jj, S0{});
+            step(jj + 1, S1{});
+            step(jj + 2, S2{});
         }
+        if (jj < steps) step(jj++, S0{});
+        if (jj < steps) step(jj, S1{});
         tile_pv(vs[(nsel - 1) % NSTAGE], pb, l32, hi, o);
     }
 
@@ -538,7 +556,7 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
 }
 
 // Raw int32 tiles through the same LDS staging and qk_tile_mfma routine as
-// the attention kernel (128 threads: 2 waves x 2 groups of 32 query rows).
+// the attention kernel (4 waves x 32 query rows).
 __global__ __launch_bounds__(ATTN_THREADS) void qk_tiles_kernel(const int8_t* __restrict__ q_i8,
                                                                 const int8_t* __restrict__ k_i8,
                                                                 int64_t BH, int N,
@@ -557,10 +575,13 @@ __global__ __launch_bounds__(ATTN_THREADS) void qk_tiles_kernel(const int8_t* __
         for (int x = tid; x < QBLK * KBLK; x += ATTN_THREADS) ot[x] = 0;
         return;
     }
-    uint32_t koff[8 / WAVES];
+    uint32_t koff[8 / WAVES], krag[8 / WAVES];
 #pragma unroll
-    for (int p = 0; p < 8 / WAVES; ++p) koff[p] = tile_voff(64 / WAVES, wave, p, lane);
-    dma_k_tile(k_i8, bh, N, j, lds_u32(ks), wave, lane, koff);
+    for (int p = 0; p < 8 / WAVES; ++p) {
+        koff[p] = tile_voff(64 / WAVES, wave, p, lane);
+        krag[p] = tile_voff_ragged(wave, p, lane, min(KBLK, N - j * KBLK));
+    }
+    dma_k_tile(k_i8, bh, N, j, lds_u32(ks), wave, koff, krag);
     wait_vm<0>();
     __syncthreads();
     i32x4 qop[G][4];
