@@ -497,8 +497,12 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
             float den = 0.f;
 #pragma unroll 2
             for (int cd = 0; cd < 8; ++cd) {
+                // k-slots of this lane: d = 16cd + 8(s/4) + 4hi + s%4, stored at
+                // positions d0 .. d0+7 of the state rows
                 const int d0 = 16 * cd + 8 * hi;
-                const u16x8 qv = ok ? *(const u16x8*)(qr + d0) : u16x8{};
+                const u16x4 q0 = ok ? *(const u16x4*)(qr + 16 * cd + 4 * hi) : u16x4{};
+                const u16x4 q1 = ok ? *(const u16x4*)(qr + 16 * cd + 8 + 4 * hi) : u16x4{};
+                const u16x8 qv = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
                 const f32x4 z0 = *(const f32x4*)(hp + HD * HD + d0);
                 const f32x4 z1 = *(const f32x4*)(hp + HD * HD + d0 + 4);
                 bf16x8 bqh, bql;

@@ -22,8 +22,12 @@ constexpr int TP = KBLK + 8;  // LDS pitch (bf16) of a [channel][token] tile: 14
 //   positions 0-3 -> keys 0-3, 4-7 -> 8-11, 8-11 -> 4-7, 12-15 -> 12-15.
 
 // Per 64-token key block: V^T re-laid for the sparse kernel, and (STATES)
-// the linear states h_j^T [e][d] (bf16, for the GEMM), z_j, and an fp32 running
-// sum over the workgroup's LIN_GROUP key blocks.
+// the linear state h_j^T and z_j as one bf16 row of HS_ROW (for the GEMM), and
+// an fp32 running sum over the workgroup's LIN_GROUP key blocks. Row e of h^T
+// holds d at position 16cd + 8hi + s for d = 16cd + 8(s/4) + 4hi + s%4 (the
+// order in which one lane of the 32x32 MFMA output holds its rows), and z
+// follows in the same d order; the GEMM and the apply only need a consistent
+// order, and each lane then stores 16-byte runs.
 template <bool STATES>
 __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v, int N,
@@ -39,10 +43,9 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
     const int64_t bh = blockIdx.y;
     const int g = blockIdx.x;
     const int G = STATES ? LIN_GROUP : 1;
-    f32x16 tot[4];
+    f32x16 tot[4], totz = f32x16{};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) tot[dt] = f32x16{};
-    float ztot = 0.f;
     for (int jb = 0; jb < G; ++jb) {
         const int j = g * G + jb;
         if (j >= nkb) break;
@@ -82,51 +85,82 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
                 u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
         }
         if (STATES) {
-            // h_j^T[e][d] = sum_u V[u][e] phi(K)[u][d]: A = V^T rows e, B = phi(K) cols d,
-            // phi(K) = hi + lo (two bf16 products, fp32 accumulation)
-            f32x16 acc[4];
+            // (h_j^T)^T[d][e] = sum_u phi(K)[u][d] V[u][e]: A = phi(K)^T rows d (hi and
+            // lo parts, two products, fp32 accumulation), B = V columns e. Wave w
+            // takes columns e = 32w .. 32w+31; acc[dt] holds rows d = 32dt + ...
+            f32x16 acc[4], accz = f32x16{};
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+            bf16x8 ones;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 #pragma unroll
             for (int uc = 0; uc < 4; ++uc) {
-                const bf16x8 a = *(const bf16x8*)(vtl + (32 * wave + l32) * TP + 16 * uc + 8 * hi);
+                const bf16x8 b = *(const bf16x8*)(vtl + (32 * wave + l32) * TP + 16 * uc + 8 * hi);
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
-                    const bf16x8 bh8 = *(const bf16x8*)(fkh + (32 * dt + l32) * TP + 16 * uc + 8 * hi);
-                    const bf16x8 bl8 = *(const bf16x8*)(fkl + (32 * dt + l32) * TP + 16 * uc + 8 * hi);
-                    acc[dt] = mfma_bf16_32x32x16(a, bh8, acc[dt]);
-                    acc[dt] = mfma_bf16_32x32x16(a, bl8, acc[dt]);
+                    const bf16x8 ah = *(const bf16x8*)(fkh + (32 * dt + l32) * TP + 16 * uc + 8 * hi);
+                    const bf16x8 al = *(const bf16x8*)(fkl + (32 * dt + l32) * TP + 16 * uc + 8 * hi);
+                    acc[dt] = mfma_bf16_32x32x16(ah, b, acc[dt]);
+                    acc[dt] = mfma_bf16_32x32x16(al, b, acc[dt]);
                 }
             }
-            uint16_t* hrow = hs + (bh * nkb + j) * HS_ROW;
+            // z_j[d] for rows d = 32w + ...: the same product against ones
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int e = 32 * wave + mfma32_row(lane, r), d = 32 * dt + l32;
-                    hrow[e * HD + d] = f2bf(acc[dt][r]);
-                    tot[dt][r] += acc[dt][r];
-                }
-            if (tid < HD) {
-                float z = 0.f;
-                for (int u = 0; u < KBLK; ++u)
-                    z += bf2f(fkh[tid * TP + u]) + bf2f(fkl[tid * TP + u]);
-                hrow[HD * HD + tid] = f2bf(z);
-                ztot += z;
+            for (int uc = 0; uc < 4; ++uc) {
+                const int o = (32 * wave + l32) * TP + 16 * uc + 8 * hi;
+                accz = mfma_bf16_32x32x16(*(const bf16x8*)(fkh + o), ones, accz);
+                accz = mfma_bf16_32x32x16(*(const bf16x8*)(fkl + o), ones, accz);
             }
+            // lane (column e = 32w + l32, hi) holds rows d = 32dt + 8(r/4) + 4hi + r%4:
+            // registers 8rb .. 8rb+7 are positions 16(2dt + rb) + 8hi + 0..7 of row e
+            uint16_t* hrow = hs + (bh * nkb + j) * (int64_t)HS_ROW;
+            const int e = 32 * wave + l32;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    u16x8 o8;
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) o8[x] = f2bf(acc[dt][8 * rb + x]);
+                    *(u16x8*)(hrow + e * HD + 16 * (2 * dt + rb) + 8 * hi) = o8;
+                }
+                tot[dt] += acc[dt];
+            }
+            if (l32 == 0) {  // z rows d = 32w + ..., every column equal
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    u16x8 o8;
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) o8[x] = f2bf(accz[8 * rb + x]);
+                    *(u16x8*)(hrow + HD * HD + 16 * (2 * wave + rb) + 8 * hi) = o8;
+                }
+            }
+            totz += accz;
         }
         __syncthreads();
     }
     if (STATES) {
-        float* prow = hpart + (bh * ngroups + g) * HS_ROW;
+        float* prow = hpart + (bh * ngroups + g) * (int64_t)HS_ROW;
+        const int e = 32 * wave + l32;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int e = 32 * wave + mfma32_row(lane, r), d = 32 * dt + l32;
-                prow[e * HD + d] = tot[dt][r];
+            for (int rb = 0; rb < 2; ++rb) {
+                float* dst = prow + e * HD + 16 * (2 * dt + rb) + 8 * hi;
+                *(f32x4*)dst = f32x4{tot[dt][8 * rb], tot[dt][8 * rb + 1], tot[dt][8 * rb + 2],
+                                     tot[dt][8 * rb + 3]};
+                *(f32x4*)(dst + 4) = f32x4{tot[dt][8 * rb + 4], tot[dt][8 * rb + 5],
+                                           tot[dt][8 * rb + 6], tot[dt][8 * rb + 7]};
             }
-        if (tid < HD) prow[HD * HD + tid] = ztot;
+        if (l32 == 0)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                float* dst = prow + HD * HD + 16 * (2 * wave + rb) + 8 * hi;
+                *(f32x4*)dst = f32x4{totz[8 * rb], totz[8 * rb + 1], totz[8 * rb + 2], totz[8 * rb + 3]};
+                *(f32x4*)(dst + 4) =
+                    f32x4{totz[8 * rb + 4], totz[8 * rb + 5], totz[8 * rb + 6], totz[8 * rb + 7]};
+            }
     }
 }
 
