@@ -46,25 +46,37 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
     f32x16 tot[4], totz = f32x16{};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) tot[dt] = f32x16{};
-    for (int jb = 0; jb < G; ++jb) {
-        const int j = g * G + jb;
-        if (j >= nkb) break;
-        // token-major global loads, channel-major LDS stores (u fastest: conflict free)
+    // raw K and V of one key block in registers: lane (tid) holds token
+    // u = tid & 63, channels 8ch .. 8ch+7 for ch = (tid >> 6) + 4*it
+    u16x8 vv[4], kk[4];
+    auto load = [&](int j) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int c = tid + 256 * it;
             const int u = c & 63, ch = c >> 6;
             const int tok = j * KBLK + u;
             const bool ok = tok < N;
-            const int64_t off = (bh * N + tok) * HD + 8 * ch;
-            u16x8 vv = ok ? *(const u16x8*)(v + off) : u16x8{};
+            const int64_t off = (bh * N + (ok ? tok : 0)) * HD + 8 * ch;
+            vv[it] = ok ? *(const u16x8*)(v + off) : u16x8{};
+            if (STATES) kk[it] = ok ? *(const u16x8*)(k + off) : u16x8{};
+        }
+    };
+    if (g * G < nkb) load(g * G);
+    for (int jb = 0; jb < G; ++jb) {
+        const int j = g * G + jb;
+        if (j >= nkb) break;
+        // channel-major LDS stores (u fastest: conflict free)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vtl[(8 * ch + e) * TP + u] = vv[e];
+        for (int it = 0; it < 4; ++it) {
+            const int c = tid + 256 * it;
+            const int u = c & 63, ch = c >> 6;
+            const bool ok = j * KBLK + u < N;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vtl[(8 * ch + e) * TP + u] = vv[it][e];
             if (STATES) {
-                u16x8 kk = ok ? *(const u16x8*)(k + off) : u16x8{};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float f = bf2f(kk[e]);
+                    const float f = bf2f(kk[it][e]);
                     const float ph = ok ? (f > 0.f ? f + 1.f : __expf(f)) : 0.f;
                     __bf16 h, l;
                     split_bf16(ph, h, l);
@@ -74,6 +86,8 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
             }
         }
         __syncthreads();
+        // the next block's loads overlap this block's work
+        if (jb + 1 < G && j + 1 < nkb) load(j + 1);
         // V^T tile in the sparse kernel's key order: 128 rows x 8 chunks of 16 B
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
