@@ -47,9 +47,10 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) tot[dt] = f32x16{};
     // raw K and V of one key block in registers: lane (tid) holds token
-    // u = tid & 63, channels 8ch .. 8ch+7 for ch = (tid >> 6) + 4*it
-    u16x8 vv[4], kk[4];
-    auto load = [&](int j) {
+    // u = tid & 63, channels 8ch .. 8ch+7 for ch = (tid >> 6) + 4*it. Two sets,
+    // so the loads of blocks j+1 and j+2 are in flight while block j is worked.
+    u16x8 va[4], ka[4], vb[4], kb[4];
+    auto load = [&](int j, u16x8 (&vv)[4], u16x8 (&kk)[4]) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int c = tid + 256 * it;
@@ -61,10 +62,8 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
             if (STATES) kk[it] = ok ? *(const u16x8*)(k + off) : u16x8{};
         }
     };
-    if (g * G < nkb) load(g * G);
-    for (int jb = 0; jb < G; ++jb) {
+    auto block = [&](int jb, u16x8 (&vv)[4], u16x8 (&kk)[4]) {
         const int j = g * G + jb;
-        if (j >= nkb) break;
         // channel-major LDS stores (u fastest: conflict free)
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -86,8 +85,8 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
             }
         }
         __syncthreads();
-        // the next block's loads overlap this block's work
-        if (jb + 1 < G && j + 1 < nkb) load(j + 1);
+        // the registers are free again: block j+2 goes in flight
+        if (jb + 2 < G && j + 2 < nkb) load(j + 2, vv, kk);
         // V^T tile in the sparse kernel's key order: 128 rows x 8 chunks of 16 B
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -153,6 +152,13 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
             totz += accz;
         }
         __syncthreads();
+    };
+    const int nb = min(G, nkb - g * G);  // key blocks of this workgroup
+    if (nb > 0) load(g * G, va, ka);
+    if (nb > 1) load(g * G + 1, vb, kb);
+    for (int jb = 0; jb < nb; jb += 2) {
+        block(jb, va, ka);
+        if (jb + 1 < nb) block(jb + 1, vb, kb);
     }
     if (STATES) {
         float* prow = hpart + (bh * ngroups + g) * (int64_t)HS_ROW;
