@@ -52,7 +52,7 @@ ssa_status check_shape(const ssa_shape& s, Dims* d) {
     d->N = s.N;
     d->nqb = (s.N + QBLK - 1) / QBLK;
     d->nkb = (s.N + KBLK - 1) / KBLK;
-    d->nkbp = (d->nkb + 31) / 32 * 32;
+    d->nkbp = (d->nkb + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
     d->ngroups = (d->nkb + LIN_GROUP - 1) / LIN_GROUP;
     return SSA_OK;
 }

@@ -16,7 +16,8 @@ hipError_t launch_score_topk(const float* qbar, const float* kbarT, int ldk, int
                              int nkb, int keep, int32_t* kidx, uint8_t* mask, hipStream_t st);
 
 // linear.hip
-constexpr int LIN_GROUP = 16;  // key blocks per linear-states workgroup
+constexpr int LIN_GROUP = 16;    // key blocks per linear-states workgroup
+constexpr int GEMM_KALIGN = 32;  // the complement GEMM's key-block count is padded to this
 hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                                 uint16_t* vt, uint16_t* hs, float* hpart, float* htot,
                                 hipStream_t st);

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void htot_kernel(const float* __restrict__ hpa
 }
 
 // msel[bh][i][j] = 1 (bf16) if key block j is kept by query block i, else 0;
-// j runs to nkbp (a multiple of 32) so the GEMM reads whole K steps.
+// j runs to nkbp (a multiple of GEMM_KALIGN) so the GEMM reads whole K steps.
 __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ kidx, int keep,
                                                    int nqb, int nkbp, uint16_t* __restrict__ msel) {
     extern __shared__ int krow[];
@@ -219,16 +219,32 @@ __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ k
 // Complement GEMM: hnon[bh][i][n] = htot[bh][n] - sum_j msel[bh][i][j] * hs[bh][j][n]
 // (i < nqb query blocks, n < HS_ROW state entries, j < nkbp key blocks; msel
 // is 0/1). bf16 operands, fp32 accumulation.
-// Workgroup tile 128 (i) x 128 (n), K step 32, 2 x 2 waves of 64 x 64, each a
+// Workgroup tile 128 (i) x 128 (n), K step GTK, 2 x 2 waves of 64 x 64, each a
 // 2 x 2 grid of 32x32x16 bf16 MFMAs. Operand tiles arrive by LDS DMA into a
-// 3-stage ring:
-//   A [128 i][32 j]: 64-byte rows, 16-byte chunk c of row r at slot
-//     c ^ ((r >> 1) & 3) (conflict-free row reads);
-//   B [32 j][128 n]: 256-byte rows kept j-major as in memory, 8-byte unit u of
-//     row r at u ^ 4*(r & 3), read with transposing loads (lds_read_tr16) so
-//     each lane gets 4 consecutive j of one column n.
-constexpr int GTM = 128, GTN = 128, GTK = 32, GSTAGE = 3;
-constexpr int GA_BYTES = GTM * GTK * 2, GB_BYTES = GTK * GTN * 2;
+// GSTAGE-deep ring:
+//   A [128 i][GTK j]: rows of GTK*2 bytes, 16-byte chunk c of row r at slot
+//     c ^ aswz(r), so the 16 rows a 16-lane group reads hit 16 distinct
+//     bank groups;
+//   B [GTK j][128 n]: 256-byte rows kept j-major as in memory, 8-byte unit u of
+//     row r at u ^ 8*(r & 3), read with transposing loads (lds_read_tr16) so
+//     each lane gets 4 consecutive j of one column n; the 32 lanes of a half
+//     wave then hit 32 distinct 8-byte bank groups.
+#ifndef SSA_GEMM_TK
+#define SSA_GEMM_TK 32
+#endif
+#ifndef SSA_GEMM_STAGES
+#define SSA_GEMM_STAGES 3
+#endif
+constexpr int GTM = 128, GTN = 128, GTK = SSA_GEMM_TK, GSTAGE = SSA_GEMM_STAGES;
+static_assert(GTK == 32 || GTK == 64, "K step");
+static_assert(GEMM_KALIGN % GTK == 0, "padded key-block count must be whole K steps");
+constexpr int GA_ROW = GTK * 2, GA_CH = GA_ROW / 16;   // A row bytes, 16-byte chunks per row
+constexpr int GA_BYTES = GTM * GA_ROW, GB_BYTES = GTK * GTN * 2;
+constexpr int NDA = 32 * GA_ROW / 1024;                // A DMAs per wave (32 rows each wave)
+constexpr int NDB = GTK / 16;                          // B DMAs per wave (GTK/4 rows each wave)
+constexpr int GPD = GSTAGE - 1;                        // prefetch distance (K steps)
+
+__device__ __forceinline__ int aswz(int r) { return GA_CH == 4 ? (r >> 2) & 3 : (r >> 1) & 7; }
 
 __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     const uint16_t* __restrict__ msel, const uint16_t* __restrict__ hs, const float* __restrict__ htot,
@@ -248,15 +264,19 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
               h = lane >> 5, wm = wave >> 1, wn = wave & 1;
 
     // loop-invariant DMA lane offsets: wave w fills A rows 32w..32w+31 and
-    // B rows 8w..8w+7, two 1 KB blocks each
-    uint32_t aoff[2], boff[2];
+    // B rows (GTK/4)w .. +GTK/4, 1 KB per DMA
+    constexpr int ARD = 1024 / GA_ROW;  // A rows per DMA
+    uint32_t aoff[NDA], boff[NDB];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int ra = 32 * wave + 16 * p + (lane >> 2);
-        const int ca = (lane & 3) ^ ((ra >> 1) & 3);
+    for (int p = 0; p < NDA; ++p) {
+        const int ra = 32 * wave + ARD * p + lane / GA_CH;
+        const int ca = (lane % GA_CH) ^ aswz(ra);
         aoff[p] = (uint32_t)(min(i0 + ra, nqb - 1) * nkbp * 2 + ca * 16);
-        const int rb = 8 * wave + 4 * p + (lane >> 4);
-        const int cb = (lane & 15) ^ (2 * (rb & 3));
+    }
+#pragma unroll
+    for (int p = 0; p < NDB; ++p) {
+        const int rb = (GTK / 4) * wave + 4 * p + (lane >> 4);
+        const int cb = (lane & 15) ^ (4 * (rb & 3));
         boff[p] = (uint32_t)(rb * HS_ROW * 2 + cb * 16);
     }
     const uint16_t* abase = msel + (bh * nqb) * (int64_t)nkbp;
@@ -264,18 +284,26 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     auto issue = [&](int ks) {
         const int j0 = ks * GTK, st = ks % GSTAGE;
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-            dma16(abase + j0, aoff[p], lds_u32(As[st] + (32 * wave + 16 * p) * 64));
-        const bool ragged = j0 + GTK > nkb;  // rows past nkb: msel is 0 there, fetch row nkb-1
+        for (int p = 0; p < NDA; ++p)
+            dma16(abase + j0, aoff[p], lds_u32(As[st] + (32 * wave + ARD * p) * GA_ROW));
+        // Rows past nkb (msel is 0 there) are fetched from row nkb-1. In such a
+        // ragged step the offset is taken from the unshifted base with the
+        // absolute row clamped: a K step may start at or past nkb (the
+        // padded count is a multiple of GEMM_KALIGN), and a row relative to
+        // j0 would then be negative, which the unsigned 32-bit lane offset of
+        // the DMA cannot express.
+        const bool ragged = j0 + GTK > nkb;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            uint32_t off = boff[p];
+        for (int p = 0; p < NDB; ++p) {
+            const uint32_t lds = lds_u32(Bs[st] + ((GTK / 4) * wave + 4 * p) * 256);
             if (ragged) {
-                const int rb = 8 * wave + 4 * p + (lane >> 4);
-                const int cb = (lane & 15) ^ (2 * (rb & 3));
-                off = (uint32_t)(min(rb, nkb - 1 - j0) * HS_ROW * 2 + cb * 16);
+                const int rb = (GTK / 4) * wave + 4 * p + (lane >> 4);
+                const int cb = (lane & 15) ^ (4 * (rb & 3));
+                const int r = min(j0 + rb, nkb - 1);
+                dma16(bbase, (uint32_t)(r * HS_ROW * 2 + cb * 16), lds);
+            } else {
+                dma16(bbase + (int64_t)j0 * HS_ROW, boff[p], lds);
             }
-            dma16(bbase + (int64_t)j0 * HS_ROW, off, lds_u32(Bs[st] + (8 * wave + 4 * p) * 256));
         }
     };
 
@@ -286,22 +314,22 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
         for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
     const int nks = nkbp / GTK;
-    issue(0);
-    if (nks > 1) issue(1);
-    if (nks > 1) wait_vm<4>(); else wait_vm<0>();
+    // prologue: steps 0 .. GPD-1 in flight, step 0 landed
+    for (int ks = 0; ks < GPD && ks < nks; ++ks) issue(ks);
+    if (GPD > 1 && nks > 1) wait_vm<(GPD - 1) * (NDA + NDB)>(); else wait_vm<0>();
     __syncthreads();
     for (int ks = 0; ks < nks; ++ks) {
-        if (ks + 2 < nks) issue(ks + 2);
+        if (ks + GPD < nks) issue(ks + GPD);
         const uint8_t* A = As[ks % GSTAGE];
         const uint8_t* B = Bs[ks % GSTAGE];
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
+        for (int kc = 0; kc < GTK / 16; ++kc) {
             bf16x8 af[2], bfr[2];
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
                 const int row = 64 * wm + 32 * a + l32;
-                const int slot = (2 * kc + h) ^ ((row >> 1) & 3);
-                af[a] = *(const bf16x8*)(A + row * 64 + slot * 16);
+                const int slot = (2 * kc + h) ^ aswz(row);
+                af[a] = *(const bf16x8*)(A + row * GA_ROW + slot * 16);
             }
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
@@ -310,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int row = 16 * kc + 8 * h + 4 * t + ((lane & 15) >> 2);
-                    const int unit = (col >> 2) ^ (4 * (row & 3));
+                    const int unit = (col >> 2) ^ (8 * (row & 3));
                     part[t] = lds_read_tr16(B + row * 256 + unit * 8);
                 }
                 // k-slots 0-3 from the first read, 4-7 from the second (whole dwords)
@@ -323,7 +351,8 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
 #pragma unroll
                 for (int b = 0; b < 2; ++b) acc[a][b] = mfma_bf16_32x32x16(af[a], bfr[b], acc[a][b]);
         }
-        if (ks + 2 < nks) wait_vm<4>(); else wait_vm<0>();
+        // step ks+1 must land; later steps may stay in flight
+        if (GPD > 1 && ks + GPD < nks) wait_vm<(GPD - 1) * (NDA + NDB)>(); else wait_vm<0>();
         __syncthreads();
     }
 #pragma unroll
@@ -362,7 +391,7 @@ hipError_t launch_vt_only(const uint16_t* v, int64_t BH, int N, uint16_t* vt, hi
 hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, const float* htot,
                              int64_t BH, int N, uint16_t* msel, float* hnon, hipStream_t st) {
     const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
-    const int nkbp = (nkb + 31) / 32 * 32;
+    const int nkbp = (nkb + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
     hipLaunchKernelGGL(msel_kernel, dim3(nqb, BH), dim3(256), keep * sizeof(int), st, kidx, keep, nqb,
                        nkbp, msel);
     const int64_t total = BH * (HS_ROW / 128) * ((nqb + 127) / 128);
