@@ -277,13 +277,13 @@ __device__ __forceinline__ void tile_pv(const uint8_t* vs, const bf16x8 (&pb)[G]
         }
 }
 
-// One pipeline step for a 32-row group (G == 1), written in issue order with
-// scheduling fences between the pieces: the 8 K fragment reads; QK(next)
-// MFMAs, each followed by one V fragment read; PV(current) MFMAs, the first 8
-// each followed by the next V read (a fragment is read ~8 MFMAs before use)
-// and, from the third on, each followed by one slice of the fresh tile's
-// softmax (2 keys: convert, scale, exp2, round to bf16, sum), which runs on
-// the VALU while the MFMA executes.
+// One pipeline step, written in issue order with scheduling fences between
+// the pieces: the 8 K fragment reads; QK(next) MFMAs, alternating between the
+// two independent 32-key accumulators, each followed by one V fragment read;
+// PV(current) MFMAs, the first 8 each followed by the next V read (a fragment
+// is read ~8 MFMAs before use) and, from the third on, each followed by one
+// slice of the fresh tile's softmax (2 keys: convert, scale, exp2, round to
+// bf16, sum), which runs on the VALU while the MFMA executes.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ void softmax_slice(int p, const i32x16 (&s)[2], float c, float nm,
@@ -299,10 +299,10 @@ __device__ __forceinline__ void softmax_slice(int p, const i32x16 (&s)[2], float
 }
 
 __device__ __forceinline__ void pipeline_step(const uint8_t* ks, const uint8_t* vs,
-                                              const i32x4 (&qop)[4], int l32, int hi,
-                                              const bf16x8 (&pb)[4], f32x16 (&o)[4], float c,
-                                              float nm, i32x16 (&s)[2], bf16x8 (&pn)[4],
-                                              float& lsum) {
+                                              const i32x4 (&qop)[G][4], int l32, int hi,
+                                              const bf16x8 (&pb)[G][4], f32x16 (&o)[G][4], float c,
+                                              const float (&nm)[G], i32x16 (&s)[G][2],
+                                              bf16x8 (&pn)[G][4], float (&lsum)[G]) {
     const int sl = swz(l32);
     auto vread = [&](int i) {  // fragment i = 4*cc + dt of V^T
         const int cc = i >> 2, dt = i & 3;
@@ -317,27 +317,38 @@ __device__ __forceinline__ void pipeline_step(const uint8_t* ks, const uint8_t* 
         ka[2 * c4 + 1] = *(const i32x4*)(ks + (32 + l32) * 128 + slot);
     }
     fence();
-    s[0] = s[1] = i32x16{};
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g][0] = s[g][1] = i32x16{};
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            s[h] = mfma_i8_32x32x32(ka[2 * c4 + h], qop[c4], s[h]);
+#pragma unroll
+            for (int g = 0; g < G; ++g) s[g][h] = mfma_i8_32x32x32(ka[2 * c4 + h], qop[g][c4], s[g][h]);
             va[2 * c4 + h] = vread(2 * c4 + h);
             fence();
         }
     }
-    float acc = 0.f;
+    float acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        o[i & 3] = mfma_bf16_32x32x16(va[i], pb[i >> 2], o[i & 3]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) o[g][i & 3] = mfma_bf16_32x32x16(va[i], pb[g][i >> 2], o[g][i & 3]);
         if (i < 8) va[i + 8] = vread(i + 8);
-        if (i >= 2) softmax_slice(i - 2, s, c, nm, pn, acc);
+        if (i >= 2) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) softmax_slice(i - 2, s[g], c, nm[g], pn[g], acc[g]);
+        }
         fence();
     }
-    softmax_slice(14, s, c, nm, pn, acc);
-    softmax_slice(15, s, c, nm, pn, acc);
-    lsum = acc;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        softmax_slice(14, s[g], c, nm[g], pn[g], acc[g]);
+        softmax_slice(15, s[g], c, nm[g], pn[g], acc[g]);
+        lsum[g] = acc[g];
+    }
 }
 
 template <bool LIN>
@@ -427,10 +438,13 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
             i32x16 s[G][2];
             bf16x8 pn[G][4];
             float lsum[G];
-            static_assert(G == 1, "the scheduled pipeline step handles one 32-row group");
-            pipeline_step(ks[(R + 1) % NSTAGE], vs[R], qop[0], l32, hi, pb[0], o[0], c, -m_run[0],
-                          s[0], pn[0], lsum[0]);
-            const bool trig = !(lsum[0] <= RESCALE_TRIGGER);
+            float nm[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) nm[g] = -m_run[g];
+            pipeline_step(ks[(R + 1) % NSTAGE], vs[R], qop, l32, hi, pb, o, c, nm, s, pn, lsum);
+            bool trig = false;
+#pragma unroll
+            for (int g = 0; g < G; ++g) trig = trig || !(lsum[g] <= RESCALE_TRIGGER);
             // keep the common-case P in this block, above the rare branch
 #pragma unroll
             for (int g = 0; g < G; ++g)
