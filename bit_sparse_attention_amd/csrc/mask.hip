@@ -6,8 +6,8 @@
 // every key block by the dot product of their mean-pooled rows (an exact fmaf
 // chain over the 128 channels) and keeps the best `keep` under (score
 // descending, key block ascending). Selection is an exact 4-pass MSB radix
-// select on order-preserving 32-bit keys, so the result is unique and
-// bit-identical to a sort.
+// select on order-preserving 32-bit keys, one wave per query block, so the
+// result is unique and bit-identical to a sort.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -19,24 +19,95 @@ __device__ __forceinline__ uint32_t order_key(float s) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive scan over a 256-thread workgroup. `wsum` holds 4 ints of LDS.
-__device__ __forceinline__ int block_incl_scan(int v, int* wsum) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Inclusive and exclusive prefix sums across one wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_up(v, o, 64);
+        const int t = __shfl_up(v, o, 64);
         if (lane >= o) v += t;
     }
-    __syncthreads();
-    if (lane == 63) wsum[w] = v;
-    __syncthreads();
-    int add = 0;
-    for (int u = 0; u < w; ++u) add += wsum[u];
-    return v + add;
+    return v;
 }
 
-// One workgroup scores R query blocks of one head against every key block and
-// selects, per query block, the `keep` best key blocks.
+// Selection of one score row by one wave: the `keep` best key blocks under
+// (score descending, j ascending), written ascending to krow (and the 0/1
+// mask row). An exact 4-pass MSB radix select finds the keep-th largest key T
+// and how many keys equal to T are kept (the lowest j first).
+__device__ __forceinline__ void wave_select_row(const float* __restrict__ s, int nkb, int keep,
+                                                int* __restrict__ hist, int32_t* __restrict__ krow,
+                                                uint8_t* __restrict__ mrow) {
+    const int lane = threadIdx.x & 63;
+    uint32_t prefix = 0u, pmask = 0u;
+    int rem = keep;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0;
+        __builtin_amdgcn_wave_barrier();
+        for (int j = lane; j < nkb; j += 64) {
+            const uint32_t key = order_key(s[j]);
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // lane l holds digits 255-4l .. 252-4l (descending); counts of digits
+        // above its first one come from the scan
+        int hb[4], hsum = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            hb[b] = hist[255 - 4 * lane - b];
+            hsum += hb[b];
+        }
+        const int incl = wave_incl_scan(hsum);
+        int above = incl - hsum;  // keys with a digit greater than 255 - 4*lane
+        int digit = -1, nrem = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (digit < 0 && above + hb[b] >= rem) {
+                digit = 255 - 4 * lane - b;
+                nrem = rem - above;
+            }
+            above += hb[b];
+        }
+        // exactly one lane found the digit: the one where the count crosses rem
+        const uint64_t who = __builtin_amdgcn_ballot_w64(digit >= 0 && (incl - hsum) < rem);
+        const int src = (int)__builtin_ctzll(who);
+        digit = __shfl(digit, src, 64);
+        nrem = __shfl(nrem, src, 64);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 255u << shift;
+        rem = nrem;
+        __builtin_amdgcn_wave_barrier();
+    }
+    const uint32_t T = prefix;  // keep-th largest key; keep `rem` of the keys equal to T
+    // emit: lane l owns the contiguous range [l*chunk, (l+1)*chunk) of j
+    const int chunk = (nkb + 63) >> 6;
+    const int j0 = lane * chunk, j1 = min(nkb, j0 + chunk);
+    int neq = 0;
+    for (int j = j0; j < j1; ++j) neq += order_key(s[j]) == T ? 1 : 0;
+    int eq_rank = wave_incl_scan(neq) - neq;  // keys equal to T before j0
+    int nsel = 0;
+    for (int j = j0; j < j1; ++j) {
+        const uint32_t key = order_key(s[j]);
+        const bool eq = key == T;
+        nsel += (key > T || (eq && eq_rank < rem)) ? 1 : 0;
+        eq_rank += eq ? 1 : 0;
+    }
+    int out = wave_incl_scan(nsel) - nsel;
+    eq_rank = wave_incl_scan(neq) - neq;
+    for (int j = j0; j < j1; ++j) {
+        const uint32_t key = order_key(s[j]);
+        const bool eq = key == T;
+        const bool sel = key > T || (eq && eq_rank < rem);
+        eq_rank += eq ? 1 : 0;
+        if (sel) krow[out++] = j;
+        if (mrow) mrow[j] = (uint8_t)sel;
+    }
+}
+
+// One workgroup scores R query blocks of one head against every key block (so
+// each pooled-K value read feeds R exact fmaf chains), then each wave selects
+// for its rows.
 // kbarT: [BH][128][ldk] pooled K means (transposed); qbar: [BH][nqb][128].
 template <int R>
 __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict__ qbar,
@@ -47,10 +118,8 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict
     extern __shared__ float dyn[];
     float* sc = dyn;                   // [R][nkb]
     __shared__ float qs[R][HD];
-    __shared__ int hist[256];
-    __shared__ int wsum[4];
-    __shared__ int sel_digit, sel_rem;
-    const int tid = threadIdx.x;
+    __shared__ int hist[4][256];
+    const int tid = threadIdx.x, wave = tid >> 6;
     const int64_t bh = blockIdx.y;
     const int i0 = blockIdx.x * R;
     for (int idx = tid; idx < R * HD; idx += 256) {
@@ -73,59 +142,12 @@ __global__ __launch_bounds__(256) void score_topk_kernel(const float* __restrict
         for (int r = 0; r < R; ++r) sc[r * nkb + j] = acc[r];
     }
     __syncthreads();
-
-    for (int r = 0; r < R; ++r) {
+    for (int r = wave; r < R; r += 4) {
         const int i = i0 + r;
-        if (i >= nqb) break;  // uniform across the workgroup
-        const float* s = sc + r * nkb;
-        // ---- radix select of the keep-th largest key
-        uint32_t prefix = 0u, pmask = 0u;
-        int rem = keep;
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            hist[tid] = 0;
-            __syncthreads();
-            for (int j = tid; j < nkb; j += 256) {
-                const uint32_t key = order_key(s[j]);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-            }
-            __syncthreads();
-            // suffix counts from the top digit down: thread t looks at digit 255-t
-            const int h = hist[255 - tid];
-            const int cum = block_incl_scan(h, wsum);  // count of digits >= 255-tid
-            if (cum >= rem && cum - h < rem) {
-                sel_digit = 255 - tid;
-                sel_rem = rem - (cum - h);
-            }
-            __syncthreads();
-            prefix |= (uint32_t)sel_digit << shift;
-            pmask |= 255u << shift;
-            rem = sel_rem;
-            __syncthreads();
-        }
-        const uint32_t T = prefix;  // keep-th largest key; take `rem` of the keys equal to T
-        // ---- emit kept blocks in ascending j
-        int eq_base = 0, out_base = 0;
-        int32_t* krow = kidx + (bh * nqb + i) * (int64_t)keep;
-        uint8_t* mrow = mask ? mask + (bh * nqb + i) * (int64_t)nkb : nullptr;
-        for (int j0 = 0; j0 < nkb; j0 += 256) {
-            const int j = j0 + tid;
-            uint32_t key = 0u;
-            bool inb = j < nkb;
-            if (inb) key = order_key(s[j]);
-            const int eq = (inb && key == T) ? 1 : 0;
-            const int eq_incl = block_incl_scan(eq, wsum);
-            const int eq_chunk = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-            const int rank_eq = eq_base + eq_incl - eq;  // equal keys before j
-            const int sel = (inb && (key > T || (eq && rank_eq < rem))) ? 1 : 0;
-            const int sel_incl = block_incl_scan(sel, wsum);
-            const int sel_chunk = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-            if (sel) krow[out_base + sel_incl - 1] = j;
-            if (mrow && inb) mrow[j] = (uint8_t)sel;
-            out_base += sel_chunk;
-            eq_base += eq_chunk;
-        }
-        __syncthreads();
+        if (i >= nqb) break;  // uniform across the wave
+        wave_select_row(sc + r * nkb, nkb, keep, hist[wave],
+                        kidx + (bh * nqb + i) * (int64_t)keep,
+                        mask ? mask + (bh * nqb + i) * (int64_t)nkb : nullptr);
     }
 }
 
@@ -133,6 +155,8 @@ hipError_t launch_score_topk(const float* qbar, const float* kbarT, int ldk, int
                              int nkb, int keep, int32_t* kidx, uint8_t* mask, hipStream_t st) {
     // largest row group whose scores fit in 48 KB of LDS (nkb <= 8192: SSA_MAX_N)
     const size_t per_row = (size_t)nkb * sizeof(float);
+    // (eight rows per workgroup would halve the pooled-K reads, but measured
+    // about three times slower on the 1182-block rows: kept at four at most)
     if (4 * per_row <= 48 * 1024) {
         hipLaunchKernelGGL((score_topk_kernel<4>), dim3((nqb + 3) / 4, BH), dim3(256), 4 * per_row,
                            st, qbar, kbarT, ldk, nqb, nkb, keep, kidx, mask);
