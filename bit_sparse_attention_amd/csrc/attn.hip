@@ -351,10 +351,23 @@ __device__ __forceinline__ void pipeline_step(const uint8_t* ks, const uint8_t* 
     }
 }
 
+// Complement state staged in LDS for the linear epilogue: row r (0..127: h^T
+// row e; 128: z) of 128 floats, 16-byte unit u at unit u ^ (r & 31).
+constexpr int HSTAGE_DMAS = (HD + 2) / 2;                   // 1 KB DMAs: rows 0..129
+constexpr int HSTAGE_BYTES = HSTAGE_DMAS * 1024;
+__device__ __forceinline__ f32x4 hstage_read(const uint8_t* smem, int row, int pos) {
+    const int unit = pos >> 2;
+    return *(const f32x4*)(smem + row * 512 + ((unit ^ (row & 31)) * 16));
+}
+
 template <bool LIN>
 __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t ks[NSTAGE][KTILE];
-    __shared__ __attribute__((aligned(1024))) uint8_t vs[NSTAGE][VTILE];
+    // K and V rings; after the main loop the same bytes hold this query
+    // block's complement state for the linear epilogue
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * (KTILE + VTILE)];
+    static_assert(NSTAGE * (KTILE + VTILE) >= HSTAGE_BYTES, "state staging fits the rings");
+    uint8_t(*ks)[KTILE] = reinterpret_cast<uint8_t(*)[KTILE]>(smem);
+    uint8_t(*vs)[VTILE] = reinterpret_cast<uint8_t(*)[VTILE]>(smem + NSTAGE * KTILE);
     const int64_t total = a.BH * a.nqb;
     const int64_t item = blockIdx.x;
     if (item >= total) return;
@@ -496,6 +509,22 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
         const float lt = l_run[g] + __shfl_xor(l_run[g], 32, 64);
         inv[g] = a.do_sparse ? 1.0f / lt : 0.f;
     }
+    if (LIN) {
+        // Stage Hnon_i (128 rows of h^T, then z: 129 rows of 512 bytes) in LDS
+        // with one batch of DMAs. The 16-byte unit u of row r sits at unit
+        // u ^ (r & 31), so the 16 rows a 16-lane group reads land in distinct
+        // banks. DMA p fills rows 2p, 2p+1; the last one's second half
+        // re-fetches the z row into the spare bytes past the state.
+        __syncthreads();  // every wave is done with the rings
+        const float* hp = a.hnon + (bh * a.nqb + i) * (int64_t)HS_ROW;
+        for (int p = wave; p < HSTAGE_DMAS; p += WAVES) {
+            const int row = min(2 * p + (lane >> 5), HD);
+            const uint32_t goff = row * 512 + ((lane & 31) ^ (row & 31)) * 16;
+            dma16(hp, goff, __builtin_amdgcn_readfirstlane(lds_u32(smem) + 1024 * p));
+        }
+        wait_vm<0>();
+        __syncthreads();
+    }
 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -505,7 +534,6 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
         for (int dt = 0; dt < 4; ++dt) ol[dt] = f32x16{};
         float linv = 0.f;
         if (LIN) {
-            const float* hp = a.hnon + (bh * a.nqb + i) * (int64_t)HS_ROW;
             const bool ok = t < N;
             const uint16_t* qr = a.q + (bh * N + (ok ? t : 0)) * HD;
             float den = 0.f;
@@ -517,8 +545,8 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
                 const u16x4 q0 = ok ? *(const u16x4*)(qr + 16 * cd + 4 * hi) : u16x4{};
                 const u16x4 q1 = ok ? *(const u16x4*)(qr + 16 * cd + 8 + 4 * hi) : u16x4{};
                 const u16x8 qv = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-                const f32x4 z0 = *(const f32x4*)(hp + HD * HD + d0);
-                const f32x4 z1 = *(const f32x4*)(hp + HD * HD + d0 + 4);
+                const f32x4 z0 = hstage_read(smem, HD, d0);
+                const f32x4 z1 = hstage_read(smem, HD, d0 + 4);
                 bf16x8 bqh, bql;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -532,8 +560,8 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
                 }
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
-                    const float* hr = hp + (32 * dt + l32) * HD + d0;
-                    const f32x4 h0 = *(const f32x4*)hr, h1 = *(const f32x4*)(hr + 4);
+                    const f32x4 h0 = hstage_read(smem, 32 * dt + l32, d0);
+                    const f32x4 h1 = hstage_read(smem, 32 * dt + l32, d0 + 4);
                     bf16x8 ah, al;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
