@@ -352,7 +352,9 @@ __device__ __forceinline__ void pipeline_step(const uint8_t* ks, const uint8_t* 
 }
 
 // Complement state staged in LDS for the linear epilogue: row r (0..127: h^T
-// row e; 128: z) of 128 floats, 16-byte unit u at unit u ^ (r & 31).
+// row e; 128: z) of 128 floats, 16-byte unit u at unit u ^ (r & 31). The h^T
+// rows are then split in place: each unit holds its four values as bf16 high
+// parts followed by the bf16 rests.
 constexpr int HSTAGE_DMAS = (HD + 2) / 2;                   // 1 KB DMAs: rows 0..129
 constexpr int HSTAGE_BYTES = HSTAGE_DMAS * 1024;
 __device__ __forceinline__ f32x4 hstage_read(const uint8_t* smem, int row, int pos) {
@@ -524,6 +526,16 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
         }
         wait_vm<0>();
         __syncthreads();
+        // split the h^T rows once for all waves: each 16-byte unit of four fp32
+        // becomes their bf16 high parts, then the bf16 rests (the z row stays)
+        for (int u = tid; u < HD * 32; u += ATTN_THREADS) {
+            const f32x4 x = *(const f32x4*)(smem + u * 16);
+            __bf16 h[4], l[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split_bf16(x[e], h[e], l[e]);
+            *(bf16x8*)(smem + u * 16) = bf16x8{h[0], h[1], h[2], h[3], l[0], l[1], l[2], l[3]};
+        }
+        __syncthreads();
     }
 
 #pragma unroll
@@ -560,16 +572,11 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
                 }
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
-                    const f32x4 h0 = hstage_read(smem, 32 * dt + l32, d0);
-                    const f32x4 h1 = hstage_read(smem, 32 * dt + l32, d0 + 4);
-                    bf16x8 ah, al;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        __bf16 x, y;
-                        split_bf16(e < 4 ? h0[e] : h1[e - 4], x, y);
-                        ah[e] = x;
-                        al[e] = y;
-                    }
+                    // two split units: high parts in dwords 0-1, rests in 2-3
+                    const u32x4 w0 = __builtin_bit_cast(u32x4, hstage_read(smem, 32 * dt + l32, d0));
+                    const u32x4 w1 = __builtin_bit_cast(u32x4, hstage_read(smem, 32 * dt + l32, d0 + 4));
+                    const bf16x8 ah = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+                    const bf16x8 al = __builtin_bit_cast(bf16x8, u32x4{w0[2], w0[3], w1[2], w1[3]});
                     ol[dt] = mfma_bf16_32x32x16(ah, bqh, ol[dt]);
                     ol[dt] = mfma_bf16_32x32x16(ah, bql, ol[dt]);
                     ol[dt] = mfma_bf16_32x32x16(al, bqh, ol[dt]);
