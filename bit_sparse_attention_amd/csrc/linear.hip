@@ -9,6 +9,8 @@
 // NOT keep. They are formed as H_i = H_total - sum_{j kept} h_j: H_total in
 // fp32, the kept-block sum as a dense 0/1 x bf16 matrix-core GEMM, so the bf16
 // rounding of h_j only touches the kept ~10% of the blocks.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -249,8 +251,9 @@ __device__ __forceinline__ int aswz(int r) { return GA_CH == 4 ? (r >> 2) & 3 : 
 __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     const uint16_t* __restrict__ msel, const uint16_t* __restrict__ hs, const float* __restrict__ htot,
     int64_t BH, int nqb, int nkb, int nkbp, float* __restrict__ hnon) {
-    __shared__ __attribute__((aligned(1024))) uint8_t As[GSTAGE][GA_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t Bs[GSTAGE][GB_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[GSTAGE * (GA_BYTES + GB_BYTES)];
+    uint8_t(*As)[GA_BYTES] = reinterpret_cast<uint8_t(*)[GA_BYTES]>(smem);
+    uint8_t(*Bs)[GB_BYTES] = reinterpret_cast<uint8_t(*)[GB_BYTES]>(smem + GSTAGE * GA_BYTES);
     const int nnt = HS_ROW / GTN, nmt = (nqb + GTM - 1) / GTM;
     const int64_t total = BH * nnt * nmt;
     const int64_t item = xcd_item(blockIdx.x, total);  // m fastest: B tiles shared in L2
@@ -281,8 +284,9 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     }
     const uint16_t* abase = msel + (bh * nqb) * (int64_t)nkbp;
     const uint16_t* bbase = hs + (bh * nkb) * (int64_t)HS_ROW + n0;
-    auto issue = [&](int ks) {
-        const int j0 = ks * GTK, st = ks % GSTAGE;
+    // K step ks into ring stage st (a compile-time constant in the main loop)
+    auto issue = [&](int ks, int st) {
+        const int j0 = ks * GTK;
 #pragma unroll
         for (int p = 0; p < NDA; ++p)
             dma16(abase + j0, aoff[p], lds_u32(As[st] + (32 * wave + ARD * p) * GA_ROW));
@@ -315,13 +319,15 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
 
     const int nks = nkbp / GTK;
     // prologue: steps 0 .. GPD-1 in flight, step 0 landed
-    for (int ks = 0; ks < GPD && ks < nks; ++ks) issue(ks);
+    for (int ks = 0; ks < GPD && ks < nks; ++ks) issue(ks, ks);
     if (GPD > 1 && nks > 1) wait_vm<(GPD - 1) * (NDA + NDB)>(); else wait_vm<0>();
     __syncthreads();
-    for (int ks = 0; ks < nks; ++ks) {
-        if (ks + GPD < nks) issue(ks + GPD);
-        const uint8_t* A = As[ks % GSTAGE];
-        const uint8_t* B = Bs[ks % GSTAGE];
+    // one K step from ring stage R (compile-time: LDS addresses are immediates)
+    auto kstep = [&](int ks, auto stage) {
+        constexpr int R = decltype(stage)::value;
+        if (ks + GPD < nks) issue(ks + GPD, (R + GPD) % GSTAGE);
+        const uint8_t* A = As[R];
+        const uint8_t* B = Bs[R];
 #pragma unroll
         for (int kc = 0; kc < GTK / 16; ++kc) {
             bf16x8 af[2], bfr[2];
@@ -354,7 +360,22 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
         // step ks+1 must land; later steps may stay in flight
         if (GPD > 1 && ks + GPD < nks) wait_vm<(GPD - 1) * (NDA + NDB)>(); else wait_vm<0>();
         __syncthreads();
+    };
+    static_assert(GSTAGE >= 2 && GSTAGE <= 4, "the K loop is unrolled by the ring depth");
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, (GSTAGE > 2 ? 2 : 0)>;
+    using S3 = std::integral_constant<int, (GSTAGE > 3 ? 3 : 0)>;
+    int ks = 0;
+    for (; ks + GSTAGE <= nks; ks += GSTAGE) {
+        kstep(ks, S0{});
+        kstep(ks + 1, S1{});
+        if (GSTAGE > 2) kstep(ks + 2, S2{});
+        if (GSTAGE > 3) kstep(ks + 3, S3{});
     }
+    if (ks < nks) kstep(ks++, S0{});
+    if (ks < nks) kstep(ks++, S1{});
+    if (GSTAGE > 3 && ks < nks) kstep(ks, S2{});
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
