@@ -192,8 +192,18 @@ __global__ __launch_bounds__(256) void htot_kernel(const float* __restrict__ hpa
     const int n = blockIdx.x * 256 + threadIdx.x;
     const int64_t bh = blockIdx.y;
     if (n >= HS_ROW) return;
+    // loads in batches of 16 so they are in flight together; the adds stay in
+    // group order
+    const float* p = hpart + bh * ngroups * (int64_t)HS_ROW + n;
     float s = 0.f;
-    for (int g = 0; g < ngroups; ++g) s += hpart[(bh * ngroups + g) * HS_ROW + n];
+    for (int g0 = 0; g0 < ngroups; g0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = g0 + u < ngroups ? p[(int64_t)(g0 + u) * HS_ROW] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            if (g0 + u < ngroups) s += v[u];
+    }
     htot[bh * HS_ROW + n] = s;
 }
 
@@ -201,21 +211,14 @@ __global__ __launch_bounds__(256) void htot_kernel(const float* __restrict__ hpa
 // j runs to nkbp (a multiple of GEMM_KALIGN) so the GEMM reads whole K steps.
 __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ kidx, int keep,
                                                    int nqb, int nkbp, uint16_t* __restrict__ msel) {
-    extern __shared__ int krow[];
     const int64_t bh = blockIdx.y;
     const int i = blockIdx.x;
     const int32_t* src = kidx + (bh * nqb + i) * (int64_t)keep;
-    for (int a = threadIdx.x; a < keep; a += 256) krow[a] = src[a];
-    __syncthreads();
     uint16_t* dst = msel + (bh * nqb + i) * (int64_t)nkbp;
-    for (int j = threadIdx.x; j < nkbp; j += 256) {
-        int lo = 0, hi = keep;  // kept blocks are ascending
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (krow[mid] < j) lo = mid + 1; else hi = mid;
-        }
-        dst[j] = (lo < keep && krow[lo] == j) ? (uint16_t)0x3F80 : (uint16_t)0;
-    }
+    // zero the row, then set the kept blocks (indices clamped into the row)
+    for (int j = threadIdx.x; j < nkbp; j += 256) dst[j] = 0;
+    __syncthreads();
+    for (int a = threadIdx.x; a < keep; a += 256) dst[min(max(src[a], 0), nkbp - 1)] = 0x3F80;
 }
 
 // Complement GEMM: hnon[bh][i][n] = htot[bh][n] - sum_j msel[bh][i][j] * hs[bh][j][n]
@@ -413,7 +416,7 @@ hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, 
                              int64_t BH, int N, uint16_t* msel, float* hnon, hipStream_t st) {
     const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
     const int nkbp = (nkb + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
-    hipLaunchKernelGGL(msel_kernel, dim3(nqb, BH), dim3(256), keep * sizeof(int), st, kidx, keep, nqb,
+    hipLaunchKernelGGL(msel_kernel, dim3(nqb, BH), dim3(256), 0, st, kidx, keep, nqb,
                        nkbp, msel);
     const int64_t total = BH * (HS_ROW / 128) * ((nqb + 127) / 128);
     const int64_t grid = (total + 7) / 8 * 8;

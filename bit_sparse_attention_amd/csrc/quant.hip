@@ -78,16 +78,17 @@ __global__ __launch_bounds__(128) void kmean_final_kernel(const float* __restric
     const int d = threadIdx.x;
     const int64_t bh = blockIdx.x;
     const float* p = part + bh * nkb * HD + d;
+    // loads in batches of 64 so they are in flight together; the adds stay in
+    // block order (only existing blocks are added: a -0.0 total keeps its sign)
     float tot = 0.f;
-    int j = 0;
-    for (; j + 8 <= nkb; j += 8) {
-        float v[8];
+    for (int j0 = 0; j0 < nkb; j0 += 64) {
+        float v[64];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(j + u) * HD];
+        for (int u = 0; u < 64; ++u) v[u] = j0 + u < nkb ? p[(int64_t)(j0 + u) * HD] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) tot += v[u];
+        for (int u = 0; u < 64; ++u)
+            if (j0 + u < nkb) tot += v[u];
     }
-    for (; j < nkb; ++j) tot += p[(int64_t)j * HD];
     mu[bh * HD + d] = tot / (float)N;
 }
 
