@@ -144,7 +144,7 @@ AttnWs ws_attn(const Dims& d, bool linear) {
         w.htot = off;
         off += align256((size_t)d.BH * HS_ROW * 4);
         w.msel = off;
-        off += align256((size_t)d.BH * d.nqb * d.nkbp * 2);
+        off += align256(msel_bytes(d.BH, d.nqb, d.nkbp));
         w.hnon = off;
         off += align256((size_t)d.BH * d.nqb * HS_ROW * 4);
     }
@@ -351,7 +351,7 @@ ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
         uint16_t* hs = (uint16_t*)(base + w.hs);
         float* hpart = (float*)(base + w.hpart);
         float* htot = (float*)(base + w.htot);
-        uint16_t* msel = (uint16_t*)(base + w.msel);
+        uint32_t* msel = (uint32_t*)(base + w.msel);
         hnon = (float*)(base + w.hnon);
         e = launch_linear_states(k, v, d.BH, (int)d.N, vt, hs, hpart, htot, st);
         if (e == hipSuccess)

@@ -22,8 +22,10 @@ hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH
                                 uint16_t* vt, uint16_t* hs, float* hpart, float* htot,
                                 hipStream_t st);
 hipError_t launch_vt_only(const uint16_t* v, int64_t BH, int N, uint16_t* vt, hipStream_t st);
+// bytes of the complement GEMM's selection rows (msel) for nkbp padded key blocks
+size_t msel_bytes(int64_t BH, int64_t nqb, int64_t nkbp);
 hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, const float* htot,
-                             int64_t BH, int N, uint16_t* msel, float* hnon, hipStream_t st);
+                             int64_t BH, int N, uint32_t* msel, float* hnon, hipStream_t st);
 
 // attn.hip
 struct AttnArgs {

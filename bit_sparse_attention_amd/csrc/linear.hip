@@ -11,6 +11,7 @@
 // rounding of h_j only touches the kept ~10% of the blocks.
 #include <type_traits>
 
+#include "../../include/ssa.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -207,188 +208,262 @@ __global__ __launch_bounds__(256) void htot_kernel(const float* __restrict__ hpa
     htot[bh * HS_ROW + n] = s;
 }
 
-// msel[bh][i][j] = 1 (bf16) if key block j is kept by query block i, else 0;
-// j runs to nkbp (a multiple of GEMM_KALIGN) so the GEMM reads whole K steps.
-__global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ kidx, int keep,
-                                                   int nqb, int nkbp, uint16_t* __restrict__ msel) {
-    const int64_t bh = blockIdx.y;
-    const int i = blockIdx.x;
-    const int32_t* src = kidx + (bh * nqb + i) * (int64_t)keep;
-    uint16_t* dst = msel + (bh * nqb + i) * (int64_t)nkbp;
-    // zero the row, then set the kept blocks (indices clamped into the row)
-    for (int j = threadIdx.x; j < nkbp; j += 256) dst[j] = 0;
-    __syncthreads();
-    for (int a = threadIdx.x; a < keep; a += 256) dst[min(max(src[a], 0), nkbp - 1)] = 0x3F80;
+// ---- the 0/1 selection matrix, as offsets into a bf16 expansion table ------
+// The complement GEMM multiplies the state stack by each query block's 0/1
+// row over the key blocks. That row is kept as bits: bit s of byte b is key
+// block 8b + s. A byte becomes one MFMA operand fragment (eight bf16 0/1
+// values) by a 16-byte read of a 256-entry table in LDS, so the selection
+// costs 1/16 of its bf16 size in memory and in the GEMM's load path.
+//
+// Table slot of entry e: 16*(e>>4) + ((e & 15) ^ h(e>>4)), h a fixed nibble
+// permutation with h(0) = 0. It puts the entries of one-bit bytes (1, 2, 4,
+// ..., 128) and 0, the common ones at 10% density, in distinct LDS bank
+// groups, so a 16-lane read of such entries has no bank conflict.
+__device__ __forceinline__ uint32_t sel_slot(uint32_t e) {
+    constexpr uint64_t H = 0x8421FED7CBA69530ull;  // h(0..15) = 0,3,5,9,6,10,11,12,7,13,14,15,1,2,4,8
+    return (e & 0xF0u) | ((e & 15u) ^ (uint32_t)((H >> (4 * (e >> 4))) & 15u));
 }
 
-// Complement GEMM: hnon[bh][i][n] = htot[bh][n] - sum_j msel[bh][i][j] * hs[bh][j][n]
-// (i < nqb query blocks, n < HS_ROW state entries, j < nkbp key blocks; msel
-// is 0/1). bf16 operands, fp32 accumulation.
-// Workgroup tile 128 (i) x 128 (n), K step GTK, 2 x 2 waves of 64 x 64, each a
-// 2 x 2 grid of 32x32x16 bf16 MFMAs. Operand tiles arrive by LDS DMA into a
-// GSTAGE-deep ring:
-//   A [128 i][GTK j]: rows of GTK*2 bytes, 16-byte chunk c of row r at slot
-//     c ^ aswz(r), so the 16 rows a 16-lane group reads hit 16 distinct
-//     bank groups;
-//   B [GTK j][128 n]: 256-byte rows kept j-major as in memory, 8-byte unit u of
-//     row r at u ^ 8*(r & 3), read with transposing loads (lds_read_tr16) so
-//     each lane gets 4 consecutive j of one column n; the 32 lanes of a half
-//     wave then hit 32 distinct 8-byte bank groups.
-#ifndef SSA_GEMM_TK
-#define SSA_GEMM_TK 32
-#endif
-#ifndef SSA_GEMM_STAGES
-#define SSA_GEMM_STAGES 3
-#endif
-constexpr int GTM = 128, GTN = 128, GTK = SSA_GEMM_TK, GSTAGE = SSA_GEMM_STAGES;
-static_assert(GTK == 32 || GTK == 64, "K step");
-static_assert(GEMM_KALIGN % GTK == 0, "padded key-block count must be whole K steps");
-constexpr int GA_ROW = GTK * 2, GA_CH = GA_ROW / 16;   // A row bytes, 16-byte chunks per row
-constexpr int GA_BYTES = GTM * GA_ROW, GB_BYTES = GTK * GTN * 2;
-constexpr int NDA = 32 * GA_ROW / 1024;                // A DMAs per wave (32 rows each wave)
-constexpr int NDB = GTK / 16;                          // B DMAs per wave (GTK/4 rows each wave)
-constexpr int GPD = GSTAGE - 1;                        // prefetch distance (K steps)
+// Table entry e: element s (0..7) of the fragment is bf16(1) if bit s of e is
+// set, else 0; element pairs (2q, 2q+1) form dword q.
+__device__ __forceinline__ u32x4 sel_entry(uint32_t e) {
+    u32x4 d;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        d[q] = (((e >> (2 * q)) & 1u) ? 0x3F80u : 0u) | (((e >> (2 * q + 1)) & 1u) ? 0x3F800000u : 0u);
+    return d;
+}
 
-__device__ __forceinline__ int aswz(int r) { return GA_CH == 4 ? (r >> 2) & 3 : (r >> 1) & 7; }
+// Selection rows in the order the GEMM reads them. K step ks covers key
+// blocks 32ks .. 32ks+31, bytes b0..b3 of that word. An MFMA lane of k-half
+// hi needs bytes hi and 2+hi of each K step, as table byte offsets:
+// dword(ks, hi) = 16*slot(b_hi) | 16*slot(b_{2+hi}) << 16. Steps are paired
+// (kp = ks/2) and stored [bh][kp][i][hi][ks&1]: the 16 bytes of one row and
+// pair are contiguous, and so are the rows of one pair. Key blocks past nkb,
+// and the second step of an unpaired last one, select nothing.
+constexpr int SEL_MAX_WORDS = SSA_MAX_N / KBLK / 32 + 2;
+__global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ kidx, int keep,
+                                                   int nqb, int nkb, int nks,
+                                                   uint32_t* __restrict__ msel) {
+    __shared__ uint32_t bits[SEL_MAX_WORDS];
+    const int64_t bh = blockIdx.y;
+    const int i = blockIdx.x;
+    const int nkp = (nks + 1) / 2;
+    const int32_t* src = kidx + (bh * nqb + i) * (int64_t)keep;
+    for (int w = threadIdx.x; w < 2 * nkp; w += 256) bits[w] = 0;
+    __syncthreads();
+    // kept block indices are clamped into [0, nkb)
+    for (int a = threadIdx.x; a < keep; a += 256) {
+        const int j = min(max(src[a], 0), nkb - 1);
+        atomicOr(&bits[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    for (int kp = threadIdx.x; kp < nkp; kp += 256) {
+        u32x4 o;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint32_t x = bits[2 * kp + half];
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) {
+                const uint32_t lo8 = (x >> (8 * hi)) & 255u, hi8 = (x >> (8 * (2 + hi))) & 255u;
+                o[2 * hi + half] = 16u * sel_slot(lo8) | (16u * sel_slot(hi8)) << 16;
+            }
+        }
+        *(u32x4*)(msel + ((bh * nkp + kp) * nqb + i) * 4) = o;
+    }
+}
+
+// Complement GEMM, computed transposed:
+//   hnon[bh][i][n] = htot[bh][n] - sum_j hs[bh][j][n] * sel[bh][i][j]
+// for query blocks i < nqb, state entries n < HS_ROW, key blocks j < nkbp.
+// C^T = Hs^T . Sel^T on 32x32x16 bf16 MFMAs with fp32 accumulation: the A
+// operand is a state fragment, the B operand a selection fragment from the
+// table, and each lane of the result holds four consecutive n of one i,
+// stored as 16-byte runs.
+//
+// Workgroup tile: 64 n x 640 i (every query block of a head, up to 640).
+// Wave w owns rows 160w .. 160w+159 (five 32-row blocks) against both 32-wide
+// halves of n: 10 accumulators. A K step is 32 key blocks. Its [32 j][64 n]
+// bf16 state tile (4 KB, 128-byte rows) arrives by LDS DMA, one 1 KB DMA per
+// wave, into a 4-deep ring, three steps ahead; 16-byte chunk c of row r sits
+// at chunk c ^ 4*((r >> 1) & 1), and the tile is read with transposing loads
+// (lds_read_tr16) that give a lane 4 consecutive j of one n, the 32 lanes of a
+// half wave hitting distinct 8-byte bank groups. The selection of a K-step
+// pair (16 bytes per row) arrives the same way into a 2-deep ring, each wave
+// fetching its own 160 rows. The whole state stack is read once.
+constexpr int CG_TN = 64;                  // state entries per workgroup
+constexpr int CG_IB = 5;                   // 32-row query blocks per wave
+constexpr int CG_WROWS = 32 * CG_IB;       // query blocks per wave
+constexpr int CG_TM = 4 * CG_WROWS;        // query blocks per workgroup
+constexpr int CG_TK = GEMM_KALIGN;         // key blocks per K step
+constexpr int CG_STAGES = 4;
+constexpr int CG_TILE = CG_TK * CG_TN * 2;  // bytes of a state tile
+constexpr int CG_SEL = CG_TM * 16;          // bytes of a K-step pair's selection
+constexpr int CG_LUT = 256 * 16;            // bytes of the expansion table
+static_assert(CG_TK == 32, "one 1 KB DMA per wave and one selection dword per lane per K step");
+static_assert(HS_ROW % CG_TN == 0, "state rows split into whole column tiles");
+static_assert(CG_WROWS == 160, "selection DMAs: two of 64 rows and one of 32 per wave");
+
+size_t msel_bytes(int64_t BH, int64_t nqb, int64_t nkbp) {
+    const int64_t nkp = (nkbp / CG_TK + 1) / 2;
+    return (size_t)BH * nkp * nqb * 16;
+}
 
 __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
-    const uint16_t* __restrict__ msel, const uint16_t* __restrict__ hs, const float* __restrict__ htot,
-    int64_t BH, int nqb, int nkb, int nkbp, float* __restrict__ hnon) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[GSTAGE * (GA_BYTES + GB_BYTES)];
-    uint8_t(*As)[GA_BYTES] = reinterpret_cast<uint8_t(*)[GA_BYTES]>(smem);
-    uint8_t(*Bs)[GB_BYTES] = reinterpret_cast<uint8_t(*)[GB_BYTES]>(smem + GSTAGE * GA_BYTES);
-    const int nnt = HS_ROW / GTN, nmt = (nqb + GTM - 1) / GTM;
+    const uint32_t* __restrict__ msel, const uint16_t* __restrict__ hs,
+    const float* __restrict__ htot, int64_t BH, int nqb, int nkb, int nkbp,
+    float* __restrict__ hnon) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[CG_STAGES * CG_TILE + 2 * CG_SEL + CG_LUT];
+    uint8_t(*Bs)[CG_TILE] = reinterpret_cast<uint8_t(*)[CG_TILE]>(smem);
+    uint8_t(*Ss)[CG_SEL] = reinterpret_cast<uint8_t(*)[CG_SEL]>(smem + CG_STAGES * CG_TILE);
+    uint8_t* lut = smem + CG_STAGES * CG_TILE + 2 * CG_SEL;
+    const int nnt = HS_ROW / CG_TN, nmt = (nqb + CG_TM - 1) / CG_TM;
     const int64_t total = BH * nnt * nmt;
-    const int64_t item = xcd_item(blockIdx.x, total);  // m fastest: B tiles shared in L2
+    const int64_t item = xcd_item(blockIdx.x, total);  // i tiles fastest: they share state tiles
     if (item >= total) return;
     const int mt = (int)(item % nmt);
     const int64_t rest = item / nmt;
     const int nt = (int)(rest % nnt);
     const int64_t bh = rest / nnt;
-    const int i0 = mt * GTM, n0 = nt * GTN;
+    const int i0 = mt * CG_TM, n0 = nt * CG_TN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
-              h = lane >> 5, wm = wave >> 1, wn = wave & 1;
+              hi = lane >> 5;
+    const int nks = nkbp / CG_TK, nkp = (nks + 1) / 2;
+    const int iw = i0 + CG_WROWS * wave;  // first query block of this wave
 
-    // loop-invariant DMA lane offsets: wave w fills A rows 32w..32w+31 and
-    // B rows (GTK/4)w .. +GTK/4, 1 KB per DMA
-    constexpr int ARD = 1024 / GA_ROW;  // A rows per DMA
-    uint32_t aoff[NDA], boff[NDB];
-#pragma unroll
-    for (int p = 0; p < NDA; ++p) {
-        const int ra = 32 * wave + ARD * p + lane / GA_CH;
-        const int ca = (lane % GA_CH) ^ aswz(ra);
-        aoff[p] = (uint32_t)(min(i0 + ra, nqb - 1) * nkbp * 2 + ca * 16);
-    }
-#pragma unroll
-    for (int p = 0; p < NDB; ++p) {
-        const int rb = (GTK / 4) * wave + 4 * p + (lane >> 4);
-        const int cb = (lane & 15) ^ (4 * (rb & 3));
-        boff[p] = (uint32_t)(rb * HS_ROW * 2 + cb * 16);
-    }
-    const uint16_t* abase = msel + (bh * nqb) * (int64_t)nkbp;
+    *(u32x4*)(lut + 16 * sel_slot((uint32_t)tid)) = sel_entry((uint32_t)tid);
+
+    // state tile of K step ks into ring stage st: wave w fills rows 8w .. 8w+7,
+    // lane l row 8w + l/8 at slot l%8, which holds chunk (l%8) ^ 4*((row >> 1) & 1)
+    const int drow = 8 * wave + (lane >> 3);
+    const int dchunk = (lane & 7) ^ (4 * ((drow >> 1) & 1));
     const uint16_t* bbase = hs + (bh * nkb) * (int64_t)HS_ROW + n0;
-    // K step ks into ring stage st (a compile-time constant in the main loop)
-    auto issue = [&](int ks, int st) {
-        const int j0 = ks * GTK;
+    auto issue_tile = [&](int ks, int st) {
+        const int j0 = ks * CG_TK;
+        // rows past nkb (their selection bits are 0) re-read row nkb-1; j0 < nkb
+        // because nkbp rounds nkb up by less than one K step
+        const int r = min(j0 + drow, nkb - 1) - j0;
+        dma16(bbase + (int64_t)j0 * HS_ROW, (uint32_t)(r * HS_ROW * 2 + dchunk * 16),
+              lds_u32(Bs[st] + 8 * wave * 128));
+    };
+    // selection of K-step pair kp into buffer b: the wave's 160 rows, 16 bytes
+    // each, lane = row (rows past nqb re-read row nqb-1; they are never stored)
+    auto issue_sel = [&](int kp, int b) {
+        const uint32_t* base = msel + (bh * nkp + kp) * (int64_t)nqb * 4;
 #pragma unroll
-        for (int p = 0; p < NDA; ++p)
-            dma16(abase + j0, aoff[p], lds_u32(As[st] + (32 * wave + ARD * p) * GA_ROW));
-        // Rows past nkb (msel is 0 there) are fetched from row nkb-1. In such a
-        // ragged step the offset is taken from the unshifted base with the
-        // absolute row clamped: a K step may start at or past nkb (the
-        // padded count is a multiple of GEMM_KALIGN), and a row relative to
-        // j0 would then be negative, which the unsigned 32-bit lane offset of
-        // the DMA cannot express.
-        const bool ragged = j0 + GTK > nkb;
-#pragma unroll
-        for (int p = 0; p < NDB; ++p) {
-            const uint32_t lds = lds_u32(Bs[st] + ((GTK / 4) * wave + 4 * p) * 256);
-            if (ragged) {
-                const int rb = (GTK / 4) * wave + 4 * p + (lane >> 4);
-                const int cb = (lane & 15) ^ (4 * (rb & 3));
-                const int r = min(j0 + rb, nkb - 1);
-                dma16(bbase, (uint32_t)(r * HS_ROW * 2 + cb * 16), lds);
-            } else {
-                dma16(bbase + (int64_t)j0 * HS_ROW, boff[p], lds);
-            }
+        for (int p = 0; p < 3; ++p) {
+            const int i = min(iw + 64 * p + lane, nqb - 1);
+            if (p < 2 || lane < 32)
+                dma16(base, (uint32_t)(i * 16), lds_u32(Ss[b] + (CG_WROWS * wave + 64 * p) * 16));
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[CG_IB][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+    for (int ib = 0; ib < CG_IB; ++ib) acc[ib][0] = acc[ib][1] = f32x16{};
 
-    const int nks = nkbp / GTK;
-    // prologue: steps 0 .. GPD-1 in flight, step 0 landed
-    for (int ks = 0; ks < GPD && ks < nks; ++ks) issue(ks, ks);
-    if (GPD > 1 && nks > 1) wait_vm<(GPD - 1) * (NDA + NDB)>(); else wait_vm<0>();
-    __syncthreads();
-    // one K step from ring stage R (compile-time: LDS addresses are immediates)
-    auto kstep = [&](int ks, auto stage) {
+    // One K step: state tile from ring stage R, selection dwords from pair
+    // buffer R/2 (step parity R&1).
+    auto kstep = [&](auto stage) {
         constexpr int R = decltype(stage)::value;
-        if (ks + GPD < nks) issue(ks + GPD, (R + GPD) % GSTAGE);
-        const uint8_t* A = As[R];
         const uint8_t* B = Bs[R];
+        const uint8_t* S = Ss[R >> 1];
+        uint32_t sd[CG_IB];
 #pragma unroll
-        for (int kc = 0; kc < GTK / 16; ++kc) {
-            bf16x8 af[2], bfr[2];
+        for (int ib = 0; ib < CG_IB; ++ib)
+            sd[ib] = *(const uint32_t*)(S + (CG_WROWS * wave + 32 * ib + l32) * 16 + 8 * hi + 4 * (R & 1));
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const int row = 64 * wm + 32 * a + l32;
-                const int slot = (2 * kc + h) ^ aswz(row);
-                af[a] = *(const bf16x8*)(A + row * GA_ROW + slot * 16);
-            }
+        for (int kc = 0; kc < 2; ++kc) {
+            bf16x8 hf[2];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int col = 64 * wn + 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            for (int nb = 0; nb < 2; ++nb) {
+                const int col = 32 * nb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
                 i16x4 part[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const int row = 16 * kc + 8 * h + 4 * t + ((lane & 15) >> 2);
-                    const int unit = (col >> 2) ^ (8 * (row & 3));
-                    part[t] = lds_read_tr16(B + row * 256 + unit * 8);
+                    const int row = 16 * kc + 8 * hi + 4 * t + ((lane & 15) >> 2);
+                    const int unit = (col >> 2) ^ (8 * ((row >> 1) & 1));
+                    part[t] = lds_read_tr16(B + row * 128 + unit * 8);
                 }
-                // k-slots 0-3 from the first read, 4-7 from the second (whole dwords)
                 const u32x2 w0 = __builtin_bit_cast(u32x2, part[0]);
                 const u32x2 w1 = __builtin_bit_cast(u32x2, part[1]);
-                bfr[b] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+                hf[nb] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
             }
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) acc[a][b] = mfma_bf16_32x32x16(af[a], bfr[b], acc[a][b]);
+            for (int ib = 0; ib < CG_IB; ++ib) {
+                const uint32_t off = kc ? (sd[ib] >> 16) : (sd[ib] & 0xFFFFu);
+                const bf16x8 sf = *(const bf16x8*)(lut + off);
+                acc[ib][0] = mfma_bf16_32x32x16(hf[0], sf, acc[ib][0]);
+                acc[ib][1] = mfma_bf16_32x32x16(hf[1], sf, acc[ib][1]);
+            }
         }
-        // step ks+1 must land; later steps may stay in flight
-        if (GPD > 1 && ks + GPD < nks) wait_vm<(GPD - 1) * (NDA + NDB)>(); else wait_vm<0>();
-        __syncthreads();
     };
-    static_assert(GSTAGE >= 2 && GSTAGE <= 4, "the K loop is unrolled by the ring depth");
+
+    // Pipeline. Step s uses tile stage s % 4 and selection pair s/2. An even
+    // step issues the selection of pair s/2 + 1 (3 DMAs) and then the tile of
+    // step s+3; an odd step only the tile of step s+3. At the end of step s the
+    // tile and selection of step s+1 must have landed: for even s all but the 5
+    // operations issued after tile s+1 (tile s+2, selection, tile s+3), for odd
+    // s all but the 2 issued after that selection (tiles s+2 and s+3). Near the
+    // end everything is drained.
+    issue_sel(0, 0);
+    issue_tile(0, 0);
+    if (nks > 1) issue_tile(1, 1);
+    if (nks > 2) issue_tile(2, 2);
+    if (nks > 2) wait_vm<2>(); else if (nks > 1) wait_vm<1>(); else wait_vm<0>();
+    __syncthreads();  // also publishes the expansion table
+    auto step = [&](int s, auto stage) {
+        constexpr int R = decltype(stage)::value;
+        if ((R & 1) == 0 && s + 2 < nks) issue_sel(s / 2 + 1, ((R >> 1) + 1) & 1);
+        if (s + 3 < nks) issue_tile(s + 3, (R + 3) % CG_STAGES);
+        kstep(stage);
+        if (s + 1 < nks) {
+            if (s + 3 < nks) {
+                if ((R & 1) == 0) wait_vm<5>(); else wait_vm<2>();
+            } else {
+                wait_vm<0>();
+            }
+            __syncthreads();
+        }
+    };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, (GSTAGE > 2 ? 2 : 0)>;
-    using S3 = std::integral_constant<int, (GSTAGE > 3 ? 3 : 0)>;
-    int ks = 0;
-    for (; ks + GSTAGE <= nks; ks += GSTAGE) {
-        kstep(ks, S0{});
-        kstep(ks + 1, S1{});
-        if (GSTAGE > 2) kstep(ks + 2, S2{});
-        if (GSTAGE > 3) kstep(ks + 3, S3{});
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    static_assert(CG_STAGES == 4, "the K loop is unrolled by the ring depth");
+    int s = 0;
+    for (; s + 4 <= nks; s += 4) {
+        step(s, S0{});
+        step(s + 1, S1{});
+        step(s + 2, S2{});
+        step(s + 3, S3{});
     }
-    if (ks < nks) kstep(ks++, S0{});
-    if (ks < nks) kstep(ks++, S1{});
-    if (GSTAGE > 3 && ks < nks) kstep(ks, S2{});
+    if (s < nks) step(s++, S0{});
+    if (s < nks) step(s++, S1{});
+    if (s < nks) step(s, S2{});
+
+    // epilogue: lane (i, hi), accumulator [ib][nb] register 4q + x holds
+    // n = 32nb + 8q + 4hi + x
+    f32x4 ht[2][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int q = 0; q < 4; ++q)
+            ht[nb][q] = *(const f32x4*)(htot + bh * HS_ROW + n0 + 32 * nb + 8 * q + 4 * hi);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = i0 + 64 * wm + 32 * a + mfma32_row(lane, r);
-                const int n = n0 + 64 * wn + 32 * b + l32;
-                if (i < nqb) hnon[(bh * nqb + i) * HS_ROW + n] = htot[bh * HS_ROW + n] - acc[a][b][r];
+    for (int ib = 0; ib < CG_IB; ++ib) {
+        const int i = iw + 32 * ib + l32;
+        if (i >= nqb) continue;
+        float* dst = hnon + (bh * nqb + i) * (int64_t)HS_ROW + n0 + 4 * hi;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x16& a = acc[ib][nb];
+                *(f32x4*)(dst + 32 * nb + 8 * q) =
+                    ht[nb][q] - f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
             }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -413,12 +488,12 @@ hipError_t launch_vt_only(const uint16_t* v, int64_t BH, int N, uint16_t* vt, hi
 }
 
 hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, const float* htot,
-                             int64_t BH, int N, uint16_t* msel, float* hnon, hipStream_t st) {
+                             int64_t BH, int N, uint32_t* msel, float* hnon, hipStream_t st) {
     const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
     const int nkbp = (nkb + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
-    hipLaunchKernelGGL(msel_kernel, dim3(nqb, BH), dim3(256), 0, st, kidx, keep, nqb,
-                       nkbp, msel);
-    const int64_t total = BH * (HS_ROW / 128) * ((nqb + 127) / 128);
+    hipLaunchKernelGGL(msel_kernel, dim3(nqb, BH), dim3(256), 0, st, kidx, keep, nqb, nkb,
+                       nkbp / GEMM_KALIGN, msel);
+    const int64_t total = BH * (HS_ROW / CG_TN) * ((nqb + CG_TM - 1) / CG_TM);
     const int64_t grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel, hs, htot,
                        BH, nqb, nkb, nkbp, hnon);
