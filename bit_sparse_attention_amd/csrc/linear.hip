@@ -283,24 +283,28 @@ __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ k
 //
 // Workgroup tile: 64 n x 640 i (every query block of a head, up to 640).
 // Wave w owns rows 160w .. 160w+159 (five 32-row blocks) against both 32-wide
-// halves of n: 10 accumulators. A K step is 32 key blocks. Its [32 j][64 n]
-// bf16 state tile (4 KB, 128-byte rows) arrives by LDS DMA, one 1 KB DMA per
-// wave, into a 4-deep ring, three steps ahead; 16-byte chunk c of row r sits
-// at chunk c ^ 4*((r >> 1) & 1), and the tile is read with transposing loads
-// (lds_read_tr16) that give a lane 4 consecutive j of one n, the 32 lanes of a
-// half wave hitting distinct 8-byte bank groups. The selection of a K-step
-// pair (16 bytes per row) arrives the same way into a 2-deep ring, each wave
-// fetching its own 160 rows. The whole state stack is read once.
+// halves of n: 10 accumulators. The K loop runs over pairs of 32-key-block
+// steps; a pair's operands form one stage of a 3-deep LDS ring, fetched by LDS
+// DMA two stages ahead:
+//   the [64 j][64 n] bf16 state tile (8 KB, 128-byte rows), two 1 KB DMAs per
+//     wave; 16-byte chunk c of row r sits at chunk c ^ 4*((r >> 1) & 1), and
+//     the tile is read with transposing loads (lds_read_tr16) that give a lane
+//     4 consecutive j of one n, the 32 lanes of a half wave hitting distinct
+//     8-byte bank groups;
+//   the pair's selection (16 bytes per row), each wave fetching its own 160
+//     rows.
+// The whole state stack is read once.
 constexpr int CG_TN = 64;                  // state entries per workgroup
 constexpr int CG_IB = 5;                   // 32-row query blocks per wave
 constexpr int CG_WROWS = 32 * CG_IB;       // query blocks per wave
 constexpr int CG_TM = 4 * CG_WROWS;        // query blocks per workgroup
-constexpr int CG_TK = GEMM_KALIGN;         // key blocks per K step
-constexpr int CG_STAGES = 4;
-constexpr int CG_TILE = CG_TK * CG_TN * 2;  // bytes of a state tile
-constexpr int CG_SEL = CG_TM * 16;          // bytes of a K-step pair's selection
-constexpr int CG_LUT = 256 * 16;            // bytes of the expansion table
-static_assert(CG_TK == 32, "one 1 KB DMA per wave and one selection dword per lane per K step");
+constexpr int CG_TK = GEMM_KALIGN;         // key blocks per selection word (half a stage)
+constexpr int CG_STAGES = 3;
+constexpr int CG_TILE = 2 * CG_TK * CG_TN * 2;  // bytes of a stage's state tile [64 j][64 n]
+constexpr int CG_SEL = CG_TM * 16;              // bytes of a stage's selection
+constexpr int CG_STAGE = CG_TILE + CG_SEL;
+constexpr int CG_LUT = 256 * 16;                // bytes of the expansion table
+static_assert(CG_TK == 32, "selection dword per lane per 32 key blocks");
 static_assert(HS_ROW % CG_TN == 0, "state rows split into whole column tiles");
 static_assert(CG_WROWS == 160, "selection DMAs: two of 64 rows and one of 32 per wave");
 
@@ -313,10 +317,8 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     const uint32_t* __restrict__ msel, const uint16_t* __restrict__ hs,
     const float* __restrict__ htot, int64_t BH, int nqb, int nkb, int nkbp,
     float* __restrict__ hnon) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[CG_STAGES * CG_TILE + 2 * CG_SEL + CG_LUT];
-    uint8_t(*Bs)[CG_TILE] = reinterpret_cast<uint8_t(*)[CG_TILE]>(smem);
-    uint8_t(*Ss)[CG_SEL] = reinterpret_cast<uint8_t(*)[CG_SEL]>(smem + CG_STAGES * CG_TILE);
-    uint8_t* lut = smem + CG_STAGES * CG_TILE + 2 * CG_SEL;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[CG_STAGES * CG_STAGE + CG_LUT];
+    uint8_t* lut = smem + CG_STAGES * CG_STAGE;
     const int nnt = HS_ROW / CG_TN, nmt = (nqb + CG_TM - 1) / CG_TM;
     const int64_t total = BH * nnt * nmt;
     const int64_t item = xcd_item(blockIdx.x, total);  // i tiles fastest: they share state tiles
@@ -333,28 +335,30 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
 
     *(u32x4*)(lut + 16 * sel_slot((uint32_t)tid)) = sel_entry((uint32_t)tid);
 
-    // state tile of K step ks into ring stage st: wave w fills rows 8w .. 8w+7,
-    // lane l row 8w + l/8 at slot l%8, which holds chunk (l%8) ^ 4*((row >> 1) & 1)
-    const int drow = 8 * wave + (lane >> 3);
-    const int dchunk = (lane & 7) ^ (4 * ((drow >> 1) & 1));
+    // stage kp: state rows j = 64kp .. 64kp+63 (wave w fills rows 16w .. 16w+15,
+    // two DMAs; lane l row 16w + 8p + l/8 at slot l%8, holding chunk
+    // (l%8) ^ 4*((row >> 1) & 1)) and the selection of that K-step pair
+    const int dchunk = (lane & 7) ^ (4 * (((lane >> 3) >> 1) & 1));
     const uint16_t* bbase = hs + (bh * nkb) * (int64_t)HS_ROW + n0;
-    auto issue_tile = [&](int ks, int st) {
-        const int j0 = ks * CG_TK;
-        // rows past nkb (their selection bits are 0) re-read row nkb-1; j0 < nkb
-        // because nkbp rounds nkb up by less than one K step
-        const int r = min(j0 + drow, nkb - 1) - j0;
-        dma16(bbase + (int64_t)j0 * HS_ROW, (uint32_t)(r * HS_ROW * 2 + dchunk * 16),
-              lds_u32(Bs[st] + 8 * wave * 128));
-    };
-    // selection of K-step pair kp into buffer b: the wave's 160 rows, 16 bytes
-    // each, lane = row (rows past nqb re-read row nqb-1; they are never stored)
-    auto issue_sel = [&](int kp, int b) {
-        const uint32_t* base = msel + (bh * nkp + kp) * (int64_t)nqb * 4;
+    auto issue = [&](int kp, int st) {
+        uint8_t* T = smem + st * CG_STAGE;
+        uint8_t* S = T + CG_TILE;
+        const uint32_t* sbase = msel + (bh * nkp + kp) * (int64_t)nqb * 4;
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
             const int i = min(iw + 64 * p + lane, nqb - 1);
             if (p < 2 || lane < 32)
-                dma16(base, (uint32_t)(i * 16), lds_u32(Ss[b] + (CG_WROWS * wave + 64 * p) * 16));
+                dma16(sbase, (uint32_t)(i * 16), lds_u32(S + (CG_WROWS * wave + 64 * p) * 16));
+        }
+        const int j0 = 2 * CG_TK * kp;
+        // rows past nkb (their selection bits are 0) re-read row nkb-1; j0 < nkb
+        // because nkbp rounds nkb up by less than one selection word
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int row = 16 * wave + 8 * p + (lane >> 3);
+            const int r = min(j0 + row, nkb - 1) - j0;
+            dma16(bbase + (int64_t)j0 * HS_ROW, (uint32_t)(r * HS_ROW * 2 + dchunk * 16),
+                  lds_u32(T + (16 * wave + 8 * p) * 128));
         }
     };
 
@@ -362,85 +366,71 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
 #pragma unroll
     for (int ib = 0; ib < CG_IB; ++ib) acc[ib][0] = acc[ib][1] = f32x16{};
 
-    // One K step: state tile from ring stage R, selection dwords from pair
-    // buffer R/2 (step parity R&1).
     auto kstep = [&](auto stage) {
         constexpr int R = decltype(stage)::value;
-        const uint8_t* B = Bs[R];
-        const uint8_t* S = Ss[R >> 1];
-        uint32_t sd[CG_IB];
+        const uint8_t* B = smem + R * CG_STAGE;
+        const uint8_t* S = B + CG_TILE;
 #pragma unroll
-        for (int ib = 0; ib < CG_IB; ++ib)
-            sd[ib] = *(const uint32_t*)(S + (CG_WROWS * wave + 32 * ib + l32) * 16 + 8 * hi + 4 * (R & 1));
+        for (int half = 0; half < 2; ++half) {
+            uint32_t sd[CG_IB];
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            bf16x8 hf[2];
+            for (int ib = 0; ib < CG_IB; ++ib)
+                sd[ib] = *(const uint32_t*)(S + (CG_WROWS * wave + 32 * ib + l32) * 16 + 8 * hi + 4 * half);
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int col = 32 * nb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-                i16x4 part[2];
+            for (int kc = 0; kc < 2; ++kc) {
+                bf16x8 hf[2];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int row = 16 * kc + 8 * hi + 4 * t + ((lane & 15) >> 2);
-                    const int unit = (col >> 2) ^ (8 * ((row >> 1) & 1));
-                    part[t] = lds_read_tr16(B + row * 128 + unit * 8);
+                for (int nb = 0; nb < 2; ++nb) {
+                    const int col = 32 * nb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                    i16x4 part[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int row = 32 * half + 16 * kc + 8 * hi + 4 * t + ((lane & 15) >> 2);
+                        const int unit = (col >> 2) ^ (8 * ((row >> 1) & 1));
+                        part[t] = lds_read_tr16(B + row * 128 + unit * 8);
+                    }
+                    const u32x2 w0 = __builtin_bit_cast(u32x2, part[0]);
+                    const u32x2 w1 = __builtin_bit_cast(u32x2, part[1]);
+                    hf[nb] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
                 }
-                const u32x2 w0 = __builtin_bit_cast(u32x2, part[0]);
-                const u32x2 w1 = __builtin_bit_cast(u32x2, part[1]);
-                hf[nb] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
-            }
 #pragma unroll
-            for (int ib = 0; ib < CG_IB; ++ib) {
-                const uint32_t off = kc ? (sd[ib] >> 16) : (sd[ib] & 0xFFFFu);
-                const bf16x8 sf = *(const bf16x8*)(lut + off);
-                acc[ib][0] = mfma_bf16_32x32x16(hf[0], sf, acc[ib][0]);
-                acc[ib][1] = mfma_bf16_32x32x16(hf[1], sf, acc[ib][1]);
+                for (int ib = 0; ib < CG_IB; ++ib) {
+                    const uint32_t off = kc ? (sd[ib] >> 16) : (sd[ib] & 0xFFFFu);
+                    const bf16x8 sf = *(const bf16x8*)(lut + off);
+                    acc[ib][0] = mfma_bf16_32x32x16(hf[0], sf, acc[ib][0]);
+                    acc[ib][1] = mfma_bf16_32x32x16(hf[1], sf, acc[ib][1]);
+                }
             }
         }
     };
 
-    // Pipeline. Step s uses tile stage s % 4 and selection pair s/2. An even
-    // step issues the selection of pair s/2 + 1 (3 DMAs) and then the tile of
-    // step s+3; an odd step only the tile of step s+3. At the end of step s the
-    // tile and selection of step s+1 must have landed: for even s all but the 5
-    // operations issued after tile s+1 (tile s+2, selection, tile s+3), for odd
-    // s all but the 2 issued after that selection (tiles s+2 and s+3). Near the
-    // end everything is drained.
-    issue_sel(0, 0);
-    issue_tile(0, 0);
-    if (nks > 1) issue_tile(1, 1);
-    if (nks > 2) issue_tile(2, 2);
-    if (nks > 2) wait_vm<2>(); else if (nks > 1) wait_vm<1>(); else wait_vm<0>();
+    // Pipeline over K-step pairs: stage kp % 3, two stages ahead. Each stage is
+    // 5 DMAs per wave; at the end of step kp only stage kp+2's may stay in flight.
+    issue(0, 0);
+    if (nkp > 1) issue(1, 1);
+    if (nkp > 1) wait_vm<5>(); else wait_vm<0>();
     __syncthreads();  // also publishes the expansion table
-    auto step = [&](int s, auto stage) {
+    auto step = [&](int kp, auto stage) {
         constexpr int R = decltype(stage)::value;
-        if ((R & 1) == 0 && s + 2 < nks) issue_sel(s / 2 + 1, ((R >> 1) + 1) & 1);
-        if (s + 3 < nks) issue_tile(s + 3, (R + 3) % CG_STAGES);
+        if (kp + 2 < nkp) issue(kp + 2, (R + 2) % CG_STAGES);
         kstep(stage);
-        if (s + 1 < nks) {
-            if (s + 3 < nks) {
-                if ((R & 1) == 0) wait_vm<5>(); else wait_vm<2>();
-            } else {
-                wait_vm<0>();
-            }
+        if (kp + 1 < nkp) {
+            if (kp + 2 < nkp) wait_vm<5>(); else wait_vm<0>();
             __syncthreads();
         }
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
-    using S3 = std::integral_constant<int, 3>;
-    static_assert(CG_STAGES == 4, "the K loop is unrolled by the ring depth");
-    int s = 0;
-    for (; s + 4 <= nks; s += 4) {
-        step(s, S0{});
-        step(s + 1, S1{});
-        step(s + 2, S2{});
-        step(s + 3, S3{});
+    static_assert(CG_STAGES == 3, "the K loop is unrolled by the ring depth");
+    int kp = 0;
+    for (; kp + 3 <= nkp; kp += 3) {
+        step(kp, S0{});
+        step(kp + 1, S1{});
+        step(kp + 2, S2{});
     }
-    if (s < nks) step(s++, S0{});
-    if (s < nks) step(s++, S1{});
-    if (s < nks) step(s, S2{});
+    if (kp < nkp) step(kp++, S0{});
+    if (kp < nkp) step(kp, S1{});
 
     // epilogue: lane (i, hi), accumulator [ib][nb] register 4q + x holds
     // n = 32nb + 8q + 4hi + x
