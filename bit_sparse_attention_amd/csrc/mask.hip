@@ -32,21 +32,38 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // Selection of one score row by one wave: the `keep` best key blocks under
 // (score descending, j ascending), written ascending to krow (and the 0/1
-// mask row). An exact 4-pass MSB radix select finds the keep-th largest key T
-// and how many keys equal to T are kept (the lowest j first).
+// mask row). An exact MSB radix select finds the keep-th largest key T and
+// how many keys equal to T are kept (the lowest j first). The leading bits
+// that every key of the row shares (sign and top exponent bits, as a rule)
+// are skipped: the keys are shifted left by that count, so the first 8-bit
+// pass already spreads over the histogram, and ceil(significant bits / 8)
+// passes suffice.
 __device__ __forceinline__ void wave_select_row(const float* __restrict__ s, int nkb, int keep,
                                                 int* __restrict__ hist, int32_t* __restrict__ krow,
                                                 uint8_t* __restrict__ mrow) {
     const int lane = threadIdx.x & 63;
-    uint32_t prefix = 0u, pmask = 0u;
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    for (int j = lane; j < nkb; j += 64) {
+        const uint32_t key = order_key(s[j]);
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    }
+    const int common = kmin == kmax ? 32 : __builtin_clz(kmin ^ kmax);  // shared leading bits
+    const int npass = (32 - common + 7) >> 3;
+    uint32_t prefix = 0u, pmask = 0u;  // over the shifted keys
     int rem = keep;
-    for (int pass = 0; pass < 4; ++pass) {
+    for (int pass = 0; pass < npass; ++pass) {
         const int shift = 24 - 8 * pass;
 #pragma unroll
         for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0;
         __builtin_amdgcn_wave_barrier();
         for (int j = lane; j < nkb; j += 64) {
-            const uint32_t key = order_key(s[j]);
+            const uint32_t key = order_key(s[j]) << common;  // common < 32 here
             if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
         }
         __builtin_amdgcn_wave_barrier();
@@ -79,7 +96,10 @@ __device__ __forceinline__ void wave_select_row(const float* __restrict__ s, int
         rem = nrem;
         __builtin_amdgcn_wave_barrier();
     }
-    const uint32_t T = prefix;  // keep-th largest key; keep `rem` of the keys equal to T
+    // keep-th largest key; keep `rem` of the keys equal to T (with no pass, every
+    // key equals kmin)
+    const uint32_t T = npass == 0 ? kmin
+                                  : (prefix >> common) | (common ? kmin & (~0u << (32 - common)) : 0u);
     // emit: lane l owns the contiguous range [l*chunk, (l+1)*chunk) of j
     const int chunk = (nkb + 63) >> 6;
     const int j0 = lane * chunk, j1 = min(nkb, j0 + chunk);
