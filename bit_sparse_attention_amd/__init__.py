@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "sage_quant_qk", "sla_block_mask", "sage_sla_attn_fwd", "sage_qk_int32_tiles", "sagesla",
-    "SageSLAPlan", "KernelTimer", "keep_blocks", "num_q_blocks", "num_k_blocks", "workspace_bytes", "lib_path",
+    "SageSLAPlan", "KernelTimer", "keep_blocks", "num_q_blocks", "num_k_blocks", "workspace_bytes",
+    "pool_bytes", "new_pool", "lib_path",
     "SPARSE", "LINEAR", "OP_QUANT", "OP_MASK", "OP_ATTN",
 ]
 
@@ -69,8 +70,9 @@ def _load():
         "ssa_workspace_bytes": (sz, [i32, Shape, i64, i32]),
         "ssa_status_str": (C.c_char_p, [i32]),
         "ssa_last_error": (C.c_char_p, []),
-        "sage_quant_qk": (i32, [_p, _p, Shape, _p, _p, _p, _p, _p, _p, sz, _p]),
-        "sla_block_mask": (i32, [_p, _p, Shape, i64, _p, _p, _p, sz, _p]),
+        "sage_quant_qk": (i32, [_p, _p, Shape, _p, _p, _p, _p, _p, _p, _p, sz, _p]),
+        "sla_block_mask": (i32, [_p, _p, Shape, i64, _p, _p, _p, _p, sz, _p]),
+        "ssa_pool_bytes": (sz, [Shape]),
         "sage_sla_attn_fwd": (i32, [_p, _p, _p, Shape, _p, _p, _p, _p, _p, i64, i32, C.c_float,
                                     _p, _p, _p, sz, _p]),
         "sage_qk_int32_tiles": (i32, [_p, _p, Shape, _p, i64, _p, _p]),
@@ -149,9 +151,20 @@ def _qkv_shape(q, k, v=None):
     return _shape_of(q)
 
 
-def sage_quant_qk(q, k):
+def pool_bytes(shape) -> int:
+    """Bytes of the pooled-means buffer that sage_quant_qk can fill for sla_block_mask."""
+    return int(_load().ssa_pool_bytes(Shape(*shape)))
+
+
+def new_pool(q):
+    """A pooled-means buffer for tensors shaped like q."""
+    return torch.empty(pool_bytes(tuple(q.shape)), dtype=torch.uint8, device=q.device)
+
+
+def sage_quant_qk(q, k, pool=None):
     """K smoothing + per-block INT8 quantization.
-    Returns (q_i8, q_scale [B,H,Nqb], k_i8, k_scale [B,H,Nkb], k_mean [B,H,D])."""
+    Returns (q_i8, q_scale [B,H,Nqb], k_i8, k_scale [B,H,Nkb], k_mean [B,H,D]).
+    pool (from new_pool) also receives the block mask's pooled means."""
     s = _qkv_shape(q, k)
     B, H, N, D = q.shape
     dev = q.device
@@ -161,24 +174,32 @@ def sage_quant_qk(q, k):
     k_scale = torch.empty((B, H, num_k_blocks(N)), dtype=torch.float32, device=dev)
     k_mean = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     ws, n = _ws(OP_QUANT, s, dev)
+    if pool is not None:
+        _need_gpu("pool", pool, torch.uint8, (pool_bytes(tuple(q.shape)),))
     _check("sage_quant_qk", _load().sage_quant_qk(
         _ptr(q), _ptr(k), s, _ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(k_mean),
-        _ptr(ws), n, _stream(dev)))
+        _ptr(pool), _ptr(ws), n, _stream(dev)))
     return q_i8, q_scale, k_i8, k_scale, k_mean
 
 
-def sla_block_mask(q, k, keep: int, return_mask: bool = False):
+def sla_block_mask(q, k, keep: int, return_mask: bool = False, pool=None):
     """kidx [B,H,Nqb,keep] (ascending key blocks), and the uint8 mask
-    [B,H,Nqb,Nkb] when return_mask."""
+    [B,H,Nqb,Nkb] when return_mask. pool: a buffer sage_quant_qk filled for the
+    same q, k (then q and k are not read)."""
     s = _qkv_shape(q, k)
     B, H, N, D = q.shape
     dev = q.device
     kidx = torch.empty((B, H, num_q_blocks(N), int(keep)), dtype=torch.int32, device=dev)
     mask = (torch.empty((B, H, num_q_blocks(N), num_k_blocks(N)), dtype=torch.uint8, device=dev)
             if return_mask else None)
-    ws, n = _ws(OP_MASK, s, dev, keep)
+    if pool is not None:
+        _need_gpu("pool", pool, torch.uint8, (pool_bytes(tuple(q.shape)),))
+        ws, n = None, 0
+    else:
+        ws, n = _ws(OP_MASK, s, dev, keep)
     _check("sla_block_mask", _load().sla_block_mask(
-        _ptr(q), _ptr(k), s, int(keep), _ptr(kidx), _ptr(mask), _ptr(ws), n, _stream(dev)))
+        _ptr(q), _ptr(k), s, int(keep), _ptr(pool), _ptr(kidx), _ptr(mask), _ptr(ws), n,
+        _stream(dev)))
     return (kidx, mask) if return_mask else kidx
 
 
@@ -229,12 +250,13 @@ def sagesla(q, k, v, topk: float | None = 0.1, linear: bool = True, sm_scale: fl
     """The whole path: quantize, select blocks (unless topk is None: dense),
     attend. The meaning of topk is --sla_topk's: the fraction of key blocks
     kept per query block."""
-    q_i8, q_scale, k_i8, k_scale, _ = sage_quant_qk(q, k)
+    pool = None if topk is None else new_pool(q)
+    q_i8, q_scale, k_i8, k_scale, _ = sage_quant_qk(q, k, pool)
     if topk is None:
         return sage_sla_attn_fwd(q, k, v, q_i8, q_scale, k_i8, k_scale, None, None, SPARSE,
                                  sm_scale, return_f32)
     keep = keep_blocks(q.shape[2], topk)
-    kidx = sla_block_mask(q, k, keep)
+    kidx = sla_block_mask(q, k, keep, pool=pool)
     br = SPARSE | (LINEAR if linear else 0)
     return sage_sla_attn_fwd(q, k, v, q_i8, q_scale, k_i8, k_scale, kidx, keep, br, sm_scale,
                              return_f32)
@@ -287,11 +309,13 @@ class SageSLAPlan:
         self.k_mean = torch.empty((B, H, HEAD_DIM), dtype=torch.float32, **e)
         self.kidx = None if self.dense else torch.empty((B, H, self.nqb, self.keep),
                                                         dtype=torch.int32, **e)
+        # pooled means: sage_quant_qk hands them to sla_block_mask
+        self.pool = None if self.dense else torch.empty(
+            int(L.ssa_pool_bytes(self.shape)), dtype=torch.uint8, **e)
         self.out = torch.empty((B, H, N, HEAD_DIM), dtype=torch.bfloat16, **e)
         self.out32 = torch.empty((B, H, N, HEAD_DIM), dtype=torch.float32, **e) if want_f32 else None
         self.ws_n = {
             OP_QUANT: workspace_bytes(OP_QUANT, self.shape),
-            OP_MASK: workspace_bytes(OP_MASK, self.shape, self.keep),
             OP_ATTN: workspace_bytes(OP_ATTN, self.shape, self.keep, self.branches),
         }
         # one workspace serves the three calls (they run in order on one stream)
@@ -309,15 +333,15 @@ class SageSLAPlan:
     def quant(self):
         _check("sage_quant_qk", self._L.sage_quant_qk(
             _ptr(self.q), _ptr(self.k), self.shape, _ptr(self.q_i8), _ptr(self.q_scale),
-            _ptr(self.k_i8), _ptr(self.k_scale), _ptr(self.k_mean), _ptr(self.ws),
-            self.ws_n[OP_QUANT], _stream(self.device)))
+            _ptr(self.k_i8), _ptr(self.k_scale), _ptr(self.k_mean), _ptr(self.pool),
+            _ptr(self.ws), self.ws_n[OP_QUANT], _stream(self.device)))
 
     def mask(self):
         if self.dense:
             return
         _check("sla_block_mask", self._L.sla_block_mask(
-            _ptr(self.q), _ptr(self.k), self.shape, self.keep, _ptr(self.kidx), None,
-            _ptr(self.ws), self.ws_n[OP_MASK], _stream(self.device)))
+            _ptr(self.q), _ptr(self.k), self.shape, self.keep, _ptr(self.pool), _ptr(self.kidx),
+            None, None, 0, _stream(self.device)))
 
     def attn(self):
         _check("sage_sla_attn_fwd", self._L.sage_sla_attn_fwd(

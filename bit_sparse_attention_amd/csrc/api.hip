@@ -203,6 +203,12 @@ int64_t ssa_keep_blocks(int64_t N, double topk) {
     return (int64_t)x;
 }
 
+size_t ssa_pool_bytes(ssa_shape s) {
+    Dims d;
+    if (check_shape(s, &d) != SSA_OK) return 0;
+    return ws_mask(d).total;
+}
+
 size_t ssa_workspace_bytes(int op, ssa_shape s, int64_t keep, int branches) {
     Dims d;
     if (check_shape(s, &d) != SSA_OK) return 0;
@@ -231,8 +237,8 @@ const char* ssa_status_str(ssa_status st) {
 const char* ssa_last_error(void) { return g_err; }
 
 ssa_status sage_quant_qk(const uint16_t* q, const uint16_t* k, ssa_shape s, int8_t* q_i8,
-                         float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, void* pool,
+                         void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
     Dims d;
     TRY(check_shape(s, &d));
@@ -245,46 +251,60 @@ ssa_status sage_quant_qk(const uint16_t* q, const uint16_t* k, ssa_shape s, int8
     TRY(need_ptr(k_mean, 4, "k_mean"));
     const size_t nel = (size_t)d.BH * d.N * HD;
     const Range ins[] = {{q, nel * 2, "q"}, {k, nel * 2, "k"}};
+    if (pool && !aligned(pool, 256)) return fail(SSA_ERR_INVALID, "pool is not 256-byte aligned");
+    const MaskWs pw = ws_mask(d);  // the pool holds the block mask's pooled means
     const Range outs[] = {{q_i8, nel, "q_i8"},
                           {k_i8, nel, "k_i8"},
                           {q_scale, (size_t)d.BH * d.nqb * 4, "q_scale"},
                           {k_scale, (size_t)d.BH * d.nkb * 4, "k_scale"},
                           {k_mean, (size_t)d.BH * HD * 4, "k_mean"},
+                          {pool, pool ? pw.total : 0, "pool"},
                           {ws, ws_bytes, "workspace"}};
-    TRY(check_alias(outs, 6, ins, 2));
+    TRY(check_alias(outs, 7, ins, 2));
     TRY(check_ws(ws, ws_bytes, ws_quant(d)));
     TRY(check_device());
+    float* qbar = pool ? (float*)((char*)pool + pw.qbar) : nullptr;
+    float* kbarT = pool ? (float*)((char*)pool + pw.kbarT) : nullptr;
     hipError_t e = launch_quant_qk(q, k, d.BH, (int)d.N, q_i8, q_scale, k_i8, k_scale, k_mean,
-                                   (float*)ws, (hipStream_t)stream);
+                                   (float*)ws, qbar, kbarT, (int)pw.ldk, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sage_quant_qk launch");
     return SSA_OK;
 }
 
 ssa_status sla_block_mask(const uint16_t* q, const uint16_t* k, ssa_shape s, int64_t keep,
-                          int32_t* kidx, uint8_t* mask, void* ws, size_t ws_bytes, void* stream) {
+                          const void* pool, int32_t* kidx, uint8_t* mask, void* ws, size_t ws_bytes,
+                          void* stream) {
     g_err[0] = 0;
     Dims d;
     TRY(check_shape(s, &d));
     if (keep < 1 || keep > d.nkb)
         return fail(SSA_ERR_INVALID, "keep=%lld outside [1, %lld]", (long long)keep,
                     (long long)d.nkb);
-    TRY(need_ptr(q, 16, "q"));
-    TRY(need_ptr(k, 16, "k"));
+    if (pool) {
+        if (!aligned(pool, 256)) return fail(SSA_ERR_INVALID, "pool is not 256-byte aligned");
+    } else {
+        TRY(need_ptr(q, 16, "q"));
+        TRY(need_ptr(k, 16, "k"));
+    }
     TRY(need_ptr(kidx, 4, "kidx"));
     if (mask && !aligned(mask, 1)) return fail(SSA_ERR_INVALID, "mask misaligned");
     const size_t nel = (size_t)d.BH * d.N * HD;
-    const Range ins[] = {{q, nel * 2, "q"}, {k, nel * 2, "k"}};
+    const MaskWs w = ws_mask(d);
+    const Range ins[] = {{pool ? nullptr : q, nel * 2, "q"},
+                         {pool ? nullptr : k, nel * 2, "k"},
+                         {pool, pool ? w.total : 0, "pool"}};
     const Range outs[] = {{kidx, (size_t)d.BH * d.nqb * keep * 4, "kidx"},
                           {mask, mask ? (size_t)d.BH * d.nqb * d.nkb : 0, "mask"},
-                          {ws, ws_bytes, "workspace"}};
-    TRY(check_alias(outs, 3, ins, 2));
-    const MaskWs w = ws_mask(d);
-    TRY(check_ws(ws, ws_bytes, w.total));
+                          {pool ? nullptr : ws, ws_bytes, "workspace"}};
+    TRY(check_alias(outs, 3, ins, 3));
+    if (!pool) TRY(check_ws(ws, ws_bytes, w.total));
     TRY(check_device());
-    char* base = (char*)ws;
+    const char* base = pool ? (const char*)pool : (const char*)ws;
     float* qbar = (float*)(base + w.qbar);
     float* kbarT = (float*)(base + w.kbarT);
-    hipError_t e = launch_pool(q, k, d.BH, (int)d.N, qbar, kbarT, (int)w.ldk, (hipStream_t)stream);
+    hipError_t e = hipSuccess;
+    if (!pool)
+        e = launch_pool(q, k, d.BH, (int)d.N, qbar, kbarT, (int)w.ldk, (hipStream_t)stream);
     if (e == hipSuccess)
         e = launch_score_topk(qbar, kbarT, (int)w.ldk, d.BH, (int)d.nqb, (int)d.nkb, (int)keep, kidx,
                               mask, (hipStream_t)stream);

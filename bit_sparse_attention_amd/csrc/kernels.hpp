@@ -6,9 +6,11 @@
 namespace ssa {
 
 // quant.hip
+// qbar / kbarT (may be null): also write the block mask's pooled means (the
+// layouts launch_pool writes), from the same passes over Q and K
 hipError_t launch_quant_qk(const uint16_t* q, const uint16_t* k, int64_t BH, int N, int8_t* q_i8,
                            float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
-                           float* ws_part, hipStream_t st);
+                           float* ws_part, float* qbar, float* kbarT, int ldk, hipStream_t st);
 hipError_t launch_pool(const uint16_t* q, const uint16_t* k, int64_t BH, int N, float* qbar,
                        float* kbarT, int ldk, hipStream_t st);
 // mask.hip

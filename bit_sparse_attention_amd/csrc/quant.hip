@@ -15,14 +15,16 @@ namespace ssa {
 // One workgroup covers NB consecutive blocks of BLK tokens; thread
 // (blk = tid/16, g = tid%16) owns channels 8g..8g+7 of its block and adds the
 // block's valid tokens in token order, starting from 0.
-//   MODE 0: out[bh][b][d] = sum                    (K mean partials)
+//   MODE 0: out[bh][b][d] = sum                    (K mean partials), and, if
+//           out2 is given, out2 as MODE 2 (the same sums give the pooled means)
 //   MODE 1: out[bh][b][d] = sum / valid            (pooled means)
 //   MODE 2: out[bh][d][b] = sum / valid, row pitch ld (pooled means, transposed)
 template <int BLK, int MODE>
 __global__ __launch_bounds__((1024 / BLK) * 16)
-void colsum_kernel(const uint16_t* __restrict__ x, int N, int nb, int ld, float* __restrict__ out) {
+void colsum_kernel(const uint16_t* __restrict__ x, int N, int nb, int ld, float* __restrict__ out,
+                   float* __restrict__ out2) {
     constexpr int NB = 1024 / BLK;
-    __shared__ float stage[MODE == 2 ? NB * HD : 1];
+    __shared__ float stage[MODE == 1 ? 1 : NB * HD];
     const int tid = threadIdx.x;
     const int bl = tid >> 4, g = tid & 15;
     const int64_t bh = blockIdx.y;
@@ -58,7 +60,9 @@ void colsum_kernel(const uint16_t* __restrict__ x, int N, int nb, int ld, float*
             *(f32x4*)o = f32x4{r[0], r[1], r[2], r[3]};
             *(f32x4*)(o + 4) = f32x4{r[4], r[5], r[6], r[7]};
         }
-    } else {
+    }
+    float* tout = MODE == 2 ? out : MODE == 0 ? out2 : nullptr;
+    if (MODE != 1 && tout) {
         if (b < nb)
 #pragma unroll
             for (int e = 0; e < 8; ++e) stage[bl * HD + 8 * g + e] = acc[e] / (float)valid;
@@ -67,7 +71,7 @@ void colsum_kernel(const uint16_t* __restrict__ x, int N, int nb, int ld, float*
         for (int idx = tid; idx < NB * HD; idx += NB * 16) {
             const int d = idx / NB, bb = idx % NB;
             const int b2 = blockIdx.x * NB + bb;
-            if (b2 < nb) out[(bh * HD + d) * ld + b2] = stage[bb * HD + d];
+            if (b2 < nb) tout[(bh * HD + d) * ld + b2] = stage[bb * HD + d];
         }
     }
 }
@@ -95,13 +99,19 @@ __global__ __launch_bounds__(128) void kmean_final_kernel(const float* __restric
 // Per-block INT8 quantization of one (head, block): scale = amax/127 over the
 // block's valid tokens and all channels, q = clamp(rint(x/scale), +-127).
 // SMOOTH subtracts the K mean first (one fp32 subtraction).
-template <int BLK, bool SMOOTH>
+// POOL also writes the block's pooled means, pooled[bh][b][d] = (sum of the
+// valid tokens of channel d in token order, from 0) / valid: the raw block is
+// staged in LDS and thread d adds its column in order, so the result is the
+// one colsum_kernel MODE 1 gives.
+template <int BLK, bool SMOOTH, bool POOL>
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ x,
                                                     const float* __restrict__ mu, int N, int nb,
                                                     int8_t* __restrict__ xq,
-                                                    float* __restrict__ scale) {
+                                                    float* __restrict__ scale,
+                                                    float* __restrict__ pooled) {
     constexpr int IT = BLK * 16 / 256;  // 16-byte chunks per thread
     __shared__ float wmax[4];
+    __shared__ __attribute__((aligned(16))) uint16_t raw[POOL ? BLK * HD : 8];
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.y;
     const int b = blockIdx.x;
@@ -122,6 +132,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
         const int row = (tid >> 4) + 16 * it;
         if (row < valid) {
             u16x8 r = *(const u16x8*)(base + (int64_t)row * HD + 8 * g);
+            if (POOL) *(u16x8*)(raw + row * HD + 8 * g) = r;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float f = bf2f(r[e]);
@@ -140,6 +151,11 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const float s = amax / 127.0f;
     if (tid == 0) scale[bh * nb + b] = s;
+    if (POOL && tid < HD) {  // the staged rows are visible after the barrier above
+        float sum = 0.f;
+        for (int row = 0; row < valid; ++row) sum += bf2f(raw[row * HD + tid]);
+        pooled[(bh * nb + b) * HD + tid] = sum / (float)valid;
+    }
     int8_t* qbase = xq + (bh * N + t0) * HD;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -165,15 +181,20 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
 
 hipError_t launch_quant_qk(const uint16_t* q, const uint16_t* k, int64_t BH, int N,
                            int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
-                           float* k_mean, float* ws_part, hipStream_t st) {
+                           float* k_mean, float* ws_part, float* qbar, float* kbarT, int ldk,
+                           hipStream_t st) {
     const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
     hipLaunchKernelGGL((colsum_kernel<KBLK, 0>), dim3((nkb + 15) / 16, BH), dim3(256), 0, st, k, N,
-                       nkb, 0, ws_part);
+                       nkb, ldk, ws_part, kbarT);
     hipLaunchKernelGGL(kmean_final_kernel, dim3(BH), dim3(128), 0, st, ws_part, nkb, N, k_mean);
-    hipLaunchKernelGGL((quant_kernel<QBLK, false>), dim3(nqb, BH), dim3(256), 0, st, q, nullptr, N,
-                       nqb, q_i8, q_scale);
-    hipLaunchKernelGGL((quant_kernel<KBLK, true>), dim3(nkb, BH), dim3(256), 0, st, k, k_mean, N,
-                       nkb, k_i8, k_scale);
+    if (qbar)
+        hipLaunchKernelGGL((quant_kernel<QBLK, false, true>), dim3(nqb, BH), dim3(256), 0, st, q,
+                           nullptr, N, nqb, q_i8, q_scale, qbar);
+    else
+        hipLaunchKernelGGL((quant_kernel<QBLK, false, false>), dim3(nqb, BH), dim3(256), 0, st, q,
+                           nullptr, N, nqb, q_i8, q_scale, nullptr);
+    hipLaunchKernelGGL((quant_kernel<KBLK, true, false>), dim3(nkb, BH), dim3(256), 0, st, k,
+                       k_mean, N, nkb, k_i8, k_scale, nullptr);
     return hipGetLastError();
 }
 
@@ -181,9 +202,9 @@ hipError_t launch_pool(const uint16_t* q, const uint16_t* k, int64_t BH, int N, 
                        float* kbarT, int ldk, hipStream_t st) {
     const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
     hipLaunchKernelGGL((colsum_kernel<QBLK, 1>), dim3((nqb + 7) / 8, BH), dim3(128), 0, st, q, N, nqb,
-                       0, qbar);
+                       0, qbar, nullptr);
     hipLaunchKernelGGL((colsum_kernel<KBLK, 2>), dim3((nkb + 15) / 16, BH), dim3(256), 0, st, k, N,
-                       nkb, ldk, kbarT);
+                       nkb, ldk, kbarT, nullptr);
     return hipGetLastError();
 }
 

@@ -90,11 +90,20 @@ const char* ssa_last_error(void);
  *   q_i8     out: int8 [B,H,N,D]      q_scale out: fp32 [B,H,Nqb]
  *   k_i8     out: int8 [B,H,N,D]      k_scale out: fp32 [B,H,Nkb]
  *   k_mean   out: fp32 [B,H,D]
+ *   pool     out: NULL, or ssa_pool_bytes(s) bytes (256-byte aligned) that
+ *                 receive the pooled block means sla_block_mask scores with
+ *                 (its qbar and kbar, bit-identical, in an internal layout),
+ *                 computed in the same passes over Q and K; hand the buffer
+ *                 to sla_block_mask so it need not read Q and K again.
  *   ws: ssa_workspace_bytes(SSA_OP_QUANT, s, 0, 0) bytes, 256-byte aligned.
  */
 ssa_status sage_quant_qk(const uint16_t* q, const uint16_t* k, ssa_shape s, int8_t* q_i8,
                          float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
-                         void* ws, size_t ws_bytes, void* stream);
+                         void* pool, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the pooled-means buffer of sage_quant_qk / sla_block_mask for
+ * shape s (0 for an invalid shape). */
+size_t ssa_pool_bytes(ssa_shape s);
 
 /* ---------------------------------------------------------------------------
  * sla_block_mask -- the SLA critical-block selection.
@@ -105,13 +114,16 @@ ssa_status sage_quant_qk(const uint16_t* q, const uint16_t* k, ssa_shape s, int8
  * kbar_j likewise for raw K; score_ij = fmaf chain over d = 0..127 from 0;
  * each query block keeps its `keep` best key blocks under (score descending,
  * j ascending), -0.0 equal to +0.0.
+ *   pool in : NULL, or the buffer sage_quant_qk filled for the same Q, K and
+ *             shape: the means are then taken from it, and q, k are not read
+ *             (they may be NULL) and ws is not used (it may be NULL).
  *   kidx out: int32 [B,H,Nqb,keep], kept key blocks in ascending order
  *   mask out: uint8 [B,H,Nqb,Nkb] (1 = kept) or NULL
- *   ws: ssa_workspace_bytes(SSA_OP_MASK, s, keep, 0) bytes.
+ *   ws: ssa_workspace_bytes(SSA_OP_MASK, s, keep, 0) bytes (without pool).
  */
 ssa_status sla_block_mask(const uint16_t* q, const uint16_t* k, ssa_shape s, int64_t keep,
-                          int32_t* kidx, uint8_t* mask, void* ws, size_t ws_bytes,
-                          void* stream);
+                          const void* pool, int32_t* kidx, uint8_t* mask, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * sage_sla_attn_fwd -- SageSLA forward: sparse INT8 softmax attention over the

@@ -82,11 +82,12 @@ def test_quant_rejects_bad_arguments():
     L = _L()
     GB = 1 << 30
     ok = [_p(0), _p(GB), _shape(), _p(2 * GB), _p(3 * GB), _p(4 * GB), _p(5 * GB), _p(6 * GB),
-          _p(7 * GB), 1 << 24, None]
+          None, _p(7 * GB), 1 << 24, None]
 
     def call(**kw):
         args = list(ok)
-        names = ["q", "k", "s", "q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "ws", "n", "st"]
+        names = ["q", "k", "s", "q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "pool", "ws", "n",
+                 "st"]
         for k_, v_ in kw.items():
             args[names.index(k_)] = v_
         return L.sage_quant_qk(*args)
@@ -102,6 +103,9 @@ def test_quant_rejects_bad_arguments():
     assert call(q_i8=_p(0)) == 1  # output aliases input q
     assert call(k_mean=_p(2 * GB + 64)) == 1  # two outputs overlap
     assert b"overlap" in L.ssa_last_error()
+    assert call(pool=_p(8 * GB + 16)) == 1  # pool misaligned
+    assert call(pool=_p(GB)) == 1  # pool overlaps input k
+    assert b"overlap" in L.ssa_last_error()
 
 
 def test_mask_rejects_bad_keep():
@@ -109,8 +113,27 @@ def test_mask_rejects_bad_keep():
     GB = 1 << 30
     s = _shape(N=1000)  # 16 key blocks
     for keep, want in ((0, 1), (17, 1), (16, 3)):
-        st = L.sla_block_mask(_p(0), _p(GB), s, keep, _p(2 * GB), None, None, 0, None)
+        st = L.sla_block_mask(_p(0), _p(GB), s, keep, None, _p(2 * GB), None, None, 0, None)
         assert st == want, (keep, st)
+
+
+def test_mask_with_pool_needs_no_workspace_nor_inputs():
+    L = _L()
+    GB = 1 << 30
+    s = _shape(N=1000)
+    # with a pool, q, k and the workspace are not needed; a bad keep is still caught
+    assert L.sla_block_mask(None, None, s, 0, _p(GB), _p(2 * GB), None, None, 0, None) == 1
+    assert L.sla_block_mask(None, None, s, 4, _p(GB + 16), _p(2 * GB), None, None, 0, None) == 1
+    assert b"pool" in L.ssa_last_error()
+    # kidx inside the pool
+    assert L.sla_block_mask(None, None, s, 4, _p(GB), _p(GB + 256), None, None, 0, None) == 1
+    assert b"overlap" in L.ssa_last_error()
+
+
+def test_pool_bytes():
+    L = _L()
+    assert L.ssa_pool_bytes(_shape(N=75600)) > 0
+    assert L.ssa_pool_bytes(_shape(N=0)) == 0
 
 
 def test_attn_rejects_bad_arguments():

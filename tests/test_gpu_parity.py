@@ -61,11 +61,18 @@ def test_mask_bitexact(orc, B, H, N, topk):
     q, k, v = make_qkv(B, H, N, 128, seed=N + 1)
     keep = ssa.keep_blocks(N, topk)
     say(f"[mask] B{B}H{H}N{N} keep={keep}")
-    kidx, mask = ssa.sla_block_mask(*_gpu(q, k), keep, return_mask=True)
+    qd, kd = _gpu(q, k)
+    kidx, mask = ssa.sla_block_mask(qd, kd, keep, return_mask=True)
+    # the same selection from the pooled means sage_quant_qk hands over
+    pool = ssa.new_pool(qd)
+    ssa.sage_quant_qk(qd, kd, pool)
+    kidx_p, mask_p = ssa.sla_block_mask(qd, kd, keep, return_mask=True, pool=pool)
     torch.cuda.synchronize()
     okidx, omask = orc.block_mask(bits(q), bits(k), keep)
     assert np.array_equal(flat(kidx), okidx)
     assert np.array_equal(flat(mask), omask)
+    assert np.array_equal(flat(kidx_p), okidx)
+    assert np.array_equal(flat(mask_p), omask)
 
 
 def test_mask_ties_break_to_lower_block(orc):
@@ -193,5 +200,5 @@ def test_workspace_too_small_is_reported():
     mu = torch.empty(128, dtype=torch.float32, device=DEV)
     st = L.sage_quant_qk(qd.data_ptr(), kd.data_ptr(), ssa.Shape(1, 1, 256, 128),
                          outs[0].data_ptr(), sc[0].data_ptr(), outs[1].data_ptr(),
-                         sc[1].data_ptr(), mu.data_ptr(), dummy.data_ptr(), 16, None)
+                         sc[1].data_ptr(), mu.data_ptr(), None, dummy.data_ptr(), 16, None)
     assert st == 3
