@@ -127,15 +127,22 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
     float v[IT][8];
     float amax = 0.f;
     const uint16_t* base = x + (bh * N + t0) * HD;
+    // every load is issued before any is used (rows past the block's end
+    // re-read its last row and are then dropped), so they are in flight together
+    u16x8 r8[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int row = min((tid >> 4) + 16 * it, valid - 1);
+        r8[it] = *(const u16x8*)(base + (int64_t)row * HD + 8 * g);
+    }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int row = (tid >> 4) + 16 * it;
         if (row < valid) {
-            u16x8 r = *(const u16x8*)(base + (int64_t)row * HD + 8 * g);
-            if (POOL) *(u16x8*)(raw + row * HD + 8 * g) = r;
+            if (POOL) *(u16x8*)(raw + row * HD + 8 * g) = r8[it];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float f = bf2f(r[e]);
+                float f = bf2f(r8[it][e]);
                 if (SMOOTH) f = f - m8[e];
                 v[it][e] = f;
                 amax = fmaxf(amax, fabsf(f));
@@ -152,8 +159,17 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
     const float s = amax / 127.0f;
     if (tid == 0) scale[bh * nb + b] = s;
     if (POOL && tid < HD) {  // the staged rows are visible after the barrier above
+        // reads in batches of 32 so they are in flight together; the adds
+        // stay in token order over the valid rows
         float sum = 0.f;
-        for (int row = 0; row < valid; ++row) sum += bf2f(raw[row * HD + tid]);
+        for (int r0 = 0; r0 < valid; r0 += 32) {
+            float t[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) t[u] = bf2f(raw[min(r0 + u, BLK - 1) * HD + tid]);
+#pragma unroll
+            for (int u = 0; u < 32; ++u)
+                if (r0 + u < valid) sum += t[u];
+        }
         pooled[(bh * nb + b) * HD + tid] = sum / (float)valid;
     }
     int8_t* qbase = xq + (bh * N + t0) * HD;
