@@ -100,28 +100,22 @@ __device__ __forceinline__ void wave_select_row(const float* __restrict__ s, int
     // key equals kmin)
     const uint32_t T = npass == 0 ? kmin
                                   : (prefix >> common) | (common ? kmin & (~0u << (32 - common)) : 0u);
-    // emit: lane l owns the contiguous range [l*chunk, (l+1)*chunk) of j
-    const int chunk = (nkb + 63) >> 6;
-    const int j0 = lane * chunk, j1 = min(nkb, j0 + chunk);
-    int neq = 0;
-    for (int j = j0; j < j1; ++j) neq += order_key(s[j]) == T ? 1 : 0;
-    int eq_rank = wave_incl_scan(neq) - neq;  // keys equal to T before j0
-    int nsel = 0;
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t key = order_key(s[j]);
-        const bool eq = key == T;
-        nsel += (key > T || (eq && eq_rank < rem)) ? 1 : 0;
-        eq_rank += eq ? 1 : 0;
-    }
-    int out = wave_incl_scan(nsel) - nsel;
-    eq_rank = wave_incl_scan(neq) - neq;
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t key = order_key(s[j]);
-        const bool eq = key == T;
-        const bool sel = key > T || (eq && eq_rank < rem);
-        eq_rank += eq ? 1 : 0;
-        if (sel) krow[out++] = j;
-        if (mrow) mrow[j] = (uint8_t)sel;
+    // emit in ascending j, 64 blocks per round: lane l looks at j = 64t + l; a
+    // key equal to T is kept while fewer than `rem` equal keys come before it,
+    // and the kept blocks of a round are compacted by their rank in the ballot
+    const uint64_t below = (1ull << lane) - 1ull;
+    int out = 0, eq_seen = 0;
+    for (int j0 = 0; j0 < nkb; j0 += 64) {
+        const int j = j0 + lane;
+        const uint32_t key = j < nkb ? order_key(s[j]) : 0u;
+        const bool eq = j < nkb && key == T;
+        const uint64_t eqm = __builtin_amdgcn_ballot_w64(eq);
+        const bool sel = j < nkb && (key > T || (eq && eq_seen + __builtin_popcountll(eqm & below) < rem));
+        const uint64_t selm = __builtin_amdgcn_ballot_w64(sel);
+        if (sel) krow[out + __builtin_popcountll(selm & below)] = j;
+        if (mrow && j < nkb) mrow[j] = (uint8_t)sel;
+        out += __builtin_popcountll(selm);
+        eq_seen += __builtin_popcountll(eqm);
     }
 }
 
