@@ -53,6 +53,8 @@ def lib():
                                        C.c_int]),
             "orc_dense_rows": (None, [_p, _p, _p, _i64, _i64, _i64, C.c_float, _p, _i64, _p,
                                       C.c_int]),
+            "orc_w8a8_quant": (None, [_p, _i64, _i64, _p, _p, C.c_int]),
+            "orc_w8a8_gemm": (None, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, C.c_int]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -276,3 +278,37 @@ def sagesla_rows(q, k, v, quantized, bh, tokens, kidx_head=None, branches=3, sm_
         res["exact"] = res["exact"] + ol
         res["linear"] = ol
     return res
+
+
+# ---------------------------------------------------------------------------
+# W8A8 linear layer (page 5, Pillar Three): 128 x 128 block INT8 quantization
+# of activations x [M][K] and weights w [N][K]; y = x . w^T.
+
+W8_BLK = 128
+
+
+def w8a8_quant(x, nthreads=None):
+    """(q int8 [rows][cols], scale fp32 [ceil(rows/128)][cols/128]) of a bf16 matrix."""
+    x = _u16(x)
+    rows, cols = x.shape
+    assert cols % W8_BLK == 0
+    q = np.empty((rows, cols), np.int8)
+    sc = np.empty(((rows + W8_BLK - 1) // W8_BLK, cols // W8_BLK), np.float32)
+    lib().orc_w8a8_quant(_ptr(x), rows, cols, _ptr(q), _ptr(sc), nthreads or threads())
+    return q, sc
+
+
+def w8a8_gemm(xq, sx, wq, sw, rows=None, nthreads=None):
+    """fp32 y [len(rows)][N] (all rows when rows is None) of the quantized product."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    sx = np.ascontiguousarray(sx, dtype=np.float32)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K and K % W8_BLK == 0 and N % W8_BLK == 0
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    y = np.empty((len(rows), N), np.float32)
+    lib().orc_w8a8_gemm(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(rows), len(rows),
+                        _ptr(y), nthreads or threads())
+    return y

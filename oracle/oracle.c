@@ -597,3 +597,86 @@ void orc_dense_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
     dense_ctx c = {q, k, v, N, D, bh, (double)default_sm(sm_scale, D), tokens, out};
     orc_parallel_for(R, nthreads, dense_task, &c);
 }
+
+/* ------------------------------------------------------------------------ */
+/* W8A8 linear layer (page 5, "Four Technical Pillars", Pillar Three: INT8  */
+/* weights and activations, quantized with a block-wise granularity of     */
+/* 128x128).                                                                */
+
+typedef struct {
+    const uint16_t* x;
+    int64_t rows, cols, nrb, ncb;
+    int8_t* q;
+    float* scale;
+} w8_quant_ctx;
+
+/* One 128 x 128 block: the Pillar One rule of orc_quant over the block's
+ * valid rows (a partial last row block) and its 128 columns. */
+static void w8_quant_task(void* vctx, int64_t idx) {
+    w8_quant_ctx* c = (w8_quant_ctx*)vctx;
+    int64_t rb = idx / c->ncb, cb = idx % c->ncb;
+    int64_t r0 = rb * ORC_W8_BLK, r1 = r0 + ORC_W8_BLK < c->rows ? r0 + ORC_W8_BLK : c->rows;
+    int64_t c0 = cb * ORC_W8_BLK;
+    float amax = 0.0f;
+    for (int64_t r = r0; r < r1; ++r)
+        for (int64_t k = c0; k < c0 + ORC_W8_BLK; ++k) {
+            float a = fabsf(orc_bf16_to_f32(c->x[r * c->cols + k]));
+            if (a > amax) amax = a;
+        }
+    float s = amax / 127.0f;
+    c->scale[rb * c->ncb + cb] = s;
+    for (int64_t r = r0; r < r1; ++r)
+        for (int64_t k = c0; k < c0 + ORC_W8_BLK; ++k) {
+            int8_t q = 0;
+            if (s > 0.0f) {
+                float v = rintf(orc_bf16_to_f32(c->x[r * c->cols + k]) / s);
+                if (v > 127.0f) v = 127.0f;
+                if (v < -127.0f) v = -127.0f;
+                q = (int8_t)v;
+            }
+            c->q[r * c->cols + k] = q;
+        }
+}
+
+void orc_w8a8_quant(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
+                    int nthreads) {
+    w8_quant_ctx c = {x, rows, cols, (rows + ORC_W8_BLK - 1) / ORC_W8_BLK, cols / ORC_W8_BLK, q,
+                      scale};
+    orc_parallel_for(c.nrb * c.ncb, nthreads, w8_quant_task, &c);
+}
+
+typedef struct {
+    const int8_t *xq, *wq;
+    const float *sx, *sw;
+    int64_t M, N, K;
+    const int64_t* rows;
+    float* y;
+} w8_gemm_ctx;
+
+/* One output row: for each column n, the exact int32 sum of each 128-wide
+ * column block kb of K, then y = fmaf((float)I_kb, s_kb, y) in ascending kb
+ * from 0, s_kb = fl32(sx[mb][kb] * sw[nb][kb]). */
+static void w8_gemm_task(void* vctx, int64_t r) {
+    w8_gemm_ctx* c = (w8_gemm_ctx*)vctx;
+    int64_t m = c->rows[r], nkb = c->K / ORC_W8_BLK, mb = m / ORC_W8_BLK;
+    const int8_t* xr = c->xq + m * c->K;
+    for (int64_t n = 0; n < c->N; ++n) {
+        const int8_t* wr = c->wq + n * c->K;
+        int64_t nb = n / ORC_W8_BLK;
+        float y = 0.0f;
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+            int32_t acc = 0;
+            for (int64_t k = kb * ORC_W8_BLK; k < (kb + 1) * ORC_W8_BLK; ++k)
+                acc += (int32_t)xr[k] * (int32_t)wr[k];
+            float s = c->sx[mb * nkb + kb] * c->sw[nb * nkb + kb];
+            y = fmaf((float)acc, s, y);
+        }
+        c->y[r * c->N + n] = y;
+    }
+}
+
+void orc_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int64_t M,
+                   int64_t N, int64_t K, const int64_t* rows, int64_t R, float* y, int nthreads) {
+    w8_gemm_ctx c = {xq, wq, sx, sw, M, N, K, rows, y};
+    orc_parallel_for(R, nthreads, w8_gemm_task, &c);
+}

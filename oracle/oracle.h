@@ -18,6 +18,10 @@
  *   scores; the sparse softmax branch over the kept blocks; the elu+1 linear
  *   branch over the other blocks; their sum.
  *
+ * And, from Pillar Three (INT8 weights and activations in the linear layers,
+ * block-wise 128x128): the block quantization of both operands and the
+ * block-dequantized INT8 product y = x . w^T.
+ *
  * Conventions: bf16 values travel as uint16_t bit patterns. Tensors are
  * row-major [BH][N][D] with D fastest (BH = B*H flattened). Query blocks are
  * 128 tokens, key blocks 64 tokens; the last block of each may be partial.
@@ -113,6 +117,27 @@ void orc_linear_rows(const uint16_t* q, int64_t N, int64_t D, int64_t bh,
 void orc_dense_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t N,
                     int64_t D, int64_t bh, float sm_scale, const int64_t* tokens, int64_t R,
                     double* out, int nthreads);
+
+/* W8A8 linear layer (page 5, "Four Technical Pillars", Pillar Three: INT8
+ * weights and activations, block-wise granularity 128x128).
+ * Readings: y = x . w^T with x [M][K] activations and w [N][K] weights (a
+ * linear layer's weight layout), no bias; K and N multiples of 128. */
+#define ORC_W8_BLK 128
+
+/* Per 128 x 128 block of a row-major [rows][cols] bf16 matrix (cols a
+ * multiple of 128, a partial last row block uses its valid rows): the
+ * Pillar One rule, scale = max|v|/127 (fp32), q = clamp(rint(v/scale),
+ * -127, 127), amax = 0 giving scale 0 and q = 0.
+ * scale: [ceil(rows/128)][cols/128]. */
+void orc_w8a8_quant(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
+                    int nthreads);
+
+/* y[r][n] for the listed rows m = rows[r]: per 128-wide column block kb of K
+ * the exact int32 I = sum_k xq[m][k] * wq[n][k]; then y = fmaf((float)I, s, y)
+ * in ascending kb from 0.0f with s = fl32(sx[m/128][kb] * sw[n/128][kb]). */
+void orc_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int64_t M,
+                   int64_t N, int64_t K, const int64_t* rows, int64_t R, float* y /*[R][N]*/,
+                   int nthreads);
 
 #ifdef __cplusplus
 }

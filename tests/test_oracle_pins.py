@@ -517,3 +517,119 @@ def test_linear_states_sum_to_global_linear_attention(orc):
     fk = _phi(kf)
     assert np.allclose(h.sum(0), fk.T @ vf, rtol=1e-13, atol=1e-10)
     assert np.allclose(z.sum(0), fk.sum(0), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# W8A8 linear layer (page 5, Pillar Three: INT8 weights and activations,
+# block-wise 128x128). y = x . w^T with x [M][K], w [N][K].
+
+def _bf16_matrix(a):
+    """float array -> bf16 bit patterns (RNE), as numpy uint16."""
+    return _bits(torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)))
+
+
+def test_w8a8_quant_golden_ties(orc):
+    # one 128x128 block whose amax is 127 has scale 1.0 exactly: the quantized
+    # values are the round-half-even integers of the inputs
+    x = np.zeros((128, 256), np.float32)
+    x[0, 0] = 127.0
+    vals = [2.5, -3.5, 0.5, 1.5, -0.5, 126.5, -127.0]
+    want = [2, -4, 0, 2, 0, 126, -127]
+    for n, v in enumerate(vals):
+        x[1 + n, 3 + n] = v
+    x[5, 200] = 3.0  # second column block: amax 3, scale 3/127
+    q, s = orc.w8a8_quant(_bf16_matrix(x))
+    assert s.shape == (1, 2)
+    assert s[0, 0] == np.float32(1.0)
+    assert s[0, 1] == np.float32(3.0) / np.float32(127.0)
+    for n, w in enumerate(want):
+        assert q[1 + n, 3 + n] == w
+    assert q[0, 0] == 127 and q[5, 200] == 127
+    assert np.count_nonzero(q) == len([w for w in want if w]) + 2
+
+
+def test_w8a8_quant_partial_row_block_and_invariants(orc):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((300, 384)).astype(np.float32)
+    x[256:, 128:256] *= 40.0  # the partial last row block alone is large
+    xb = _bf16_matrix(x)
+    q, s = orc.w8a8_quant(xb)
+    xf = _f(xb)
+    assert s.shape == (3, 3)
+    for rb in range(3):
+        for cb in range(3):
+            blk = xf[128 * rb:128 * (rb + 1), 128 * cb:128 * (cb + 1)]
+            qb = q[128 * rb:128 * (rb + 1), 128 * cb:128 * (cb + 1)].astype(np.float64)
+            amax = np.float32(np.abs(blk).max())
+            assert s[rb, cb] == amax / np.float32(127.0)  # only the block's own rows count
+            assert np.abs(qb).max() == 127
+            err = np.abs(blk.astype(np.float64) - qb * float(s[rb, cb]))
+            assert err.max() <= float(s[rb, cb]) / 2 * (1 + 2.0 ** -20)
+
+
+def test_w8a8_gemm_is_the_exact_fma_chain(orc):
+    # independent recomputation in exact rational arithmetic: int64 block sums,
+    # s = fl32(sx * sw), then y = fl32(I * s + y) per column block in order
+    rng = np.random.default_rng(5)
+    M, K, N = 5, 384, 128
+    x = _bf16_matrix(rng.standard_normal((M, K)) * 3)
+    w = _bf16_matrix(rng.standard_normal((N, K)) * 0.05)
+    xq, sx = orc.w8a8_quant(x)
+    wq, sw = orc.w8a8_quant(w)
+    y = orc.w8a8_gemm(xq, sx, wq, sw)
+    for m in range(M):
+        for n in range(0, N, 7):
+            acc = Fraction(0)
+            for kb in range(K // 128):
+                sl = slice(128 * kb, 128 * (kb + 1))
+                i = int(np.dot(xq[m, sl].astype(np.int64), wq[n, sl].astype(np.int64)))
+                s = f32_of(Fraction(float(sx[m // 128, kb])) * Fraction(float(sw[n // 128, kb])))
+                acc = Fraction(f32_of(Fraction(i) * Fraction(s) + acc))
+            assert y[m, n] == np.float32(float(acc)), (m, n)
+
+
+def test_w8a8_gemm_power_of_two_scales_is_an_integer_product(orc):
+    # every block's amax is 127 * 2^e, so every scale is a power of two, every
+    # quantized value is x / scale exactly, and the product is exact integers
+    rng = np.random.default_rng(7)
+    M, K, N = 130, 256, 256
+    ex = rng.integers(-3, 3, size=(2, 2))
+    ew = rng.integers(-3, 3, size=(2, 2))
+    xi = rng.integers(-127, 128, size=(M, K))
+    wi = rng.integers(-127, 128, size=(N, K))
+    for rb in range(2):
+        for cb in range(2):
+            xi[128 * rb, 128 * cb] = 127
+            wi[128 * rb, 128 * cb] = -127
+    x = np.zeros((M, K)); w = np.zeros((N, K))
+    for rb in range(2):
+        for cb in range(2):
+            rs, cs = slice(128 * rb, 128 * (rb + 1)), slice(128 * cb, 128 * (cb + 1))
+            x[rs, cs] = xi[rs, cs] * 2.0 ** ex[rb, cb]
+            w[rs, cs] = wi[rs, cs] * 2.0 ** ew[rb, cb]
+    xq, sx = orc.w8a8_quant(_bf16_matrix(x))
+    wq, sw = orc.w8a8_quant(_bf16_matrix(w))
+    assert np.array_equal(xq, xi) and np.array_equal(wq, wi)
+    y = orc.w8a8_gemm(xq, sx, wq, sw)
+    want = np.zeros((M, N))
+    for kb in range(2):
+        cs = slice(128 * kb, 128 * (kb + 1))
+        prod = xi[:, cs].astype(np.int64) @ wi[:, cs].astype(np.int64).T
+        scale = (2.0 ** ex[(np.arange(M) // 128), kb])[:, None] * (2.0 ** ew[(np.arange(N) // 128), kb])[None, :]
+        want += prod * scale
+    assert np.array_equal(y.astype(np.float64), want)
+
+
+def test_w8a8_gemm_close_to_fp64_product(orc):
+    # the quantized product stays within the 8-bit quantization error of the
+    # plain fp64 product of the bf16 operands
+    rng = np.random.default_rng(11)
+    M, K, N = 200, 512, 256
+    x = _bf16_matrix(rng.standard_normal((M, K)))
+    w = _bf16_matrix(rng.standard_normal((N, K)) * 0.02)
+    xq, sx = orc.w8a8_quant(x)
+    wq, sw = orc.w8a8_quant(w)
+    y = orc.w8a8_gemm(xq, sx, wq, sw).astype(np.float64)
+    ref = _f(x).astype(np.float64) @ _f(w).astype(np.float64).T
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert 1e-3 < rel < 2e-2, rel
