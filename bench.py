@@ -236,6 +236,89 @@ def copy_calibration(mib):
     print(f"# copy calibration: 3 x {mib} MiB device copies", file=sys.stderr, flush=True)
 
 
+def bench_w8a8(args):
+    """The W8A8 linear layer (page 5, Pillar Three) on the 14B / 720p linear
+    shape: per step, the block quantization of the activations and the
+    block-dequantized INT8 product with weights quantized once beforehand."""
+    import torch
+
+    import bit_sparse_attention_amd as ssa
+    from bit_sparse_attention_amd.workloads import (LINEAR_BENCH_WORKLOAD, LINEAR_WORKLOADS,
+                                                    make_linear_workload)
+
+    wl = LINEAR_WORKLOADS[args.workload or LINEAR_BENCH_WORKLOAD]
+    dev = torch.device("cuda:0")
+    print(f"# generating {wl.name}", file=sys.stderr, flush=True)
+    x, wt = make_linear_workload(wl)
+    xd, wd = x.to(dev), wt.to(dev)
+    wq, sw = ssa.w8a8_quant(wd)
+    xq, sx = ssa.w8a8_quant(xd)
+    for _ in range(args.warmup):
+        xq, sx = ssa.w8a8_quant(xd)
+        y = ssa.w8a8_gemm(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        xq, sx = ssa.w8a8_quant(xd)
+        e1.record()
+        y = ssa.w8a8_gemm(xq, sx, wq, sw)
+        e2.record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    q_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    g_ms = [b.elapsed_time(c) for _, b, c in ev]
+    ops = 2.0 * wl.M * wl.N * wl.K
+    g_mean = float(np.mean(g_ms))
+    g_tops = ops / (g_mean * 1e-3) / 1e12
+    line = {
+        "metric": "W8A8 linear (block-128x128 INT8) ms/call + TOPS (% INT8 MFMA peak), 14B-720p linear shape, 1 GPU",
+        "value": ops / (ms_step * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 x int8 -> int32 per 128-block, fp32 dequantized accumulation",
+        "data": "synthetic (seeded; x ~ N(0,1) with 1% of channels x20, w ~ N(0,1)/sqrt(K))",
+        "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "block": 128},
+        "quant_ms": float(np.mean(q_ms)),
+        "gemm_ms": g_mean,
+        "gemm_ms_pct": {f"p{p}": float(np.percentile(g_ms, p)) for p in (10, 50, 90)},
+        "roofline": {"bound": "mfma", "achieved": g_tops, "peak": INT8_PEAK_TOPS,
+                     "unit": "TOP/s", "frac": g_tops / INT8_PEAK_TOPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from bit_sparse_attention_amd.workloads import bf16_bits
+
+        nthreads = min(16, os.cpu_count() or 1)
+        xb = bf16_bits(x).reshape(wl.M, wl.K)
+        wb = bf16_bits(wt).reshape(wl.N, wl.K)
+        t0 = time.perf_counter()
+        oxq, osx = oracle.w8a8_quant(xb, nthreads)
+        owq, osw = oracle.w8a8_quant(wb, nthreads)
+        tq = time.perf_counter() - t0
+        rows = np.arange(0, wl.M, max(1, wl.M // 512))
+        t0 = time.perf_counter()
+        oracle.w8a8_gemm(oxq, osx, owq, osw, rows=rows, nthreads=nthreads)
+        tg = time.perf_counter() - t0
+        t_full = tq + tg * wl.M / len(rows)
+        line["cpu_baseline"] = {
+            "value": ops / t_full / 1e12, "unit": "TOPS", "cores": nthreads, "kind": "oracle",
+            "sample": (f"quantization of x and w in full ({tq:.1f} s) and the product for "
+                       f"{len(rows)} of {wl.M} rows ({tg:.1f} s) on {nthreads} threads of "
+                       f"{_cpu_model()}, extrapolated over the rows to {t_full:.0f} s"),
+        }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +337,8 @@ def main():
                     help="print a per-dispatch counter table for the attention kernel and exit")
     ap.add_argument("--pmc-command", action="append", default=[],
                     help="command line recorded in the summary outputs")
+    ap.add_argument("--w8a8", action="store_true",
+                    help="benchmark the W8A8 linear layer instead (its own JSON line)")
     args = ap.parse_args()
     if args.pmc_summary or args.trace_summary or args.pmc_table:
         from bit_sparse_attention_amd.workloads import BENCH_WORKLOAD
@@ -271,6 +356,10 @@ def main():
               "per-head independent and this build measures one GPU's share; no multi-GPU "
               "figure is produced.", file=sys.stderr)
         sys.exit(2)
+
+    if args.w8a8:
+        bench_w8a8(args)
+        return
 
     import torch
 

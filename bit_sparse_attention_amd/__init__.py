@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "sage_quant_qk", "sla_block_mask", "sage_sla_attn_fwd", "sage_qk_int32_tiles", "sagesla",
     "SageSLAPlan", "KernelTimer", "keep_blocks", "num_q_blocks", "num_k_blocks", "workspace_bytes",
-    "pool_bytes", "new_pool", "lib_path",
+    "pool_bytes", "new_pool", "lib_path", "w8a8_quant", "w8a8_gemm", "w8a8_linear",
     "SPARSE", "LINEAR", "OP_QUANT", "OP_MASK", "OP_ATTN",
 ]
 
@@ -73,6 +73,8 @@ def _load():
         "sage_quant_qk": (i32, [_p, _p, Shape, _p, _p, _p, _p, _p, _p, _p, sz, _p]),
         "sla_block_mask": (i32, [_p, _p, Shape, i64, _p, _p, _p, _p, sz, _p]),
         "ssa_pool_bytes": (sz, [Shape]),
+        "w8a8_quant": (i32, [_p, i64, i64, _p, _p, _p]),
+        "w8a8_gemm": (i32, [_p, _p, _p, _p, i64, i64, i64, _p, _p, _p]),
         "sage_sla_attn_fwd": (i32, [_p, _p, _p, Shape, _p, _p, _p, _p, _p, i64, i32, C.c_float,
                                     _p, _p, _p, sz, _p]),
         "sage_qk_int32_tiles": (i32, [_p, _p, Shape, _p, i64, _p, _p]),
@@ -260,6 +262,48 @@ def sagesla(q, k, v, topk: float | None = 0.1, linear: bool = True, sm_scale: fl
     br = SPARSE | (LINEAR if linear else 0)
     return sage_sla_attn_fwd(q, k, v, q_i8, q_scale, k_i8, k_scale, kidx, keep, br, sm_scale,
                              return_f32)
+
+
+W8_BLK = 128
+
+
+def w8a8_quant(x):
+    """128x128 block INT8 quantization of a bf16 [rows][cols] matrix (page 5,
+    Pillar Three). Returns (q int8 [rows][cols], scale fp32 [ceil(rows/128)][cols/128])."""
+    _need_gpu("x", x, torch.bfloat16)
+    if x.dim() != 2 or x.shape[1] % W8_BLK:
+        raise ValueError(f"x must be [rows][cols] with cols a multiple of 128, got {tuple(x.shape)}")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    sc = torch.empty(((rows + W8_BLK - 1) // W8_BLK, cols // W8_BLK), dtype=torch.float32,
+                     device=x.device)
+    _check("w8a8_quant", _load().w8a8_quant(_ptr(x), rows, cols, _ptr(q), _ptr(sc),
+                                            _stream(x.device)))
+    return q, sc
+
+
+def w8a8_gemm(xq, sx, wq, sw, return_f32: bool = False):
+    """y = x . w^T from the block-quantized operands (w in the [out][in] layout)."""
+    _need_gpu("xq", xq, torch.int8)
+    M, K = xq.shape
+    _need_gpu("wq", wq, torch.int8)
+    N = wq.shape[0]
+    if wq.shape[1] != K or K % W8_BLK or N % W8_BLK:
+        raise ValueError("wq must be [N][K] with N and K multiples of 128")
+    _need_gpu("sx", sx, torch.float32, ((M + W8_BLK - 1) // W8_BLK, K // W8_BLK))
+    _need_gpu("sw", sw, torch.float32, (N // W8_BLK, K // W8_BLK))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    y32 = torch.empty((M, N), dtype=torch.float32, device=xq.device) if return_f32 else None
+    _check("w8a8_gemm", _load().w8a8_gemm(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K,
+                                          _ptr(y), _ptr(y32), _stream(xq.device)))
+    return (y, y32) if return_f32 else y
+
+
+def w8a8_linear(x, wq, sw, return_f32: bool = False):
+    """The W8A8 linear layer on bf16 activations x [M][K] with pre-quantized
+    weights (w8a8_quant of w [N][K]): quantize x, then the INT8 product."""
+    xq, sx = w8a8_quant(x)
+    return w8a8_gemm(xq, sx, wq, sw, return_f32)
 
 
 class KernelTimer:

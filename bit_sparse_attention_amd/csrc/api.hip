@@ -426,6 +426,57 @@ ssa_status sage_qk_int32_tiles(const int8_t* q_i8, const int8_t* k_i8, ssa_shape
     return SSA_OK;
 }
 
+// ---- W8A8 linear layer --------------------------------------------------------
+
+static const int64_t W8_MAX = 1 << 20;  // rows, columns and K at most 2^20
+
+ssa_status w8a8_quant(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
+                      void* stream) {
+    g_err[0] = 0;
+    if (rows < 1 || rows > W8_MAX || cols < 128 || cols > W8_MAX || cols % 128)
+        return fail(SSA_ERR_INVALID, "w8a8_quant: rows=%lld cols=%lld (cols a multiple of 128, "
+                    "both in [1, 2^20])", (long long)rows, (long long)cols);
+    TRY(need_ptr(x, 16, "x"));
+    TRY(need_ptr(q, 16, "q"));
+    TRY(need_ptr(scale, 4, "scale"));
+    const size_t nel = (size_t)rows * cols;
+    const size_t nsc = (size_t)((rows + 127) / 128) * (cols / 128);
+    const Range ins[] = {{x, nel * 2, "x"}};
+    const Range outs[] = {{q, nel, "q"}, {scale, nsc * 4, "scale"}};
+    TRY(check_alias(outs, 2, ins, 1));
+    TRY(check_device());
+    hipError_t e = launch_w8a8_quant(x, (int)rows, (int)cols, q, scale, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "w8a8_quant launch");
+    return SSA_OK;
+}
+
+ssa_status w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                     int64_t M, int64_t N, int64_t K, uint16_t* y, float* y32, void* stream) {
+    g_err[0] = 0;
+    if (M < 1 || M > W8_MAX || N < 128 || N > W8_MAX || N % 128 || K < 128 || K > W8_MAX ||
+        K % 128)
+        return fail(SSA_ERR_INVALID, "w8a8_gemm: M=%lld N=%lld K=%lld (N, K multiples of 128, "
+                    "all in [1, 2^20])", (long long)M, (long long)N, (long long)K);
+    TRY(need_ptr(xq, 16, "xq"));
+    TRY(need_ptr(wq, 16, "wq"));
+    TRY(need_ptr(sx, 4, "sx"));
+    TRY(need_ptr(sw, 4, "sw"));
+    TRY(need_ptr(y, 16, "y"));
+    if (y32 && !aligned(y32, 16)) return fail(SSA_ERR_INVALID, "y32 is not 16-byte aligned");
+    const size_t nkb = (size_t)K / 128;
+    const Range ins[] = {{xq, (size_t)M * K, "xq"},
+                         {wq, (size_t)N * K, "wq"},
+                         {sx, (size_t)((M + 127) / 128) * nkb * 4, "sx"},
+                         {sw, (size_t)(N / 128) * nkb * 4, "sw"}};
+    const Range outs[] = {{y, (size_t)M * N * 2, "y"}, {y32, y32 ? (size_t)M * N * 4 : 0, "y32"}};
+    TRY(check_alias(outs, 2, ins, 4));
+    TRY(check_device());
+    hipError_t e = launch_w8a8_gemm(xq, sx, wq, sw, (int)M, (int)N, (int)K, y, y32,
+                                    (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "w8a8_gemm launch");
+    return SSA_OK;
+}
+
 ssa_status ssa_kernel_timer_start(int max_launches) {
     g_err[0] = 0;
     if (max_launches < 1 || max_launches > (1 << 16))

@@ -29,6 +29,12 @@ size_t msel_bytes(int64_t BH, int64_t nqb, int64_t nkbp);
 hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, const float* htot,
                              int64_t BH, int N, uint32_t* msel, float* hnon, hipStream_t st);
 
+// w8a8.hip
+hipError_t launch_w8a8_quant(const uint16_t* x, int rows, int cols, int8_t* q, float* scale,
+                             hipStream_t st);
+hipError_t launch_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                            int M, int N, int K, uint16_t* y, float* y32, hipStream_t st);
+
 // attn.hip
 struct AttnArgs {
     const int8_t* q_i8;

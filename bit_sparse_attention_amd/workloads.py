@@ -96,3 +96,50 @@ def make_workload(w: Workload | str):
 def bf16_bits(x: torch.Tensor):
     """View a contiguous bf16 tensor as a numpy uint16 array (no copy)."""
     return x.contiguous().view(torch.int16).numpy().view("uint16")
+
+
+# ---------------------------------------------------------------------------
+# W8A8 linear layer (page 5, Pillar Three). The benchmarked shape is a linear
+# layer of the 14B / 720p model on one frame sequence: 75600 tokens of width
+# H * D = 40 * 128 = 5120, mapped 5120 -> 5120.
+#
+# Recipe (one torch.Generator seeded with ``seed``): x = randn(M, K); then
+# w = randn(N, K) / sqrt(K) (the scale of a default-initialised linear layer);
+# if ``outliers``: 1% of the K channels of x (randperm(K)[: K // 100]) are
+# multiplied by 20 after drawing (the activation outlier channels block
+# quantization meets). Every draw is fp32, cast to bf16 with round-to-nearest-even.
+
+@dataclass(frozen=True)
+class LinearWorkload:
+    name: str
+    M: int
+    N: int
+    K: int
+    outliers: bool = False
+    seed: int = 0
+
+
+LINEAR_WORKLOADS = {
+    w.name: w
+    for w in (
+        LinearWorkload("w8a8_m1000_k512_n384", 1000, 384, 512, outliers=True),
+        LinearWorkload("w8a8_m75600_k5120_n5120", 75600, 5120, 5120, outliers=True),
+    )
+}
+
+LINEAR_BENCH_WORKLOAD = "w8a8_m75600_k5120_n5120"
+
+
+def make_linear(M: int, N: int, K: int, seed: int = 0, outliers: bool = False):
+    """Return bf16 CPU tensors x [M][K] and w [N][K] (recipe above)."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((M, K), generator=g)
+    w = torch.randn((N, K), generator=g) / (K ** 0.5)
+    if outliers:
+        idx = torch.randperm(K, generator=g)[: max(1, K // 100)]
+        x[:, idx] *= 20.0
+    return x.to(torch.bfloat16), w.to(torch.bfloat16)
+
+
+def make_linear_workload(w: LinearWorkload):
+    return make_linear(w.M, w.N, w.K, w.seed, w.outliers)

@@ -171,6 +171,40 @@ ssa_status sage_qk_int32_tiles(const int8_t* q_i8, const int8_t* k_i8, ssa_shape
                                const int32_t* tiles, int64_t T, int32_t* out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * W8A8 linear layer -- page 5, "Four Technical Pillars", Pillar Three: the
+ * linear layers run with INT8 weights and activations, quantized with a
+ * block-wise granularity of 128x128.
+ * Readings: y = x . w^T for activations x [M][K] and weights w [N][K] (a
+ * linear layer's [out][in] layout), no bias; K and N multiples of 128. Each
+ * operand is quantized per 128-row x 128-column block with the rule of
+ * sage_quant_qk (scale = max|v|/127 in fp32 over the block's valid rows,
+ * q = clamp(rint(v/scale), -127, 127), ties to even, scale 0 and q = 0 for an
+ * all-zero block).
+ *
+ * w8a8_quant -- block quantization of a row-major bf16 [rows][cols] matrix
+ * (activations or weights; cols a multiple of 128, rows and cols <= 2^20).
+ *   x     in : bf16 [rows][cols], 16-byte aligned
+ *   q     out: int8 [rows][cols], 16-byte aligned
+ *   scale out: fp32 [ceil(rows/128)][cols/128]
+ */
+ssa_status w8a8_quant(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, float* scale,
+                      void* stream);
+
+/* w8a8_gemm -- the block-dequantized INT8 product. For each 128-wide block kb
+ * of K, I = sum over the block of xq[m][k] * wq[n][k] (exact int32), and
+ * y[m][n] = fmaf((float)I, fl32(sx[m/128][kb] * sw[n/128][kb]), y) in
+ * ascending kb from 0 (INT8 matrix cores, fp32 accumulation).
+ *   xq, sx in : w8a8_quant of x [M][K];  wq, sw in : w8a8_quant of w [N][K]
+ *   y      out: bf16 [M][N] (round to nearest even of the fp32 result)
+ *   y32    out: fp32 [M][N] copy before rounding, or NULL (16-byte aligned)
+ * M, N, K <= 2^20; N and K multiples of 128. Errors as for the entry points
+ * above (validation before anything is enqueued, SSA_ERR_HIP on a failed
+ * launch).
+ */
+ssa_status w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                     int64_t M, int64_t N, int64_t K, uint16_t* y, float* y32, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel timer (for benchmarks). After ssa_kernel_timer_start(n), each of the
  * next n sage_sla_attn_fwd calls records a pair of HIP events on its stream
  * immediately around its sparse-attention kernel launch (after the linear

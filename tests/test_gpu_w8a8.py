@@ -1,0 +1,90 @@
+"""GPU parity of the W8A8 linear layer (page 5, "Four Technical Pillars",
+Pillar Three: INT8 weights and activations, block-wise 128x128) against the
+CPU oracle: quantized tensors and scales bit-exact, and the fp32 product
+bit-exact too (the oracle follows the same exact int32 block sums and the
+same fmaf chain over the K blocks); the bf16 output is the RNE of the fp32
+one."""
+import numpy as np
+import pytest
+import torch
+
+import bit_sparse_attention_amd as ssa
+from bit_sparse_attention_amd.workloads import (LINEAR_WORKLOADS, bf16_bits, make_linear,
+                                                make_linear_workload)
+
+from gpu_common import say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _u16(t):
+    return bf16_bits(t.detach().cpu()).reshape(t.shape)
+
+
+def _check_quant(orc, x, what):
+    xd = x.to(DEV)
+    q, s = ssa.w8a8_quant(xd)
+    torch.cuda.synchronize()
+    oq, os_ = orc.w8a8_quant(_u16(x))
+    assert np.array_equal(q.cpu().numpy(), oq), f"{what}: int8 differs"
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32)), f"{what}: scales differ"
+    return q, s, oq, os_
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (127, 256), (300, 384), (1000, 512)])
+def test_w8a8_quant_bitexact(orc, rows, cols):
+    say(f"[w8a8 quant] {rows}x{cols}")
+    x, _ = make_linear(rows, 128, cols, seed=rows + cols, outliers=True)
+    _check_quant(orc, x, f"{rows}x{cols}")
+
+
+def test_w8a8_quant_zero_block(orc):
+    x, _ = make_linear(200, 128, 256, seed=1)
+    x[:128, 128:] = 0  # one all-zero block: scale 0, q 0
+    q, s, _, _ = _check_quant(orc, x, "zero block")
+    assert float(s[0, 1]) == 0.0 and int(q[:128, 128:].abs().max()) == 0
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (300, 256, 384), (700, 384, 1280),
+                                   (257, 128, 640)])
+def test_w8a8_gemm_bitexact(orc, M, N, K):
+    say(f"[w8a8 gemm] M={M} N={N} K={K}")
+    x, w = make_linear(M, N, K, seed=M * 7 + K, outliers=True)
+    xq, sx, oxq, osx = _check_quant(orc, x, "x")
+    wq, sw, owq, osw = _check_quant(orc, w, "w")
+    y, y32 = ssa.w8a8_gemm(xq, sx, wq, sw, return_f32=True)
+    torch.cuda.synchronize()
+    oy = orc.w8a8_gemm(oxq, osx, owq, osw)
+    got = y32.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), oy.view(np.uint32)), \
+        f"max |diff| {np.abs(got - oy).max():.3e}"
+    assert torch.equal(y.cpu(), y32.cpu().to(torch.bfloat16))
+
+
+def test_w8a8_linear_matches_the_two_calls(orc):
+    x, w = make_linear(300, 256, 384, seed=3, outliers=True)
+    xd, wd = x.to(DEV), w.to(DEV)
+    wq, sw = ssa.w8a8_quant(wd)
+    y1 = ssa.w8a8_linear(xd, wq, sw)
+    xq, sx = ssa.w8a8_quant(xd)
+    y2 = ssa.w8a8_gemm(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_w8a8_fullsize_sampled(orc):
+    wl = LINEAR_WORKLOADS["w8a8_m75600_k5120_n5120"]
+    say(f"[w8a8 full] {wl.name}: generating")
+    x, w = make_linear_workload(wl)
+    xq, sx, oxq, osx = _check_quant(orc, x, "x full")
+    wq, sw, owq, osw = _check_quant(orc, w, "w full")
+    say(f"[w8a8 full] {wl.name}: quantization bit-exact; GEMM")
+    y, y32 = ssa.w8a8_gemm(xq, sx, wq, sw, return_f32=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(wl.M - 4, wl.M),
+                                     np.random.default_rng(0).integers(0, wl.M, 16)]))
+    oy = orc.w8a8_gemm(oxq, osx, owq, osw, rows=rows)
+    got = y32[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), oy.view(np.uint32))
+    say(f"[w8a8 full] {len(rows)} sampled rows bit-exact")
