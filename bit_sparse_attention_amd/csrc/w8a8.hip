@@ -160,10 +160,9 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(
     for (int ks = 0; ks < 4; ++ks) coff[ks] = (uint32_t)(((2 * ks + hi) ^ sl) * 16);
     const uint32_t wrow = (uint32_t)(WG_XT + (64 * wn + l32) * W8), xrow = (uint32_t)((64 * wm + l32) * W8);
 
-    // The int32 sums of a K block are dequantized during the next block: its
-    // 16 MFMAs are issued first and run on the matrix cores while the VALU
-    // converts and scales the previous block's sums (two sets of int32
-    // accumulators, alternating).
+    // The int32 sums of a K block are dequantized during the next block, while
+    // the matrix cores compute that block's sums into the other set of int32
+    // accumulators (two sets, alternating).
     i32x16 ia[2][2][2];  // [set][n tile][m tile]
     float sprev = 0.f;   // the scale of the block in the other set
     auto dequant = [&](auto set, float s) {
@@ -182,12 +181,15 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(
 #pragma unroll
             for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(acc[a][b]));
     };
-    // K block kb from ring stage R into int32 set P, then the dequantization
-    // of block kb-1 (set 1-P)
+    // K block kb from ring stage R into int32 set P, with the dequantization
+    // of block kb-1 (set 1-P) woven between its MFMAs: 4 accumulator entries
+    // after each of the 16 MFMAs, so the VALU works while the matrix core does
     auto kblock = [&](int kb, auto stage, auto set) {
         constexpr int R = decltype(stage)::value;
         constexpr int P = decltype(set)::value;
         const uint8_t* S = smem + R * WG_STAGE;
+        const bool dq = kb > 0;
+        const float s = sprev;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             i32x4 wf[2], xf[2];
@@ -201,10 +203,23 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < 2; ++b) {
                     ia[P][a][b] = mfma_i8_32x32x32(wf[a], xf[b], ks ? ia[P][a][b] : i32x16{});
+                    if (dq) {
+                        // entries 4ks .. 4ks+3 of tile [a][b] of the previous block
+#pragma unroll
+                        for (int r = 4 * ks; r < 4 * ks + 4; ++r)
+                            acc[a][b][r] = __builtin_fmaf((float)ia[1 - P][a][b][r], s, acc[a][b][r]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
         }
-        if (kb > 0) dequant(std::integral_constant<int, 1 - P>{}, sprev);
+        if (dq) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(acc[a][b]));
+        }
         sprev = sxr[kb] * swr[kb];
     };
 
