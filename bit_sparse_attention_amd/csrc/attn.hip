@@ -65,6 +65,9 @@ __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // Two wave-uniform 32-bit loads through the scalar cache, completed inside
 // the asm block. They stay off the vector-memory counter, so fetching the
 // next kept-block index and scale never waits for the tile DMAs in flight.
+// The outputs are early-clobber: the first load's destination is written
+// while the second load's address may still be needed, so no output may
+// share a register with either address.
 __device__ __forceinline__ void sload2(const void* p1, const void* p2, int& v1, int& v2) {
     const uint64_t a = (uint64_t)p1, b = (uint64_t)p2;
     const uint64_t sa = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
@@ -73,7 +76,7 @@ __device__ __forceinline__ void sload2(const void* p1, const void* p2, int& v1, 
                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
     asm volatile(
         "s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
-        : "=s"(v1), "=s"(v2)
+        : "=&s"(v1), "=&s"(v2)
         : "s"((const void*)sa), "s"((const void*)sb));
 }
 

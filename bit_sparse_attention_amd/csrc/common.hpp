@@ -77,12 +77,17 @@ __device__ __forceinline__ int64_t xcd_item(int64_t wg, int64_t total) {
 // clobber: callers only target LDS buffers nobody reads in the same pipeline
 // step (a clobber would also demote read-only scalar loads to vector loads,
 // whose vmcnt(0) waits would drain the pipeline).
+// The compiler's hazard recognizer does not look inside the asm, so the block
+// keeps the GFX9-family wait states itself: a vector memory instruction must
+// not read an SGPR within 5 wait states of a VALU write of it (the base may
+// come straight from v_readfirstlane), and an LDS DMA must not read M0 in the
+// wait state right after an SALU write of it. The s_mov and s_nop 3 give 5.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
     const uint64_t b = (uint64_t)base;
     const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
     const void* sbase = (const void*)sb;
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1\n\ts_nop 0" ::"v"(voff),
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, %1\n\ts_nop 0" ::"v"(voff),
                  "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr)));
 }
 
