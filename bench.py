@@ -97,29 +97,35 @@ def cpu_baseline(q, k, v, w, keep, kidx_np):
     }
 
 
-# Sources that define the sparse attention kernel; an HBM-traffic record taken
-# with rocprofv3 counters is valid only while these are unchanged.
-ATTN_SOURCES = ("bit_sparse_attention_amd/csrc/attn.hip", "bit_sparse_attention_amd/csrc/common.hpp")
+# The dominant kernel of each benchmark and the sources that define it; an
+# HBM-traffic record taken with rocprofv3 counters is valid only while these
+# are unchanged.
 ATTN_KERNEL = "sagesla_attn_kernel"
+W8_KERNEL = "w8a8_gemm_kernel"
+KERNEL_SOURCES = {
+    ATTN_KERNEL: ("bit_sparse_attention_amd/csrc/attn.hip", "bit_sparse_attention_amd/csrc/common.hpp"),
+    W8_KERNEL: ("bit_sparse_attention_amd/csrc/w8a8.hip", "bit_sparse_attention_amd/csrc/common.hpp"),
+}
+RECORD_PREFIX = {ATTN_KERNEL: "attn_kernel", W8_KERNEL: "w8a8_gemm"}
 COPY_KERNEL = "copyBuffer"
 
 
-def attn_sources_sha256():
+def sources_sha256(kernel):
     h = hashlib.sha256()
-    for rel in ATTN_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def traffic_record_path(workload):
-    return os.path.join(ROOT, "profiles", f"attn_kernel_hbm_traffic_{workload}.md")
+def traffic_record_path(workload, kernel=ATTN_KERNEL):
+    return os.path.join(ROOT, "profiles", f"{RECORD_PREFIX[kernel]}_hbm_traffic_{workload}.md")
 
 
-def traffic_from_record(workload):
-    """HBM bytes per attention-kernel launch from the committed counter record,
-    or None when there is none or the kernel sources changed since."""
-    path = traffic_record_path(workload)
+def traffic_from_record(workload, kernel=ATTN_KERNEL):
+    """HBM bytes per launch of the kernel from the committed counter record,
+    or None when there is none or the kernel's sources changed since."""
+    path = traffic_record_path(workload, kernel)
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -127,9 +133,9 @@ def traffic_from_record(workload):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("attn_sources_sha256") != attn_sources_sha256():
+    if rec.get("kernel") != kernel or rec.get("sources_sha256") != sources_sha256(kernel):
         return None
-    k = rec["kernels"].get(ATTN_KERNEL)
+    k = rec["kernels"].get(kernel)
     return None if k is None else k["fetch_bytes"] + k["write_bytes"]
 
 
@@ -148,7 +154,7 @@ def _pmc_per_kernel(path, counter):
     return out
 
 
-def pmc_summary(fetch_csv, write_csv, copy_mib, workload, command):
+def pmc_summary(fetch_csv, write_csv, copy_mib, workload, command, kernel=ATTN_KERNEL):
     """Markdown record of HBM traffic per launch from a FETCH_SIZE run and a
     WRITE_SIZE run, each scaled by what the same counter reads for a plain
     device copy of copy_mib MiB (which moves exactly that much each way)."""
@@ -175,15 +181,15 @@ def pmc_summary(fetch_csv, write_csv, copy_mib, workload, command):
     lines += ["", "| kernel | dispatches | FETCH KiB | WRITE KiB | scaled read MB | scaled write MB |",
               "|---|---|---|---|---|---|"]
     rec = {"workload": workload, "copy_mib": copy_mib, "fetch_scale": sf, "write_scale": sw,
-           "attn_sources_sha256": attn_sources_sha256(), "kernels": {}}
+           "kernel": kernel, "sources_sha256": sources_sha256(kernel), "kernels": {}}
     for name in sorted(fetch, key=lambda n: -fetch[n][1]):
         n, f = fetch[name]
         w = write.get(name, (0, float("nan")))[1]
         short = re.sub(r"\(.*", "", name)
         lines.append(f"| `{short}` | {n} | {f:.0f} | {w:.0f} | {f * sf * 1024 / 1e6:.1f} | "
                      f"{w * sw * 1024 / 1e6:.1f} |")
-        if ATTN_KERNEL in name:
-            rec["kernels"][ATTN_KERNEL] = {"fetch_bytes": f * sf * 1024, "write_bytes": w * sw * 1024}
+        if kernel in name:
+            rec["kernels"][kernel] = {"fetch_bytes": f * sf * 1024, "write_bytes": w * sw * 1024}
     lines += ["", "```json", json.dumps(rec), "```", ""]
     return "\n".join(lines)
 
@@ -292,8 +298,12 @@ def bench_w8a8(args):
         "gemm_ms": g_mean,
         "gemm_ms_pct": {f"p{p}": float(np.percentile(g_ms, p)) for p in (10, 50, 90)},
         "roofline": {"bound": "mfma", "achieved": g_tops, "peak": INT8_PEAK_TOPS,
-                     "unit": "TOP/s", "frac": g_tops / INT8_PEAK_TOPS, "traffic": None},
+                     "unit": "TOP/s", "frac": g_tops / INT8_PEAK_TOPS,
+                     "traffic": traffic_from_record(wl.name, W8_KERNEL),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled)"},
     }
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
     if not args.no_cpu_baseline:
         import oracle
         from bit_sparse_attention_amd.workloads import bf16_bits
@@ -341,15 +351,16 @@ def main():
                     help="benchmark the W8A8 linear layer instead (its own JSON line)")
     args = ap.parse_args()
     if args.pmc_summary or args.trace_summary or args.pmc_table:
-        from bit_sparse_attention_amd.workloads import BENCH_WORKLOAD
-        wl = args.workload or BENCH_WORKLOAD
+        from bit_sparse_attention_amd.workloads import BENCH_WORKLOAD, LINEAR_BENCH_WORKLOAD
+        kernel = W8_KERNEL if args.w8a8 else ATTN_KERNEL
+        wl = args.workload or (LINEAR_BENCH_WORKLOAD if args.w8a8 else BENCH_WORKLOAD)
         if args.pmc_summary:
             print(pmc_summary(*args.pmc_summary, args.copy_calibration or 1024, wl,
-                              args.pmc_command))
+                              args.pmc_command, kernel))
         elif args.trace_summary:
             print(trace_summary(args.trace_summary, wl, args.pmc_command))
         else:
-            print(pmc_table(args.pmc_table, wl, args.pmc_command, ATTN_KERNEL))
+            print(pmc_table(args.pmc_table, wl, args.pmc_command, kernel))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the SageSLA path is "
