@@ -162,6 +162,49 @@ def test_tiles_reject_bad_count():
     assert L.sage_qk_int32_tiles(_p(0), _p(GB), _shape(), _p(2 * GB), 0, _p(3 * GB), None) == 1
 
 
+def test_w8a8_quant_rejects_bad_arguments():
+    L = _L()
+    GB = 1 << 30
+
+    def call(x=_p(0), rows=300, cols=384, q=_p(GB), sc=_p(2 * GB)):
+        return L.w8a8_quant(x, rows, cols, q, sc, None)
+
+    assert call(rows=0) == 1
+    assert call(rows=(1 << 20) + 1) == 1
+    assert call(cols=100) == 1  # not a multiple of 128
+    assert call(cols=0) == 1
+    assert call(x=None) == 1
+    assert call(x=_p(8)) == 1  # misaligned
+    assert call(q=_p(GB + 4)) == 1
+    assert call(sc=_p(2 * GB + 2)) == 1
+    assert call(q=_p(16)) == 1  # q overlaps x
+    assert b"overlap" in L.ssa_last_error()
+    assert call(sc=_p(GB + 64)) == 1  # scale inside q
+    assert b"overlap" in L.ssa_last_error()
+
+
+def test_w8a8_gemm_rejects_bad_arguments():
+    L = _L()
+    GB = 1 << 30
+
+    def call(xq=_p(0), sx=_p(GB), wq=_p(2 * GB), sw=_p(3 * GB), M=300, N=256, K=384,
+             y=_p(4 * GB), y32=None):
+        return L.w8a8_gemm(xq, sx, wq, sw, M, N, K, y, y32, None)
+
+    assert call(M=0) == 1
+    assert call(M=(1 << 20) + 1) == 1
+    assert call(N=200) == 1 and call(K=200) == 1  # not multiples of 128
+    assert call(N=0) == 1 and call(K=0) == 1
+    assert call(xq=None) == 1 and call(wq=None) == 1 and call(y=None) == 1
+    assert call(sx=None) == 1 and call(sw=None) == 1
+    assert call(xq=_p(8)) == 1  # misaligned
+    assert call(y32=_p(5 * GB + 8)) == 1
+    assert call(y=_p(2 * GB + 64)) == 1  # output overlaps wq
+    assert b"overlap" in L.ssa_last_error()
+    assert call(y32=_p(4 * GB + 1024)) == 1  # the two outputs overlap
+    assert b"overlap" in L.ssa_last_error()
+
+
 def test_status_strings():
     L = _L()
     for st in range(5):
