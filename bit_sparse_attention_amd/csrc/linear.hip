@@ -18,6 +18,8 @@
 namespace ssa {
 
 constexpr int TP = KBLK + 8;  // LDS pitch (bf16) of a [channel][token] tile: 144 B
+constexpr int LS_THREADS = 512;                       // 8 waves
+constexpr int LS_IT = KBLK * HD / 8 / LS_THREADS;     // 16-byte chunks per thread per tile
 
 // Position p (0..63) of a re-laid V tile row holds key 16*(p/16) + kperm(p%16):
 // the order in which one lane of the 32x32 MFMA output holds its keys, so the
@@ -32,7 +34,7 @@ constexpr int TP = KBLK + 8;  // LDS pitch (bf16) of a [channel][token] tile: 14
 // follows in the same d order; the GEMM and the apply only need a consistent
 // order, and each lane then stores 16-byte runs.
 template <bool STATES>
-__global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v, int N,
                                                             int nkb, int ngroups,
                                                             uint16_t* __restrict__ vt,
@@ -43,20 +45,24 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
     __shared__ __attribute__((aligned(16))) uint16_t fkl[STATES ? HD * TP : 8];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
               hi = lane >> 5;
+    // wave (eg, dh) owns the state columns e = 32eg .. 32eg+31 and rows
+    // d = 64dh .. 64dh+63 (row tiles dt = 2dh, 2dh+1); the waves with dh = 0
+    // also own z rows d = 32eg .. 32eg+31
+    const int eg = wave & 3, dh = wave >> 2;
     const int64_t bh = blockIdx.y;
     const int g = blockIdx.x;
     const int G = STATES ? LIN_GROUP : 1;
-    f32x16 tot[4], totz = f32x16{};
+    f32x16 tot[2], totz = f32x16{};
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) tot[dt] = f32x16{};
+    for (int t = 0; t < 2; ++t) tot[t] = f32x16{};
     // raw K and V of one key block in registers: lane (tid) holds token
-    // u = tid & 63, channels 8ch .. 8ch+7 for ch = (tid >> 6) + 4*it. Two sets,
+    // u = tid & 63, channels 8ch .. 8ch+7 for ch = (tid >> 6) + 8*it. Two sets,
     // so the loads of blocks j+1 and j+2 are in flight while block j is worked.
-    u16x8 va[4], ka[4], vb[4], kb[4];
-    auto load = [&](int j, u16x8 (&vv)[4], u16x8 (&kk)[4]) {
+    u16x8 va[LS_IT], ka[LS_IT], vb[LS_IT], kb[LS_IT];
+    auto load = [&](int j, u16x8 (&vv)[LS_IT], u16x8 (&kk)[LS_IT]) {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int c = tid + 256 * it;
+        for (int it = 0; it < LS_IT; ++it) {
+            const int c = tid + LS_THREADS * it;
             const int u = c & 63, ch = c >> 6;
             const int tok = j * KBLK + u;
             const bool ok = tok < N;
@@ -65,12 +71,12 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
             if (STATES) kk[it] = ok ? *(const u16x8*)(k + off) : u16x8{};
         }
     };
-    auto block = [&](int jb, u16x8 (&vv)[4], u16x8 (&kk)[4]) {
+    auto block = [&](int jb, u16x8 (&vv)[LS_IT], u16x8 (&kk)[LS_IT]) {
         const int j = g * G + jb;
         // channel-major LDS stores (u fastest: conflict free)
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int c = tid + 256 * it;
+        for (int it = 0; it < LS_IT; ++it) {
+            const int c = tid + LS_THREADS * it;
             const int u = c & 63, ch = c >> 6;
             const bool ok = j * KBLK + u < N;
 #pragma unroll
@@ -92,8 +98,8 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
         if (jb + 2 < G && j + 2 < nkb) load(j + 2, vv, kk);
         // V^T tile in the sparse kernel's key order: 128 rows x 8 chunks of 16 B
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int c = tid + 256 * it;
+        for (int it = 0; it < LS_IT; ++it) {
+            const int c = tid + LS_THREADS * it;
             const int dv = c >> 3, pc = c & 7, cc = pc >> 1, h2 = pc & 1;
             const u16x4 a = *(const u16x4*)(vtl + dv * TP + 16 * cc + 4 * h2);
             const u16x4 b = *(const u16x4*)(vtl + dv * TP + 16 * cc + 8 + 4 * h2);
@@ -102,57 +108,64 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
         }
         if (STATES) {
             // (h_j^T)^T[d][e] = sum_u phi(K)[u][d] V[u][e]: A = phi(K)^T rows d (hi and
-            // lo parts, two products, fp32 accumulation), B = V columns e. Wave w
-            // takes columns e = 32w .. 32w+31; acc[dt] holds rows d = 32dt + ...
-            f32x16 acc[4], accz = f32x16{};
+            // lo parts, two products, fp32 accumulation), B = V columns e. This
+            // wave takes columns e = 32eg .. 32eg+31; acc[t] holds rows
+            // d = 32(2dh + t) + ...
+            f32x16 acc[2], accz = f32x16{};
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+            for (int t = 0; t < 2; ++t) acc[t] = f32x16{};
             bf16x8 ones;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 #pragma unroll
             for (int uc = 0; uc < 4; ++uc) {
-                const bf16x8 b = *(const bf16x8*)(vtl + (32 * wave + l32) * TP + 16 * uc + 8 * hi);
+                const bf16x8 b = *(const bf16x8*)(vtl + (32 * eg + l32) * TP + 16 * uc + 8 * hi);
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
+                for (int t = 0; t < 2; ++t) {
+                    const int dt = 2 * dh + t;
                     const bf16x8 ah = *(const bf16x8*)(fkh + (32 * dt + l32) * TP + 16 * uc + 8 * hi);
                     const bf16x8 al = *(const bf16x8*)(fkl + (32 * dt + l32) * TP + 16 * uc + 8 * hi);
-                    acc[dt] = mfma_bf16_32x32x16(ah, b, acc[dt]);
-                    acc[dt] = mfma_bf16_32x32x16(al, b, acc[dt]);
+                    acc[t] = mfma_bf16_32x32x16(ah, b, acc[t]);
+                    acc[t] = mfma_bf16_32x32x16(al, b, acc[t]);
                 }
             }
-            // z_j[d] for rows d = 32w + ...: the same product against ones
+            // z_j[d] for rows d = 32eg + ...: the same product against ones
+            if (dh == 0) {
 #pragma unroll
-            for (int uc = 0; uc < 4; ++uc) {
-                const int o = (32 * wave + l32) * TP + 16 * uc + 8 * hi;
-                accz = mfma_bf16_32x32x16(*(const bf16x8*)(fkh + o), ones, accz);
-                accz = mfma_bf16_32x32x16(*(const bf16x8*)(fkl + o), ones, accz);
+                for (int uc = 0; uc < 4; ++uc) {
+                    const int o = (32 * eg + l32) * TP + 16 * uc + 8 * hi;
+                    accz = mfma_bf16_32x32x16(*(const bf16x8*)(fkh + o), ones, accz);
+                    accz = mfma_bf16_32x32x16(*(const bf16x8*)(fkl + o), ones, accz);
+                }
             }
-            // lane (column e = 32w + l32, hi) holds rows d = 32dt + 8(r/4) + 4hi + r%4:
+            // lane (column e = 32eg + l32, hi) holds rows d = 32dt + 8(r/4) + 4hi + r%4:
             // registers 8rb .. 8rb+7 are positions 16(2dt + rb) + 8hi + 0..7 of row e
             uint16_t* hrow = hs + (bh * nkb + j) * (int64_t)HS_ROW;
-            const int e = 32 * wave + l32;
+            const int e = 32 * eg + l32;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
+            for (int t = 0; t < 2; ++t) {
+                const int dt = 2 * dh + t;
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     u16x8 o8;
 #pragma unroll
-                    for (int x = 0; x < 8; ++x) o8[x] = f2bf(acc[dt][8 * rb + x]);
+                    for (int x = 0; x < 8; ++x) o8[x] = f2bf(acc[t][8 * rb + x]);
                     *(u16x8*)(hrow + e * HD + 16 * (2 * dt + rb) + 8 * hi) = o8;
                 }
-                tot[dt] += acc[dt];
+                tot[t] += acc[t];
             }
-            if (l32 == 0) {  // z rows d = 32w + ..., every column equal
+            if (dh == 0) {
+                if (l32 == 0) {  // z rows d = 32eg + ..., every column equal
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    u16x8 o8;
+                    for (int rb = 0; rb < 2; ++rb) {
+                        u16x8 o8;
 #pragma unroll
-                    for (int x = 0; x < 8; ++x) o8[x] = f2bf(accz[8 * rb + x]);
-                    *(u16x8*)(hrow + HD * HD + 16 * (2 * wave + rb) + 8 * hi) = o8;
+                        for (int x = 0; x < 8; ++x) o8[x] = f2bf(accz[8 * rb + x]);
+                        *(u16x8*)(hrow + HD * HD + 16 * (2 * eg + rb) + 8 * hi) = o8;
+                    }
                 }
+                totz += accz;
             }
-            totz += accz;
         }
         __syncthreads();
     };
@@ -165,21 +178,21 @@ __global__ __launch_bounds__(256) void linear_states_kernel(const uint16_t* __re
     }
     if (STATES) {
         float* prow = hpart + (bh * ngroups + g) * (int64_t)HS_ROW;
-        const int e = 32 * wave + l32;
+        const int e = 32 * eg + l32;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-                float* dst = prow + e * HD + 16 * (2 * dt + rb) + 8 * hi;
-                *(f32x4*)dst = f32x4{tot[dt][8 * rb], tot[dt][8 * rb + 1], tot[dt][8 * rb + 2],
-                                     tot[dt][8 * rb + 3]};
-                *(f32x4*)(dst + 4) = f32x4{tot[dt][8 * rb + 4], tot[dt][8 * rb + 5],
-                                           tot[dt][8 * rb + 6], tot[dt][8 * rb + 7]};
+                float* dst = prow + e * HD + 16 * (2 * (2 * dh + t) + rb) + 8 * hi;
+                *(f32x4*)dst = f32x4{tot[t][8 * rb], tot[t][8 * rb + 1], tot[t][8 * rb + 2],
+                                     tot[t][8 * rb + 3]};
+                *(f32x4*)(dst + 4) = f32x4{tot[t][8 * rb + 4], tot[t][8 * rb + 5],
+                                           tot[t][8 * rb + 6], tot[t][8 * rb + 7]};
             }
-        if (l32 == 0)
+        if (dh == 0 && l32 == 0)
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-                float* dst = prow + HD * HD + 16 * (2 * wave + rb) + 8 * hi;
+                float* dst = prow + HD * HD + 16 * (2 * eg + rb) + 8 * hi;
                 *(f32x4*)dst = f32x4{totz[8 * rb], totz[8 * rb + 1], totz[8 * rb + 2], totz[8 * rb + 3]};
                 *(f32x4*)(dst + 4) =
                     f32x4{totz[8 * rb + 4], totz[8 * rb + 5], totz[8 * rb + 6], totz[8 * rb + 7]};
@@ -463,7 +476,7 @@ hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH
                                 hipStream_t st) {
     const int nkb = (N + KBLK - 1) / KBLK;
     const int ngroups = (nkb + LIN_GROUP - 1) / LIN_GROUP;
-    hipLaunchKernelGGL((linear_states_kernel<true>), dim3(ngroups, BH), dim3(256), 0, st, k, v, N,
+    hipLaunchKernelGGL((linear_states_kernel<true>), dim3(ngroups, BH), dim3(LS_THREADS), 0, st, k, v, N,
                        nkb, ngroups, vt, hs, hpart);
     hipLaunchKernelGGL(htot_kernel, dim3((HS_ROW + 255) / 256, BH), dim3(256), 0, st, hpart, ngroups,
                        htot);
@@ -472,7 +485,7 @@ hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH
 
 hipError_t launch_vt_only(const uint16_t* v, int64_t BH, int N, uint16_t* vt, hipStream_t st) {
     const int nkb = (N + KBLK - 1) / KBLK;
-    hipLaunchKernelGGL((linear_states_kernel<false>), dim3(nkb, BH), dim3(256), 0, st, nullptr, v, N,
+    hipLaunchKernelGGL((linear_states_kernel<false>), dim3(nkb, BH), dim3(LS_THREADS), 0, st, nullptr, v, N,
                        nkb, nkb, vt, nullptr, nullptr);
     return hipGetLastError();
 }
