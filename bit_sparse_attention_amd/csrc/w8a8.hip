@@ -79,22 +79,26 @@ __global__ __launch_bounds__(256) void w8a8_quant_kernel(const uint16_t* __restr
 // m), so each lane of a result holds four consecutive n of one m and stores
 // them as one run.
 //
-// Workgroup: 8 waves, tile 256 m x 128 n. Wave w owns m 64*(w/2) .. +63 and
-// n 64*(w%2) .. +63: a 2 x 2 grid of 32x32 tiles, each with an int32
+// Workgroup: 16 waves (four per SIMD), tile 256 m x 128 n. Wave w owns
+// m 64*(w/4) .. +63 and n 32*(w%4) .. +31: two 32x32 tiles, each with an int32
 // accumulator for the current 128-wide K block and an fp32 one for the
-// dequantized sum. A stage is one K block: the X tile [256 m][128 k] (32 KB)
-// and the W tile [128 n][128 k] (16 KB), 128-byte rows with 16-byte chunk c of
-// row r at slot c ^ swz(r) (a 16-lane group reading 16 consecutive rows at one
-// chunk hits 16 distinct bank groups), fetched by LDS DMA into a 3-deep ring
-// two stages ahead: 6 DMAs of 1 KB per wave per stage.
+// dequantized sum (about 120 VGPRs: four waves per SIMD hide each other's
+// LDS-read and dequantization latencies). A stage is one K block: the X tile
+// [256 m][128 k] (32 KB) and the W tile [128 n][128 k] (16 KB), 128-byte rows
+// with 16-byte chunk c of row r at slot c ^ swz(r) (a 16-lane group reading 16
+// consecutive rows at one chunk hits 16 distinct bank groups), fetched by LDS
+// DMA into a 3-deep ring two stages ahead: 3 DMAs of 1 KB per wave per stage.
 constexpr int WG_TM = 256, WG_TN = 128, WG_STAGES = 3;
+constexpr int WG_WAVES = 16, WG_THREADS = 64 * WG_WAVES;
 constexpr int WG_XT = WG_TM * W8, WG_WT = WG_TN * W8;  // bytes of the stage's tiles
 constexpr int WG_STAGE = WG_XT + WG_WT;
+constexpr int XD = WG_TM / 8 / WG_WAVES, WD = WG_TN / 8 / WG_WAVES;  // DMAs per wave per stage
 constexpr int WG_GROUP_M = 4;  // m tiles per group of the tile order
+static_assert(XD == 2 && WD == 1, "the stage is 48 DMAs of 1 KB over 16 waves");
 
 __device__ __forceinline__ int w8swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-__global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(
+__global__ __launch_bounds__(WG_THREADS, 1) void w8a8_gemm_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
     const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y,
     float* __restrict__ y32) {
@@ -115,19 +119,20 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(
     // derived from it in scalar registers and loads the scales through the
     // scalar cache)
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63,
-              l32 = lane & 31, hi = lane >> 5, wm = wave >> 1, wn = wave & 1;
+              l32 = lane & 31, hi = lane >> 5, wm = wave >> 2, wn = wave & 3;
 
-    // DMA lane offsets: DMA p of wave w fills 8 rows at 8*(4w + p) (X, p < 4) or
-    // 8*(2w + p - 4) (W, p >= 4); lane l fetches row + l/8, chunk (l%8) ^ swz(row)
-    uint32_t xoff[4], woff[2];
+    // DMA lane offsets: DMA p of wave w fills 8 rows at 8*(2w + p) (X) or 8w
+    // (W); lane l fetches row + l/8, chunk (l%8) ^ swz(row). X rows past M
+    // re-read row M-1 (never stored).
+    uint32_t xoff[XD], woff[WD];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int row = 8 * (4 * wave + p) + (lane >> 3);
+    for (int p = 0; p < XD; ++p) {
+        const int row = 8 * (XD * wave + p) + (lane >> 3);
         xoff[p] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + 16 * ((lane & 7) ^ w8swz(row));
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int row = 8 * (2 * wave + p) + (lane >> 3);
+    for (int p = 0; p < WD; ++p) {
+        const int row = 8 * (WD * wave + p) + (lane >> 3);
         woff[p] = (uint32_t)row * (uint32_t)K + 16 * ((lane & 7) ^ w8swz(row));
     }
     const int8_t* xbase = xq + (int64_t)m0 * K;
@@ -136,146 +141,102 @@ __global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(
         uint8_t* X = smem + st * WG_STAGE;
         uint8_t* W = X + WG_XT;
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-            dma16(xbase + kb * W8, xoff[p], lds_u32(X + 8 * (4 * wave + p) * W8));
+        for (int p = 0; p < XD; ++p)
+            dma16(xbase + kb * W8, xoff[p], lds_u32(X + 8 * (XD * wave + p) * W8));
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-            dma16(wbase + kb * W8, woff[p], lds_u32(W + 8 * (2 * wave + p) * W8));
+        for (int p = 0; p < WD; ++p)
+            dma16(wbase + kb * W8, woff[p], lds_u32(W + 8 * (WD * wave + p) * W8));
     };
 
-    f32x16 acc[2][2];  // [n tile][m tile], dequantized
-#pragma unroll
-    for (int a = 0; a < 2; ++a) acc[a][0] = acc[a][1] = f32x16{};
+    f32x16 acc[2] = {f32x16{}, f32x16{}};  // [m tile], dequantized
     // this wave's 128-blocks (rows past M, never stored, use the last m block)
     const int mb = min((m0 + 64 * wm) / W8, (M - 1) / W8), nb = n0 / W8;
     const float* sxr = sx + (int64_t)mb * nkb;
     const float* swr = sw + (int64_t)nb * nkb;
 
-    // Fragment addresses: the rows a lane reads are 64wn + 32t + l32 (W) and
+    // Fragment addresses: the rows a lane reads are 32wn + l32 (W) and
     // 64wm + 32t + l32 (X), whose swizzle depends on l32 only, so a lane needs
     // one chunk offset per K step; t and the ring stage are immediate offsets.
     const int sl = w8swz(l32);
     uint32_t coff[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) coff[ks] = (uint32_t)(((2 * ks + hi) ^ sl) * 16);
-    const uint32_t wrow = (uint32_t)(WG_XT + (64 * wn + l32) * W8), xrow = (uint32_t)((64 * wm + l32) * W8);
+    const uint32_t wrow = (uint32_t)(WG_XT + (32 * wn + l32) * W8), xrow = (uint32_t)((64 * wm + l32) * W8);
 
-    // The int32 sums of a K block are dequantized during the next block, while
-    // the matrix cores compute that block's sums into the other set of int32
-    // accumulators (two sets, alternating).
-    i32x16 ia[2][2][2];  // [set][n tile][m tile]
-    float sprev = 0.f;   // the scale of the block in the other set
-    auto dequant = [&](auto set, float s) {
-        constexpr int P = decltype(set)::value;
+    // K block kb from ring stage R: 4 K steps of 2 MFMAs, the fragments of
+    // step ks+1 read while those of step ks are in use; then the block's
+    // int32 sums are scaled into the fp32 sums (y = fmaf(I, sx*sw, y)).
+    auto kblock = [&](int kb, auto stage) {
+        constexpr int R = decltype(stage)::value;
+        const uint8_t* S = smem + R * WG_STAGE;
+        auto frag = [&](int ks, i32x4& w, i32x4 (&x)[2]) {
+            w = *(const i32x4*)(S + wrow + coff[ks]);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+            for (int t = 0; t < 2; ++t) x[t] = *(const i32x4*)(S + xrow + coff[ks] + 32 * t * W8);
+        };
+        i32x4 nwf, nxf[2];
+        frag(0, nwf, nxf);
+        i32x16 ia[2];
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+        for (int ks = 0; ks < 4; ++ks) {
+            const i32x4 wf = nwf, xf[2] = {nxf[0], nxf[1]};
+            if (ks < 3) frag(ks + 1, nwf, nxf);
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[a][b][r] = __builtin_fmaf((float)ia[P][a][b][r], s, acc[a][b][r]);
+            for (int b = 0; b < 2; ++b) ia[b] = mfma_i8_32x32x32(wf, xf[b], ks ? ia[b] : i32x16{});
+        }
+        const float s = sxr[kb] * swr[kb];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[b][r] = __builtin_fmaf((float)ia[b][r], s, acc[b][r]);
         // pin the dequantization here: left free, the compiler sinks it past
         // the following blocks and keeps their int32 sums all live
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(acc[a][b]));
-    };
-    // K block kb from ring stage R into int32 set P, with the dequantization
-    // of block kb-1 (set 1-P) woven between its MFMAs: 4 accumulator entries
-    // after each of the 16 MFMAs, so the VALU works while the matrix core does
-    auto kblock = [&](int kb, auto stage, auto set) {
-        constexpr int R = decltype(stage)::value;
-        constexpr int P = decltype(set)::value;
-        const uint8_t* S = smem + R * WG_STAGE;
-        const bool dq = kb > 0;
-        const float s = sprev;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            i32x4 wf[2], xf[2];
-            const uint8_t* wp = S + wrow + coff[ks];
-            const uint8_t* xp = S + xrow + coff[ks];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                wf[t] = *(const i32x4*)(wp + 32 * t * W8);
-                xf[t] = *(const i32x4*)(xp + 32 * t * W8);
-            }
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    ia[P][a][b] = mfma_i8_32x32x32(wf[a], xf[b], ks ? ia[P][a][b] : i32x16{});
-                    if (dq) {
-                        // entries 4ks .. 4ks+3 of tile [a][b] of the previous block
-#pragma unroll
-                        for (int r = 4 * ks; r < 4 * ks + 4; ++r)
-                            acc[a][b][r] = __builtin_fmaf((float)ia[1 - P][a][b][r], s, acc[a][b][r]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-        }
-        if (dq) {
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(acc[a][b]));
-        }
-        sprev = sxr[kb] * swr[kb];
+        for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(acc[b]));
     };
 
     // Pipeline: stage kb % 3, two stages ahead; at the end of step kb only the
-    // 6 DMAs of stage kb+2 may still be in flight.
+    // DMAs of stage kb+2 may still be in flight.
     issue(0, 0);
     if (nkb > 1) issue(1, 1);
-    if (nkb > 1) wait_vm<6>(); else wait_vm<0>();
+    if (nkb > 1) wait_vm<XD + WD>(); else wait_vm<0>();
     __syncthreads();
-    auto step = [&](int kb, auto stage, auto set) {
+    auto step = [&](int kb, auto stage) {
         constexpr int R = decltype(stage)::value;
         if (kb + 2 < nkb) issue(kb + 2, (R + 2) % WG_STAGES);
-        kblock(kb, stage, set);
+        kblock(kb, stage);
         if (kb + 1 < nkb) {
-            if (kb + 2 < nkb) wait_vm<6>(); else wait_vm<0>();
+            if (kb + 2 < nkb) wait_vm<XD + WD>(); else wait_vm<0>();
             __syncthreads();
         }
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
-    static_assert(WG_STAGES == 3, "the K loop is unrolled by the ring depth and the two sets");
+    static_assert(WG_STAGES == 3, "the K loop is unrolled by the ring depth");
     int kb = 0;
-    for (; kb + 6 <= nkb; kb += 6) {
-        step(kb, S0{}, S0{});
-        step(kb + 1, S1{}, S1{});
-        step(kb + 2, S2{}, S0{});
-        step(kb + 3, S0{}, S1{});
-        step(kb + 4, S1{}, S0{});
-        step(kb + 5, S2{}, S1{});
+    for (; kb + 3 <= nkb; kb += 3) {
+        step(kb, S0{});
+        step(kb + 1, S1{});
+        step(kb + 2, S2{});
     }
-    // the rest (at most 5 blocks), then the last block's dequantization
-    if (kb < nkb) step(kb++, S0{}, S0{});
-    if (kb < nkb) step(kb++, S1{}, S1{});
-    if (kb < nkb) step(kb++, S2{}, S0{});
-    if (kb < nkb) step(kb++, S0{}, S1{});
-    if (kb < nkb) step(kb++, S1{}, S0{});
-    if (nkb & 1) dequant(S0{}, sprev); else dequant(S1{}, sprev);
+    if (kb < nkb) step(kb++, S0{});
+    if (kb < nkb) step(kb++, S1{});
 
-    // lane (m = l32, hi), tile [a][b] register 4q + x holds n = 32a + 8q + 4hi + x
+    // lane (m = l32, hi), tile [b] register 4q + x holds n = 8q + 4hi + x
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int m = m0 + 64 * wm + 32 * b + l32;
         if (m >= M) continue;
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const int n = n0 + 64 * wn + 32 * a + 8 * qd + 4 * hi;
-                const f32x16& c = acc[a][b];
-                *(u16x4*)(y + (int64_t)m * N + n) =
-                    u16x4{f2bf(c[4 * qd]), f2bf(c[4 * qd + 1]), f2bf(c[4 * qd + 2]), f2bf(c[4 * qd + 3])};
-                if (y32)
-                    *(f32x4*)(y32 + (int64_t)m * N + n) =
-                        f32x4{c[4 * qd], c[4 * qd + 1], c[4 * qd + 2], c[4 * qd + 3]};
-            }
+        for (int qd = 0; qd < 4; ++qd) {
+            const int n = n0 + 32 * wn + 8 * qd + 4 * hi;
+            const f32x16& c = acc[b];
+            *(u16x4*)(y + (int64_t)m * N + n) =
+                u16x4{f2bf(c[4 * qd]), f2bf(c[4 * qd + 1]), f2bf(c[4 * qd + 2]), f2bf(c[4 * qd + 3])};
+            if (y32)
+                *(f32x4*)(y32 + (int64_t)m * N + n) = f32x4{c[4 * qd], c[4 * qd + 1], c[4 * qd + 2], c[4 * qd + 3]};
+        }
     }
 }
 
@@ -290,7 +251,7 @@ hipError_t launch_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq,
                             int M, int N, int K, uint16_t* y, float* y32, hipStream_t st) {
     const int64_t total = (int64_t)((M + WG_TM - 1) / WG_TM) * (N / WG_TN);
     const int64_t grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL(w8a8_gemm_kernel, dim3((unsigned)grid), dim3(512), 0, st, xq, sx, wq, sw, M,
+    hipLaunchKernelGGL(w8a8_gemm_kernel, dim3((unsigned)grid), dim3(WG_THREADS), 0, st, xq, sx, wq, sw, M,
                        N, K, y, y32);
     return hipGetLastError();
 }
