@@ -399,3 +399,23 @@ class SageSLAPlan:
         self.mask()
         self.attn()
         return self.out
+
+    def capture(self):
+        """Record one run() into a HIP graph (torch.cuda.CUDAGraph). The calls
+        allocate nothing, set no memory with hipMemset and synchronize nothing,
+        so the whole step is capturable; replay() then re-executes it on the
+        bound tensors (rebinding other tensors needs a new capture). An eager
+        run() first checks the device and loads the code objects."""
+        self.run()
+        torch.cuda.synchronize(self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        self._graph = g
+        return g
+
+    def replay(self):
+        if getattr(self, "_graph", None) is None:
+            raise RuntimeError("capture() the plan before replay()")
+        self._graph.replay()
+        return self.out
