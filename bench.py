@@ -29,14 +29,16 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 HEAD_DIM = 128
 
 
-def effective_ops(kidx, N, nqb, nkb, dense):
+def effective_ops(kidx, N, nqb, nkb, dense, BH=1):
     """4*D*sum over computed (query block, key block) pairs of valid-token
-    products: QK^T and PV multiply-adds over the blocks actually computed."""
+    products: QK^T and PV multiply-adds over the blocks actually computed, over
+    all B*H heads (kidx [B][H][nqb][keep] covers them; a dense run has BH heads
+    of every pair)."""
     nq = np.minimum(128, N - 128 * np.arange(nqb)).astype(np.float64)
     nk = np.minimum(64, N - 64 * np.arange(nkb)).astype(np.float64)
     if dense:
         per_head = nq.sum() * nk.sum()
-        return 4.0 * HEAD_DIM * per_head, None
+        return 4.0 * HEAD_DIM * per_head * BH, None
     kid = kidx.reshape(-1, nqb, kidx.shape[-1])
     tot = (nk[kid].sum(axis=2) * nq[None, :]).sum()
     return 4.0 * HEAD_DIM * tot, None
@@ -84,7 +86,7 @@ def cpu_baseline(q, k, v, w, keep, kidx_np):
             oracle.linear_rows(qb, hs, zs, 0, toks, kh, nthreads)
         t_heads += time.perf_counter() - t0
     t_full = t_heads / len(heads) * B * H
-    ops_full, _ = effective_ops(kidx_np, N, nqb, nkb, w.dense)
+    ops_full, _ = effective_ops(kidx_np, N, nqb, nkb, w.dense, B * H)
     return {
         "value": ops_full / t_full / 1e12,
         "unit": "TOPS",
@@ -417,7 +419,7 @@ def main():
             stages[name] = round(e0.elapsed_time(e1) / K, 4)
 
     kidx_np = None if plan.dense else plan.kidx.cpu().numpy()
-    ops, _ = effective_ops(kidx_np, w.N, plan.nqb, plan.nkb, plan.dense)
+    ops, _ = effective_ops(kidx_np, w.N, plan.nqb, plan.nkb, plan.dense, w.B * w.H)
     k_ms = float(np.mean(kern_ms)) if kern_ms else float("nan")
     k_pct = ({f"p{p}": float(np.percentile(kern_ms, p)) for p in (10, 50, 90)}
              if kern_ms else None)

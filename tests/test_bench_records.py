@@ -102,3 +102,20 @@ def test_committed_records_name_their_kernel(bench):
         assert len(rec["sources_sha256"]) == 64 and rec["kernels"][rec["kernel"]]["fetch_bytes"] > 0
         found += 1
     assert found >= 2
+
+
+def test_effective_ops_counts_every_head(bench):
+    """Dense: 4*D*N^2 per head, over all heads; a sparse selection that keeps
+    every block counts the same; ragged tails count only valid tokens."""
+    import numpy as np
+    B, H, N = 2, 3, 1000  # 8 query blocks (last 104 tokens), 16 key blocks (last 40)
+    nqb, nkb = 8, 16
+    dense, _ = bench.effective_ops(None, N, nqb, nkb, True, B * H)
+    assert dense == 4 * 128 * N * N * B * H
+    every = np.broadcast_to(np.arange(nkb, dtype=np.int32), (B, H, nqb, nkb)).copy()
+    full, _ = bench.effective_ops(every, N, nqb, nkb, False, B * H)
+    assert full == dense
+    # keep only the ragged last key block: 40 keys for every query of every head
+    last = np.full((B, H, nqb, 1), nkb - 1, dtype=np.int32)
+    one, _ = bench.effective_ops(last, N, nqb, nkb, False, B * H)
+    assert one == 4 * 128 * N * 40 * B * H
