@@ -74,7 +74,7 @@ def _load():
         "sla_block_mask": (i32, [_p, _p, Shape, i64, _p, _p, _p, _p, sz, _p]),
         "ssa_pool_bytes": (sz, [Shape]),
         "w8a8_quant": (i32, [_p, i64, i64, _p, _p, _p]),
-        "w8a8_gemm": (i32, [_p, _p, _p, _p, i64, i64, i64, _p, _p, _p]),
+        "w8a8_gemm": (i32, [_p, _p, _p, _p, _p, i64, i64, i64, _p, _p, _p]),
         "sage_sla_attn_fwd": (i32, [_p, _p, _p, Shape, _p, _p, _p, _p, _p, i64, i32, C.c_float,
                                     _p, _p, _p, sz, _p]),
         "sage_qk_int32_tiles": (i32, [_p, _p, Shape, _p, i64, _p, _p]),
@@ -282,8 +282,9 @@ def w8a8_quant(x):
     return q, sc
 
 
-def w8a8_gemm(xq, sx, wq, sw, return_f32: bool = False):
-    """y = x . w^T from the block-quantized operands (w in the [out][in] layout)."""
+def w8a8_gemm(xq, sx, wq, sw, return_f32: bool = False, bias=None):
+    """y = x . w^T (+ bias) from the block-quantized operands (w in the
+    [out][in] layout; bias fp32 [N] or None)."""
     _need_gpu("xq", xq, torch.int8)
     M, K = xq.shape
     _need_gpu("wq", wq, torch.int8)
@@ -292,18 +293,21 @@ def w8a8_gemm(xq, sx, wq, sw, return_f32: bool = False):
         raise ValueError("wq must be [N][K] with N and K multiples of 128")
     _need_gpu("sx", sx, torch.float32, ((M + W8_BLK - 1) // W8_BLK, K // W8_BLK))
     _need_gpu("sw", sw, torch.float32, (N // W8_BLK, K // W8_BLK))
+    if bias is not None:
+        _need_gpu("bias", bias, torch.float32, (N,))
     y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     y32 = torch.empty((M, N), dtype=torch.float32, device=xq.device) if return_f32 else None
-    _check("w8a8_gemm", _load().w8a8_gemm(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K,
-                                          _ptr(y), _ptr(y32), _stream(xq.device)))
+    _check("w8a8_gemm", _load().w8a8_gemm(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(bias), M,
+                                          N, K, _ptr(y), _ptr(y32), _stream(xq.device)))
     return (y, y32) if return_f32 else y
 
 
-def w8a8_linear(x, wq, sw, return_f32: bool = False):
+def w8a8_linear(x, wq, sw, bias=None, return_f32: bool = False):
     """The W8A8 linear layer on bf16 activations x [M][K] with pre-quantized
-    weights (w8a8_quant of w [N][K]): quantize x, then the INT8 product."""
+    weights (w8a8_quant of w [N][K]) and an optional fp32 bias [N]: quantize
+    x, then the INT8 product."""
     xq, sx = w8a8_quant(x)
-    return w8a8_gemm(xq, sx, wq, sw, return_f32)
+    return w8a8_gemm(xq, sx, wq, sw, return_f32, bias)
 
 
 class KernelTimer:

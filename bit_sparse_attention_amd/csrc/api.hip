@@ -451,7 +451,8 @@ ssa_status w8a8_quant(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, 
 }
 
 ssa_status w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                     int64_t M, int64_t N, int64_t K, uint16_t* y, float* y32, void* stream) {
+                     const float* bias, int64_t M, int64_t N, int64_t K, uint16_t* y, float* y32,
+                     void* stream) {
     g_err[0] = 0;
     if (M < 1 || M > W8_MAX || N < 128 || N > W8_MAX || N % 128 || K < 128 || K > W8_MAX ||
         K % 128)
@@ -463,15 +464,17 @@ ssa_status w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const 
     TRY(need_ptr(sw, 4, "sw"));
     TRY(need_ptr(y, 16, "y"));
     if (y32 && !aligned(y32, 16)) return fail(SSA_ERR_INVALID, "y32 is not 16-byte aligned");
+    if (bias && !aligned(bias, 16)) return fail(SSA_ERR_INVALID, "bias is not 16-byte aligned");
     const size_t nkb = (size_t)K / 128;
     const Range ins[] = {{xq, (size_t)M * K, "xq"},
                          {wq, (size_t)N * K, "wq"},
                          {sx, (size_t)((M + 127) / 128) * nkb * 4, "sx"},
-                         {sw, (size_t)(N / 128) * nkb * 4, "sw"}};
+                         {sw, (size_t)(N / 128) * nkb * 4, "sw"},
+                         {bias, bias ? (size_t)N * 4 : 0, "bias"}};
     const Range outs[] = {{y, (size_t)M * N * 2, "y"}, {y32, y32 ? (size_t)M * N * 4 : 0, "y32"}};
-    TRY(check_alias(outs, 2, ins, 4));
+    TRY(check_alias(outs, 2, ins, 5));
     TRY(check_device());
-    hipError_t e = launch_w8a8_gemm(xq, sx, wq, sw, (int)M, (int)N, (int)K, y, y32,
+    hipError_t e = launch_w8a8_gemm(xq, sx, wq, sw, bias, (int)M, (int)N, (int)K, y, y32,
                                     (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "w8a8_gemm launch");
     return SSA_OK;

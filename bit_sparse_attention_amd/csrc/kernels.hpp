@@ -33,7 +33,8 @@ hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, 
 hipError_t launch_w8a8_quant(const uint16_t* x, int rows, int cols, int8_t* q, float* scale,
                              hipStream_t st);
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                            int M, int N, int K, uint16_t* y, float* y32, hipStream_t st);
+                            const float* bias, int M, int N, int K, uint16_t* y, float* y32,
+                            hipStream_t st);
 
 // attn.hip
 struct AttnArgs {

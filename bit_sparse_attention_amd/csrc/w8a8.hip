@@ -100,8 +100,8 @@ __device__ __forceinline__ int w8swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __global__ __launch_bounds__(WG_THREADS, 1) void w8a8_gemm_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int8_t* __restrict__ wq,
-    const float* __restrict__ sw, int M, int N, int K, uint16_t* __restrict__ y,
-    float* __restrict__ y32) {
+    const float* __restrict__ sw, const float* __restrict__ bias, int M, int N, int K,
+    uint16_t* __restrict__ y, float* __restrict__ y32) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[WG_STAGES * WG_STAGE];
     const int nmt = (M + WG_TM - 1) / WG_TM, nnt = N / WG_TN, nkb = K / W8;
     const int64_t total = (int64_t)nmt * nnt;
@@ -223,7 +223,12 @@ __global__ __launch_bounds__(WG_THREADS, 1) void w8a8_gemm_kernel(
     if (kb < nkb) step(kb++, S0{});
     if (kb < nkb) step(kb++, S1{});
 
-    // lane (m = l32, hi), tile [b] register 4q + x holds n = 8q + 4hi + x
+    // lane (m = l32, hi), tile [b] register 4q + x holds n = 8q + 4hi + x; the
+    // bias (one fp32 add after the whole chain) is the same for both m tiles
+    f32x4 bq[4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+        bq[qd] = bias ? *(const f32x4*)(bias + n0 + 32 * wn + 8 * qd + 4 * hi) : f32x4{};
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int m = m0 + 64 * wm + 32 * b + l32;
@@ -231,11 +236,10 @@ __global__ __launch_bounds__(WG_THREADS, 1) void w8a8_gemm_kernel(
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
             const int n = n0 + 32 * wn + 8 * qd + 4 * hi;
-            const f32x16& c = acc[b];
-            *(u16x4*)(y + (int64_t)m * N + n) =
-                u16x4{f2bf(c[4 * qd]), f2bf(c[4 * qd + 1]), f2bf(c[4 * qd + 2]), f2bf(c[4 * qd + 3])};
-            if (y32)
-                *(f32x4*)(y32 + (int64_t)m * N + n) = f32x4{c[4 * qd], c[4 * qd + 1], c[4 * qd + 2], c[4 * qd + 3]};
+            f32x4 c = f32x4{acc[b][4 * qd], acc[b][4 * qd + 1], acc[b][4 * qd + 2], acc[b][4 * qd + 3]};
+            if (bias) c = c + bq[qd];
+            *(u16x4*)(y + (int64_t)m * N + n) = u16x4{f2bf(c[0]), f2bf(c[1]), f2bf(c[2]), f2bf(c[3])};
+            if (y32) *(f32x4*)(y32 + (int64_t)m * N + n) = c;
         }
     }
 }
@@ -248,11 +252,12 @@ hipError_t launch_w8a8_quant(const uint16_t* x, int rows, int cols, int8_t* q, f
 }
 
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                            int M, int N, int K, uint16_t* y, float* y32, hipStream_t st) {
+                            const float* bias, int M, int N, int K, uint16_t* y, float* y32,
+                            hipStream_t st) {
     const int64_t total = (int64_t)((M + WG_TM - 1) / WG_TM) * (N / WG_TN);
     const int64_t grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL(w8a8_gemm_kernel, dim3((unsigned)grid), dim3(WG_THREADS), 0, st, xq, sx, wq, sw, M,
-                       N, K, y, y32);
+    hipLaunchKernelGGL(w8a8_gemm_kernel, dim3((unsigned)grid), dim3(WG_THREADS), 0, st, xq, sx, wq, sw,
+                       bias, M, N, K, y, y32);
     return hipGetLastError();
 }
 

@@ -193,8 +193,10 @@ ssa_status w8a8_quant(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, 
 /* w8a8_gemm -- the block-dequantized INT8 product. For each 128-wide block kb
  * of K, I = sum over the block of xq[m][k] * wq[n][k] (exact int32), and
  * y[m][n] = fmaf((float)I, fl32(sx[m/128][kb] * sw[n/128][kb]), y) in
- * ascending kb from 0 (INT8 matrix cores, fp32 accumulation).
+ * ascending kb from 0 (INT8 matrix cores, fp32 accumulation); then, for a
+ * layer with a bias, y = fl32(y + bias[n]).
  *   xq, sx in : w8a8_quant of x [M][K];  wq, sw in : w8a8_quant of w [N][K]
+ *   bias   in : fp32 [N], or NULL for none (16-byte aligned)
  *   y      out: bf16 [M][N] (round to nearest even of the fp32 result)
  *   y32    out: fp32 [M][N] copy before rounding, or NULL (16-byte aligned)
  * M, N, K <= 2^20; N and K multiples of 128. Errors as for the entry points
@@ -202,7 +204,8 @@ ssa_status w8a8_quant(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, 
  * launch).
  */
 ssa_status w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                     int64_t M, int64_t N, int64_t K, uint16_t* y, float* y32, void* stream);
+                     const float* bias, int64_t M, int64_t N, int64_t K, uint16_t* y, float* y32,
+                     void* stream);
 
 /* ---------------------------------------------------------------------------
  * Kernel timer (for benchmarks). After ssa_kernel_timer_start(n), each of the

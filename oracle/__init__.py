@@ -54,7 +54,7 @@ def lib():
             "orc_dense_rows": (None, [_p, _p, _p, _i64, _i64, _i64, C.c_float, _p, _i64, _p,
                                       C.c_int]),
             "orc_w8a8_quant": (None, [_p, _i64, _i64, _p, _p, C.c_int]),
-            "orc_w8a8_gemm": (None, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, C.c_int]),
+            "orc_w8a8_gemm": (None, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, C.c_int]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -298,8 +298,9 @@ def w8a8_quant(x, nthreads=None):
     return q, sc
 
 
-def w8a8_gemm(xq, sx, wq, sw, rows=None, nthreads=None):
-    """fp32 y [len(rows)][N] (all rows when rows is None) of the quantized product."""
+def w8a8_gemm(xq, sx, wq, sw, rows=None, nthreads=None, bias=None):
+    """fp32 y [len(rows)][N] (all rows when rows is None) of the quantized
+    product, plus the fp32 bias [N] when given."""
     xq = np.ascontiguousarray(xq, dtype=np.int8)
     wq = np.ascontiguousarray(wq, dtype=np.int8)
     sx = np.ascontiguousarray(sx, dtype=np.float32)
@@ -309,6 +310,9 @@ def w8a8_gemm(xq, sx, wq, sw, rows=None, nthreads=None):
     assert wq.shape[1] == K and K % W8_BLK == 0 and N % W8_BLK == 0
     rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
     y = np.empty((len(rows), N), np.float32)
-    lib().orc_w8a8_gemm(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, _ptr(rows), len(rows),
-                        _ptr(y), nthreads or threads())
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        assert bias.shape == (N,)
+    lib().orc_w8a8_gemm(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(bias), M, N, K, _ptr(rows),
+                        len(rows), _ptr(y), nthreads or threads())
     return y

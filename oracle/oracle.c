@@ -647,7 +647,7 @@ void orc_w8a8_quant(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, fl
 
 typedef struct {
     const int8_t *xq, *wq;
-    const float *sx, *sw;
+    const float *sx, *sw, *bias;
     int64_t M, N, K;
     const int64_t* rows;
     float* y;
@@ -655,7 +655,8 @@ typedef struct {
 
 /* One output row: for each column n, the exact int32 sum of each 128-wide
  * column block kb of K, then y = fmaf((float)I_kb, s_kb, y) in ascending kb
- * from 0, s_kb = fl32(sx[mb][kb] * sw[nb][kb]). */
+ * from 0, s_kb = fl32(sx[mb][kb] * sw[nb][kb]); then y = fl32(y + bias[n])
+ * when the layer has a bias. */
 static void w8_gemm_task(void* vctx, int64_t r) {
     w8_gemm_ctx* c = (w8_gemm_ctx*)vctx;
     int64_t m = c->rows[r], nkb = c->K / ORC_W8_BLK, mb = m / ORC_W8_BLK;
@@ -671,12 +672,14 @@ static void w8_gemm_task(void* vctx, int64_t r) {
             float s = c->sx[mb * nkb + kb] * c->sw[nb * nkb + kb];
             y = fmaf((float)acc, s, y);
         }
+        if (c->bias) y = y + c->bias[n];
         c->y[r * c->N + n] = y;
     }
 }
 
-void orc_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int64_t M,
-                   int64_t N, int64_t K, const int64_t* rows, int64_t R, float* y, int nthreads) {
-    w8_gemm_ctx c = {xq, wq, sx, sw, M, N, K, rows, y};
+void orc_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                   const float* bias, int64_t M, int64_t N, int64_t K, const int64_t* rows,
+                   int64_t R, float* y, int nthreads) {
+    w8_gemm_ctx c = {xq, wq, sx, sw, bias, M, N, K, rows, y};
     orc_parallel_for(R, nthreads, w8_gemm_task, &c);
 }

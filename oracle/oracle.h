@@ -134,10 +134,11 @@ void orc_w8a8_quant(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, fl
 
 /* y[r][n] for the listed rows m = rows[r]: per 128-wide column block kb of K
  * the exact int32 I = sum_k xq[m][k] * wq[n][k]; then y = fmaf((float)I, s, y)
- * in ascending kb from 0.0f with s = fl32(sx[m/128][kb] * sw[n/128][kb]). */
-void orc_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int64_t M,
-                   int64_t N, int64_t K, const int64_t* rows, int64_t R, float* y /*[R][N]*/,
-                   int nthreads);
+ * in ascending kb from 0.0f with s = fl32(sx[m/128][kb] * sw[n/128][kb]);
+ * then, if bias is not NULL, y = fl32(y + bias[n]). */
+void orc_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                   const float* bias /*[N] or NULL*/, int64_t M, int64_t N, int64_t K,
+                   const int64_t* rows, int64_t R, float* y /*[R][N]*/, int nthreads);
 
 #ifdef __cplusplus
 }

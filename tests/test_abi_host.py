@@ -188,8 +188,8 @@ def test_w8a8_gemm_rejects_bad_arguments():
     GB = 1 << 30
 
     def call(xq=_p(0), sx=_p(GB), wq=_p(2 * GB), sw=_p(3 * GB), M=300, N=256, K=384,
-             y=_p(4 * GB), y32=None):
-        return L.w8a8_gemm(xq, sx, wq, sw, M, N, K, y, y32, None)
+             y=_p(4 * GB), y32=None, bias=None):
+        return L.w8a8_gemm(xq, sx, wq, sw, bias, M, N, K, y, y32, None)
 
     assert call(M=0) == 1
     assert call(M=(1 << 20) + 1) == 1
@@ -202,6 +202,9 @@ def test_w8a8_gemm_rejects_bad_arguments():
     assert call(y=_p(2 * GB + 64)) == 1  # output overlaps wq
     assert b"overlap" in L.ssa_last_error()
     assert call(y32=_p(4 * GB + 1024)) == 1  # the two outputs overlap
+    assert b"overlap" in L.ssa_last_error()
+    assert call(bias=_p(6 * GB + 4)) == 1  # misaligned bias
+    assert call(bias=_p(4 * GB + 256)) == 1  # bias inside the output
     assert b"overlap" in L.ssa_last_error()
 
 

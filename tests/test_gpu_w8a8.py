@@ -46,16 +46,20 @@ def test_w8a8_quant_zero_block(orc):
     assert float(s[0, 1]) == 0.0 and int(q[:128, 128:].abs().max()) == 0
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (300, 256, 384), (700, 384, 1280),
-                                   (257, 128, 640)])
-def test_w8a8_gemm_bitexact(orc, M, N, K):
-    say(f"[w8a8 gemm] M={M} N={N} K={K}")
+@pytest.mark.parametrize("M,N,K,with_bias", [(1, 128, 128, False), (300, 256, 384, False),
+                                             (700, 384, 1280, False), (257, 128, 640, False),
+                                             (300, 256, 384, True), (1, 128, 640, True)])
+def test_w8a8_gemm_bitexact(orc, M, N, K, with_bias):
+    say(f"[w8a8 gemm] M={M} N={N} K={K} bias={with_bias}")
     x, w = make_linear(M, N, K, seed=M * 7 + K, outliers=True)
     xq, sx, oxq, osx = _check_quant(orc, x, "x")
     wq, sw, owq, osw = _check_quant(orc, w, "w")
-    y, y32 = ssa.w8a8_gemm(xq, sx, wq, sw, return_f32=True)
+    bias = (torch.randn(N, generator=torch.Generator().manual_seed(N + K)) * 0.5
+            if with_bias else None)
+    y, y32 = ssa.w8a8_gemm(xq, sx, wq, sw, return_f32=True,
+                           bias=None if bias is None else bias.to(DEV))
     torch.cuda.synchronize()
-    oy = orc.w8a8_gemm(oxq, osx, owq, osw)
+    oy = orc.w8a8_gemm(oxq, osx, owq, osw, bias=None if bias is None else bias.numpy())
     got = y32.cpu().numpy()
     assert np.array_equal(got.view(np.uint32), oy.view(np.uint32)), \
         f"max |diff| {np.abs(got - oy).max():.3e}"
@@ -65,12 +69,16 @@ def test_w8a8_gemm_bitexact(orc, M, N, K):
 def test_w8a8_linear_matches_the_two_calls(orc):
     x, w = make_linear(300, 256, 384, seed=3, outliers=True)
     xd, wd = x.to(DEV), w.to(DEV)
+    bias = torch.linspace(-1.0, 1.0, 256, device=DEV)
     wq, sw = ssa.w8a8_quant(wd)
     y1 = ssa.w8a8_linear(xd, wq, sw)
+    y1b = ssa.w8a8_linear(xd, wq, sw, bias=bias)
     xq, sx = ssa.w8a8_quant(xd)
     y2 = ssa.w8a8_gemm(xq, sx, wq, sw)
+    y2b = ssa.w8a8_gemm(xq, sx, wq, sw, bias=bias)
     torch.cuda.synchronize()
-    assert torch.equal(y1, y2)
+    assert torch.equal(y1, y2) and torch.equal(y1b, y2b)
+    assert not torch.equal(y1, y1b)
 
 
 def test_w8a8_fullsize_sampled(orc):

@@ -588,6 +588,23 @@ def test_w8a8_gemm_is_the_exact_fma_chain(orc):
             assert y[m, n] == np.float32(float(acc)), (m, n)
 
 
+def test_w8a8_gemm_bias_is_one_fp32_add(orc):
+    # the bias enters after the chain as one IEEE single add (numpy float32
+    # arithmetic, an implementation independent of the oracle's C), and a
+    # bias equal to the negated product gives exact zeros
+    rng = np.random.default_rng(9)
+    M, K, N = 7, 256, 256
+    x = _bf16_matrix(rng.standard_normal((M, K)))
+    w = _bf16_matrix(rng.standard_normal((N, K)) * 0.05)
+    xq, sx = orc.w8a8_quant(x)
+    wq, sw = orc.w8a8_quant(w)
+    y = orc.w8a8_gemm(xq, sx, wq, sw)
+    bias = (rng.standard_normal(N) * 3).astype(np.float32)
+    yb = orc.w8a8_gemm(xq, sx, wq, sw, bias=bias)
+    assert np.array_equal(yb.view(np.uint32), (y + bias[None, :]).astype(np.float32).view(np.uint32))
+    assert np.all(orc.w8a8_gemm(xq, sx, wq, sw, rows=[3], bias=-y[3]) == 0.0)
+
+
 def test_w8a8_gemm_power_of_two_scales_is_an_integer_product(orc):
     # every block's amax is 127 * 2^e, so every scale is a power of two, every
     # quantized value is x / scale exactly, and the product is exact integers
