@@ -338,7 +338,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stages", action="store_true", help="also time each ABI call on its own")
+    ap.add_argument("--stages", action="store_true",
+                    help="also time each staged ABI call on its own, and the staged step")
+    ap.add_argument("--staged", action="store_true",
+                    help="time the three staged calls instead of the one-call step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain MIB-MiB device copy (for counter scaling)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -383,7 +386,7 @@ def main():
     dev = torch.device("cuda:0")
     print(f"# generating {w.name}", file=sys.stderr, flush=True)
     q, k, v = make_workload(w)
-    plan = ssa.SageSLAPlan(w.B, w.H, w.N, w.topk, linear=True, device=dev)
+    plan = ssa.SageSLAPlan(w.B, w.H, w.N, w.topk, linear=True, device=dev, fused=not args.staged)
     plan.bind(q.to(dev), k.to(dev), v.to(dev))
     for _ in range(args.warmup):
         plan.run()
@@ -409,7 +412,8 @@ def main():
     if args.stages:
         stages = {}
         for name, fn in (("sage_quant_qk", plan.quant), ("sla_block_mask", plan.mask),
-                         ("sage_sla_attn_fwd", plan.attn)):
+                         ("sage_sla_attn_fwd", plan.attn), ("staged_step", plan.run_staged),
+                         ("sage_sla_fwd", plan.step)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(K):
@@ -439,7 +443,8 @@ def main():
         "data": "synthetic (seeded; Q,V ~ N(0,1), K ~ N(0,1) + per-channel N(0,3) offset)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": HEAD_DIM,
                    "topk": w.topk, "keep": plan.keep, "branches": "sparse+linear"
-                   if plan.branches == 3 else "sparse", "spikes": w.spikes},
+                   if plan.branches == 3 else "sparse", "spikes": w.spikes,
+                   "call": "sage_sla_fwd" if plan.fused else "staged"},
         "attn_kernel_ms": k_ms,
         "attn_kernel_ms_pct": k_pct,
         "attn_kernel_tops": k_tops,

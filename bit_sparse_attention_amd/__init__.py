@@ -18,17 +18,18 @@ import os
 import torch
 
 __all__ = [
-    "sage_quant_qk", "sla_block_mask", "sage_sla_attn_fwd", "sage_qk_int32_tiles", "sagesla",
+    "sage_quant_qk", "sla_block_mask", "sage_sla_attn_fwd", "sage_sla_fwd", "sage_qk_int32_tiles",
+    "sagesla",
     "SageSLAPlan", "KernelTimer", "keep_blocks", "num_q_blocks", "num_k_blocks", "workspace_bytes",
     "pool_bytes", "new_pool", "lib_path", "w8a8_quant", "w8a8_gemm", "w8a8_linear",
-    "SPARSE", "LINEAR", "OP_QUANT", "OP_MASK", "OP_ATTN",
+    "SPARSE", "LINEAR", "OP_QUANT", "OP_MASK", "OP_ATTN", "OP_STEP",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssa.so")
 
 SPARSE, LINEAR = 1, 2
-OP_QUANT, OP_MASK, OP_ATTN = 0, 1, 2
+OP_QUANT, OP_MASK, OP_ATTN, OP_STEP = 0, 1, 2, 3
 HEAD_DIM = 128
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
@@ -77,6 +78,8 @@ def _load():
         "w8a8_gemm": (i32, [_p, _p, _p, _p, _p, i64, i64, i64, _p, _p, _p]),
         "sage_sla_attn_fwd": (i32, [_p, _p, _p, Shape, _p, _p, _p, _p, _p, i64, i32, C.c_float,
                                     _p, _p, _p, sz, _p]),
+        "sage_sla_fwd": (i32, [_p, _p, _p, Shape, i64, i32, C.c_float, _p, _p, _p, _p, _p, _p,
+                               _p, _p, _p, _p, sz, _p]),
         "sage_qk_int32_tiles": (i32, [_p, _p, Shape, _p, i64, _p, _p]),
         "ssa_kernel_timer_start": (i32, [i32]),
         "ssa_kernel_timer_read": (i32, [C.POINTER(C.c_float), i32]),
@@ -247,11 +250,51 @@ def sage_qk_int32_tiles(q_i8, k_i8, tiles):
     return out
 
 
+def sage_sla_fwd(q, k, v, topk: float | None = 0.1, linear: bool = True, sm_scale: float = 0.0,
+                 return_f32: bool = False, return_mask: bool = False, return_all: bool = False):
+    """The whole step in one library call (quantize, select unless topk is
+    None, attend), bit-identical to the three staged calls. return_all adds a
+    dict of the intermediates (q_i8, q_scale, k_i8, k_scale, k_mean, kidx and,
+    with return_mask, mask)."""
+    s = _qkv_shape(q, k, v)
+    B, H, N, D = q.shape
+    dev = q.device
+    nqb, nkb = num_q_blocks(N), num_k_blocks(N)
+    dense = topk is None
+    keep = nkb if dense else keep_blocks(N, topk)
+    branches = SPARSE | (LINEAR if (linear and not dense) else 0)
+    e = dict(device=dev)
+    q_i8 = torch.empty((B, H, N, D), dtype=torch.int8, **e)
+    k_i8 = torch.empty_like(q_i8)
+    q_scale = torch.empty((B, H, nqb), dtype=torch.float32, **e)
+    k_scale = torch.empty((B, H, nkb), dtype=torch.float32, **e)
+    k_mean = torch.empty((B, H, D), dtype=torch.float32, **e)
+    kidx = None if dense else torch.empty((B, H, nqb, keep), dtype=torch.int32, **e)
+    mask = (torch.empty((B, H, nqb, nkb), dtype=torch.uint8, **e)
+            if (return_mask and not dense) else None)
+    out = torch.empty((B, H, N, D), dtype=torch.bfloat16, **e)
+    out32 = torch.empty((B, H, N, D), dtype=torch.float32, **e) if return_f32 else None
+    ws, n = _ws(OP_STEP, s, dev, keep, branches)
+    _check("sage_sla_fwd", _load().sage_sla_fwd(
+        _ptr(q), _ptr(k), _ptr(v), s, int(keep), int(branches), float(sm_scale), _ptr(q_i8),
+        _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(k_mean), _ptr(kidx), _ptr(mask),
+        _ptr(out), _ptr(out32), _ptr(ws), n, _stream(dev)))
+    res = (out, out32) if return_f32 else (out,)
+    if return_all:
+        inter = dict(q_i8=q_i8, q_scale=q_scale, k_i8=k_i8, k_scale=k_scale, k_mean=k_mean,
+                     kidx=kidx)
+        if return_mask:
+            inter["mask"] = mask
+        res = res + (inter,)
+    return res if len(res) > 1 else res[0]
+
+
 def sagesla(q, k, v, topk: float | None = 0.1, linear: bool = True, sm_scale: float = 0.0,
             return_f32: bool = False):
-    """The whole path: quantize, select blocks (unless topk is None: dense),
-    attend. The meaning of topk is --sla_topk's: the fraction of key blocks
-    kept per query block."""
+    """The whole path as the three staged calls: quantize, select blocks
+    (unless topk is None: dense), attend. The meaning of topk is --sla_topk's:
+    the fraction of key blocks kept per query block. sage_sla_fwd gives the
+    same result from one call."""
     pool = None if topk is None else new_pool(q)
     q_i8, q_scale, k_i8, k_scale, _ = sage_quant_qk(q, k, pool)
     if topk is None:
@@ -334,12 +377,14 @@ class KernelTimer:
 class SageSLAPlan:
     """Preallocated buffers for repeated SageSLA calls on one shape.
 
-    run() enqueues sage_quant_qk, sla_block_mask (unless dense) and
-    sage_sla_attn_fwd on the current stream; each stage can also be enqueued on
-    its own (quant(), mask(), attn())."""
+    run() enqueues the step on the current stream: one sage_sla_fwd call, or
+    with fused=False the staged calls sage_quant_qk, sla_block_mask (unless
+    dense) and sage_sla_attn_fwd (run_staged()); each stage can also be
+    enqueued on its own (quant(), mask(), attn()). Both forms write the same
+    buffers with bit-identical contents."""
 
     def __init__(self, B, H, N, topk: float | None, linear: bool = True, device="cuda",
-                 sm_scale: float = 0.0, want_f32: bool = False):
+                 sm_scale: float = 0.0, want_f32: bool = False, fused: bool = True):
         L = _load()
         dev = torch.device(device)
         self.shape = Shape(B, H, N, HEAD_DIM)
@@ -365,8 +410,10 @@ class SageSLAPlan:
         self.ws_n = {
             OP_QUANT: workspace_bytes(OP_QUANT, self.shape),
             OP_ATTN: workspace_bytes(OP_ATTN, self.shape, self.keep, self.branches),
+            OP_STEP: workspace_bytes(OP_STEP, self.shape, self.keep, self.branches),
         }
-        # one workspace serves the three calls (they run in order on one stream)
+        self.fused = bool(fused)
+        # one workspace serves every call (they run in order on one stream)
         self.ws = torch.empty(max(self.ws_n.values()), dtype=torch.uint8, **e)
         self.device = dev
         self._L = L
@@ -398,10 +445,23 @@ class SageSLAPlan:
             self.branches, self.sm_scale, _ptr(self.out), _ptr(self.out32), _ptr(self.ws),
             self.ws_n[OP_ATTN], _stream(self.device)))
 
-    def run(self):
+    def step(self):
+        _check("sage_sla_fwd", self._L.sage_sla_fwd(
+            _ptr(self.q), _ptr(self.k), _ptr(self.v), self.shape, self.keep, self.branches,
+            self.sm_scale, _ptr(self.q_i8), _ptr(self.q_scale), _ptr(self.k_i8),
+            _ptr(self.k_scale), _ptr(self.k_mean), _ptr(self.kidx), None, _ptr(self.out),
+            _ptr(self.out32), _ptr(self.ws), self.ws_n[OP_STEP], _stream(self.device)))
+
+    def run_staged(self):
         self.quant()
         self.mask()
         self.attn()
+        return self.out
+
+    def run(self):
+        if not self.fused:
+            return self.run_staged()
+        self.step()
         return self.out
 
     def capture(self):

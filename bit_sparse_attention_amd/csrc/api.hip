@@ -152,6 +152,21 @@ AttnWs ws_attn(const Dims& d, bool linear) {
     return w;
 }
 
+// the whole step: the attention's workspace, then the pooled means, then the
+// K-mean block partials
+struct StepWs {
+    AttnWs attn;
+    size_t pool, part, total;
+};
+StepWs ws_step(const Dims& d, bool linear) {
+    StepWs w;
+    w.attn = ws_attn(d, linear);
+    w.pool = w.attn.total;
+    w.part = w.pool + ws_mask(d).total;
+    w.total = w.part + ws_quant(d);
+    return w;
+}
+
 ssa_status check_ws(void* ws, size_t have, size_t need) {
     if (need == 0) return SSA_OK;
     if (!ws) return fail(SSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -186,6 +201,58 @@ int timer_slot() {
         if (_st != SSA_OK) return _st;  \
     } while (0)
 
+// The attention call's launches after validation, shared by the staged and
+// the one-call step. kpart non-null: the V-layout pass also writes the K-mean
+// block partials (and, with kbarT, the pooled key means).
+hipError_t enqueue_states(const Dims& d, bool linear, const uint16_t* k, const uint16_t* v,
+                          char* base, const AttnWs& w, float* kpart, float* kbarT, int ldk,
+                          hipStream_t st) {
+    uint16_t* vt = (uint16_t*)(base + w.vt);
+    if (linear)
+        return launch_linear_states(k, v, d.BH, (int)d.N, vt, (uint16_t*)(base + w.hs),
+                                    (float*)(base + w.hpart), (float*)(base + w.htot), kpart,
+                                    kbarT, ldk, st);
+    return launch_vt_only(k, v, d.BH, (int)d.N, vt, kpart, kbarT, ldk, st);
+}
+
+hipError_t enqueue_complement(const Dims& d, const int32_t* kidx, int64_t keep, char* base,
+                              const AttnWs& w, hipStream_t st) {
+    return launch_complement(kidx, (int)keep, (const uint16_t*)(base + w.hs),
+                             (const float*)(base + w.htot), d.BH, (int)d.N,
+                             (uint32_t*)(base + w.msel), (float*)(base + w.hnon), st);
+}
+
+hipError_t enqueue_attn(const Dims& d, bool sparse, bool linear, const uint16_t* q,
+                        const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                        const float* k_scale, const int32_t* kidx, int64_t keep, float sm_scale,
+                        uint16_t* out, float* out_f32, char* base, const AttnWs& w,
+                        hipStream_t st) {
+    const float sm = sm_scale > 0.f ? sm_scale : (float)(1.0 / std::sqrt((double)HD));
+    AttnArgs a;
+    a.q_i8 = q_i8;
+    a.q_scale = q_scale;
+    a.k_i8 = k_i8;
+    a.k_scale = k_scale;
+    a.vt = (const uint16_t*)(base + w.vt);
+    a.kidx = kidx;
+    a.keep = (int)keep;
+    a.N = (int)d.N;
+    a.nqb = (int)d.nqb;
+    a.nkb = (int)d.nkb;
+    a.BH = d.BH;
+    a.K32 = (float)((double)sm * 1.4426950408889634074);
+    a.do_sparse = sparse ? 1 : 0;
+    a.q = q;
+    a.hnon = linear ? (const float*)(base + w.hnon) : nullptr;
+    a.out = out;
+    a.out32 = out_f32;
+    const int slot = timer_slot();
+    if (slot >= 0) (void)hipEventRecord(g_ev0[slot], st);
+    const hipError_t e = launch_attn(a, st);
+    if (slot >= 0) (void)hipEventRecord(g_ev1[slot], st);
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,9 +282,10 @@ size_t ssa_workspace_bytes(int op, ssa_shape s, int64_t keep, int branches) {
     switch (op) {
         case SSA_OP_QUANT: return ws_quant(d);
         case SSA_OP_MASK: return ws_mask(d).total;
-        case SSA_OP_ATTN: {
+        case SSA_OP_ATTN:
+        case SSA_OP_STEP: {
             const bool linear = (branches & SSA_BRANCH_LINEAR) && keep >= 1 && keep < d.nkb;
-            return ws_attn(d, linear).total;
+            return op == SSA_OP_ATTN ? ws_attn(d, linear).total : ws_step(d, linear).total;
         }
         default: return 0;
     }
@@ -361,48 +429,86 @@ ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
     TRY(check_ws(ws, ws_bytes, w.total));
     TRY(check_device());
 
-    const float sm = sm_scale > 0.f ? sm_scale : (float)(1.0 / std::sqrt((double)HD));
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = enqueue_states(d, linear, k, v, (char*)ws, w, nullptr, nullptr, 0, st);
+    if (e == hipSuccess && linear) e = enqueue_complement(d, kidx, keep, (char*)ws, w, st);
+    if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_fwd launch (linear / V layout)");
+    e = enqueue_attn(d, sparse, linear, q, q_i8, q_scale, k_i8, k_scale, kidx, keep, sm_scale,
+                     out, out_f32, (char*)ws, w, st);
+    if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_fwd launch");
+    return SSA_OK;
+}
+
+ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, ssa_shape s,
+                        int64_t keep, int branches, float sm_scale, int8_t* q_i8, float* q_scale,
+                        int8_t* k_i8, float* k_scale, float* k_mean, int32_t* kidx,
+                        uint8_t* mask, uint16_t* out, float* out_f32, void* ws, size_t ws_bytes,
+                        void* stream) {
+    g_err[0] = 0;
+    Dims d;
+    TRY(check_shape(s, &d));
+    if (branches < 1 || branches > 3)
+        return fail(SSA_ERR_INVALID, "branches=%d must be SPARSE, LINEAR or both", branches);
+    if (keep < 1 || keep > d.nkb)
+        return fail(SSA_ERR_INVALID, "keep=%lld outside [1, %lld]", (long long)keep,
+                    (long long)d.nkb);
+    if (!kidx && keep != d.nkb)
+        return fail(SSA_ERR_INVALID, "dense call (kidx NULL) needs keep == Nkb (%lld)",
+                    (long long)d.nkb);
+    if (mask && !kidx) return fail(SSA_ERR_INVALID, "mask needs kidx (a dense call selects nothing)");
+    if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
+        return fail(SSA_ERR_INVALID, "sm_scale is not finite");
+    const bool sparse = branches & SSA_BRANCH_SPARSE;
+    const bool linear = (branches & SSA_BRANCH_LINEAR) && kidx && keep < d.nkb;
+    TRY(need_ptr(q, 16, "q"));
+    TRY(need_ptr(k, 16, "k"));
+    TRY(need_ptr(v, 16, "v"));
+    TRY(need_ptr(q_i8, 16, "q_i8"));
+    TRY(need_ptr(k_i8, 16, "k_i8"));
+    TRY(need_ptr(q_scale, 4, "q_scale"));
+    TRY(need_ptr(k_scale, 4, "k_scale"));
+    TRY(need_ptr(k_mean, 4, "k_mean"));
+    TRY(need_ptr(out, 16, "out"));
+    if (out_f32) TRY(need_ptr(out_f32, 16, "out_f32"));
+    if (kidx) TRY(need_ptr(kidx, 4, "kidx"));
+    const size_t nel = (size_t)d.BH * d.N * HD;
+    const Range ins[] = {{q, nel * 2, "q"}, {k, nel * 2, "k"}, {v, nel * 2, "v"}};
+    const Range outs[] = {{q_i8, nel, "q_i8"},
+                          {k_i8, nel, "k_i8"},
+                          {q_scale, (size_t)d.BH * d.nqb * 4, "q_scale"},
+                          {k_scale, (size_t)d.BH * d.nkb * 4, "k_scale"},
+                          {k_mean, (size_t)d.BH * HD * 4, "k_mean"},
+                          {kidx, kidx ? (size_t)d.BH * d.nqb * keep * 4 : 0, "kidx"},
+                          {mask, mask ? (size_t)d.BH * d.nqb * d.nkb : 0, "mask"},
+                          {out, nel * 2, "out"},
+                          {out_f32, out_f32 ? nel * 4 : 0, "out_f32"},
+                          {ws, ws_bytes, "workspace"}};
+    TRY(check_alias(outs, 10, ins, 3));
+    const StepWs w = ws_step(d, linear);
+    TRY(check_ws(ws, ws_bytes, w.total));
+    TRY(check_device());
+
     hipStream_t st = (hipStream_t)stream;
     char* base = (char*)ws;
-    uint16_t* vt = (uint16_t*)(base + w.vt);
-    hipError_t e;
-    float* hnon = nullptr;
-    if (linear) {
-        uint16_t* hs = (uint16_t*)(base + w.hs);
-        float* hpart = (float*)(base + w.hpart);
-        float* htot = (float*)(base + w.htot);
-        uint32_t* msel = (uint32_t*)(base + w.msel);
-        hnon = (float*)(base + w.hnon);
-        e = launch_linear_states(k, v, d.BH, (int)d.N, vt, hs, hpart, htot, st);
-        if (e == hipSuccess)
-            e = launch_complement(kidx, (int)keep, hs, htot, d.BH, (int)d.N, msel, hnon, st);
-    } else {
-        e = launch_vt_only(v, d.BH, (int)d.N, vt, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_fwd launch (linear / V layout)");
-    AttnArgs a;
-    a.q_i8 = q_i8;
-    a.q_scale = q_scale;
-    a.k_i8 = k_i8;
-    a.k_scale = k_scale;
-    a.vt = vt;
-    a.kidx = kidx;
-    a.keep = (int)keep;
-    a.N = (int)d.N;
-    a.nqb = (int)d.nqb;
-    a.nkb = (int)d.nkb;
-    a.BH = d.BH;
-    a.K32 = (float)((double)sm * 1.4426950408889634074);
-    a.do_sparse = sparse ? 1 : 0;
-    a.q = q;
-    a.hnon = hnon;
-    a.out = out;
-    a.out32 = out_f32;
-    const int slot = timer_slot();
-    if (slot >= 0) (void)hipEventRecord(g_ev0[slot], st);
-    e = launch_attn(a, st);
-    if (slot >= 0) (void)hipEventRecord(g_ev1[slot], st);
-    if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_fwd launch");
+    const MaskWs pw = ws_mask(d);
+    float* qbar = (float*)(base + w.pool + pw.qbar);
+    float* kbarT = (float*)(base + w.pool + pw.kbarT);
+    float* part = (float*)(base + w.part);
+    // one pass over K and V: V layout (and linear states), K-mean partials and
+    // pooled key means; then mean, quantization and pooled query means
+    hipError_t e = enqueue_states(d, linear, k, v, base, w.attn, part, kidx ? kbarT : nullptr,
+                                  (int)pw.ldk, st);
+    if (e == hipSuccess)
+        e = launch_quant_from_sums(q, k, d.BH, (int)d.N, q_i8, q_scale, k_i8, k_scale, k_mean,
+                                   part, kidx ? qbar : nullptr, st);
+    if (e == hipSuccess && kidx)
+        e = launch_score_topk(qbar, kbarT, (int)pw.ldk, d.BH, (int)d.nqb, (int)d.nkb, (int)keep,
+                              kidx, mask, st);
+    if (e == hipSuccess && linear) e = enqueue_complement(d, kidx, keep, base, w.attn, st);
+    if (e != hipSuccess) return hip_fail(e, "sage_sla_fwd launch (quantization / selection)");
+    e = enqueue_attn(d, sparse, linear, q, q_i8, q_scale, k_i8, k_scale, kidx, keep, sm_scale,
+                     out, out_f32, base, w.attn, st);
+    if (e != hipSuccess) return hip_fail(e, "sage_sla_fwd launch");
     return SSA_OK;
 }
 

@@ -11,6 +11,12 @@ namespace ssa {
 hipError_t launch_quant_qk(const uint16_t* q, const uint16_t* k, int64_t BH, int N, int8_t* q_i8,
                            float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
                            float* ws_part, float* qbar, float* kbarT, int ldk, hipStream_t st);
+// the same minus the K-mean partial pass: ws_part already holds the per-block
+// K sums (from launch_linear_states / launch_vt_only with kpart)
+hipError_t launch_quant_from_sums(const uint16_t* q, const uint16_t* k, int64_t BH, int N,
+                                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                                  float* k_mean, const float* ws_part, float* qbar,
+                                  hipStream_t st);
 hipError_t launch_pool(const uint16_t* q, const uint16_t* k, int64_t BH, int N, float* qbar,
                        float* kbarT, int ldk, hipStream_t st);
 // mask.hip
@@ -20,10 +26,13 @@ hipError_t launch_score_topk(const float* qbar, const float* kbarT, int ldk, int
 // linear.hip
 constexpr int LIN_GROUP = 16;    // key blocks per linear-states workgroup
 constexpr int GEMM_KALIGN = 32;  // the complement GEMM's key-block count is padded to this
+// kpart (may be null): also write the per-block K sums of the K mean, and
+// kbarT (may be null) the pooled key means, from the same pass over K
 hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                                 uint16_t* vt, uint16_t* hs, float* hpart, float* htot,
-                                hipStream_t st);
-hipError_t launch_vt_only(const uint16_t* v, int64_t BH, int N, uint16_t* vt, hipStream_t st);
+                                float* kpart, float* kbarT, int ldk, hipStream_t st);
+hipError_t launch_vt_only(const uint16_t* k, const uint16_t* v, int64_t BH, int N, uint16_t* vt,
+                          float* kpart, float* kbarT, int ldk, hipStream_t st);
 // bytes of the complement GEMM's selection rows (msel) for nkbp padded key blocks
 size_t msel_bytes(int64_t BH, int64_t nqb, int64_t nkbp);
 hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, const float* htot,

@@ -33,16 +33,31 @@ constexpr int LS_IT = KBLK * HD / 8 / LS_THREADS;     // 16-byte chunks per thre
 // order in which one lane of the 32x32 MFMA output holds its rows), and z
 // follows in the same d order; the GEMM and the apply only need a consistent
 // order, and each lane then stores 16-byte runs.
-template <bool STATES>
+//
+// SUMS: the same pass over K also yields what the K mean and the block mask
+// need from raw K, so that K is read once before its quantization instead of
+// twice: per key block, kpart[bh][j][d] = the fp32 sum of the block's valid
+// tokens of channel d, added in token order from 0 (the block partial of the
+// K mean), and kbarT[bh][d][j] = kpart / valid (the pooled key mean, stored
+// transposed with row pitch ldk; skipped when kbarT is null). Raw K is staged
+// token-major in LDS and one thread adds one channel's column in order, so
+// both equal what colsum_kernel<64, 0> writes, bit for bit.
+template <bool STATES, bool SUMS>
 __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v, int N,
                                                             int nkb, int ngroups,
                                                             uint16_t* __restrict__ vt,
                                                             uint16_t* __restrict__ hs,
-                                                            float* __restrict__ hpart) {
+                                                            float* __restrict__ hpart,
+                                                            float* __restrict__ kpart,
+                                                            float* __restrict__ kbarT, int ldk) {
+    constexpr int KBP = HD + 1;  // pitch of the staged pooled means (no bank conflicts)
     __shared__ __attribute__((aligned(16))) uint16_t vtl[HD * TP];
     __shared__ __attribute__((aligned(16))) uint16_t fkh[STATES ? HD * TP : 8];
     __shared__ __attribute__((aligned(16))) uint16_t fkl[STATES ? HD * TP : 8];
+    constexpr int KP = HD + 8;  // LDS pitch (bf16) of the token-major raw K tile: 272 B
+    __shared__ __attribute__((aligned(16))) uint16_t kraw[SUMS ? KBLK * KP : 8];
+    __shared__ float kbs[SUMS ? LIN_GROUP * KBP : 1];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
               hi = lane >> 5;
     // wave (eg, dh) owns the state columns e = 32eg .. 32eg+31 and rows
@@ -51,7 +66,7 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
     const int eg = wave & 3, dh = wave >> 2;
     const int64_t bh = blockIdx.y;
     const int g = blockIdx.x;
-    const int G = STATES ? LIN_GROUP : 1;
+    const int G = (STATES || SUMS) ? LIN_GROUP : 1;
     f32x16 tot[2], totz = f32x16{};
 #pragma unroll
     for (int t = 0; t < 2; ++t) tot[t] = f32x16{};
@@ -68,7 +83,7 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
             const bool ok = tok < N;
             const int64_t off = (bh * N + (ok ? tok : 0)) * HD + 8 * ch;
             vv[it] = ok ? *(const u16x8*)(v + off) : u16x8{};
-            if (STATES) kk[it] = ok ? *(const u16x8*)(k + off) : u16x8{};
+            if (STATES || SUMS) kk[it] = ok ? *(const u16x8*)(k + off) : u16x8{};
         }
     };
     auto block = [&](int jb, u16x8 (&vv)[LS_IT], u16x8 (&kk)[LS_IT]) {
@@ -81,6 +96,7 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
             const bool ok = j * KBLK + u < N;
 #pragma unroll
             for (int e = 0; e < 8; ++e) vtl[(8 * ch + e) * TP + u] = vv[it][e];
+            if (SUMS) *(u16x8*)(kraw + u * KP + 8 * ch) = kk[it];  // token-major
             if (STATES) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -106,6 +122,30 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
             *(u16x8*)(vt + ((bh * nkb + j) * HD + dv) * KBLK + 8 * pc) =
                 u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
         }
+        // K sums: waves 4 and 5 (the z products weigh on waves 0-3) add the
+        // column of channel d = tid - 256 in token order, 16 tokens at a time;
+        // with the states, each piece sits after one step of MFMAs so that
+        // the dependent adds run while the matrix core works
+        const bool sumw = SUMS && tid >= 256 && tid < 256 + HD;
+        const int dsum = tid - 256;
+        const int valid = min(KBLK, N - j * KBLK);
+        float ksum = 0.f;
+        auto sum16 = [&](int uc) {
+            uint16_t r[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r[e] = kraw[(16 * uc + e) * KP + dsum];
+            if (valid == KBLK) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) ksum += bf2f(r[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (16 * uc + e < valid) ksum += bf2f(r[e]);
+            }
+        };
+        if (SUMS && !STATES && sumw)
+#pragma unroll
+            for (int uc = 0; uc < 4; ++uc) sum16(uc);
         if (STATES) {
             // (h_j^T)^T[d][e] = sum_u phi(K)[u][d] V[u][e]: A = phi(K)^T rows d (hi and
             // lo parts, two products, fp32 accumulation), B = V columns e. This
@@ -128,6 +168,7 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
                     acc[t] = mfma_bf16_32x32x16(ah, b, acc[t]);
                     acc[t] = mfma_bf16_32x32x16(al, b, acc[t]);
                 }
+                if (SUMS && sumw) sum16(uc);
             }
             // z_j[d] for rows d = 32eg + ...: the same product against ones
             if (dh == 0) {
@@ -167,6 +208,10 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
                 totz += accz;
             }
         }
+        if (SUMS && sumw) {
+            kpart[(bh * nkb + j) * HD + dsum] = ksum;
+            kbs[jb * KBP + dsum] = ksum / (float)valid;
+        }
         __syncthreads();
     };
     const int nb = min(G, nkb - g * G);  // key blocks of this workgroup
@@ -175,6 +220,14 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
     for (int jb = 0; jb < nb; jb += 2) {
         block(jb, va, ka);
         if (jb + 1 < nb) block(jb + 1, vb, kb);
+    }
+    if (SUMS && kbarT) {
+        // the group's pooled means (staged before the last barrier of the
+        // block loop) as runs of up to LIN_GROUP consecutive blocks per channel
+        for (int idx = tid; idx < HD * LIN_GROUP; idx += LS_THREADS) {
+            const int d = idx / LIN_GROUP, i = idx % LIN_GROUP;
+            if (i < nb) kbarT[(bh * HD + d) * (int64_t)ldk + g * G + i] = kbs[i * KBP + d];
+        }
     }
     if (STATES) {
         float* prow = hpart + (bh * ngroups + g) * (int64_t)HS_ROW;
@@ -473,20 +526,33 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
 
 hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                                 uint16_t* vt, uint16_t* hs, float* hpart, float* htot,
-                                hipStream_t st) {
+                                float* kpart, float* kbarT, int ldk, hipStream_t st) {
     const int nkb = (N + KBLK - 1) / KBLK;
     const int ngroups = (nkb + LIN_GROUP - 1) / LIN_GROUP;
-    hipLaunchKernelGGL((linear_states_kernel<true>), dim3(ngroups, BH), dim3(LS_THREADS), 0, st, k, v, N,
-                       nkb, ngroups, vt, hs, hpart);
+    if (kpart)
+        hipLaunchKernelGGL((linear_states_kernel<true, true>), dim3(ngroups, BH), dim3(LS_THREADS),
+                           0, st, k, v, N, nkb, ngroups, vt, hs, hpart, kpart, kbarT, ldk);
+    else
+        hipLaunchKernelGGL((linear_states_kernel<true, false>), dim3(ngroups, BH), dim3(LS_THREADS),
+                           0, st, k, v, N, nkb, ngroups, vt, hs, hpart, nullptr, nullptr, 0);
     hipLaunchKernelGGL(htot_kernel, dim3((HS_ROW + 255) / 256, BH), dim3(256), 0, st, hpart, ngroups,
                        htot);
     return hipGetLastError();
 }
 
-hipError_t launch_vt_only(const uint16_t* v, int64_t BH, int N, uint16_t* vt, hipStream_t st) {
+hipError_t launch_vt_only(const uint16_t* k, const uint16_t* v, int64_t BH, int N, uint16_t* vt,
+                          float* kpart, float* kbarT, int ldk, hipStream_t st) {
     const int nkb = (N + KBLK - 1) / KBLK;
-    hipLaunchKernelGGL((linear_states_kernel<false>), dim3(nkb, BH), dim3(LS_THREADS), 0, st, nullptr, v, N,
-                       nkb, nkb, vt, nullptr, nullptr);
+    if (kpart) {
+        const int ngroups = (nkb + LIN_GROUP - 1) / LIN_GROUP;
+        hipLaunchKernelGGL((linear_states_kernel<false, true>), dim3(ngroups, BH),
+                           dim3(LS_THREADS), 0, st, k, v, N, nkb, ngroups, vt, nullptr, nullptr,
+                           kpart, kbarT, ldk);
+    } else {
+        hipLaunchKernelGGL((linear_states_kernel<false, false>), dim3(nkb, BH), dim3(LS_THREADS),
+                           0, st, nullptr, v, N, nkb, nkb, vt, nullptr, nullptr, nullptr, nullptr,
+                           0);
+    }
     return hipGetLastError();
 }
 

@@ -199,9 +199,18 @@ hipError_t launch_quant_qk(const uint16_t* q, const uint16_t* k, int64_t BH, int
                            int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
                            float* k_mean, float* ws_part, float* qbar, float* kbarT, int ldk,
                            hipStream_t st) {
-    const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
+    const int nkb = (N + KBLK - 1) / KBLK;
     hipLaunchKernelGGL((colsum_kernel<KBLK, 0>), dim3((nkb + 15) / 16, BH), dim3(256), 0, st, k, N,
                        nkb, ldk, ws_part, kbarT);
+    return launch_quant_from_sums(q, k, BH, N, q_i8, q_scale, k_i8, k_scale, k_mean, ws_part, qbar,
+                                  st);
+}
+
+hipError_t launch_quant_from_sums(const uint16_t* q, const uint16_t* k, int64_t BH, int N,
+                                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                                  float* k_mean, const float* ws_part, float* qbar,
+                                  hipStream_t st) {
+    const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
     hipLaunchKernelGGL(kmean_final_kernel, dim3(BH), dim3(128), 0, st, ws_part, nkb, N, k_mean);
     if (qbar)
         hipLaunchKernelGGL((quant_kernel<QBLK, false, true>), dim3(nqb, BH), dim3(256), 0, st, q,

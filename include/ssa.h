@@ -53,7 +53,7 @@ typedef struct ssa_shape {
     int64_t B, H, N, D;
 } ssa_shape;
 
-enum { SSA_OP_QUANT = 0, SSA_OP_MASK = 1, SSA_OP_ATTN = 2 };
+enum { SSA_OP_QUANT = 0, SSA_OP_MASK = 1, SSA_OP_ATTN = 2, SSA_OP_STEP = 3 };
 enum { SSA_BRANCH_SPARSE = 1, SSA_BRANCH_LINEAR = 2 };
 
 #define SSA_HEAD_DIM 128
@@ -69,8 +69,8 @@ int64_t ssa_num_k_blocks(int64_t N); /* ceil(N/64) */
 int64_t ssa_keep_blocks(int64_t N, double topk);
 
 /* Bytes of device workspace the entry point `op` needs for shape s (keep and
- * branches only matter for SSA_OP_ATTN; pass keep = Nkb for dense). Returns 0
- * for an invalid shape. */
+ * branches only matter for SSA_OP_ATTN and SSA_OP_STEP; pass keep = Nkb for
+ * dense). Returns 0 for an invalid shape. */
 size_t ssa_workspace_bytes(int op, ssa_shape s, int64_t keep, int branches);
 
 const char* ssa_status_str(ssa_status st);
@@ -156,6 +156,31 @@ ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
                              const int8_t* k_i8, const float* k_scale, const int32_t* kidx,
                              int64_t keep, int branches, float sm_scale, uint16_t* out,
                              float* out_f32, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sage_sla_fwd -- the whole SageSLA step in one call (page 5, Pillars One and
+ * Two, "SageSLA"): K smoothing and INT8 quantization, the block selection and
+ * the attention, with every result bit-identical to sage_quant_qk (with a
+ * pool), then sla_block_mask (from that pool), then sage_sla_attn_fwd on the
+ * same arguments. Enqueued as one pass, it reads raw K once less: the per-block
+ * K sums of the mean and the pooled key means come out of the pass that lays
+ * out V (and forms the linear states), which reads K anyway. K is still read
+ * twice in all, since K' = K - mu needs the finished mean.
+ *   q, k, v         in : bf16 [B,H,N,D]
+ *   keep, branches, sm_scale: as for sage_sla_attn_fwd
+ *   q_i8..k_mean    out: as sage_quant_qk writes them
+ *   kidx            out: int32 [B,H,Nqb,keep] as sla_block_mask writes it, or
+ *                        NULL = dense (keep must equal Nkb; no selection runs)
+ *   mask            out: uint8 [B,H,Nqb,Nkb] or NULL (needs kidx)
+ *   out, out_f32    out: as for sage_sla_attn_fwd
+ *   ws: ssa_workspace_bytes(SSA_OP_STEP, s, keep, branches) bytes, 256-byte
+ *       aligned; its contents on return are unspecified.
+ */
+ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, ssa_shape s,
+                        int64_t keep, int branches, float sm_scale, int8_t* q_i8, float* q_scale,
+                        int8_t* k_i8, float* k_scale, float* k_mean, int32_t* kidx,
+                        uint8_t* mask, uint16_t* out, float* out_f32, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* ---------------------------------------------------------------------------
  * sage_qk_int32_tiles -- test export of raw int32 score tiles computed by the

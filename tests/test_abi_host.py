@@ -59,6 +59,12 @@ def test_workspace_sizes():
     assert dense == sparse < lin  # all blocks kept: no linear states needed
     assert ssa.workspace_bytes(ssa.OP_ATTN, (1, 1, 100, 64), 1, 1) == 0  # D != 128
     assert ssa.workspace_bytes(7, s) == 0
+    # the one-call step holds the attention's workspace, the pooled means and
+    # the K-mean partials
+    for keep, br in ((1182, 3), (118, 1), (118, 3)):
+        step = ssa.workspace_bytes(ssa.OP_STEP, s, keep, br)
+        assert step >= (ssa.workspace_bytes(ssa.OP_ATTN, s, keep, br) + ssa.pool_bytes(s)
+                        + ssa.workspace_bytes(ssa.OP_QUANT, s))
 
 
 def _L():
@@ -154,6 +160,43 @@ def test_attn_rejects_bad_arguments():
     assert call(out=_p(2 * GB)) == 1  # out aliases v
     assert call() == 3  # workspace missing
     assert b"workspace" in L.ssa_last_error()
+
+
+def test_step_rejects_bad_arguments():
+    L = _L()
+    GB = 1 << 30
+    s = _shape(N=1000)  # 16 key blocks
+    names = ["q", "k", "v", "s", "keep", "branches", "sm", "q_i8", "q_scale", "k_i8", "k_scale",
+             "k_mean", "kidx", "mask", "out", "out32", "ws", "n", "st"]
+    ok = [_p(0), _p(GB), _p(2 * GB), s, 4, 3, 0.0, _p(3 * GB), _p(4 * GB), _p(5 * GB),
+          _p(6 * GB), _p(6 * GB + (1 << 20)), _p(7 * GB), None, _p(8 * GB), None, _p(9 * GB),
+          1 << 30, None]
+
+    def call(**kw):
+        args = list(ok)
+        for k_, v_ in kw.items():
+            args[names.index(k_)] = v_
+        return L.sage_sla_fwd(*args)
+
+    assert call(branches=0) == 1
+    assert call(branches=4) == 1
+    assert call(keep=0) == 1
+    assert call(keep=17) == 1
+    assert call(kidx=None) == 1  # dense needs keep == Nkb
+    assert call(kidx=None, keep=16, mask=_p(10 * GB)) == 1  # a mask needs the selection
+    assert b"mask" in L.ssa_last_error()
+    assert call(sm=float("inf")) == 1
+    assert call(q=None) == 1
+    assert call(v=_p(2 * GB + 8)) == 1  # misaligned
+    assert call(k_mean=None) == 1
+    assert call(s=_shape(N=1000, D=64)) == 2
+    assert call(out=_p(2 * GB)) == 1  # out aliases v
+    assert call(kidx=_p(5 * GB + 64)) == 1  # kidx overlaps k_i8
+    assert call(mask=_p(9 * GB)) == 1  # mask inside the workspace
+    assert b"overlap" in L.ssa_last_error()
+    assert call(ws=None) == 3
+    assert call(n=1 << 10) == 3
+    assert call(ws=_p(9 * GB + 16)) == 3  # workspace misaligned
 
 
 def test_tiles_reject_bad_count():

@@ -1,5 +1,6 @@
 """GPU parity at the full workload sizes, in the launch configuration the bench
-times (SageSLAPlan: quant -> mask -> attention on one stream).
+times (SageSLAPlan.run: the one-call step on one stream), and the staged calls
+against it.
 
 Integer outputs are compared whole where the oracle is cheap (quantized
 tensors, scales, K mean) and on samples otherwise (block-mask rows, int32
@@ -68,3 +69,12 @@ def test_workload_parity(orc, name):
         flips = int((ref["amb"] > 0).sum())
         say(f"    bh={bh} rows={len(toks)} rel-L2={rel:.2e} max={mx:.2e} "
             f"vs-exact={rel_ex:.2e} rows-with-flip-bound={flips}")
+
+    # the staged calls write the same buffers bit for bit
+    say(f"[full] {name}: staged calls against the one-call step")
+    names = ("q_i8", "k_i8", "q_scale", "k_scale", "k_mean", "kidx", "out", "out32")
+    ref = {n: getattr(plan, n).clone() for n in names if getattr(plan, n) is not None}
+    plan.run_staged()
+    torch.cuda.synchronize()
+    for n, want in ref.items():
+        assert torch.equal(getattr(plan, n).view(torch.uint8), want.view(torch.uint8)), n
