@@ -122,14 +122,20 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
             *(u16x8*)(vt + ((bh * nkb + j) * HD + dv) * KBLK + 8 * pc) =
                 u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
         }
-        // K sums: waves 4 and 5 (the z products weigh on waves 0-3) add the
-        // column of channel d = tid - 256 in token order, 16 tokens at a time;
-        // with the states, each piece sits after one step of MFMAs so that
-        // the dependent adds run while the matrix core works
+        // K sums: thread tid adds the column of channel d = tid % 128 in token
+        // order, 16 tokens at a time, and waves 4 and 5 store the result. With
+        // the states every wave runs the adds, one piece after each step of
+        // MFMAs: that measured 40 us faster at 40 x 75600 tokens than adds in
+        // waves 4 and 5 only, whose per-lane branch kept the scheduler from
+        // overlapping them with the MFMAs.
         const bool sumw = SUMS && tid >= 256 && tid < 256 + HD;
-        const int dsum = tid - 256;
+        const int dsum = tid & (HD - 1);
         const int valid = min(KBLK, N - j * KBLK);
         float ksum = 0.f;
+        // The full-block / ragged-block choice is uniform; its branch also
+        // keeps each piece of adds between its group of MFMAs and the next
+        // (without it the compiler moves all 64 adds behind the last MFMA,
+        // measured 60 us slower at 40 x 75600 tokens).
         auto sum16 = [&](int uc) {
             uint16_t r[16];
 #pragma unroll
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
                     acc[t] = mfma_bf16_32x32x16(ah, b, acc[t]);
                     acc[t] = mfma_bf16_32x32x16(al, b, acc[t]);
                 }
-                if (SUMS && sumw) sum16(uc);
+                if (SUMS) sum16(uc);
             }
             // z_j[d] for rows d = 32eg + ...: the same product against ones
             if (dh == 0) {
