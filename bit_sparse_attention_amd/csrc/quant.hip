@@ -77,23 +77,41 @@ void colsum_kernel(const uint16_t* __restrict__ x, int N, int nb, int ld, float*
 }
 
 // mu[bh][d] = (sum over key blocks j in order of part[bh][j][d]) / N.
-__global__ __launch_bounds__(128) void kmean_final_kernel(const float* __restrict__ part, int nkb,
-                                                           int N, float* __restrict__ mu) {
-    const int d = threadIdx.x;
+// One workgroup per (head, 32 channels). The partials arrive in chunks of
+// KM_CHUNK key blocks, loaded by all threads into LDS (many loads in flight),
+// then one thread per channel adds its column of the chunk in block order.
+// The sum starts at +0.0 and only existing blocks are added.
+constexpr int KM_CH = 32;      // channels per workgroup
+constexpr int KM_CHUNK = 256;  // key blocks per LDS chunk
+__global__ __launch_bounds__(256) void kmean_final_kernel(const float* __restrict__ part, int nkb,
+                                                          int N, float* __restrict__ mu) {
+    __shared__ float st[KM_CHUNK][KM_CH + 1];
+    const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x;
-    const float* p = part + bh * nkb * HD + d;
-    // loads in batches of 64 so they are in flight together; the adds stay in
-    // block order (only existing blocks are added: a -0.0 total keeps its sign)
+    const int d0 = blockIdx.y * KM_CH;
+    const float* p = part + bh * nkb * HD + d0;
     float tot = 0.f;
-    for (int j0 = 0; j0 < nkb; j0 += 64) {
-        float v[64];
+    for (int j0 = 0; j0 < nkb; j0 += KM_CHUNK) {
+        const int nj = min(KM_CHUNK, nkb - j0);
+        // 8 float4 per thread: row r = idx / 8, channels 4 * (idx % 8) .. + 3
 #pragma unroll
-        for (int u = 0; u < 64; ++u) v[u] = j0 + u < nkb ? p[(int64_t)(j0 + u) * HD] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 64; ++u)
-            if (j0 + u < nkb) tot += v[u];
+        for (int k = 0; k < KM_CHUNK * KM_CH / 4 / 256; ++k) {
+            const int idx = tid + 256 * k;
+            const int r = idx >> 3, c4 = (idx & 7) * 4;
+            if (r < nj) {
+                const f32x4 v = *(const f32x4*)(p + (int64_t)(j0 + r) * HD + c4);
+                st[r][c4] = v[0];
+                st[r][c4 + 1] = v[1];
+                st[r][c4 + 2] = v[2];
+                st[r][c4 + 3] = v[3];
+            }
+        }
+        __syncthreads();
+        if (tid < KM_CH)
+            for (int r = 0; r < nj; ++r) tot += st[r][tid];
+        __syncthreads();
     }
-    mu[bh * HD + d] = tot / (float)N;
+    if (tid < KM_CH) mu[bh * HD + d0 + tid] = tot / (float)N;
 }
 
 // Per-block INT8 quantization of one (head, block): scale = amax/127 over the
@@ -211,7 +229,8 @@ hipError_t launch_quant_from_sums(const uint16_t* q, const uint16_t* k, int64_t 
                                   float* k_mean, const float* ws_part, float* qbar,
                                   hipStream_t st) {
     const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
-    hipLaunchKernelGGL(kmean_final_kernel, dim3(BH), dim3(128), 0, st, ws_part, nkb, N, k_mean);
+    hipLaunchKernelGGL(kmean_final_kernel, dim3(BH, HD / KM_CH), dim3(256), 0, st, ws_part, nkb, N,
+                       k_mean);
     if (qbar)
         hipLaunchKernelGGL((quant_kernel<QBLK, false, true>), dim3(nqb, BH), dim3(256), 0, st, q,
                            nullptr, N, nqb, q_i8, q_scale, qbar);
