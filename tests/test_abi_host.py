@@ -23,7 +23,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("sage_quant_qk", "sla_block_mask", "sage_sla_attn_fwd", "sage_qk_int32_tiles",
+    for n in ("sage_quant_qk", "sla_block_mask", "sage_sla_attn_fwd", "sage_sla_fwd",
+              "sage_qk_int32_tiles", "w8a8_quant", "w8a8_gemm",
               "ssa_workspace_bytes", "ssa_keep_blocks", "ssa_status_str", "ssa_last_error",
               "ssa_num_q_blocks", "ssa_num_k_blocks"):
         assert n in names, n
