@@ -253,9 +253,10 @@ def sage_qk_int32_tiles(q_i8, k_i8, tiles):
 def sage_sla_fwd(q, k, v, topk: float | None = 0.1, linear: bool = True, sm_scale: float = 0.0,
                  return_f32: bool = False, return_mask: bool = False, return_all: bool = False):
     """The whole step in one library call (quantize, select unless topk is
-    None, attend), bit-identical to the three staged calls. return_all adds a
-    dict of the intermediates (q_i8, q_scale, k_i8, k_scale, k_mean, kidx and,
-    with return_mask, mask)."""
+    None, attend), bit-identical to the three staged calls. Returns out, then
+    out32 if return_f32, then the u8 block mask if return_mask (None when
+    dense), then, if return_all, a dict of the intermediates (q_i8, q_scale,
+    k_i8, k_scale, k_mean, kidx)."""
     s = _qkv_shape(q, k, v)
     B, H, N, D = q.shape
     dev = q.device
@@ -280,12 +281,11 @@ def sage_sla_fwd(q, k, v, topk: float | None = 0.1, linear: bool = True, sm_scal
         _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(k_mean), _ptr(kidx), _ptr(mask),
         _ptr(out), _ptr(out32), _ptr(ws), n, _stream(dev)))
     res = (out, out32) if return_f32 else (out,)
+    if return_mask:
+        res = res + (mask,)
     if return_all:
-        inter = dict(q_i8=q_i8, q_scale=q_scale, k_i8=k_i8, k_scale=k_scale, k_mean=k_mean,
-                     kidx=kidx)
-        if return_mask:
-            inter["mask"] = mask
-        res = res + (inter,)
+        res = res + (dict(q_i8=q_i8, q_scale=q_scale, k_i8=k_i8, k_scale=k_scale, k_mean=k_mean,
+                          kidx=kidx),)
     return res if len(res) > 1 else res[0]
 
 

@@ -49,10 +49,10 @@ def test_step_equals_staged_calls(B, H, N, topk, linear):
     say(f"[step] B{B}H{H}N{N} topk={topk} branches={branches}")
     want_mask = topk is not None
     ref = _staged(qd, kd, vd, topk, branches, want_mask)
-    out, out32, got = ssa.sage_sla_fwd(qd, kd, vd, topk, linear=linear, return_f32=True,
-                                       return_mask=want_mask, return_all=True)
+    out, out32, mask, got = ssa.sage_sla_fwd(qd, kd, vd, topk, linear=linear, return_f32=True,
+                                             return_mask=True, return_all=True)
     torch.cuda.synchronize()
-    got = dict(got, out=out, out32=out32)
+    got = dict(got, out=out, out32=out32, mask=mask)
     for name, want in ref.items():
         if want is None:
             assert got.get(name) is None, name
