@@ -96,3 +96,27 @@ def test_w8a8_fullsize_sampled(orc):
     got = y32[torch.from_numpy(rows).to(DEV)].cpu().numpy()
     assert np.array_equal(got.view(np.uint32), oy.view(np.uint32))
     say(f"[w8a8 full] {len(rows)} sampled rows bit-exact")
+
+
+def test_w8a8_beyond_32bit_offsets(orc):
+    """The most rows the library takes (2^20) at K = 2304, so x holds more than
+    2^31 elements and its offsets need 64 bits: the quantization whole and
+    rows at both ends of the product bit-exact."""
+    M, N, K = 1 << 20, 256, 2304
+    assert M * K > 2**31
+    say(f"[w8a8 max] generating {M}x{K}, {N} outputs")
+    x, w = make_linear(M, N, K, seed=5, outliers=True)
+    xq, sx, oxq, osx = _check_quant(orc, x, "x max")
+    wq, sw, owq, osw = _check_quant(orc, w, "w max")
+    say("[w8a8 max] quantization bit-exact; GEMM")
+    y, y32 = ssa.w8a8_gemm(xq, sx, wq, sw, return_f32=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 2), np.arange(M - 130, M - 126),
+                                     np.arange(M - 4, M),
+                                     np.random.default_rng(1).integers(0, M, 8)]))
+    oy = orc.w8a8_gemm(oxq, osx, owq, osw, rows=rows)
+    got = y32[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), oy.view(np.uint32))
+    want16 = torch.from_numpy(got).to(torch.bfloat16)
+    assert torch.equal(y[torch.from_numpy(rows).to(DEV)].cpu(), want16)
+    say(f"[w8a8 max] {len(rows)} sampled rows bit-exact")
