@@ -441,6 +441,10 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
             qk_tile_mfma(ks[0], qop, l32, hi, s);
             tile_softmax(s, c0, min(KBLK, N - j0 * KBLK), hi, m_run, l_run, o, pb);
         }
+        // Step 0 refills ring stage 0 (K(3)) with its first DMA: every wave
+        // must be done reading K(0) there first. Later steps reuse a stage only
+        // after the barrier that ends the step which read it.
+        __syncthreads();
 
         // Step jj (ring stage R = jj % NSTAGE, a compile-time constant so every
         // LDS address is an immediate offset): resident K(jj+1), V(jj); in
