@@ -40,6 +40,7 @@ def lib():
             "orc_bf16_to_f32": (C.c_float, [C.c_uint16]),
             "orc_f32_to_bf16": (C.c_uint16, [C.c_float]),
             "orc_round_bf16": (C.c_double, [C.c_double]),
+            "orc_p_ambiguous": (C.c_double, [C.c_double, C.c_double, C.c_double, C.c_double]),
             "orc_k_mean": (None, [_p, _i64, _i64, _i64, _p]),
             "orc_quant": (None, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, C.c_int]),
             "orc_qk_tile": (None, [_p, _p, _i64, _i64, _i64, _i64, _i64, _p]),
@@ -69,7 +70,17 @@ def _ptr(a):
 
 
 def threads() -> int:
-    return max(1, os.cpu_count() or 1)
+    """Worker threads: the CPUs this process may run on (its affinity set,
+    which a batch job's CPU share restricts), capped by OMP_NUM_THREADS when
+    that is set."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
 
 
 def nqb(N):
@@ -86,6 +97,15 @@ def keep_blocks(N, topk):
 
 def round_bf16(x: float) -> float:
     return float(lib().orc_round_bf16(float(x)))
+
+
+def p_ambiguous(p, xa, xabs_max, m) -> float:
+    """bf16 ulp at p if a GPU may round p = 2^(x - m) the other way (the flip
+    window of the declared numerics), else 0."""
+    return float(lib().orc_p_ambiguous(float(p), float(xa), float(xabs_max), float(m)))
+
+
+NORM_LAG = 64.0  # the normalizer lag the flip window allows (oracle.h ORC_NORM_LAG)
 
 
 def f32_to_bf16_bits(x: float) -> int:

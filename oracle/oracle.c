@@ -288,6 +288,27 @@ void orc_topk(const float* score, int64_t R, int64_t Nkb, int64_t keep, int32_t*
 /* visits the blocks (rescaling by powers of two is exact), and the row sum  */
 /* uses the same rounded p_u the PV product sees.                            */
 
+/* Which rounded p may legitimately differ on a GPU (reading C12). A GPU      */
+/* forms the exponent as one fp32 fma, y = S*c - m', against a running       */
+/* integer normalizer m' that may lag the row's m = ceil(max x) by up to     */
+/* ORC_NORM_LAG (it raises m' only when a tile's max exceeds it by more than */
+/* that), so |y| <= |x| + |m| + ORC_NORM_LAG and the fp32 rounding of y moves */
+/* 2^y by at most 2^-24 |y| ln 2 relative; its hardware 2^y adds about one   */
+/* fp32 ulp. Both bf16 roundings of p are accepted when 2^(x - m) lies       */
+/* within p (2^-20 + 2^-23 (|x| + max|x| + |m| + ORC_NORM_LAG + 2)) of a     */
+/* bf16 rounding midpoint, a window at least twice those errors. Returns the */
+/* bf16 ulp at p when p is ambiguous, else 0.                                */
+double orc_p_ambiguous(double p, double xa, double xabs_max, double m) {
+    if (!(p >= 0x1p-126)) return 0.0;
+    int ex;
+    frexp(p, &ex);
+    double ulp = ldexp(1.0, ex - 8);
+    double k = p / ulp;
+    double dist = fabs(k - floor(k) - 0.5) * ulp;
+    double win = p * (0x1p-20 + 0x1p-23 * (xa + xabs_max + fabs(m) + ORC_NORM_LAG + 2.0));
+    return dist <= win ? ulp : 0.0;
+}
+
 typedef struct {
     const int8_t* q_i8;
     const float* q_scale;
@@ -355,11 +376,6 @@ static void sparse_task(void* vctx, int64_t r) {
     if (c->o_decl)
         for (int64_t e = 0; e < D; ++e) c->o_decl[r * D + e] = acc[e] / l;
     if (c->amb) {
-        /* A GPU evaluates the exponent in fp32 (fma against a running integer
-         * normalizer) and 2^y with a hardware approximation. Both roundings of
-         * p are legitimate when 2^y lies within that evaluation error of a
-         * bf16 rounding midpoint. Error window, relative to p: 2^-20 for the
-         * exponential plus 2^-23 * (|x| + max|x| + 2) for the fp32 exponent. */
         double xabs_max = 0.0;
         for (int64_t a = 0; a < n; ++a) {
             double xa = fabs((double)((float)S[a] * C[a]));
@@ -367,16 +383,9 @@ static void sparse_task(void* vctx, int64_t r) {
         }
         double bound = 0.0;
         for (int64_t a = 0; a < n; ++a) {
-            double p = pe[a];
-            if (p < 0x1p-126) continue;
-            int ex;
-            frexp(p, &ex);
-            double ulp = ldexp(1.0, ex - 8);
-            double k = p / ulp;
-            double dist = fabs(k - floor(k) - 0.5) * ulp;
             double xa = fabs((double)((float)S[a] * C[a]));
-            double win = p * (0x1p-20 + 0x1p-23 * (xa + xabs_max + fabs((double)m) + 2.0));
-            if (dist <= win) {
+            double ulp = orc_p_ambiguous(pe[a], xa, xabs_max, (double)m);
+            if (ulp > 0.0) {
                 const uint16_t* vr = vh + U[a] * D;
                 double dv = 0.0;
                 for (int64_t e = 0; e < D; ++e) {
@@ -444,8 +453,9 @@ void orc_sparse_rows(const int8_t* q_i8, const float* q_scale, const int8_t* k_i
 }
 
 /* ------------------------------------------------------------------------ */
-/* Linear branch (page 5, Pillar Two: "a lightweight global linear attention */
-/* component" for the interactions the sparse part skips). Reading: feature  */
+/* Linear branch (page 5, "The Four Technical Pillars", Pillar Two: the      */
+/* interactions the sparse part skips are covered by a cheap linear         */
+/* attention over the whole sequence). Reading: feature                     */
 /* map phi = elu + 1, no softmax scale, no learned projection; for a query   */
 /* block the states are summed over exactly the key blocks it did not keep. */
 

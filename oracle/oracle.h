@@ -81,6 +81,17 @@ void orc_block_scores(const float* qbar, const float* kbar, int64_t Nkb, int64_t
 void orc_topk(const float* score, int64_t R, int64_t Nkb, int64_t keep,
               int32_t* kidx /*[R][keep]*/, uint8_t* mask /*[R][Nkb] or NULL*/);
 
+/* Normalizer lag a GPU may have (reading C12): the GPU keeps an integer     */
+/* normalizer that can sit up to this many log2 units below the row's       */
+/* ceil(max) while it still yields the same rounded p up to a power of two.  */
+#define ORC_NORM_LAG 64.0
+
+/* Flip window of one rounded p (reading C12): p = 2^(x - m) evaluated       */
+/* exactly, xa = |x|, xabs_max = max |x| of the row, m = ceil(max x). Returns */
+/* the bf16 ulp at p when a GPU's fp32 evaluation may round p the other way, */
+/* else 0. */
+double orc_p_ambiguous(double p, double xa, double xabs_max, double m);
+
 /* Sparse softmax branch for the listed tokens of head bh.
  * kidx_head: [Nqb][keep] ascending key blocks, or NULL for dense (keep == Nkb).
  * sm_scale <= 0 selects 1/sqrt(D).

@@ -464,6 +464,50 @@ def test_amb_flags_a_near_midpoint(orc):
     assert res["amb"][0] == 0
 
 
+def _bf16_round_array(x):
+    """RNE of float64 values in the normal range straight to bf16."""
+    _, e = np.frexp(x)
+    q = e - 8
+    return np.ldexp(np.rint(np.ldexp(x, -q)), q)
+
+
+@pytest.mark.parametrize("lag", [0, 16, 64])
+def test_flip_window_covers_a_lagging_normalizer(orc, lag):
+    # A GPU forms y = fma(S, c, -m') in fp32 against an integer normalizer m'
+    # that may sit up to 64 below the row's m = ceil(max), takes 2^y with about
+    # one fp32 ulp of error and rounds to bf16; scaling by 2^(m' - m) is exact.
+    # Emulated here exactly (S*c is exact in fp64, one rounding to fp32), on p
+    # placed within 2^-17 of bf16 midpoints: every p whose rounding differs
+    # from the oracle's must lie inside the oracle's flip window.
+    rng = np.random.default_rng(2)
+    n = 60000
+    b = 128 + rng.integers(0, 128, n)
+    tgt = np.log2((b + 0.5) / 256.0 * (1 + rng.uniform(-2**-17, 2**-17, n)))
+    c = 2.0**-21
+    x = np.rint(tgt / c) * c                  # x = S c, S an integer
+    m = 0.0
+    yg = (x - (m - lag)).astype(np.float32).astype(np.float64)
+    po = _bf16_round_array(np.exp2(x - m))
+    flips = 0
+    for sgn in (-1, 1):
+        pg = _bf16_round_array(np.exp2(yg) * (1 + sgn * 2**-23)) * 2.0**-lag
+        idx = np.nonzero(pg != po)[0]
+        flips += len(idx)
+        for a in idx:
+            pe = 2.0**(x[a] - m)
+            assert orc.p_ambiguous(pe, abs(x[a]), abs(x[a]), m) > 0, (lag, x[a])
+    assert flips > 0
+    if lag == 64:
+        # the window without the lag term is too narrow here: the pin bites
+        pe = np.exp2(x - m)
+        _, e = np.frexp(pe)
+        ulp = np.ldexp(1.0, e - 8)
+        dist = np.abs(pe / ulp - np.floor(pe / ulp) - 0.5) * ulp
+        narrow = dist <= pe * (2**-20 + 2**-23 * (2 * np.abs(x) + 2.0))
+        pg = _bf16_round_array(np.exp2(yg) * (1 - 2**-23)) * 2.0**-lag
+        assert np.any((pg != po) & ~narrow)
+
+
 # --------------------------------------------------------------------------
 # linear branch (page 5, Pillar Two: light global linear attention)
 
