@@ -8,7 +8,9 @@
 // z_j = sum_u phi(k_u). A query block needs the sums over the key blocks it did
 // NOT keep. They are formed as H_i = H_total - sum_{j kept} h_j: H_total in
 // fp32, the kept-block sum as a dense 0/1 x bf16 matrix-core GEMM, so the bf16
-// rounding of h_j only touches the kept ~10% of the blocks.
+// rounding of h_j only touches the kept ~10% of the blocks. When more than
+// half the blocks are kept the GEMM sums the non-kept ones directly instead,
+// H_i = sum_{j not kept} h_j, so the rounding always touches the smaller set.
 #include <type_traits>
 
 #include "../../include/ssa.h"
@@ -315,7 +317,7 @@ __device__ __forceinline__ u32x4 sel_entry(uint32_t e) {
 // and the second step of an unpaired last one, select nothing.
 constexpr int SEL_MAX_WORDS = SSA_MAX_N / KBLK / 32 + 2;
 __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ kidx, int keep,
-                                                   int nqb, int nkb, int nks,
+                                                   int nqb, int nkb, int nks, int complement,
                                                    uint32_t* __restrict__ msel) {
     __shared__ uint32_t bits[SEL_MAX_WORDS];
     const int64_t bh = blockIdx.y;
@@ -330,6 +332,15 @@ __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ k
         atomicOr(&bits[j >> 5], 1u << (j & 31));
     }
     __syncthreads();
+    if (complement) {
+        // the blocks below nkb that are not kept
+        for (int w = threadIdx.x; w < 2 * nkp; w += 256) {
+            const int lo = 32 * w;
+            const uint32_t valid = lo >= nkb ? 0u : (nkb - lo >= 32 ? ~0u : (1u << (nkb - lo)) - 1u);
+            bits[w] = ~bits[w] & valid;
+        }
+        __syncthreads();
+    }
     for (int kp = threadIdx.x; kp < nkp; kp += 256) {
         u32x4 o;
 #pragma unroll
@@ -347,6 +358,8 @@ __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ k
 
 // Complement GEMM, computed transposed:
 //   hnon[bh][i][n] = htot[bh][n] - sum_j hs[bh][j][n] * sel[bh][i][j]
+// or, with `complement` (the selection rows then mark the non-kept blocks),
+//   hnon[bh][i][n] = sum_j hs[bh][j][n] * sel[bh][i][j]
 // for query blocks i < nqb, state entries n < HS_ROW, key blocks j < nkbp.
 // C^T = Hs^T . Sel^T on 32x32x16 bf16 MFMAs with fp32 accumulation: the A
 // operand is a state fragment, the B operand a selection fragment from the
@@ -380,6 +393,10 @@ static_assert(CG_TK == 32, "selection dword per lane per 32 key blocks");
 static_assert(HS_ROW % CG_TN == 0, "state rows split into whole column tiles");
 static_assert(CG_WROWS == 160, "selection DMAs: two of 64 rows and one of 32 per wave");
 
+int64_t complement_tiles_per_head(int64_t nqb) {
+    return (int64_t)(HS_ROW / CG_TN) * ((nqb + CG_TM - 1) / CG_TM);
+}
+
 size_t msel_bytes(int64_t BH, int64_t nqb, int64_t nkbp) {
     const int64_t nkp = (nkbp / CG_TK + 1) / 2;
     return (size_t)BH * nkp * nqb * 16;
@@ -387,7 +404,7 @@ size_t msel_bytes(int64_t BH, int64_t nqb, int64_t nkbp) {
 
 __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     const uint32_t* __restrict__ msel, const uint16_t* __restrict__ hs,
-    const float* __restrict__ htot, int64_t BH, int nqb, int nkb, int nkbp,
+    const float* __restrict__ htot, int64_t BH, int nqb, int nkb, int nkbp, int complement,
     float* __restrict__ hnon) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[CG_STAGES * CG_STAGE + CG_LUT];
     uint8_t* lut = smem + CG_STAGES * CG_STAGE;
@@ -522,8 +539,8 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x16& a = acc[ib][nb];
-                *(f32x4*)(dst + 32 * nb + 8 * q) =
-                    ht[nb][q] - f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                const f32x4 sum = f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                *(f32x4*)(dst + 32 * nb + 8 * q) = complement ? sum : ht[nb][q] - sum;
             }
     }
 }
@@ -566,12 +583,14 @@ hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, 
                              int64_t BH, int N, uint32_t* msel, float* hnon, hipStream_t st) {
     const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
     const int nkbp = (nkb + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
+    // sum whichever of the kept and the non-kept sets is smaller
+    const int complement = 2 * keep > nkb ? 1 : 0;
     hipLaunchKernelGGL(msel_kernel, dim3(nqb, BH), dim3(256), 0, st, kidx, keep, nqb, nkb,
-                       nkbp / GEMM_KALIGN, msel);
-    const int64_t total = BH * (HS_ROW / CG_TN) * ((nqb + CG_TM - 1) / CG_TM);
+                       nkbp / GEMM_KALIGN, complement, msel);
+    const int64_t total = BH * complement_tiles_per_head(nqb);
     const int64_t grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel, hs, htot,
-                       BH, nqb, nkb, nkbp, hnon);
+                       BH, nqb, nkb, nkbp, complement, hnon);
     return hipGetLastError();
 }
 

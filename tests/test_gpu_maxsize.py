@@ -2,8 +2,9 @@
 that every bf16 tensor holds more than 2^31 elements, so every offset into Q,
 K, V, the quantized tensors, the outputs and the workspaces needs 64 bits.
 The last head (the largest offsets) is checked against the oracle: quantized
-tensors, scales and K mean whole; sampled block-mask rows, int32 tiles and
-attention rows. The staged calls must agree with the one-call step."""
+tensors, scales and K mean whole; the block-mask rows of every query block
+that holds a checked token (the reference uses the oracle's rows), int32 tiles
+and attention rows. The staged calls must agree with the one-call step."""
 import numpy as np
 import pytest
 import torch
@@ -38,11 +39,17 @@ def test_max_sequence_beyond_32bit_offsets(orc):
     assert np.array_equal(plan.k_i8[0, bh].cpu().numpy(), oki[0])
 
     nqb, nkb = plan.nqb, plan.nkb
+    toks = np.unique(np.concatenate([[0, 1, 127, N - 129, N - 2, N - 1],
+                                     np.random.default_rng(3).integers(0, N, 8)]))
+    # the selection of every query block that holds a checked token (and the
+    # middle ones), from the oracle; the GPU's rows must equal them
+    rows = np.unique(np.concatenate([toks // 128, [nqb // 2, nqb - 2]]))
     kidx = plan.kidx[0, bh].cpu().numpy()
-    rows = np.array([0, 1, nqb // 2, nqb - 2, nqb - 1])
     say(f"[max] oracle mask rows {rows.tolist()}")
-    okidx, _ = orc.block_mask_head(qh, kh, 0, plan.keep, rows)
-    assert np.array_equal(kidx[rows], okidx)
+    okrows, _ = orc.block_mask_head(qh, kh, 0, plan.keep, rows)
+    assert np.array_equal(kidx[rows], okrows)
+    okidx = np.zeros_like(kidx)
+    okidx[rows] = okrows
 
     say("[max] int32 tiles at the end of the head")
     trip = [(i, j) for i, j in ((nqb - 1, nkb - 1), (nqb - 1, 0), (0, nkb - 1), (nqb // 2, nkb // 3))]
@@ -51,10 +58,8 @@ def test_max_sequence_beyond_32bit_offsets(orc):
     for t, (i, j) in enumerate(trip):
         assert np.array_equal(out[t], orc.qk_tile(oqi, oki, 0, i, j)), (i, j)
 
-    toks = np.unique(np.concatenate([[0, 1, 127, N - 129, N - 2, N - 1],
-                                     np.random.default_rng(3).integers(0, N, 8)]))
     say(f"[max] oracle attention rows of head {bh}: {len(toks)} tokens")
-    ref = orc.sagesla_rows(qh, kh, vh, (oqi, oqs, oki, oks), 0, toks, kidx, branches=3)
+    ref = orc.sagesla_rows(qh, kh, vh, (oqi, oqs, oki, oks), 0, toks, okidx, branches=3)
     g32 = plan.out32[0, bh].cpu().numpy()[toks]
     g16 = plan.out[0, bh].float().cpu().numpy()[toks]
     rel, mx, _ = check_attn(g32, g16, ref, "max-size last head")

@@ -112,6 +112,22 @@ ATTN_PARAMS = [(B, H, N, topk, br) for (B, H, N, topk) in ATTN_CASES for br in (
                if topk is not None or br == 1]
 
 
+def _oracle_intermediates(orc, q_i8, q_scale, k_i8, k_scale, kidx, qb, kb, keep, label):
+    """The oracle's quantized tensors, scales and selection for the same
+    inputs, after asserting the GPU's equal them bit for bit: the attention
+    reference is then built from the oracle's values only."""
+    oqi, oqs, oki, oks, _ = orc.quant_qk(qb, kb)
+    assert np.array_equal(flat(q_i8), oqi), f"{label}: q_i8"
+    assert np.array_equal(flat(k_i8), oki), f"{label}: k_i8"
+    assert np.array_equal(flat(q_scale).view(np.uint32), oqs.view(np.uint32)), f"{label}: q_scale"
+    assert np.array_equal(flat(k_scale).view(np.uint32), oks.view(np.uint32)), f"{label}: k_scale"
+    okidx = None
+    if kidx is not None:
+        okidx, _ = orc.block_mask(qb, kb, keep)
+        assert np.array_equal(flat(kidx), okidx), f"{label}: kidx"
+    return (oqi, oqs, oki, oks), okidx
+
+
 @pytest.mark.parametrize("B,H,N,topk,branches", ATTN_PARAMS)
 def test_attn_parity(orc, B, H, N, topk, branches):
     q, k, v = make_qkv(B, H, N, 128, seed=7 * N + branches)
@@ -128,14 +144,13 @@ def test_attn_parity(orc, B, H, N, topk, branches):
                                        branches, 0.0, return_f32=True)
     torch.cuda.synchronize()
     qb, kb, vb = bits(q), bits(k), bits(v)
-    quant = tuple(x.cpu().numpy().reshape((B * H,) + x.shape[2:])
-                  for x in (q_i8, q_scale, k_i8, k_scale))
-    kidx_np = None if kidx is None else flat(kidx)
+    quant, okidx = _oracle_intermediates(orc, q_i8, q_scale, k_i8, k_scale, kidx, qb, kb, keep,
+                                         label)
     g32, g16 = flat(out32), flat(out.float())
     toks = np.arange(N)
     for bh in range(B * H):
         ref = orc.sagesla_rows(qb, kb, vb, quant, bh, toks,
-                               None if kidx_np is None else kidx_np[bh], branches=branches)
+                               None if okidx is None else okidx[bh], branches=branches)
         if branches == 2:
             ref = {"decl": ref["linear"], "exact": ref["linear"], "amb": np.zeros(N)}
             if keep == ssa.num_k_blocks(N):
@@ -143,6 +158,40 @@ def test_attn_parity(orc, B, H, N, topk, branches):
                 continue
         rel, mx, rel_ex = check_attn(g32[bh], g16[bh], ref, f"{label} bh={bh}")
         say(f"    bh={bh} rel-L2={rel:.2e} max={mx:.2e} rel-L2 vs exact={rel_ex:.2e}")
+
+
+@pytest.mark.parametrize("topk", [0.4, 0.6, 0.9, 0.97])
+def test_linear_branch_high_keep(orc, topk):
+    # The complement states subtract the kept blocks from the total while
+    # fewer than half are kept, and sum the non-kept blocks directly beyond
+    # that; either way only the smaller set carries bf16 rounding. Linear
+    # branch alone on every row, both branches on two rows per query block.
+    B, H, N = 1, 1, 32760
+    q, k, v = make_qkv(B, H, N, 128, seed=41)
+    qd, kd, vd = _gpu(q, k, v)
+    label = f"N{N} topk={topk}"
+    say(f"[linear-high-keep] {label}")
+    qq = ssa.sage_quant_qk(qd, kd)[:4]
+    keep = ssa.keep_blocks(N, topk)
+    kidx = ssa.sla_block_mask(qd, kd, keep)
+    lin32 = ssa.sage_sla_attn_fwd(qd, kd, vd, *qq, kidx, keep, ssa.LINEAR, return_f32=True)[1]
+    out, out32 = ssa.sage_sla_attn_fwd(qd, kd, vd, *qq, kidx, keep, 3, return_f32=True)
+    torch.cuda.synchronize()
+    qb, kb, vb = bits(q), bits(k), bits(v)
+    quant, okidx = _oracle_intermediates(orc, *qq, kidx, qb, kb, keep, label)
+    h, z = orc.linear_states(kb, vb, 0)
+    ol = orc.linear_rows(qb, h, z, 0, np.arange(N), okidx[0])
+    g = flat(lin32)[0]
+    rel = np.linalg.norm(g - ol) / np.linalg.norm(ol)
+    err = np.abs(g - ol).max()
+    say(f"    linear branch rel-L2={rel:.2e} max={err:.2e}")
+    assert rel <= 1e-3 and err <= 2e-3, (rel, err)
+    nqb = ssa.num_q_blocks(N)
+    toks = np.unique(np.concatenate([128 * np.arange(nqb),
+                                     np.minimum(128 * np.arange(nqb) + 77, N - 1)]))
+    ref = orc.sagesla_rows(qb, kb, vb, quant, 0, toks, okidx[0], branches=3)
+    rel3, mx3, _ = check_attn(flat(out32)[0][toks], flat(out.float())[0][toks], ref, label)
+    say(f"    both branches rows={len(toks)} rel-L2={rel3:.2e} max={mx3:.2e}")
 
 
 def test_dense_equals_all_blocks_kept():
@@ -184,9 +233,11 @@ def test_explicit_sm_scale(orc):
     keep = ssa.keep_blocks(N, 0.3)
     kidx = ssa.sla_block_mask(qd, kd, keep)
     out, out32 = ssa.sage_sla_attn_fwd(qd, kd, vd, *qq, kidx, keep, 3, 0.05, return_f32=True)
-    quant = tuple(x.cpu().numpy().reshape((1,) + x.shape[2:]) for x in qq)
-    ref = orc.sagesla_rows(bits(q), bits(k), bits(v), quant, 0, np.arange(N), flat(kidx)[0],
-                           branches=3, sm_scale=0.05)
+    torch.cuda.synchronize()
+    qb, kb = bits(q), bits(k)
+    quant, okidx = _oracle_intermediates(orc, *qq, kidx, qb, kb, keep, "sm_scale=0.05")
+    ref = orc.sagesla_rows(qb, kb, bits(v), quant, 0, np.arange(N), okidx[0], branches=3,
+                           sm_scale=0.05)
     check_attn(flat(out32)[0], flat(out.float())[0], ref, "sm_scale=0.05")
 
 
