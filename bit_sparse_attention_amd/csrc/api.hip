@@ -1,6 +1,8 @@
 // api.hip -- the C ABI (include/ssa.h): argument validation, workspace layout
 // and kernel launches. Validation runs before any HIP call, so every argument
-// error returns with nothing enqueued.
+// error (shapes whose launch grids the device cannot take included) returns
+// with nothing enqueued. A call that enqueues several kernels and then sees a
+// launch fail returns SSA_ERR_HIP with the earlier launches still enqueued.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -39,6 +41,11 @@ struct Dims {
     int64_t BH, N, nqb, nkb, nkbp, ngroups;
 };
 
+// Largest launch grids, in workgroups: a dispatch covers fewer than 2^32
+// work-items per dimension, and B*H rides on the grid's y dimension.
+constexpr int64_t MAX_GRID_Y = 65535;
+constexpr int64_t MAX_WG_256 = ((int64_t)1 << 24) - 1;  // 256-thread workgroups in x
+
 ssa_status check_shape(const ssa_shape& s, Dims* d) {
     if (s.B < 1 || s.H < 1 || s.N < 1 || s.D < 1)
         return fail(SSA_ERR_INVALID, "shape must be positive (B=%lld H=%lld N=%lld D=%lld)",
@@ -46,14 +53,24 @@ ssa_status check_shape(const ssa_shape& s, Dims* d) {
     if (s.D != SSA_HEAD_DIM) return fail(SSA_ERR_UNSUPPORTED, "head dim %lld != 128", (long long)s.D);
     if (s.N > SSA_MAX_N)
         return fail(SSA_ERR_UNSUPPORTED, "N=%lld exceeds %d", (long long)s.N, SSA_MAX_N);
-    if (s.B > (1 << 20) || s.H > (1 << 20) || s.B * s.H > (1 << 20))
-        return fail(SSA_ERR_UNSUPPORTED, "B*H too large");
+    if (s.B > MAX_GRID_Y || s.H > MAX_GRID_Y || s.B * s.H > MAX_GRID_Y)
+        return fail(SSA_ERR_UNSUPPORTED, "B*H=%lld exceeds %lld", (long long)(s.B * s.H),
+                    (long long)MAX_GRID_Y);
     d->BH = s.B * s.H;
     d->N = s.N;
     d->nqb = (s.N + QBLK - 1) / QBLK;
     d->nkb = (s.N + KBLK - 1) / KBLK;
     d->nkbp = (d->nkb + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
     d->ngroups = (d->nkb + LIN_GROUP - 1) / LIN_GROUP;
+    // the attention grid (one workgroup per head and query block) and the
+    // complement GEMM grid (every 64-entry state tile of every 640 query
+    // blocks of every head)
+    if (d->BH * d->nqb > MAX_WG_256)
+        return fail(SSA_ERR_UNSUPPORTED, "B*H*Nqb=%lld exceeds %lld (attention grid)",
+                    (long long)(d->BH * d->nqb), (long long)MAX_WG_256);
+    if (d->BH * complement_tiles_per_head(d->nqb) > MAX_WG_256)
+        return fail(SSA_ERR_UNSUPPORTED, "B*H=%lld too large for N=%lld (linear-branch grid)",
+                    (long long)d->BH, (long long)s.N);
     return SSA_OK;
 }
 
@@ -564,6 +581,9 @@ ssa_status w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const 
         K % 128)
         return fail(SSA_ERR_INVALID, "w8a8_gemm: M=%lld N=%lld K=%lld (N, K multiples of 128, "
                     "all in [1, 2^20])", (long long)M, (long long)N, (long long)K);
+    if (w8a8_gemm_workgroups(M, N) > ((int64_t)1 << 22) - 8)
+        return fail(SSA_ERR_UNSUPPORTED, "w8a8_gemm: M=%lld N=%lld give more workgroups than one "
+                    "launch takes", (long long)M, (long long)N);
     TRY(need_ptr(xq, 16, "xq"));
     TRY(need_ptr(wq, 16, "wq"));
     TRY(need_ptr(sx, 4, "sx"));

@@ -11,8 +11,11 @@
 //   S^T = K_j . Q^T        v_mfma_i32_32x32x32_i8, exact int32
 //   x = S * c_ij           c_ij = fl32(fl32(sq*sk) * fl32(sm*log2 e))
 //   m = integer normalizer (raised only when a tile's max exceeds it by more
-//       than HEADROOM); rescaling by 2^k is exact, so p = bf16(2^(S*c - m))
-//       and the final output do not depend on the tile order
+//       than HEADROOM); rescaling by 2^k is exact and bf16 rounding commutes
+//       with it, so p and the output do not depend on the tile order except
+//       through the fp32 rounding of the exponent S*c - m, which depends on
+//       the m in use: a p within that error of a bf16 rounding midpoint may
+//       round either way (the flip window its tests allow for)
 //   p = bf16(2^(S*c - m)), l += p (v_dot2 on packed pairs)
 //   O^T += V_j^T . P^T     v_mfma_f32_32x32x16_bf16, fp32 accumulation
 // S^T puts one query per lane column: row max and row sum stay in a lane
@@ -35,12 +38,9 @@
 
 namespace ssa {
 
-// Query groups (32 rows each) per wave: 1 -> 4 waves per query block, two
-// waves per SIMD; 2 -> 2 waves of 64 rows sharing every LDS fragment.
-#ifndef SSA_ATTN_GROUPS
-#define SSA_ATTN_GROUPS 1
-#endif
-constexpr int G = SSA_ATTN_GROUPS;
+// Query groups of 32 rows per wave: one, so a query block takes 4 waves and
+// two workgroups share a CU (two waves per SIMD).
+constexpr int G = 1;
 constexpr int WAVES = 4 / G;
 constexpr int ATTN_THREADS = 64 * WAVES;
 constexpr int NSTAGE = 3;            // LDS buffers per operand

@@ -35,12 +35,16 @@ hipError_t launch_vt_only(const uint16_t* k, const uint16_t* v, int64_t BH, int 
                           float* kpart, float* kbarT, int ldk, hipStream_t st);
 // bytes of the complement GEMM's selection rows (msel) for nkbp padded key blocks
 size_t msel_bytes(int64_t BH, int64_t nqb, int64_t nkbp);
+// workgroups of the complement GEMM per head (256 threads each)
+int64_t complement_tiles_per_head(int64_t nqb);
 hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, const float* htot,
                              int64_t BH, int N, uint32_t* msel, float* hnon, hipStream_t st);
 
 // w8a8.hip
 hipError_t launch_w8a8_quant(const uint16_t* x, int rows, int cols, int8_t* q, float* scale,
                              hipStream_t st);
+// workgroups (1024 threads each) of the product's launch
+int64_t w8a8_gemm_workgroups(int64_t M, int64_t N);
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                             const float* bias, int M, int N, int K, uint16_t* y, float* y32,
                             hipStream_t st);

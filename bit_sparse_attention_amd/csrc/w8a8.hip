@@ -251,11 +251,15 @@ hipError_t launch_w8a8_quant(const uint16_t* x, int rows, int cols, int8_t* q, f
     return hipGetLastError();
 }
 
+int64_t w8a8_gemm_workgroups(int64_t M, int64_t N) {
+    const int64_t total = ((M + WG_TM - 1) / WG_TM) * (N / WG_TN);
+    return (total + 7) / 8 * 8;
+}
+
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                             const float* bias, int M, int N, int K, uint16_t* y, float* y32,
                             hipStream_t st) {
-    const int64_t total = (int64_t)((M + WG_TM - 1) / WG_TM) * (N / WG_TN);
-    const int64_t grid = (total + 7) / 8 * 8;
+    const int64_t grid = w8a8_gemm_workgroups(M, N);
     hipLaunchKernelGGL(w8a8_gemm_kernel, dim3((unsigned)grid), dim3(WG_THREADS), 0, st, xq, sx, wq, sw,
                        bias, M, N, K, y, y32);
     return hipGetLastError();

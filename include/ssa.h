@@ -22,13 +22,19 @@
  *     (Nkb = ceil(N/64)); the last block of each may be partial.
  *   - Ownership: the caller owns every buffer, including the workspace whose
  *     size ssa_workspace_bytes() reports. The library never allocates device
- *     memory, keeps no per-call state and never synchronizes: every call only
- *     enqueues work on `stream` (a hipStream_t; NULL = the null stream).
+ *     memory and keeps no per-call state. Every compute call only enqueues
+ *     work on `stream` (a hipStream_t; NULL = the null stream) and returns
+ *     without synchronizing; the one call that waits on the device is the
+ *     benchmark hook ssa_kernel_timer_read, which waits for the events it reads.
  *   - Errors: argument problems are reported synchronously with nothing
- *     enqueued (SSA_ERR_INVALID / SSA_ERR_UNSUPPORTED / SSA_ERR_WORKSPACE). A
- *     failed HIP launch returns SSA_ERR_HIP. Device faults surface at the
- *     caller's next synchronization. ssa_last_error() gives a message for the
- *     last failing call on the calling thread. Nothing is printed.
+ *     enqueued (SSA_ERR_INVALID / SSA_ERR_UNSUPPORTED / SSA_ERR_WORKSPACE),
+ *     shapes whose launch grids the device cannot take included (B*H at most
+ *     65535, B*H*Nqb below 2^24, and B*H*258*ceil(Nqb/640) below 2^24 for
+ *     the linear branch's state GEMM). A failed HIP launch returns SSA_ERR_HIP; in
+ *     a call that enqueues several kernels the launches before the failing
+ *     one stay enqueued. Device faults surface at the caller's next
+ *     synchronization. ssa_last_error() gives a message for the last failing
+ *     call on the calling thread. Nothing is printed.
  *   - Outputs must not overlap inputs (checked).
  */
 #ifndef SSA_H
@@ -224,9 +230,9 @@ ssa_status w8a8_quant(const uint16_t* x, int64_t rows, int64_t cols, int8_t* q, 
  *   bias   in : fp32 [N], or NULL for none (16-byte aligned)
  *   y      out: bf16 [M][N] (round to nearest even of the fp32 result)
  *   y32    out: fp32 [M][N] copy before rounding, or NULL (16-byte aligned)
- * M, N, K <= 2^20; N and K multiples of 128. Errors as for the entry points
- * above (validation before anything is enqueued, SSA_ERR_HIP on a failed
- * launch).
+ * M, N, K <= 2^20; N and K multiples of 128; ceil(M/256) * N/128 below 2^22
+ * (the launch grid). Errors as for the entry points above (validation before
+ * anything is enqueued, SSA_ERR_HIP on a failed launch).
  */
 ssa_status w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                      const float* bias, int64_t M, int64_t N, int64_t K, uint16_t* y, float* y32,

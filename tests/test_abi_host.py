@@ -252,6 +252,41 @@ def test_w8a8_gemm_rejects_bad_arguments():
     assert b"overlap" in L.ssa_last_error()
 
 
+def test_shapes_beyond_the_launch_grids_are_rejected():
+    # B*H rides on the grid's y dimension (at most 65535); the attention grid
+    # has one 256-thread workgroup per head and query block (fewer than 2^24);
+    # both must fail in validation, before anything is enqueued
+    L = _L()
+    GB = 1 << 30
+    for shape, ok in (((1, 65000, 64), True), ((1, 65100, 64), False), ((1, 65536, 64), False),
+                      ((2, 40000, 64), False),
+                      ((1, 4095, 1 << 19), True), ((1, 4096, 1 << 19), False),
+                      ((64, 64, 1 << 19), False)):
+        s = _shape(*shape)
+        want_ws = L.ssa_workspace_bytes(ssa.OP_QUANT, s, 0, 0)
+        assert (want_ws > 0) == ok, shape
+        st = L.sage_quant_qk(_p(0), _p(16 * GB), s, _p(32 * GB), _p(48 * GB), _p(64 * GB),
+                             _p(80 * GB), _p(96 * GB), None, _p(112 * GB), 1 << 40, None)
+        if not ok:
+            assert st == 2, (shape, st)
+            assert b"exceeds" in L.ssa_last_error() or b"too large" in L.ssa_last_error()
+        st = L.sage_sla_attn_fwd(_p(0), _p(16 * GB), _p(32 * GB), s, _p(48 * GB), _p(64 * GB),
+                                 _p(80 * GB), _p(96 * GB), None, ssa.num_k_blocks(shape[2]),
+                                 ssa.SPARSE, 0.0, _p(112 * GB), None, _p(128 * GB), 0, None)
+        if not ok:
+            assert st == 2, (shape, st)
+
+
+def test_w8a8_gemm_rejects_a_grid_too_large():
+    # ceil(M/256) * N/128 workgroups of 1024 threads: at most 2^22 per launch
+    L = _L()
+    GB = 1 << 30
+    M = N = 1 << 20
+    st = L.w8a8_gemm(_p(0), _p(GB), _p(2 * GB), _p(3 * GB), None, M, N, 128, _p(4 * GB), None,
+                     None)
+    assert st == 2 and b"workgroups" in L.ssa_last_error()
+
+
 def test_status_strings():
     L = _L()
     for st in range(5):
