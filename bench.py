@@ -62,7 +62,7 @@ def cpu_baseline(q, k, v, w, keep, kidx_np):
     import oracle
     from bit_sparse_attention_amd.workloads import bf16_bits
 
-    nthreads = min(16, os.cpu_count() or 1)
+    nthreads = oracle.threads()
     N, H, B = w.N, w.H, w.B
     nqb, nkb = (N + 127) // 128, (N + 63) // 64
     heads = sorted({0, B * H - 1})
@@ -94,8 +94,8 @@ def cpu_baseline(q, k, v, w, keep, kidx_np):
         "kind": "oracle",
         "sample": (f"heads {heads} of {B * H} in full (quantization, block mask, linear states, "
                    f"sparse and linear attention rows of all {nqb} query blocks): {t_heads:.1f} s "
-                   f"on {nthreads} threads of {_cpu_model()}, extrapolated x{B * H / len(heads):g} "
-                   f"over heads to {t_full:.0f} s for the workload"),
+                   f"on {nthreads} threads (the job's CPU share) of {_cpu_model()}, extrapolated "
+                   f"x{B * H / len(heads):g} over heads to {t_full:.0f} s for the workload"),
     }
 
 
@@ -110,6 +110,39 @@ KERNEL_SOURCES = {
 }
 RECORD_PREFIX = {ATTN_KERNEL: "attn_kernel", W8_KERNEL: "w8a8_gemm"}
 COPY_KERNEL = "copyBuffer"
+TRAFFIC_UNIT = ("bytes past L2 per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled): "
+                "HBM and Infinity Cache (MALL) together")
+XCDS = 8
+
+
+def _md_value(path, pattern):
+    if not os.path.exists(path):
+        return None
+    m = re.search(pattern, open(path).read())
+    return float(m.group(1)) if m else None
+
+
+def mfma_bound(workload, ops, kern_ms):
+    """The attention kernel's matrix-core bound at the sustained clock.
+
+    The clock is GRBM_GUI_ACTIVE per XCD over the kernel's mean duration, both
+    from the committed records of the same workload (a counter run and a
+    kernel trace). The bound is the time the MFMAs alone take at that clock:
+    half the effective ops are INT8 (QK^T) at the INT8 rate, half bf16 (PV) at
+    half that rate."""
+    cpath = os.path.join(ROOT, "profiles", f"attn_kernel_counters_{workload}.md")
+    tpath = os.path.join(ROOT, "profiles", f"kernel_time_{workload}.md")
+    grbm = _md_value(cpath, r"sagesla_attn_kernel[^|]*\| GRBM_GUI_ACTIVE \| \d+ \| ([0-9.e+]+)")
+    t_us = _md_value(tpath, r"sagesla_attn_kernel[^|]*` \| \d+ \| ([0-9.]+)")
+    if grbm is None or t_us is None:
+        return None
+    ghz = grbm / XCDS / (t_us * 1e3)
+    scale = ghz / 2.4
+    ms = ((ops / 2) / (INT8_PEAK_TOPS * 1e12 * scale) + (ops / 2) / (INT8_PEAK_TOPS / 2 * 1e12 * scale)) * 1e3
+    return {"clock_ghz": round(ghz, 4), "ms": ms, "frac": ms / kern_ms if kern_ms else None,
+            "frac_of_int8_peak": ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+            "source": f"profiles/attn_kernel_counters_{workload}.md (GRBM_GUI_ACTIVE per XCD) over "
+                      f"profiles/kernel_time_{workload}.md (mean kernel time)"}
 
 
 def sources_sha256(kernel):
@@ -302,7 +335,7 @@ def bench_w8a8(args):
         "roofline": {"bound": "mfma", "achieved": g_tops, "peak": INT8_PEAK_TOPS,
                      "unit": "TOP/s", "frac": g_tops / INT8_PEAK_TOPS,
                      "traffic": traffic_from_record(wl.name, W8_KERNEL),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled)"},
+                     "traffic_unit": TRAFFIC_UNIT},
     }
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -310,7 +343,7 @@ def bench_w8a8(args):
         import oracle
         from bit_sparse_attention_amd.workloads import bf16_bits
 
-        nthreads = min(16, os.cpu_count() or 1)
+        nthreads = oracle.threads()
         xb = bf16_bits(x).reshape(wl.M, wl.K)
         wb = bf16_bits(wt).reshape(wl.N, wl.K)
         t0 = time.perf_counter()
@@ -325,7 +358,8 @@ def bench_w8a8(args):
         line["cpu_baseline"] = {
             "value": ops / t_full / 1e12, "unit": "TOPS", "cores": nthreads, "kind": "oracle",
             "sample": (f"quantization of x and w in full ({tq:.1f} s) and the product for "
-                       f"{len(rows)} of {wl.M} rows ({tg:.1f} s) on {nthreads} threads of "
+                       f"{len(rows)} of {wl.M} rows ({tg:.1f} s) on {nthreads} threads (the job's "
+                       f"CPU share) of "
                        f"{_cpu_model()}, extrapolated over the rows to {t_full:.0f} s"),
         }
     print(json.dumps(line), flush=True)
@@ -342,6 +376,9 @@ def main():
                     help="also time each staged ABI call on its own, and the staged step")
     ap.add_argument("--staged", action="store_true",
                     help="time the three staged calls instead of the one-call step")
+    ap.add_argument("--flush", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, time K more, each after overwriting a MIB-MiB "
+                         "buffer (evicts L2 and the Infinity Cache); reported as 'flushed'")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain MIB-MiB device copy (for counter scaling)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -405,6 +442,24 @@ def main():
     ms_step = (t1 - t0) * 1e3 / K
     print(f"# timed {K} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
 
+    flushed = None
+    if args.flush:
+        junk = torch.empty(args.flush << 20, dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        with ssa.KernelTimer(K) as ftimer:
+            for e0, e1 in ev:
+                junk.fill_(1)
+                e0.record()
+                plan.run()
+                e1.record()
+            torch.cuda.synchronize()
+            fk = ftimer.read()
+        fs = [a.elapsed_time(b) for a, b in ev]
+        flushed = {"flush_mib": args.flush, "ms_per_step": float(np.mean(fs)),
+                   "attn_kernel_ms": float(np.mean(fk)) if fk else None}
+        del junk
+
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
 
@@ -451,10 +506,15 @@ def main():
         "effective_ops": ops,
         "roofline": {"bound": "mfma", "achieved": k_tops, "peak": INT8_PEAK_TOPS,
                      "unit": "TOP/s", "frac": k_tops / INT8_PEAK_TOPS, "traffic": traffic_from_record(w.name),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled)"},
+                     "traffic_unit": TRAFFIC_UNIT},
     }
+    bound = mfma_bound(w.name, ops, k_ms)
+    if bound is not None:
+        line["mfma_bound"] = bound
     if stages is not None:
         line["stages_ms"] = stages
+    if flushed is not None:
+        line["flushed"] = flushed
     if not args.no_cpu_baseline:
         print("# timing the oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(q, k, v, w, plan.keep, kidx_np)
