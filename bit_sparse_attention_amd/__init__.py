@@ -72,6 +72,7 @@ def _load():
         "ssa_status_str": (C.c_char_p, [i32]),
         "ssa_last_error": (C.c_char_p, []),
         "sage_quant_qk": (i32, [_p, _p, Shape, _p, _p, _p, _p, _p, _p, _p, sz, _p]),
+        "sage_quant_qk_noalloc": (i32, [_p, _p, Shape, _p, _p, _p, _p, _p, _p, _p]),
         "sla_block_mask": (i32, [_p, _p, Shape, i64, _p, _p, _p, _p, sz, _p]),
         "ssa_pool_bytes": (sz, [Shape]),
         "w8a8_quant": (i32, [_p, i64, i64, _p, _p, _p]),

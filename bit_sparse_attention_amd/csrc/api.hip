@@ -19,6 +19,14 @@
 
 using namespace ssa;
 
+// Fixed device scratch of the allocation-free quantization call: the K-mean
+// block partials (B*H*Nkb*128 fp32) that sage_quant_qk keeps in the caller's
+// workspace. Every GPU the library runs on holds its own copy until the
+// process ends. Host code never uses this name as an address: the per-device
+// address comes from hipGetSymbolAddress (scratch_address below).
+constexpr size_t SCRATCH_BYTES = (size_t)32 << 20;  // 32 MiB: B*H*Nkb <= 65536
+static __device__ __align__(256) float scratch[SCRATCH_BYTES / sizeof(float)];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -125,6 +133,28 @@ ssa_status check_device() {
         g_dev_ok[dev].store(st, std::memory_order_release);
     }
     if (st != 1) return fail(SSA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return SSA_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64];
+
+ssa_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(SSA_ERR_UNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(SSA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
     return SSA_OK;
 }
 
@@ -353,6 +383,49 @@ ssa_status sage_quant_qk(const uint16_t* q, const uint16_t* k, ssa_shape s, int8
     hipError_t e = launch_quant_qk(q, k, d.BH, (int)d.N, q_i8, q_scale, k_i8, k_scale, k_mean,
                                    (float*)ws, qbar, kbarT, (int)pw.ldk, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sage_quant_qk launch");
+    return SSA_OK;
+}
+
+ssa_status sage_quant_qk_noalloc(const uint16_t* q, const uint16_t* k, ssa_shape s, int8_t* q_i8,
+                                 float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                                 void* pool, void* stream) {
+    g_err[0] = 0;
+    Dims d;
+    TRY(check_shape(s, &d));
+    const size_t need = ws_quant(d);
+    if (need > SCRATCH_BYTES)
+        return fail(SSA_ERR_UNSUPPORTED,
+                    "sage_quant_qk_noalloc: B*H*Nkb=%lld needs %zu bytes of scratch; the library "
+                    "holds %zu (B*H*Nkb <= 65536); use sage_quant_qk with a workspace",
+                    (long long)(d.BH * d.nkb), need, SCRATCH_BYTES);
+    TRY(need_ptr(q, 16, "q"));
+    TRY(need_ptr(k, 16, "k"));
+    TRY(need_ptr(q_i8, 16, "q_i8"));
+    TRY(need_ptr(k_i8, 16, "k_i8"));
+    TRY(need_ptr(q_scale, 4, "q_scale"));
+    TRY(need_ptr(k_scale, 4, "k_scale"));
+    TRY(need_ptr(k_mean, 4, "k_mean"));
+    const size_t nel = (size_t)d.BH * d.N * HD;
+    const Range ins[] = {{q, nel * 2, "q"}, {k, nel * 2, "k"}};
+    if (pool && !aligned(pool, 256)) return fail(SSA_ERR_INVALID, "pool is not 256-byte aligned");
+    const MaskWs pw = ws_mask(d);
+    const Range outs[] = {{q_i8, nel, "q_i8"},
+                          {k_i8, nel, "k_i8"},
+                          {q_scale, (size_t)d.BH * d.nqb * 4, "q_scale"},
+                          {k_scale, (size_t)d.BH * d.nkb * 4, "k_scale"},
+                          {k_mean, (size_t)d.BH * HD * 4, "k_mean"},
+                          {pool, pool ? pw.total : 0, "pool"}};
+    TRY(check_alias(outs, 6, ins, 2));
+    TRY(check_device());
+    void* part = nullptr;
+    TRY(scratch_address(&part));
+    float* qbar = pool ? (float*)((char*)pool + pw.qbar) : nullptr;
+    float* kbarT = pool ? (float*)((char*)pool + pw.kbarT) : nullptr;
+    // every block partial the mean reads is written first by the same call,
+    // so the scratch needs no clearing
+    hipError_t e = launch_quant_qk(q, k, d.BH, (int)d.N, q_i8, q_scale, k_i8, k_scale, k_mean,
+                                   (float*)part, qbar, kbarT, (int)pw.ldk, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sage_quant_qk_noalloc launch");
     return SSA_OK;
 }
 

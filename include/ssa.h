@@ -112,6 +112,24 @@ ssa_status sage_quant_qk(const uint16_t* q, const uint16_t* k, ssa_shape s, int8
 size_t ssa_pool_bytes(ssa_shape s);
 
 /* ---------------------------------------------------------------------------
+ * sage_quant_qk_noalloc -- sage_quant_qk for callers that cannot allocate
+ * device memory or hand over a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, results
+ * and errors as sage_quant_qk, bit for bit, without ws / ws_bytes: the K-mean
+ * block partials go to a fixed 32 MiB device array inside the library (one
+ * per GPU, held until the process ends). Limit: B*H*Nkb <= 65536 (e.g. 40
+ * heads of 75600 tokens); larger shapes return SSA_ERR_UNSUPPORTED with
+ * nothing enqueued. The call allocates nothing; its first call on a device
+ * looks up that device's array once. Every call on one GPU shares the array,
+ * and each call writes every entry it reads: calls on one GPU whose work
+ * overlaps in time (other streams, other threads) race and must be ordered
+ * by the caller.
+ */
+ssa_status sage_quant_qk_noalloc(const uint16_t* q, const uint16_t* k, ssa_shape s,
+                                 int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                                 float* k_mean, void* pool, void* stream);
+
+/* ---------------------------------------------------------------------------
  * sla_block_mask -- the SLA critical-block selection.
  * Page 5, Pillar Two (only the most important interactions are computed) and
  * "Hands-On Tutorial" (--sla_topk = fraction kept).
