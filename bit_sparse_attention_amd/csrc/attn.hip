@@ -38,10 +38,7 @@
 
 namespace ssa {
 
-// Query groups of 32 rows per wave: one, so a query block takes 4 waves and
-// two workgroups share a CU (two waves per SIMD).
-constexpr int G = 1;
-constexpr int WAVES = 4 / G;
+constexpr int WAVES = 4;               // 32 query rows each
 constexpr int ATTN_THREADS = 64 * WAVES;
 constexpr int NSTAGE = 3;            // LDS buffers per operand
 constexpr int KTILE = KBLK * HD;     // bytes of an int8 K tile
@@ -129,34 +126,29 @@ __device__ __forceinline__ void load_q_operand(const int8_t* __restrict__ q_i8, 
     for (int c = 0; c < 4; ++c) qop[c] = ok ? *(const i32x4*)(qp + 32 * c + 16 * hi) : i32x4{};
 }
 
-// The shared QK^T routine: S^T of the LDS K tile against the wave's two
-// 32-query groups. Lane (l32, hi), register r of s[g][0] holds key
-// 8*(r/4) + 4*hi + r%4 for query l32 of group g (s[g][1]: that key + 32).
-__device__ __forceinline__ void qk_tile_mfma(const uint8_t* ks, const i32x4 (&qop)[G][4], int l32,
-                                             int hi, i32x16 (&s)[G][2]) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) s[g][0] = s[g][1] = i32x16{};
+// The shared QK^T routine: S^T of the LDS K tile against the wave's 32
+// queries. Lane (l32, hi), register r of s[0] holds key 8*(r/4) + 4*hi + r%4
+// for query l32 (s[1]: that key + 32).
+__device__ __forceinline__ void qk_tile_mfma(const uint8_t* ks, const i32x4 (&qop)[4], int l32,
+                                             int hi, i32x16 (&s)[2]) {
+    s[0] = s[1] = i32x16{};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int slot = ((2 * c + hi) ^ swz(l32)) * 16;
         const i32x4 a0 = *(const i32x4*)(ks + l32 * 128 + slot);
         const i32x4 a1 = *(const i32x4*)(ks + (32 + l32) * 128 + slot);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            s[g][0] = mfma_i8_32x32x32(a0, qop[g][c], s[g][0]);
-            s[g][1] = mfma_i8_32x32x32(a1, qop[g][c], s[g][1]);
-        }
+        s[0] = mfma_i8_32x32x32(a0, qop[c], s[0]);
+        s[1] = mfma_i8_32x32x32(a1, qop[c], s[1]);
     }
 }
 
-// Row max of one group's S^T tile (the lane pair holds a query's 64 keys).
-// In the ragged last key block the rows past N hold copies of row N-1, a key
-// of the same block, so the max over all 64 columns is the max over the valid
-// ones.
-__device__ __forceinline__ int tile_rowmax(const i32x16& s0, const i32x16& s1) {
-    int smax = max(s0[0], s1[0]);
+// Row max of an S^T tile (the lane pair holds a query's 64 keys). In the
+// ragged last key block the rows past N hold copies of row N-1, a key of the
+// same block, so the max over all 64 columns is the max over the valid ones.
+__device__ __forceinline__ int tile_rowmax(const i32x16 (&s)[2]) {
+    int smax = max(s[0][0], s[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) smax = max(smax, max(s0[r], s1[r]));
+    for (int r = 1; r < 16; ++r) smax = max(smax, max(s[0][r], s[1][r]));
     return max(smax, __shfl_xor(smax, 32, 64));
 }
 
@@ -167,27 +159,27 @@ __device__ __forceinline__ void add_pair(bf16x2 pr, float& acc) {
     acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
 }
 
-// p = bf16(2^(S*c - m)) for one group's tile, packed as the PV B operand
-// (chunk cc holds keys 16cc + 8*(s/4) + 4*hi + s%4); returns the sum of the
-// rounded p.
-__device__ __forceinline__ float tile_p(const i32x16& s0, const i32x16& s1, float c, float nm,
-                                        bf16x8 (&pb)[4]) {
+// One slice of the softmax of a tile: keys 2p and 2p+1 of this lane's 32
+// (convert, scale, exp2, round the pair to bf16, add the pair to the sum),
+// written into the PV B operand (chunk cc holds keys 16cc + 8*(s/4) + 4*hi
+// + s%4).
+__device__ __forceinline__ void softmax_slice(int p, const i32x16 (&s)[2], float c, float nm,
+                                              bf16x8 (&pn)[4], float& acc) {
+    const int cc = p >> 2, e = 2 * (p & 3), r = 8 * (cc & 1) + e;
+    const int sa = s[cc >> 1][r], sb = s[cc >> 1][r + 1];
+    const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sa, c, nm));
+    const float pz = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sb, c, nm));
+    const bf16x2 pr = __builtin_convertvector(f32x2{pa, pz}, bf16x2);
+    add_pair(pr, acc);
+    pn[cc][e] = pr[0];
+    pn[cc][e + 1] = pr[1];
+}
+
+// p = bf16(2^(S*c + nm)) of a whole tile; returns the sum of the rounded p.
+__device__ __forceinline__ float tile_p(const i32x16 (&s)[2], float c, float nm, bf16x8 (&pb)[4]) {
     float acc = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-        for (int s = 0; s < 8; s += 2) {
-            const int r = 8 * (cc & 1) + s;
-            const int sa = (cc < 2) ? s0[r] : s1[r];
-            const int sb = (cc < 2) ? s0[r + 1] : s1[r + 1];
-            const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sa, c, nm));
-            const float pz = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sb, c, nm));
-            const bf16x2 pr = __builtin_convertvector(f32x2{pa, pz}, bf16x2);
-            add_pair(pr, acc);
-            pb[cc][s] = pr[0];
-            pb[cc][s + 1] = pr[1];
-        }
-    }
+    for (int p = 0; p < 16; ++p) softmax_slice(p, s, c, nm, pb, acc);
     return acc;
 }
 
@@ -207,7 +199,7 @@ __device__ __forceinline__ float mask_p(int kval, int hi, bf16x8 (&pb)[4]) {
     return acc;
 }
 
-// Softmax of a fresh S tile for every group, in two parts. The fast part
+// Softmax of a tile, in two parts. The fast part (softmax_slice / tile_p)
 // computes P with the current normalizer and its sum. The tile's row max is
 // not needed there: if some query's max exceeds the normalizer by more than
 // HEADROOM, one of its p is >= 2^HEADROOM, so the lane holding it sees a sum
@@ -217,141 +209,92 @@ __device__ __forceinline__ float mask_p(int kval, int hi, bf16x8 (&pb)[4]) {
 // past N of the ragged last key block (kval < 64).
 constexpr float RESCALE_TRIGGER = 0x1p63f;  // 2^(HEADROOM - 1)
 
-__device__ __forceinline__ bool softmax_fast(const i32x16 (&s)[G][2], float c,
-                                             const float (&m_run)[G], bf16x8 (&pb)[G][4],
-                                             float (&lsum)[G]) {
-    bool trig = false;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        lsum[g] = tile_p(s[g][0], s[g][1], c, -m_run[g], pb[g]);
-        trig = trig || !(lsum[g] <= RESCALE_TRIGGER);
-    }
-    return trig;
-}
-
-__device__ __forceinline__ void softmax_rare(bool trig, const i32x16 (&s)[G][2], float c, int kval,
-                                             int hi, float (&m_run)[G], float (&l_run)[G],
-                                             f32x16 (&o)[G][4], bf16x8 (&pb)[G][4],
-                                             float (&lsum)[G]) {
+__device__ __forceinline__ void softmax_rare(bool trig, const i32x16 (&s)[2], float c, int kval,
+                                             int hi, float& m_run, float& l_run, f32x16 (&o)[4],
+                                             bf16x8 (&pb)[4], float& lsum) {
     if (__builtin_amdgcn_ballot_w64(trig)) {
+        const float mt = ceilf((float)tile_rowmax(s) * c);  // c > 0
+        const bool need = mt > m_run + HEADROOM;
+        const float alpha =
+            need ? ((m_run == -INFINITY) ? 0.f : __builtin_amdgcn_ldexpf(1.0f, (int)(m_run - mt)))
+                 : 1.0f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mt = ceilf((float)tile_rowmax(s[g][0], s[g][1]) * c);  // c > 0
-            const bool need = mt > m_run[g] + HEADROOM;
-            const float alpha =
-                need ? ((m_run[g] == -INFINITY)
-                            ? 0.f
-                            : __builtin_amdgcn_ldexpf(1.0f, (int)(m_run[g] - mt)))
-                     : 1.0f;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[g][dt] *= alpha;
-            l_run[g] *= alpha;
-            m_run[g] = need ? mt : m_run[g];
-            lsum[g] = tile_p(s[g][0], s[g][1], c, -m_run[g], pb[g]);
-        }
+        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+        l_run *= alpha;
+        m_run = need ? mt : m_run;
+        lsum = tile_p(s, c, -m_run, pb);
     }
-    if (kval < KBLK) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) lsum[g] = mask_p(kval, hi, pb[g]);
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) l_run[g] += lsum[g];
+    if (kval < KBLK) lsum = mask_p(kval, hi, pb);
+    l_run += lsum;
 }
 
-__device__ __forceinline__ void tile_softmax(const i32x16 (&s)[G][2], float c, int kval, int hi,
-                                             float (&m_run)[G], float (&l_run)[G],
-                                             f32x16 (&o)[G][4], bf16x8 (&pb)[G][4]) {
-    float lsum[G];
-    const bool trig = softmax_fast(s, c, m_run, pb, lsum);
-    softmax_rare(trig, s, c, kval, hi, m_run, l_run, o, pb, lsum);
-}
-
-// O^T += V^T . P^T for both groups; each V fragment feeds two MFMAs.
-__device__ __forceinline__ void tile_pv(const uint8_t* vs, const bf16x8 (&pb)[G][4], int l32,
-                                        int hi, f32x16 (&o)[G][4]) {
+// O^T += V^T . P^T for one tile.
+__device__ __forceinline__ void tile_pv(const uint8_t* vs, const bf16x8 (&pb)[4], int l32, int hi,
+                                        f32x16 (&o)[4]) {
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
             const bf16x8 va =
                 *(const bf16x8*)(vs + (32 * dt + l32) * 128 + ((2 * cc + hi) ^ swz(l32)) * 16);
-#pragma unroll
-            for (int g = 0; g < G; ++g) o[g][dt] = mfma_bf16_32x32x16(va, pb[g][cc], o[g][dt]);
+            o[dt] = mfma_bf16_32x32x16(va, pb[cc], o[dt]);
         }
 }
 
-// One pipeline step, written in issue order with scheduling fences between
-// the pieces: the 8 K fragment reads; QK(next) MFMAs, alternating between the
-// two independent 32-key accumulators, each followed by one V fragment read;
-// PV(current) MFMAs, the first 8 each followed by the next V read (a fragment
-// is read ~8 MFMAs before use) and, from the third on, each followed by one
-// slice of the fresh tile's softmax (2 keys: convert, scale, exp2, round to
-// bf16, sum), which runs on the VALU while the MFMA executes.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-__device__ __forceinline__ void softmax_slice(int p, const i32x16 (&s)[2], float c, float nm,
-                                              bf16x8 (&pn)[4], float& acc) {
-    const int cc = p >> 2, e = 2 * (p & 3), r = 8 * (cc & 1) + e;
-    const int sa = s[cc >> 1][r], sb = s[cc >> 1][r + 1];
-    const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sa, c, nm));
-    const float pz = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sb, c, nm));
-    const bf16x2 pr = __builtin_convertvector(f32x2{pa, pz}, bf16x2);
-    add_pair(pr, acc);
-    pn[cc][e] = pr[0];
-    pn[cc][e + 1] = pr[1];
-}
-
+// One step of the three-tile pipeline, written in issue order with
+// scheduling fences between the pieces. For kept blocks j, j+1, j+2:
+//   PV(j)   16 bf16 MFMAs with P(j) (pb) and the LDS V^T tile vs;
+//   QK(j+2)  8 int8 MFMAs against the LDS K tile ks, into sn (only with QK);
+//   softmax(j+1) of sc, already in registers, into pn: 16 slices of 2 keys.
+// The MFMAs run as QK, PV, PV, QK, PV, PV, ... so the VALU slices (one after
+// each PV) sit beside every kind of MFMA, and each LDS fragment is read three
+// MFMAs before its use. The softmax of a tile never waits for its own QK.
+template <bool QK>
 __device__ __forceinline__ void pipeline_step(const uint8_t* ks, const uint8_t* vs,
-                                              const i32x4 (&qop)[G][4], int l32, int hi,
-                                              const bf16x8 (&pb)[G][4], f32x16 (&o)[G][4], float c,
-                                              const float (&nm)[G], i32x16 (&s)[G][2],
-                                              bf16x8 (&pn)[G][4], float (&lsum)[G]) {
+                                              const i32x4 (&qop)[4], int l32, int hi,
+                                              const bf16x8 (&pb)[4], f32x16 (&o)[4],
+                                              const i32x16 (&sc)[2], float c, float nm,
+                                              i32x16 (&sn)[2], bf16x8 (&pn)[4], float& lsum) {
+    constexpr int NT = QK ? 24 : 16;  // MFMAs in the step
+    constexpr int AHEAD = 3;          // fragment read distance, in MFMAs
     const int sl = swz(l32);
-    auto vread = [&](int i) {  // fragment i = 4*cc + dt of V^T
-        const int cc = i >> 2, dt = i & 3;
-        return *(const bf16x8*)(vs + (32 * dt + l32) * 128 + ((2 * cc + hi) ^ sl) * 16);
-    };
+    // MFMA t: with QK, t = 3g is QK(g) (K fragment g = 2*c4 + h), t = 3g+1,
+    // 3g+2 are PV(2g), PV(2g+1); without, t is PV(t). PV i uses the V^T
+    // fragment i = 4*cc + dt.
+    auto is_qk = [](int t) { return QK && (t % 3 == 0); };
+    auto pv_of = [](int t) { return QK ? 2 * (t / 3) + (t % 3) - 1 : t; };
     i32x4 ka[8];
     bf16x8 va[16];
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-        const int slot = ((2 * c4 + hi) ^ sl) * 16;
-        ka[2 * c4] = *(const i32x4*)(ks + l32 * 128 + slot);
-        ka[2 * c4 + 1] = *(const i32x4*)(ks + (32 + l32) * 128 + slot);
-    }
-    fence();
-#pragma unroll
-    for (int g = 0; g < G; ++g) s[g][0] = s[g][1] = i32x16{};
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) s[g][h] = mfma_i8_32x32x32(ka[2 * c4 + h], qop[g][c4], s[g][h]);
-            va[2 * c4 + h] = vread(2 * c4 + h);
-            fence();
+    auto fetch = [&](int t) {
+        if (is_qk(t)) {
+            const int g = t / 3, c4 = g >> 1, h = g & 1;
+            ka[g] = *(const i32x4*)(ks + (32 * h + l32) * 128 + ((2 * c4 + hi) ^ sl) * 16);
+        } else {
+            const int i = pv_of(t), cc = i >> 2, dt = i & 3;
+            va[i] = *(const bf16x8*)(vs + (32 * dt + l32) * 128 + ((2 * cc + hi) ^ sl) * 16);
         }
-    }
-    float acc[G];
+    };
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+    for (int t = 0; t < AHEAD; ++t) fetch(t);
+    fence();
+    if (QK) sn[0] = sn[1] = i32x16{};
+    float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) o[g][i & 3] = mfma_bf16_32x32x16(va[i], pb[g][i >> 2], o[g][i & 3]);
-        if (i < 8) va[i + 8] = vread(i + 8);
-        if (i >= 2) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) softmax_slice(i - 2, s[g], c, nm[g], pn[g], acc[g]);
+    for (int t = 0; t < NT; ++t) {
+        if (t + AHEAD < NT) fetch(t + AHEAD);
+        if (is_qk(t)) {
+            const int g = t / 3, c4 = g >> 1, h = g & 1;
+            sn[h] = mfma_i8_32x32x32(ka[g], qop[c4], sn[h]);
+        } else {
+            const int i = pv_of(t);
+            o[i & 3] = mfma_bf16_32x32x16(va[i], pb[i >> 2], o[i & 3]);
+            softmax_slice(i, sc, c, nm, pn, acc);
         }
         fence();
     }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        softmax_slice(14, s[g], c, nm[g], pn[g], acc[g]);
-        softmax_slice(15, s[g], c, nm[g], pn[g], acc[g]);
-        lsum[g] = acc[g];
-    }
+    lsum = acc;
 }
 
 // Complement state staged in LDS for the linear epilogue: row r (0..127: h^T
@@ -365,34 +308,25 @@ __device__ __forceinline__ f32x4 hstage_read(const uint8_t* smem, int row, int p
     return *(const f32x4*)(smem + row * 512 + ((unit ^ (row & 31)) * 16));
 }
 
+// One query block i of head bh. smem holds the K and V rings; after the main
+// loop the same bytes hold the block's complement state for the linear
+// epilogue.
+constexpr int ATTN_LDS = NSTAGE * (KTILE + VTILE);
+static_assert(ATTN_LDS >= HSTAGE_BYTES, "state staging fits the rings");
+
 template <bool LIN>
-__global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnArgs a) {
-    // K and V rings; after the main loop the same bytes hold this query
-    // block's complement state for the linear epilogue
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * (KTILE + VTILE)];
-    static_assert(NSTAGE * (KTILE + VTILE) >= HSTAGE_BYTES, "state staging fits the rings");
+__device__ __forceinline__ void attn_block(const AttnArgs& a, uint8_t* smem, int64_t bh, int i) {
     uint8_t(*ks)[KTILE] = reinterpret_cast<uint8_t(*)[KTILE]>(smem);
     uint8_t(*vs)[VTILE] = reinterpret_cast<uint8_t(*)[VTILE]>(smem + NSTAGE * KTILE);
-    const int64_t total = a.BH * a.nqb;
-    const int64_t item = blockIdx.x;
-    if (item >= total) return;
-    const int64_t bh = item / a.nqb;
-    const int i = (int)(item % a.nqb);
     const int N = a.N, nkb = a.nkb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
               hi = lane >> 5;
-    int tq[G];  // this lane's query token in each group
-#pragma unroll
-    for (int g = 0; g < G; ++g) tq[g] = i * QBLK + 32 * G * wave + 32 * g + l32;
+    const int tq = i * QBLK + 32 * wave + l32;  // this lane's query token
 
-    f32x16 o[G][4];
+    f32x16 o[4];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[g][dt] = f32x16{};
-    float m_run[G], l_run[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) m_run[g] = -INFINITY, l_run[g] = 0.f;
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
 
     if (a.do_sparse) {
         const float sq = a.q_scale[bh * a.nqb + i];
@@ -403,6 +337,7 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
         // kept block indices are clamped into [0, nkb): a malformed kidx can
         // give wrong values but never an access outside K or V
         auto blk = [&](int jj) { return krow ? min(max(krow[jj], 0), nkb - 1) : jj; };
+        auto kval_of = [&](int j) { return min(KBLK, N - j * KBLK); };
         uint32_t koff[8 / WAVES], krag[8 / WAVES], voff[16 / WAVES];
         const int nlast = N - (nkb - 1) * KBLK;  // valid keys of the last key block
 #pragma unroll
@@ -418,106 +353,115 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
         auto vdma = [&](int j, int stage) {
             dma_v_tile(vtb + (int64_t)j * HD * KBLK, lds_u32(vs[stage]), wave, voff);
         };
+        constexpr int KD = 8 / WAVES, VD = 16 / WAVES;  // DMAs per wave per tile
 
-        // prologue: K(0), V(0), K(1) resident; K(2), V(1) in flight
+        // Prologue: K(0), V(0), K(1), K(2) resident; P(0) and S(1) in
+        // registers; V(1) and K(3) in flight. jn1..jn4 hold kept blocks 1..4,
+        // ksc1 the k_scale of block 1.
         const int j0 = blk(0);
-        int jn1 = nsel > 1 ? blk(1) : 0, jn2 = nsel > 2 ? blk(2) : 0, jn3 = nsel > 3 ? blk(3) : 0;
+        int jn1 = nsel > 1 ? blk(1) : 0, jn2 = nsel > 2 ? blk(2) : 0, jn3 = nsel > 3 ? blk(3) : 0,
+            jn4 = nsel > 4 ? blk(4) : 0;
         float ksc1 = ksc[jn1];
         kdma(j0, 0);
         vdma(j0, 0);
         if (nsel > 1) kdma(jn1, 1);
-        i32x4 qop[G][4];
-#pragma unroll
-        for (int g = 0; g < G; ++g) load_q_operand(a.q_i8, bh, N, tq[g], hi, qop[g]);
+        if (nsel > 2) kdma(jn2, 2);
+        i32x4 qop[4];
+        load_q_operand(a.q_i8, bh, N, tq, hi, qop);
         const float c0 = (sq * ksc[j0]) * a.K32;
         wait_vm<0>();
         __syncthreads();
-        if (nsel > 2) kdma(jn2, 2);
         if (nsel > 1) vdma(jn1, 1);
 
-        bf16x8 pb[G][4];
+        bf16x8 pb[4];
+        i32x16 sc[2];
         {
-            i32x16 s[G][2];
-            qk_tile_mfma(ks[0], qop, l32, hi, s);
-            tile_softmax(s, c0, min(KBLK, N - j0 * KBLK), hi, m_run, l_run, o, pb);
+            i32x16 s0[2];
+            qk_tile_mfma(ks[0], qop, l32, hi, s0);
+            float lsum = tile_p(s0, c0, -m_run, pb);
+            softmax_rare(!(lsum <= RESCALE_TRIGGER), s0, c0, kval_of(j0), hi, m_run, l_run, o, pb,
+                         lsum);
         }
-        // Step 0 refills ring stage 0 (K(3)) with its first DMA: every wave
-        // must be done reading K(0) there first. Later steps reuse a stage only
-        // after the barrier that ends the step which read it.
+        if (nsel > 1) qk_tile_mfma(ks[1], qop, l32, hi, sc);
+        // K(3) refills stage 0: every wave must be done reading K(0) and K(1)
+        // first (step 0 refills stage 1). Later steps reuse a stage only after
+        // the barrier that ends the step which read it.
         __syncthreads();
+        if (nsel > 3) kdma(jn3, 0);
 
-        // Step jj (ring stage R = jj % NSTAGE, a compile-time constant so every
-        // LDS address is an immediate offset): resident K(jj+1), V(jj); in
-        // flight K(jj+2), V(jj+1); pb = P(jj); jn1..jn3 = kept blocks jj+1..jj+3
-        // and ksc1 = the k_scale of jn1.
+        // Full step jj (ring stage R = jj % NSTAGE, a compile-time constant so
+        // every LDS address is an immediate offset), for jj + 2 < nsel:
+        // resident K(jj+2), V(jj); in flight K(jj+3), V(jj+1); registers
+        // P(jj) (pb) and S(jj+1) (sc). Issues K(jj+4), V(jj+2).
         auto step = [&](int jj, auto stage) {
             constexpr int R = decltype(stage)::value;
-            if (jj + 3 < nsel) kdma(jn3, R);
-            if (jj + 2 < nsel) vdma(jn2, (R + 2) % NSTAGE);
-            const float c = (sq * ksc1) * a.K32;
-            // QK(jj+1) and PV(jj) on the matrix cores, the softmax of tile jj+1
-            // on the VALU between the PV MFMAs
-            i32x16 s[G][2];
-            bf16x8 pn[G][4];
-            float lsum[G];
-            float nm[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) nm[g] = -m_run[g];
-            pipeline_step(ks[(R + 1) % NSTAGE], vs[R], qop, l32, hi, pb, o, c, nm, s, pn, lsum);
-            bool trig = false;
-#pragma unroll
-            for (int g = 0; g < G; ++g) trig = trig || !(lsum[g] <= RESCALE_TRIGGER);
+            const bool k4 = jj + 4 < nsel;
+            if (k4) kdma(jn4, (R + 1) % NSTAGE);
+            vdma(jn2, (R + 2) % NSTAGE);
+            const float c = (sq * ksc1) * a.K32;  // of tile jj+1
+            i32x16 sn[2];
+            bf16x8 pn[4];
+            float lsum;
+            pipeline_step<true>(ks[(R + 2) % NSTAGE], vs[R], qop, l32, hi, pb, o, sc, c, -m_run,
+                                sn, pn, lsum);
+            const bool trig = !(lsum <= RESCALE_TRIGGER);
             // keep the common-case P in this block, above the rare branch
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-                asm volatile("" ::"v"(pn[g][0]), "v"(pn[g][1]), "v"(pn[g][2]), "v"(pn[g][3]),
-                             "v"(lsum[g]));
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) pb[g][cc] = pn[g][cc];
-            softmax_rare(trig, s, c, min(KBLK, N - jn1 * KBLK), hi, m_run, l_run, o, pb, lsum);
-            // next kept block (jj+4) and the scale of jn2 via the scalar cache
+            asm volatile("" ::"v"(pn[0]), "v"(pn[1]), "v"(pn[2]), "v"(pn[3]), "v"(lsum));
+            softmax_rare(trig, sc, c, kval_of(jn1), hi, m_run, l_run, o, pn, lsum);
+            // next kept block (jj+5) and the scale of jn2 via the scalar cache
             int nxt = 0, kscb = 0;
-            const int32_t* kp = krow ? krow + min(jj + 4, nsel - 1) : (const int32_t*)ksc;
+            const int32_t* kp = krow ? krow + min(jj + 5, nsel - 1) : (const int32_t*)ksc;
             sload2(kp, ksc + jn2, nxt, kscb);
-            const int jn4 = krow ? min(max(nxt, 0), nkb - 1) : min(jj + 4, nkb - 1);
-            // K(jj+2) and V(jj+1) must land; this step's DMAs may stay in flight
-            constexpr int KD = 8 / WAVES, VD = 16 / WAVES;  // DMAs per wave per tile
-            if (jj + 3 < nsel)
+            // K(jj+3) and V(jj+1) must land; this step's DMAs may stay in flight
+            if (k4)
                 wait_vm<KD + VD>();
-            else if (jj + 2 < nsel)
-                wait_vm<VD>();
             else
-                wait_vm<0>();
+                wait_vm<VD>();
             __syncthreads();
             jn1 = jn2;
             jn2 = jn3;
             jn3 = jn4;
+            jn4 = krow ? min(max(nxt, 0), nkb - 1) : min(jj + 5, nkb - 1);
             ksc1 = __int_as_float(kscb);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) sc[h] = sn[h];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) pb[cc] = pn[cc];
         };
         using S0 = std::integral_constant<int, 0>;
         using S1 = std::integral_constant<int, 1>;
         using S2 = std::integral_constant<int, 2>;
         static_assert(NSTAGE == 3, "the step loop is unrolled by the ring depth");
-        const int steps = nsel - 1;
+        const int full = nsel - 2;  // full steps: jj = 0 .. nsel-3
         int jj = 0;
-        for (; jj + 3 <= steps; jj += 3) {
+        for (; jj + 3 <= full; jj += 3) {
             step(jj, S0{});
             step(jj + 1, S1{});
             step(jj + 2, S2{});
         }
-        if (jj < steps) step(jj++, S0{});
-        if (jj < steps) step(jj, S1{});
+        if (jj < full) step(jj++, S0{});
+        if (jj < full) step(jj++, S1{});
+        // Last two tiles: PV(nsel-2) with the softmax of tile nsel-1, then
+        // PV(nsel-1).
+        if (nsel > 1) {
+            const float c = (sq * ksc1) * a.K32;
+            i32x16 sn[2];
+            bf16x8 pn[4];
+            float lsum;
+            pipeline_step<false>(nullptr, vs[(nsel - 2) % NSTAGE], qop, l32, hi, pb, o, sc, c,
+                                 -m_run, sn, pn, lsum);
+            softmax_rare(!(lsum <= RESCALE_TRIGGER), sc, c, kval_of(jn1), hi, m_run, l_run, o, pn,
+                         lsum);
+            wait_vm<0>();
+            __syncthreads();
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) pb[cc] = pn[cc];
+        }
         tile_pv(vs[(nsel - 1) % NSTAGE], pb, l32, hi, o);
     }
 
-    float inv[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float lt = l_run[g] + __shfl_xor(l_run[g], 32, 64);
-        inv[g] = a.do_sparse ? 1.0f / lt : 0.f;
-    }
+    const float lt = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = a.do_sparse ? 1.0f / lt : 0.f;
     if (LIN) {
         // Stage Hnon_i (128 rows of h^T, then z: 129 rows of 512 bytes) in LDS
         // with one batch of DMAs. The 16-byte unit u of row r sits at unit
@@ -545,74 +489,78 @@ __global__ __launch_bounds__(ATTN_THREADS, 3 - G) void sagesla_attn_kernel(AttnA
         __syncthreads();
     }
 
+    const int t = tq;
+    f32x16 ol[4];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int t = tq[g];
-        f32x16 ol[4];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) ol[dt] = f32x16{};
-        float linv = 0.f;
-        if (LIN) {
-            const bool ok = t < N;
-            const uint16_t* qr = a.q + (bh * N + (ok ? t : 0)) * HD;
-            float den = 0.f;
+    for (int dt = 0; dt < 4; ++dt) ol[dt] = f32x16{};
+    float linv = 0.f;
+    if (LIN) {
+        const bool ok = t < N;
+        const uint16_t* qr = a.q + (bh * N + (ok ? t : 0)) * HD;
+        float den = 0.f;
 #pragma unroll 2
-            for (int cd = 0; cd < 8; ++cd) {
-                // k-slots of this lane: d = 16cd + 8(s/4) + 4hi + s%4, stored at
-                // positions d0 .. d0+7 of the state rows
-                const int d0 = 16 * cd + 8 * hi;
-                const u16x4 q0 = ok ? *(const u16x4*)(qr + 16 * cd + 4 * hi) : u16x4{};
-                const u16x4 q1 = ok ? *(const u16x4*)(qr + 16 * cd + 8 + 4 * hi) : u16x4{};
-                const u16x8 qv = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-                const f32x4 z0 = hstage_read(smem, HD, d0);
-                const f32x4 z1 = hstage_read(smem, HD, d0 + 4);
-                bf16x8 bqh, bql;
+        for (int cd = 0; cd < 8; ++cd) {
+            // k-slots of this lane: d = 16cd + 8(s/4) + 4hi + s%4, stored at
+            // positions d0 .. d0+7 of the state rows
+            const int d0 = 16 * cd + 8 * hi;
+            const u16x4 q0 = ok ? *(const u16x4*)(qr + 16 * cd + 4 * hi) : u16x4{};
+            const u16x4 q1 = ok ? *(const u16x4*)(qr + 16 * cd + 8 + 4 * hi) : u16x4{};
+            const u16x8 qv = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+            const f32x4 z0 = hstage_read(smem, HD, d0);
+            const f32x4 z1 = hstage_read(smem, HD, d0 + 4);
+            bf16x8 bqh, bql;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float f = bf2f(qv[e]);
-                    const float ph = f > 0.f ? f + 1.f : __expf(f);
-                    __bf16 x, y;
-                    split_bf16(ph, x, y);
-                    bqh[e] = x;
-                    bql[e] = y;
-                    den = __builtin_fmaf(ph, e < 4 ? z0[e] : z1[e - 4], den);
-                }
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    // two split units: high parts in dwords 0-1, rests in 2-3
-                    const u32x4 w0 = __builtin_bit_cast(u32x4, hstage_read(smem, 32 * dt + l32, d0));
-                    const u32x4 w1 = __builtin_bit_cast(u32x4, hstage_read(smem, 32 * dt + l32, d0 + 4));
-                    const bf16x8 ah = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
-                    const bf16x8 al = __builtin_bit_cast(bf16x8, u32x4{w0[2], w0[3], w1[2], w1[3]});
-                    ol[dt] = mfma_bf16_32x32x16(ah, bqh, ol[dt]);
-                    ol[dt] = mfma_bf16_32x32x16(ah, bql, ol[dt]);
-                    ol[dt] = mfma_bf16_32x32x16(al, bqh, ol[dt]);
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float f = bf2f(qv[e]);
+                const float ph = f > 0.f ? f + 1.f : __expf(f);
+                __bf16 x, y;
+                split_bf16(ph, x, y);
+                bqh[e] = x;
+                bql[e] = y;
+                den = __builtin_fmaf(ph, e < 4 ? z0[e] : z1[e - 4], den);
             }
-            den += __shfl_xor(den, 32, 64);
-            linv = 1.0f / den;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                // two split units: high parts in dwords 0-1, rests in 2-3
+                const u32x4 w0 = __builtin_bit_cast(u32x4, hstage_read(smem, 32 * dt + l32, d0));
+                const u32x4 w1 = __builtin_bit_cast(u32x4, hstage_read(smem, 32 * dt + l32, d0 + 4));
+                const bf16x8 ah = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+                const bf16x8 al = __builtin_bit_cast(bf16x8, u32x4{w0[2], w0[3], w1[2], w1[3]});
+                ol[dt] = mfma_bf16_32x32x16(ah, bqh, ol[dt]);
+                ol[dt] = mfma_bf16_32x32x16(ah, bql, ol[dt]);
+                ol[dt] = mfma_bf16_32x32x16(al, bqh, ol[dt]);
+            }
         }
-        if (t < N) {
-            uint16_t* orow = a.out + (bh * N + t) * HD;
-            float* orow32 = a.out32 ? a.out32 + (bh * N + t) * HD : nullptr;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int dv = 32 * dt + 8 * q4 + 4 * hi;
-                    float r4[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        float val = o[g][dt][4 * q4 + u] * inv[g];
-                        if (LIN) val += ol[dt][4 * q4 + u] * linv;
-                        r4[u] = val;
-                    }
-                    *(u16x4*)(orow + dv) =
-                        u16x4{f2bf(r4[0]), f2bf(r4[1]), f2bf(r4[2]), f2bf(r4[3])};
-                    if (orow32) *(f32x4*)(orow32 + dv) = f32x4{r4[0], r4[1], r4[2], r4[3]};
-                }
-        }
+        den += __shfl_xor(den, 32, 64);
+        linv = 1.0f / den;
     }
+    if (t < N) {
+        uint16_t* orow = a.out + (bh * N + t) * HD;
+        float* orow32 = a.out32 ? a.out32 + (bh * N + t) * HD : nullptr;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int dv = 32 * dt + 8 * q4 + 4 * hi;
+                float r4[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    float val = o[dt][4 * q4 + u] * inv;
+                    if (LIN) val += ol[dt][4 * q4 + u] * linv;
+                    r4[u] = val;
+                }
+                *(u16x4*)(orow + dv) = u16x4{f2bf(r4[0]), f2bf(r4[1]), f2bf(r4[2]), f2bf(r4[3])};
+                if (orow32) *(f32x4*)(orow32 + dv) = f32x4{r4[0], r4[1], r4[2], r4[3]};
+            }
+    }
+}
+
+template <bool LIN>
+__global__ __launch_bounds__(ATTN_THREADS, 2) void sagesla_attn_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[ATTN_LDS];
+    const int64_t item = blockIdx.x;
+    if (item >= a.BH * a.nqb) return;
+    attn_block<LIN>(a, smem, item / a.nqb, (int)(item % a.nqb));
 }
 
 // Raw int32 tiles through the same LDS staging and qk_tile_mfma routine as
@@ -644,23 +592,18 @@ __global__ __launch_bounds__(ATTN_THREADS) void qk_tiles_kernel(const int8_t* __
     dma_k_tile(k_i8, bh, N, j, lds_u32(ks), wave, koff, krag);
     wait_vm<0>();
     __syncthreads();
-    i32x4 qop[G][4];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-        load_q_operand(q_i8, bh, N, i * QBLK + 32 * G * wave + 32 * g + l32, hi, qop[g]);
-    i32x16 s[G][2];
+    i32x4 qop[4];
+    load_q_operand(q_i8, bh, N, i * QBLK + 32 * wave + l32, hi, qop);
+    i32x16 s[2];
     qk_tile_mfma(ks, qop, l32, hi, s);
     const int kval = min(KBLK, N - j * KBLK);
+    const int row = 32 * wave + l32;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int row = 32 * G * wave + 32 * g + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = mfma32_row(lane, r);
-            // keys past N were staged from row N-1; the export reports them as 0
-            ot[row * KBLK + key] = key < kval ? s[g][0][r] : 0;
-            ot[row * KBLK + key + 32] = key + 32 < kval ? s[g][1][r] : 0;
-        }
+    for (int r = 0; r < 16; ++r) {
+        const int key = mfma32_row(lane, r);
+        // keys past N were staged from row N-1; the export reports them as 0
+        ot[row * KBLK + key] = key < kval ? s[0][r] : 0;
+        ot[row * KBLK + key + 32] = key + 32 < kval ? s[1][r] : 0;
     }
 }
 
