@@ -54,6 +54,10 @@ def lib():
                                        C.c_int]),
             "orc_dense_rows": (None, [_p, _p, _p, _i64, _i64, _i64, C.c_float, _p, _i64, _p,
                                       C.c_int]),
+            "orc_sagesla_bwd": (None, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64,
+                                       C.c_int, C.c_float, _p, _p, _p, _p, C.c_int]),
+            "orc_sagesla_loss": (C.c_double, [_p, _p, _p, _p, _p, _i64, _i64, _p, _i64, C.c_int,
+                                              C.c_double, _p]),
             "orc_w8a8_quant": (None, [_p, _i64, _i64, _p, _p, C.c_int]),
             "orc_w8a8_gemm": (None, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, C.c_int]),
         }
@@ -298,6 +302,45 @@ def sagesla_rows(q, k, v, quantized, bh, tokens, kidx_head=None, branches=3, sm_
         res["exact"] = res["exact"] + ol
         res["linear"] = ol
     return res
+
+
+def sagesla_bwd(q, k, v, quantized, bh, dout, kidx_head=None, branches=3, sm_scale=0.0,
+                nthreads=None):
+    """fp64 (dq, dk, dv) [N, D] of head bh: the SageSLA backward with the
+    quantizer passed straight through and the selection held fixed.
+    q, k, v, dout: uint16 bf16 bits [BH, N, D]; quantized = (q_i8, q_scale,
+    k_i8, k_scale) as quant_qk returns them."""
+    q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
+    q_i8, q_scale, k_i8, k_scale = (np.ascontiguousarray(x) for x in quantized)
+    BH, N, D = q.shape
+    keep = 0
+    if kidx_head is not None:
+        kidx_head = np.ascontiguousarray(kidx_head, np.int32)
+        keep = kidx_head.shape[-1]
+    dq = np.empty((N, D))
+    dk = np.empty((N, D))
+    dv = np.empty((N, D))
+    lib().orc_sagesla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q_i8),
+                          _ptr(np.ascontiguousarray(q_scale, np.float32)), _ptr(k_i8),
+                          _ptr(np.ascontiguousarray(k_scale, np.float32)), N, D, bh,
+                          _ptr(kidx_head), keep, int(branches), float(sm_scale), _ptr(dout),
+                          _ptr(dq), _ptr(dk), _ptr(dv), nthreads or threads())
+    return dq, dk, dv
+
+
+def sagesla_loss(qh, kh, vv, ql, kl, dout, kidx_head=None, branches=3, sm=None):
+    """sum(dout * O) of the forward on continuous fp64 inputs [N, D] (one head)."""
+    arrs = [np.ascontiguousarray(x, np.float64) for x in (qh, kh, vv, ql, kl, dout)]
+    N, D = arrs[0].shape
+    keep = 0
+    if kidx_head is not None:
+        kidx_head = np.ascontiguousarray(kidx_head, np.int32)
+        keep = kidx_head.shape[-1]
+    if sm is None:
+        sm = float(np.float32(1.0 / np.sqrt(D)))
+    return float(lib().orc_sagesla_loss(_ptr(arrs[0]), _ptr(arrs[1]), _ptr(arrs[2]),
+                                        _ptr(arrs[3]), _ptr(arrs[4]), N, D, _ptr(kidx_head),
+                                        keep, int(branches), float(sm), _ptr(arrs[5])))
 
 
 # ---------------------------------------------------------------------------

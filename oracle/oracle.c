@@ -693,3 +693,362 @@ void orc_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const fl
     w8_gemm_ctx c = {xq, wq, sx, sw, bias, M, N, K, rows, y};
     orc_parallel_for(R, nthreads, w8_gemm_task, &c);
 }
+
+/* ------------------------------------------------------------------------ */
+/* SageSLA backward (page 5, "What is TurboDiffusion?" and the training      */
+/* guide: the sparse-linear attention is trainable and is fine-tuned). The   */
+/* pages do not say how gradients pass the 8-bit quantizer. Reading: the     */
+/* quantizer is a straight-through estimator (its derivative is taken as the */
+/* identity), the block selection is held fixed (it is piecewise constant),  */
+/* and the gradient is the exact derivative of the forward as a function of  */
+/* the dequantized operands qh = sq * q_i8, kh = sk * k_i8 (sparse branch)   */
+/* and of the raw bf16 Q, K (linear branch), evaluated at the forward's      */
+/* values; V enters both branches directly. dQ and dK collect both branches. */
+/* The K mean needs no term: moving every key of a row by the same vector    */
+/* moves every score of the row by the same amount, so the softmax ignores  */
+/* it (the rows of dS sum to zero).                                          */
+/* Everything is fp64. Sparse branch, with s = sm * qh . kh over the kept    */
+/* keys u of a query t, P = softmax(s), dP_tu = dO_t . v_u,                  */
+/* Dt = sum_u P_tu dP_tu, dS_tu = P_tu (dP_tu - Dt):                          */
+/*   dq_t += sm sum_u dS_tu kh_u, dk_u += sm sum_t dS_tu qh_t,               */
+/*   dv_u += sum_t P_tu dO_t.                                                */
+/* Linear branch, with a = phi(q_t), H, z the sums over the non-kept blocks, */
+/* den = a . z, o_l = a^T H / den, g = dO_t:                                 */
+/*   dnum = g / den, dden = -(g . o_l) / den,                                */
+/*   dq_t += (H dnum + z dden) * phi'(q_t),                                  */
+/*   G_i = sum_{t in i} a dnum^T, w_i = sum_{t in i} a dden,                 */
+/*   for a key u of block j, with Gc, wc the sums of G_i, w_i over the query */
+/*   blocks i that did NOT keep j:                                           */
+/*   dk_u += (Gc v_u + wc) * phi'(k_u), dv_u += Gc^T phi(k_u);               */
+/* phi'(x) = 1 for x > 0, e^x otherwise.                                     */
+
+static double dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+/* does query block i keep key block j (kidx_head NULL: dense, all kept) */
+static int kept_by(const int32_t* kidx, int64_t keep, int64_t i, int64_t j) {
+    if (!kidx) return 1;
+    for (int64_t a = 0; a < keep; ++a)
+        if (kidx[i * keep + a] == j) return 1;
+    return 0;
+}
+
+typedef struct {
+    const int8_t *q_i8, *k_i8;
+    const float *q_scale, *k_scale;
+    const uint16_t *v, *dout;
+    int64_t N, D, bh, nqb, nkb, keep;
+    const int32_t* kidx;
+    double sm;
+    double *rmax, *rsum, *rD; /* per query row */
+    double *dq, *dk, *dv;
+} sbwd_ctx;
+
+/* exact score s_tu (fp64) */
+static double sb_score(const sbwd_ctx* c, int64_t t, int64_t u) {
+    const int8_t* qr = c->q_i8 + (c->bh * c->N + t) * c->D;
+    const int8_t* kr = c->k_i8 + (c->bh * c->N + u) * c->D;
+    int64_t S = 0;
+    for (int64_t d = 0; d < c->D; ++d) S += (int64_t)qr[d] * (int64_t)kr[d];
+    return (double)S * (double)c->q_scale[c->bh * c->nqb + t / ORC_QBLK] *
+           (double)c->k_scale[c->bh * c->nkb + u / ORC_KBLK] * c->sm;
+}
+
+static double sb_dp(const sbwd_ctx* c, int64_t t, int64_t u) {
+    const uint16_t* gr = c->dout + (c->bh * c->N + t) * c->D;
+    const uint16_t* vr = c->v + (c->bh * c->N + u) * c->D;
+    double a = 0.0;
+    for (int64_t e = 0; e < c->D; ++e)
+        a += (double)orc_bf16_to_f32(gr[e]) * (double)orc_bf16_to_f32(vr[e]);
+    return a;
+}
+
+/* pass 1 (per query row t): softmax statistics, D_t and dq_t */
+static void sbwd_rows_task(void* vctx, int64_t t) {
+    sbwd_ctx* c = (sbwd_ctx*)vctx;
+    int64_t N = c->N, D = c->D, i = t / ORC_QBLK;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < c->nkb; ++j) {
+        if (!kept_by(c->kidx, c->keep, i, j)) continue;
+        int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
+        for (int64_t u = j * ORC_KBLK; u < u1; ++u) {
+            double s = sb_score(c, t, u);
+            if (s > m) m = s;
+        }
+    }
+    double l = 0.0, Dt = 0.0;
+    for (int64_t j = 0; j < c->nkb; ++j) {
+        if (!kept_by(c->kidx, c->keep, i, j)) continue;
+        int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
+        for (int64_t u = j * ORC_KBLK; u < u1; ++u) l += exp(sb_score(c, t, u) - m);
+    }
+    for (int64_t j = 0; j < c->nkb; ++j) {
+        if (!kept_by(c->kidx, c->keep, i, j)) continue;
+        int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
+        for (int64_t u = j * ORC_KBLK; u < u1; ++u)
+            Dt += exp(sb_score(c, t, u) - m) / l * sb_dp(c, t, u);
+    }
+    c->rmax[t] = m;
+    c->rsum[t] = l;
+    c->rD[t] = Dt;
+    double* dq = c->dq + t * D;
+    for (int64_t j = 0; j < c->nkb; ++j) {
+        if (!kept_by(c->kidx, c->keep, i, j)) continue;
+        double sk = (double)c->k_scale[c->bh * c->nkb + j];
+        int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
+        for (int64_t u = j * ORC_KBLK; u < u1; ++u) {
+            double P = exp(sb_score(c, t, u) - m) / l;
+            double dS = P * (sb_dp(c, t, u) - Dt);
+            const int8_t* kr = c->k_i8 + (c->bh * N + u) * D;
+            for (int64_t d = 0; d < D; ++d) dq[d] += c->sm * dS * sk * (double)kr[d];
+        }
+    }
+}
+
+/* pass 2 (per key u): dk_u and dv_u over the queries whose block kept u's */
+static void sbwd_keys_task(void* vctx, int64_t u) {
+    sbwd_ctx* c = (sbwd_ctx*)vctx;
+    int64_t N = c->N, D = c->D, j = u / ORC_KBLK;
+    double* dk = c->dk + u * D;
+    double* dv = c->dv + u * D;
+    for (int64_t i = 0; i < c->nqb; ++i) {
+        if (!kept_by(c->kidx, c->keep, i, j)) continue;
+        double sq = (double)c->q_scale[c->bh * c->nqb + i];
+        int64_t t1 = (i + 1) * ORC_QBLK < N ? (i + 1) * ORC_QBLK : N;
+        for (int64_t t = i * ORC_QBLK; t < t1; ++t) {
+            double P = exp(sb_score(c, t, u) - c->rmax[t]) / c->rsum[t];
+            double dS = P * (sb_dp(c, t, u) - c->rD[t]);
+            const int8_t* qr = c->q_i8 + (c->bh * N + t) * D;
+            const uint16_t* gr = c->dout + (c->bh * N + t) * D;
+            for (int64_t d = 0; d < D; ++d) {
+                dk[d] += c->sm * dS * sq * (double)qr[d];
+                dv[d] += P * (double)orc_bf16_to_f32(gr[d]);
+            }
+        }
+    }
+}
+
+typedef struct {
+    const uint16_t *q, *k, *v, *dout;
+    int64_t N, D, bh, nqb, nkb, keep;
+    const int32_t* kidx;
+    const double *h, *z; /* per key block states */
+    double *G, *w;       /* per query block [D][D], [D] */
+    double *dq, *dk, *dv;
+} lbwd_ctx;
+
+/* per query block i: dq (linear part), G_i, w_i */
+static void lbwd_q_task(void* vctx, int64_t i) {
+    lbwd_ctx* c = (lbwd_ctx*)vctx;
+    int64_t N = c->N, D = c->D;
+    double* H = (double*)calloc((size_t)(D * D), sizeof(double));
+    double* z = (double*)calloc((size_t)D, sizeof(double));
+    int64_t ncomp = 0;
+    for (int64_t j = 0; j < c->nkb; ++j) {
+        if (kept_by(c->kidx, c->keep, i, j)) continue;
+        ++ncomp;
+        for (int64_t x = 0; x < D * D; ++x) H[x] += c->h[j * D * D + x];
+        for (int64_t d = 0; d < D; ++d) z[d] += c->z[j * D + d];
+    }
+    double* G = c->G + i * D * D;
+    double* w = c->w + i * D;
+    memset(G, 0, sizeof(double) * (size_t)(D * D));
+    memset(w, 0, sizeof(double) * (size_t)D);
+    if (ncomp > 0) {
+        double* a = (double*)malloc(sizeof(double) * (size_t)D);
+        double* ol = (double*)malloc(sizeof(double) * (size_t)D);
+        double* dnum = (double*)malloc(sizeof(double) * (size_t)D);
+        int64_t t1 = (i + 1) * ORC_QBLK < N ? (i + 1) * ORC_QBLK : N;
+        for (int64_t t = i * ORC_QBLK; t < t1; ++t) {
+            const uint16_t* qr = c->q + (c->bh * N + t) * D;
+            const uint16_t* gr = c->dout + (c->bh * N + t) * D;
+            double den = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                a[d] = phi((double)orc_bf16_to_f32(qr[d]));
+                den += a[d] * z[d];
+            }
+            double go = 0.0;
+            for (int64_t e = 0; e < D; ++e) {
+                double num = 0.0;
+                for (int64_t d = 0; d < D; ++d) num += a[d] * H[d * D + e];
+                ol[e] = num / den;
+                go += (double)orc_bf16_to_f32(gr[e]) * ol[e];
+            }
+            double dden = -go / den;
+            for (int64_t e = 0; e < D; ++e) dnum[e] = (double)orc_bf16_to_f32(gr[e]) / den;
+            for (int64_t d = 0; d < D; ++d) {
+                double da = z[d] * dden;
+                for (int64_t e = 0; e < D; ++e) da += H[d * D + e] * dnum[e];
+                c->dq[t * D + d] += da * dphi((double)orc_bf16_to_f32(qr[d]));
+                for (int64_t e = 0; e < D; ++e) G[d * D + e] += a[d] * dnum[e];
+                w[d] += a[d] * dden;
+            }
+        }
+        free(a);
+        free(ol);
+        free(dnum);
+    }
+    free(H);
+    free(z);
+}
+
+/* per key block j: dk, dv (linear part) of its keys */
+static void lbwd_k_task(void* vctx, int64_t j) {
+    lbwd_ctx* c = (lbwd_ctx*)vctx;
+    int64_t N = c->N, D = c->D;
+    double* Gc = (double*)calloc((size_t)(D * D), sizeof(double));
+    double* wc = (double*)calloc((size_t)D, sizeof(double));
+    for (int64_t i = 0; i < c->nqb; ++i) {
+        if (kept_by(c->kidx, c->keep, i, j)) continue;
+        for (int64_t x = 0; x < D * D; ++x) Gc[x] += c->G[i * D * D + x];
+        for (int64_t d = 0; d < D; ++d) wc[d] += c->w[i * D + d];
+    }
+    double* f = (double*)malloc(sizeof(double) * (size_t)D);
+    int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
+    for (int64_t u = j * ORC_KBLK; u < u1; ++u) {
+        const uint16_t* kr = c->k + (c->bh * N + u) * D;
+        const uint16_t* vr = c->v + (c->bh * N + u) * D;
+        for (int64_t d = 0; d < D; ++d) f[d] = phi((double)orc_bf16_to_f32(kr[d]));
+        for (int64_t d = 0; d < D; ++d) {
+            double g = wc[d];
+            for (int64_t e = 0; e < D; ++e) g += Gc[d * D + e] * (double)orc_bf16_to_f32(vr[e]);
+            c->dk[u * D + d] += g * dphi((double)orc_bf16_to_f32(kr[d]));
+        }
+        for (int64_t e = 0; e < D; ++e) {
+            double g = 0.0;
+            for (int64_t d = 0; d < D; ++d) g += Gc[d * D + e] * f[d];
+            c->dv[u * D + e] += g;
+        }
+    }
+    free(f);
+    free(Gc);
+    free(wc);
+}
+
+void orc_sagesla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int8_t* q_i8,
+                     const float* q_scale, const int8_t* k_i8, const float* k_scale, int64_t N,
+                     int64_t D, int64_t bh, const int32_t* kidx_head, int64_t keep, int branches,
+                     float sm_scale, const uint16_t* dout, double* dq, double* dk, double* dv,
+                     int nthreads) {
+    int64_t nqb = orc_nqb(N), nkb = orc_nkb(N);
+    if (!kidx_head) keep = nkb;
+    memset(dq, 0, sizeof(double) * (size_t)(N * D));
+    memset(dk, 0, sizeof(double) * (size_t)(N * D));
+    memset(dv, 0, sizeof(double) * (size_t)(N * D));
+    if (branches & 1) {
+        sbwd_ctx c;
+        c.q_i8 = q_i8;
+        c.k_i8 = k_i8;
+        c.q_scale = q_scale;
+        c.k_scale = k_scale;
+        c.v = v;
+        c.dout = dout;
+        c.N = N;
+        c.D = D;
+        c.bh = bh;
+        c.nqb = nqb;
+        c.nkb = nkb;
+        c.keep = keep;
+        c.kidx = kidx_head;
+        c.sm = (double)default_sm(sm_scale, D);
+        c.rmax = (double*)malloc(sizeof(double) * (size_t)N);
+        c.rsum = (double*)malloc(sizeof(double) * (size_t)N);
+        c.rD = (double*)malloc(sizeof(double) * (size_t)N);
+        c.dq = dq;
+        c.dk = dk;
+        c.dv = dv;
+        orc_parallel_for(N, nthreads, sbwd_rows_task, &c);
+        orc_parallel_for(N, nthreads, sbwd_keys_task, &c);
+        free(c.rmax);
+        free(c.rsum);
+        free(c.rD);
+    }
+    if ((branches & 2) && kidx_head && keep < nkb) {
+        double* h = (double*)malloc(sizeof(double) * (size_t)(nkb * D * D));
+        double* z = (double*)malloc(sizeof(double) * (size_t)(nkb * D));
+        orc_linear_states(k, v, N, D, bh, h, z, nthreads);
+        lbwd_ctx c = {q, k, v, dout, N, D, bh, nqb, nkb, keep, kidx_head, h, z, NULL, NULL,
+                      dq, dk, dv};
+        c.G = (double*)malloc(sizeof(double) * (size_t)(nqb * D * D));
+        c.w = (double*)malloc(sizeof(double) * (size_t)(nqb * D));
+        orc_parallel_for(nqb, nthreads, lbwd_q_task, &c);
+        orc_parallel_for(nkb, nthreads, lbwd_k_task, &c);
+        free(c.G);
+        free(c.w);
+        free(h);
+        free(z);
+    }
+}
+
+/* The scalar loss L = sum_{t,e} dO_te O_te of the SageSLA forward written
+ * for continuous inputs, fp64: qh, kh feed the sparse branch (exact softmax
+ * of sm * qh . kh over the kept keys, no quantization), ql, kl the linear
+ * branch, vv both. One head, rows [N][D]. Its central differences pin
+ * orc_sagesla_bwd: dQ = dL/dqh + dL/dql at equal positions (the straight-
+ * through reading), likewise dK; dV = dL/dvv. */
+double orc_sagesla_loss(const double* qh, const double* kh, const double* vv, const double* ql,
+                        const double* kl, int64_t N, int64_t D, const int32_t* kidx_head,
+                        int64_t keep, int branches, double sm, const double* dout) {
+    int64_t nqb = orc_nqb(N), nkb = orc_nkb(N);
+    if (!kidx_head) keep = nkb;
+    double L = 0.0;
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    double* o = (double*)malloc(sizeof(double) * (size_t)D);
+    double* a = (double*)malloc(sizeof(double) * (size_t)D);
+    double* H = (double*)malloc(sizeof(double) * (size_t)(D * D));
+    double* z = (double*)malloc(sizeof(double) * (size_t)D);
+    for (int64_t i = 0; i < nqb; ++i) {
+        int64_t t1 = (i + 1) * ORC_QBLK < N ? (i + 1) * ORC_QBLK : N;
+        const int lin = (branches & 2) && kidx_head && keep < nkb;
+        if (lin) { /* the query block's states: sums over its non-kept keys */
+            for (int64_t x = 0; x < D * D; ++x) H[x] = 0.0;
+            for (int64_t d = 0; d < D; ++d) z[d] = 0.0;
+            for (int64_t u = 0; u < N; ++u) {
+                if (kept_by(kidx_head, keep, i, u / ORC_KBLK)) continue;
+                for (int64_t d = 0; d < D; ++d) {
+                    double f = phi(kl[u * D + d]);
+                    z[d] += f;
+                    for (int64_t e = 0; e < D; ++e) H[d * D + e] += f * vv[u * D + e];
+                }
+            }
+        }
+        for (int64_t t = i * ORC_QBLK; t < t1; ++t) {
+            if (branches & 1) {
+                double m = -INFINITY;
+                for (int64_t u = 0; u < N; ++u) {
+                    if (!kept_by(kidx_head, keep, i, u / ORC_KBLK)) continue;
+                    double acc = 0.0;
+                    for (int64_t d = 0; d < D; ++d) acc += qh[t * D + d] * kh[u * D + d];
+                    s[u] = sm * acc;
+                    if (s[u] > m) m = s[u];
+                }
+                double l = 0.0;
+                for (int64_t e = 0; e < D; ++e) o[e] = 0.0;
+                for (int64_t u = 0; u < N; ++u) {
+                    if (!kept_by(kidx_head, keep, i, u / ORC_KBLK)) continue;
+                    double p = exp(s[u] - m);
+                    l += p;
+                    for (int64_t e = 0; e < D; ++e) o[e] += p * vv[u * D + e];
+                }
+                for (int64_t e = 0; e < D; ++e) L += dout[t * D + e] * o[e] / l;
+            }
+            if (lin) {
+                double den = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    a[d] = phi(ql[t * D + d]);
+                    den += a[d] * z[d];
+                }
+                for (int64_t e = 0; e < D; ++e) {
+                    double num = 0.0;
+                    for (int64_t d = 0; d < D; ++d) num += a[d] * H[d * D + e];
+                    L += dout[t * D + e] * num / den;
+                }
+            }
+        }
+    }
+    free(s);
+    free(o);
+    free(a);
+    free(H);
+    free(z);
+    return L;
+}

@@ -129,6 +129,28 @@ void orc_dense_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
                     int64_t D, int64_t bh, float sm_scale, const int64_t* tokens, int64_t R,
                     double* out, int nthreads);
 
+/* SageSLA backward for head bh (page 5: SLA is trainable, fine-tuned in
+ * training). Reading: the 8-bit quantizer passes gradients straight through,
+ * the block selection is held fixed, and the gradient is the exact fp64
+ * derivative of the forward in the dequantized operands (sparse branch:
+ * exact softmax of sm * (sq q_i8) . (sk k_i8) over the kept keys) and the raw
+ * bf16 Q, K (linear branch, phi = elu + 1 over the non-kept blocks); V feeds
+ * both. dout: bf16 dL/dO [BH][N][D]; dq, dk, dv: fp64 [N][D] of head bh.
+ * branches: 1 sparse, 2 linear, 3 both (as the forward); kidx_head NULL =
+ * dense. sm_scale <= 0 selects 1/sqrt(D). */
+void orc_sagesla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int8_t* q_i8,
+                     const float* q_scale, const int8_t* k_i8, const float* k_scale, int64_t N,
+                     int64_t D, int64_t bh, const int32_t* kidx_head, int64_t keep, int branches,
+                     float sm_scale, const uint16_t* dout, double* dq, double* dk, double* dv,
+                     int nthreads);
+
+/* sum_{t,e} dout[t][e] * O[t][e] of the forward on continuous fp64 inputs of
+ * one head: qh, kh (sparse branch, no quantization), ql, kl (linear branch),
+ * vv (both); for pinning orc_sagesla_bwd by central differences. */
+double orc_sagesla_loss(const double* qh, const double* kh, const double* vv, const double* ql,
+                        const double* kl, int64_t N, int64_t D, const int32_t* kidx_head,
+                        int64_t keep, int branches, double sm, const double* dout);
+
 /* W8A8 linear layer (page 5, "Four Technical Pillars", Pillar Three: INT8
  * weights and activations, block-wise granularity 128x128).
  * Readings: y = x . w^T with x [M][K] activations and w [N][K] weights (a

@@ -127,6 +127,25 @@ int main(void) {
     orc_dense_rows(q, k, v, N, D, 0, 0.f, tok, 16, dn, 7);
     for (int64_t x = 0; x < 16 * D; ++x) CHECK(isfinite(dn[x]), "dense finite");
 
+    /* backward of head 1 on 1 and 7 threads, both branches */
+    {
+        uint16_t* dout = malloc(sizeof(uint16_t) * nel);
+        for (int64_t x = 0; x < nel; ++x) dout[x] = rand_bf16(1.f, 0.f);
+        double* g[2][3];
+        for (int r = 0; r < 2; ++r) {
+            for (int n = 0; n < 3; ++n) g[r][n] = malloc(sizeof(double) * N * D);
+            orc_sagesla_bwd(q, k, v, qi[0], qs[0], ki[0], ks[0], N, D, 1, kidx, keep, 3, 0.f, dout,
+                            g[r][0], g[r][1], g[r][2], threads[r]);
+        }
+        for (int n = 0; n < 3; ++n) {
+            CHECK(memcmp(g[0][n], g[1][n], sizeof(double) * N * D) == 0, "backward threads");
+            for (int64_t x = 0; x < N * D; ++x) CHECK(isfinite(g[0][n][x]), "backward finite");
+        }
+        for (int r = 0; r < 2; ++r)
+            for (int n = 0; n < 3; ++n) free(g[r][n]);
+        free(dout);
+    }
+
     /* W8A8 */
     const int64_t M = 300, K = 256, NO = 128;
     uint16_t* xw = malloc(sizeof(uint16_t) * M * K);

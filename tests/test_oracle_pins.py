@@ -694,3 +694,103 @@ def test_w8a8_gemm_close_to_fp64_product(orc):
     ref = _f(x).astype(np.float64) @ _f(w).astype(np.float64).T
     rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
     assert 1e-3 < rel < 2e-2, rel
+
+
+# --------------------------------------------------------------------------
+# backward (page 5: SLA is trainable; the quantizer passes gradients straight
+# through, the block selection is held fixed)
+
+def _bwd_case(orc, N, D, topk, seed, branches=3):
+    q, k, v = make_qkv(1, 1, N, D, seed=seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    dout = torch.randn(1, 1, N, D, generator=g).to(torch.bfloat16)
+    qb, kb, vb, gb = (_bits(t).reshape(1, N, D) for t in (q, k, v, dout))
+    qi, qs, ki, ks, _ = orc.quant_qk(qb, kb)
+    kidx = None
+    if topk is not None:
+        keep = orc.keep_blocks(N, topk)
+        kidx, _ = orc.block_mask(qb, kb, keep)
+        kidx = kidx[0]
+    dq, dk, dv = orc.sagesla_bwd(qb, kb, vb, (qi, qs, ki, ks), 0, gb, kidx, branches)
+    # the continuous inputs the gradient is taken in
+    qh = qi[0].astype(np.float64) * np.repeat(qs[0].astype(np.float64), 128)[:N, None]
+    kh = ki[0].astype(np.float64) * np.repeat(ks[0].astype(np.float64), 64)[:N, None]
+    f = lambda t: t.float().numpy().reshape(N, D).astype(np.float64)  # noqa: E731
+    return dict(q=f(q), k=f(k), v=f(v), dout=f(dout), qh=qh, kh=kh, kidx=kidx,
+                dq=dq, dk=dk, dv=dv, branches=branches)
+
+
+@pytest.mark.parametrize("N,topk,branches", [(200, 0.5, 3), (200, 0.5, 1), (200, 0.5, 2),
+                                             (130, None, 1)])
+def test_backward_matches_central_differences(orc, N, topk, branches):
+    # D = 32 keeps the loss cheap; every formula is generic in D. Each checked
+    # entry moves the sparse and the linear input of Q (or K) together: the
+    # straight-through reading.
+    D = 32
+    c = _bwd_case(orc, N, D, topk, seed=N + branches, branches=branches)
+    sm = float(np.float32(1.0 / np.sqrt(D)))
+    args = dict(kidx_head=c["kidx"], branches=branches, sm=sm)
+
+    def loss(qh, kh, vv, ql, kl):
+        return orc.sagesla_loss(qh, kh, vv, ql, kl, c["dout"], **args)
+
+    rng = np.random.default_rng(7)
+    h = 1e-5
+    for name in ("dq", "dk", "dv"):
+        for _ in range(6):
+            t, d = int(rng.integers(0, N)), int(rng.integers(0, D))
+            ins = {n: c[n].copy() for n in ("qh", "kh", "v", "q", "k")}
+            pairs = {"dq": ("qh", "q"), "dk": ("kh", "k"), "dv": ("v",)}[name]
+            vals = []
+            for sgn in (1, -1):
+                x = {n: a.copy() for n, a in ins.items()}
+                for n in pairs:
+                    x[n][t, d] += sgn * h
+                vals.append(loss(x["qh"], x["kh"], x["v"], x["q"], x["k"]))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            an = c[name][t, d]
+            scale = max(1.0, np.abs(c[name]).max())
+            assert abs(fd - an) <= 1e-6 * scale, (name, t, d, fd, an)
+
+
+def test_backward_sparse_dense_matches_torch_autograd(orc):
+    # full density, sparse branch: the gradient of sum(dO * softmax(sm qh kh^T) v)
+    # by torch's fp64 autograd on the dequantized operands
+    N, D = 300, 64
+    c = _bwd_case(orc, N, D, None, seed=5, branches=1)
+    sm = float(np.float32(1.0 / np.sqrt(D)))
+    qh = torch.tensor(c["qh"], requires_grad=True)
+    kh = torch.tensor(c["kh"], requires_grad=True)
+    vv = torch.tensor(c["v"], requires_grad=True)
+    o = torch.softmax(sm * qh @ kh.T, dim=-1) @ vv
+    (o * torch.tensor(c["dout"])).sum().backward()
+    for got, want in ((c["dq"], qh.grad), (c["dk"], kh.grad), (c["dv"], vv.grad)):
+        want = want.numpy()
+        assert np.abs(got - want).max() <= 1e-10 * max(1.0, np.abs(want).max())
+
+
+def test_backward_invariants(orc):
+    # every query row's dS sums to zero over its keys, so the sparse dK summed
+    # over all keys vanishes; its softmax weights sum to one, so the sparse dV
+    # summed over all keys equals dO summed over all queries (each query block
+    # keeps at least one block); zero dO gives zero gradients; with every block
+    # kept the linear branch contributes nothing
+    N, D = 640, 32
+    c = _bwd_case(orc, N, D, 0.3, seed=11, branches=1)
+    assert np.abs(c["dk"].sum(axis=0)).max() <= 1e-10 * np.abs(c["dk"]).max()
+    assert np.allclose(c["dv"].sum(axis=0), c["dout"].sum(axis=0), rtol=0, atol=1e-9)
+    q, k, v = make_qkv(1, 1, N, D, seed=3)
+    qb, kb, vb = (_bits(t).reshape(1, N, D) for t in (q, k, v))
+    quant = orc.quant_qk(qb, kb)[:4]
+    zero = np.zeros_like(qb)
+    keep = orc.keep_blocks(N, 0.3)
+    kidx = orc.block_mask(qb, kb, keep)[0][0]
+    for g in orc.sagesla_bwd(qb, kb, vb, quant, 0, zero, kidx, 3):
+        assert not g.any()
+    gb = _bits(torch.randn(1, N, D).to(torch.bfloat16)).reshape(1, N, D)
+    nkb = orc.nkb(N)
+    allk = np.tile(np.arange(nkb, dtype=np.int32), (orc.nqb(N), 1))
+    a = orc.sagesla_bwd(qb, kb, vb, quant, 0, gb, allk, 3)
+    b = orc.sagesla_bwd(qb, kb, vb, quant, 0, gb, None, 1)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
