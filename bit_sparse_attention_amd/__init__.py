@@ -29,7 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssa.so")
 
 SPARSE, LINEAR = 1, 2
-OP_QUANT, OP_MASK, OP_ATTN, OP_STEP = 0, 1, 2, 3
+OP_QUANT, OP_MASK, OP_ATTN, OP_STEP, OP_BWD = 0, 1, 2, 3, 4
 HEAD_DIM = 128
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
@@ -82,6 +82,8 @@ def _load():
         "sage_sla_fwd": (i32, [_p, _p, _p, Shape, i64, i32, C.c_float, _p, _p, _p, _p, _p, _p,
                                _p, _p, _p, _p, sz, _p]),
         "sage_qk_int32_tiles": (i32, [_p, _p, Shape, _p, i64, _p, _p]),
+        "sage_sla_attn_bwd": (i32, [_p, _p, _p, Shape, _p, _p, _p, _p, _p, i64, i32, C.c_float,
+                                    _p, _p, _p, _p, _p, sz, _p]),
         "ssa_kernel_timer_start": (i32, [i32]),
         "ssa_kernel_timer_read": (i32, [C.POINTER(C.c_float), i32]),
         "ssa_kernel_timer_stop": (None, []),
@@ -234,6 +236,33 @@ def sage_sla_attn_fwd(q, k, v, q_i8, q_scale, k_i8, k_scale, kidx=None, keep=Non
         _ptr(kidx), int(keep), int(branches), float(sm_scale), _ptr(out), _ptr(out32), _ptr(ws), n,
         _stream(dev)))
     return (out, out32) if return_f32 else out
+
+
+def sage_sla_attn_bwd(q, k, v, q_i8, q_scale, k_i8, k_scale, dout, kidx=None, keep=None,
+                      branches: int = SPARSE | LINEAR, sm_scale: float = 0.0):
+    """SageSLA backward: (dq, dk, dv) fp32 [B,H,N,D] for dL/dO = dout (bf16),
+    with the same quantized tensors, selection and branches as the forward."""
+    s = _qkv_shape(q, k, v)
+    B, H, N, D = q.shape
+    dev = q.device
+    nqb, nkb = num_q_blocks(N), num_k_blocks(N)
+    _need_gpu("q_i8", q_i8, torch.int8, q.shape)
+    _need_gpu("k_i8", k_i8, torch.int8, q.shape)
+    _need_gpu("q_scale", q_scale, torch.float32, (B, H, nqb))
+    _need_gpu("k_scale", k_scale, torch.float32, (B, H, nkb))
+    _need_gpu("dout", dout, torch.bfloat16, q.shape)
+    if kidx is None:
+        keep = nkb
+    else:
+        keep = kidx.shape[-1] if keep is None else int(keep)
+        _need_gpu("kidx", kidx, torch.int32, (B, H, nqb, keep))
+    grads = [torch.empty((B, H, N, D), dtype=torch.float32, device=dev) for _ in range(3)]
+    ws, n = _ws(OP_BWD, s, dev, keep, branches)
+    _check("sage_sla_attn_bwd", _load().sage_sla_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), s, _ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale),
+        _ptr(kidx), int(keep), int(branches), float(sm_scale), _ptr(dout), *map(_ptr, grads),
+        _ptr(ws), n, _stream(dev)))
+    return tuple(grads)
 
 
 def sage_qk_int32_tiles(q_i8, k_i8, tiles):

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libssa.so")
-SOURCES = ["api.hip", "quant.hip", "mask.hip", "attn.hip", "linear.hip", "w8a8.hip"]
+SOURCES = ["api.hip", "quant.hip", "mask.hip", "attn.hip", "linear.hip", "w8a8.hip", "bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

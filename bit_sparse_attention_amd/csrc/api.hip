@@ -176,16 +176,23 @@ MaskWs ws_mask(const Dims& d) {
 }
 
 struct AttnWs {
-    size_t vt, hs, hpart, htot, msel, hnon, total;
+    size_t vt, hs, hs_lo, hpart, htot, msel, hnon, total;
+    bool lo;
 };
-AttnWs ws_attn(const Dims& d, bool linear) {
+// lo: also the states' bf16 rests (the backward's complement states)
+AttnWs ws_attn(const Dims& d, bool linear, bool lo = false) {
     AttnWs w{};
+    w.lo = linear && lo;
     size_t off = 0;
     w.vt = off;
     off += align256((size_t)d.BH * d.nkb * HD * KBLK * 2);
     if (linear) {
         w.hs = off;
         off += align256((size_t)d.BH * d.nkb * HS_ROW * 2);
+        if (w.lo) {
+            w.hs_lo = off;
+            off += align256((size_t)d.BH * d.nkb * HS_ROW * 2);
+        }
         w.hpart = off;
         off += align256((size_t)d.BH * d.ngroups * HS_ROW * 4);
         w.htot = off;
@@ -211,6 +218,44 @@ StepWs ws_step(const Dims& d, bool linear) {
     w.pool = w.attn.total;
     w.part = w.pool + ws_mask(d).total;
     w.total = w.part + ws_quant(d);
+    return w;
+}
+
+// the backward: the forward attention's workspace (V layout, and the linear
+// branch's complement states), the row statistics, the channel-first bf16
+// tiles, the inverse selection lists and the linear branch's gradient states
+struct BwdWs {
+    AttnWs attn;
+    size_t mlog, dstat, kt16, qt16, dot, counts, lists, gf, gs, gs_lo, gtot, msel, gc, total;
+};
+BwdWs ws_bwd(const Dims& d, bool sel, bool linear) {
+    BwdWs w{};
+    w.attn = ws_attn(d, linear, true);
+    size_t off = w.attn.total;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    w.mlog = take((size_t)d.BH * d.N * 4);
+    w.dstat = take((size_t)d.BH * d.N * 4);
+    w.kt16 = take((size_t)d.BH * d.nkb * HD * KBLK * 2);
+    w.qt16 = take((size_t)d.BH * d.nqb * HD * QBLK * 2);
+    w.dot = take((size_t)d.BH * d.nqb * HD * QBLK * 2);
+    if (sel) {
+        w.counts = take((size_t)d.BH * d.nkb * 4);
+        w.lists = take((size_t)d.BH * d.nkb * d.nqb * 2);
+    }
+    if (linear) {
+        const int64_t nqbp = (d.nqb + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
+        w.gf = take((size_t)d.BH * d.nqb * HS_ROW * 4);
+        w.gs = take((size_t)d.BH * d.nqb * HS_ROW * 2);
+        w.gs_lo = take((size_t)d.BH * d.nqb * HS_ROW * 2);
+        w.gtot = take((size_t)d.BH * HS_ROW * 4);
+        w.msel = take(msel_bytes(d.BH, d.nkb, nqbp));
+        w.gc = take((size_t)d.BH * d.nkb * HS_ROW * 4);
+    }
+    w.total = off;
     return w;
 }
 
@@ -257,6 +302,7 @@ hipError_t enqueue_states(const Dims& d, bool linear, const uint16_t* k, const u
     uint16_t* vt = (uint16_t*)(base + w.vt);
     if (linear)
         return launch_linear_states(k, v, d.BH, (int)d.N, vt, (uint16_t*)(base + w.hs),
+                                    w.lo ? (uint16_t*)(base + w.hs_lo) : nullptr,
                                     (float*)(base + w.hpart), (float*)(base + w.htot), kpart,
                                     kbarT, ldk, st);
     return launch_vt_only(k, v, d.BH, (int)d.N, vt, kpart, kbarT, ldk, st);
@@ -265,6 +311,7 @@ hipError_t enqueue_states(const Dims& d, bool linear, const uint16_t* k, const u
 hipError_t enqueue_complement(const Dims& d, const int32_t* kidx, int64_t keep, char* base,
                               const AttnWs& w, hipStream_t st) {
     return launch_complement(kidx, (int)keep, (const uint16_t*)(base + w.hs),
+                             w.lo ? (const uint16_t*)(base + w.hs_lo) : nullptr,
                              (const float*)(base + w.htot), d.BH, (int)d.N,
                              (uint32_t*)(base + w.msel), (float*)(base + w.hnon), st);
 }
@@ -293,6 +340,9 @@ hipError_t enqueue_attn(const Dims& d, bool sparse, bool linear, const uint16_t*
     a.hnon = linear ? (const float*)(base + w.hnon) : nullptr;
     a.out = out;
     a.out32 = out_f32;
+    a.dout = nullptr;
+    a.mlog = nullptr;
+    a.dstat = nullptr;
     const int slot = timer_slot();
     if (slot >= 0) (void)hipEventRecord(g_ev0[slot], st);
     const hipError_t e = launch_attn(a, st);
@@ -333,6 +383,11 @@ size_t ssa_workspace_bytes(int op, ssa_shape s, int64_t keep, int branches) {
         case SSA_OP_STEP: {
             const bool linear = (branches & SSA_BRANCH_LINEAR) && keep >= 1 && keep < d.nkb;
             return op == SSA_OP_ATTN ? ws_attn(d, linear).total : ws_step(d, linear).total;
+        }
+        case SSA_OP_BWD: {
+            const bool sel = keep >= 1 && keep < d.nkb;
+            const bool linear = (branches & SSA_BRANCH_LINEAR) && sel;
+            return ws_bwd(d, sel, linear).total;
         }
         default: return 0;
     }
@@ -599,6 +654,159 @@ ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     e = enqueue_attn(d, sparse, linear, q, q_i8, q_scale, k_i8, k_scale, kidx, keep, sm_scale,
                      out, out_f32, base, w.attn, st);
     if (e != hipSuccess) return hip_fail(e, "sage_sla_fwd launch");
+    return SSA_OK;
+}
+
+ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, ssa_shape s,
+                             const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                             const float* k_scale, const int32_t* kidx, int64_t keep, int branches,
+                             float sm_scale, const uint16_t* dout, float* dq, float* dk, float* dv,
+                             void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    Dims d;
+    TRY(check_shape(s, &d));
+    if (branches < 1 || branches > 3)
+        return fail(SSA_ERR_INVALID, "branches=%d must be SPARSE, LINEAR or both", branches);
+    if (keep < 1 || keep > d.nkb)
+        return fail(SSA_ERR_INVALID, "keep=%lld outside [1, %lld]", (long long)keep,
+                    (long long)d.nkb);
+    if (!kidx && keep != d.nkb)
+        return fail(SSA_ERR_INVALID, "dense call (kidx NULL) needs keep == Nkb (%lld)",
+                    (long long)d.nkb);
+    if (!(sm_scale == sm_scale) || std::isinf(sm_scale))
+        return fail(SSA_ERR_INVALID, "sm_scale is not finite");
+    const bool sparse = branches & SSA_BRANCH_SPARSE;
+    const bool sel = kidx && keep < d.nkb;
+    const bool linear = (branches & SSA_BRANCH_LINEAR) && sel;
+    // the linear branch's transposed state GEMM has a row per key block
+    if (linear && d.BH * complement_tiles_per_head(d.nkb) > MAX_WG_256)
+        return fail(SSA_ERR_UNSUPPORTED, "B*H=%lld too large for N=%lld (linear-branch grid)",
+                    (long long)d.BH, (long long)s.N);
+    TRY(need_ptr(q, 16, "q"));
+    TRY(need_ptr(k, 16, "k"));
+    TRY(need_ptr(v, 16, "v"));
+    TRY(need_ptr(q_i8, 16, "q_i8"));
+    TRY(need_ptr(k_i8, 16, "k_i8"));
+    TRY(need_ptr(q_scale, 4, "q_scale"));
+    TRY(need_ptr(k_scale, 4, "k_scale"));
+    TRY(need_ptr(dout, 16, "dout"));
+    TRY(need_ptr(dq, 16, "dq"));
+    TRY(need_ptr(dk, 16, "dk"));
+    TRY(need_ptr(dv, 16, "dv"));
+    if (kidx) TRY(need_ptr(kidx, 4, "kidx"));
+    const size_t nel = (size_t)d.BH * d.N * HD;
+    const Range ins[] = {{q, nel * 2, "q"},
+                         {k, nel * 2, "k"},
+                         {v, nel * 2, "v"},
+                         {q_i8, nel, "q_i8"},
+                         {k_i8, nel, "k_i8"},
+                         {q_scale, (size_t)d.BH * d.nqb * 4, "q_scale"},
+                         {k_scale, (size_t)d.BH * d.nkb * 4, "k_scale"},
+                         {kidx, kidx ? (size_t)d.BH * d.nqb * keep * 4 : 0, "kidx"},
+                         {dout, nel * 2, "dout"}};
+    const Range outs[] = {{dq, nel * 4, "dq"},
+                          {dk, nel * 4, "dk"},
+                          {dv, nel * 4, "dv"},
+                          {ws, ws_bytes, "workspace"}};
+    TRY(check_alias(outs, 4, ins, 9));
+    const BwdWs w = ws_bwd(d, sel, linear);
+    TRY(check_ws(ws, ws_bytes, w.total));
+    TRY(check_device());
+
+    hipStream_t st = (hipStream_t)stream;
+    char* base = (char*)ws;
+    const float sm = sm_scale > 0.f ? sm_scale : (float)(1.0 / std::sqrt((double)HD));
+    hipError_t e = hipSuccess;
+    if (!sparse && !linear) {
+        // only the linear branch was asked for and it is empty: zero gradients
+        e = launch_zero(dq, (int64_t)nel, st);
+        if (e == hipSuccess) e = launch_zero(dk, (int64_t)nel, st);
+        if (e == hipSuccess) e = launch_zero(dv, (int64_t)nel, st);
+        if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch");
+        return SSA_OK;
+    }
+    // the forward's V layout and, for the linear branch, its complement states
+    e = enqueue_states(d, linear, k, v, base, w.attn, nullptr, nullptr, 0, st);
+    if (e == hipSuccess && linear) e = enqueue_complement(d, kidx, keep, base, w.attn, st);
+    if (e == hipSuccess && sel)
+        e = launch_inv_lists(kidx, (int)keep, d.BH, (int)d.nqb, (int)d.nkb,
+                             (uint16_t*)(base + w.lists), (int32_t*)(base + w.counts), st);
+    if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (states)");
+    if (sparse) {
+        // the forward's row statistics
+        AttnArgs f;
+        f.q_i8 = q_i8;
+        f.q_scale = q_scale;
+        f.k_i8 = k_i8;
+        f.k_scale = k_scale;
+        f.vt = (const uint16_t*)(base + w.attn.vt);
+        f.kidx = kidx;
+        f.keep = (int)keep;
+        f.N = (int)d.N;
+        f.nqb = (int)d.nqb;
+        f.nkb = (int)d.nkb;
+        f.BH = d.BH;
+        f.K32 = (float)((double)sm * 1.4426950408889634074);
+        f.do_sparse = 1;
+        f.q = q;
+        f.hnon = nullptr;
+        f.out = nullptr;
+        f.out32 = nullptr;
+        f.dout = dout;
+        f.mlog = (float*)(base + w.mlog);
+        f.dstat = (float*)(base + w.dstat);
+        e = launch_attn(f, st);
+        BwdArgs b;
+        b.q_i8 = q_i8;
+        b.q_scale = q_scale;
+        b.k_i8 = k_i8;
+        b.k_scale = k_scale;
+        b.v = v;
+        b.dout = dout;
+        b.kt16 = (const uint16_t*)(base + w.kt16);
+        b.qt16 = (const uint16_t*)(base + w.qt16);
+        b.dot = (const uint16_t*)(base + w.dot);
+        b.kidx = kidx;
+        b.keep = (int)keep;
+        b.lists = sel ? (const uint16_t*)(base + w.lists) : nullptr;
+        b.counts = sel ? (const int32_t*)(base + w.counts) : nullptr;
+        b.N = (int)d.N;
+        b.nqb = (int)d.nqb;
+        b.nkb = (int)d.nkb;
+        b.BH = d.BH;
+        b.K32 = f.K32;
+        b.sm = sm;
+        b.mlog = f.mlog;
+        b.dstat = f.dstat;
+        b.dq = dq;
+        b.dk = dk;
+        b.dv = dv;
+        if (e == hipSuccess)
+            e = launch_bwd_prep(b, dout, (uint16_t*)(base + w.kt16), (uint16_t*)(base + w.qt16),
+                                (uint16_t*)(base + w.dot), st);
+        if (e == hipSuccess) e = launch_bwd_sparse(b, st);
+        if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (sparse branch)");
+    }
+    if (linear) {
+        const int acc = sparse ? 1 : 0;
+        float* gf = (float*)(base + w.gf);
+        uint16_t* gs = (uint16_t*)(base + w.gs);
+        uint16_t* gs_lo = (uint16_t*)(base + w.gs_lo);
+        float* gtot = (float*)(base + w.gtot);
+        float* gc = (float*)(base + w.gc);
+        e = launch_lin_bwd_q(q, dout, (const float*)(base + w.attn.hnon), d.BH, (int)d.N, acc, dq,
+                             gf, gs, gs_lo, st);
+        if (e == hipSuccess) e = launch_state_total(gf, (int)d.nqb, d.BH, gtot, st);
+        // the gradient states summed over the query blocks that did not keep
+        // each key block: the complement GEMM on the transposed selection
+        if (e == hipSuccess)
+            e = launch_complement_lists((const uint16_t*)(base + w.lists),
+                                        (const int32_t*)(base + w.counts), (int)d.nkb, (int)d.nqb,
+                                        2 * keep > d.nkb ? 1 : 0, gs, gs_lo, gtot, d.BH,
+                                        (uint32_t*)(base + w.msel), gc, st);
+        if (e == hipSuccess) e = launch_lin_bwd_k(k, v, gc, d.BH, (int)d.N, acc, dk, dv, st);
+        if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (linear branch)");
+    }
     return SSA_OK;
 }
 

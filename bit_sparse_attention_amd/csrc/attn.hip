@@ -314,8 +314,14 @@ __device__ __forceinline__ f32x4 hstage_read(const uint8_t* smem, int row, int p
 constexpr int ATTN_LDS = NSTAGE * (KTILE + VTILE);
 static_assert(ATTN_LDS >= HSTAGE_BYTES, "state staging fits the rings");
 
-template <bool LIN>
+// MODE: ATTN_SPARSE (sparse branch only), ATTN_LINEAR (plus the linear
+// epilogue), ATTN_STATS (the backward's row statistics: instead of the
+// output, the normalizer m + log2(l) and D = dO . o_s of every query row).
+enum { ATTN_SPARSE = 0, ATTN_LINEAR = 1, ATTN_STATS = 2 };
+
+template <int MODE>
 __device__ __forceinline__ void attn_block(const AttnArgs& a, uint8_t* smem, int64_t bh, int i) {
+    constexpr bool LIN = MODE == ATTN_LINEAR;
     uint8_t(*ks)[KTILE] = reinterpret_cast<uint8_t(*)[KTILE]>(smem);
     uint8_t(*vs)[VTILE] = reinterpret_cast<uint8_t(*)[VTILE]>(smem + NSTAGE * KTILE);
     const int N = a.N, nkb = a.nkb;
@@ -462,6 +468,27 @@ __device__ __forceinline__ void attn_block(const AttnArgs& a, uint8_t* smem, int
 
     const float lt = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = a.do_sparse ? 1.0f / lt : 0.f;
+    if (MODE == ATTN_STATS) {
+        // P of the backward is 2^(S*c - (m + log2 l)); D = dO . (o / l), the
+        // lane pair holding the query's 128 channels
+        float dsum = 0.f;
+        const bool ok = tq < N;
+        const uint16_t* grow = a.dout + (bh * N + (ok ? tq : 0)) * HD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const u16x4 g4 = ok ? *(const u16x4*)(grow + 32 * dt + 8 * q4 + 4 * hi) : u16x4{};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dsum = __builtin_fmaf(bf2f(g4[u]), o[dt][4 * q4 + u] * inv, dsum);
+            }
+        dsum += __shfl_xor(dsum, 32, 64);
+        if (ok && hi == 0) {
+            a.mlog[bh * N + tq] = m_run + __log2f(lt);
+            a.dstat[bh * N + tq] = dsum;
+        }
+        return;
+    }
     if (LIN) {
         // Stage Hnon_i (128 rows of h^T, then z: 129 rows of 512 bytes) in LDS
         // with one batch of DMAs. The 16-byte unit u of row r sits at unit
@@ -555,12 +582,12 @@ __device__ __forceinline__ void attn_block(const AttnArgs& a, uint8_t* smem, int
     }
 }
 
-template <bool LIN>
+template <int MODE>
 __global__ __launch_bounds__(ATTN_THREADS, 2) void sagesla_attn_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ATTN_LDS];
     const int64_t item = blockIdx.x;
     if (item >= a.BH * a.nqb) return;
-    attn_block<LIN>(a, smem, item / a.nqb, (int)(item % a.nqb));
+    attn_block<MODE>(a, smem, item / a.nqb, (int)(item % a.nqb));
 }
 
 // Raw int32 tiles through the same LDS staging and qk_tile_mfma routine as
@@ -609,12 +636,15 @@ __global__ __launch_bounds__(ATTN_THREADS) void qk_tiles_kernel(const int8_t* __
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     const int64_t total = a.BH * a.nqb;
-    if (a.hnon)
-        hipLaunchKernelGGL((sagesla_attn_kernel<true>), dim3((unsigned)total), dim3(ATTN_THREADS), 0,
-                           st, a);
+    if (a.mlog)
+        hipLaunchKernelGGL((sagesla_attn_kernel<ATTN_STATS>), dim3((unsigned)total),
+                           dim3(ATTN_THREADS), 0, st, a);
+    else if (a.hnon)
+        hipLaunchKernelGGL((sagesla_attn_kernel<ATTN_LINEAR>), dim3((unsigned)total),
+                           dim3(ATTN_THREADS), 0, st, a);
     else
-        hipLaunchKernelGGL((sagesla_attn_kernel<false>), dim3((unsigned)total), dim3(ATTN_THREADS),
-                           0, st, a);
+        hipLaunchKernelGGL((sagesla_attn_kernel<ATTN_SPARSE>), dim3((unsigned)total),
+                           dim3(ATTN_THREADS), 0, st, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,604 @@
+// bwd.hip -- the SageSLA backward on gfx950.
+//
+// TurboDiffusion pages, page 5 "What is TurboDiffusion?" and the training
+// guide: the sparse-linear attention is trainable (fine-tuned in training).
+// Gradients pass the 8-bit quantizer straight through (its derivative is
+// taken as the identity) and the block selection is held fixed. With the
+// forward's row statistics m' = m + log2(l) and D = dO . o_s (from the
+// forward kernel's statistics mode), for a query t and a kept key u:
+//   P = 2^(S*c - m'),  dP = dO_t . v_u,  dS = P (dP - D)
+//   dq_t += sm sum_u dS sk k_i8_u      (query-block-major: dq_kernel)
+//   dk_u += sm sum_t dS sq q_i8_t,  dv_u += sum_t P dO_t
+//                                      (key-block-major over the query blocks
+//                                       that kept the block: dkdv_kernel)
+// S is the exact int32 product on the INT8 matrix cores; dP, dq, dk and dv
+// run on the bf16 matrix cores with fp32 accumulation (P and dS rounded to
+// bf16; the int8 operands are exact in bf16). The linear branch (phi = elu+1
+// over the non-kept blocks) follows the same reading in fp32: per query block
+// its gradient states G_i = sum_t phi(q_t) dnum_t^T, w_i = sum_t phi(q_t) dden_t,
+// their sums over the query blocks that did NOT keep each key block (the
+// forward's complement GEMM on the transposed selection), then per key block
+// the key and value gradients.
+#include <algorithm>
+
+#include "../../include/ssa.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssa {
+
+// Position p of a re-laid 16-token group holds token perm16(p): positions
+// 0-3 -> 0-3, 4-7 -> 8-11, 8-11 -> 4-7, 12-15 -> 12-15 (bits 2 and 3 swapped):
+// the order in which one lane of the 32x32 MFMA output holds its rows, so a
+// tile computed on the matrix cores feeds the next product without shuffles.
+__device__ __forceinline__ int perm16(int p) {
+    return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
+
+// ---- prep: bf16 tiles with the channel dimension first --------------------
+// y[bh][b][d][p] = bf16(x[bh][BLK*b + 16(p/16) + perm16(p%16)][d]) for the
+// BLK-token blocks b of an int8 or bf16 [BH][N][128] tensor; 0 past N.
+template <typename T, int BLK>
+__global__ __launch_bounds__(256) void transpose_tiles_kernel(const T* __restrict__ x, int N, int nb,
+                                                              uint16_t* __restrict__ y) {
+    __shared__ uint16_t t[BLK][HD + 2];
+    const int b = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    constexpr int CH = 16 / sizeof(T);  // elements per 16-byte load
+    for (int c = tid; c < BLK * HD / CH; c += 256) {
+        const int r = c / (HD / CH), d0 = (c % (HD / CH)) * CH;
+        const int tok = BLK * b + r;
+        uint16_t v[CH];
+        if (tok < N) {
+            const T* src = x + (bh * N + tok) * HD + d0;
+            if (sizeof(T) == 1) {
+                const i32x4 w = *(const i32x4*)src;
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    const int8_t q = (int8_t)((w[e >> 2] >> (8 * (e & 3))) & 255);
+                    v[e] = f2bf((float)q);  // exact: |q| <= 127
+                }
+            } else {
+                const u16x8 w = *(const u16x8*)src;
+#pragma unroll
+                for (int e = 0; e < CH; ++e) v[e] = w[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < CH; ++e) v[e] = 0;
+        }
+#pragma unroll
+        for (int e = 0; e < CH; ++e) t[r][d0 + e] = v[e];
+    }
+    __syncthreads();
+    uint16_t* out = y + (bh * nb + b) * (int64_t)HD * BLK;
+    for (int c = tid; c < HD * BLK / 8; c += 256) {
+        const int d = c / (BLK / 8), p0 = 8 * (c % (BLK / 8));
+        u16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int p = p0 + e;
+            w[e] = t[16 * (p >> 4) + perm16(p & 15)][d];
+        }
+        *(u16x8*)(out + (int64_t)d * BLK + p0) = w;
+    }
+}
+
+// ---- the query blocks that kept each key block ----------------------------
+// lists[bh][j][0..counts[bh][j]) = the query blocks i (ascending) whose kept
+// list kidx[bh][i] (ascending) holds j, found by binary search.
+__global__ __launch_bounds__(256) void inv_lists_kernel(const int32_t* __restrict__ kidx, int keep,
+                                                        int nqb, int nkb,
+                                                        uint16_t* __restrict__ lists,
+                                                        int32_t* __restrict__ counts) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int64_t bh = blockIdx.y;
+    if (j >= nkb) return;
+    const int32_t* rows = kidx + bh * nqb * (int64_t)keep;
+    uint16_t* out = lists + (bh * nkb + j) * (int64_t)nqb;
+    int cnt = 0;
+    for (int i = 0; i < nqb; ++i) {
+        const int32_t* r = rows + (int64_t)i * keep;
+        int lo = 0, hi = keep;  // first entry >= j
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (r[mid] < j) lo = mid + 1; else hi = mid;
+        }
+        if (lo < keep && r[lo] == j) out[cnt++] = (uint16_t)i;
+    }
+    counts[bh * nkb + j] = cnt;
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int64_t n) {
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256)
+        p[x] = 0.f;
+}
+
+// ---- dq: one workgroup per (head, query block), 4 waves x 32 queries ------
+// For each kept key block: its int8 K tile (8 KB, 64 rows of 128 channels),
+// raw bf16 V tile (16 KB, 64 rows of 256 B) and bf16 K^T tile (16 KB, 128
+// channel rows of 64 re-laid keys) arrive in a double-buffered LDS ring by
+// LDS DMA. Per wave (queries 32w + l32, lane pair hi):
+//   S^T = K . Q^T         (int8; lane holds query l32, keys 8(r/4)+4hi+r%4 (+32))
+//   dP^T = V . dO^T       (bf16; same layout)
+//   dS^T = P (dP - D) sk  (registers, packed as the next product's B operand)
+//   dQ^T += K^T . dS^T    (bf16, fp32 accumulation)
+constexpr int DQ_KT = KBLK * HD;           // int8 K tile
+constexpr int DQ_VT = KBLK * HD * 2;       // raw V tile
+constexpr int DQ_TT = HD * KBLK * 2;       // K^T tile
+constexpr int DQ_STAGE = DQ_KT + DQ_VT + DQ_TT;
+constexpr int DQ_DMAS = (DQ_STAGE / 1024) / 4;  // 1 KB LDS DMAs per wave per stage
+
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <bool DENSE>
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * DQ_STAGE];
+    const int64_t item = blockIdx.x;
+    if (item >= a.BH * a.nqb) return;
+    const int64_t bh = item / a.nqb;
+    const int i = (int)(item % a.nqb);
+    const int N = a.N, nkb = a.nkb;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
+              hi = lane >> 5;
+    const int tq = i * QBLK + 32 * wave + l32;
+    const bool qok = tq < N;
+    const int nsel = DENSE ? nkb : a.keep;
+    const int32_t* krow = DENSE ? nullptr : a.kidx + (bh * a.nqb + i) * (int64_t)a.keep;
+    auto blk = [&](int jj) { return DENSE ? jj : min(max(krow[jj], 0), nkb - 1); };
+    const float sq = a.q_scale[bh * a.nqb + i];
+    const float* ksc = a.k_scale + bh * nkb;
+
+    // stage layout: K tile | V tile | K^T tile
+    auto issue = [&](int jj, int st) {
+        const int j = blk(jj);
+        uint8_t* base = smem + st * DQ_STAGE;
+        const int nval = min(KBLK, N - j * KBLK);
+        // K: 64 rows of 128 B, chunk c of row r at slot c ^ swz8(r); rows past
+        // N re-read row N-1
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int row = 16 * wave + 8 * p + (lane >> 3);
+            const int rr = min(row, nval - 1);
+            dma16(a.k_i8 + (bh * N + (int64_t)j * KBLK) * HD,
+                  rr * 128 + 16 * ((lane & 7) ^ swz8(row)),
+                  lds_u32(base) + (16 * wave + 8 * p) * 128);
+        }
+        // V: 64 rows of 256 B, 16-byte chunk c of key row r at slot c ^ (r & 15)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row = 16 * wave + 4 * p + (lane >> 4);
+            const int rr = min(row, nval - 1);
+            dma16(a.v + (bh * N + (int64_t)j * KBLK) * HD,
+                  rr * 256 + 16 * ((lane & 15) ^ (row & 15)),
+                  lds_u32(base + DQ_KT) + (16 * wave + 4 * p) * 256);
+        }
+        // K^T: 128 rows of 128 B (the V^T tile layout), zero past N
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row = 32 * wave + 8 * p + (lane >> 3);
+            dma16(a.kt16 + (bh * nkb + j) * (int64_t)HD * KBLK,
+                  row * 128 + 16 * ((lane & 7) ^ swz8(row)),
+                  lds_u32(base + DQ_KT + DQ_VT) + (32 * wave + 8 * p) * 128);
+        }
+    };
+
+    // per-lane operands: Q (int8 B operand of S^T), dO (bf16 B operand of dP^T)
+    i32x4 qop[4];
+    bf16x8 dop[8];
+    {
+        const int8_t* qp = a.q_i8 + (bh * N + (qok ? tq : 0)) * HD;
+        const uint16_t* gp = a.dout + (bh * N + (qok ? tq : 0)) * HD;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qop[c] = qok ? *(const i32x4*)(qp + 32 * c + 16 * hi) : i32x4{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            dop[s] = qok ? __builtin_bit_cast(bf16x8, *(const u16x8*)(gp + 16 * s + 8 * hi)) : bf16x8{};
+    }
+    const float mq = qok ? a.mlog[bh * N + tq] : 0.f;
+    const float Dq = qok ? a.dstat[bh * N + tq] : 0.f;
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+
+    issue(0, 0);
+    for (int jj = 0; jj < nsel; ++jj) {
+        const int st = jj & 1;
+        if (jj + 1 < nsel) {
+            issue(jj + 1, st ^ 1);
+            wait_vm<DQ_DMAS>();
+        } else {
+            wait_vm<0>();
+        }
+        __syncthreads();
+        const int j = blk(jj);
+        const int kval = min(KBLK, N - j * KBLK);
+        const float sk = ksc[j];
+        const float c = (sq * sk) * a.K32;
+        const uint8_t* kt = smem + st * DQ_STAGE;
+        const uint8_t* vt = kt + DQ_KT;
+        const uint8_t* tt = vt + DQ_VT;
+        i32x16 s[2];
+        f32x16 dp[2];
+        s[0] = s[1] = i32x16{};
+        dp[0] = dp[1] = f32x16{};
+#pragma unroll
+        for (int cq = 0; cq < 4; ++cq) {
+            const int slot = ((2 * cq + hi) ^ swz8(l32)) * 16;
+            s[0] = mfma_i8_32x32x32(*(const i32x4*)(kt + l32 * 128 + slot), qop[cq], s[0]);
+            s[1] = mfma_i8_32x32x32(*(const i32x4*)(kt + (32 + l32) * 128 + slot), qop[cq], s[1]);
+        }
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int key = 32 * h + l32;
+                const bf16x8 va = *(const bf16x8*)(vt + key * 256 + 16 * ((2 * sd + hi) ^ (key & 15)));
+                dp[h] = mfma_bf16_32x32x16(va, dop[sd], dp[h]);
+            }
+        }
+        bf16x8 dsb[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 32 * h + mfma32_row(lane, r);
+                const float p = key < kval ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[h][r], c, -mq)) : 0.f;
+                const float ds = p * (dp[h][r] - Dq) * sk;
+                dsb[2 * h + (r >> 3)][r & 7] = (__bf16)ds;
+            }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x8 ka =
+                    *(const bf16x8*)(tt + (32 * dt + l32) * 128 + ((2 * cc + hi) ^ swz8(l32)) * 16);
+                acc[dt] = mfma_bf16_32x32x16(ka, dsb[cc], acc[dt]);
+            }
+        __syncthreads();  // the next issue refills this stage
+    }
+    if (qok) {
+        float* row = a.dq + (bh * N + tq) * HD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int dv = 32 * dt + 8 * q4 + 4 * hi;
+                *(f32x4*)(row + dv) = f32x4{acc[dt][4 * q4] * a.sm, acc[dt][4 * q4 + 1] * a.sm,
+                                            acc[dt][4 * q4 + 2] * a.sm, acc[dt][4 * q4 + 3] * a.sm};
+            }
+    }
+}
+
+// ---- dk, dv: one workgroup per (head, key block), 2 waves x 32 keys -------
+// Over the query blocks that kept the block (every block when dense), in
+// quarters of 32 queries. Per wave (keys 64j + 32w + l32, lane pair hi):
+//   S = Q . K^T     (int8; lane holds key l32, queries 8(r/4)+4hi+r%4 of the quarter)
+//   dP = dO . V^T   (bf16; same layout)
+//   dS = P (dP - D) sq
+//   dV^T += dO^T . P,  dK^T += Q^T . dS   (bf16; the A operands from the
+//                                          channel-first re-laid tiles, whose
+//                                          query order matches P's registers)
+// Operands come straight from global memory (the two waves share them
+// through the caches).
+template <bool DENSE>
+__global__ __launch_bounds__(128) void dkdv_kernel(BwdArgs a) {
+    const int64_t item = blockIdx.x;
+    if (item >= a.BH * a.nkb) return;
+    const int64_t bh = item / a.nkb;
+    const int j = (int)(item % a.nkb);
+    const int N = a.N, nqb = a.nqb;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
+              hi = lane >> 5;
+    const int u = j * KBLK + 32 * wave + l32;
+    const bool kok = u < N;
+    i32x4 kop[4];
+    bf16x8 vop[8];
+    {
+        const int8_t* kp = a.k_i8 + (bh * N + (kok ? u : 0)) * HD;
+        const uint16_t* vp = a.v + (bh * N + (kok ? u : 0)) * HD;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kop[c] = kok ? *(const i32x4*)(kp + 32 * c + 16 * hi) : i32x4{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            vop[s] = kok ? __builtin_bit_cast(bf16x8, *(const u16x8*)(vp + 16 * s + 8 * hi)) : bf16x8{};
+    }
+    const float sk = a.k_scale[bh * a.nkb + j];
+    f32x16 dva[4], dka[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) dva[dt] = dka[dt] = f32x16{};
+    const int cnt = DENSE ? nqb : a.counts[bh * a.nkb + j];
+    const uint16_t* list = DENSE ? nullptr : a.lists + (bh * a.nkb + j) * (int64_t)nqb;
+    for (int x = 0; x < cnt; ++x) {
+        const int i = DENSE ? x : (int)list[x];
+        const float sq = a.q_scale[bh * nqb + i];
+        const float c = (sq * sk) * a.K32;
+        const uint16_t* dot = a.dot + (bh * nqb + i) * (int64_t)HD * QBLK;
+        const uint16_t* qt = a.qt16 + (bh * nqb + i) * (int64_t)HD * QBLK;
+#pragma unroll 1
+        for (int qq = 0; qq < 4; ++qq) {
+            const int t0 = i * QBLK + 32 * qq;
+            const int tr = t0 + l32;  // the query row this lane supplies
+            const bool rok = tr < N;
+            i32x16 s = i32x16{};
+            f32x16 dp = f32x16{};
+            {
+                const int8_t* qp = a.q_i8 + (bh * N + (rok ? tr : 0)) * HD;
+                const uint16_t* gp = a.dout + (bh * N + (rok ? tr : 0)) * HD;
+#pragma unroll
+                for (int cq = 0; cq < 4; ++cq) {
+                    const i32x4 qa = rok ? *(const i32x4*)(qp + 32 * cq + 16 * hi) : i32x4{};
+                    s = mfma_i8_32x32x32(qa, kop[cq], s);
+                }
+#pragma unroll
+                for (int sd = 0; sd < 8; ++sd) {
+                    const bf16x8 ga =
+                        rok ? __builtin_bit_cast(bf16x8, *(const u16x8*)(gp + 16 * sd + 8 * hi)) : bf16x8{};
+                    dp = mfma_bf16_32x32x16(ga, vop[sd], dp);
+                }
+            }
+            bf16x8 pb[2], db[2];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int q0 = t0 + 8 * g + 4 * hi;  // queries q0 .. q0+3 of registers 4g..4g+3
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    const int qn = q0 + e;
+                    const bool ok = kok && qn < N;
+                    const float mq = ok ? a.mlog[bh * N + qn] : 0.f;
+                    const float Dq = ok ? a.dstat[bh * N + qn] : 0.f;
+                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], c, -mq)) : 0.f;
+                    pb[r >> 3][r & 7] = (__bf16)p;
+                    db[r >> 3][r & 7] = (__bf16)(p * (dp[r] - Dq) * sq);
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const int64_t off = (int64_t)(32 * dt + l32) * QBLK + 32 * qq + 16 * ks + 8 * hi;
+                    const bf16x8 ga = __builtin_bit_cast(bf16x8, *(const u16x8*)(dot + off));
+                    const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u16x8*)(qt + off));
+                    dva[dt] = mfma_bf16_32x32x16(ga, pb[ks], dva[dt]);
+                    dka[dt] = mfma_bf16_32x32x16(qa, db[ks], dka[dt]);
+                }
+        }
+    }
+    if (kok) {
+        float* vrow = a.dv + (bh * N + u) * HD;
+        float* krow = a.dk + (bh * N + u) * HD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 32 * dt + 8 * q4 + 4 * hi;
+                *(f32x4*)(vrow + d) = f32x4{dva[dt][4 * q4], dva[dt][4 * q4 + 1], dva[dt][4 * q4 + 2],
+                                            dva[dt][4 * q4 + 3]};
+                *(f32x4*)(krow + d) = f32x4{dka[dt][4 * q4] * a.sm, dka[dt][4 * q4 + 1] * a.sm,
+                                            dka[dt][4 * q4 + 2] * a.sm, dka[dt][4 * q4 + 3] * a.sm};
+            }
+    }
+}
+
+// ---- the linear branch ------------------------------------------------------
+// State rows (the forward's complement states and the gradient states alike):
+// row e of the transposed 128 x 128 matrix, channel d at position
+// pos(d) = 16(d/16) + 8((d>>2)&1) + 4(d>>3 & 1) + d%4, then the vector part at
+// the same positions (the order one lane of the 32x32 MFMA output holds rows).
+__device__ __forceinline__ int state_pos(int d) {
+    return (d & ~15) | (((d >> 2) & 1) << 3) | (((d >> 3) & 1) << 2) | (d & 3);
+}
+
+__device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ __forceinline__ float dphi_f(float x) { return x > 0.f ? 1.f : __expf(x); }
+
+constexpr int LB_CH = 16;    // tokens per chunk
+constexpr int LB_P = HD + 1;  // LDS pitch of the staged 128 x 128 matrix
+
+// Stage a state row as M[d][e] (pitch LB_P) and its vector part as vec[d].
+__device__ __forceinline__ void stage_state(const float* __restrict__ row, float* M, float* vec) {
+    for (int x = threadIdx.x; x < HD * HD; x += 256) {
+        const int e = x >> 7, p = x & 127;  // coalesced over the row
+        // position p holds channel d with state_pos(d) == p; the map is its own inverse
+        M[state_pos(p) * LB_P + e] = row[x];
+    }
+    for (int p = threadIdx.x; p < HD; p += 256) vec[state_pos(p)] = row[HD * HD + p];
+}
+
+// Per (head, query block): with H, z its forward complement state,
+// a = phi(q_t), den = a . z, o_l = a^T H / den, g = dO_t, dnum = g / den,
+// dden = -(g . o_l) / den: dq_t (+)= (H dnum + z dden) * phi'(q_t), and the
+// gradient state G^T[e][d] = sum_t dnum[e] a[d], w[d] = sum_t a[d] dden,
+// written in fp32 (gf, for the total) and as bf16 plus its bf16 rest (gs,
+// gs_lo: the GEMM's two stacks).
+__global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ dout,
+                                                           const float* __restrict__ hnon, int N,
+                                                           int nqb, int accumulate,
+                                                           float* __restrict__ dq,
+                                                           float* __restrict__ gf,
+                                                           uint16_t* __restrict__ gs,
+                                                           uint16_t* __restrict__ gs_lo) {
+    __shared__ float M[HD * LB_P];
+    __shared__ float zv[HD];
+    __shared__ float A[LB_CH][HD], G[LB_CH][HD], DN[LB_CH][HD], NUM[LB_CH][HD];
+    __shared__ float den[LB_CH], dden[LB_CH];
+    const int i = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    stage_state(hnon + (bh * nqb + i) * (int64_t)HS_ROW, M, zv);
+    // this thread's share of the gradient state: row e = tid/2, channels d0..d0+63
+    const int ge = tid >> 1, gd0 = 64 * (tid & 1);
+    float gacc[64];
+#pragma unroll
+    for (int x = 0; x < 64; ++x) gacc[x] = 0.f;
+    float wacc = 0.f;  // threads 0..127: w[tid]
+    const int nt = min(QBLK, N - i * QBLK);
+    for (int t0 = 0; t0 < nt; t0 += LB_CH) {
+        __syncthreads();  // the state is staged / the previous chunk is done
+        for (int x = tid; x < LB_CH * HD; x += 256) {
+            const int tt = x >> 7, d = x & 127;
+            const int tok = i * QBLK + t0 + tt;
+            const bool ok = t0 + tt < nt;
+            A[tt][d] = ok ? phi_f(bf2f(q[(bh * N + tok) * HD + d])) : 0.f;
+            G[tt][d] = ok ? bf2f(dout[(bh * N + tok) * HD + d]) : 0.f;
+        }
+        __syncthreads();
+        {  // num[t][e] = sum_d a[t][d] H[d][e]
+            const int e = tid & 127, h = tid >> 7;
+            for (int tt = h; tt < LB_CH; tt += 2) {
+                float acc = 0.f;
+                for (int d = 0; d < HD; ++d) acc = __builtin_fmaf(A[tt][d], M[d * LB_P + e], acc);
+                NUM[tt][e] = acc;
+            }
+        }
+        if (tid < LB_CH) {
+            float dn = 0.f;
+            for (int d = 0; d < HD; ++d) dn = __builtin_fmaf(A[tid][d], zv[d], dn);
+            den[tid] = t0 + tid < nt ? dn : 1.f;
+        }
+        __syncthreads();
+        if (tid < LB_CH) {
+            float go = 0.f;
+            for (int e = 0; e < HD; ++e) go = __builtin_fmaf(G[tid][e], NUM[tid][e], go);
+            dden[tid] = -go / (den[tid] * den[tid]);
+        }
+        for (int x = tid; x < LB_CH * HD; x += 256) {
+            const int tt = x >> 7, e = x & 127;
+            DN[tt][e] = G[tt][e] / den[tt];
+        }
+        __syncthreads();
+        {  // dq[t][d] (+)= (sum_e H[d][e] dnum[t][e] + z[d] dden[t]) * phi'(q[t][d])
+            const int d = tid & 127, h = tid >> 7;
+            for (int tt = h; tt < LB_CH; tt += 2) {
+                if (t0 + tt >= nt) continue;
+                float acc = zv[d] * dden[tt];
+                for (int e = 0; e < HD; ++e) acc = __builtin_fmaf(M[d * LB_P + e], DN[tt][e], acc);
+                const int64_t o = (bh * N + i * QBLK + t0 + tt) * HD + d;
+                const float g = acc * dphi_f(bf2f(q[o]));
+                dq[o] = accumulate ? dq[o] + g : g;
+            }
+            if (h == 0)
+                for (int tt = 0; tt < LB_CH; ++tt) wacc = __builtin_fmaf(A[tt][d], dden[tt], wacc);
+        }
+        for (int tt = 0; tt < LB_CH; ++tt) {
+            const float dn = DN[tt][ge];
+#pragma unroll
+            for (int x = 0; x < 64; ++x) gacc[x] = __builtin_fmaf(dn, A[tt][gd0 + x], gacc[x]);
+        }
+    }
+    float* fr = gf + (bh * nqb + i) * (int64_t)HS_ROW;
+    uint16_t* sr = gs + (bh * nqb + i) * (int64_t)HS_ROW;
+    uint16_t* lr = gs_lo + (bh * nqb + i) * (int64_t)HS_ROW;
+    auto put = [&](int64_t o, float x) {
+        const uint16_t h = f2bf(x);
+        fr[o] = x;
+        sr[o] = h;
+        lr[o] = f2bf(x - bf2f(h));
+    };
+#pragma unroll
+    for (int x = 0; x < 64; ++x) put((int64_t)ge * HD + state_pos(gd0 + x), gacc[x]);
+    if (tid < HD) put(HD * HD + state_pos(tid), wacc);
+}
+
+// Per (head, key block): with Gc, wc the gradient-state sums over the query
+// blocks that did not keep the block, for each key u: f = phi(k_u),
+// dk_u (+)= (Gc v_u + wc) * phi'(k_u), dv_u (+)= Gc^T f.
+__global__ __launch_bounds__(256, 1) void lin_bwd_k_kernel(const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v,
+                                                           const float* __restrict__ gc, int N,
+                                                           int nkb, int accumulate,
+                                                           float* __restrict__ dk,
+                                                           float* __restrict__ dv) {
+    __shared__ float M[HD * LB_P];
+    __shared__ float wv[HD];
+    __shared__ float F[LB_CH][HD], V[LB_CH][HD];
+    const int j = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    stage_state(gc + (bh * nkb + j) * (int64_t)HS_ROW, M, wv);
+    const int nk = min(KBLK, N - j * KBLK);
+    for (int u0 = 0; u0 < nk; u0 += LB_CH) {
+        __syncthreads();
+        for (int x = tid; x < LB_CH * HD; x += 256) {
+            const int uu = x >> 7, d = x & 127;
+            const bool ok = u0 + uu < nk;
+            const int64_t o = (bh * N + j * KBLK + u0 + uu) * HD + d;
+            F[uu][d] = ok ? phi_f(bf2f(k[o])) : 0.f;
+            V[uu][d] = ok ? bf2f(v[o]) : 0.f;
+        }
+        __syncthreads();
+        const int c = tid & 127, h = tid >> 7;
+        for (int uu = h; uu < LB_CH; uu += 2) {
+            if (u0 + uu >= nk) continue;
+            const int64_t o = (bh * N + j * KBLK + u0 + uu) * HD + c;
+            float gk = wv[c];  // channel d = c
+            for (int e = 0; e < HD; ++e) gk = __builtin_fmaf(M[c * LB_P + e], V[uu][e], gk);
+            gk *= dphi_f(bf2f(k[o]));
+            float gv = 0.f;  // channel e = c
+            for (int d = 0; d < HD; ++d) gv = __builtin_fmaf(M[d * LB_P + c], F[uu][d], gv);
+            dk[o] = accumulate ? dk[o] + gk : gk;
+            dv[o] = accumulate ? dv[o] + gv : gv;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+
+hipError_t launch_bwd_prep(const BwdArgs& a, const uint16_t* dout, uint16_t* kt16, uint16_t* qt16,
+                           uint16_t* dot, hipStream_t st) {
+    hipLaunchKernelGGL((transpose_tiles_kernel<int8_t, KBLK>), dim3(a.nkb, a.BH), dim3(256), 0, st,
+                       a.k_i8, a.N, a.nkb, kt16);
+    hipLaunchKernelGGL((transpose_tiles_kernel<int8_t, QBLK>), dim3(a.nqb, a.BH), dim3(256), 0, st,
+                       a.q_i8, a.N, a.nqb, qt16);
+    hipLaunchKernelGGL((transpose_tiles_kernel<uint16_t, QBLK>), dim3(a.nqb, a.BH), dim3(256), 0,
+                       st, dout, a.N, a.nqb, dot);
+    return hipGetLastError();
+}
+
+hipError_t launch_inv_lists(const int32_t* kidx, int keep, int64_t BH, int nqb, int nkb,
+                            uint16_t* lists, int32_t* counts, hipStream_t st) {
+    hipLaunchKernelGGL(inv_lists_kernel, dim3((nkb + 255) / 256, BH), dim3(256), 0, st, kidx, keep,
+                       nqb, nkb, lists, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_sparse(const BwdArgs& a, hipStream_t st) {
+    const int64_t nq = a.BH * a.nqb, nk = a.BH * a.nkb;
+    if (a.kidx) {
+        hipLaunchKernelGGL(dq_kernel<false>, dim3((unsigned)nq), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(dkdv_kernel<false>, dim3((unsigned)nk), dim3(128), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(dq_kernel<true>, dim3((unsigned)nq), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(dkdv_kernel<true>, dim3((unsigned)nk), dim3(128), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_lin_bwd_q(const uint16_t* q, const uint16_t* dout, const float* hnon, int64_t BH,
+                            int N, int accumulate, float* dq, float* gf, uint16_t* gs,
+                            uint16_t* gs_lo, hipStream_t st) {
+    const int nqb = (N + QBLK - 1) / QBLK;
+    hipLaunchKernelGGL(lin_bwd_q_kernel, dim3(nqb, BH), dim3(256), 0, st, q, dout, hnon, N, nqb,
+                       accumulate, dq, gf, gs, gs_lo);
+    return hipGetLastError();
+}
+
+hipError_t launch_lin_bwd_k(const uint16_t* k, const uint16_t* v, const float* gc, int64_t BH,
+                            int N, int accumulate, float* dk, float* dv, hipStream_t st) {
+    const int nkb = (N + KBLK - 1) / KBLK;
+    hipLaunchKernelGGL(lin_bwd_k_kernel, dim3(nkb, BH), dim3(256), 0, st, k, v, gc, N, nkb,
+                       accumulate, dk, dv);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero(float* p, int64_t n, hipStream_t st) {
+    const int64_t wg = std::min<int64_t>((n + 255) / 256, 65536);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)wg), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace ssa

@@ -28,17 +28,66 @@ constexpr int LIN_GROUP = 16;    // key blocks per linear-states workgroup
 constexpr int GEMM_KALIGN = 32;  // the complement GEMM's key-block count is padded to this
 // kpart (may be null): also write the per-block K sums of the K mean, and
 // kbarT (may be null) the pooled key means, from the same pass over K
+// hs_lo (may be null): also the bf16 rests of the states (see linear.hip)
 hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH, int N,
-                                uint16_t* vt, uint16_t* hs, float* hpart, float* htot,
-                                float* kpart, float* kbarT, int ldk, hipStream_t st);
+                                uint16_t* vt, uint16_t* hs, uint16_t* hs_lo, float* hpart,
+                                float* htot, float* kpart, float* kbarT, int ldk, hipStream_t st);
 hipError_t launch_vt_only(const uint16_t* k, const uint16_t* v, int64_t BH, int N, uint16_t* vt,
                           float* kpart, float* kbarT, int ldk, hipStream_t st);
 // bytes of the complement GEMM's selection rows (msel) for nkbp padded key blocks
 size_t msel_bytes(int64_t BH, int64_t nqb, int64_t nkbp);
 // workgroups of the complement GEMM per head (256 threads each)
 int64_t complement_tiles_per_head(int64_t nqb);
-hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, const float* htot,
-                             int64_t BH, int N, uint32_t* msel, float* hnon, hipStream_t st);
+// hs_lo (may be null): a second pass with the states' bf16 rests
+hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs,
+                             const uint16_t* hs_lo, const float* htot, int64_t BH, int N,
+                             uint32_t* msel, float* hnon, hipStream_t st);
+
+// as launch_complement, with the selection rows taken from lists instead of
+// kidx: row r (of nrows) selects the reduction entries lists[bh][r][0..counts)
+// (of nred); the stack has nred rows; out gets nrows rows
+hipError_t launch_complement_lists(const uint16_t* lists, const int32_t* counts, int nrows,
+                                   int nred, int complement, const uint16_t* stack,
+                                   const uint16_t* stack_lo, const float* total, int64_t BH,
+                                   uint32_t* msel, float* out, hipStream_t st);
+// H_total-style sums: out[bh][n] = sum over groups g, in order, of part[bh][g][n]
+hipError_t launch_state_total(const float* part, int ngroups, int64_t BH, float* out,
+                              hipStream_t st);
+
+// bwd.hip
+struct BwdArgs {
+    const int8_t* q_i8;
+    const float* q_scale;
+    const int8_t* k_i8;
+    const float* k_scale;
+    const uint16_t* v;       // raw bf16 V [BH][N][128]
+    const uint16_t* dout;    // bf16 dL/dO [BH][N][128]
+    const uint16_t* kt16;    // bf16 k_i8, channel-first per key block [BH][nkb][128][64]
+    const uint16_t* qt16;    // bf16 q_i8, channel-first per query block [BH][nqb][128][128]
+    const uint16_t* dot;     // dout, channel-first per query block [BH][nqb][128][128]
+    const int32_t* kidx;     // [BH][nqb][keep] or null (dense)
+    int keep;
+    const uint16_t* lists;   // [BH][nkb][nqb]: query blocks that kept each key block
+    const int32_t* counts;   // [BH][nkb]
+    int N, nqb, nkb;
+    int64_t BH;
+    float K32;               // fl32(sm * log2 e)
+    float sm;
+    const float* mlog;       // [BH][N] m + log2(l) of the forward
+    const float* dstat;      // [BH][N] dO . o_s
+    float *dq, *dk, *dv;     // fp32 [BH][N][128]
+};
+hipError_t launch_bwd_prep(const BwdArgs& a, const uint16_t* dout, uint16_t* kt16, uint16_t* qt16,
+                           uint16_t* dot, hipStream_t st);
+hipError_t launch_inv_lists(const int32_t* kidx, int keep, int64_t BH, int nqb, int nkb,
+                            uint16_t* lists, int32_t* counts, hipStream_t st);
+hipError_t launch_bwd_sparse(const BwdArgs& a, hipStream_t st);
+hipError_t launch_lin_bwd_q(const uint16_t* q, const uint16_t* dout, const float* hnon, int64_t BH,
+                            int N, int accumulate, float* dq, float* gf, uint16_t* gs,
+                            uint16_t* gs_lo, hipStream_t st);
+hipError_t launch_lin_bwd_k(const uint16_t* k, const uint16_t* v, const float* gc, int64_t BH,
+                            int N, int accumulate, float* dk, float* dv, hipStream_t st);
+hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
 
 // w8a8.hip
 hipError_t launch_w8a8_quant(const uint16_t* x, int rows, int cols, int8_t* q, float* scale,
@@ -66,6 +115,11 @@ struct AttnArgs {
     const float* hnon;     // [BH][nqb][HS_ROW] complement states, or null
     uint16_t* out;
     float* out32;
+    // backward row statistics (both set: the statistics pass, no output):
+    // mlog[bh][t] = m + log2(l), dstat[bh][t] = dO . o_s, from dout
+    const uint16_t* dout;
+    float* mlog;
+    float* dstat;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_qk_tiles(const int8_t* q_i8, const int8_t* k_i8, int64_t BH, int N,

@@ -44,12 +44,17 @@ constexpr int LS_IT = KBLK * HD / 8 / LS_THREADS;     // 16-byte chunks per thre
 // transposed with row pitch ldk; skipped when kbarT is null). Raw K is staged
 // token-major in LDS and one thread adds one channel's column in order, so
 // both equal what colsum_kernel<64, 0> writes, bit for bit.
-template <bool STATES, bool SUMS>
+//
+// LO: also write hs_lo = bf16(state - hs), the bf16 rest of each state entry,
+// so that a product taken with both stacks carries ~16 significant bits (the
+// backward's states, whose cancellations the bf16 rounding alone would show).
+template <bool STATES, bool SUMS, bool LO = false>
 __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v, int N,
                                                             int nkb, int ngroups,
                                                             uint16_t* __restrict__ vt,
                                                             uint16_t* __restrict__ hs,
+                                                            uint16_t* __restrict__ hs_lo,
                                                             float* __restrict__ hpart,
                                                             float* __restrict__ kpart,
                                                             float* __restrict__ kbarT, int ldk) {
@@ -196,10 +201,15 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
                 const int dt = 2 * dh + t;
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
-                    u16x8 o8;
+                    u16x8 o8, l8;
 #pragma unroll
-                    for (int x = 0; x < 8; ++x) o8[x] = f2bf(acc[t][8 * rb + x]);
+                    for (int x = 0; x < 8; ++x) {
+                        o8[x] = f2bf(acc[t][8 * rb + x]);
+                        if (LO) l8[x] = f2bf(acc[t][8 * rb + x] - bf2f(o8[x]));
+                    }
                     *(u16x8*)(hrow + e * HD + 16 * (2 * dt + rb) + 8 * hi) = o8;
+                    if (LO)
+                        *(u16x8*)(hs_lo + (hrow - hs) + e * HD + 16 * (2 * dt + rb) + 8 * hi) = l8;
                 }
                 tot[t] += acc[t];
             }
@@ -207,10 +217,15 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
                 if (l32 == 0) {  // z rows d = 32eg + ..., every column equal
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb) {
-                        u16x8 o8;
+                        u16x8 o8, l8;
 #pragma unroll
-                        for (int x = 0; x < 8; ++x) o8[x] = f2bf(accz[8 * rb + x]);
+                        for (int x = 0; x < 8; ++x) {
+                            o8[x] = f2bf(accz[8 * rb + x]);
+                            if (LO) l8[x] = f2bf(accz[8 * rb + x] - bf2f(o8[x]));
+                        }
                         *(u16x8*)(hrow + HD * HD + 16 * (2 * eg + rb) + 8 * hi) = o8;
+                        if (LO)
+                            *(u16x8*)(hs_lo + (hrow - hs) + HD * HD + 16 * (2 * eg + rb) + 8 * hi) = l8;
                     }
                 }
                 totz += accz;
@@ -315,21 +330,35 @@ __device__ __forceinline__ u32x4 sel_entry(uint32_t e) {
 // (kp = ks/2) and stored [bh][kp][i][hi][ks&1]: the 16 bytes of one row and
 // pair are contiguous, and so are the rows of one pair. Key blocks past nkb,
 // and the second step of an unpaired last one, select nothing.
+// Rows come from kidx (keep entries each) or, for the backward's transposed
+// selection, from lists (counts[bh][row] entries each, row length ld).
 constexpr int SEL_MAX_WORDS = SSA_MAX_N / KBLK / 32 + 2;
+template <bool LISTS>
 __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ kidx, int keep,
+                                                   const uint16_t* __restrict__ lists,
+                                                   const int32_t* __restrict__ counts, int ld,
                                                    int nqb, int nkb, int nks, int complement,
                                                    uint32_t* __restrict__ msel) {
     __shared__ uint32_t bits[SEL_MAX_WORDS];
     const int64_t bh = blockIdx.y;
     const int i = blockIdx.x;
     const int nkp = (nks + 1) / 2;
-    const int32_t* src = kidx + (bh * nqb + i) * (int64_t)keep;
     for (int w = threadIdx.x; w < 2 * nkp; w += 256) bits[w] = 0;
     __syncthreads();
     // kept block indices are clamped into [0, nkb)
-    for (int a = threadIdx.x; a < keep; a += 256) {
-        const int j = min(max(src[a], 0), nkb - 1);
-        atomicOr(&bits[j >> 5], 1u << (j & 31));
+    if (LISTS) {
+        const uint16_t* src = lists + (bh * nqb + i) * (int64_t)ld;
+        const int n = counts[bh * nqb + i];
+        for (int a = threadIdx.x; a < n; a += 256) {
+            const int j = min((int)src[a], nkb - 1);
+            atomicOr(&bits[j >> 5], 1u << (j & 31));
+        }
+    } else {
+        const int32_t* src = kidx + (bh * nqb + i) * (int64_t)keep;
+        for (int a = threadIdx.x; a < keep; a += 256) {
+            const int j = min(max(src[a], 0), nkb - 1);
+            atomicOr(&bits[j >> 5], 1u << (j & 31));
+        }
     }
     __syncthreads();
     if (complement) {
@@ -405,7 +434,7 @@ size_t msel_bytes(int64_t BH, int64_t nqb, int64_t nkbp) {
 __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     const uint32_t* __restrict__ msel, const uint16_t* __restrict__ hs,
     const float* __restrict__ htot, int64_t BH, int nqb, int nkb, int nkbp, int complement,
-    float* __restrict__ hnon) {
+    int accum, float* __restrict__ hnon) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[CG_STAGES * CG_STAGE + CG_LUT];
     uint8_t* lut = smem + CG_STAGES * CG_STAGE;
     const int nnt = HS_ROW / CG_TN, nmt = (nqb + CG_TM - 1) / CG_TM;
@@ -540,7 +569,10 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
             for (int q = 0; q < 4; ++q) {
                 const f32x16& a = acc[ib][nb];
                 const f32x4 sum = f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-                *(f32x4*)(dst + 32 * nb + 8 * q) = complement ? sum : ht[nb][q] - sum;
+                f32x4* o = (f32x4*)(dst + 32 * nb + 8 * q);
+                // accum: a second pass (the stack's bf16 rests) onto the first
+                const f32x4 base = accum ? *o : (complement ? f32x4{} : ht[nb][q]);
+                *o = complement ? base + sum : base - sum;
             }
     }
 }
@@ -548,16 +580,20 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
 // ---------------------------------------------------------------------------
 
 hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH, int N,
-                                uint16_t* vt, uint16_t* hs, float* hpart, float* htot,
-                                float* kpart, float* kbarT, int ldk, hipStream_t st) {
+                                uint16_t* vt, uint16_t* hs, uint16_t* hs_lo, float* hpart,
+                                float* htot, float* kpart, float* kbarT, int ldk, hipStream_t st) {
     const int nkb = (N + KBLK - 1) / KBLK;
     const int ngroups = (nkb + LIN_GROUP - 1) / LIN_GROUP;
     if (kpart)
         hipLaunchKernelGGL((linear_states_kernel<true, true>), dim3(ngroups, BH), dim3(LS_THREADS),
-                           0, st, k, v, N, nkb, ngroups, vt, hs, hpart, kpart, kbarT, ldk);
+                           0, st, k, v, N, nkb, ngroups, vt, hs, nullptr, hpart, kpart, kbarT, ldk);
+    else if (hs_lo)
+        hipLaunchKernelGGL((linear_states_kernel<true, false, true>), dim3(ngroups, BH),
+                           dim3(LS_THREADS), 0, st, k, v, N, nkb, ngroups, vt, hs, hs_lo, hpart,
+                           nullptr, nullptr, 0);
     else
         hipLaunchKernelGGL((linear_states_kernel<true, false>), dim3(ngroups, BH), dim3(LS_THREADS),
-                           0, st, k, v, N, nkb, ngroups, vt, hs, hpart, nullptr, nullptr, 0);
+                           0, st, k, v, N, nkb, ngroups, vt, hs, nullptr, hpart, nullptr, nullptr, 0);
     hipLaunchKernelGGL(htot_kernel, dim3((HS_ROW + 255) / 256, BH), dim3(256), 0, st, hpart, ngroups,
                        htot);
     return hipGetLastError();
@@ -570,27 +606,55 @@ hipError_t launch_vt_only(const uint16_t* k, const uint16_t* v, int64_t BH, int 
         const int ngroups = (nkb + LIN_GROUP - 1) / LIN_GROUP;
         hipLaunchKernelGGL((linear_states_kernel<false, true>), dim3(ngroups, BH),
                            dim3(LS_THREADS), 0, st, k, v, N, nkb, ngroups, vt, nullptr, nullptr,
-                           kpart, kbarT, ldk);
+                           nullptr, kpart, kbarT, ldk);
     } else {
         hipLaunchKernelGGL((linear_states_kernel<false, false>), dim3(nkb, BH), dim3(LS_THREADS),
                            0, st, nullptr, v, N, nkb, nkb, vt, nullptr, nullptr, nullptr, nullptr,
-                           0);
+                           nullptr, 0);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs, const float* htot,
-                             int64_t BH, int N, uint32_t* msel, float* hnon, hipStream_t st) {
+hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs,
+                             const uint16_t* hs_lo, const float* htot, int64_t BH, int N,
+                             uint32_t* msel, float* hnon, hipStream_t st) {
     const int nqb = (N + QBLK - 1) / QBLK, nkb = (N + KBLK - 1) / KBLK;
     const int nkbp = (nkb + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
     // sum whichever of the kept and the non-kept sets is smaller
     const int complement = 2 * keep > nkb ? 1 : 0;
-    hipLaunchKernelGGL(msel_kernel, dim3(nqb, BH), dim3(256), 0, st, kidx, keep, nqb, nkb,
-                       nkbp / GEMM_KALIGN, complement, msel);
+    hipLaunchKernelGGL(msel_kernel<false>, dim3(nqb, BH), dim3(256), 0, st, kidx, keep, nullptr,
+                       nullptr, 0, nqb, nkb, nkbp / GEMM_KALIGN, complement, msel);
     const int64_t total = BH * complement_tiles_per_head(nqb);
     const int64_t grid = (total + 7) / 8 * 8;
     hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel, hs, htot,
-                       BH, nqb, nkb, nkbp, complement, hnon);
+                       BH, nqb, nkb, nkbp, complement, 0, hnon);
+    if (hs_lo)
+        hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel,
+                           hs_lo, htot, BH, nqb, nkb, nkbp, complement, 1, hnon);
+    return hipGetLastError();
+}
+
+hipError_t launch_complement_lists(const uint16_t* lists, const int32_t* counts, int nrows,
+                                   int nred, int complement, const uint16_t* stack,
+                                   const uint16_t* stack_lo, const float* total, int64_t BH,
+                                   uint32_t* msel, float* out, hipStream_t st) {
+    const int nredp = (nred + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
+    hipLaunchKernelGGL(msel_kernel<true>, dim3(nrows, BH), dim3(256), 0, st, nullptr, 0, lists,
+                       counts, nred, nrows, nred, nredp / GEMM_KALIGN, complement, msel);
+    const int64_t tiles = BH * complement_tiles_per_head(nrows);
+    const int64_t grid = (tiles + 7) / 8 * 8;
+    hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel, stack,
+                       total, BH, nrows, nred, nredp, complement, 0, out);
+    if (stack_lo)
+        hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel,
+                           stack_lo, total, BH, nrows, nred, nredp, complement, 1, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_total(const float* part, int ngroups, int64_t BH, float* out,
+                              hipStream_t st) {
+    hipLaunchKernelGGL(htot_kernel, dim3((HS_ROW + 255) / 256, BH), dim3(256), 0, st, part,
+                       ngroups, out);
     return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ typedef struct ssa_shape {
     int64_t B, H, N, D;
 } ssa_shape;
 
-enum { SSA_OP_QUANT = 0, SSA_OP_MASK = 1, SSA_OP_ATTN = 2, SSA_OP_STEP = 3 };
+enum { SSA_OP_QUANT = 0, SSA_OP_MASK = 1, SSA_OP_ATTN = 2, SSA_OP_STEP = 3, SSA_OP_BWD = 4 };
 enum { SSA_BRANCH_SPARSE = 1, SSA_BRANCH_LINEAR = 2 };
 
 #define SSA_HEAD_DIM 128
@@ -205,6 +205,38 @@ ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int8_t* k_i8, float* k_scale, float* k_mean, int32_t* kidx,
                         uint8_t* mask, uint16_t* out, float* out_f32, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sage_sla_attn_bwd -- SageSLA backward: the gradients of a loss L with
+ * respect to Q, K and V given dL/dO of sage_sla_attn_fwd's output, for
+ * training the sparse-linear attention (page 5: SLA is trainable and is
+ * fine-tuned; training guide, "SLA Adaptation Fine-tuning").
+ * Readings: the 8-bit quantizer passes gradients straight through and the
+ * block selection is held fixed. Sparse branch: with the forward's P over the
+ * kept keys (recomputed from the exact int32 scores, normalized with the
+ * forward's m + log2(l)) and D = dO . o_s per query row, dS = P (dP - D),
+ * dP = dO . v:  dQ = sm dS K', dK = sm dS^T Q', dV = P^T dO, with Q' and K'
+ * the dequantized quantized operands (q_scale q_i8, k_scale k_i8); K's mean
+ * needs no term (each row of dS sums to zero). Linear branch: the exact
+ * gradient of phi(q)^T H_i / phi(q)^T z_i over the non-kept blocks (phi =
+ * elu + 1 on raw Q, K). Arithmetic: int8 scores exact; P and dS rounded to
+ * bf16 for the bf16 matrix-core products (fp32 accumulation); the linear
+ * branch in fp32 (its states summed as the forward's, bf16 stack with an fp32
+ * total). Relative L2 error against the exact gradient ~1e-3.
+ *   q, k, v, q_i8..k_scale, kidx, keep, branches, sm_scale: as for
+ *                     sage_sla_attn_fwd (the same values the forward used)
+ *   dout         in : bf16 [B,H,N,D], dL/d(out)
+ *   dq, dk, dv   out: fp32 [B,H,N,D] (both branches' gradients summed)
+ *   ws: ssa_workspace_bytes(SSA_OP_BWD, s, keep, branches) bytes, 256-byte
+ *       aligned (the forward's workspace plus the backward's).
+ * Errors as for the entry points above.
+ */
+ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             ssa_shape s, const int8_t* q_i8, const float* q_scale,
+                             const int8_t* k_i8, const float* k_scale, const int32_t* kidx,
+                             int64_t keep, int branches, float sm_scale, const uint16_t* dout,
+                             float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* ---------------------------------------------------------------------------
  * sage_qk_int32_tiles -- test export of raw int32 score tiles computed by the

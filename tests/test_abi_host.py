@@ -24,6 +24,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("sage_quant_qk", "sla_block_mask", "sage_sla_attn_fwd", "sage_sla_fwd",
+              "sage_sla_attn_bwd", "sage_quant_qk_noalloc",
               "sage_qk_int32_tiles", "w8a8_quant", "w8a8_gemm",
               "ssa_workspace_bytes", "ssa_keep_blocks", "ssa_status_str", "ssa_last_error",
               "ssa_num_q_blocks", "ssa_num_k_blocks"):
@@ -198,6 +199,32 @@ def test_step_rejects_bad_arguments():
     assert call(ws=None) == 3
     assert call(n=1 << 10) == 3
     assert call(ws=_p(9 * GB + 16)) == 3  # workspace misaligned
+
+
+def test_bwd_rejects_bad_arguments():
+    L = _L()
+    GB = 1 << 30
+    s = _shape(N=1000)  # 16 key blocks
+
+    def call(kidx=_p(8 * GB), keep=4, branches=3, sm=0.0, dq=_p(9 * GB), ws=_p(12 * GB),
+             n=1 << 34, dout=_p(7 * GB)):
+        return L.sage_sla_attn_bwd(_p(0), _p(GB), _p(2 * GB), s, _p(3 * GB), _p(4 * GB),
+                                   _p(5 * GB), _p(6 * GB), kidx, keep, branches, sm, dout, dq,
+                                   _p(10 * GB), _p(11 * GB), ws, n, None)
+
+    assert call(branches=0) == 1 and call(branches=4) == 1
+    assert call(keep=0) == 1 and call(keep=17) == 1
+    assert call(kidx=None) == 1  # dense needs keep == Nkb
+    assert call(sm=float("nan")) == 1
+    assert call(dout=None) == 1
+    assert call(dq=_p(9 * GB + 8)) == 1  # misaligned
+    assert call(dq=_p(7 * GB)) == 1  # dq aliases dout
+    assert b"overlap" in L.ssa_last_error()
+    assert call(ws=None) == 3
+    assert call(n=1 << 10) == 3
+    s2 = _shape(N=1000)
+    assert L.ssa_workspace_bytes(ssa.OP_BWD, s2, 4, 3) > L.ssa_workspace_bytes(ssa.OP_BWD, s2, 4, 1)
+    assert L.ssa_workspace_bytes(ssa.OP_BWD, s2, 16, 3) == L.ssa_workspace_bytes(ssa.OP_BWD, s2, 16, 1)
 
 
 def test_tiles_reject_bad_count():
