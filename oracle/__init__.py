@@ -60,6 +60,8 @@ def lib():
                                               C.c_double, _p]),
             "orc_w8a8_quant": (None, [_p, _i64, _i64, _p, _p, C.c_int]),
             "orc_w8a8_gemm": (None, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, C.c_int]),
+            "orc_w8a8_gemm_f64": (None, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _p,
+                                         C.c_int]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -379,3 +381,22 @@ def w8a8_gemm(xq, sx, wq, sw, rows=None, nthreads=None, bias=None):
     lib().orc_w8a8_gemm(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(bias), M, N, K, _ptr(rows),
                         len(rows), _ptr(y), nthreads or threads())
     return y
+
+
+def w8a8_gemm_f64(xq, sx, wq, sw, rows=None, nthreads=None, bias=None):
+    """(y, yabs) fp64 [len(rows)][N]: the quantized product dequantized in
+    fp64, and the sum of its terms' magnitudes."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    sx = np.ascontiguousarray(sx, dtype=np.float32)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    y = np.empty((len(rows), N))
+    ya = np.empty((len(rows), N))
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+    lib().orc_w8a8_gemm_f64(_ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(bias), M, N, K, _ptr(rows),
+                            len(rows), _ptr(y), _ptr(ya), nthreads or threads())
+    return y, ya

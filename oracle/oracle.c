@@ -694,6 +694,47 @@ void orc_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const fl
     orc_parallel_for(R, nthreads, w8_gemm_task, &c);
 }
 
+/* The same product with the dequantization carried in fp64 (the plainest
+ * exact reading of Pillar Three's block dequantization): y64 = sum over kb of
+ * (double)I_kb * (double)sx * (double)sw, plus the bias; yabs = sum over kb of
+ * |I_kb| * sx * sw, the scale of the terms (for error bounds). */
+typedef struct {
+    const int8_t *xq, *wq;
+    const float *sx, *sw, *bias;
+    int64_t M, N, K;
+    const int64_t* rows;
+    double *y, *yabs;
+} w8_f64_ctx;
+
+static void w8_f64_task(void* vctx, int64_t r) {
+    w8_f64_ctx* c = (w8_f64_ctx*)vctx;
+    int64_t m = c->rows[r], nkb = c->K / ORC_W8_BLK, mb = m / ORC_W8_BLK;
+    const int8_t* xr = c->xq + m * c->K;
+    for (int64_t n = 0; n < c->N; ++n) {
+        const int8_t* wr = c->wq + n * c->K;
+        int64_t nb = n / ORC_W8_BLK;
+        double y = 0.0, ya = 0.0;
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+            int64_t acc = 0;
+            for (int64_t k = kb * ORC_W8_BLK; k < (kb + 1) * ORC_W8_BLK; ++k)
+                acc += (int64_t)xr[k] * (int64_t)wr[k];
+            double s = (double)c->sx[mb * nkb + kb] * (double)c->sw[nb * nkb + kb];
+            y += (double)acc * s;
+            ya += fabs((double)acc) * s;
+        }
+        if (c->bias) y += (double)c->bias[n];
+        c->y[r * c->N + n] = y;
+        c->yabs[r * c->N + n] = ya;
+    }
+}
+
+void orc_w8a8_gemm_f64(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                       const float* bias, int64_t M, int64_t N, int64_t K, const int64_t* rows,
+                       int64_t R, double* y, double* yabs, int nthreads) {
+    w8_f64_ctx c = {xq, wq, sx, sw, bias, M, N, K, rows, y, yabs};
+    orc_parallel_for(R, nthreads, w8_f64_task, &c);
+}
+
 /* ------------------------------------------------------------------------ */
 /* SageSLA backward (page 5, "What is TurboDiffusion?" and the training      */
 /* guide: the sparse-linear attention is trainable and is fine-tuned). The   */

@@ -173,6 +173,13 @@ void orc_w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* wq, const fl
                    const float* bias /*[N] or NULL*/, int64_t M, int64_t N, int64_t K,
                    const int64_t* rows, int64_t R, float* y /*[R][N]*/, int nthreads);
 
+/* The same rows with the dequantization in fp64: y = sum over kb of
+ * (double)I_kb * (double)sx * (double)sw (+ bias); yabs = sum over kb of
+ * |I_kb| * sx * sw. */
+void orc_w8a8_gemm_f64(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                       const float* bias, int64_t M, int64_t N, int64_t K, const int64_t* rows,
+                       int64_t R, double* y, double* yabs, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

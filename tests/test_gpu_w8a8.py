@@ -3,7 +3,11 @@ Pillar Three: INT8 weights and activations, block-wise 128x128) against the
 CPU oracle: quantized tensors and scales bit-exact, and the fp32 product
 bit-exact too (the oracle follows the same exact int32 block sums and the
 same fmaf chain over the K blocks); the bf16 output is the RNE of the fp32
-one."""
+one. Beside the bit-exact chain, the product is also gated against the
+dequantization carried in fp64 (exact int32 block sums times the fp64 product
+of the two scales): each of the nkb = K/128 steps of the fp32 chain rounds
+twice (the scale product and the fma), so |y32 - y64| <= (nkb + 2) 2^-24
+sum_kb |I_kb| sx sw per element."""
 import numpy as np
 import pytest
 import torch
@@ -120,3 +124,27 @@ def test_w8a8_beyond_32bit_offsets(orc):
     want16 = torch.from_numpy(got).to(torch.bfloat16)
     assert torch.equal(y[torch.from_numpy(rows).to(DEV)].cpu(), want16)
     say(f"[w8a8 max] {len(rows)} sampled rows bit-exact")
+
+
+@pytest.mark.parametrize("M,N,K,full", [(1000, 512, 5120, False), (75600, 5120, 5120, True)])
+def test_w8a8_gemm_within_the_fp64_dequantization_bound(orc, M, N, K, full):
+    if full:
+        x, w = make_linear_workload(LINEAR_WORKLOADS["w8a8_m75600_k5120_n5120"])
+    else:
+        x, w = make_linear(M, N, K, seed=13, outliers=True)
+    say(f"[w8a8 fp64] M={M} N={N} K={K}")
+    xq, sx, oxq, osx = _check_quant(orc, x, "x")
+    wq, sw, owq, osw = _check_quant(orc, w, "w")
+    y, y32 = ssa.w8a8_gemm(xq, sx, wq, sw, return_f32=True)
+    torch.cuda.synchronize()
+    rows = (np.unique(np.concatenate([np.arange(0, 4), np.arange(M - 4, M),
+                                      np.random.default_rng(1).integers(0, M, 24)]))
+            if full else np.arange(M))
+    y64, yabs = orc.w8a8_gemm_f64(oxq, osx, owq, osw, rows=rows)
+    got = y32[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    bound = (K // 128 + 2) * 2.0**-24 * yabs
+    err = np.abs(got - y64)
+    assert np.all(err <= bound), f"max excess {(err - bound).max():.3e}"
+    rel = np.linalg.norm(got - y64) / np.linalg.norm(y64)
+    say(f"    rows={len(rows)} rel-L2 vs fp64 = {rel:.2e}, max err / bound = {(err / bound).max():.3f}")
+

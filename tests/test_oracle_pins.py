@@ -794,3 +794,29 @@ def test_backward_invariants(orc):
     b = orc.sagesla_bwd(qb, kb, vb, quant, 0, gb, None, 1)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_w8a8_gemm_f64_is_the_exact_block_dequantization(orc):
+    # an int64 matmul per K block (numpy), times the fp64 product of the two
+    # fp32 scales, summed over blocks; and the fp32 chain stays within its
+    # rounding bound of it
+    M, N, K = 200, 256, 384
+    rng = np.random.default_rng(4)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((N, K)) * 0.05).astype(np.float32)).to(torch.bfloat16)
+    xq, sx = orc.w8a8_quant(_bits(x).reshape(M, K))
+    wq, sw = orc.w8a8_quant(_bits(w).reshape(N, K))
+    y, ya = orc.w8a8_gemm_f64(xq, sx, wq, sw)
+    want = np.zeros((M, N))
+    want_abs = np.zeros((M, N))
+    for kb in range(K // 128):
+        sl = slice(128 * kb, 128 * kb + 128)
+        I = xq[:, sl].astype(np.int64) @ wq[:, sl].astype(np.int64).T
+        s = sx[np.arange(M) // 128, kb].astype(np.float64)[:, None] * \
+            sw[np.arange(N) // 128, kb].astype(np.float64)[None, :]
+        want += I * s
+        want_abs += np.abs(I) * s
+    assert np.allclose(y, want, rtol=1e-13, atol=0) and np.allclose(ya, want_abs, rtol=1e-13)
+    y32 = orc.w8a8_gemm(xq, sx, wq, sw).astype(np.float64)
+    nkb = K // 128
+    assert np.all(np.abs(y32 - y) <= (nkb + 2) * 2.0**-24 * ya)
