@@ -365,6 +365,116 @@ def bench_w8a8(args):
     print(json.dumps(line), flush=True)
 
 
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def bench_bwd(args):
+    """The SageSLA backward (sage_sla_attn_bwd) on the benchmarked workload:
+    per step, the gradients of Q, K, V for a seeded dL/dO, from the forward's
+    quantized tensors and selection (computed once before timing). Useful work
+    = the four gradient products per computed block pair, 8*D*n_q*n_k
+    (dP, dV, dQ, dK; the recomputed scores and row statistics not counted)."""
+    import ctypes as C
+
+    import torch
+
+    import bit_sparse_attention_amd as ssa
+    from bit_sparse_attention_amd.workloads import BENCH_WORKLOAD, WORKLOADS, make_workload
+
+    w = WORKLOADS[args.workload or BENCH_WORKLOAD]
+    dev = torch.device("cuda:0")
+    print(f"# generating {w.name}", file=sys.stderr, flush=True)
+    q, k, v = make_workload(w)
+    plan = ssa.SageSLAPlan(w.B, w.H, w.N, w.topk, linear=True, device=dev)
+    plan.bind(q.to(dev), k.to(dev), v.to(dev))
+    plan.run()
+    g = torch.Generator().manual_seed(1)
+    dout = torch.randn(w.B, w.H, w.N, HEAD_DIM, generator=g).to(torch.bfloat16).to(dev)
+    grads = [torch.empty((w.B, w.H, w.N, HEAD_DIM), dtype=torch.float32, device=dev)
+             for _ in range(3)]
+    L = ssa._load()
+    ws_n = ssa.workspace_bytes(ssa.OP_BWD, plan.shape, plan.keep, plan.branches)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    p = lambda t: None if t is None else C.c_void_p(t.data_ptr())  # noqa: E731
+
+    def step():
+        st = L.sage_sla_attn_bwd(p(plan.q), p(plan.k), p(plan.v), plan.shape, p(plan.q_i8),
+                                 p(plan.q_scale), p(plan.k_i8), p(plan.k_scale), p(plan.kidx),
+                                 plan.keep, plan.branches, plan.sm_scale, p(dout),
+                                 *map(p, grads), p(ws), ws_n,
+                                 C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(L.ssa_last_error().decode())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    ev_ms = e0.elapsed_time(e1) / K
+    kidx_np = None if plan.dense else plan.kidx.cpu().numpy()
+    fwd_ops, _ = effective_ops(kidx_np, w.N, plan.nqb, plan.nkb, plan.dense, w.B * w.H)
+    ops = 2.0 * fwd_ops  # 8*D*n_q*n_k against the forward's 4*D*n_q*n_k
+    tflops = ops / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": "SageSLA backward ms/call + effective TFLOP/s (% bf16 MFMA peak), 14B-720p shape, 1 GPU",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "event_ms_per_step": ev_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 score recompute; bf16 x bf16 -> fp32 gradient products; fp32 linear branch",
+        "data": "synthetic (seeded; the forward's inputs, dL/dO ~ N(0,1))",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": HEAD_DIM,
+                   "topk": w.topk, "keep": plan.keep, "branches": "sparse+linear"
+                   if plan.branches == 3 else "sparse", "call": "sage_sla_attn_bwd"},
+        "effective_ops": ops,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "note": "whole backward call (statistics pass, prep, dq, dk/dv and linear "
+                             "kernels) against the bf16 peak; per-kernel times in profiles/"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from bit_sparse_attention_amd.workloads import bf16_bits, make_qkv
+
+        # one head, the first 100 query blocks (12800 tokens) at the same keep fraction
+        Ns = 12800
+        qs, ks_, vs = make_qkv(1, 1, Ns, HEAD_DIM, seed=0)
+        gs = torch.randn(1, 1, Ns, HEAD_DIM, generator=g).to(torch.bfloat16)
+        qb, kb, vb, gb = (bf16_bits(t).reshape(1, Ns, HEAD_DIM) for t in (qs, ks_, vs, gs))
+        nthreads = oracle.threads()
+        t0 = time.perf_counter()
+        quant = oracle.quant_qk(qb, kb, nthreads)[:4]
+        keep_s = oracle.keep_blocks(Ns, w.topk)
+        kh, _ = oracle.block_mask_head(qb, kb, 0, keep_s)
+        oracle.sagesla_bwd(qb, kb, vb, quant, 0, gb, kh, plan.branches, nthreads=nthreads)
+        ts = time.perf_counter() - t0
+        sops, _ = effective_ops(kh[None], Ns, (Ns + 127) // 128, (Ns + 63) // 64, False, 1)
+        t_full = ts * ops / (2.0 * sops)
+        line["cpu_baseline"] = {
+            "value": ops / t_full / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": (f"one head of {Ns} tokens at keep {keep_s} (quantization, mask and the "
+                       f"fp64 backward): {ts:.1f} s on {nthreads} threads (the job's CPU share) "
+                       f"of {_cpu_model()}, extrapolated by the computed-pair work to "
+                       f"{t_full:.0f} s for the workload"),
+        }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,6 +501,8 @@ def main():
                     help="command line recorded in the summary outputs")
     ap.add_argument("--w8a8", action="store_true",
                     help="benchmark the W8A8 linear layer instead (its own JSON line)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="benchmark the SageSLA backward instead (its own JSON line)")
     args = ap.parse_args()
     if args.pmc_summary or args.trace_summary or args.pmc_table:
         from bit_sparse_attention_amd.workloads import BENCH_WORKLOAD, LINEAR_BENCH_WORKLOAD
@@ -412,6 +524,9 @@ def main():
 
     if args.w8a8:
         bench_w8a8(args)
+        return
+    if args.bwd:
+        bench_bwd(args)
         return
 
     import torch

@@ -272,19 +272,31 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     }
 }
 
-// ---- dk, dv: one workgroup per (head, key block), 2 waves x 32 keys -------
-// Over the query blocks that kept the block (every block when dense), in
-// quarters of 32 queries. Per wave (keys 64j + 32w + l32, lane pair hi):
-//   S = Q . K^T     (int8; lane holds key l32, queries 8(r/4)+4hi+r%4 of the quarter)
-//   dP = dO . V^T   (bf16; same layout)
-//   dS = P (dP - D) sq
-//   dV^T += dO^T . P,  dK^T += Q^T . dS   (bf16; the A operands from the
-//                                          channel-first re-laid tiles, whose
-//                                          query order matches P's registers)
-// Operands come straight from global memory (the two waves share them
-// through the caches).
+// ---- dk, dv: one workgroup per (head, key block), 4 waves -----------------
+// Over the query blocks that kept the block (every block when dense). The K
+// and V tiles of the block sit in LDS for the whole workgroup. Per query
+// block, wave w first takes its 32 queries t (32w + ...) against all 64 keys:
+//   S = Q . K^T    (int8; lane holds key l32 (+32 for the second tile),
+//                   queries 8(r/4)+4hi+r%4 of the wave's 32)
+//   dP = dO . V^T  (bf16; same layout)
+//   P = 2^(S c - m'), dS = P (dP - D) sq
+// and stores P and dS in LDS as the next products' B fragments (their
+// registers already are: k = 16 queries in the re-laid order, n = keys). Then
+// wave w accumulates channels 32w .. 32w+31 of
+//   dV^T += dO^T . P,  dK^T += Q^T . dS
+// over all 128 queries, the A fragments from the channel-first re-laid tiles
+// (rows 32w.. only). Every input is read once per workgroup.
+constexpr int KV_K = KBLK * HD;        // int8 K tile, 64 rows of 128 B
+constexpr int KV_V = KBLK * HD * 2;    // bf16 V tile, 64 rows of 256 B
+constexpr int KV_F = 8 * 2 * 64 * 16;  // one fragment set: [8 query steps][2 key tiles][64 lanes] x 16 B
+
 template <bool DENSE>
-__global__ __launch_bounds__(128) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[KV_K + KV_V + 2 * KV_F];
+    uint8_t* kt = smem;
+    uint8_t* vt = smem + KV_K;
+    uint8_t* pf = smem + KV_K + KV_V;  // P fragments
+    uint8_t* df = pf + KV_F;           // dS fragments
     const int64_t item = blockIdx.x;
     if (item >= a.BH * a.nkb) return;
     const int64_t bh = item / a.nkb;
@@ -292,94 +304,133 @@ __global__ __launch_bounds__(128) void dkdv_kernel(BwdArgs a) {
     const int N = a.N, nqb = a.nqb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
               hi = lane >> 5;
-    const int u = j * KBLK + 32 * wave + l32;
-    const bool kok = u < N;
-    i32x4 kop[4];
-    bf16x8 vop[8];
-    {
-        const int8_t* kp = a.k_i8 + (bh * N + (kok ? u : 0)) * HD;
-        const uint16_t* vp = a.v + (bh * N + (kok ? u : 0)) * HD;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kop[c] = kok ? *(const i32x4*)(kp + 32 * c + 16 * hi) : i32x4{};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            vop[s] = kok ? __builtin_bit_cast(bf16x8, *(const u16x8*)(vp + 16 * s + 8 * hi)) : bf16x8{};
+    const int nval = min(KBLK, N - j * KBLK);
+    // the block's K (chunk c of key row r at slot c ^ swz8(r)) and V (chunk c
+    // of key row r at slot c ^ (r & 15)); rows past N re-read row N-1 (their
+    // P is zeroed)
+    for (int x = tid; x < KBLK * 8; x += 256) {
+        const int r = x >> 3, c = x & 7, rr = min(r, nval - 1);
+        *(i32x4*)(kt + r * 128 + 16 * (c ^ swz8(r))) =
+            *(const i32x4*)(a.k_i8 + (bh * N + (int64_t)j * KBLK + rr) * HD + 16 * c);
     }
+    for (int x = tid; x < KBLK * 16; x += 256) {
+        const int r = x >> 4, c = x & 15, rr = min(r, nval - 1);
+        *(u16x8*)(vt + r * 256 + 16 * (c ^ (r & 15))) =
+            *(const u16x8*)(a.v + (bh * N + (int64_t)j * KBLK + rr) * HD + 8 * c);
+    }
+    __syncthreads();
     const float sk = a.k_scale[bh * a.nkb + j];
-    f32x16 dva[4], dka[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) dva[dt] = dka[dt] = f32x16{};
+    f32x16 dva[2], dka[2];  // channels 32w + ..., key tiles 0, 1
+    dva[0] = dva[1] = dka[0] = dka[1] = f32x16{};
     const int cnt = DENSE ? nqb : a.counts[bh * a.nkb + j];
     const uint16_t* list = DENSE ? nullptr : a.lists + (bh * a.nkb + j) * (int64_t)nqb;
     for (int x = 0; x < cnt; ++x) {
         const int i = DENSE ? x : (int)list[x];
         const float sq = a.q_scale[bh * nqb + i];
         const float c = (sq * sk) * a.K32;
-        const uint16_t* dot = a.dot + (bh * nqb + i) * (int64_t)HD * QBLK;
-        const uint16_t* qt = a.qt16 + (bh * nqb + i) * (int64_t)HD * QBLK;
-#pragma unroll 1
-        for (int qq = 0; qq < 4; ++qq) {
-            const int t0 = i * QBLK + 32 * qq;
-            const int tr = t0 + l32;  // the query row this lane supplies
-            const bool rok = tr < N;
-            i32x16 s = i32x16{};
-            f32x16 dp = f32x16{};
-            {
-                const int8_t* qp = a.q_i8 + (bh * N + (rok ? tr : 0)) * HD;
-                const uint16_t* gp = a.dout + (bh * N + (rok ? tr : 0)) * HD;
+        const int tr = i * QBLK + 32 * wave + l32;  // the query row this lane supplies
+        const bool rok = tr < N;
+        i32x16 s[2];
+        f32x16 dp[2];
+        s[0] = s[1] = i32x16{};
+        dp[0] = dp[1] = f32x16{};
+        {
+            const int8_t* qp = a.q_i8 + (bh * N + (rok ? tr : 0)) * HD;
+            const uint16_t* gp = a.dout + (bh * N + (rok ? tr : 0)) * HD;
 #pragma unroll
-                for (int cq = 0; cq < 4; ++cq) {
-                    const i32x4 qa = rok ? *(const i32x4*)(qp + 32 * cq + 16 * hi) : i32x4{};
-                    s = mfma_i8_32x32x32(qa, kop[cq], s);
-                }
+            for (int cq = 0; cq < 4; ++cq) {
+                const i32x4 qa = rok ? *(const i32x4*)(qp + 32 * cq + 16 * hi) : i32x4{};
 #pragma unroll
-                for (int sd = 0; sd < 8; ++sd) {
-                    const bf16x8 ga =
-                        rok ? __builtin_bit_cast(bf16x8, *(const u16x8*)(gp + 16 * sd + 8 * hi)) : bf16x8{};
-                    dp = mfma_bf16_32x32x16(ga, vop[sd], dp);
+                for (int h = 0; h < 2; ++h) {
+                    const int key = 32 * h + l32;
+                    const i32x4 kb = *(const i32x4*)(kt + key * 128 + 16 * ((2 * cq + hi) ^ swz8(key)));
+                    s[h] = mfma_i8_32x32x32(qa, kb, s[h]);
                 }
             }
-            bf16x8 pb[2], db[2];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int q0 = t0 + 8 * g + 4 * hi;  // queries q0 .. q0+3 of registers 4g..4g+3
+            for (int sd = 0; sd < 8; ++sd) {
+                const bf16x8 ga =
+                    rok ? __builtin_bit_cast(bf16x8, *(const u16x8*)(gp + 16 * sd + 8 * hi)) : bf16x8{};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int key = 32 * h + l32;
+                    const bf16x8 vb =
+                        *(const bf16x8*)(vt + key * 256 + 16 * ((2 * sd + hi) ^ (key & 15)));
+                    dp[h] = mfma_bf16_32x32x16(ga, vb, dp[h]);
+                }
+            }
+        }
+        // P and dS, stored as fragment [query step 2w + r/8][key tile h][lane]
+        f32x16 pr[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float mq[4], Dq[4];
+            const int q0 = i * QBLK + 32 * wave + 8 * g + 4 * hi;  // rows 4g .. 4g+3
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = q0 + e < N;
+                mq[e] = ok ? a.mlog[bh * N + q0 + e] : 0.f;
+                Dq[e] = ok ? a.dstat[bh * N + q0 + e] : 0.f;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool kok = 32 * h + l32 < nval;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
-                    const int qn = q0 + e;
-                    const bool ok = kok && qn < N;
-                    const float mq = ok ? a.mlog[bh * N + qn] : 0.f;
-                    const float Dq = ok ? a.dstat[bh * N + qn] : 0.f;
-                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], c, -mq)) : 0.f;
-                    pb[r >> 3][r & 7] = (__bf16)p;
-                    db[r >> 3][r & 7] = (__bf16)(p * (dp[r] - Dq) * sq);
+                    const bool ok = kok && q0 + e < N;
+                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[h][r], c, -mq[e])) : 0.f;
+                    pr[h][r] = p;
+                    dp[h][r] = p * (dp[h][r] - Dq[e]) * sq;
                 }
             }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const int64_t off = (int64_t)(32 * dt + l32) * QBLK + 32 * qq + 16 * ks + 8 * hi;
-                    const bf16x8 ga = __builtin_bit_cast(bf16x8, *(const u16x8*)(dot + off));
-                    const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u16x8*)(qt + off));
-                    dva[dt] = mfma_bf16_32x32x16(ga, pb[ks], dva[dt]);
-                    dka[dt] = mfma_bf16_32x32x16(qa, db[ks], dka[dt]);
-                }
         }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 pb, db;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pb[e] = (__bf16)pr[h][8 * ks + e];
+                    db[e] = (__bf16)dp[h][8 * ks + e];
+                }
+                const int slot = ((2 * wave + ks) * 2 + h) * 64 + lane;
+                *(bf16x8*)(pf + 16 * slot) = pb;
+                *(bf16x8*)(df + 16 * slot) = db;
+            }
+        __syncthreads();
+        const uint16_t* dot = a.dot + (bh * nqb + i) * (int64_t)HD * QBLK;
+        const uint16_t* qt = a.qt16 + (bh * nqb + i) * (int64_t)HD * QBLK;
+        const int64_t arow = (int64_t)(32 * wave + l32) * QBLK + 8 * hi;
+#pragma unroll
+        for (int qs = 0; qs < 8; ++qs) {
+            const bf16x8 ga = __builtin_bit_cast(bf16x8, *(const u16x8*)(dot + arow + 16 * qs));
+            const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u16x8*)(qt + arow + 16 * qs));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int slot = (qs * 2 + h) * 64 + lane;
+                dva[h] = mfma_bf16_32x32x16(ga, *(const bf16x8*)(pf + 16 * slot), dva[h]);
+                dka[h] = mfma_bf16_32x32x16(qa, *(const bf16x8*)(df + 16 * slot), dka[h]);
+            }
+        }
+        __syncthreads();  // the next query block rewrites the fragments
     }
-    if (kok) {
+    // lane (key column l32 of tile h, hi) holds channels 32w + 8(r/4) + 4hi + r%4
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int u = j * KBLK + 32 * h + l32;
+        if (32 * h + l32 >= nval) continue;
         float* vrow = a.dv + (bh * N + u) * HD;
         float* krow = a.dk + (bh * N + u) * HD;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * dt + 8 * q4 + 4 * hi;
-                *(f32x4*)(vrow + d) = f32x4{dva[dt][4 * q4], dva[dt][4 * q4 + 1], dva[dt][4 * q4 + 2],
-                                            dva[dt][4 * q4 + 3]};
-                *(f32x4*)(krow + d) = f32x4{dka[dt][4 * q4] * a.sm, dka[dt][4 * q4 + 1] * a.sm,
-                                            dka[dt][4 * q4 + 2] * a.sm, dka[dt][4 * q4 + 3] * a.sm};
-            }
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = 32 * wave + 8 * q4 + 4 * hi;
+            *(f32x4*)(vrow + d) = f32x4{dva[h][4 * q4], dva[h][4 * q4 + 1], dva[h][4 * q4 + 2],
+                                        dva[h][4 * q4 + 3]};
+            *(f32x4*)(krow + d) = f32x4{dka[h][4 * q4] * a.sm, dka[h][4 * q4 + 1] * a.sm,
+                                        dka[h][4 * q4 + 2] * a.sm, dka[h][4 * q4 + 3] * a.sm};
+        }
     }
 }
 
@@ -570,10 +621,10 @@ hipError_t launch_bwd_sparse(const BwdArgs& a, hipStream_t st) {
     const int64_t nq = a.BH * a.nqb, nk = a.BH * a.nkb;
     if (a.kidx) {
         hipLaunchKernelGGL(dq_kernel<false>, dim3((unsigned)nq), dim3(256), 0, st, a);
-        hipLaunchKernelGGL(dkdv_kernel<false>, dim3((unsigned)nk), dim3(128), 0, st, a);
+        hipLaunchKernelGGL(dkdv_kernel<false>, dim3((unsigned)nk), dim3(256), 0, st, a);
     } else {
         hipLaunchKernelGGL(dq_kernel<true>, dim3((unsigned)nq), dim3(256), 0, st, a);
-        hipLaunchKernelGGL(dkdv_kernel<true>, dim3((unsigned)nk), dim3(128), 0, st, a);
+        hipLaunchKernelGGL(dkdv_kernel<true>, dim3((unsigned)nk), dim3(256), 0, st, a);
     }
     return hipGetLastError();
 }
