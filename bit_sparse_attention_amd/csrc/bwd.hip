@@ -446,25 +446,82 @@ __device__ __forceinline__ int state_pos(int d) {
 __device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 __device__ __forceinline__ float dphi_f(float x) { return x > 0.f ? 1.f : __expf(x); }
 
-constexpr int LB_CH = 16;    // tokens per chunk
-constexpr int LB_P = HD + 1;  // LDS pitch of the staged 128 x 128 matrix
+constexpr int LB_P = HD + 1;  // odd LDS pitch: row- and column-wise fragment reads hit distinct banks
+constexpr int LB_T = 64;      // tokens staged at a time
 
-// Stage a state row as M[d][e] (pitch LB_P) and its vector part as vec[d].
+// Stage a state row as M[d][e] (pitch LB_P) and its vector part as vec[d]:
+// every load of the thread is issued before the first LDS store.
 __device__ __forceinline__ void stage_state(const float* __restrict__ row, float* M, float* vec) {
-    for (int x = threadIdx.x; x < HD * HD; x += 256) {
-        const int e = x >> 7, p = x & 127;  // coalesced over the row
-        // position p holds channel d with state_pos(d) == p; the map is its own inverse
-        M[state_pos(p) * LB_P + e] = row[x];
+    const int tid = threadIdx.x;
+    f32x4 r[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) r[it] = *(const f32x4*)(row + 4 * (tid + 256 * it));
+    const f32x4 zr = tid < 32 ? *(const f32x4*)(row + HD * HD + 4 * tid) : f32x4{};
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int x4 = tid + 256 * it, e = x4 >> 5;
+        // positions 4c .. 4c+3 hold channels state_pos(4c) + 0 .. 3 (the map is
+        // its own inverse and keeps the two low bits)
+        const int d0 = state_pos(4 * (x4 & 31));
+#pragma unroll
+        for (int m = 0; m < 4; ++m) M[(d0 + m) * LB_P + e] = r[it][m];
     }
-    for (int p = threadIdx.x; p < HD; p += 256) vec[state_pos(p)] = row[HD * HD + p];
+    if (tid < 32) {
+        const int d0 = state_pos(4 * tid);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) vec[d0 + m] = zr[m];
+    }
 }
 
-// Per (head, query block): with H, z its forward complement state,
-// a = phi(q_t), den = a . z, o_l = a^T H / den, g = dO_t, dnum = g / den,
-// dden = -(g . o_l) / den: dq_t (+)= (H dnum + z dden) * phi'(q_t), and the
-// gradient state G^T[e][d] = sum_t dnum[e] a[d], w[d] = sum_t a[d] dden,
-// written in fp32 (gf, for the total) and as bf16 plus its bf16 rest (gs,
-// gs_lo: the GEMM's two stacks).
+// Stage rows r0 .. r0+nrow-1 (64 of them, rows past nval zero) of a bf16
+// [tokens x 128] tensor into X[row][channel] (pitch LB_P) in fp32, through fn.
+template <typename F>
+__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int nval, float* X,
+                                           F fn) {
+    const int tid = threadIdx.x;
+    u16x8 r[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int c = tid + 256 * it, tt = c >> 4;
+        r[it] = tt < nval ? *(const u16x8*)(src + (int64_t)tt * HD + 8 * (c & 15)) : u16x8{};
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int c = tid + 256 * it, tt = c >> 4, d0 = 8 * (c & 15);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) X[tt * LB_P + d0 + m] = tt < nval ? fn(bf2f(r[it][m])) : 0.f;
+    }
+}
+
+// Sum 16 per-lane values over the 32 lanes of a half-wave with 16 exchanges
+// (each step keeps half of the values and adds the partner's copy of them).
+// On return lane l holds the sum of value 8 b4 + 4 b3 + 2 b2 + b1, where
+// b4 .. b1 are bits 4 .. 1 of l (bit 0 holds a duplicate).
+__device__ __forceinline__ float halfwave_sum16(const float (&v)[16], int lane) {
+    float a[8], b[4], c[2];
+    const bool s4 = lane & 16, s3 = lane & 8, s2 = lane & 4, s1 = lane & 2;
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+        a[x] = (s4 ? v[8 + x] : v[x]) + __shfl_xor(s4 ? v[x] : v[8 + x], 16, 64);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) b[x] = (s3 ? a[4 + x] : a[x]) + __shfl_xor(s3 ? a[x] : a[4 + x], 8, 64);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) c[x] = (s2 ? b[2 + x] : b[x]) + __shfl_xor(s2 ? b[x] : b[2 + x], 4, 64);
+    const float d = (s1 ? c[1] : c[0]) + __shfl_xor(s1 ? c[0] : c[1], 2, 64);
+    return d + __shfl_xor(d, 1, 64);
+}
+
+// Per (head, query block), with H, z its forward complement state (H[d][e],
+// z[d]), a = phi(q_t), den = a . z, g = dO_t:
+//   u = H g                  (so that g . o_l = a . u / den)
+//   dden = -(a . u) / den^2
+//   dq_t (+)= (u / den + z dden) * phi'(q_t),   phi'(x) = min(phi(x), 1)
+//   G^T[e][d] = sum_t (g[e] / den) a[d],  w[d] = sum_t a[d] dden
+// The two products run on the fp32 matrix cores (exact fp32 products, fp32
+// sums). G^T and w are written in fp32 (gf, for the total) and as bf16 plus
+// its bf16 rest (gs, gs_lo: the GEMM's two stacks).
+// Waves: u for row tile (w & 1) and channel tiles 2(w >> 1), +1; G^T for
+// e-tile w and all four channel tiles.
 __global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ dout,
                                                            const float* __restrict__ hnon, int N,
@@ -473,72 +530,87 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __res
                                                            float* __restrict__ gf,
                                                            uint16_t* __restrict__ gs,
                                                            uint16_t* __restrict__ gs_lo) {
-    __shared__ float M[HD * LB_P];
+    __shared__ float Hs[HD * LB_P];
     __shared__ float zv[HD];
-    __shared__ float A[LB_CH][HD], G[LB_CH][HD], DN[LB_CH][HD], NUM[LB_CH][HD];
-    __shared__ float den[LB_CH], dden[LB_CH];
+    __shared__ float As[LB_T * LB_P], Gs[LB_T * LB_P];  // a and g, then g / den
+    __shared__ float den_s[LB_T], dden_s[LB_T], gop[2][LB_T];
     const int i = blockIdx.x;
     const int64_t bh = blockIdx.y;
-    const int tid = threadIdx.x;
-    stage_state(hnon + (bh * nqb + i) * (int64_t)HS_ROW, M, zv);
-    // this thread's share of the gradient state: row e = tid/2, channels d0..d0+63
-    const int ge = tid >> 1, gd0 = 64 * (tid & 1);
-    float gacc[64];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    stage_state(hnon + (bh * nqb + i) * (int64_t)HS_ROW, Hs, zv);
+    f32x16 gacc[4];
 #pragma unroll
-    for (int x = 0; x < 64; ++x) gacc[x] = 0.f;
+    for (int dt = 0; dt < 4; ++dt) gacc[dt] = f32x16{};
     float wacc = 0.f;  // threads 0..127: w[tid]
     const int nt = min(QBLK, N - i * QBLK);
-    for (int t0 = 0; t0 < nt; t0 += LB_CH) {
-        __syncthreads();  // the state is staged / the previous chunk is done
-        for (int x = tid; x < LB_CH * HD; x += 256) {
-            const int tt = x >> 7, d = x & 127;
-            const int tok = i * QBLK + t0 + tt;
-            const bool ok = t0 + tt < nt;
-            A[tt][d] = ok ? phi_f(bf2f(q[(bh * N + tok) * HD + d])) : 0.f;
-            G[tt][d] = ok ? bf2f(dout[(bh * N + tok) * HD + d]) : 0.f;
-        }
+    const int rt = wave & 1, ct0 = 2 * (wave >> 1);
+    for (int h0 = 0; h0 < nt; h0 += LB_T) {
+        __syncthreads();  // the state is staged / the previous half is done
+        const int64_t r0 = bh * N + i * QBLK + h0;
+        stage_rows(q + r0 * HD, nt - h0, As, [](float x) { return phi_f(x); });
+        stage_rows(dout + r0 * HD, nt - h0, Gs, [](float x) { return x; });
         __syncthreads();
-        {  // num[t][e] = sum_d a[t][d] H[d][e]
-            const int e = tid & 127, h = tid >> 7;
-            for (int tt = h; tt < LB_CH; tt += 2) {
-                float acc = 0.f;
-                for (int d = 0; d < HD; ++d) acc = __builtin_fmaf(A[tt][d], M[d * LB_P + e], acc);
-                NUM[tt][e] = acc;
-            }
-        }
-        if (tid < LB_CH) {
+        {  // den: four threads per token
+            const int tt = tid >> 2, part = tid & 3;
             float dn = 0.f;
-            for (int d = 0; d < HD; ++d) dn = __builtin_fmaf(A[tid][d], zv[d], dn);
-            den[tid] = t0 + tid < nt ? dn : 1.f;
+            for (int d = 32 * part; d < 32 * part + 32; ++d)
+                dn = __builtin_fmaf(As[tt * LB_P + d], zv[d], dn);
+            dn += __shfl_xor(dn, 1, 64);
+            dn += __shfl_xor(dn, 2, 64);
+            if (part == 0) den_s[tt] = h0 + tt < nt ? dn : 1.f;
+        }
+        // u[t][d] = sum_e g[t][e] H[d][e]
+        f32x16 u[2] = {f32x16{}, f32x16{}};
+        for (int k0 = 0; k0 < HD; k0 += 2) {
+            const float ga = Gs[(32 * rt + l32) * LB_P + k0 + hi];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                u[c] = mfma_f32_32x32x2(ga, Hs[(32 * (ct0 + c) + l32) * LB_P + k0 + hi], u[c]);
+        }
+        {  // partial a . u over this wave's 64 channels, one value per row
+            float gp[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int t = 32 * rt + mfma32_row(lane, r);
+                gp[r] = As[t * LB_P + 32 * ct0 + l32] * u[0][r] +
+                        As[t * LB_P + 32 * (ct0 + 1) + l32] * u[1][r];
+            }
+            const float sum = halfwave_sum16(gp, lane);
+            const int rr = (l32 >> 1) & 15;  // the value this lane holds the sum of
+            if ((l32 & 1) == 0) gop[wave >> 1][32 * rt + mfma32_row(lane, rr)] = sum;
         }
         __syncthreads();
-        if (tid < LB_CH) {
-            float go = 0.f;
-            for (int e = 0; e < HD; ++e) go = __builtin_fmaf(G[tid][e], NUM[tid][e], go);
-            dden[tid] = -go / (den[tid] * den[tid]);
-        }
-        for (int x = tid; x < LB_CH * HD; x += 256) {
-            const int tt = x >> 7, e = x & 127;
-            DN[tt][e] = G[tt][e] / den[tt];
+        if (tid < LB_T) {
+            const float dn = den_s[tid];
+            dden_s[tid] = h0 + tid < nt ? -(gop[0][tid] + gop[1][tid]) / (dn * dn) : 0.f;
         }
         __syncthreads();
-        {  // dq[t][d] (+)= (sum_e H[d][e] dnum[t][e] + z[d] dden[t]) * phi'(q[t][d])
-            const int d = tid & 127, h = tid >> 7;
-            for (int tt = h; tt < LB_CH; tt += 2) {
-                if (t0 + tt >= nt) continue;
-                float acc = zv[d] * dden[tt];
-                for (int e = 0; e < HD; ++e) acc = __builtin_fmaf(M[d * LB_P + e], DN[tt][e], acc);
-                const int64_t o = (bh * N + i * QBLK + t0 + tt) * HD + d;
-                const float g = acc * dphi_f(bf2f(q[o]));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int d = 32 * (ct0 + c) + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int t = 32 * rt + mfma32_row(lane, r);
+                if (h0 + t >= nt) continue;
+                const float g =
+                    (u[c][r] / den_s[t] + zv[d] * dden_s[t]) * fminf(As[t * LB_P + d], 1.f);
+                const int64_t o = (bh * N + i * QBLK + h0 + t) * HD + d;
                 dq[o] = accumulate ? dq[o] + g : g;
             }
-            if (h == 0)
-                for (int tt = 0; tt < LB_CH; ++tt) wacc = __builtin_fmaf(A[tt][d], dden[tt], wacc);
         }
-        for (int tt = 0; tt < LB_CH; ++tt) {
-            const float dn = DN[tt][ge];
+        for (int x = tid; x < LB_T * HD; x += 256) {
+            const int tt = x >> 7, e = x & 127;
+            Gs[tt * LB_P + e] = Gs[tt * LB_P + e] / den_s[tt];
+        }
+        if (tid < HD)
+            for (int tt = 0; tt < LB_T; ++tt) wacc = __builtin_fmaf(As[tt * LB_P + tid], dden_s[tt], wacc);
+        __syncthreads();
+        // G^T[e][d] += sum_t (g / den)[t][e] a[t][d]
+        for (int k0 = 0; k0 < LB_T; k0 += 2) {
+            const float da = Gs[(k0 + hi) * LB_P + 32 * wave + l32];
 #pragma unroll
-            for (int x = 0; x < 64; ++x) gacc[x] = __builtin_fmaf(dn, A[tt][gd0 + x], gacc[x]);
+            for (int dt = 0; dt < 4; ++dt)
+                gacc[dt] = mfma_f32_32x32x2(da, As[(k0 + hi) * LB_P + 32 * dt + l32], gacc[dt]);
         }
     }
     float* fr = gf + (bh * nqb + i) * (int64_t)HS_ROW;
@@ -551,48 +623,59 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __res
         lr[o] = f2bf(x - bf2f(h));
     };
 #pragma unroll
-    for (int x = 0; x < 64; ++x) put((int64_t)ge * HD + state_pos(gd0 + x), gacc[x]);
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            put((int64_t)(32 * wave + mfma32_row(lane, r)) * HD + state_pos(32 * dt + l32), gacc[dt][r]);
     if (tid < HD) put(HD * HD + state_pos(tid), wacc);
 }
 
-// Per (head, key block): with Gc, wc the gradient-state sums over the query
-// blocks that did not keep the block, for each key u: f = phi(k_u),
-// dk_u (+)= (Gc v_u + wc) * phi'(k_u), dv_u (+)= Gc^T f.
+// Per (head, key block): with Gc[d][e], wc the gradient-state sums over the
+// query blocks that did not keep the block, for each key u: f = phi(k_u),
+//   dk_u (+)= (Gc v_u + wc) * phi'(k_u),  dv_u (+)= Gc^T f
+// on the fp32 matrix cores. Waves: row tile (w & 1), channel tiles
+// 2(w >> 1), +1 of both products.
 __global__ __launch_bounds__(256, 1) void lin_bwd_k_kernel(const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
                                                            const float* __restrict__ gc, int N,
                                                            int nkb, int accumulate,
                                                            float* __restrict__ dk,
                                                            float* __restrict__ dv) {
-    __shared__ float M[HD * LB_P];
+    __shared__ float Ms[HD * LB_P];
     __shared__ float wv[HD];
-    __shared__ float F[LB_CH][HD], V[LB_CH][HD];
+    __shared__ float Fs[KBLK * LB_P], Vs[KBLK * LB_P];
     const int j = blockIdx.x;
     const int64_t bh = blockIdx.y;
-    const int tid = threadIdx.x;
-    stage_state(gc + (bh * nkb + j) * (int64_t)HS_ROW, M, wv);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    stage_state(gc + (bh * nkb + j) * (int64_t)HS_ROW, Ms, wv);
     const int nk = min(KBLK, N - j * KBLK);
-    for (int u0 = 0; u0 < nk; u0 += LB_CH) {
-        __syncthreads();
-        for (int x = tid; x < LB_CH * HD; x += 256) {
-            const int uu = x >> 7, d = x & 127;
-            const bool ok = u0 + uu < nk;
-            const int64_t o = (bh * N + j * KBLK + u0 + uu) * HD + d;
-            F[uu][d] = ok ? phi_f(bf2f(k[o])) : 0.f;
-            V[uu][d] = ok ? bf2f(v[o]) : 0.f;
+    const int64_t r0 = bh * N + j * KBLK;
+    stage_rows(k + r0 * HD, nk, Fs, [](float x) { return phi_f(x); });
+    stage_rows(v + r0 * HD, nk, Vs, [](float x) { return x; });
+    __syncthreads();
+    const int rt = wave & 1, ct0 = 2 * (wave >> 1);
+    f32x16 gk[2] = {f32x16{}, f32x16{}}, gv[2] = {f32x16{}, f32x16{}};
+    for (int k0 = 0; k0 < HD; k0 += 2) {
+        const float va = Vs[(32 * rt + l32) * LB_P + k0 + hi];  // v[u][e = k]
+        const float fa = Fs[(32 * rt + l32) * LB_P + k0 + hi];  // f[u][d = k]
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int n = 32 * (ct0 + c) + l32;
+            gk[c] = mfma_f32_32x32x2(va, Ms[n * LB_P + k0 + hi], gk[c]);    // Gc[d = n][e = k]
+            gv[c] = mfma_f32_32x32x2(fa, Ms[(k0 + hi) * LB_P + n], gv[c]);  // Gc[d = k][e = n]
         }
-        __syncthreads();
-        const int c = tid & 127, h = tid >> 7;
-        for (int uu = h; uu < LB_CH; uu += 2) {
-            if (u0 + uu >= nk) continue;
-            const int64_t o = (bh * N + j * KBLK + u0 + uu) * HD + c;
-            float gk = wv[c];  // channel d = c
-            for (int e = 0; e < HD; ++e) gk = __builtin_fmaf(M[c * LB_P + e], V[uu][e], gk);
-            gk *= dphi_f(bf2f(k[o]));
-            float gv = 0.f;  // channel e = c
-            for (int d = 0; d < HD; ++d) gv = __builtin_fmaf(M[d * LB_P + c], F[uu][d], gv);
-            dk[o] = accumulate ? dk[o] + gk : gk;
-            dv[o] = accumulate ? dv[o] + gv : gv;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int n = 32 * (ct0 + c) + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int uu = 32 * rt + mfma32_row(lane, r);
+            if (uu >= nk) continue;
+            const int64_t o = (bh * N + j * KBLK + uu) * HD + n;
+            const float g = (gk[c][r] + wv[n]) * fminf(Fs[uu * LB_P + n], 1.f);
+            dk[o] = accumulate ? dk[o] + g : g;
+            dv[o] = accumulate ? dv[o] + gv[c][r] : gv[c][r];
         }
     }
 }
