@@ -275,9 +275,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 // ---- dk, dv: one workgroup per (head, key block), 4 waves -----------------
 // Over the query blocks that kept the block (every block when dense). The K
 // and V tiles of the block sit in LDS for the whole workgroup. Per query
-// block, wave w first takes its 32 queries t (32w + ...) against all 64 keys:
-//   S = Q . K^T    (int8; lane holds key l32 (+32 for the second tile),
-//                   queries 8(r/4)+4hi+r%4 of the wave's 32)
+// block, wave w first takes its 32 queries t (32w + ...) against the 64 keys,
+// one 32-key tile h at a time:
+//   S = Q . K^T    (int8; lane holds key 32h + l32, queries 8(r/4)+4hi+r%4
+//                   of the wave's 32)
 //   dP = dO . V^T  (bf16; same layout)
 //   P = 2^(S c - m'), dS = P (dP - D) sq
 // and stores P and dS in LDS as the next products' B fragments (their
@@ -285,7 +286,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 // wave w accumulates channels 32w .. 32w+31 of
 //   dV^T += dO^T . P,  dK^T += Q^T . dS
 // over all 128 queries, the A fragments from the channel-first re-laid tiles
-// (rows 32w.. only). Every input is read once per workgroup.
+// (rows 32w.. only). Every input is read once per workgroup, and loads are
+// issued ahead of their use: half of the second products' A fragments before
+// the first products, the next query block's rows and row statistics (m', D,
+// through a two-deep LDS buffer) before the second products.
 constexpr int KV_K = KBLK * HD;        // int8 K tile, 64 rows of 128 B
 constexpr int KV_V = KBLK * HD * 2;    // bf16 V tile, 64 rows of 256 B
 constexpr int KV_F = 8 * 2 * 64 * 16;  // one fragment set: [8 query steps][2 key tiles][64 lanes] x 16 B
@@ -293,6 +297,7 @@ constexpr int KV_F = 8 * 2 * 64 * 16;  // one fragment set: [8 query steps][2 ke
 template <bool DENSE>
 __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[KV_K + KV_V + 2 * KV_F];
+    __shared__ __attribute__((aligned(16))) float stat[2][2][QBLK];  // [buffer][m', D][query]
     uint8_t* kt = smem;
     uint8_t* vt = smem + KV_K;
     uint8_t* pf = smem + KV_K + KV_V;  // P fragments
@@ -318,102 +323,128 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
         *(u16x8*)(vt + r * 256 + 16 * (c ^ (r & 15))) =
             *(const u16x8*)(a.v + (bh * N + (int64_t)j * KBLK + rr) * HD + 8 * c);
     }
-    __syncthreads();
     const float sk = a.k_scale[bh * a.nkb + j];
     f32x16 dva[2], dka[2];  // channels 32w + ..., key tiles 0, 1
     dva[0] = dva[1] = dka[0] = dka[1] = f32x16{};
     const int cnt = DENSE ? nqb : a.counts[bh * a.nkb + j];
     const uint16_t* list = DENSE ? nullptr : a.lists + (bh * a.nkb + j) * (int64_t)nqb;
+    auto qblock = [&](int x) { return DENSE ? x : (int)list[x]; };
+    // the lane's query row of query block i (S and dP A operands); rows past
+    // N re-read row N-1 (their P and dS are zeroed)
+    i32x4 qa[4];
+    bf16x8 ga[8];
+    auto load_rows = [&](int i) {
+        const int tr = min(i * QBLK + 32 * wave + l32, N - 1);
+        const int8_t* qp = a.q_i8 + (bh * N + tr) * HD;
+        const uint16_t* gp = a.dout + (bh * N + tr) * HD;
+#pragma unroll
+        for (int cq = 0; cq < 4; ++cq) qa[cq] = *(const i32x4*)(qp + 32 * cq + 16 * hi);
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd)
+            ga[sd] = __builtin_bit_cast(bf16x8, *(const u16x8*)(gp + 16 * sd + 8 * hi));
+    };
+    // threads 0..127: m' of query tid of block i; 128..255: its D
+    auto load_stat = [&](int i) {
+        const int t = min(i * QBLK + (tid & (QBLK - 1)), N - 1);
+        return (tid < QBLK ? a.mlog : a.dstat)[bh * N + t];
+    };
+    if (cnt > 0) {
+        const int i0 = qblock(0);
+        load_rows(i0);
+        stat[0][tid >> 7][tid & (QBLK - 1)] = load_stat(i0);
+    }
+    __syncthreads();
+    const int64_t arow = (int64_t)(32 * wave + l32) * QBLK + 8 * hi;
     for (int x = 0; x < cnt; ++x) {
-        const int i = DENSE ? x : (int)list[x];
+        const int i = qblock(x);
+        const bool more = x + 1 < cnt;
         const float sq = a.q_scale[bh * nqb + i];
         const float c = (sq * sk) * a.K32;
-        const int tr = i * QBLK + 32 * wave + l32;  // the query row this lane supplies
-        const bool rok = tr < N;
-        i32x16 s[2];
-        f32x16 dp[2];
-        s[0] = s[1] = i32x16{};
-        dp[0] = dp[1] = f32x16{};
-        {
-            const int8_t* qp = a.q_i8 + (bh * N + (rok ? tr : 0)) * HD;
-            const uint16_t* gp = a.dout + (bh * N + (rok ? tr : 0)) * HD;
+        // the second products' A fragments: query steps 0..3 in flight during
+        // the first products, 4..7 during steps 0..3
+        u16x8 g2[8], q2[8];
+        const uint16_t* dot = a.dot + (bh * nqb + i) * (int64_t)HD * QBLK + arow;
+        const uint16_t* qt = a.qt16 + (bh * nqb + i) * (int64_t)HD * QBLK + arow;
 #pragma unroll
-            for (int cq = 0; cq < 4; ++cq) {
-                const i32x4 qa = rok ? *(const i32x4*)(qp + 32 * cq + 16 * hi) : i32x4{};
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int key = 32 * h + l32;
-                    const i32x4 kb = *(const i32x4*)(kt + key * 128 + 16 * ((2 * cq + hi) ^ swz8(key)));
-                    s[h] = mfma_i8_32x32x32(qa, kb, s[h]);
-                }
-            }
-#pragma unroll
-            for (int sd = 0; sd < 8; ++sd) {
-                const bf16x8 ga =
-                    rok ? __builtin_bit_cast(bf16x8, *(const u16x8*)(gp + 16 * sd + 8 * hi)) : bf16x8{};
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int key = 32 * h + l32;
-                    const bf16x8 vb =
-                        *(const bf16x8*)(vt + key * 256 + 16 * ((2 * sd + hi) ^ (key & 15)));
-                    dp[h] = mfma_bf16_32x32x16(ga, vb, dp[h]);
-                }
-            }
+        for (int qs = 0; qs < 4; ++qs) {
+            g2[qs] = *(const u16x8*)(dot + 16 * qs);
+            q2[qs] = *(const u16x8*)(qt + 16 * qs);
         }
-        // P and dS, stored as fragment [query step 2w + r/8][key tile h][lane]
-        f32x16 pr[2];
+        __builtin_amdgcn_sched_barrier(0);
+        const float* mrow = stat[x & 1][0];
+        const float* drow = stat[x & 1][1];
+#pragma unroll 1
+        for (int h = 0; h < 2; ++h) {
+            const int key = 32 * h + l32;
+            i32x16 s = i32x16{};
+            f32x16 dp = f32x16{};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float mq[4], Dq[4];
-            const int q0 = i * QBLK + 32 * wave + 8 * g + 4 * hi;  // rows 4g .. 4g+3
+            for (int cq = 0; cq < 4; ++cq)
+                s = mfma_i8_32x32x32(
+                    qa[cq], *(const i32x4*)(kt + key * 128 + 16 * ((2 * cq + hi) ^ swz8(key))), s);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool ok = q0 + e < N;
-                mq[e] = ok ? a.mlog[bh * N + q0 + e] : 0.f;
-                Dq[e] = ok ? a.dstat[bh * N + q0 + e] : 0.f;
-            }
+            for (int sd = 0; sd < 8; ++sd)
+                dp = mfma_bf16_32x32x16(
+                    ga[sd], *(const bf16x8*)(vt + key * 256 + 16 * ((2 * sd + hi) ^ (key & 15))), dp);
+            const bool kok = key < nval;
+            f32x16 pr;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bool kok = 32 * h + l32 < nval;
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = 32 * wave + 8 * g + 4 * hi;  // queries of registers 4g .. 4g+3
+                const f32x4 mq = *(const f32x4*)(mrow + r0);
+                const f32x4 Dq = *(const f32x4*)(drow + r0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
-                    const bool ok = kok && q0 + e < N;
-                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[h][r], c, -mq[e])) : 0.f;
-                    pr[h][r] = p;
-                    dp[h][r] = p * (dp[h][r] - Dq[e]) * sq;
+                    const bool ok = kok && i * QBLK + r0 + e < N;
+                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], c, -mq[e])) : 0.f;
+                    pr[r] = p;
+                    dp[r] = p * (dp[r] - Dq[e]) * sq;
                 }
             }
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
+            // fragment [query step 2w + ks][key tile h][lane]
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 bf16x8 pb, db;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    pb[e] = (__bf16)pr[h][8 * ks + e];
-                    db[e] = (__bf16)dp[h][8 * ks + e];
+                    pb[e] = (__bf16)pr[8 * ks + e];
+                    db[e] = (__bf16)dp[8 * ks + e];
                 }
                 const int slot = ((2 * wave + ks) * 2 + h) * 64 + lane;
                 *(bf16x8*)(pf + 16 * slot) = pb;
                 *(bf16x8*)(df + 16 * slot) = db;
             }
+        }
+        // the next query block's rows and statistics, in flight during the
+        // second products
+        float stn = 0.f;
+        if (more) {
+            const int in = qblock(x + 1);
+            load_rows(in);
+            stn = load_stat(in);
+        }
         __syncthreads();
-        const uint16_t* dot = a.dot + (bh * nqb + i) * (int64_t)HD * QBLK;
-        const uint16_t* qt = a.qt16 + (bh * nqb + i) * (int64_t)HD * QBLK;
-        const int64_t arow = (int64_t)(32 * wave + l32) * QBLK + 8 * hi;
+#pragma unroll
+        for (int qs = 4; qs < 8; ++qs) {
+            g2[qs] = *(const u16x8*)(dot + 16 * qs);
+            q2[qs] = *(const u16x8*)(qt + 16 * qs);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qs = 0; qs < 8; ++qs) {
-            const bf16x8 ga = __builtin_bit_cast(bf16x8, *(const u16x8*)(dot + arow + 16 * qs));
-            const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u16x8*)(qt + arow + 16 * qs));
+            const bf16x8 gb = __builtin_bit_cast(bf16x8, g2[qs]);
+            const bf16x8 qb = __builtin_bit_cast(bf16x8, q2[qs]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int slot = (qs * 2 + h) * 64 + lane;
-                dva[h] = mfma_bf16_32x32x16(ga, *(const bf16x8*)(pf + 16 * slot), dva[h]);
-                dka[h] = mfma_bf16_32x32x16(qa, *(const bf16x8*)(df + 16 * slot), dka[h]);
+                dva[h] = mfma_bf16_32x32x16(gb, *(const bf16x8*)(pf + 16 * slot), dva[h]);
+                dka[h] = mfma_bf16_32x32x16(qb, *(const bf16x8*)(df + 16 * slot), dka[h]);
             }
         }
+        // the buffer (x + 1) & 1 was last read by the first products of
+        // query block x - 1, before this iteration's first barrier
+        if (more) stat[(x + 1) & 1][tid >> 7][tid & (QBLK - 1)] = stn;
         __syncthreads();  // the next query block rewrites the fragments
     }
     // lane (key column l32 of tile h, hi) holds channels 32w + 8(r/4) + 4hi + r%4
