@@ -477,6 +477,12 @@ __device__ __forceinline__ int state_pos(int d) {
 __device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 __device__ __forceinline__ float dphi_f(float x) { return x > 0.f ? 1.f : __expf(x); }
 
+// fp32 x fp32 -> fp32 on the matrix cores: lane l supplies A[l & 31][l >> 5]
+// and B[l >> 5][l & 31]; the result has the 32x32 layout of mfma32_row.
+__device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
 constexpr int LB_P = HD + 1;  // odd LDS pitch: row- and column-wise fragment reads hit distinct banks
 constexpr int LB_T = 64;      // tokens staged at a time
 

@@ -39,11 +39,6 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// fp32 x fp32 -> fp32: lane l supplies A[l & 31][l >> 5] and B[l >> 5][l & 31].
-__device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
 // Output layout of the 32x32 MFMA families: lane l, accumulator r holds
 // column (l & 31) and row 8*(r/4) + 4*(l/32) + (r%4).
 __device__ __forceinline__ int mfma32_row(int lane, int r) {
