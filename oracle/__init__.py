@@ -56,6 +56,9 @@ def lib():
                                       C.c_int]),
             "orc_sagesla_bwd": (None, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64,
                                        C.c_int, C.c_float, _p, _p, _p, _p, C.c_int]),
+            "orc_sagesla_bwd_sel": (None, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p,
+                                           _i64, C.c_int, C.c_float, _p, _p, _p, _p, _p, _p,
+                                           C.c_int]),
             "orc_sagesla_loss": (C.c_double, [_p, _p, _p, _p, _p, _i64, _i64, _p, _i64, C.c_int,
                                               C.c_double, _p]),
             "orc_w8a8_quant": (None, [_p, _i64, _i64, _p, _p, C.c_int]),
@@ -307,11 +310,13 @@ def sagesla_rows(q, k, v, quantized, bh, tokens, kidx_head=None, branches=3, sm_
 
 
 def sagesla_bwd(q, k, v, quantized, bh, dout, kidx_head=None, branches=3, sm_scale=0.0,
-                nthreads=None):
+                nthreads=None, qrows=None, kcols=None):
     """fp64 (dq, dk, dv) [N, D] of head bh: the SageSLA backward with the
     quantizer passed straight through and the selection held fixed.
     q, k, v, dout: uint16 bf16 bits [BH, N, D]; quantized = (q_i8, q_scale,
-    k_i8, k_scale) as quant_qk returns them."""
+    k_i8, k_scale) as quant_qk returns them. qrows / kcols (token indices)
+    restrict the work to those rows of dq / of dk and dv; the other rows of
+    the results are then unspecified."""
     q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
     q_i8, q_scale, k_i8, k_scale = (np.ascontiguousarray(x) for x in quantized)
     BH, N, D = q.shape
@@ -322,11 +327,21 @@ def sagesla_bwd(q, k, v, quantized, bh, dout, kidx_head=None, branches=3, sm_sca
     dq = np.empty((N, D))
     dk = np.empty((N, D))
     dv = np.empty((N, D))
-    lib().orc_sagesla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(q_i8),
-                          _ptr(np.ascontiguousarray(q_scale, np.float32)), _ptr(k_i8),
-                          _ptr(np.ascontiguousarray(k_scale, np.float32)), N, D, bh,
-                          _ptr(kidx_head), keep, int(branches), float(sm_scale), _ptr(dout),
-                          _ptr(dq), _ptr(dk), _ptr(dv), nthreads or threads())
+
+    def sel(rows):
+        if rows is None:
+            return None
+        m = np.zeros(N, np.uint8)
+        m[np.asarray(rows, np.int64)] = 1
+        return m
+
+    qsel, ksel = sel(qrows), sel(kcols)
+    lib().orc_sagesla_bwd_sel(_ptr(q), _ptr(k), _ptr(v), _ptr(q_i8),
+                              _ptr(np.ascontiguousarray(q_scale, np.float32)), _ptr(k_i8),
+                              _ptr(np.ascontiguousarray(k_scale, np.float32)), N, D, bh,
+                              _ptr(kidx_head), keep, int(branches), float(sm_scale), _ptr(dout),
+                              _ptr(qsel), _ptr(ksel), _ptr(dq), _ptr(dk), _ptr(dv),
+                              nthreads or threads())
     return dq, dk, dv
 
 

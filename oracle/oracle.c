@@ -778,7 +778,9 @@ typedef struct {
     const float *q_scale, *k_scale;
     const uint16_t *v, *dout;
     int64_t N, D, bh, nqb, nkb, keep;
-    const int32_t* kidx;
+    const uint8_t* kept;        /* [nqb][nkb]: 1 where query block i keeps key block j */
+    const uint8_t* need_stats;  /* [N]: rows whose statistics are needed */
+    const uint8_t *qsel, *ksel; /* [N] or NULL (every row): rows of dq, keys of dk and dv */
     double sm;
     double *rmax, *rsum, *rD; /* per query row */
     double *dq, *dk, *dv;
@@ -803,56 +805,63 @@ static double sb_dp(const sbwd_ctx* c, int64_t t, int64_t u) {
     return a;
 }
 
-/* pass 1 (per query row t): softmax statistics, D_t and dq_t */
+/* pass 1 (per query row t): softmax statistics, D_t and dq_t. The row's
+ * scores and dP over its kept keys are formed once and reused by the later
+ * sweeps, which take them in the same order (j, then u, ascending). */
 static void sbwd_rows_task(void* vctx, int64_t t) {
     sbwd_ctx* c = (sbwd_ctx*)vctx;
+    if (!c->need_stats[t]) return;
     int64_t N = c->N, D = c->D, i = t / ORC_QBLK;
+    const uint8_t* kept = c->kept + i * c->nkb;
+    int64_t nk = 0;
+    for (int64_t j = 0; j < c->nkb; ++j)
+        if (kept[j]) nk += ((j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N) - j * ORC_KBLK;
+    double* sv = (double*)malloc(sizeof(double) * (size_t)(2 * nk));
+    double* dpv = sv + nk;
     double m = -INFINITY;
+    int64_t x = 0;
     for (int64_t j = 0; j < c->nkb; ++j) {
-        if (!kept_by(c->kidx, c->keep, i, j)) continue;
+        if (!kept[j]) continue;
         int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
-        for (int64_t u = j * ORC_KBLK; u < u1; ++u) {
-            double s = sb_score(c, t, u);
-            if (s > m) m = s;
+        for (int64_t u = j * ORC_KBLK; u < u1; ++u, ++x) {
+            sv[x] = sb_score(c, t, u);
+            dpv[x] = sb_dp(c, t, u);
+            if (sv[x] > m) m = sv[x];
         }
     }
     double l = 0.0, Dt = 0.0;
-    for (int64_t j = 0; j < c->nkb; ++j) {
-        if (!kept_by(c->kidx, c->keep, i, j)) continue;
-        int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
-        for (int64_t u = j * ORC_KBLK; u < u1; ++u) l += exp(sb_score(c, t, u) - m);
-    }
-    for (int64_t j = 0; j < c->nkb; ++j) {
-        if (!kept_by(c->kidx, c->keep, i, j)) continue;
-        int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
-        for (int64_t u = j * ORC_KBLK; u < u1; ++u)
-            Dt += exp(sb_score(c, t, u) - m) / l * sb_dp(c, t, u);
-    }
+    for (x = 0; x < nk; ++x) l += exp(sv[x] - m);
+    for (x = 0; x < nk; ++x) Dt += exp(sv[x] - m) / l * dpv[x];
     c->rmax[t] = m;
     c->rsum[t] = l;
     c->rD[t] = Dt;
-    double* dq = c->dq + t * D;
-    for (int64_t j = 0; j < c->nkb; ++j) {
-        if (!kept_by(c->kidx, c->keep, i, j)) continue;
-        double sk = (double)c->k_scale[c->bh * c->nkb + j];
-        int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
-        for (int64_t u = j * ORC_KBLK; u < u1; ++u) {
-            double P = exp(sb_score(c, t, u) - m) / l;
-            double dS = P * (sb_dp(c, t, u) - Dt);
-            const int8_t* kr = c->k_i8 + (c->bh * N + u) * D;
-            for (int64_t d = 0; d < D; ++d) dq[d] += c->sm * dS * sk * (double)kr[d];
+    if (!c->qsel || c->qsel[t]) {
+        double* dq = c->dq + t * D;
+        x = 0;
+        for (int64_t j = 0; j < c->nkb; ++j) {
+            if (!kept[j]) continue;
+            double sk = (double)c->k_scale[c->bh * c->nkb + j];
+            int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
+            for (int64_t u = j * ORC_KBLK; u < u1; ++u, ++x) {
+                double P = exp(sv[x] - m) / l;
+                double dS = P * (dpv[x] - Dt);
+                const int8_t* kr = c->k_i8 + (c->bh * N + u) * D;
+                for (int64_t d = 0; d < D; ++d) dq[d] += c->sm * dS * sk * (double)kr[d];
+            }
         }
     }
+    free(sv);
 }
 
 /* pass 2 (per key u): dk_u and dv_u over the queries whose block kept u's */
 static void sbwd_keys_task(void* vctx, int64_t u) {
     sbwd_ctx* c = (sbwd_ctx*)vctx;
+    if (c->ksel && !c->ksel[u]) return;
     int64_t N = c->N, D = c->D, j = u / ORC_KBLK;
     double* dk = c->dk + u * D;
     double* dv = c->dv + u * D;
     for (int64_t i = 0; i < c->nqb; ++i) {
-        if (!kept_by(c->kidx, c->keep, i, j)) continue;
+        if (!c->kept[i * c->nkb + j]) continue;
         double sq = (double)c->q_scale[c->bh * c->nqb + i];
         int64_t t1 = (i + 1) * ORC_QBLK < N ? (i + 1) * ORC_QBLK : N;
         for (int64_t t = i * ORC_QBLK; t < t1; ++t) {
@@ -871,7 +880,8 @@ static void sbwd_keys_task(void* vctx, int64_t u) {
 typedef struct {
     const uint16_t *q, *k, *v, *dout;
     int64_t N, D, bh, nqb, nkb, keep;
-    const int32_t* kidx;
+    const uint8_t* kept;   /* [nqb][nkb] */
+    const uint8_t* ksel;   /* [N] or NULL: keys of dk and dv */
     const double *h, *z; /* per key block states */
     double *G, *w;       /* per query block [D][D], [D] */
     double *dq, *dk, *dv;
@@ -885,7 +895,7 @@ static void lbwd_q_task(void* vctx, int64_t i) {
     double* z = (double*)calloc((size_t)D, sizeof(double));
     int64_t ncomp = 0;
     for (int64_t j = 0; j < c->nkb; ++j) {
-        if (kept_by(c->kidx, c->keep, i, j)) continue;
+        if (c->kept[i * c->nkb + j]) continue;
         ++ncomp;
         for (int64_t x = 0; x < D * D; ++x) H[x] += c->h[j * D * D + x];
         for (int64_t d = 0; d < D; ++d) z[d] += c->z[j * D + d];
@@ -936,16 +946,22 @@ static void lbwd_q_task(void* vctx, int64_t i) {
 static void lbwd_k_task(void* vctx, int64_t j) {
     lbwd_ctx* c = (lbwd_ctx*)vctx;
     int64_t N = c->N, D = c->D;
+    int64_t u0 = j * ORC_KBLK, u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
+    if (c->ksel) {
+        int any = 0;
+        for (int64_t u = u0; u < u1; ++u) any |= c->ksel[u];
+        if (!any) return;
+    }
     double* Gc = (double*)calloc((size_t)(D * D), sizeof(double));
     double* wc = (double*)calloc((size_t)D, sizeof(double));
     for (int64_t i = 0; i < c->nqb; ++i) {
-        if (kept_by(c->kidx, c->keep, i, j)) continue;
+        if (c->kept[i * c->nkb + j]) continue;
         for (int64_t x = 0; x < D * D; ++x) Gc[x] += c->G[i * D * D + x];
         for (int64_t d = 0; d < D; ++d) wc[d] += c->w[i * D + d];
     }
     double* f = (double*)malloc(sizeof(double) * (size_t)D);
-    int64_t u1 = (j + 1) * ORC_KBLK < N ? (j + 1) * ORC_KBLK : N;
-    for (int64_t u = j * ORC_KBLK; u < u1; ++u) {
+    for (int64_t u = u0; u < u1; ++u) {
+        if (c->ksel && !c->ksel[u]) continue;
         const uint16_t* kr = c->k + (c->bh * N + u) * D;
         const uint16_t* vr = c->v + (c->bh * N + u) * D;
         for (int64_t d = 0; d < D; ++d) f[d] = phi((double)orc_bf16_to_f32(kr[d]));
@@ -965,17 +981,34 @@ static void lbwd_k_task(void* vctx, int64_t j) {
     free(wc);
 }
 
-void orc_sagesla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int8_t* q_i8,
-                     const float* q_scale, const int8_t* k_i8, const float* k_scale, int64_t N,
-                     int64_t D, int64_t bh, const int32_t* kidx_head, int64_t keep, int branches,
-                     float sm_scale, const uint16_t* dout, double* dq, double* dk, double* dv,
-                     int nthreads) {
+void orc_sagesla_bwd_sel(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                         const float* k_scale, int64_t N, int64_t D, int64_t bh,
+                         const int32_t* kidx_head, int64_t keep, int branches, float sm_scale,
+                         const uint16_t* dout, const uint8_t* qsel, const uint8_t* ksel,
+                         double* dq, double* dk, double* dv, int nthreads) {
     int64_t nqb = orc_nqb(N), nkb = orc_nkb(N);
     if (!kidx_head) keep = nkb;
     memset(dq, 0, sizeof(double) * (size_t)(N * D));
     memset(dk, 0, sizeof(double) * (size_t)(N * D));
     memset(dv, 0, sizeof(double) * (size_t)(N * D));
+    /* the kept-block table, from kidx (every block when dense) */
+    uint8_t* kept = (uint8_t*)malloc((size_t)(nqb * nkb));
+    for (int64_t i = 0; i < nqb; ++i)
+        for (int64_t j = 0; j < nkb; ++j) kept[i * nkb + j] = (uint8_t)kept_by(kidx_head, keep, i, j);
     if (branches & 1) {
+        /* statistics are needed for the selected rows and for every row of a
+         * query block that keeps the block of a selected key */
+        uint8_t* need = (uint8_t*)malloc((size_t)N);
+        uint8_t* kbsel = (uint8_t*)calloc((size_t)nkb, 1);
+        for (int64_t u = 0; u < N; ++u)
+            if (!ksel || ksel[u]) kbsel[u / ORC_KBLK] = 1;
+        for (int64_t i = 0; i < nqb; ++i) {
+            uint8_t blk = 0;
+            for (int64_t j = 0; j < nkb && !blk; ++j) blk = kept[i * nkb + j] && kbsel[j];
+            int64_t t1 = (i + 1) * ORC_QBLK < N ? (i + 1) * ORC_QBLK : N;
+            for (int64_t t = i * ORC_QBLK; t < t1; ++t) need[t] = blk || !qsel || qsel[t];
+        }
         sbwd_ctx c;
         c.q_i8 = q_i8;
         c.k_i8 = k_i8;
@@ -989,7 +1022,10 @@ void orc_sagesla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
         c.nqb = nqb;
         c.nkb = nkb;
         c.keep = keep;
-        c.kidx = kidx_head;
+        c.kept = kept;
+        c.need_stats = need;
+        c.qsel = qsel;
+        c.ksel = ksel;
         c.sm = (double)default_sm(sm_scale, D);
         c.rmax = (double*)malloc(sizeof(double) * (size_t)N);
         c.rsum = (double*)malloc(sizeof(double) * (size_t)N);
@@ -1002,12 +1038,14 @@ void orc_sagesla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
         free(c.rmax);
         free(c.rsum);
         free(c.rD);
+        free(need);
+        free(kbsel);
     }
     if ((branches & 2) && kidx_head && keep < nkb) {
         double* h = (double*)malloc(sizeof(double) * (size_t)(nkb * D * D));
         double* z = (double*)malloc(sizeof(double) * (size_t)(nkb * D));
         orc_linear_states(k, v, N, D, bh, h, z, nthreads);
-        lbwd_ctx c = {q, k, v, dout, N, D, bh, nqb, nkb, keep, kidx_head, h, z, NULL, NULL,
+        lbwd_ctx c = {q, k, v, dout, N, D, bh, nqb, nkb, keep, kept, ksel, h, z, NULL, NULL,
                       dq, dk, dv};
         c.G = (double*)malloc(sizeof(double) * (size_t)(nqb * D * D));
         c.w = (double*)malloc(sizeof(double) * (size_t)(nqb * D));
@@ -1018,6 +1056,16 @@ void orc_sagesla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
         free(h);
         free(z);
     }
+    free(kept);
+}
+
+void orc_sagesla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int8_t* q_i8,
+                     const float* q_scale, const int8_t* k_i8, const float* k_scale, int64_t N,
+                     int64_t D, int64_t bh, const int32_t* kidx_head, int64_t keep, int branches,
+                     float sm_scale, const uint16_t* dout, double* dq, double* dk, double* dv,
+                     int nthreads) {
+    orc_sagesla_bwd_sel(q, k, v, q_i8, q_scale, k_i8, k_scale, N, D, bh, kidx_head, keep, branches,
+                        sm_scale, dout, NULL, NULL, dq, dk, dv, nthreads);
 }
 
 /* The scalar loss L = sum_{t,e} dO_te O_te of the SageSLA forward written

@@ -144,6 +144,17 @@ void orc_sagesla_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
                      float sm_scale, const uint16_t* dout, double* dq, double* dk, double* dv,
                      int nthreads);
 
+/* orc_sagesla_bwd restricted to sampled outputs: qsel[N] marks the query rows
+ * whose dq is computed, ksel[N] the keys whose dk and dv are (NULL: every row).
+ * Selected rows hold exactly what orc_sagesla_bwd gives them; the others are
+ * unspecified. Row statistics are formed for the rows the selection needs. */
+void orc_sagesla_bwd_sel(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                         const float* k_scale, int64_t N, int64_t D, int64_t bh,
+                         const int32_t* kidx_head, int64_t keep, int branches, float sm_scale,
+                         const uint16_t* dout, const uint8_t* qsel, const uint8_t* ksel,
+                         double* dq, double* dk, double* dv, int nthreads);
+
 /* sum_{t,e} dout[t][e] * O[t][e] of the forward on continuous fp64 inputs of
  * one head: qh, kh (sparse branch, no quantization), ql, kl (linear branch),
  * vv (both); for pinning orc_sagesla_bwd by central differences. */

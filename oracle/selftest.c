@@ -141,6 +141,29 @@ int main(void) {
             CHECK(memcmp(g[0][n], g[1][n], sizeof(double) * N * D) == 0, "backward threads");
             for (int64_t x = 0; x < N * D; ++x) CHECK(isfinite(g[0][n][x]), "backward finite");
         }
+        /* sampled rows and keys on 7 threads equal the full computation */
+        {
+            uint8_t* qsel = calloc((size_t)N, 1);
+            uint8_t* ksel = calloc((size_t)N, 1);
+            qsel[0] = qsel[130] = qsel[N - 1] = 1;
+            ksel[3] = ksel[64] = ksel[N - 1] = 1;
+            double* h3[3];
+            for (int n = 0; n < 3; ++n) h3[n] = malloc(sizeof(double) * N * D);
+            orc_sagesla_bwd_sel(q, k, v, qi[0], qs[0], ki[0], ks[0], N, D, 1, kidx, keep, 3, 0.f,
+                                dout, qsel, ksel, h3[0], h3[1], h3[2], 7);
+            for (int64_t t = 0; t < N; ++t) {
+                if (qsel[t])
+                    CHECK(memcmp(h3[0] + t * D, g[0][0] + t * D, sizeof(double) * D) == 0,
+                          "sampled dq");
+                if (ksel[t])
+                    for (int n = 1; n < 3; ++n)
+                        CHECK(memcmp(h3[n] + t * D, g[0][n] + t * D, sizeof(double) * D) == 0,
+                              "sampled dk, dv");
+            }
+            for (int n = 0; n < 3; ++n) free(h3[n]);
+            free(qsel);
+            free(ksel);
+        }
         for (int r = 0; r < 2; ++r)
             for (int n = 0; n < 3; ++n) free(g[r][n]);
         free(dout);

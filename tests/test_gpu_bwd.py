@@ -1,6 +1,7 @@
 """GPU parity of the SageSLA backward (sage_sla_attn_bwd, through the C ABI)
-against the oracle's fp64 gradients, on the dense 1024-token case and on
-ragged sparse shapes with every branch mix.
+against the oracle's fp64 gradients, on the dense 1024-token case, on ragged
+sparse shapes with every branch mix, and at the benchmarked size (40 heads x
+75600 tokens, as bench.py --bwd runs it) on sampled rows.
 
 Every reference is built from the oracle's own quantized tensors and block
 selection, each first asserted equal to the GPU's.
@@ -20,7 +21,7 @@ import pytest
 import torch
 
 import bit_sparse_attention_amd as ssa
-from bit_sparse_attention_amd.workloads import make_qkv
+from bit_sparse_attention_amd.workloads import BENCH_WORKLOAD, WORKLOADS, make_qkv, make_workload
 from gpu_common import bits, flat, say
 
 pytestmark = pytest.mark.gpu
@@ -94,3 +95,50 @@ def test_bwd_repeat_runs_bit_identical():
     torch.cuda.synchronize()
     for a, b in zip(*runs):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_bwd_at_the_benchmarked_size(orc):
+    # the call bench.py --bwd times: the plan's one-call forward, then the
+    # backward on its quantized tensors and selection with the same seeded dO.
+    # Heads 0 and H-1: the oracle's quantization and selection checked equal
+    # to the GPU's, then dq at the first and last token of every query block
+    # and dk, dv at every key of the first, a middle and the ragged last key
+    # block, each computed by the oracle one row at a time.
+    w = WORKLOADS[BENCH_WORKLOAD]
+    say(f"[bwd-full] {w.name}: generating B={w.B} H={w.H} N={w.N}")
+    q, k, v = make_workload(w)
+    plan = ssa.SageSLAPlan(w.B, w.H, w.N, w.topk, linear=True, device=DEV)
+    plan.bind(*(t.to(DEV) for t in (q, k, v)))
+    plan.run()
+    g = torch.Generator().manual_seed(1)
+    dout = torch.randn(w.B, w.H, w.N, 128, generator=g).to(torch.bfloat16)
+    grads = ssa.sage_sla_attn_bwd(plan.q, plan.k, plan.v, plan.q_i8, plan.q_scale, plan.k_i8,
+                                  plan.k_scale, dout.to(DEV), plan.kidx, plan.keep, plan.branches,
+                                  plan.sm_scale)
+    BH, N, nqb, nkb = w.B * w.H, w.N, plan.nqb, plan.nkb
+    heads = [0, BH - 1]
+    sel = torch.tensor(heads, device=DEV)
+    got = [t.reshape(BH, N, 128).index_select(0, sel).cpu().numpy() for t in grads]
+    gq8, gk8 = (t.reshape(BH, N, 128).index_select(0, sel).cpu().numpy()
+                for t in (plan.q_i8, plan.k_i8))
+    gqs, gks = (t.reshape(BH, -1)[heads].cpu().numpy() for t in (plan.q_scale, plan.k_scale))
+    gkidx = plan.kidx.reshape(BH, nqb, plan.keep)[heads].cpu().numpy()
+    del grads
+    say(f"[bwd-full] {w.name}: GPU done; oracle quantization and selection of heads {heads}")
+    qb, kb, vb, gb = (bits(t).reshape(BH, N, 128)[heads] for t in (q, k, v, dout))
+    oqi, oqs, oki, oks, _ = orc.quant_qk(qb, kb)
+    assert np.array_equal(gq8, oqi) and np.array_equal(gk8, oki)
+    assert np.array_equal(gqs.view(np.uint32), oqs.view(np.uint32))
+    assert np.array_equal(gks.view(np.uint32), oks.view(np.uint32))
+    starts = 128 * np.arange(nqb)
+    qrows = np.unique(np.concatenate([starts, np.minimum(starts + 127, N - 1)]))
+    kcols = np.concatenate([np.arange(64 * j, min(64 * j + 64, N)) for j in (0, nkb // 2, nkb - 1)])
+    for x, bh in enumerate(heads):
+        okidx, _ = orc.block_mask_head(qb, kb, x, plan.keep)
+        assert np.array_equal(gkidx[x], okidx), bh
+        say(f"[bwd-full] {w.name}: oracle backward of head {bh} on {len(qrows)} query rows "
+            f"and {len(kcols)} keys")
+        want = orc.sagesla_bwd(qb, kb, vb, (oqi, oqs, oki, oks), x, gb, okidx, plan.branches,
+                               plan.sm_scale, qrows=qrows, kcols=kcols)
+        _check_grads([got[0][x][qrows], got[1][x][kcols], got[2][x][kcols]],
+                     [want[0][qrows], want[1][kcols], want[2][kcols]], f"{w.name} bh={bh}")

@@ -796,6 +796,29 @@ def test_backward_invariants(orc):
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("topk,branches", [(0.3, 3), (None, 1)])
+def test_backward_sampled_rows_equal_the_full_backward(orc, topk, branches):
+    # restricting the work to sampled rows and keys leaves those rows bit for
+    # bit as the full computation gives them
+    N, D = 700, 64
+    q, k, v = make_qkv(1, 1, N, D, seed=21)
+    qb, kb, vb = (_bits(t).reshape(1, N, D) for t in (q, k, v))
+    quant = orc.quant_qk(qb, kb)[:4]
+    kidx = None
+    if topk is not None:
+        kidx = orc.block_mask(qb, kb, orc.keep_blocks(N, topk))[0][0]
+    g = torch.Generator().manual_seed(22)
+    dout = _bits(torch.randn(1, N, D, generator=g).to(torch.bfloat16)).reshape(1, N, D)
+    full = orc.sagesla_bwd(qb, kb, vb, quant, 0, dout, kidx, branches=branches)
+    qrows = np.array([0, 5, 127, 128, 300, N - 1])
+    kcols = np.array([1, 63, 64, 200, 640, N - 1])
+    part = orc.sagesla_bwd(qb, kb, vb, quant, 0, dout, kidx, branches=branches, qrows=qrows,
+                           kcols=kcols)
+    assert np.array_equal(part[0][qrows], full[0][qrows])
+    for n in (1, 2):
+        assert np.array_equal(part[n][kcols], full[n][kcols])
+
+
 def test_w8a8_gemm_f64_is_the_exact_block_dequantization(orc):
     # an int64 matmul per K block (numpy), times the fp64 product of the two
     # fp32 scales, summed over blocks; and the fp32 chain stays within its
