@@ -20,6 +20,7 @@
 // forward's complement GEMM on the transposed selection), then per key block
 // the key and value gradients.
 #include <algorithm>
+#include <type_traits>
 
 #include "../../include/ssa.h"
 #include "common.hpp"
@@ -239,16 +240,25 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
                 dp[h] = mfma_bf16_32x32x16(va, dop[sd], dp[h]);
             }
         }
+        // dS; in a ragged last key block the keys past N (copies of key N-1,
+        // so p stays finite) are zeroed after the exp: one uniform branch per
+        // block instead of a masked branch per score
         bf16x8 dsb[4];
+        auto softmax = [&](auto ragged) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 32 * h + mfma32_row(lane, r);
-                const float p = key < kval ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[h][r], c, -mq)) : 0.f;
-                const float ds = p * (dp[h][r] - Dq) * sk;
-                dsb[2 * h + (r >> 3)][r & 7] = (__bf16)ds;
-            }
+                for (int r = 0; r < 16; ++r) {
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[h][r], c, -mq));
+                    if constexpr (decltype(ragged)::value) p = 32 * h + mfma32_row(lane, r) < kval ? p : 0.f;
+                    const float ds = p * (dp[h][r] - Dq) * sk;
+                    dsb[2 * h + (r >> 3)][r & 7] = (__bf16)ds;
+                }
+        };
+        if (kval == KBLK)
+            softmax(std::false_type{});
+        else
+            softmax(std::true_type{});
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
@@ -272,36 +282,48 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     }
 }
 
-// ---- dk, dv: one workgroup per (head, key block), 4 waves -----------------
+// ---- dk, dv: one workgroup per (head, key block), 8 waves -----------------
 // Over the query blocks that kept the block (every block when dense). The K
-// and V tiles of the block sit in LDS for the whole workgroup. Per query
-// block, wave w first takes its 32 queries t (32w + ...) against the 64 keys,
-// one 32-key tile h at a time:
-//   S = Q . K^T    (int8; lane holds key 32h + l32, queries 8(r/4)+4hi+r%4
-//                   of the wave's 32)
-//   dP = dO . V^T  (bf16; same layout)
-//   P = 2^(S c - m'), dS = P (dP - D) sq
-// and stores P and dS in LDS as the next products' B fragments (their
-// registers already are: k = 16 queries in the re-laid order, n = keys). Then
-// wave w accumulates channels 32w .. 32w+31 of
-//   dV^T += dO^T . P,  dK^T += Q^T . dS
-// over all 128 queries, the A fragments from the channel-first re-laid tiles
-// (rows 32w.. only). Every input is read once per workgroup, and loads are
-// issued ahead of their use: half of the second products' A fragments before
-// the first products, the next query block's rows and row statistics (m', D,
-// through a two-deep LDS buffer) before the second products.
-constexpr int KV_K = KBLK * HD;        // int8 K tile, 64 rows of 128 B
-constexpr int KV_V = KBLK * HD * 2;    // bf16 V tile, 64 rows of 256 B
-constexpr int KV_F = 8 * 2 * 64 * 16;  // one fragment set: [8 query steps][2 key tiles][64 lanes] x 16 B
+// and V tiles of the block sit in LDS for the whole workgroup. Per query block
+// the workgroup stages q_i8 (as int8, and widened to bf16) and dO in LDS, and
+// these two tiles serve every product:
+//   phase 1, wave w (queries 32(w&3) .., key tile h = w>>2):
+//     S = Q . K^T  (int8; lane holds key 32h + l32, queries 8(r/4)+4hi+r%4)
+//     dP = dO . V^T (bf16; same layout)
+//     P = 2^(S c - m'), dS = P (dP - D) sq, stored in LDS as the B fragments
+//     of phase 2 (k = 16 queries in the re-laid order, n = keys);
+//   phase 2, wave w (channels 32(w&3) .., queries 64(w>>2) ..):
+//     dV^T += dO^T . P, dK^T += Q^T . dS for both key tiles, the A fragments
+//     read from the row-major tiles with transposing LDS reads
+//     (ds_read_b64_tr_b16), which give a lane 4 consecutive queries of one
+//     channel; two reads make a fragment in the order P's registers hold.
+// The two query halves' sums are added once at the end. Only q_i8 and dO
+// cross the memory hierarchy per block pair (48 KB), loaded into registers a
+// whole query block ahead. The bf16 tiles [128 rows][256 B] keep 16-byte
+// chunk c of row r at chunk c ^ qswz(r): 16 consecutive rows at one chunk
+// (the row reads) and 4 consecutive rows at 4 chunks (the transposing reads)
+// both cover all banks.
+__device__ __forceinline__ int qswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+constexpr int DK_THREADS = 512;
+constexpr int KV_F = 8 * 2 * 64 * 16;          // one fragment set: [8 query steps][2 key tiles][64 lanes] x 16 B
+constexpr int DK_KT = 0;                       // int8 K tile [64][128 B], chunk c at c ^ swz8(r)
+constexpr int DK_VT = DK_KT + KBLK * HD;       // bf16 V tile [64][256 B], chunk c at c ^ (r & 15)
+constexpr int DK_QI = DK_VT + KBLK * HD * 2;   // int8 Q tile [128][128 B], chunk c at c ^ swz8(r)
+constexpr int DK_QB = DK_QI + QBLK * HD;       // bf16 Q tile [128][256 B], chunk c at c ^ qswz(r)
+constexpr int DK_GO = DK_QB + QBLK * HD * 2;   // bf16 dO tile, same layout
+constexpr int DK_PF = DK_GO + QBLK * HD * 2;   // P fragments
+constexpr int DK_DF = DK_PF + KV_F;            // dS fragments
+constexpr int DK_ST = DK_DF + KV_F;            // m' and D of the block's 128 queries
+constexpr int DK_LDS = DK_ST + 2 * QBLK * 4;
+static_assert(DK_LDS <= 160 * 1024, "one workgroup per CU");
+static_assert(DK_GO == DK_QB + QBLK * HD * 2 && 4 * 16 * 64 * 16 <= 2 * QBLK * HD * 2,
+              "the final partial sums fit the two bf16 tiles");
 
 template <bool DENSE>
-__global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[KV_K + KV_V + 2 * KV_F];
-    __shared__ __attribute__((aligned(16))) float stat[2][2][QBLK];  // [buffer][m', D][query]
-    uint8_t* kt = smem;
-    uint8_t* vt = smem + KV_K;
-    uint8_t* pf = smem + KV_K + KV_V;  // P fragments
-    uint8_t* df = pf + KV_F;           // dS fragments
+__global__ __launch_bounds__(DK_THREADS, 1) void dkdv_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[DK_LDS];
+    float* stat = reinterpret_cast<float*>(smem + DK_ST);  // [m', D][query]
     const int64_t item = blockIdx.x;
     if (item >= a.BH * a.nkb) return;
     const int64_t bh = item / a.nkb;
@@ -310,99 +332,127 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
               hi = lane >> 5;
     const int nval = min(KBLK, N - j * KBLK);
-    // the block's K (chunk c of key row r at slot c ^ swz8(r)) and V (chunk c
-    // of key row r at slot c ^ (r & 15)); rows past N re-read row N-1 (their
-    // P is zeroed)
-    for (int x = tid; x < KBLK * 8; x += 256) {
-        const int r = x >> 3, c = x & 7, rr = min(r, nval - 1);
-        *(i32x4*)(kt + r * 128 + 16 * (c ^ swz8(r))) =
+    // the block's K and V; rows past N re-read row N-1 (their P is zeroed)
+    {
+        const int r = tid >> 3, c = tid & 7, rr = min(r, nval - 1);
+        *(i32x4*)(smem + DK_KT + r * 128 + 16 * (c ^ swz8(r))) =
             *(const i32x4*)(a.k_i8 + (bh * N + (int64_t)j * KBLK + rr) * HD + 16 * c);
     }
-    for (int x = tid; x < KBLK * 16; x += 256) {
-        const int r = x >> 4, c = x & 15, rr = min(r, nval - 1);
-        *(u16x8*)(vt + r * 256 + 16 * (c ^ (r & 15))) =
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int x = tid + DK_THREADS * it, r = x >> 4, c = x & 15, rr = min(r, nval - 1);
+        *(u16x8*)(smem + DK_VT + r * 256 + 16 * (c ^ (r & 15))) =
             *(const u16x8*)(a.v + (bh * N + (int64_t)j * KBLK + rr) * HD + 8 * c);
     }
     const float sk = a.k_scale[bh * a.nkb + j];
-    f32x16 dva[2], dka[2];  // channels 32w + ..., key tiles 0, 1
-    dva[0] = dva[1] = dka[0] = dka[1] = f32x16{};
     const int cnt = DENSE ? nqb : a.counts[bh * a.nkb + j];
     const uint16_t* list = DENSE ? nullptr : a.lists + (bh * a.nkb + j) * (int64_t)nqb;
     auto qblock = [&](int x) { return DENSE ? x : (int)list[x]; };
-    // the lane's query row of query block i (S and dP A operands); rows past
-    // N re-read row N-1 (their P and dS are zeroed)
-    i32x4 qa[4];
-    bf16x8 ga[8];
-    auto load_rows = [&](int i) {
-        const int tr = min(i * QBLK + 32 * wave + l32, N - 1);
-        const int8_t* qp = a.q_i8 + (bh * N + tr) * HD;
-        const uint16_t* gp = a.dout + (bh * N + tr) * HD;
+
+    // one query block's q_i8 and dO rows (rows past N re-read row N-1: their
+    // P and dS are zeroed) and statistics, in registers until staged
+    u16x8 gpre[4];
+    i32x4 qpre[2];
+    float spre = 0.f;
+    auto prefetch = [&](int i) {
 #pragma unroll
-        for (int cq = 0; cq < 4; ++cq) qa[cq] = *(const i32x4*)(qp + 32 * cq + 16 * hi);
+        for (int it = 0; it < 4; ++it) {
+            const int x = tid + DK_THREADS * it, row = x >> 4, c = x & 15;
+            const int t = min(i * QBLK + row, N - 1);
+            gpre[it] = *(const u16x8*)(a.dout + (bh * N + t) * HD + 8 * c);
+        }
 #pragma unroll
-        for (int sd = 0; sd < 8; ++sd)
-            ga[sd] = __builtin_bit_cast(bf16x8, *(const u16x8*)(gp + 16 * sd + 8 * hi));
+        for (int it = 0; it < 2; ++it) {
+            const int x = tid + DK_THREADS * it, row = x >> 3, c = x & 7;
+            const int t = min(i * QBLK + row, N - 1);
+            qpre[it] = *(const i32x4*)(a.q_i8 + (bh * N + t) * HD + 16 * c);
+        }
+        if (tid < 2 * QBLK) {
+            const int t = min(i * QBLK + (tid & (QBLK - 1)), N - 1);
+            spre = (tid < QBLK ? a.mlog : a.dstat)[bh * N + t];
+        }
     };
-    // threads 0..127: m' of query tid of block i; 128..255: its D
-    auto load_stat = [&](int i) {
-        const int t = min(i * QBLK + (tid & (QBLK - 1)), N - 1);
-        return (tid < QBLK ? a.mlog : a.dstat)[bh * N + t];
+    auto stage = [&]() {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int x = tid + DK_THREADS * it, row = x >> 4, c = x & 15;
+            *(u16x8*)(smem + DK_GO + row * 256 + 16 * (c ^ qswz(row))) = gpre[it];
+        }
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int x = tid + DK_THREADS * it, row = x >> 3, c = x & 7;
+            *(i32x4*)(smem + DK_QI + row * 128 + 16 * (c ^ swz8(row))) = qpre[it];
+            bf16x8 w[2];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int b = (int)((uint32_t)qpre[it][e >> 2] << (24 - 8 * (e & 3))) >> 24;  // signed byte e
+                w[e >> 3][e & 7] = (__bf16)(float)b;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                *(bf16x8*)(smem + DK_QB + row * 256 + 16 * ((2 * c + h) ^ qswz(row))) = w[h];
+        }
+        if (tid < 2 * QBLK) stat[tid] = spre;
     };
-    if (cnt > 0) {
-        const int i0 = qblock(0);
-        load_rows(i0);
-        stat[0][tid >> 7][tid & (QBLK - 1)] = load_stat(i0);
-    }
-    __syncthreads();
-    const int64_t arow = (int64_t)(32 * wave + l32) * QBLK + 8 * hi;
+
+    f32x16 dva[2], dka[2];  // channels 32(w&3) + ..., key tiles 0, 1; this wave's query half
+    dva[0] = dva[1] = dka[0] = dka[1] = f32x16{};
+    if (cnt > 0) prefetch(qblock(0));
+    // phase-1 roles
+    const int qw = wave & 3, kh = wave >> 2;
+    const int key = 32 * kh + l32, trow = 32 * qw + l32;
+    const bool kok = key < nval;
+    // phase-2 roles and transposing-read addresses: lane l supplies row
+    // 16qs + 8t + 4hi + (l&15)/4 at channels col .. col+3
+    const int ct = wave & 3, qh = wave >> 2;
+    const int col = 32 * ct + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int rsub = 4 * hi + ((lane & 15) >> 2);
     for (int x = 0; x < cnt; ++x) {
         const int i = qblock(x);
-        const bool more = x + 1 < cnt;
+        stage();
+        __syncthreads();  // tiles and statistics of block i visible
+        if (x + 1 < cnt) prefetch(qblock(x + 1));
         const float sq = a.q_scale[bh * nqb + i];
         const float c = (sq * sk) * a.K32;
-        // the second products' A fragments: query steps 0..3 in flight during
-        // the first products, 4..7 during steps 0..3
-        u16x8 g2[8], q2[8];
-        const uint16_t* dot = a.dot + (bh * nqb + i) * (int64_t)HD * QBLK + arow;
-        const uint16_t* qt = a.qt16 + (bh * nqb + i) * (int64_t)HD * QBLK + arow;
-#pragma unroll
-        for (int qs = 0; qs < 4; ++qs) {
-            g2[qs] = *(const u16x8*)(dot + 16 * qs);
-            q2[qs] = *(const u16x8*)(qt + 16 * qs);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        const float* mrow = stat[x & 1][0];
-        const float* drow = stat[x & 1][1];
-#pragma unroll 1
-        for (int h = 0; h < 2; ++h) {
-            const int key = 32 * h + l32;
+        {
             i32x16 s = i32x16{};
             f32x16 dp = f32x16{};
 #pragma unroll
             for (int cq = 0; cq < 4; ++cq)
                 s = mfma_i8_32x32x32(
-                    qa[cq], *(const i32x4*)(kt + key * 128 + 16 * ((2 * cq + hi) ^ swz8(key))), s);
+                    *(const i32x4*)(smem + DK_QI + trow * 128 + 16 * ((2 * cq + hi) ^ swz8(trow))),
+                    *(const i32x4*)(smem + DK_KT + key * 128 + 16 * ((2 * cq + hi) ^ swz8(key))), s);
 #pragma unroll
             for (int sd = 0; sd < 8; ++sd)
                 dp = mfma_bf16_32x32x16(
-                    ga[sd], *(const bf16x8*)(vt + key * 256 + 16 * ((2 * sd + hi) ^ (key & 15))), dp);
-            const bool kok = key < nval;
+                    *(const bf16x8*)(smem + DK_GO + trow * 256 + 16 * ((2 * sd + hi) ^ qswz(trow))),
+                    *(const bf16x8*)(smem + DK_VT + key * 256 + 16 * ((2 * sd + hi) ^ (key & 15))), dp);
+            // P and dS; in the ragged last query or key block the rows and keys
+            // past N (clamped copies of valid ones, so p stays finite) are
+            // zeroed after the exp, under one uniform branch
             f32x16 pr;
+            auto softmax = [&](auto ragged) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r0 = 32 * wave + 8 * g + 4 * hi;  // queries of registers 4g .. 4g+3
-                const f32x4 mq = *(const f32x4*)(mrow + r0);
-                const f32x4 Dq = *(const f32x4*)(drow + r0);
+                for (int g = 0; g < 4; ++g) {
+                    const int r0 = 32 * qw + 8 * g + 4 * hi;  // queries of registers 4g .. 4g+3
+                    const f32x4 mq = *(const f32x4*)(stat + r0);
+                    const f32x4 Dq = *(const f32x4*)(stat + QBLK + r0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g + e;
-                    const bool ok = kok && i * QBLK + r0 + e < N;
-                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], c, -mq[e])) : 0.f;
-                    pr[r] = p;
-                    dp[r] = p * (dp[r] - Dq[e]) * sq;
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g + e;
+                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], c, -mq[e]));
+                        if constexpr (decltype(ragged)::value)
+                            p = (kok && i * QBLK + r0 + e < N) ? p : 0.f;
+                        pr[r] = p;
+                        dp[r] = p * (dp[r] - Dq[e]) * sq;
+                    }
                 }
-            }
-            // fragment [query step 2w + ks][key tile h][lane]
+            };
+            if (nval == KBLK && (i + 1) * QBLK <= N)
+                softmax(std::false_type{});
+            else
+                softmax(std::true_type{});
+            // fragment [query step 2qw + ks][key tile kh][lane]
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 bf16x8 pb, db;
@@ -411,43 +461,53 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
                     pb[e] = (__bf16)pr[8 * ks + e];
                     db[e] = (__bf16)dp[8 * ks + e];
                 }
-                const int slot = ((2 * wave + ks) * 2 + h) * 64 + lane;
-                *(bf16x8*)(pf + 16 * slot) = pb;
-                *(bf16x8*)(df + 16 * slot) = db;
+                const int slot = ((2 * qw + ks) * 2 + kh) * 64 + lane;
+                *(bf16x8*)(smem + DK_PF + 16 * slot) = pb;
+                *(bf16x8*)(smem + DK_DF + 16 * slot) = db;
             }
         }
-        // the next query block's rows and statistics, in flight during the
-        // second products
-        float stn = 0.f;
-        if (more) {
-            const int in = qblock(x + 1);
-            load_rows(in);
-            stn = load_stat(in);
-        }
-        __syncthreads();
+        __syncthreads();  // fragments visible
 #pragma unroll
-        for (int qs = 4; qs < 8; ++qs) {
-            g2[qs] = *(const u16x8*)(dot + 16 * qs);
-            q2[qs] = *(const u16x8*)(qt + 16 * qs);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int qq = 0; qq < 4; ++qq) {
+            const int qs = 4 * qh + qq;
+            i16x4 gp[2], qp[2];
 #pragma unroll
-        for (int qs = 0; qs < 8; ++qs) {
-            const bf16x8 gb = __builtin_bit_cast(bf16x8, g2[qs]);
-            const bf16x8 qb = __builtin_bit_cast(bf16x8, q2[qs]);
+            for (int t = 0; t < 2; ++t) {
+                const int row = 16 * qs + 8 * t + rsub;
+                const int off = row * 256 + 16 * ((col >> 3) ^ qswz(row)) + 8 * ((col >> 2) & 1);
+                gp[t] = lds_read_tr16(smem + DK_GO + off);
+                qp[t] = lds_read_tr16(smem + DK_QB + off);
+            }
+            const u32x2 g0 = __builtin_bit_cast(u32x2, gp[0]), g1 = __builtin_bit_cast(u32x2, gp[1]);
+            const u32x2 q0 = __builtin_bit_cast(u32x2, qp[0]), q1 = __builtin_bit_cast(u32x2, qp[1]);
+            const bf16x8 gT = __builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]});
+            const bf16x8 qT = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int slot = (qs * 2 + h) * 64 + lane;
-                dva[h] = mfma_bf16_32x32x16(gb, *(const bf16x8*)(pf + 16 * slot), dva[h]);
-                dka[h] = mfma_bf16_32x32x16(qb, *(const bf16x8*)(df + 16 * slot), dka[h]);
+                dva[h] = mfma_bf16_32x32x16(gT, *(const bf16x8*)(smem + DK_PF + 16 * slot), dva[h]);
+                dka[h] = mfma_bf16_32x32x16(qT, *(const bf16x8*)(smem + DK_DF + 16 * slot), dka[h]);
             }
         }
-        // the buffer (x + 1) & 1 was last read by the first products of
-        // query block x - 1, before this iteration's first barrier
-        if (more) stat[(x + 1) & 1][tid >> 7][tid & (QBLK - 1)] = stn;
-        __syncthreads();  // the next query block rewrites the fragments
+        __syncthreads();  // the next block rewrites the tiles and fragments
     }
-    // lane (key column l32 of tile h, hi) holds channels 32w + 8(r/4) + 4hi + r%4
+    // add the second query half's sums to the first's: [ct][16-byte unit u][lane]
+    f32x4* red = reinterpret_cast<f32x4*>(smem + DK_QB);
+    auto unit = [&](int u) -> f32x4& { return red[(ct * 16 + u) * 64 + lane]; };
+    if (qh == 1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                unit(4 * h + q4) = f32x4{dva[h][4 * q4], dva[h][4 * q4 + 1], dva[h][4 * q4 + 2],
+                                         dva[h][4 * q4 + 3]};
+                unit(8 + 4 * h + q4) = f32x4{dka[h][4 * q4], dka[h][4 * q4 + 1], dka[h][4 * q4 + 2],
+                                             dka[h][4 * q4 + 3]};
+            }
+    }
+    __syncthreads();
+    if (qh == 1) return;
+    // lane (key column l32 of tile h, hi) holds channels 32ct + 8(r/4) + 4hi + r%4
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int u = j * KBLK + 32 * h + l32;
@@ -456,11 +516,14 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
         float* krow = a.dk + (bh * N + u) * HD;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const int d = 32 * wave + 8 * q4 + 4 * hi;
-            *(f32x4*)(vrow + d) = f32x4{dva[h][4 * q4], dva[h][4 * q4 + 1], dva[h][4 * q4 + 2],
-                                        dva[h][4 * q4 + 3]};
-            *(f32x4*)(krow + d) = f32x4{dka[h][4 * q4] * a.sm, dka[h][4 * q4 + 1] * a.sm,
-                                        dka[h][4 * q4 + 2] * a.sm, dka[h][4 * q4 + 3] * a.sm};
+            const int d = 32 * ct + 8 * q4 + 4 * hi;
+            const f32x4 ov = unit(4 * h + q4), ok4 = unit(8 + 4 * h + q4);
+            *(f32x4*)(vrow + d) = f32x4{dva[h][4 * q4] + ov[0], dva[h][4 * q4 + 1] + ov[1],
+                                        dva[h][4 * q4 + 2] + ov[2], dva[h][4 * q4 + 3] + ov[3]};
+            *(f32x4*)(krow + d) = f32x4{(dka[h][4 * q4] + ok4[0]) * a.sm,
+                                        (dka[h][4 * q4 + 1] + ok4[1]) * a.sm,
+                                        (dka[h][4 * q4 + 2] + ok4[2]) * a.sm,
+                                        (dka[h][4 * q4 + 3] + ok4[3]) * a.sm};
         }
     }
 }
@@ -741,10 +804,10 @@ hipError_t launch_bwd_sparse(const BwdArgs& a, hipStream_t st) {
     const int64_t nq = a.BH * a.nqb, nk = a.BH * a.nkb;
     if (a.kidx) {
         hipLaunchKernelGGL(dq_kernel<false>, dim3((unsigned)nq), dim3(256), 0, st, a);
-        hipLaunchKernelGGL(dkdv_kernel<false>, dim3((unsigned)nk), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(dkdv_kernel<false>, dim3((unsigned)nk), dim3(DK_THREADS), 0, st, a);
     } else {
         hipLaunchKernelGGL(dq_kernel<true>, dim3((unsigned)nq), dim3(256), 0, st, a);
-        hipLaunchKernelGGL(dkdv_kernel<true>, dim3((unsigned)nk), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(dkdv_kernel<true>, dim3((unsigned)nk), dim3(DK_THREADS), 0, st, a);
     }
     return hipGetLastError();
 }
