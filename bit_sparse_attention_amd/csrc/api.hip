@@ -226,7 +226,7 @@ StepWs ws_step(const Dims& d, bool linear) {
 // tiles, the inverse selection lists and the linear branch's gradient states
 struct BwdWs {
     AttnWs attn;
-    size_t mlog, dstat, kt16, qt16, dot, counts, lists, gf, gs, gs_lo, gtot, msel, gc, total;
+    size_t mlog, dstat, kt16, counts, lists, gf, gs, gs_lo, gtot, msel, gc, total;
 };
 BwdWs ws_bwd(const Dims& d, bool sel, bool linear) {
     BwdWs w{};
@@ -240,8 +240,6 @@ BwdWs ws_bwd(const Dims& d, bool sel, bool linear) {
     w.mlog = take((size_t)d.BH * d.N * 4);
     w.dstat = take((size_t)d.BH * d.N * 4);
     w.kt16 = take((size_t)d.BH * d.nkb * HD * KBLK * 2);
-    w.qt16 = take((size_t)d.BH * d.nqb * HD * QBLK * 2);
-    w.dot = take((size_t)d.BH * d.nqb * HD * QBLK * 2);
     if (sel) {
         w.counts = take((size_t)d.BH * d.nkb * 4);
         w.lists = take((size_t)d.BH * d.nkb * d.nqb * 2);
@@ -764,8 +762,6 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
         b.v = v;
         b.dout = dout;
         b.kt16 = (const uint16_t*)(base + w.kt16);
-        b.qt16 = (const uint16_t*)(base + w.qt16);
-        b.dot = (const uint16_t*)(base + w.dot);
         b.kidx = kidx;
         b.keep = (int)keep;
         b.lists = sel ? (const uint16_t*)(base + w.lists) : nullptr;
@@ -782,8 +778,7 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
         b.dk = dk;
         b.dv = dv;
         if (e == hipSuccess)
-            e = launch_bwd_prep(b, dout, (uint16_t*)(base + w.kt16), (uint16_t*)(base + w.qt16),
-                                (uint16_t*)(base + w.dot), st);
+            e = launch_bwd_prep(b, (uint16_t*)(base + w.kt16), st);
         if (e == hipSuccess) e = launch_bwd_sparse(b, st);
         if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (sparse branch)");
     }

@@ -782,14 +782,9 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_k_kernel(const uint16_t* __res
 
 // ---------------------------------------------------------------------------
 
-hipError_t launch_bwd_prep(const BwdArgs& a, const uint16_t* dout, uint16_t* kt16, uint16_t* qt16,
-                           uint16_t* dot, hipStream_t st) {
+hipError_t launch_bwd_prep(const BwdArgs& a, uint16_t* kt16, hipStream_t st) {
     hipLaunchKernelGGL((transpose_tiles_kernel<int8_t, KBLK>), dim3(a.nkb, a.BH), dim3(256), 0, st,
                        a.k_i8, a.N, a.nkb, kt16);
-    hipLaunchKernelGGL((transpose_tiles_kernel<int8_t, QBLK>), dim3(a.nqb, a.BH), dim3(256), 0, st,
-                       a.q_i8, a.N, a.nqb, qt16);
-    hipLaunchKernelGGL((transpose_tiles_kernel<uint16_t, QBLK>), dim3(a.nqb, a.BH), dim3(256), 0,
-                       st, dout, a.N, a.nqb, dot);
     return hipGetLastError();
 }
 

@@ -63,8 +63,6 @@ struct BwdArgs {
     const uint16_t* v;       // raw bf16 V [BH][N][128]
     const uint16_t* dout;    // bf16 dL/dO [BH][N][128]
     const uint16_t* kt16;    // bf16 k_i8, channel-first per key block [BH][nkb][128][64]
-    const uint16_t* qt16;    // bf16 q_i8, channel-first per query block [BH][nqb][128][128]
-    const uint16_t* dot;     // dout, channel-first per query block [BH][nqb][128][128]
     const int32_t* kidx;     // [BH][nqb][keep] or null (dense)
     int keep;
     const uint16_t* lists;   // [BH][nkb][nqb]: query blocks that kept each key block
@@ -77,8 +75,7 @@ struct BwdArgs {
     const float* dstat;      // [BH][N] dO . o_s
     float *dq, *dk, *dv;     // fp32 [BH][N][128]
 };
-hipError_t launch_bwd_prep(const BwdArgs& a, const uint16_t* dout, uint16_t* kt16, uint16_t* qt16,
-                           uint16_t* dot, hipStream_t st);
+hipError_t launch_bwd_prep(const BwdArgs& a, uint16_t* kt16, hipStream_t st);
 hipError_t launch_inv_lists(const int32_t* kidx, int keep, int64_t BH, int nqb, int nkb,
                             uint16_t* lists, int32_t* counts, hipStream_t st);
 hipError_t launch_bwd_sparse(const BwdArgs& a, hipStream_t st);
