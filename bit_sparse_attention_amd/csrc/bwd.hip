@@ -537,8 +537,12 @@ __device__ __forceinline__ int state_pos(int d) {
     return (d & ~15) | (((d >> 2) & 1) << 3) | (((d >> 3) & 1) << 2) | (d & 3);
 }
 
-__device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
-__device__ __forceinline__ float dphi_f(float x) { return x > 0.f ? 1.f : __expf(x); }
+// elu + 1 without branches: the exp of min(x, 0) is finite and is selected
+// only for x <= 0
+__device__ __forceinline__ float phi_f(float x) {
+    const float ex = __expf(fminf(x, 0.f));
+    return x > 0.f ? x + 1.f : ex;
+}
 
 // fp32 x fp32 -> fp32 on the matrix cores: lane l supplies A[l & 31][l >> 5]
 // and B[l >> 5][l & 31]; the result has the 32x32 layout of mfma32_row.
@@ -582,14 +586,15 @@ __device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int
     u16x8 r[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        const int c = tid + 256 * it, tt = c >> 4;
-        r[it] = tt < nval ? *(const u16x8*)(src + (int64_t)tt * HD + 8 * (c & 15)) : u16x8{};
+        // rows past nval re-read row nval-1 (finite values, scaled to 0 below)
+        const int c = tid + 256 * it, tt = min(c >> 4, nval - 1);
+        r[it] = *(const u16x8*)(src + (int64_t)tt * HD + 8 * (c & 15));
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int c = tid + 256 * it, tt = c >> 4, d0 = 8 * (c & 15);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) X[tt * LB_P + d0 + m] = tt < nval ? fn(bf2f(r[it][m])) : 0.f;
+        for (int m = 0; m < 8; ++m) X[tt * LB_P + d0 + m] = fn(bf2f(r[it][m])) * (tt < nval ? 1.f : 0.f);
     }
 }
 
@@ -685,18 +690,28 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __res
             dden_s[tid] = h0 + tid < nt ? -(gop[0][tid] + gop[1][tid]) / (dn * dn) : 0.f;
         }
         __syncthreads();
+        // the row check only in a ragged last piece (one uniform branch)
+        auto store_dq = [&](auto ragged, auto acc) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int d = 32 * (ct0 + c) + l32;
+            for (int c = 0; c < 2; ++c) {
+                const int d = 32 * (ct0 + c) + l32;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = 32 * rt + mfma32_row(lane, r);
-                if (h0 + t >= nt) continue;
-                const float g =
-                    (u[c][r] / den_s[t] + zv[d] * dden_s[t]) * fminf(As[t * LB_P + d], 1.f);
-                const int64_t o = (bh * N + i * QBLK + h0 + t) * HD + d;
-                dq[o] = accumulate ? dq[o] + g : g;
+                for (int r = 0; r < 16; ++r) {
+                    const int t = 32 * rt + mfma32_row(lane, r);
+                    if (decltype(ragged)::value && h0 + t >= nt) continue;
+                    const float g =
+                        (u[c][r] / den_s[t] + zv[d] * dden_s[t]) * fminf(As[t * LB_P + d], 1.f);
+                    const int64_t o = (bh * N + i * QBLK + h0 + t) * HD + d;
+                    dq[o] = decltype(acc)::value ? dq[o] + g : g;
+                }
             }
+        };
+        if (h0 + LB_T <= nt) {
+            if (accumulate) store_dq(std::false_type{}, std::true_type{});
+            else store_dq(std::false_type{}, std::false_type{});
+        } else {
+            if (accumulate) store_dq(std::true_type{}, std::true_type{});
+            else store_dq(std::true_type{}, std::false_type{});
         }
         for (int x = tid; x < LB_T * HD; x += 256) {
             const int tt = x >> 7, e = x & 127;
@@ -765,18 +780,28 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_k_kernel(const uint16_t* __res
             gv[c] = mfma_f32_32x32x2(fa, Ms[(k0 + hi) * LB_P + n], gv[c]);  // Gc[d = k][e = n]
         }
     }
+    // the key check only in the ragged last block (one uniform branch)
+    auto store = [&](auto ragged, auto acc) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int n = 32 * (ct0 + c) + l32;
+        for (int c = 0; c < 2; ++c) {
+            const int n = 32 * (ct0 + c) + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int uu = 32 * rt + mfma32_row(lane, r);
-            if (uu >= nk) continue;
-            const int64_t o = (bh * N + j * KBLK + uu) * HD + n;
-            const float g = (gk[c][r] + wv[n]) * fminf(Fs[uu * LB_P + n], 1.f);
-            dk[o] = accumulate ? dk[o] + g : g;
-            dv[o] = accumulate ? dv[o] + gv[c][r] : gv[c][r];
+            for (int r = 0; r < 16; ++r) {
+                const int uu = 32 * rt + mfma32_row(lane, r);
+                if (decltype(ragged)::value && uu >= nk) continue;
+                const int64_t o = (bh * N + j * KBLK + uu) * HD + n;
+                const float g = (gk[c][r] + wv[n]) * fminf(Fs[uu * LB_P + n], 1.f);
+                dk[o] = decltype(acc)::value ? dk[o] + g : g;
+                dv[o] = decltype(acc)::value ? dv[o] + gv[c][r] : gv[c][r];
+            }
         }
+    };
+    if (nk == KBLK) {
+        if (accumulate) store(std::false_type{}, std::true_type{});
+        else store(std::false_type{}, std::false_type{});
+    } else {
+        if (accumulate) store(std::true_type{}, std::true_type{});
+        else store(std::true_type{}, std::false_type{});
     }
 }
 

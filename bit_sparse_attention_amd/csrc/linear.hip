@@ -108,7 +108,10 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float f = bf2f(kk[it][e]);
-                    const float ph = ok ? (f > 0.f ? f + 1.f : __expf(f)) : 0.f;
+                    // elu + 1 without branches: the exp of min(f, 0) is finite and
+                    // is selected only for f <= 0; invalid tokens are scaled to 0
+                    const float ex = __expf(fminf(f, 0.f));
+                    const float ph = (f > 0.f ? f + 1.f : ex) * (ok ? 1.f : 0.f);
                     __bf16 h, l;
                     split_bf16(ph, h, l);
                     fkh[(8 * ch + e) * TP + u] = __builtin_bit_cast(uint16_t, h);
