@@ -2,8 +2,8 @@
 // the sparse kernel reads.
 //
 // TurboDiffusion pages, page 5 "Four Technical Pillars", Pillar Two: the
-// block interactions the sparse part skips are covered by a light global
-// linear-attention term. With phi = elu + 1 on raw K, each 64-token key block
+// block interactions the sparse part skips are handled by a cheap
+// linear-attention term instead. With phi = elu + 1 on raw K, each 64-token key block
 // j contributes the state h_j = sum_u phi(k_u) v_u^T (128 x 128) and
 // z_j = sum_u phi(k_u). A query block needs the sums over the key blocks it did
 // NOT keep. They are formed as H_i = H_total - sum_{j kept} h_j: H_total in

@@ -5,8 +5,8 @@
  *   Pillar One (SageAttention): attention computed in 8-bit integers, with a
  *   smoothing step that tames outliers.
  *   Pillar Two (SLA): only the most important block interactions are computed
- *   exactly (about 10% of them), a light global linear-attention term covers
- *   the rest; the two stack as "SageSLA".
+ *   exactly (about 10% of them), a cheap linear-attention term handles the
+ *   others; the two stack as "SageSLA".
  *   "Hands-On Tutorial": --attention_type sagesla selects it, --sla_topk is the
  *   fraction of connections kept (0.1 -> 90% sparsity).
  * The concrete numerics (block sizes, scale formula, rounding, block scoring,

@@ -9,8 +9,8 @@
  * Source of the method: the TurboDiffusion pages, page 5 "Four Technical
  * Pillars" (Pillar One: SageAttention quantizes attention to INT8 and smooths
  * outliers; Pillar Two: SLA keeps the important block interactions, about 10%
- * of them, and covers the rest with a light global linear attention; the two
- * stack as "SageSLA") and page 5 "Hands-On Tutorial" (--attention_type
+ * of them, and a cheap linear-attention term stands in for the others; the
+ * two stack as "SageSLA") and page 5 "Hands-On Tutorial" (--attention_type
  * sagesla, --sla_topk = fraction of connections kept). Where the pages are
  * silent the concrete reading is stated at each function.
  */

@@ -9,7 +9,7 @@
  * What it computes (TurboDiffusion pages; page 5 "Four Technical Pillars",
  * Pillar One (SageAttention: INT8 attention with smoothing of outliers) and
  * Pillar Two (SLA: a small set of important block interactions computed
- * exactly plus a light global linear-attention term, 10% of connections kept
+ * exactly, the others through a cheap linear-attention term, 10% of connections kept
  * at --sla_topk 0.1), and the "Hands-On Tutorial" flags):
  *
  *   K mean smoothing, per-block INT8 quantization of Q (128-token blocks) and

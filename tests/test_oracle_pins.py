@@ -509,7 +509,7 @@ def test_flip_window_covers_a_lagging_normalizer(orc, lag):
 
 
 # --------------------------------------------------------------------------
-# linear branch (page 5, Pillar Two: light global linear attention)
+# linear branch (page 5, Pillar Two: the linear-attention term)
 
 def _phi(x):
     return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
