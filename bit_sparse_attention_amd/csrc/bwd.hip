@@ -282,48 +282,48 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     }
 }
 
-// ---- dk, dv: one workgroup per (head, key block), 8 waves -----------------
-// Over the query blocks that kept the block (every block when dense). The K
-// and V tiles of the block sit in LDS for the whole workgroup. Per query block
-// the workgroup stages q_i8 (as int8, and widened to bf16) and dO in LDS, and
-// these two tiles serve every product:
-//   phase 1, wave w (queries 32(w&3) .., key tile h = w>>2):
+// ---- dk, dv: one workgroup per (head, key block), 4 waves, two per CU -----
+// Over the query blocks that kept the block (every block when dense), each in
+// two steps of 64 queries. The V tile of the block sits in LDS and each
+// wave's K fragments in registers for the workgroup's whole life. Per step
+// the workgroup stages q_i8 (as int8, and widened to bf16) and dO of the 64
+// queries in LDS, and these tiles serve every product:
+//   phase 1, wave w (queries 32(w&1) .. of the step, key tile h = w>>1):
 //     S = Q . K^T  (int8; lane holds key 32h + l32, queries 8(r/4)+4hi+r%4)
 //     dP = dO . V^T (bf16; same layout)
 //     P = 2^(S c - m'), dS = P (dP - D) sq, stored in LDS as the B fragments
 //     of phase 2 (k = 16 queries in the re-laid order, n = keys);
-//   phase 2, wave w (channels 32(w&3) .., queries 64(w>>2) ..):
-//     dV^T += dO^T . P, dK^T += Q^T . dS for both key tiles, the A fragments
-//     read from the row-major tiles with transposing LDS reads
-//     (ds_read_b64_tr_b16), which give a lane 4 consecutive queries of one
-//     channel; two reads make a fragment in the order P's registers hold.
-// The two query halves' sums are added once at the end. Only q_i8 and dO
-// cross the memory hierarchy per block pair (48 KB), loaded into registers a
-// whole query block ahead. The bf16 tiles [128 rows][256 B] keep 16-byte
+//   phase 2, wave w (channels 32w ..):
+//     dV^T += dO^T . P, dK^T += Q^T . dS over the step's 64 queries, for both
+//     key tiles, the A fragments read from the row-major tiles with
+//     transposing LDS reads (ds_read_b64_tr_b16), which give a lane 4
+//     consecutive queries of one channel; two reads make a fragment in the
+//     order P's registers hold.
+// Only q_i8 and dO cross the memory hierarchy per block pair (48 KB), loaded
+// into registers a step ahead. The bf16 tiles [64 rows][256 B] keep 16-byte
 // chunk c of row r at chunk c ^ qswz(r): 16 consecutive rows at one chunk
 // (the row reads) and 4 consecutive rows at 4 chunks (the transposing reads)
-// both cover all banks.
+// both cover all banks. 72.5 KB of LDS, so that two workgroups share a CU
+// and each runs while the other waits at a barrier.
 __device__ __forceinline__ int qswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-constexpr int DK_THREADS = 512;
-constexpr int KV_F = 8 * 2 * 64 * 16;          // one fragment set: [8 query steps][2 key tiles][64 lanes] x 16 B
-constexpr int DK_KT = 0;                       // int8 K tile [64][128 B], chunk c at c ^ swz8(r)
-constexpr int DK_VT = DK_KT + KBLK * HD;       // bf16 V tile [64][256 B], chunk c at c ^ (r & 15)
-constexpr int DK_QI = DK_VT + KBLK * HD * 2;   // int8 Q tile [128][128 B], chunk c at c ^ swz8(r)
-constexpr int DK_QB = DK_QI + QBLK * HD;       // bf16 Q tile [128][256 B], chunk c at c ^ qswz(r)
-constexpr int DK_GO = DK_QB + QBLK * HD * 2;   // bf16 dO tile, same layout
-constexpr int DK_PF = DK_GO + QBLK * HD * 2;   // P fragments
+constexpr int DK_THREADS = 256;
+constexpr int DK_Q = 64;                       // queries per step
+constexpr int KV_F = 4 * 2 * 64 * 16;          // one fragment set: [4 query steps][2 key tiles][64 lanes] x 16 B
+constexpr int DK_VT = 0;                       // bf16 V tile [64][256 B], chunk c at c ^ (r & 15)
+constexpr int DK_QI = DK_VT + KBLK * HD * 2;   // int8 Q tile [64][128 B], chunk c at c ^ swz8(r)
+constexpr int DK_QB = DK_QI + DK_Q * HD;       // bf16 Q tile [64][256 B], chunk c at c ^ qswz(r)
+constexpr int DK_GO = DK_QB + DK_Q * HD * 2;   // bf16 dO tile, same layout
+constexpr int DK_PF = DK_GO + DK_Q * HD * 2;   // P fragments
 constexpr int DK_DF = DK_PF + KV_F;            // dS fragments
-constexpr int DK_ST = DK_DF + KV_F;            // m' and D of the block's 128 queries
-constexpr int DK_LDS = DK_ST + 2 * QBLK * 4;
-static_assert(DK_LDS <= 160 * 1024, "one workgroup per CU");
-static_assert(DK_GO == DK_QB + QBLK * HD * 2 && 4 * 16 * 64 * 16 <= 2 * QBLK * HD * 2,
-              "the final partial sums fit the two bf16 tiles");
+constexpr int DK_ST = DK_DF + KV_F;            // m' and D of the step's 64 queries
+constexpr int DK_LDS = DK_ST + 2 * DK_Q * 4;
+static_assert(2 * DK_LDS <= 160 * 1024, "two workgroups per CU");
 
 template <bool DENSE>
-__global__ __launch_bounds__(DK_THREADS, 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(DK_THREADS, 2) void dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[DK_LDS];
-    float* stat = reinterpret_cast<float*>(smem + DK_ST);  // [m', D][query]
+    float* stat = reinterpret_cast<float*>(smem + DK_ST);  // [m', D][query of the step]
     const int64_t item = blockIdx.x;
     if (item >= a.BH * a.nkb) return;
     const int64_t bh = item / a.nkb;
@@ -332,44 +332,52 @@ __global__ __launch_bounds__(DK_THREADS, 1) void dkdv_kernel(BwdArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
               hi = lane >> 5;
     const int nval = min(KBLK, N - j * KBLK);
-    // the block's K and V; rows past N re-read row N-1 (their P is zeroed)
-    {
-        const int r = tid >> 3, c = tid & 7, rr = min(r, nval - 1);
-        *(i32x4*)(smem + DK_KT + r * 128 + 16 * (c ^ swz8(r))) =
-            *(const i32x4*)(a.k_i8 + (bh * N + (int64_t)j * KBLK + rr) * HD + 16 * c);
-    }
+    // the block's V in LDS; rows past N re-read row N-1 (their P is zeroed)
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < 4; ++it) {
         const int x = tid + DK_THREADS * it, r = x >> 4, c = x & 15, rr = min(r, nval - 1);
         *(u16x8*)(smem + DK_VT + r * 256 + 16 * (c ^ (r & 15))) =
             *(const u16x8*)(a.v + (bh * N + (int64_t)j * KBLK + rr) * HD + 8 * c);
     }
+    // phase-1 roles; the wave's K fragments (key 32kh + l32, channels
+    // 32cq + 16hi ..) stay in registers
+    const int qw = wave & 1, kh = wave >> 1;
+    const int key = 32 * kh + l32, trow = 32 * qw + l32;
+    const bool kok = key < nval;
+    i32x4 kfr[4];
+    {
+        const int8_t* kp = a.k_i8 + (bh * N + (int64_t)j * KBLK + min(key, nval - 1)) * HD;
+#pragma unroll
+        for (int cq = 0; cq < 4; ++cq) kfr[cq] = *(const i32x4*)(kp + 32 * cq + 16 * hi);
+    }
     const float sk = a.k_scale[bh * a.nkb + j];
     const int cnt = DENSE ? nqb : a.counts[bh * a.nkb + j];
     const uint16_t* list = DENSE ? nullptr : a.lists + (bh * a.nkb + j) * (int64_t)nqb;
+    // steps: (kept query block x, half f), halves entirely past N skipped
     auto qblock = [&](int x) { return DENSE ? x : (int)list[x]; };
+    auto has_half = [&](int i, int f) { return i * QBLK + DK_Q * f < N; };
 
-    // one query block's q_i8 and dO rows (rows past N re-read row N-1: their
-    // P and dS are zeroed) and statistics, in registers until staged
+    // one step's q_i8 and dO rows (rows past N re-read row N-1: their P and
+    // dS are zeroed) and statistics, in registers until staged
     u16x8 gpre[4];
     i32x4 qpre[2];
     float spre = 0.f;
-    auto prefetch = [&](int i) {
+    auto prefetch = [&](int q0) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int x = tid + DK_THREADS * it, row = x >> 4, c = x & 15;
-            const int t = min(i * QBLK + row, N - 1);
+            const int t = min(q0 + row, N - 1);
             gpre[it] = *(const u16x8*)(a.dout + (bh * N + t) * HD + 8 * c);
         }
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int x = tid + DK_THREADS * it, row = x >> 3, c = x & 7;
-            const int t = min(i * QBLK + row, N - 1);
+            const int t = min(q0 + row, N - 1);
             qpre[it] = *(const i32x4*)(a.q_i8 + (bh * N + t) * HD + 16 * c);
         }
-        if (tid < 2 * QBLK) {
-            const int t = min(i * QBLK + (tid & (QBLK - 1)), N - 1);
-            spre = (tid < QBLK ? a.mlog : a.dstat)[bh * N + t];
+        if (tid < 2 * DK_Q) {
+            const int t = min(q0 + (tid & (DK_Q - 1)), N - 1);
+            spre = (tid < DK_Q ? a.mlog : a.dstat)[bh * N + t];
         }
     };
     auto stage = [&]() {
@@ -392,26 +400,29 @@ __global__ __launch_bounds__(DK_THREADS, 1) void dkdv_kernel(BwdArgs a) {
             for (int h = 0; h < 2; ++h)
                 *(bf16x8*)(smem + DK_QB + row * 256 + 16 * ((2 * c + h) ^ qswz(row))) = w[h];
         }
-        if (tid < 2 * QBLK) stat[tid] = spre;
+        if (tid < 2 * DK_Q) stat[tid] = spre;
     };
 
-    f32x16 dva[2], dka[2];  // channels 32(w&3) + ..., key tiles 0, 1; this wave's query half
+    f32x16 dva[2], dka[2];  // channels 32w + ..., key tiles 0, 1
     dva[0] = dva[1] = dka[0] = dka[1] = f32x16{};
-    if (cnt > 0) prefetch(qblock(0));
-    // phase-1 roles
-    const int qw = wave & 3, kh = wave >> 2;
-    const int key = 32 * kh + l32, trow = 32 * qw + l32;
-    const bool kok = key < nval;
-    // phase-2 roles and transposing-read addresses: lane l supplies row
+    // phase-2 transposing-read addresses: lane l supplies row
     // 16qs + 8t + 4hi + (l&15)/4 at channels col .. col+3
-    const int ct = wave & 3, qh = wave >> 2;
-    const int col = 32 * ct + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int col = 32 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const int rsub = 4 * hi + ((lane & 15) >> 2);
-    for (int x = 0; x < cnt; ++x) {
+    int x = 0, f = 0;
+    if (cnt > 0) prefetch(qblock(0) * QBLK);
+    while (x < cnt) {
         const int i = qblock(x);
+        const int q0 = i * QBLK + DK_Q * f;
+        // the step after this one
+        int xn = x, fn = f + 1;
+        if (fn == 2 || !has_half(i, fn)) {
+            xn = x + 1;
+            fn = 0;
+        }
         stage();
-        __syncthreads();  // tiles and statistics of block i visible
-        if (x + 1 < cnt) prefetch(qblock(x + 1));
+        __syncthreads();  // tiles and statistics of the step visible
+        if (xn < cnt) prefetch(qblock(xn) * QBLK + DK_Q * fn);
         const float sq = a.q_scale[bh * nqb + i];
         const float c = (sq * sk) * a.K32;
         {
@@ -421,13 +432,13 @@ __global__ __launch_bounds__(DK_THREADS, 1) void dkdv_kernel(BwdArgs a) {
             for (int cq = 0; cq < 4; ++cq)
                 s = mfma_i8_32x32x32(
                     *(const i32x4*)(smem + DK_QI + trow * 128 + 16 * ((2 * cq + hi) ^ swz8(trow))),
-                    *(const i32x4*)(smem + DK_KT + key * 128 + 16 * ((2 * cq + hi) ^ swz8(key))), s);
+                    kfr[cq], s);
 #pragma unroll
             for (int sd = 0; sd < 8; ++sd)
                 dp = mfma_bf16_32x32x16(
                     *(const bf16x8*)(smem + DK_GO + trow * 256 + 16 * ((2 * sd + hi) ^ qswz(trow))),
                     *(const bf16x8*)(smem + DK_VT + key * 256 + 16 * ((2 * sd + hi) ^ (key & 15))), dp);
-            // P and dS; in the ragged last query or key block the rows and keys
+            // P and dS; in a ragged last query or key block the rows and keys
             // past N (clamped copies of valid ones, so p stays finite) are
             // zeroed after the exp, under one uniform branch
             f32x16 pr;
@@ -436,19 +447,18 @@ __global__ __launch_bounds__(DK_THREADS, 1) void dkdv_kernel(BwdArgs a) {
                 for (int g = 0; g < 4; ++g) {
                     const int r0 = 32 * qw + 8 * g + 4 * hi;  // queries of registers 4g .. 4g+3
                     const f32x4 mq = *(const f32x4*)(stat + r0);
-                    const f32x4 Dq = *(const f32x4*)(stat + QBLK + r0);
+                    const f32x4 Dq = *(const f32x4*)(stat + DK_Q + r0);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * g + e;
                         float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], c, -mq[e]));
-                        if constexpr (decltype(ragged)::value)
-                            p = (kok && i * QBLK + r0 + e < N) ? p : 0.f;
+                        if constexpr (decltype(ragged)::value) p = (kok && q0 + r0 + e < N) ? p : 0.f;
                         pr[r] = p;
                         dp[r] = p * (dp[r] - Dq[e]) * sq;
                     }
                 }
             };
-            if (nval == KBLK && (i + 1) * QBLK <= N)
+            if (nval == KBLK && q0 + DK_Q <= N)
                 softmax(std::false_type{});
             else
                 softmax(std::true_type{});
@@ -468,8 +478,7 @@ __global__ __launch_bounds__(DK_THREADS, 1) void dkdv_kernel(BwdArgs a) {
         }
         __syncthreads();  // fragments visible
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int qs = 4 * qh + qq;
+        for (int qs = 0; qs < 4; ++qs) {
             i16x4 gp[2], qp[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -479,9 +488,9 @@ __global__ __launch_bounds__(DK_THREADS, 1) void dkdv_kernel(BwdArgs a) {
                 qp[t] = lds_read_tr16(smem + DK_QB + off);
             }
             const u32x2 g0 = __builtin_bit_cast(u32x2, gp[0]), g1 = __builtin_bit_cast(u32x2, gp[1]);
-            const u32x2 q0 = __builtin_bit_cast(u32x2, qp[0]), q1 = __builtin_bit_cast(u32x2, qp[1]);
+            const u32x2 q0v = __builtin_bit_cast(u32x2, qp[0]), q1v = __builtin_bit_cast(u32x2, qp[1]);
             const bf16x8 gT = __builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]});
-            const bf16x8 qT = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
+            const bf16x8 qT = __builtin_bit_cast(bf16x8, u32x4{q0v[0], q0v[1], q1v[0], q1v[1]});
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int slot = (qs * 2 + h) * 64 + lane;
@@ -489,25 +498,11 @@ __global__ __launch_bounds__(DK_THREADS, 1) void dkdv_kernel(BwdArgs a) {
                 dka[h] = mfma_bf16_32x32x16(qT, *(const bf16x8*)(smem + DK_DF + 16 * slot), dka[h]);
             }
         }
-        __syncthreads();  // the next block rewrites the tiles and fragments
+        __syncthreads();  // the next step rewrites the tiles and fragments
+        x = xn;
+        f = fn;
     }
-    // add the second query half's sums to the first's: [ct][16-byte unit u][lane]
-    f32x4* red = reinterpret_cast<f32x4*>(smem + DK_QB);
-    auto unit = [&](int u) -> f32x4& { return red[(ct * 16 + u) * 64 + lane]; };
-    if (qh == 1) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                unit(4 * h + q4) = f32x4{dva[h][4 * q4], dva[h][4 * q4 + 1], dva[h][4 * q4 + 2],
-                                         dva[h][4 * q4 + 3]};
-                unit(8 + 4 * h + q4) = f32x4{dka[h][4 * q4], dka[h][4 * q4 + 1], dka[h][4 * q4 + 2],
-                                             dka[h][4 * q4 + 3]};
-            }
-    }
-    __syncthreads();
-    if (qh == 1) return;
-    // lane (key column l32 of tile h, hi) holds channels 32ct + 8(r/4) + 4hi + r%4
+    // lane (key column l32 of tile h, hi) holds channels 32w + 8(r/4) + 4hi + r%4
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int u = j * KBLK + 32 * h + l32;
@@ -516,14 +511,11 @@ __global__ __launch_bounds__(DK_THREADS, 1) void dkdv_kernel(BwdArgs a) {
         float* krow = a.dk + (bh * N + u) * HD;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const int d = 32 * ct + 8 * q4 + 4 * hi;
-            const f32x4 ov = unit(4 * h + q4), ok4 = unit(8 + 4 * h + q4);
-            *(f32x4*)(vrow + d) = f32x4{dva[h][4 * q4] + ov[0], dva[h][4 * q4 + 1] + ov[1],
-                                        dva[h][4 * q4 + 2] + ov[2], dva[h][4 * q4 + 3] + ov[3]};
-            *(f32x4*)(krow + d) = f32x4{(dka[h][4 * q4] + ok4[0]) * a.sm,
-                                        (dka[h][4 * q4 + 1] + ok4[1]) * a.sm,
-                                        (dka[h][4 * q4 + 2] + ok4[2]) * a.sm,
-                                        (dka[h][4 * q4 + 3] + ok4[3]) * a.sm};
+            const int d = 32 * wave + 8 * q4 + 4 * hi;
+            *(f32x4*)(vrow + d) = f32x4{dva[h][4 * q4], dva[h][4 * q4 + 1], dva[h][4 * q4 + 2],
+                                        dva[h][4 * q4 + 3]};
+            *(f32x4*)(krow + d) = f32x4{dka[h][4 * q4] * a.sm, dka[h][4 * q4 + 1] * a.sm,
+                                        dka[h][4 * q4 + 2] * a.sm, dka[h][4 * q4 + 3] * a.sm};
         }
     }
 }
