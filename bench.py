@@ -371,9 +371,10 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 def bench_bwd(args):
     """The SageSLA backward (sage_sla_attn_bwd) on the benchmarked workload:
     per step, the gradients of Q, K, V for a seeded dL/dO, from the forward's
-    quantized tensors and selection (computed once before timing). Useful work
-    = the four gradient products per computed block pair, 8*D*n_q*n_k
-    (dP, dV, dQ, dK; the recomputed scores and row statistics not counted)."""
+    quantized tensors, selection, fp32 output and row statistics (the forward
+    runs once before timing, as in training, where it precedes the backward).
+    Useful work = the four gradient products per computed block pair,
+    8*D*n_q*n_k (dP, dV, dQ, dK; the recomputed scores not counted)."""
     import ctypes as C
 
     import torch
@@ -385,7 +386,9 @@ def bench_bwd(args):
     dev = torch.device("cuda:0")
     print(f"# generating {w.name}", file=sys.stderr, flush=True)
     q, k, v = make_workload(w)
-    plan = ssa.SageSLAPlan(w.B, w.H, w.N, w.topk, linear=True, device=dev)
+    # the forward keeps its fp32 output and row statistics for the backward
+    plan = ssa.SageSLAPlan(w.B, w.H, w.N, w.topk, linear=True, device=dev, want_f32=True,
+                           want_lse=True)
     plan.bind(q.to(dev), k.to(dev), v.to(dev))
     plan.run()
     g = torch.Generator().manual_seed(1)
@@ -401,7 +404,7 @@ def bench_bwd(args):
         st = L.sage_sla_attn_bwd(p(plan.q), p(plan.k), p(plan.v), plan.shape, p(plan.q_i8),
                                  p(plan.q_scale), p(plan.k_i8), p(plan.k_scale), p(plan.kidx),
                                  plan.keep, plan.branches, plan.sm_scale, p(dout),
-                                 *map(p, grads), p(ws), ws_n,
+                                 p(plan.out32), p(plan.lse), *map(p, grads), p(ws), ws_n,
                                  C.c_void_p(torch.cuda.current_stream().cuda_stream))
         if st != 0:
             raise RuntimeError(L.ssa_last_error().decode())

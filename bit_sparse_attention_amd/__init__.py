@@ -78,12 +78,12 @@ def _load():
         "w8a8_quant": (i32, [_p, i64, i64, _p, _p, _p]),
         "w8a8_gemm": (i32, [_p, _p, _p, _p, _p, i64, i64, i64, _p, _p, _p]),
         "sage_sla_attn_fwd": (i32, [_p, _p, _p, Shape, _p, _p, _p, _p, _p, i64, i32, C.c_float,
-                                    _p, _p, _p, sz, _p]),
+                                    _p, _p, _p, _p, sz, _p]),
         "sage_sla_fwd": (i32, [_p, _p, _p, Shape, i64, i32, C.c_float, _p, _p, _p, _p, _p, _p,
-                               _p, _p, _p, _p, sz, _p]),
+                               _p, _p, _p, _p, _p, sz, _p]),
         "sage_qk_int32_tiles": (i32, [_p, _p, Shape, _p, i64, _p, _p]),
         "sage_sla_attn_bwd": (i32, [_p, _p, _p, Shape, _p, _p, _p, _p, _p, i64, i32, C.c_float,
-                                    _p, _p, _p, _p, _p, sz, _p]),
+                                    _p, _p, _p, _p, _p, _p, _p, sz, _p]),
         "ssa_kernel_timer_start": (i32, [i32]),
         "ssa_kernel_timer_read": (i32, [C.POINTER(C.c_float), i32]),
         "ssa_kernel_timer_stop": (None, []),
@@ -213,8 +213,10 @@ def sla_block_mask(q, k, keep: int, return_mask: bool = False, pool=None):
 
 def sage_sla_attn_fwd(q, k, v, q_i8, q_scale, k_i8, k_scale, kidx=None, keep=None,
                       branches: int = SPARSE | LINEAR, sm_scale: float = 0.0,
-                      return_f32: bool = False):
-    """SageSLA forward. kidx=None runs dense (every key block kept)."""
+                      return_f32: bool = False, return_lse: bool = False):
+    """SageSLA forward. kidx=None runs dense (every key block kept). Returns
+    out, then out32 if return_f32, then lse [B,H,N] (m + log2 l per row, for
+    the backward) if return_lse."""
     s = _qkv_shape(q, k, v)
     B, H, N, D = q.shape
     dev = q.device
@@ -230,18 +232,23 @@ def sage_sla_attn_fwd(q, k, v, q_i8, q_scale, k_i8, k_scale, kidx=None, keep=Non
         _need_gpu("kidx", kidx, torch.int32, (B, H, nqb, keep))
     out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
     out32 = torch.empty((B, H, N, D), dtype=torch.float32, device=dev) if return_f32 else None
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
     ws, n = _ws(OP_ATTN, s, dev, keep, branches)
     _check("sage_sla_attn_fwd", _load().sage_sla_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), s, _ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale),
-        _ptr(kidx), int(keep), int(branches), float(sm_scale), _ptr(out), _ptr(out32), _ptr(ws), n,
-        _stream(dev)))
-    return (out, out32) if return_f32 else out
+        _ptr(kidx), int(keep), int(branches), float(sm_scale), _ptr(out), _ptr(out32), _ptr(lse),
+        _ptr(ws), n, _stream(dev)))
+    res = (out,) + ((out32,) if return_f32 else ()) + ((lse,) if return_lse else ())
+    return res if len(res) > 1 else out
 
 
 def sage_sla_attn_bwd(q, k, v, q_i8, q_scale, k_i8, k_scale, dout, kidx=None, keep=None,
-                      branches: int = SPARSE | LINEAR, sm_scale: float = 0.0):
+                      branches: int = SPARSE | LINEAR, sm_scale: float = 0.0, out32=None,
+                      lse=None):
     """SageSLA backward: (dq, dk, dv) fp32 [B,H,N,D] for dL/dO = dout (bf16),
-    with the same quantized tensors, selection and branches as the forward."""
+    with the same quantized tensors, selection and branches as the forward.
+    out32 and lse (the forward's fp32 output and row statistics, given
+    together) spare the backward its recomputation of the forward."""
     s = _qkv_shape(q, k, v)
     B, H, N, D = q.shape
     dev = q.device
@@ -256,12 +263,17 @@ def sage_sla_attn_bwd(q, k, v, q_i8, q_scale, k_i8, k_scale, dout, kidx=None, ke
     else:
         keep = kidx.shape[-1] if keep is None else int(keep)
         _need_gpu("kidx", kidx, torch.int32, (B, H, nqb, keep))
+    if (out32 is None) != (lse is None):
+        raise ValueError("out32 and lse are given together or not at all")
+    if out32 is not None:
+        _need_gpu("out32", out32, torch.float32, q.shape)
+        _need_gpu("lse", lse, torch.float32, (B, H, N))
     grads = [torch.empty((B, H, N, D), dtype=torch.float32, device=dev) for _ in range(3)]
     ws, n = _ws(OP_BWD, s, dev, keep, branches)
     _check("sage_sla_attn_bwd", _load().sage_sla_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), s, _ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale),
-        _ptr(kidx), int(keep), int(branches), float(sm_scale), _ptr(dout), *map(_ptr, grads),
-        _ptr(ws), n, _stream(dev)))
+        _ptr(kidx), int(keep), int(branches), float(sm_scale), _ptr(dout), _ptr(out32),
+        _ptr(lse), *map(_ptr, grads), _ptr(ws), n, _stream(dev)))
     return tuple(grads)
 
 
@@ -281,12 +293,13 @@ def sage_qk_int32_tiles(q_i8, k_i8, tiles):
 
 
 def sage_sla_fwd(q, k, v, topk: float | None = 0.1, linear: bool = True, sm_scale: float = 0.0,
-                 return_f32: bool = False, return_mask: bool = False, return_all: bool = False):
+                 return_f32: bool = False, return_mask: bool = False, return_all: bool = False,
+                 return_lse: bool = False):
     """The whole step in one library call (quantize, select unless topk is
     None, attend), bit-identical to the three staged calls. Returns out, then
     out32 if return_f32, then the u8 block mask if return_mask (None when
-    dense), then, if return_all, a dict of the intermediates (q_i8, q_scale,
-    k_i8, k_scale, k_mean, kidx)."""
+    dense), then lse if return_lse, then, if return_all, a dict of the
+    intermediates (q_i8, q_scale, k_i8, k_scale, k_mean, kidx)."""
     s = _qkv_shape(q, k, v)
     B, H, N, D = q.shape
     dev = q.device
@@ -305,14 +318,17 @@ def sage_sla_fwd(q, k, v, topk: float | None = 0.1, linear: bool = True, sm_scal
             if (return_mask and not dense) else None)
     out = torch.empty((B, H, N, D), dtype=torch.bfloat16, **e)
     out32 = torch.empty((B, H, N, D), dtype=torch.float32, **e) if return_f32 else None
+    lse = torch.empty((B, H, N), dtype=torch.float32, **e) if return_lse else None
     ws, n = _ws(OP_STEP, s, dev, keep, branches)
     _check("sage_sla_fwd", _load().sage_sla_fwd(
         _ptr(q), _ptr(k), _ptr(v), s, int(keep), int(branches), float(sm_scale), _ptr(q_i8),
         _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(k_mean), _ptr(kidx), _ptr(mask),
-        _ptr(out), _ptr(out32), _ptr(ws), n, _stream(dev)))
+        _ptr(out), _ptr(out32), _ptr(lse), _ptr(ws), n, _stream(dev)))
     res = (out, out32) if return_f32 else (out,)
     if return_mask:
         res = res + (mask,)
+    if return_lse:
+        res = res + (lse,)
     if return_all:
         res = res + (dict(q_i8=q_i8, q_scale=q_scale, k_i8=k_i8, k_scale=k_scale, k_mean=k_mean,
                           kidx=kidx),)
@@ -414,7 +430,8 @@ class SageSLAPlan:
     buffers with bit-identical contents."""
 
     def __init__(self, B, H, N, topk: float | None, linear: bool = True, device="cuda",
-                 sm_scale: float = 0.0, want_f32: bool = False, fused: bool = True):
+                 sm_scale: float = 0.0, want_f32: bool = False, fused: bool = True,
+                 want_lse: bool = False):
         L = _load()
         dev = torch.device(device)
         self.shape = Shape(B, H, N, HEAD_DIM)
@@ -437,6 +454,8 @@ class SageSLAPlan:
             int(L.ssa_pool_bytes(self.shape)), dtype=torch.uint8, **e)
         self.out = torch.empty((B, H, N, HEAD_DIM), dtype=torch.bfloat16, **e)
         self.out32 = torch.empty((B, H, N, HEAD_DIM), dtype=torch.float32, **e) if want_f32 else None
+        # each row's m + log2 l, kept with out32 for a backward pass
+        self.lse = torch.empty((B, H, N), dtype=torch.float32, **e) if want_lse else None
         self.ws_n = {
             OP_QUANT: workspace_bytes(OP_QUANT, self.shape),
             OP_ATTN: workspace_bytes(OP_ATTN, self.shape, self.keep, self.branches),
@@ -472,15 +491,16 @@ class SageSLAPlan:
         _check("sage_sla_attn_fwd", self._L.sage_sla_attn_fwd(
             _ptr(self.q), _ptr(self.k), _ptr(self.v), self.shape, _ptr(self.q_i8),
             _ptr(self.q_scale), _ptr(self.k_i8), _ptr(self.k_scale), _ptr(self.kidx), self.keep,
-            self.branches, self.sm_scale, _ptr(self.out), _ptr(self.out32), _ptr(self.ws),
-            self.ws_n[OP_ATTN], _stream(self.device)))
+            self.branches, self.sm_scale, _ptr(self.out), _ptr(self.out32), _ptr(self.lse),
+            _ptr(self.ws), self.ws_n[OP_ATTN], _stream(self.device)))
 
     def step(self):
         _check("sage_sla_fwd", self._L.sage_sla_fwd(
             _ptr(self.q), _ptr(self.k), _ptr(self.v), self.shape, self.keep, self.branches,
             self.sm_scale, _ptr(self.q_i8), _ptr(self.q_scale), _ptr(self.k_i8),
             _ptr(self.k_scale), _ptr(self.k_mean), _ptr(self.kidx), None, _ptr(self.out),
-            _ptr(self.out32), _ptr(self.ws), self.ws_n[OP_STEP], _stream(self.device)))
+            _ptr(self.out32), _ptr(self.lse), _ptr(self.ws), self.ws_n[OP_STEP],
+            _stream(self.device)))
 
     def run_staged(self):
         self.quant()

@@ -226,7 +226,7 @@ StepWs ws_step(const Dims& d, bool linear) {
 // tiles, the inverse selection lists and the linear branch's gradient states
 struct BwdWs {
     AttnWs attn;
-    size_t mlog, dstat, kt16, counts, lists, gf, gs, gs_lo, gtot, msel, gc, total;
+    size_t mlog, dstat, dol, kt16, counts, lists, gf, gs, gs_lo, gtot, msel, gc, total;
 };
 BwdWs ws_bwd(const Dims& d, bool sel, bool linear) {
     BwdWs w{};
@@ -239,6 +239,7 @@ BwdWs ws_bwd(const Dims& d, bool sel, bool linear) {
     };
     w.mlog = take((size_t)d.BH * d.N * 4);
     w.dstat = take((size_t)d.BH * d.N * 4);
+    w.dol = linear ? take((size_t)d.BH * d.N * 4) : 0;
     w.kt16 = take((size_t)d.BH * d.nkb * HD * KBLK * 2);
     if (sel) {
         w.counts = take((size_t)d.BH * d.nkb * 4);
@@ -317,8 +318,8 @@ hipError_t enqueue_complement(const Dims& d, const int32_t* kidx, int64_t keep, 
 hipError_t enqueue_attn(const Dims& d, bool sparse, bool linear, const uint16_t* q,
                         const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                         const float* k_scale, const int32_t* kidx, int64_t keep, float sm_scale,
-                        uint16_t* out, float* out_f32, char* base, const AttnWs& w,
-                        hipStream_t st) {
+                        uint16_t* out, float* out_f32, float* lse, char* base,
+                        const AttnWs& w, hipStream_t st) {
     const float sm = sm_scale > 0.f ? sm_scale : (float)(1.0 / std::sqrt((double)HD));
     AttnArgs a;
     a.q_i8 = q_i8;
@@ -341,6 +342,7 @@ hipError_t enqueue_attn(const Dims& d, bool sparse, bool linear, const uint16_t*
     a.dout = nullptr;
     a.mlog = nullptr;
     a.dstat = nullptr;
+    a.lse = lse;
     const int slot = timer_slot();
     if (slot >= 0) (void)hipEventRecord(g_ev0[slot], st);
     const hipError_t e = launch_attn(a, st);
@@ -526,7 +528,7 @@ ssa_status sla_block_mask(const uint16_t* q, const uint16_t* k, ssa_shape s, int
 ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, ssa_shape s,
                              const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                              const float* k_scale, const int32_t* kidx, int64_t keep, int branches,
-                             float sm_scale, uint16_t* out, float* out_f32, void* ws,
+                             float sm_scale, uint16_t* out, float* out_f32, float* lse, void* ws,
                              size_t ws_bytes, void* stream) {
     g_err[0] = 0;
     Dims d;
@@ -550,6 +552,7 @@ ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
     TRY(need_ptr(k_scale, 4, "k_scale"));
     TRY(need_ptr(out, 16, "out"));
     if (out_f32) TRY(need_ptr(out_f32, 16, "out_f32"));
+    if (lse) TRY(need_ptr(lse, 4, "lse"));
     if (kidx) TRY(need_ptr(kidx, 4, "kidx"));
     if (linear) {
         TRY(need_ptr(q, 16, "q"));
@@ -566,8 +569,9 @@ ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
                          {kidx, kidx ? (size_t)d.BH * d.nqb * keep * 4 : 0, "kidx"}};
     const Range outs[] = {{out, nel * 2, "out"},
                           {out_f32, out_f32 ? nel * 4 : 0, "out_f32"},
+                          {lse, lse ? (size_t)d.BH * d.N * 4 : 0, "lse"},
                           {ws, ws_bytes, "workspace"}};
-    TRY(check_alias(outs, 3, ins, 8));
+    TRY(check_alias(outs, 4, ins, 8));
     const AttnWs w = ws_attn(d, linear);
     TRY(check_ws(ws, ws_bytes, w.total));
     TRY(check_device());
@@ -577,7 +581,7 @@ ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
     if (e == hipSuccess && linear) e = enqueue_complement(d, kidx, keep, (char*)ws, w, st);
     if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_fwd launch (linear / V layout)");
     e = enqueue_attn(d, sparse, linear, q, q_i8, q_scale, k_i8, k_scale, kidx, keep, sm_scale,
-                     out, out_f32, (char*)ws, w, st);
+                     out, out_f32, lse, (char*)ws, w, st);
     if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_fwd launch");
     return SSA_OK;
 }
@@ -585,8 +589,8 @@ ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
 ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, ssa_shape s,
                         int64_t keep, int branches, float sm_scale, int8_t* q_i8, float* q_scale,
                         int8_t* k_i8, float* k_scale, float* k_mean, int32_t* kidx,
-                        uint8_t* mask, uint16_t* out, float* out_f32, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        uint8_t* mask, uint16_t* out, float* out_f32, float* lse, void* ws,
+                        size_t ws_bytes, void* stream) {
     g_err[0] = 0;
     Dims d;
     TRY(check_shape(s, &d));
@@ -613,6 +617,7 @@ ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     TRY(need_ptr(k_mean, 4, "k_mean"));
     TRY(need_ptr(out, 16, "out"));
     if (out_f32) TRY(need_ptr(out_f32, 16, "out_f32"));
+    if (lse) TRY(need_ptr(lse, 4, "lse"));
     if (kidx) TRY(need_ptr(kidx, 4, "kidx"));
     const size_t nel = (size_t)d.BH * d.N * HD;
     const Range ins[] = {{q, nel * 2, "q"}, {k, nel * 2, "k"}, {v, nel * 2, "v"}};
@@ -625,8 +630,9 @@ ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                           {mask, mask ? (size_t)d.BH * d.nqb * d.nkb : 0, "mask"},
                           {out, nel * 2, "out"},
                           {out_f32, out_f32 ? nel * 4 : 0, "out_f32"},
+                          {lse, lse ? (size_t)d.BH * d.N * 4 : 0, "lse"},
                           {ws, ws_bytes, "workspace"}};
-    TRY(check_alias(outs, 10, ins, 3));
+    TRY(check_alias(outs, 11, ins, 3));
     const StepWs w = ws_step(d, linear);
     TRY(check_ws(ws, ws_bytes, w.total));
     TRY(check_device());
@@ -650,7 +656,7 @@ ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     if (e == hipSuccess && linear) e = enqueue_complement(d, kidx, keep, base, w.attn, st);
     if (e != hipSuccess) return hip_fail(e, "sage_sla_fwd launch (quantization / selection)");
     e = enqueue_attn(d, sparse, linear, q, q_i8, q_scale, k_i8, k_scale, kidx, keep, sm_scale,
-                     out, out_f32, base, w.attn, st);
+                     out, out_f32, lse, base, w.attn, st);
     if (e != hipSuccess) return hip_fail(e, "sage_sla_fwd launch");
     return SSA_OK;
 }
@@ -658,8 +664,9 @@ ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, ssa_shape s,
                              const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                              const float* k_scale, const int32_t* kidx, int64_t keep, int branches,
-                             float sm_scale, const uint16_t* dout, float* dq, float* dk, float* dv,
-                             void* ws, size_t ws_bytes, void* stream) {
+                             float sm_scale, const uint16_t* dout, const float* out_f32,
+                             const float* lse, float* dq, float* dk, float* dv, void* ws,
+                             size_t ws_bytes, void* stream) {
     g_err[0] = 0;
     Dims d;
     TRY(check_shape(s, &d));
@@ -692,6 +699,11 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     TRY(need_ptr(dk, 16, "dk"));
     TRY(need_ptr(dv, 16, "dv"));
     if (kidx) TRY(need_ptr(kidx, 4, "kidx"));
+    if (!out_f32 != !lse)
+        return fail(SSA_ERR_INVALID, "out_f32 and lse are given together or not at all");
+    const bool saved = sparse && out_f32;  // the forward's output and row statistics
+    if (out_f32) TRY(need_ptr(out_f32, 16, "out_f32"));
+    if (lse) TRY(need_ptr(lse, 4, "lse"));
     const size_t nel = (size_t)d.BH * d.N * HD;
     const Range ins[] = {{q, nel * 2, "q"},
                          {k, nel * 2, "k"},
@@ -701,12 +713,14 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
                          {q_scale, (size_t)d.BH * d.nqb * 4, "q_scale"},
                          {k_scale, (size_t)d.BH * d.nkb * 4, "k_scale"},
                          {kidx, kidx ? (size_t)d.BH * d.nqb * keep * 4 : 0, "kidx"},
-                         {dout, nel * 2, "dout"}};
+                         {dout, nel * 2, "dout"},
+                         {out_f32, out_f32 ? nel * 4 : 0, "out_f32"},
+                         {lse, lse ? (size_t)d.BH * d.N * 4 : 0, "lse"}};
     const Range outs[] = {{dq, nel * 4, "dq"},
                           {dk, nel * 4, "dk"},
                           {dv, nel * 4, "dv"},
                           {ws, ws_bytes, "workspace"}};
-    TRY(check_alias(outs, 4, ins, 9));
+    TRY(check_alias(outs, 4, ins, 11));
     const BwdWs w = ws_bwd(d, sel, linear);
     TRY(check_ws(ws, ws_bytes, w.total));
     TRY(check_device());
@@ -730,30 +744,50 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
         e = launch_inv_lists(kidx, (int)keep, d.BH, (int)d.nqb, (int)d.nkb,
                              (uint16_t*)(base + w.lists), (int32_t*)(base + w.counts), st);
     if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (states)");
+    // the linear branch's dq first (the sparse branch adds to it), with dO . o_l
+    // per row when D comes from the forward's output
+    float* gf = linear ? (float*)(base + w.gf) : nullptr;
+    uint16_t* gs = linear ? (uint16_t*)(base + w.gs) : nullptr;
+    uint16_t* gs_lo = linear ? (uint16_t*)(base + w.gs_lo) : nullptr;
+    float* dol = (linear && saved) ? (float*)(base + w.dol) : nullptr;
+    if (linear) {
+        e = launch_lin_bwd_q(q, dout, (const float*)(base + w.attn.hnon), d.BH, (int)d.N, 0, dq, gf,
+                             gs, gs_lo, dol, st);
+        if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (linear branch)");
+    }
     if (sparse) {
-        // the forward's row statistics
-        AttnArgs f;
-        f.q_i8 = q_i8;
-        f.q_scale = q_scale;
-        f.k_i8 = k_i8;
-        f.k_scale = k_scale;
-        f.vt = (const uint16_t*)(base + w.attn.vt);
-        f.kidx = kidx;
-        f.keep = (int)keep;
-        f.N = (int)d.N;
-        f.nqb = (int)d.nqb;
-        f.nkb = (int)d.nkb;
-        f.BH = d.BH;
-        f.K32 = (float)((double)sm * 1.4426950408889634074);
-        f.do_sparse = 1;
-        f.q = q;
-        f.hnon = nullptr;
-        f.out = nullptr;
-        f.out32 = nullptr;
-        f.dout = dout;
-        f.mlog = (float*)(base + w.mlog);
-        f.dstat = (float*)(base + w.dstat);
-        e = launch_attn(f, st);
+        const float K32 = (float)((double)sm * 1.4426950408889634074);
+        float* dstat = (float*)(base + w.dstat);
+        const float* mlog = saved ? lse : (const float*)(base + w.mlog);
+        if (saved) {
+            // D = dO . o_s = dO . out - dO . o_l from the forward's output
+            e = launch_dstat(dout, out_f32, dol, d.BH * d.N, dstat, st);
+        } else {
+            // the forward's row statistics, recomputed
+            AttnArgs f;
+            f.q_i8 = q_i8;
+            f.q_scale = q_scale;
+            f.k_i8 = k_i8;
+            f.k_scale = k_scale;
+            f.vt = (const uint16_t*)(base + w.attn.vt);
+            f.kidx = kidx;
+            f.keep = (int)keep;
+            f.N = (int)d.N;
+            f.nqb = (int)d.nqb;
+            f.nkb = (int)d.nkb;
+            f.BH = d.BH;
+            f.K32 = K32;
+            f.do_sparse = 1;
+            f.q = q;
+            f.hnon = nullptr;
+            f.out = nullptr;
+            f.out32 = nullptr;
+            f.dout = dout;
+            f.mlog = (float*)(base + w.mlog);
+            f.dstat = dstat;
+            f.lse = nullptr;
+            e = launch_attn(f, st);
+        }
         BwdArgs b;
         b.q_i8 = q_i8;
         b.q_scale = q_scale;
@@ -766,14 +800,15 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
         b.keep = (int)keep;
         b.lists = sel ? (const uint16_t*)(base + w.lists) : nullptr;
         b.counts = sel ? (const int32_t*)(base + w.counts) : nullptr;
+        b.dq_accumulate = linear ? 1 : 0;
         b.N = (int)d.N;
         b.nqb = (int)d.nqb;
         b.nkb = (int)d.nkb;
         b.BH = d.BH;
-        b.K32 = f.K32;
+        b.K32 = K32;
         b.sm = sm;
-        b.mlog = f.mlog;
-        b.dstat = f.dstat;
+        b.mlog = mlog;
+        b.dstat = dstat;
         b.dq = dq;
         b.dk = dk;
         b.dv = dv;
@@ -783,15 +818,9 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
         if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (sparse branch)");
     }
     if (linear) {
-        const int acc = sparse ? 1 : 0;
-        float* gf = (float*)(base + w.gf);
-        uint16_t* gs = (uint16_t*)(base + w.gs);
-        uint16_t* gs_lo = (uint16_t*)(base + w.gs_lo);
         float* gtot = (float*)(base + w.gtot);
         float* gc = (float*)(base + w.gc);
-        e = launch_lin_bwd_q(q, dout, (const float*)(base + w.attn.hnon), d.BH, (int)d.N, acc, dq,
-                             gf, gs, gs_lo, st);
-        if (e == hipSuccess) e = launch_state_total(gf, (int)d.nqb, d.BH, gtot, st);
+        e = launch_state_total(gf, (int)d.nqb, d.BH, gtot, st);
         // the gradient states summed over the query blocks that did not keep
         // each key block: the complement GEMM on the transposed selection
         if (e == hipSuccess)
@@ -799,7 +828,8 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
                                         (const int32_t*)(base + w.counts), (int)d.nkb, (int)d.nqb,
                                         2 * keep > d.nkb ? 1 : 0, gs, gs_lo, gtot, d.BH,
                                         (uint32_t*)(base + w.msel), gc, st);
-        if (e == hipSuccess) e = launch_lin_bwd_k(k, v, gc, d.BH, (int)d.N, acc, dk, dv, st);
+        if (e == hipSuccess)
+            e = launch_lin_bwd_k(k, v, gc, d.BH, (int)d.N, sparse ? 1 : 0, dk, dv, st);
         if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (linear branch)");
     }
     return SSA_OK;

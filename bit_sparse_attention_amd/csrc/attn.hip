@@ -468,6 +468,10 @@ __device__ __forceinline__ void attn_block(const AttnArgs& a, uint8_t* smem, int
 
     const float lt = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = a.do_sparse ? 1.0f / lt : 0.f;
+    // the row's m + log2(l) for a backward pass (the statistics mode writes the
+    // same expression)
+    if (MODE != ATTN_STATS && a.lse && a.do_sparse && tq < N && hi == 0)
+        a.lse[bh * N + tq] = m_run + __log2f(lt);
     if (MODE == ATTN_STATS) {
         // P of the backward is 2^(S*c - (m + log2 l)); D = dO . (o / l), the
         // lane pair holding the query's 128 channels
@@ -539,7 +543,8 @@ __device__ __forceinline__ void attn_block(const AttnArgs& a, uint8_t* smem, int
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float f = bf2f(qv[e]);
-                const float ph = f > 0.f ? f + 1.f : __expf(f);
+                const float ex = __expf(fminf(f, 0.f));  // selected for f <= 0 only: no branch
+                const float ph = f > 0.f ? f + 1.f : ex;
                 __bf16 x, y;
                 split_bf16(ph, x, y);
                 bqh[e] = x;

@@ -276,9 +276,31 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int dv = 32 * dt + 8 * q4 + 4 * hi;
-                *(f32x4*)(row + dv) = f32x4{acc[dt][4 * q4] * a.sm, acc[dt][4 * q4 + 1] * a.sm,
-                                            acc[dt][4 * q4 + 2] * a.sm, acc[dt][4 * q4 + 3] * a.sm};
+                f32x4 g = f32x4{acc[dt][4 * q4] * a.sm, acc[dt][4 * q4 + 1] * a.sm,
+                                acc[dt][4 * q4 + 2] * a.sm, acc[dt][4 * q4 + 3] * a.sm};
+                if (a.dq_accumulate) g = g + *(const f32x4*)(row + dv);
+                *(f32x4*)(row + dv) = g;
             }
+    }
+}
+
+// D[t] = dO_t . out_t - dol[t] per query row, from the forward's fp32 output
+// (o_s + o_l) and the linear branch's dO . o_l (dol null: sparse branch only):
+// the sparse branch's D = dO . o_s without re-running the forward. One wave
+// per row, two channels per lane, the sum as a butterfly over the wave.
+__global__ __launch_bounds__(256) void dstat_kernel(const uint16_t* __restrict__ dout,
+                                                    const float* __restrict__ out32,
+                                                    const float* __restrict__ dol, int64_t rows,
+                                                    float* __restrict__ dstat) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < rows;
+         t += (int64_t)gridDim.x * 4) {
+        const uint32_t g2 = *(const uint32_t*)(dout + t * HD + 2 * lane);
+        const f32x2 o2 = *(const f32x2*)(out32 + t * HD + 2 * lane);
+        float s = __builtin_fmaf(bf2f((uint16_t)(g2 & 0xFFFFu)), o2[0], bf2f((uint16_t)(g2 >> 16)) * o2[1]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (lane == 0) dstat[t] = dol ? s - dol[t] : s;
     }
 }
 
@@ -626,7 +648,8 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __res
                                                            float* __restrict__ dq,
                                                            float* __restrict__ gf,
                                                            uint16_t* __restrict__ gs,
-                                                           uint16_t* __restrict__ gs_lo) {
+                                                           uint16_t* __restrict__ gs_lo,
+                                                           float* __restrict__ dol) {
     __shared__ float Hs[HD * LB_P];
     __shared__ float zv[HD];
     __shared__ float As[LB_T * LB_P], Gs[LB_T * LB_P];  // a and g, then g / den
@@ -679,7 +702,9 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __res
         __syncthreads();
         if (tid < LB_T) {
             const float dn = den_s[tid];
-            dden_s[tid] = h0 + tid < nt ? -(gop[0][tid] + gop[1][tid]) / (dn * dn) : 0.f;
+            const float go = gop[0][tid] + gop[1][tid];  // g . o_l = go / den
+            dden_s[tid] = h0 + tid < nt ? -go / (dn * dn) : 0.f;
+            if (dol && h0 + tid < nt) dol[bh * N + i * QBLK + h0 + tid] = go / dn;
         }
         __syncthreads();
         // the row check only in a ragged last piece (one uniform branch)
@@ -826,10 +851,18 @@ hipError_t launch_bwd_sparse(const BwdArgs& a, hipStream_t st) {
 
 hipError_t launch_lin_bwd_q(const uint16_t* q, const uint16_t* dout, const float* hnon, int64_t BH,
                             int N, int accumulate, float* dq, float* gf, uint16_t* gs,
-                            uint16_t* gs_lo, hipStream_t st) {
+                            uint16_t* gs_lo, float* dol, hipStream_t st) {
     const int nqb = (N + QBLK - 1) / QBLK;
     hipLaunchKernelGGL(lin_bwd_q_kernel, dim3(nqb, BH), dim3(256), 0, st, q, dout, hnon, N, nqb,
-                       accumulate, dq, gf, gs, gs_lo);
+                       accumulate, dq, gf, gs, gs_lo, dol);
+    return hipGetLastError();
+}
+
+hipError_t launch_dstat(const uint16_t* dout, const float* out32, const float* dol, int64_t rows,
+                        float* dstat, hipStream_t st) {
+    const int64_t wg = std::min<int64_t>((rows + 3) / 4, 65536);
+    hipLaunchKernelGGL(dstat_kernel, dim3((unsigned)wg), dim3(256), 0, st, dout, out32, dol, rows,
+                       dstat);
     return hipGetLastError();
 }
 

@@ -67,6 +67,7 @@ struct BwdArgs {
     int keep;
     const uint16_t* lists;   // [BH][nkb][nqb]: query blocks that kept each key block
     const int32_t* counts;   // [BH][nkb]
+    int dq_accumulate;       // dq_kernel adds to dq (the linear branch wrote it first)
     int N, nqb, nkb;
     int64_t BH;
     float K32;               // fl32(sm * log2 e)
@@ -81,7 +82,9 @@ hipError_t launch_inv_lists(const int32_t* kidx, int keep, int64_t BH, int nqb, 
 hipError_t launch_bwd_sparse(const BwdArgs& a, hipStream_t st);
 hipError_t launch_lin_bwd_q(const uint16_t* q, const uint16_t* dout, const float* hnon, int64_t BH,
                             int N, int accumulate, float* dq, float* gf, uint16_t* gs,
-                            uint16_t* gs_lo, hipStream_t st);
+                            uint16_t* gs_lo, float* dol, hipStream_t st);
+hipError_t launch_dstat(const uint16_t* dout, const float* out32, const float* dol, int64_t rows,
+                        float* dstat, hipStream_t st);
 hipError_t launch_lin_bwd_k(const uint16_t* k, const uint16_t* v, const float* gc, int64_t BH,
                             int N, int accumulate, float* dk, float* dv, hipStream_t st);
 hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
@@ -117,6 +120,8 @@ struct AttnArgs {
     const uint16_t* dout;
     float* mlog;
     float* dstat;
+    // forward: also write lse[bh][t] = m + log2(l) of the sparse branch (or null)
+    float* lse;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_qk_tiles(const int8_t* q_i8, const int8_t* k_i8, int64_t BH, int N,

@@ -173,13 +173,18 @@ ssa_status sla_block_mask(const uint16_t* q, const uint16_t* k, ssa_shape s, int
  *   sm_scale     in : softmax scale; <= 0 selects 1/sqrt(D) rounded to fp32
  *   out          out: bf16 [B,H,N,D] (round to nearest even of the fp32 result)
  *   out_f32      out: fp32 [B,H,N,D] copy of the result before rounding, or NULL
+ *   lse          out: fp32 [B,H,N], each query row's m + log2(sum p) of the
+ *                     sparse branch (written when that branch runs), or NULL:
+ *                     with out_f32, what sage_sla_attn_bwd needs to skip
+ *                     recomputing the forward
  *   ws: ssa_workspace_bytes(SSA_OP_ATTN, s, keep, branches) bytes.
  */
 ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              ssa_shape s, const int8_t* q_i8, const float* q_scale,
                              const int8_t* k_i8, const float* k_scale, const int32_t* kidx,
                              int64_t keep, int branches, float sm_scale, uint16_t* out,
-                             float* out_f32, void* ws, size_t ws_bytes, void* stream);
+                             float* out_f32, float* lse, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* ---------------------------------------------------------------------------
  * sage_sla_fwd -- the whole SageSLA step in one call (page 5, Pillars One and
@@ -196,15 +201,15 @@ ssa_status sage_sla_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
  *   kidx            out: int32 [B,H,Nqb,keep] as sla_block_mask writes it, or
  *                        NULL = dense (keep must equal Nkb; no selection runs)
  *   mask            out: uint8 [B,H,Nqb,Nkb] or NULL (needs kidx)
- *   out, out_f32    out: as for sage_sla_attn_fwd
+ *   out, out_f32, lse out: as for sage_sla_attn_fwd
  *   ws: ssa_workspace_bytes(SSA_OP_STEP, s, keep, branches) bytes, 256-byte
  *       aligned; its contents on return are unspecified.
  */
 ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, ssa_shape s,
                         int64_t keep, int branches, float sm_scale, int8_t* q_i8, float* q_scale,
                         int8_t* k_i8, float* k_scale, float* k_mean, int32_t* kidx,
-                        uint8_t* mask, uint16_t* out, float* out_f32, void* ws, size_t ws_bytes,
-                        void* stream);
+                        uint8_t* mask, uint16_t* out, float* out_f32, float* lse, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * sage_sla_attn_bwd -- SageSLA backward: the gradients of a loss L with
@@ -226,17 +231,25 @@ ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   q, k, v, q_i8..k_scale, kidx, keep, branches, sm_scale: as for
  *                     sage_sla_attn_fwd (the same values the forward used)
  *   dout         in : bf16 [B,H,N,D], dL/d(out)
+ *   out_f32, lse in : the forward's out_f32 and lse (from the same inputs and
+ *                     branches), or both NULL. Given, the row statistics come
+ *                     from them (D = dO . out - dO . o_l, o_l from the linear
+ *                     branch's own pass) and the forward is not recomputed;
+ *                     NULL, a pass of the forward's sparse branch recomputes
+ *                     them. Either way within the same error of the exact
+ *                     gradient.
  *   dq, dk, dv   out: fp32 [B,H,N,D] (both branches' gradients summed)
  *   ws: ssa_workspace_bytes(SSA_OP_BWD, s, keep, branches) bytes, 256-byte
  *       aligned (the forward's workspace plus the backward's).
- * Errors as for the entry points above.
+ * Errors as for the entry points above; SSA_ERR_INVALID when only one of
+ * out_f32 and lse is given.
  */
 ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              ssa_shape s, const int8_t* q_i8, const float* q_scale,
                              const int8_t* k_i8, const float* k_scale, const int32_t* kidx,
                              int64_t keep, int branches, float sm_scale, const uint16_t* dout,
-                             float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
-                             void* stream);
+                             const float* out_f32, const float* lse, float* dq, float* dk,
+                             float* dv, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * sage_qk_int32_tiles -- test export of raw int32 score tiles computed by the

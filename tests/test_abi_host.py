@@ -149,10 +149,10 @@ def test_attn_rejects_bad_arguments():
     GB = 1 << 30
     s = _shape(N=1000)
 
-    def call(kidx=_p(6 * GB), keep=4, branches=3, sm=0.0, out=_p(7 * GB), ws=None, n=0):
+    def call(kidx=_p(6 * GB), keep=4, branches=3, sm=0.0, out=_p(7 * GB), lse=None, ws=None, n=0):
         return L.sage_sla_attn_fwd(_p(0), _p(GB), _p(2 * GB), s, _p(3 * GB), _p(4 * GB),
                                    _p(5 * GB), _p(5 * GB + (1 << 20)), kidx, keep, branches,
-                                   sm, out, None, ws, n, None)
+                                   sm, out, None, lse, ws, n, None)
 
     assert call(branches=0) == 1
     assert call(branches=4) == 1
@@ -160,6 +160,8 @@ def test_attn_rejects_bad_arguments():
     assert call(kidx=None, keep=4) == 1  # dense needs keep == Nkb
     assert call(sm=float("nan")) == 1
     assert call(out=_p(2 * GB)) == 1  # out aliases v
+    assert call(lse=_p(8 * GB + 2)) == 1  # lse misaligned
+    assert call(lse=_p(7 * GB + 64)) == 1  # lse overlaps out
     assert call() == 3  # workspace missing
     assert b"workspace" in L.ssa_last_error()
 
@@ -169,10 +171,10 @@ def test_step_rejects_bad_arguments():
     GB = 1 << 30
     s = _shape(N=1000)  # 16 key blocks
     names = ["q", "k", "v", "s", "keep", "branches", "sm", "q_i8", "q_scale", "k_i8", "k_scale",
-             "k_mean", "kidx", "mask", "out", "out32", "ws", "n", "st"]
+             "k_mean", "kidx", "mask", "out", "out32", "lse", "ws", "n", "st"]
     ok = [_p(0), _p(GB), _p(2 * GB), s, 4, 3, 0.0, _p(3 * GB), _p(4 * GB), _p(5 * GB),
-          _p(6 * GB), _p(6 * GB + (1 << 20)), _p(7 * GB), None, _p(8 * GB), None, _p(9 * GB),
-          1 << 30, None]
+          _p(6 * GB), _p(6 * GB + (1 << 20)), _p(7 * GB), None, _p(8 * GB), None, None,
+          _p(9 * GB), 1 << 30, None]
 
     def call(**kw):
         args = list(ok)
@@ -196,6 +198,7 @@ def test_step_rejects_bad_arguments():
     assert call(kidx=_p(5 * GB + 64)) == 1  # kidx overlaps k_i8
     assert call(mask=_p(9 * GB)) == 1  # mask inside the workspace
     assert b"overlap" in L.ssa_last_error()
+    assert call(lse=_p(8 * GB)) == 1  # lse aliases out
     assert call(ws=None) == 3
     assert call(n=1 << 10) == 3
     assert call(ws=_p(9 * GB + 16)) == 3  # workspace misaligned
@@ -207,10 +210,10 @@ def test_bwd_rejects_bad_arguments():
     s = _shape(N=1000)  # 16 key blocks
 
     def call(kidx=_p(8 * GB), keep=4, branches=3, sm=0.0, dq=_p(9 * GB), ws=_p(12 * GB),
-             n=1 << 34, dout=_p(7 * GB)):
+             n=1 << 34, dout=_p(7 * GB), out32=None, lse=None):
         return L.sage_sla_attn_bwd(_p(0), _p(GB), _p(2 * GB), s, _p(3 * GB), _p(4 * GB),
-                                   _p(5 * GB), _p(6 * GB), kidx, keep, branches, sm, dout, dq,
-                                   _p(10 * GB), _p(11 * GB), ws, n, None)
+                                   _p(5 * GB), _p(6 * GB), kidx, keep, branches, sm, dout, out32,
+                                   lse, dq, _p(10 * GB), _p(11 * GB), ws, n, None)
 
     assert call(branches=0) == 1 and call(branches=4) == 1
     assert call(keep=0) == 1 and call(keep=17) == 1
@@ -220,6 +223,9 @@ def test_bwd_rejects_bad_arguments():
     assert call(dq=_p(9 * GB + 8)) == 1  # misaligned
     assert call(dq=_p(7 * GB)) == 1  # dq aliases dout
     assert b"overlap" in L.ssa_last_error()
+    assert call(out32=_p(13 * GB)) == 1  # out32 without lse
+    assert call(lse=_p(13 * GB)) == 1  # lse without out32
+    assert call(out32=_p(13 * GB), lse=_p(9 * GB)) == 1  # lse aliases dq
     assert call(ws=None) == 3
     assert call(n=1 << 10) == 3
     s2 = _shape(N=1000)
@@ -299,7 +305,7 @@ def test_shapes_beyond_the_launch_grids_are_rejected():
             assert b"exceeds" in L.ssa_last_error() or b"too large" in L.ssa_last_error()
         st = L.sage_sla_attn_fwd(_p(0), _p(16 * GB), _p(32 * GB), s, _p(48 * GB), _p(64 * GB),
                                  _p(80 * GB), _p(96 * GB), None, ssa.num_k_blocks(shape[2]),
-                                 ssa.SPARSE, 0.0, _p(112 * GB), None, _p(128 * GB), 0, None)
+                                 ssa.SPARSE, 0.0, _p(112 * GB), None, None, _p(128 * GB), 0, None)
         if not ok:
             assert st == 2, (shape, st)
 

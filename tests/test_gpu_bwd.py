@@ -52,12 +52,15 @@ BWD_CASES = [(1, 1, 1024, None, 1),      # the dense 1024-token workload
              (1, 1, 64, None, 1), (1, 1, 130, 0.5, 2)]
 
 
+@pytest.mark.parametrize("saved", [False, True], ids=["recomputed-stats", "forward-stats"])
 @pytest.mark.parametrize("B,H,N,topk,branches", BWD_CASES)
-def test_bwd_parity(orc, B, H, N, topk, branches):
+def test_bwd_parity(orc, B, H, N, topk, branches, saved):
+    # saved: the forward's fp32 output and row statistics are handed over;
+    # otherwise the backward recomputes them
     q, k, v = make_qkv(B, H, N, 128, seed=3 * N + branches)
     dout = _dout(B, H, N, seed=N + 17)
     qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
-    label = f"B{B}H{H}N{N} topk={topk} branches={branches}"
+    label = f"B{B}H{H}N{N} topk={topk} branches={branches} saved={saved}"
     say(f"[bwd] {label}")
     q_i8, q_scale, k_i8, k_scale, _ = ssa.sage_quant_qk(qd, kd)
     if topk is None:
@@ -65,8 +68,13 @@ def test_bwd_parity(orc, B, H, N, topk, branches):
     else:
         keep = ssa.keep_blocks(N, topk)
         kidx = ssa.sla_block_mask(qd, kd, keep)
+    fwd = {}
+    if saved:
+        _, fwd["out32"], fwd["lse"] = ssa.sage_sla_attn_fwd(
+            qd, kd, vd, q_i8, q_scale, k_i8, k_scale, kidx, keep, branches, return_f32=True,
+            return_lse=True)
     dq, dk, dv = ssa.sage_sla_attn_bwd(qd, kd, vd, q_i8, q_scale, k_i8, k_scale, gd, kidx, keep,
-                                       branches)
+                                       branches, **fwd)
     torch.cuda.synchronize()
     qb, kb, vb, gb = bits(q), bits(k), bits(v), bits(dout)
     oqi, oqs, oki, oks, _ = orc.quant_qk(qb, kb)
@@ -82,6 +90,29 @@ def test_bwd_parity(orc, B, H, N, topk, branches):
         want = orc.sagesla_bwd(qb, kb, vb, (oqi, oqs, oki, oks), bh, gb,
                                None if okidx is None else okidx[bh], branches)
         _check_grads([g[bh] for g in got], want, f"{label} bh={bh}")
+
+
+def test_forward_lse_is_the_statistics_the_backward_recomputes():
+    # the forward's lse and the backward's own statistics pass are the same
+    # expression over the same sums: handing lse over changes nothing in P,
+    # so the sparse-only gradients differ from the recomputed ones only
+    # through D (dO . out from the fp32 output instead of dO . o_s in the
+    # statistics pass), within fp32 rounding
+    B, H, N = 1, 2, 1500
+    q, k, v = (t.to(DEV) for t in make_qkv(B, H, N, 128, seed=4))
+    gd = _dout(B, H, N, seed=5).to(DEV)
+    qq = ssa.sage_quant_qk(q, k)[:4]
+    keep = ssa.keep_blocks(N, 0.3)
+    kidx = ssa.sla_block_mask(q, k, keep)
+    _, out32, lse = ssa.sage_sla_attn_fwd(q, k, v, *qq, kidx, keep, ssa.SPARSE, return_f32=True,
+                                          return_lse=True)
+    a = ssa.sage_sla_attn_bwd(q, k, v, *qq, gd, kidx, keep, ssa.SPARSE)
+    b = ssa.sage_sla_attn_bwd(q, k, v, *qq, gd, kidx, keep, ssa.SPARSE, out32=out32, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all()
+    for x, y in zip(a, b):
+        rel = ((x - y).norm() / y.norm()).item()
+        assert rel < 1e-5, rel
 
 
 def test_bwd_repeat_runs_bit_identical():
@@ -107,14 +138,15 @@ def test_bwd_at_the_benchmarked_size(orc):
     w = WORKLOADS[BENCH_WORKLOAD]
     say(f"[bwd-full] {w.name}: generating B={w.B} H={w.H} N={w.N}")
     q, k, v = make_workload(w)
-    plan = ssa.SageSLAPlan(w.B, w.H, w.N, w.topk, linear=True, device=DEV)
+    plan = ssa.SageSLAPlan(w.B, w.H, w.N, w.topk, linear=True, device=DEV, want_f32=True,
+                           want_lse=True)
     plan.bind(*(t.to(DEV) for t in (q, k, v)))
     plan.run()
     g = torch.Generator().manual_seed(1)
     dout = torch.randn(w.B, w.H, w.N, 128, generator=g).to(torch.bfloat16)
     grads = ssa.sage_sla_attn_bwd(plan.q, plan.k, plan.v, plan.q_i8, plan.q_scale, plan.k_i8,
                                   plan.k_scale, dout.to(DEV), plan.kidx, plan.keep, plan.branches,
-                                  plan.sm_scale)
+                                  plan.sm_scale, out32=plan.out32, lse=plan.lse)
     BH, N, nqb, nkb = w.B * w.H, w.N, plan.nqb, plan.nkb
     heads = [0, BH - 1]
     sel = torch.tensor(heads, device=DEV)
