@@ -4,8 +4,9 @@
 // guide: the sparse-linear attention is trainable (fine-tuned in training).
 // Gradients pass the 8-bit quantizer straight through (its derivative is
 // taken as the identity) and the block selection is held fixed. With the
-// forward's row statistics m' = m + log2(l) and D = dO . o_s (from the
-// forward kernel's statistics mode), for a query t and a kept key u:
+// forward's row statistics m' = m + log2(l) and D = dO . o_s (handed over by
+// the forward, D via dstat_kernel, or recomputed by the forward kernel's
+// statistics mode), for a query t and a kept key u:
 //   P = 2^(S*c - m'),  dP = dO_t . v_u,  dS = P (dP - D)
 //   dq_t += sm sum_u dS sk k_i8_u      (query-block-major: dq_kernel)
 //   dk_u += sm sum_t dS sq q_i8_t,  dv_u += sum_t P dO_t
