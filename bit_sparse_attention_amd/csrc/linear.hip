@@ -20,8 +20,24 @@
 namespace ssa {
 
 constexpr int TP = KBLK + 8;  // LDS pitch (bf16) of a [channel][token] tile: 144 B
+// LDS pitch (bf16) of a [token][channel] tile: 288 B, so the four token rows a
+// transposing read touches land in disjoint groups of 8 banks
+constexpr int RP = HD + 16;
 constexpr int LS_THREADS = 512;                       // 8 waves
 constexpr int LS_IT = KBLK * HD / 8 / LS_THREADS;     // 16-byte chunks per thread per tile
+
+// Eight consecutive tokens t0 .. t0+7 of channel c0 + (lane & 15), from a
+// token-major LDS tile of pitch RP, as one bf16 MFMA operand (element k =
+// token t0 + k). t0 and c0 are uniform within each 16-lane group: lane i
+// points at token t0 + i/4, channels c0 + 4(i%4) .. +3, and the transposing
+// read hands it channel c0 + i at tokens t0 .. t0+3 (then t0+4 .. t0+7).
+__device__ __forceinline__ bf16x8 tok8(const uint16_t* tile, int t0, int c0, int lane) {
+    const int i = lane & 15;
+    const uint16_t* p = tile + (t0 + (i >> 2)) * RP + c0 + 4 * (i & 3);
+    const i16x4 a = lds_read_tr16(p), b = lds_read_tr16(p + 4 * RP);
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_bit_cast(bf16x8, i16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+}
 
 // Position p (0..63) of a re-laid V tile row holds key 16*(p/16) + kperm(p%16):
 // the order in which one lane of the 32x32 MFMA output holds its keys, so the
@@ -59,11 +75,14 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
                                                             float* __restrict__ kpart,
                                                             float* __restrict__ kbarT, int ldk) {
     constexpr int KBP = HD + 1;  // pitch of the staged pooled means (no bank conflicts)
+    // token-major tiles of the block (V; elu+1 of K as bf16 high parts and
+    // rests; raw K), written with one 16-byte store per chunk, and V^T
+    // channel-major for the re-laid copy
+    __shared__ __attribute__((aligned(16))) uint16_t vtok[KBLK * RP];
     __shared__ __attribute__((aligned(16))) uint16_t vtl[HD * TP];
-    __shared__ __attribute__((aligned(16))) uint16_t fkh[STATES ? HD * TP : 8];
-    __shared__ __attribute__((aligned(16))) uint16_t fkl[STATES ? HD * TP : 8];
-    constexpr int KP = HD + 8;  // LDS pitch (bf16) of the token-major raw K tile: 272 B
-    __shared__ __attribute__((aligned(16))) uint16_t kraw[SUMS ? KBLK * KP : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t fh[STATES ? KBLK * RP : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t fl[STATES ? KBLK * RP : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t kraw[SUMS ? KBLK * RP : 8];
     __shared__ float kbs[SUMS ? LIN_GROUP * KBP : 1];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
               hi = lane >> 5;
@@ -77,15 +96,16 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
     f32x16 tot[2], totz = f32x16{};
 #pragma unroll
     for (int t = 0; t < 2; ++t) tot[t] = f32x16{};
-    // raw K and V of one key block in registers: lane (tid) holds token
-    // u = tid & 63, channels 8ch .. 8ch+7 for ch = (tid >> 6) + 8*it. Two sets,
-    // so the loads of blocks j+1 and j+2 are in flight while block j is worked.
+    // raw K and V of one key block in registers: thread tid holds chunk c =
+    // tid + 512*it, i.e. token u = c / 16, channels 8ch .. 8ch+7 for ch = c % 16,
+    // so each wave reads four whole 256-byte token rows. Two sets, so the loads
+    // of blocks j+1 and j+2 are in flight while block j is worked.
     u16x8 va[LS_IT], ka[LS_IT], vb[LS_IT], kb[LS_IT];
     auto load = [&](int j, u16x8 (&vv)[LS_IT], u16x8 (&kk)[LS_IT]) {
 #pragma unroll
         for (int it = 0; it < LS_IT; ++it) {
             const int c = tid + LS_THREADS * it;
-            const int u = c & 63, ch = c >> 6;
+            const int u = c >> 4, ch = c & 15;
             const int tok = j * KBLK + u;
             const bool ok = tok < N;
             const int64_t off = (bh * N + (ok ? tok : 0)) * HD + 8 * ch;
@@ -95,16 +115,16 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
     };
     auto block = [&](int jb, u16x8 (&vv)[LS_IT], u16x8 (&kk)[LS_IT]) {
         const int j = g * G + jb;
-        // channel-major LDS stores (u fastest: conflict free)
+        // token-major LDS stores: a 16-lane group writes one 256-byte row
 #pragma unroll
         for (int it = 0; it < LS_IT; ++it) {
             const int c = tid + LS_THREADS * it;
-            const int u = c & 63, ch = c >> 6;
+            const int u = c >> 4, ch = c & 15;
             const bool ok = j * KBLK + u < N;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vtl[(8 * ch + e) * TP + u] = vv[it][e];
-            if (SUMS) *(u16x8*)(kraw + u * KP + 8 * ch) = kk[it];  // token-major
+            *(u16x8*)(vtok + u * RP + 8 * ch) = vv[it];
+            if (SUMS) *(u16x8*)(kraw + u * RP + 8 * ch) = kk[it];
             if (STATES) {
+                u16x8 h8, l8;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float f = bf2f(kk[it][e]);
@@ -114,23 +134,25 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
                     const float ph = (f > 0.f ? f + 1.f : ex) * (ok ? 1.f : 0.f);
                     __bf16 h, l;
                     split_bf16(ph, h, l);
-                    fkh[(8 * ch + e) * TP + u] = __builtin_bit_cast(uint16_t, h);
-                    fkl[(8 * ch + e) * TP + u] = __builtin_bit_cast(uint16_t, l);
+                    h8[e] = __builtin_bit_cast(uint16_t, h);
+                    l8[e] = __builtin_bit_cast(uint16_t, l);
                 }
+                *(u16x8*)(fh + u * RP + 8 * ch) = h8;
+                *(u16x8*)(fl + u * RP + 8 * ch) = l8;
             }
         }
         __syncthreads();
         // the registers are free again: block j+2 goes in flight
         if (jb + 2 < G && j + 2 < nkb) load(j + 2, vv, kk);
-        // V^T tile in the sparse kernel's key order: 128 rows x 8 chunks of 16 B
+        // V^T channel-major for the re-laid copy (stored after the block's
+        // last barrier): 16 token quads x 8 groups of 16 channels, four per
+        // 16-lane group, each a transposing read and one 8-byte store
 #pragma unroll
-        for (int it = 0; it < LS_IT; ++it) {
-            const int c = tid + LS_THREADS * it;
-            const int dv = c >> 3, pc = c & 7, cc = pc >> 1, h2 = pc & 1;
-            const u16x4 a = *(const u16x4*)(vtl + dv * TP + 16 * cc + 4 * h2);
-            const u16x4 b = *(const u16x4*)(vtl + dv * TP + 16 * cc + 8 + 4 * h2);
-            *(u16x8*)(vt + ((bh * nkb + j) * HD + dv) * KBLK + 8 * pc) =
-                u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        for (int r = 0; r < 4; ++r) {
+            const int item = (tid >> 4) + 32 * r;
+            const int c0 = 16 * (item & 7), t0 = 4 * (item >> 3), i = tid & 15;
+            const i16x4 q = lds_read_tr16(vtok + (t0 + (i >> 2)) * RP + c0 + 4 * (i & 3));
+            *(i16x4*)(vtl + (c0 + i) * TP + t0) = q;
         }
         // K sums: thread tid adds the column of channel d = tid % 128 in token
         // order, 16 tokens at a time, and waves 4 and 5 store the result. With
@@ -147,9 +169,16 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
         // (without it the compiler moves all 64 adds behind the last MFMA,
         // measured 60 us slower at 40 x 75600 tokens).
         auto sum16 = [&](int uc) {
+            // tokens 16uc .. 16uc+15 of channel dsum (= 16*(dsum/16) + lane % 16)
             uint16_t r[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) r[e] = kraw[(16 * uc + e) * KP + dsum];
+            for (int q = 0; q < 4; ++q) {
+                const int i = tid & 15;
+                const i16x4 x = lds_read_tr16(kraw + (16 * uc + 4 * q + (i >> 2)) * RP +
+                                              (dsum & ~15) + 4 * (i & 3));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[4 * q + e] = (uint16_t)x[e];
+            }
             if (valid == KBLK) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) ksum += bf2f(r[e]);
@@ -173,14 +202,18 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
             bf16x8 ones;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+            // operands through transposing reads: lane (l32, hi) takes tokens
+            // 16uc + 8hi .. +7 of its row d (or column e); its 16-lane group
+            // covers 16 consecutive channels from 32(tile) + 16(l32 / 16)
+            const int cq = 16 * (l32 >> 4);
 #pragma unroll
             for (int uc = 0; uc < 4; ++uc) {
-                const bf16x8 b = *(const bf16x8*)(vtl + (32 * eg + l32) * TP + 16 * uc + 8 * hi);
+                const bf16x8 b = tok8(vtok, 16 * uc + 8 * hi, 32 * eg + cq, lane);
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int dt = 2 * dh + t;
-                    const bf16x8 ah = *(const bf16x8*)(fkh + (32 * dt + l32) * TP + 16 * uc + 8 * hi);
-                    const bf16x8 al = *(const bf16x8*)(fkl + (32 * dt + l32) * TP + 16 * uc + 8 * hi);
+                    const bf16x8 ah = tok8(fh, 16 * uc + 8 * hi, 32 * dt + cq, lane);
+                    const bf16x8 al = tok8(fl, 16 * uc + 8 * hi, 32 * dt + cq, lane);
                     acc[t] = mfma_bf16_32x32x16(ah, b, acc[t]);
                     acc[t] = mfma_bf16_32x32x16(al, b, acc[t]);
                 }
@@ -190,9 +223,8 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
             if (dh == 0) {
 #pragma unroll
                 for (int uc = 0; uc < 4; ++uc) {
-                    const int o = (32 * eg + l32) * TP + 16 * uc + 8 * hi;
-                    accz = mfma_bf16_32x32x16(*(const bf16x8*)(fkh + o), ones, accz);
-                    accz = mfma_bf16_32x32x16(*(const bf16x8*)(fkl + o), ones, accz);
+                    accz = mfma_bf16_32x32x16(tok8(fh, 16 * uc + 8 * hi, 32 * eg + cq, lane), ones, accz);
+                    accz = mfma_bf16_32x32x16(tok8(fl, 16 * uc + 8 * hi, 32 * eg + cq, lane), ones, accz);
                 }
             }
             // lane (column e = 32eg + l32, hi) holds rows d = 32dt + 8(r/4) + 4hi + r%4:
@@ -239,6 +271,18 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
             kbs[jb * KBP + dsum] = ksum / (float)valid;
         }
         __syncthreads();
+        // V^T tile in the sparse kernel's key order: 128 rows x 8 chunks of
+        // 16 B (the next block writes vtl only after its first barrier, which
+        // every thread reaches after these reads)
+#pragma unroll
+        for (int it = 0; it < LS_IT; ++it) {
+            const int c = tid + LS_THREADS * it;
+            const int dv = c >> 3, pc = c & 7, cc = pc >> 1, h2 = pc & 1;
+            const u16x4 a = *(const u16x4*)(vtl + dv * TP + 16 * cc + 4 * h2);
+            const u16x4 b = *(const u16x4*)(vtl + dv * TP + 16 * cc + 8 + 4 * h2);
+            *(u16x8*)(vt + ((bh * nkb + j) * HD + dv) * KBLK + 8 * pc) =
+                u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        }
     };
     const int nb = min(G, nkb - g * G);  // key blocks of this workgroup
     if (nb > 0) load(g * G, va, ka);
