@@ -84,6 +84,12 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
     __shared__ __attribute__((aligned(16))) uint16_t fl[STATES ? KBLK * RP : 8];
     __shared__ __attribute__((aligned(16))) uint16_t kraw[SUMS ? KBLK * RP : 8];
     __shared__ float kbs[SUMS ? LIN_GROUP * KBP : 1];
+    // the block's state rows h^T (and their bf16 rests), staged so that they
+    // leave as whole rows; pitch 272 B, so the 16 rows a 16-lane group writes
+    // at one position fall in distinct banks
+    constexpr int HP = HD + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t hst[STATES ? HD * HP : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t hstl[(STATES && LO) ? HD * HP : 8];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
               hi = lane >> 5;
     // wave (eg, dh) owns the state columns e = 32eg .. 32eg+31 and rows
@@ -242,9 +248,8 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
                         o8[x] = f2bf(acc[t][8 * rb + x]);
                         if (LO) l8[x] = f2bf(acc[t][8 * rb + x] - bf2f(o8[x]));
                     }
-                    *(u16x8*)(hrow + e * HD + 16 * (2 * dt + rb) + 8 * hi) = o8;
-                    if (LO)
-                        *(u16x8*)(hs_lo + (hrow - hs) + e * HD + 16 * (2 * dt + rb) + 8 * hi) = l8;
+                    *(u16x8*)(hst + e * HP + 16 * (2 * dt + rb) + 8 * hi) = o8;
+                    if (LO) *(u16x8*)(hstl + e * HP + 16 * (2 * dt + rb) + 8 * hi) = l8;
                 }
                 tot[t] += acc[t];
             }
@@ -271,6 +276,19 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
             kbs[jb * KBP + dsum] = ksum / (float)valid;
         }
         __syncthreads();
+        // The state rows from LDS as whole 256-byte rows (a wave stores 1 KB
+        // at a time); like vtl below, hst is written again only after the next
+        // block's first barrier.
+        if (STATES) {
+            const int64_t hoff = (bh * nkb + j) * (int64_t)HS_ROW;
+#pragma unroll
+            for (int c = tid; c < HD * 16; c += LS_THREADS) {
+                const int r = c >> 4, q = c & 15;
+                *(u16x8*)(hs + hoff + r * HD + 8 * q) = *(const u16x8*)(hst + r * HP + 8 * q);
+                if (LO)
+                    *(u16x8*)(hs_lo + hoff + r * HD + 8 * q) = *(const u16x8*)(hstl + r * HP + 8 * q);
+            }
+        }
         // V^T tile in the sparse kernel's key order: 128 rows x 8 chunks of
         // 16 B (the next block writes vtl only after its first barrier, which
         // every thread reaches after these reads)
