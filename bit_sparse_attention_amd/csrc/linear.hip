@@ -615,30 +615,41 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     if (kp < nkp) step(kp++, S0{});
     if (kp < nkp) step(kp, S1{});
 
-    // epilogue: lane (i, hi), accumulator [ib][nb] register 4q + x holds
-    // n = 32nb + 8q + 4hi + x
-    f32x4 ht[2][4];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            ht[nb][q] = *(const f32x4*)(htot + bh * HS_ROW + n0 + 32 * nb + 8 * q + 4 * hi);
+    // Epilogue: lane (i, hi), accumulator [ib][nb] register 4q + x holds
+    // n = 32nb + 8q + 4hi + x. Each wave stages one 32-row block at a time in
+    // LDS (the rings are free once every wave has left the K loop), signed so
+    // that the result is base + staged, and stores it as whole 256-byte row
+    // pieces: 16 lanes per row instead of 32-byte runs in 32 rows.
+    constexpr int EP = CG_TN + 4;  // pitch (floats) of a staged row: 272 B
+    static_assert(4 * 32 * EP * 4 <= CG_STAGES * CG_STAGE, "the staging fits the rings");
+    float* stg = reinterpret_cast<float*>(smem) + wave * 32 * EP;
+    const float sgn = complement ? 1.f : -1.f;  // base - sum == base + (-sum) exactly
+    const int rc = lane & 15;                   // the 16-byte piece of a row this lane stores
+    const f32x4 ht = *(const f32x4*)(htot + bh * HS_ROW + n0 + 4 * rc);
+    __syncthreads();
 #pragma unroll
     for (int ib = 0; ib < CG_IB; ++ib) {
-        const int i = iw + 32 * ib + l32;
-        if (i >= nqb) continue;
-        float* dst = hnon + (bh * nqb + i) * (int64_t)HS_ROW + n0 + 4 * hi;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x16& a = acc[ib][nb];
-                const f32x4 sum = f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-                f32x4* o = (f32x4*)(dst + 32 * nb + 8 * q);
-                // accum: a second pass (the stack's bf16 rests) onto the first
-                const f32x4 base = accum ? *o : (complement ? f32x4{} : ht[nb][q]);
-                *o = complement ? base + sum : base - sum;
+                *(f32x4*)(stg + l32 * EP + 32 * nb + 8 * q + 4 * hi) =
+                    f32x4{sgn * a[4 * q], sgn * a[4 * q + 1], sgn * a[4 * q + 2], sgn * a[4 * q + 3]};
             }
+        __syncthreads();
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const int r = 4 * rr + (lane >> 4);
+            const int i = iw + 32 * ib + r;
+            if (i >= nqb) continue;
+            const f32x4 sum = *(const f32x4*)(stg + r * EP + 4 * rc);
+            f32x4* o = (f32x4*)(hnon + (bh * nqb + i) * (int64_t)HS_ROW + n0 + 4 * rc);
+            // accum: a second pass (the stack's bf16 rests) onto the first
+            const f32x4 base = accum ? *o : (complement ? f32x4{} : ht);
+            *o = base + sum;
+        }
+        __syncthreads();
     }
 }
 
