@@ -6,6 +6,8 @@
 // Every fp32 operation here is bit-reproducible: sums run in token order
 // (then block order), divisions are IEEE (this file is compiled with
 // -ffp-contract=off), and round-half-even comes from v_rndne_f32.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -191,23 +193,33 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
         pooled[(bh * nb + b) * HD + tid] = sum / (float)valid;
     }
     int8_t* qbase = xq + (bh * N + t0) * HD;
+    // q = clamp(rint(v / s)); the quotient through div_by_scale when the
+    // (block-uniform) scale allows, which gives the same bytes
+    auto store = [&](auto fast) {
+        const float rs = decltype(fast)::value ? 1.0f / s : 0.f;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int row = (tid >> 4) + 16 * it;
-        if (row < valid) {
-            uint32_t w[2] = {0u, 0u};
-            if (s > 0.f) {
+        for (int it = 0; it < IT; ++it) {
+            const int row = (tid >> 4) + 16 * it;
+            if (row < valid) {
+                uint32_t w[2] = {0u, 0u};
+                if (s > 0.f) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float r = __builtin_rintf(v[it][e] / s);
-                    r = fminf(fmaxf(r, -127.f), 127.f);
-                    const uint32_t byte = (uint32_t)(uint8_t)(int8_t)(int)r;
-                    w[e >> 2] |= byte << (8 * (e & 3));
+                    for (int e = 0; e < 8; ++e) {
+                        const float qt = decltype(fast)::value ? div_by_scale(v[it][e], s, rs)
+                                                               : v[it][e] / s;
+                        const float r = fminf(fmaxf(__builtin_rintf(qt), -127.f), 127.f);
+                        const uint32_t byte = (uint32_t)(uint8_t)(int8_t)(int)r;
+                        w[e >> 2] |= byte << (8 * (e & 3));
+                    }
                 }
+                *(u32x2*)(qbase + (int64_t)row * HD + 8 * g) = u32x2{w[0], w[1]};
             }
-            *(u32x2*)(qbase + (int64_t)row * HD + 8 * g) = u32x2{w[0], w[1]};
         }
-    }
+    };
+    if (s >= FAST_DIV_MIN_SCALE)
+        store(std::true_type{});
+    else
+        store(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------

@@ -55,22 +55,32 @@ __global__ __launch_bounds__(256) void w8a8_quant_kernel(const uint16_t* __restr
     const float s = amax / 127.0f;
     if (tid == 0) scale[rb * ncb + cb] = s;
     int8_t* qbase = q + (int64_t)r0 * cols + cb * W8 + 8 * g;
+    // q = clamp(rint(v / s)); the quotient through div_by_scale when the
+    // (block-uniform) scale allows, which gives the same bytes
+    auto store = [&](auto fast) {
+        const float rs = decltype(fast)::value ? 1.0f / s : 0.f;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int row = (tid >> 4) + 16 * it;
-        if (row < valid) {
-            uint32_t w[2] = {0u, 0u};
-            if (s > 0.f) {
+        for (int it = 0; it < 8; ++it) {
+            const int row = (tid >> 4) + 16 * it;
+            if (row < valid) {
+                uint32_t w[2] = {0u, 0u};
+                if (s > 0.f) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float r = __builtin_rintf(v[it][e] / s);
-                    r = fminf(fmaxf(r, -127.f), 127.f);
-                    w[e >> 2] |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * (e & 3));
+                    for (int e = 0; e < 8; ++e) {
+                        const float qt = decltype(fast)::value ? div_by_scale(v[it][e], s, rs)
+                                                               : v[it][e] / s;
+                        const float r = fminf(fmaxf(__builtin_rintf(qt), -127.f), 127.f);
+                        w[e >> 2] |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * (e & 3));
+                    }
                 }
+                *(u32x2*)(qbase + (int64_t)row * cols) = u32x2{w[0], w[1]};
             }
-            *(u32x2*)(qbase + (int64_t)row * cols) = u32x2{w[0], w[1]};
         }
-    }
+    };
+    if (s >= FAST_DIV_MIN_SCALE)
+        store(std::true_type{});
+    else
+        store(std::false_type{});
 }
 
 // ---- the product -------------------------------------------------------------
