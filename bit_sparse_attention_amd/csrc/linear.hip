@@ -50,7 +50,7 @@ __device__ __forceinline__ bf16x8 tok8(const uint16_t* tile, int t0, int c0, int
 // holds d at position 16cd + 8hi + s for d = 16cd + 8(s/4) + 4hi + s%4 (the
 // order in which one lane of the 32x32 MFMA output holds its rows), and z
 // follows in the same d order; the GEMM and the apply only need a consistent
-// order, and each lane then stores 16-byte runs.
+// order. The h^T rows are staged in LDS and stored as whole rows.
 //
 // SUMS: the same pass over K also yields what the K mean and the block mask
 // need from raw K, so that K is read once before its quantization instead of
