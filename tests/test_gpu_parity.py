@@ -54,6 +54,39 @@ def test_quant_ties_zero_block_and_spikes(orc):
     assert qi[0, 0, 0, :10].tolist() == [127, -127, 2, -4, 0, 2, 0, 126, -2, 3]
 
 
+def _with_denormals(x, rows, count, seed):
+    """x (bf16, [B,H,N,D]) with `count` elements of each given token row set to
+    bf16 denormals of random sign (bit patterns 1 .. 127 in the mantissa)."""
+    g = torch.Generator().manual_seed(seed)
+    xb = x.contiguous().view(torch.int16).clone()
+    for t in rows:
+        cols = torch.randperm(x.shape[-1], generator=g)[:count]
+        mant = torch.randint(1, 128, (count,), generator=g, dtype=torch.int16)
+        sign = torch.randint(0, 2, (count,), generator=g, dtype=torch.int16) * -32768
+        xb[0, 0, t, cols] = mant | sign
+    return xb.view(torch.bfloat16)
+
+
+def test_quant_tiny_scales_and_denormals(orc):
+    # Q blocks (128 tokens): block 0 scaled by 2^-100 and block 3 by 2^-88
+    # (scales below 2^-90, where the kernel divides), block 1 by 2^-80 and
+    # block 2 unscaled (the reciprocal path), blocks 1 and 2 with denormal
+    # elements; K scaled by 2^-100 throughout (tiny smoothed blocks)
+    q, k, v = make_qkv(1, 1, 512, 128, seed=21)
+    qf = q.float()
+    qf[0, 0, 0:128] *= 2.0 ** -100
+    qf[0, 0, 128:256] *= 2.0 ** -80
+    qf[0, 0, 384:512] *= 2.0 ** -88
+    q = _with_denormals(qf.to(torch.bfloat16), range(128, 384, 5), 16, seed=3)
+    kt = (k.float() * 2.0 ** -100).to(torch.bfloat16)
+    (qi, qs, _, ks), _ = _quant_and_check(orc, q, kt, "tiny scales / denormals")
+    s = qs.flatten().cpu()
+    assert s[0] < 2.0 ** -90 and s[3] < 2.0 ** -90 and s[1] > 2.0 ** -90 and s[2] > 2.0 ** -90
+    assert float(ks.max()) < 2.0 ** -90
+    # and unscaled K with denormals in Q only: the reciprocal path for both
+    _quant_and_check(orc, q, k, "denormals, normal K")
+
+
 @pytest.mark.parametrize("B,H,N,topk", [(1, 2, 1000, 0.25), (1, 1, 4100, 0.1), (1, 2, 8192, 0.05),
                                         (1, 1, 1000, 1.0), (1, 1, 1000, 0.0), (1, 1, 64, 0.5),
                                         (2, 1, 3000, 0.3)])

@@ -50,6 +50,29 @@ def test_w8a8_quant_zero_block(orc):
     assert float(s[0, 1]) == 0.0 and int(q[:128, 128:].abs().max()) == 0
 
 
+def test_w8a8_quant_tiny_scales_and_denormals(orc):
+    # 128x128 blocks scaled by 2^-100 and 2^-88 (scales below 2^-90: the kernel
+    # divides) and by 2^-80 or not at all (the reciprocal path), with bf16
+    # denormals sprinkled into the latter: bytes and scales bit-exact
+    x, _ = make_linear(256, 128, 256, seed=4)
+    xf = x.float()
+    xf[:128, :128] *= 2.0 ** -100
+    xf[:128, 128:] *= 2.0 ** -88
+    xf[128:, :128] *= 2.0 ** -80
+    xb = xf.to(torch.bfloat16).view(torch.int16).clone()
+    g = torch.Generator().manual_seed(7)
+    idx = torch.randint(0, 256 * 256, (600,), generator=g)
+    rows, cols = idx // 256, idx % 256
+    keep = rows >= 128  # the two blocks of the reciprocal path
+    mant = torch.randint(1, 128, (600,), generator=g, dtype=torch.int16)
+    xb[rows[keep], cols[keep]] = mant[keep]
+    x = xb.view(torch.bfloat16)
+    say("[w8a8 quant] tiny scales / denormals")
+    q, s, _, _ = _check_quant(orc, x, "tiny scales / denormals")
+    sc = s.cpu()
+    assert sc[0, 0] < 2.0 ** -90 and sc[0, 1] < 2.0 ** -90 and sc[1, 0] > 2.0 ** -90
+
+
 @pytest.mark.parametrize("M,N,K,with_bias", [(1, 128, 128, False), (300, 256, 384, False),
                                              (700, 384, 1280, False), (257, 128, 640, False),
                                              (300, 256, 384, True), (1, 128, 640, True)])
