@@ -226,7 +226,7 @@ StepWs ws_step(const Dims& d, bool linear) {
 // tiles, the inverse selection lists and the linear branch's gradient states
 struct BwdWs {
     AttnWs attn;
-    size_t mlog, dstat, dol, kt16, counts, lists, gf, gs, gs_lo, gtot, msel, gc, total;
+    size_t mlog, dstat, dol, kt16, counts, lists, bits, gf, gs, gs_lo, gtot, msel, gc, total;
 };
 BwdWs ws_bwd(const Dims& d, bool sel, bool linear) {
     BwdWs w{};
@@ -244,6 +244,7 @@ BwdWs ws_bwd(const Dims& d, bool sel, bool linear) {
     if (sel) {
         w.counts = take((size_t)d.BH * d.nkb * 4);
         w.lists = take((size_t)d.BH * d.nkb * d.nqb * 2);
+        w.bits = take(keep_bits_bytes(d.BH, d.nqb, d.nkb));
     }
     if (linear) {
         const int64_t nqbp = (d.nqb + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
@@ -742,7 +743,8 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     if (e == hipSuccess && linear) e = enqueue_complement(d, kidx, keep, base, w.attn, st);
     if (e == hipSuccess && sel)
         e = launch_inv_lists(kidx, (int)keep, d.BH, (int)d.nqb, (int)d.nkb,
-                             (uint16_t*)(base + w.lists), (int32_t*)(base + w.counts), st);
+                             (uint32_t*)(base + w.bits), (uint16_t*)(base + w.lists),
+                             (int32_t*)(base + w.counts), st);
     if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (states)");
     // the linear branch's dq first (the sparse branch adds to it), with dO . o_l
     // per row when D comes from the forward's output

@@ -89,25 +89,41 @@ __global__ __launch_bounds__(256) void transpose_tiles_kernel(const T* __restric
 
 // ---- the query blocks that kept each key block ----------------------------
 // lists[bh][j][0..counts[bh][j]) = the query blocks i (ascending) whose kept
-// list kidx[bh][i] (ascending) holds j, found by binary search.
-__global__ __launch_bounds__(256) void inv_lists_kernel(const int32_t* __restrict__ kidx, int keep,
+// list kidx[bh][i] holds j. Two passes over a bit matrix bits[bh][j][i / 32]
+// (cleared beforehand): one thread per kept entry sets bit i of its block's
+// row, then one thread per key block emits the set bits of its row in
+// ascending i. Entries outside [0, nkb) are ignored.
+__global__ __launch_bounds__(256) void keep_bits_kernel(const int32_t* __restrict__ kidx, int keep,
+                                                        int nqb, int nkb, int64_t entries,
+                                                        uint32_t* __restrict__ bits) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= entries) return;
+    const int64_t row = e / keep;  // bh * nqb + i
+    const int i = (int)(row % nqb);
+    const int64_t bh = row / nqb;
+    const int j = kidx[e];
+    if (j < 0 || j >= nkb) return;
+    const int words = (nqb + 31) >> 5;
+    atomicOr(bits + (bh * nkb + j) * words + (i >> 5), 1u << (i & 31));
+}
+
+__global__ __launch_bounds__(256) void inv_lists_kernel(const uint32_t* __restrict__ bits,
                                                         int nqb, int nkb,
                                                         uint16_t* __restrict__ lists,
                                                         int32_t* __restrict__ counts) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     const int64_t bh = blockIdx.y;
     if (j >= nkb) return;
-    const int32_t* rows = kidx + bh * nqb * (int64_t)keep;
+    const int words = (nqb + 31) >> 5;
+    const uint32_t* row = bits + (bh * nkb + j) * words;
     uint16_t* out = lists + (bh * nkb + j) * (int64_t)nqb;
     int cnt = 0;
-    for (int i = 0; i < nqb; ++i) {
-        const int32_t* r = rows + (int64_t)i * keep;
-        int lo = 0, hi = keep;  // first entry >= j
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (r[mid] < j) lo = mid + 1; else hi = mid;
+    for (int w = 0; w < words; ++w) {
+        uint32_t x = row[w];
+        while (x) {
+            out[cnt++] = (uint16_t)(32 * w + __builtin_ctz(x));
+            x &= x - 1u;
         }
-        if (lo < keep && r[lo] == j) out[cnt++] = (uint16_t)i;
     }
     counts[bh * nkb + j] = cnt;
 }
@@ -831,10 +847,20 @@ hipError_t launch_bwd_prep(const BwdArgs& a, uint16_t* kt16, hipStream_t st) {
     return hipGetLastError();
 }
 
+size_t keep_bits_bytes(int64_t BH, int64_t nqb, int64_t nkb) {
+    return (size_t)BH * nkb * ((nqb + 31) / 32) * 4;
+}
+
 hipError_t launch_inv_lists(const int32_t* kidx, int keep, int64_t BH, int nqb, int nkb,
-                            uint16_t* lists, int32_t* counts, hipStream_t st) {
-    hipLaunchKernelGGL(inv_lists_kernel, dim3((nkb + 255) / 256, BH), dim3(256), 0, st, kidx, keep,
-                       nqb, nkb, lists, counts);
+                            uint32_t* bits, uint16_t* lists, int32_t* counts, hipStream_t st) {
+    const int64_t nwords = (int64_t)BH * nkb * ((nqb + 31) / 32);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<int64_t>((nwords + 255) / 256, 65536)),
+                       dim3(256), 0, st, (float*)bits, nwords);
+    const int64_t entries = (int64_t)BH * nqb * keep;
+    hipLaunchKernelGGL(keep_bits_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, st,
+                       kidx, keep, nqb, nkb, entries, bits);
+    hipLaunchKernelGGL(inv_lists_kernel, dim3((nkb + 255) / 256, BH), dim3(256), 0, st, bits, nqb,
+                       nkb, lists, counts);
     return hipGetLastError();
 }
 

@@ -91,8 +91,10 @@ struct BwdArgs {
     float *dq, *dk, *dv;     // fp32 [BH][N][128]
 };
 hipError_t launch_bwd_prep(const BwdArgs& a, uint16_t* kt16, hipStream_t st);
+// bytes of the bit matrix launch_inv_lists builds the lists from
+size_t keep_bits_bytes(int64_t BH, int64_t nqb, int64_t nkb);
 hipError_t launch_inv_lists(const int32_t* kidx, int keep, int64_t BH, int nqb, int nkb,
-                            uint16_t* lists, int32_t* counts, hipStream_t st);
+                            uint32_t* bits, uint16_t* lists, int32_t* counts, hipStream_t st);
 hipError_t launch_bwd_sparse(const BwdArgs& a, hipStream_t st);
 hipError_t launch_lin_bwd_q(const uint16_t* q, const uint16_t* dout, const float* hnon, int64_t BH,
                             int N, int accumulate, float* dq, float* gf, uint16_t* gs,
