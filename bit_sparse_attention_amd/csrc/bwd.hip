@@ -303,21 +303,25 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 
 // D[t] = dO_t . out_t - dol[t] per query row, from the forward's fp32 output
 // (o_s + o_l) and the linear branch's dO . o_l (dol null: sparse branch only):
-// the sparse branch's D = dO . o_s without re-running the forward. One wave
-// per row, two channels per lane, the sum as a butterfly over the wave.
+// the sparse branch's D = dO . o_s without re-running the forward. Sixteen
+// lanes per row (each 8 channels: one 16-byte dO load, two 16-byte output
+// loads), four rows per wave, the sum as a butterfly over the 16 lanes.
 __global__ __launch_bounds__(256) void dstat_kernel(const uint16_t* __restrict__ dout,
                                                     const float* __restrict__ out32,
                                                     const float* __restrict__ dol, int64_t rows,
                                                     float* __restrict__ dstat) {
-    const int lane = threadIdx.x & 63;
-    for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < rows;
-         t += (int64_t)gridDim.x * 4) {
-        const uint32_t g2 = *(const uint32_t*)(dout + t * HD + 2 * lane);
-        const f32x2 o2 = *(const f32x2*)(out32 + t * HD + 2 * lane);
-        float s = __builtin_fmaf(bf2f((uint16_t)(g2 & 0xFFFFu)), o2[0], bf2f((uint16_t)(g2 >> 16)) * o2[1]);
+    const int c = threadIdx.x & 15;
+    for (int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); t < rows;
+         t += (int64_t)gridDim.x * 16) {
+        const u16x8 g = *(const u16x8*)(dout + t * HD + 8 * c);
+        const f32x4 o0 = *(const f32x4*)(out32 + t * HD + 8 * c);
+        const f32x4 o1 = *(const f32x4*)(out32 + t * HD + 8 * c + 4);
+        float s = bf2f(g[0]) * o0[0];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-        if (lane == 0) dstat[t] = dol ? s - dol[t] : s;
+        for (int e = 1; e < 8; ++e) s = __builtin_fmaf(bf2f(g[e]), e < 4 ? o0[e] : o1[e - 4], s);
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (c == 0) dstat[t] = dol ? s - dol[t] : s;
     }
 }
 
@@ -887,7 +891,7 @@ hipError_t launch_lin_bwd_q(const uint16_t* q, const uint16_t* dout, const float
 
 hipError_t launch_dstat(const uint16_t* dout, const float* out32, const float* dol, int64_t rows,
                         float* dstat, hipStream_t st) {
-    const int64_t wg = std::min<int64_t>((rows + 3) / 4, 65536);
+    const int64_t wg = std::min<int64_t>((rows + 15) / 16, 65536);
     hipLaunchKernelGGL(dstat_kernel, dim3((unsigned)wg), dim3(256), 0, st, dout, out32, dol, rows,
                        dstat);
     return hipGetLastError();
