@@ -344,22 +344,23 @@ __global__ __launch_bounds__(LS_THREADS, 1) void linear_states_kernel(const uint
 // H_total[bh][n] = sum over groups, in group order, of the fp32 partials.
 __global__ __launch_bounds__(256) void htot_kernel(const float* __restrict__ hpart, int ngroups,
                                                    float* __restrict__ htot) {
-    const int n = blockIdx.x * 256 + threadIdx.x;
+    // thread: four consecutive entries n = 4*n4 .. +3, one 16-byte load per group
+    const int n4 = blockIdx.x * 256 + threadIdx.x;
     const int64_t bh = blockIdx.y;
-    if (n >= HS_ROW) return;
-    // loads in batches of 16 so they are in flight together; the adds stay in
-    // group order
-    const float* p = hpart + bh * ngroups * (int64_t)HS_ROW + n;
-    float s = 0.f;
+    if (n4 >= HS_ROW / 4) return;
+    // loads in batches of 16 groups so they are in flight together (the index
+    // clamped, so every load is unconditional); the adds stay in group order
+    const float* p = hpart + bh * ngroups * (int64_t)HS_ROW + 4 * n4;
+    f32x4 s = f32x4{};
     for (int g0 = 0; g0 < ngroups; g0 += 16) {
-        float v[16];
+        f32x4 v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = g0 + u < ngroups ? p[(int64_t)(g0 + u) * HS_ROW] : 0.f;
+        for (int u = 0; u < 16; ++u) v[u] = *(const f32x4*)(p + (int64_t)min(g0 + u, ngroups - 1) * HS_ROW);
 #pragma unroll
         for (int u = 0; u < 16; ++u)
             if (g0 + u < ngroups) s += v[u];
     }
-    htot[bh * HS_ROW + n] = s;
+    *(f32x4*)(htot + bh * HS_ROW + 4 * n4) = s;
 }
 
 // ---- the 0/1 selection matrix, as offsets into a bf16 expansion table ------
@@ -670,7 +671,7 @@ hipError_t launch_linear_states(const uint16_t* k, const uint16_t* v, int64_t BH
     else
         hipLaunchKernelGGL((linear_states_kernel<true, false>), dim3(ngroups, BH), dim3(LS_THREADS),
                            0, st, k, v, N, nkb, ngroups, vt, hs, nullptr, hpart, nullptr, nullptr, 0);
-    hipLaunchKernelGGL(htot_kernel, dim3((HS_ROW + 255) / 256, BH), dim3(256), 0, st, hpart, ngroups,
+    hipLaunchKernelGGL(htot_kernel, dim3((HS_ROW / 4 + 255) / 256, BH), dim3(256), 0, st, hpart, ngroups,
                        htot);
     return hipGetLastError();
 }
@@ -729,7 +730,7 @@ hipError_t launch_complement_lists(const uint16_t* lists, const int32_t* counts,
 
 hipError_t launch_state_total(const float* part, int ngroups, int64_t BH, float* out,
                               hipStream_t st) {
-    hipLaunchKernelGGL(htot_kernel, dim3((HS_ROW + 255) / 256, BH), dim3(256), 0, st, part,
+    hipLaunchKernelGGL(htot_kernel, dim3((HS_ROW / 4 + 255) / 256, BH), dim3(256), 0, st, part,
                        ngroups, out);
     return hipGetLastError();
 }
