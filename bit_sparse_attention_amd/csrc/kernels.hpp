@@ -9,11 +9,14 @@ namespace ssa {
 // division, from rs = 1/s (itself an IEEE division): q0 = x*rs, then one fma
 // correction with the exact residual x - s*q0 (Markstein's method, 1990: with a
 // correctly rounded reciprocal the corrected quotient is correctly rounded as
-// long as the residual does not underflow). Callers use it only when
+// long as the residual does not underflow). Callers use it only for finite
 // s >= 2^-90; then a residual can underflow only for |x| < s/4, whose quotient
-// rounds to the integer 0 either way. Checked against the IEEE division on
-// 1.6e8 (x, s) pairs: every quotient with |x| >= s/4 equal bit for bit.
+// rounds to the integer 0 either way. (An infinite scale, from an infinite
+// element, takes the division: there 1/s = 0 would turn finite x into NaN.)
+// Checked against the IEEE division on 1.6e8 (x, s) pairs: every quotient
+// with |x| >= s/4 equal bit for bit.
 constexpr float FAST_DIV_MIN_SCALE = 0x1p-90f;
+constexpr float FAST_DIV_MAX_SCALE = 3.40282347e+38f;  // the largest finite float
 __device__ __forceinline__ float div_by_scale(float x, float s, float rs) {
     const float q0 = x * rs;
     return __builtin_fmaf(__builtin_fmaf(-s, q0, x), rs, q0);

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
             }
         }
     };
-    if (s >= FAST_DIV_MIN_SCALE)
+    if (s >= FAST_DIV_MIN_SCALE && s <= FAST_DIV_MAX_SCALE)
         store(std::true_type{});
     else
         store(std::false_type{});

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void w8a8_quant_kernel(const uint16_t* __restr
             }
         }
     };
-    if (s >= FAST_DIV_MIN_SCALE)
+    if (s >= FAST_DIV_MIN_SCALE && s <= FAST_DIV_MAX_SCALE)
         store(std::true_type{});
     else
         store(std::false_type{});

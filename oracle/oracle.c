@@ -139,6 +139,11 @@ void orc_k_mean(const uint16_t* k, int64_t BH, int64_t N, int64_t D, float* mu) 
 /* Per-block INT8 quantization (page 5, Pillar One: attention in 8-bit      */
 /* integers). Reading: one fp32 scale per (head, block) over all channels,  */
 /* scale = amax/127, q = rint(x/scale) with ties to even, symmetric range.  */
+/* The clamp to +-127 is IEEE minNum/maxNum (C99 fminf/fmaxf), which drops  */
+/* a NaN operand: a NaN quotient (a NaN element, or an infinite element    */
+/* over its block's infinite scale) becomes -127. The pages do not cover    */
+/* non-finite inputs; this is the reading, and it keeps every conversion    */
+/* to int8 defined.                                                          */
 
 typedef struct {
     const uint16_t* x;
@@ -171,9 +176,7 @@ static void quant_task(void* vctx, int64_t idx) {
             if (mu) v = v - mu[d];
             int8_t q = 0;
             if (s > 0.0f) {
-                float r = rintf(v / s);
-                if (r > 127.0f) r = 127.0f;
-                if (r < -127.0f) r = -127.0f;
+                const float r = fminf(fmaxf(rintf(v / s), -127.0f), 127.0f);
                 q = (int8_t)r;
             }
             c->xq[(bh * N + t) * D + d] = q;
@@ -639,9 +642,9 @@ static void w8_quant_task(void* vctx, int64_t idx) {
         for (int64_t k = c0; k < c0 + ORC_W8_BLK; ++k) {
             int8_t q = 0;
             if (s > 0.0f) {
-                float v = rintf(orc_bf16_to_f32(c->x[r * c->cols + k]) / s);
-                if (v > 127.0f) v = 127.0f;
-                if (v < -127.0f) v = -127.0f;
+                /* the clamp as in the attention quantizer (NaN -> -127) */
+                const float v =
+                    fminf(fmaxf(rintf(orc_bf16_to_f32(c->x[r * c->cols + k]) / s), -127.0f), 127.0f);
                 q = (int8_t)v;
             }
             c->q[r * c->cols + k] = q;

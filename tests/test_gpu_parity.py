@@ -85,6 +85,11 @@ def test_quant_tiny_scales_and_denormals(orc):
     assert float(ks.max()) < 2.0 ** -90
     # and unscaled K with denormals in Q only: the reciprocal path for both
     _quant_and_check(orc, q, k, "denormals, normal K")
+    # an infinite element in Q block 2: an infinite scale, which must divide
+    qi16 = q.contiguous().view(torch.int16).clone()
+    qi16[0, 0, 300, 7] = 0x7F80
+    (qi, qs, _, _), _ = _quant_and_check(orc, qi16.view(torch.bfloat16), k, "infinite element")
+    assert torch.isinf(qs.flatten()[2].cpu())
 
 
 @pytest.mark.parametrize("B,H,N,topk", [(1, 2, 1000, 0.25), (1, 1, 4100, 0.1), (1, 2, 8192, 0.05),

@@ -66,11 +66,14 @@ def test_w8a8_quant_tiny_scales_and_denormals(orc):
     keep = rows >= 128  # the two blocks of the reciprocal path
     mant = torch.randint(1, 128, (600,), generator=g, dtype=torch.int16)
     xb[rows[keep], cols[keep]] = mant[keep]
+    xb[200, 200] = 0x7F80  # +inf: block [1][1] gets an infinite scale (the division path)
+    xb[201, 201] = -0x80   # -inf (0xFF80) in the same block
     x = xb.view(torch.bfloat16)
-    say("[w8a8 quant] tiny scales / denormals")
-    q, s, _, _ = _check_quant(orc, x, "tiny scales / denormals")
+    say("[w8a8 quant] tiny scales / denormals / infinities")
+    q, s, _, _ = _check_quant(orc, x, "tiny scales / denormals / infinities")
     sc = s.cpu()
     assert sc[0, 0] < 2.0 ** -90 and sc[0, 1] < 2.0 ** -90 and sc[1, 0] > 2.0 ** -90
+    assert torch.isinf(sc[1, 1])
 
 
 @pytest.mark.parametrize("M,N,K,with_bias", [(1, 128, 128, False), (300, 256, 384, False),

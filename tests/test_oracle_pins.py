@@ -219,6 +219,29 @@ def test_quant_zero_block(orc):
     assert sc[0, 1] == np.float32(1.0) / np.float32(127.0) and np.all(xq[0, 150:] == 127)
 
 
+def test_quant_non_finite_elements(orc):
+    # Reading (the pages do not cover non-finite inputs): the clamp to +-127 is
+    # IEEE minNum/maxNum, so a NaN quotient becomes -127. An infinite element
+    # makes its block's scale infinite: every finite element then quantizes to
+    # 0 and the infinite ones (inf/inf = NaN) to -127; a NaN element in a finite
+    # block does not change the scale and also gives -127.
+    x = np.zeros((1, 256, 128), np.float32)
+    x[0, :128, :] = 0.5
+    x[0, 3, 7] = np.inf
+    x[0, 4, 9] = -np.inf
+    x[0, 128:, :] = 2.0
+    x[0, 130, 1] = np.nan
+    xq, sc = orc.quant(_bits(torch.from_numpy(x)), None, 128)
+    assert np.isinf(sc[0, 0]) and sc[0, 1] == np.float32(2.0) / np.float32(127.0)
+    assert xq[0, 3, 7] == -127 and xq[0, 4, 9] == -127
+    blk0 = xq[0, :128].copy()
+    blk0[3, 7] = blk0[4, 9] = 0
+    assert np.all(blk0 == 0)
+    assert xq[0, 130, 1] == -127 and xq[0, 129, 1] == 127
+    q, s = orc.w8a8_quant(_bits(torch.from_numpy(x[0, :128])))
+    assert np.isinf(s[0, 0]) and q[3, 7] == -127 and q[4, 9] == -127 and q[0, 0] == 0
+
+
 # --------------------------------------------------------------------------
 # int32 scores
 
