@@ -68,6 +68,7 @@ def test_w8a8_quant_tiny_scales_and_denormals(orc):
     xb[rows[keep], cols[keep]] = mant[keep]
     xb[200, 200] = 0x7F80  # +inf: block [1][1] gets an infinite scale (the division path)
     xb[201, 201] = -0x80   # -inf (0xFF80) in the same block
+    xb[150, 20] = 0x7FC0   # a NaN in block [1][0] (finite scale, the reciprocal path)
     x = xb.view(torch.bfloat16)
     say("[w8a8 quant] tiny scales / denormals / infinities")
     q, s, _, _ = _check_quant(orc, x, "tiny scales / denormals / infinities")
