@@ -588,14 +588,21 @@ __device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, f32x16 c) {
 constexpr int LB_P = HD + 1;  // odd LDS pitch: row- and column-wise fragment reads hit distinct banks
 constexpr int LB_T = 64;      // tokens staged at a time
 
-// Stage a state row as M[d][e] (pitch LB_P) and its vector part as vec[d]:
-// every load of the thread is issued before the first LDS store.
-__device__ __forceinline__ void stage_state(const float* __restrict__ row, float* M, float* vec) {
-    const int tid = threadIdx.x;
+// Stage a state row as M[d][e] (pitch LB_P) and its vector part as vec[d],
+// in two halves so that a caller can put other loads in flight between them:
+// load_state issues every load of the thread, store_state writes LDS.
+struct StateRegs {
     f32x4 r[16];
+    f32x4 z;
+};
+__device__ __forceinline__ void load_state(const float* __restrict__ row, StateRegs& s) {
+    const int tid = threadIdx.x;
 #pragma unroll
-    for (int it = 0; it < 16; ++it) r[it] = *(const f32x4*)(row + 4 * (tid + 256 * it));
-    const f32x4 zr = tid < 32 ? *(const f32x4*)(row + HD * HD + 4 * tid) : f32x4{};
+    for (int it = 0; it < 16; ++it) s.r[it] = *(const f32x4*)(row + 4 * (tid + 256 * it));
+    s.z = tid < 32 ? *(const f32x4*)(row + HD * HD + 4 * tid) : f32x4{};
+}
+__device__ __forceinline__ void store_state(const StateRegs& s, float* M, float* vec) {
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
         const int x4 = tid + 256 * it, e = x4 >> 5;
@@ -603,28 +610,30 @@ __device__ __forceinline__ void stage_state(const float* __restrict__ row, float
         // its own inverse and keeps the two low bits)
         const int d0 = state_pos(4 * (x4 & 31));
 #pragma unroll
-        for (int m = 0; m < 4; ++m) M[(d0 + m) * LB_P + e] = r[it][m];
+        for (int m = 0; m < 4; ++m) M[(d0 + m) * LB_P + e] = s.r[it][m];
     }
     if (tid < 32) {
         const int d0 = state_pos(4 * tid);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) vec[d0 + m] = zr[m];
+        for (int m = 0; m < 4; ++m) vec[d0 + m] = s.z[m];
     }
 }
 
 // Stage rows r0 .. r0+nrow-1 (64 of them, rows past nval zero) of a bf16
-// [tokens x 128] tensor into X[row][channel] (pitch LB_P) in fp32, through fn.
-template <typename F>
-__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int nval, float* X,
-                                           F fn) {
+// [tokens x 128] tensor into X[row][channel] (pitch LB_P) in fp32, through fn;
+// again as a load half and a store half.
+__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ src, int nval, u16x8 (&r)[4]) {
     const int tid = threadIdx.x;
-    u16x8 r[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         // rows past nval re-read row nval-1 (finite values, scaled to 0 below)
         const int c = tid + 256 * it, tt = min(c >> 4, nval - 1);
         r[it] = *(const u16x8*)(src + (int64_t)tt * HD + 8 * (c & 15));
     }
+}
+template <typename F>
+__device__ __forceinline__ void store_rows(const u16x8 (&r)[4], int nval, float* X, F fn) {
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int c = tid + 256 * it, tt = c >> 4, d0 = 8 * (c & 15);
@@ -678,19 +687,33 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __res
     const int i = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    stage_state(hnon + (bh * nqb + i) * (int64_t)HS_ROW, Hs, zv);
+    const int nt = min(QBLK, N - i * QBLK);
+    // rows of the half being staged (q and dO), loaded a half ahead: the
+    // first half's together with the state, the second during the first's
+    // products
+    u16x8 qr[4], gr[4];
+    {
+        StateRegs sr;
+        load_state(hnon + (bh * nqb + i) * (int64_t)HS_ROW, sr);
+        load_rows(q + (bh * N + i * QBLK) * HD, nt, qr);
+        load_rows(dout + (bh * N + i * QBLK) * HD, nt, gr);
+        store_state(sr, Hs, zv);
+    }
     f32x16 gacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) gacc[dt] = f32x16{};
     float wacc = 0.f;  // threads 0..127: w[tid]
-    const int nt = min(QBLK, N - i * QBLK);
     const int rt = wave & 1, ct0 = 2 * (wave >> 1);
     for (int h0 = 0; h0 < nt; h0 += LB_T) {
         __syncthreads();  // the state is staged / the previous half is done
-        const int64_t r0 = bh * N + i * QBLK + h0;
-        stage_rows(q + r0 * HD, nt - h0, As, [](float x) { return phi_f(x); });
-        stage_rows(dout + r0 * HD, nt - h0, Gs, [](float x) { return x; });
+        store_rows(qr, nt - h0, As, [](float x) { return phi_f(x); });
+        store_rows(gr, nt - h0, Gs, [](float x) { return x; });
         __syncthreads();
+        if (h0 + LB_T < nt) {
+            const int64_t rn = bh * N + i * QBLK + h0 + LB_T;
+            load_rows(q + rn * HD, nt - h0 - LB_T, qr);
+            load_rows(dout + rn * HD, nt - h0 - LB_T, gr);
+        }
         {  // den: four threads per token
             const int tt = tid >> 2, part = tid & 3;
             float dn = 0.f;
@@ -800,13 +823,36 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_k_kernel(const uint16_t* __res
     const int j = blockIdx.x;
     const int64_t bh = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    stage_state(gc + (bh * nkb + j) * (int64_t)HS_ROW, Ms, wv);
     const int nk = min(KBLK, N - j * KBLK);
     const int64_t r0 = bh * N + j * KBLK;
-    stage_rows(k + r0 * HD, nk, Fs, [](float x) { return phi_f(x); });
-    stage_rows(v + r0 * HD, nk, Vs, [](float x) { return x; });
+    {
+        // every staging load (the state, K and V rows) in flight together
+        StateRegs sr;
+        u16x8 kr[4], vr[4];
+        load_state(gc + (bh * nkb + j) * (int64_t)HS_ROW, sr);
+        load_rows(k + r0 * HD, nk, kr);
+        load_rows(v + r0 * HD, nk, vr);
+        store_state(sr, Ms, wv);
+        store_rows(kr, nk, Fs, [](float x) { return phi_f(x); });
+        store_rows(vr, nk, Vs, [](float x) { return x; });
+    }
     __syncthreads();
     const int rt = wave & 1, ct0 = 2 * (wave >> 1);
+    // With accumulate, the sparse branch's dk and dv of this lane's outputs
+    // are loaded before the products, so their latency hides behind them
+    // (rows past nk re-read row nk-1; those outputs are not stored).
+    float odk[2][16], odv[2][16];
+    if (accumulate) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int uu = min(32 * rt + mfma32_row(lane, r), nk - 1);
+                const int64_t o = (bh * N + j * KBLK + uu) * HD + 32 * (ct0 + c) + l32;
+                odk[c][r] = dk[o];
+                odv[c][r] = dv[o];
+            }
+    }
     f32x16 gk[2] = {f32x16{}, f32x16{}}, gv[2] = {f32x16{}, f32x16{}};
     for (int k0 = 0; k0 < HD; k0 += 2) {
         const float va = Vs[(32 * rt + l32) * LB_P + k0 + hi];  // v[u][e = k]
@@ -829,8 +875,8 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_k_kernel(const uint16_t* __res
                 if (decltype(ragged)::value && uu >= nk) continue;
                 const int64_t o = (bh * N + j * KBLK + uu) * HD + n;
                 const float g = (gk[c][r] + wv[n]) * fminf(Fs[uu * LB_P + n], 1.f);
-                dk[o] = decltype(acc)::value ? dk[o] + g : g;
-                dv[o] = decltype(acc)::value ? dv[o] + gv[c][r] : gv[c][r];
+                dk[o] = decltype(acc)::value ? odk[c][r] + g : g;
+                dv[o] = decltype(acc)::value ? odv[c][r] + gv[c][r] : gv[c][r];
             }
         }
     };
