@@ -627,9 +627,22 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     const float sgn = complement ? 1.f : -1.f;  // base - sum == base + (-sum) exactly
     const int rc = lane & 15;                   // the 16-byte piece of a row this lane stores
     const f32x4 ht = *(const f32x4*)(htot + bh * HS_ROW + n0 + 4 * rc);
+    // accumulate pass: the first pass's values of a 32-row block, loaded one
+    // block ahead so that their latency overlaps the previous block's stores
+    // (rows past nqb re-read row nqb-1; they are not stored)
+    f32x4 bv[2][8];
+    auto load_base = [&](int ib, f32x4 (&v)[8]) {
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const int i = min(iw + 32 * ib + 4 * rr + (lane >> 4), nqb - 1);
+            v[rr] = *(const f32x4*)(hnon + (bh * nqb + i) * (int64_t)HS_ROW + n0 + 4 * rc);
+        }
+    };
+    if (accum) load_base(0, bv[0]);
     __syncthreads();
 #pragma unroll
     for (int ib = 0; ib < CG_IB; ++ib) {
+        if (accum && ib + 1 < CG_IB) load_base(ib + 1, bv[(ib + 1) & 1]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -647,7 +660,7 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
             const f32x4 sum = *(const f32x4*)(stg + r * EP + 4 * rc);
             f32x4* o = (f32x4*)(hnon + (bh * nqb + i) * (int64_t)HS_ROW + n0 + 4 * rc);
             // accum: a second pass (the stack's bf16 rests) onto the first
-            const f32x4 base = accum ? *o : (complement ? f32x4{} : ht);
+            const f32x4 base = accum ? bv[ib & 1][rr] : (complement ? f32x4{} : ht);
             *o = base + sum;
         }
         __syncthreads();
