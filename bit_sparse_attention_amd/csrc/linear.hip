@@ -391,13 +391,15 @@ __device__ __forceinline__ u32x4 sel_entry(uint32_t e) {
 
 // Selection rows in the order the GEMM reads them. K step ks covers key
 // blocks 32ks .. 32ks+31, bytes b0..b3 of that word. An MFMA lane of k-half
-// hi needs bytes hi and 2+hi of each K step, as table byte offsets:
-// dword(ks, hi) = 16*slot(b_hi) | 16*slot(b_{2+hi}) << 16. Steps are paired
-// (kp = ks/2) and stored [bh][kp][i][hi][ks&1]: the 16 bytes of one row and
-// pair are contiguous, and so are the rows of one pair. Key blocks past nkb,
-// and the second step of an unpaired last one, select nothing.
-// Rows come from kidx (keep entries each) or, for the backward's transposed
-// selection, from lists (counts[bh][row] entries each, row length ld).
+// hi needs bytes hi and 2+hi of each K step, as table slots. Steps are paired
+// (kp = ks/2) and a row of a pair is 8 bytes: dword hi holds
+// slot(b_hi), slot(b_{2+hi}) of step 2kp, then the same of step 2kp+1, one
+// byte each. Layout [bh][kp][i][8 bytes] over an even row count (rows past
+// the last one select nothing), so that one 16-byte load takes two rows.
+// Key blocks past nkb, and the second step of an unpaired last one, select
+// nothing. Rows come from kidx (keep entries each) or, for the backward's
+// transposed selection, from lists (counts[bh][row] entries each, row length
+// ld).
 constexpr int SEL_MAX_WORDS = SSA_MAX_N / KBLK / 32 + 2;
 template <bool LISTS>
 __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ kidx, int keep,
@@ -408,11 +410,13 @@ __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ k
     __shared__ uint32_t bits[SEL_MAX_WORDS];
     const int64_t bh = blockIdx.y;
     const int i = blockIdx.x;
-    const int nkp = (nks + 1) / 2;
+    const int nkp = (nks + 1) / 2, nqbp = (nqb + 1) & ~1;
+    const bool pad = i >= nqb;
     for (int w = threadIdx.x; w < 2 * nkp; w += 256) bits[w] = 0;
     __syncthreads();
     // kept block indices are clamped into [0, nkb)
-    if (LISTS) {
+    if (pad) {
+    } else if (LISTS) {
         const uint16_t* src = lists + (bh * nqb + i) * (int64_t)ld;
         const int n = counts[bh * nqb + i];
         for (int a = threadIdx.x; a < n; a += 256) {
@@ -427,7 +431,7 @@ __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ k
         }
     }
     __syncthreads();
-    if (complement) {
+    if (complement && !pad) {
         // the blocks below nkb that are not kept
         for (int w = threadIdx.x; w < 2 * nkp; w += 256) {
             const int lo = 32 * w;
@@ -437,17 +441,17 @@ __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ k
         __syncthreads();
     }
     for (int kp = threadIdx.x; kp < nkp; kp += 256) {
-        u32x4 o;
+        u32x2 o = u32x2{0u, 0u};
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const uint32_t x = bits[2 * kp + half];
 #pragma unroll
             for (int hi = 0; hi < 2; ++hi) {
                 const uint32_t lo8 = (x >> (8 * hi)) & 255u, hi8 = (x >> (8 * (2 + hi))) & 255u;
-                o[2 * hi + half] = 16u * sel_slot(lo8) | (16u * sel_slot(hi8)) << 16;
+                o[hi] |= (sel_slot(lo8) | sel_slot(hi8) << 8) << (16 * half);
             }
         }
-        *(u32x4*)(msel + ((bh * nkp + kp) * nqb + i) * 4) = o;
+        *(u32x2*)(msel + ((bh * nkp + kp) * nqbp + i) * 2) = o;
     }
 }
 
@@ -456,23 +460,25 @@ __global__ __launch_bounds__(256) void msel_kernel(const int32_t* __restrict__ k
 // or, with `complement` (the selection rows then mark the non-kept blocks),
 //   hnon[bh][i][n] = sum_j hs[bh][j][n] * sel[bh][i][j]
 // for query blocks i < nqb, state entries n < HS_ROW, key blocks j < nkbp.
+// With LO the states are given as a bf16 stack and a second stack of each
+// entry's bf16 rest, and hs[j][n] is their sum: both products go into the
+// same fp32 accumulators.
 // C^T = Hs^T . Sel^T on 32x32x16 bf16 MFMAs with fp32 accumulation: the A
 // operand is a state fragment, the B operand a selection fragment from the
-// table, and each lane of the result holds four consecutive n of one i,
-// stored as 16-byte runs.
+// table, and each lane of the result holds four consecutive n of one i.
 //
 // Workgroup tile: 64 n x 640 i (every query block of a head, up to 640).
 // Wave w owns rows 160w .. 160w+159 (five 32-row blocks) against both 32-wide
 // halves of n: 10 accumulators. The K loop runs over pairs of 32-key-block
 // steps; a pair's operands form one stage of a 3-deep LDS ring, fetched by LDS
 // DMA two stages ahead:
-//   the [64 j][64 n] bf16 state tile (8 KB, 128-byte rows), two 1 KB DMAs per
-//     wave; 16-byte chunk c of row r sits at chunk c ^ 4*((r >> 1) & 1), and
-//     the tile is read with transposing loads (lds_read_tr16) that give a lane
-//     4 consecutive j of one n, the 32 lanes of a half wave hitting distinct
-//     8-byte bank groups;
-//   the pair's selection (16 bytes per row), each wave fetching its own 160
-//     rows.
+//   the [64 j][64 n] bf16 state tile (8 KB, 128-byte rows; with LO the rest
+//     tile after it), two 1 KB DMAs per wave and tile; 16-byte chunk c of row
+//     r sits at chunk c ^ 4*((r >> 1) & 1), and the tile is read with
+//     transposing loads (lds_read_tr16) that give a lane 4 consecutive j of
+//     one n, the 32 lanes of a half wave hitting distinct 8-byte bank groups;
+//   the pair's selection (8 bytes per row), each wave fetching its own 160
+//     rows (1280 bytes: one full DMA and a quarter of one).
 // The whole state stack is read once.
 constexpr int CG_TN = 64;                  // state entries per workgroup
 constexpr int CG_IB = 5;                   // 32-row query blocks per wave
@@ -481,12 +487,17 @@ constexpr int CG_TM = 4 * CG_WROWS;        // query blocks per workgroup
 constexpr int CG_TK = GEMM_KALIGN;         // key blocks per selection word (half a stage)
 constexpr int CG_STAGES = 3;
 constexpr int CG_TILE = 2 * CG_TK * CG_TN * 2;  // bytes of a stage's state tile [64 j][64 n]
-constexpr int CG_SEL = CG_TM * 16;              // bytes of a stage's selection
-constexpr int CG_STAGE = CG_TILE + CG_SEL;
+constexpr int CG_SELROW = 8;                    // selection bytes per row and stage
+constexpr int CG_SEL = CG_TM * CG_SELROW;       // bytes of a stage's selection
 constexpr int CG_LUT = 256 * 16;                // bytes of the expansion table
+template <bool LO>
+constexpr int cg_stage() { return (LO ? 2 : 1) * CG_TILE + CG_SEL; }
+template <bool LO>
+constexpr int cg_lds() { return CG_STAGES * cg_stage<LO>() + CG_LUT; }
 static_assert(CG_TK == 32, "selection dword per lane per 32 key blocks");
 static_assert(HS_ROW % CG_TN == 0, "state rows split into whole column tiles");
-static_assert(CG_WROWS == 160, "selection DMAs: two of 64 rows and one of 32 per wave");
+static_assert(CG_WROWS * CG_SELROW == 1024 + 16 * 16, "selection DMAs: one of 128 rows and one of 32 per wave");
+static_assert(2 * cg_lds<true>() <= 160 * 1024, "two workgroups per CU");
 
 int64_t complement_tiles_per_head(int64_t nqb) {
     return (int64_t)(HS_ROW / CG_TN) * ((nqb + CG_TM - 1) / CG_TM);
@@ -494,15 +505,19 @@ int64_t complement_tiles_per_head(int64_t nqb) {
 
 size_t msel_bytes(int64_t BH, int64_t nqb, int64_t nkbp) {
     const int64_t nkp = (nkbp / CG_TK + 1) / 2;
-    return (size_t)BH * nkp * nqb * 16;
+    return (size_t)BH * nkp * ((nqb + 1) & ~int64_t(1)) * CG_SELROW;
 }
 
+template <bool LO>
 __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     const uint32_t* __restrict__ msel, const uint16_t* __restrict__ hs,
-    const float* __restrict__ htot, int64_t BH, int nqb, int nkb, int nkbp, int complement,
-    int accum, float* __restrict__ hnon) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[CG_STAGES * CG_STAGE + CG_LUT];
-    uint8_t* lut = smem + CG_STAGES * CG_STAGE;
+    const uint16_t* __restrict__ hs_lo, const float* __restrict__ htot, int64_t BH, int nqb,
+    int nkb, int nkbp, int complement, float* __restrict__ hnon) {
+    constexpr int STAGE = cg_stage<LO>();
+    constexpr int NT = LO ? 2 : 1;  // state tiles per stage
+    constexpr int DMAS = 2 * NT + 2;  // LDS DMAs per wave and stage
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[cg_lds<LO>()];
+    uint8_t* lut = smem + CG_STAGES * STAGE;
     const int nnt = HS_ROW / CG_TN, nmt = (nqb + CG_TM - 1) / CG_TM;
     const int64_t total = BH * nnt * nmt;
     const int64_t item = xcd_item(blockIdx.x, total);  // i tiles fastest: they share state tiles
@@ -514,36 +529,41 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     const int i0 = mt * CG_TM, n0 = nt * CG_TN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31,
               hi = lane >> 5;
-    const int nks = nkbp / CG_TK, nkp = (nks + 1) / 2;
-    const int iw = i0 + CG_WROWS * wave;  // first query block of this wave
+    const int nks = nkbp / CG_TK, nkp = (nks + 1) / 2, nqbp = (nqb + 1) & ~1;
+    const int iw = i0 + CG_WROWS * wave;  // first query block of this wave (even)
 
     *(u32x4*)(lut + 16 * sel_slot((uint32_t)tid)) = sel_entry((uint32_t)tid);
 
-    // stage kp: state rows j = 64kp .. 64kp+63 (wave w fills rows 16w .. 16w+15,
-    // two DMAs; lane l row 16w + 8p + l/8 at slot l%8, holding chunk
-    // (l%8) ^ 4*((row >> 1) & 1)) and the selection of that K-step pair
+    // stage kp: state rows j = 64kp .. 64kp+63 (wave w fills rows 16w .. 16w+15
+    // of each tile, two DMAs; lane l row 16w + 8p + l/8 at slot l%8, holding
+    // chunk (l%8) ^ 4*((row >> 1) & 1)) and the selection of that K-step pair
+    // (lane l of DMA p: rows 2(64p + l), +1 of the wave's, past the padded row
+    // count re-reading the last two)
     const int dchunk = (lane & 7) ^ (4 * (((lane >> 3) >> 1) & 1));
-    const uint16_t* bbase = hs + (bh * nkb) * (int64_t)HS_ROW + n0;
+    const int64_t sbase0 = (bh * nkb) * (int64_t)HS_ROW + n0;
     auto issue = [&](int kp, int st) {
-        uint8_t* T = smem + st * CG_STAGE;
-        uint8_t* S = T + CG_TILE;
-        const uint32_t* sbase = msel + (bh * nkp + kp) * (int64_t)nqb * 4;
+        uint8_t* T = smem + st * STAGE;
+        uint8_t* S = T + NT * CG_TILE;
+        const uint32_t* sbase = msel + (bh * nkp + kp) * (int64_t)nqbp * 2;
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
-            const int i = min(iw + 64 * p + lane, nqb - 1);
-            if (p < 2 || lane < 32)
-                dma16(sbase, (uint32_t)(i * 16), lds_u32(S + (CG_WROWS * wave + 64 * p) * 16));
+        for (int p = 0; p < 2; ++p) {
+            const int c = min((iw >> 1) + 64 * p + lane, (nqbp >> 1) - 1);
+            if (p == 0 || lane < 16)
+                dma16(sbase, (uint32_t)(c * 16), lds_u32(S + CG_WROWS * CG_SELROW * wave + 1024 * p));
         }
         const int j0 = 2 * CG_TK * kp;
         // rows past nkb (their selection bits are 0) re-read row nkb-1; j0 < nkb
         // because nkbp rounds nkb up by less than one selection word
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int row = 16 * wave + 8 * p + (lane >> 3);
-            const int r = min(j0 + row, nkb - 1) - j0;
-            dma16(bbase + (int64_t)j0 * HS_ROW, (uint32_t)(r * HS_ROW * 2 + dchunk * 16),
-                  lds_u32(T + (16 * wave + 8 * p) * 128));
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int row = 16 * wave + 8 * p + (lane >> 3);
+                const int r = min(j0 + row, nkb - 1) - j0;
+                dma16((t ? hs_lo : hs) + sbase0 + (int64_t)j0 * HS_ROW,
+                      (uint32_t)(r * HS_ROW * 2 + dchunk * 16),
+                      lds_u32(T + t * CG_TILE + (16 * wave + 8 * p) * 128));
+            }
     };
 
     f32x16 acc[CG_IB][2];
@@ -552,54 +572,63 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
 
     auto kstep = [&](auto stage) {
         constexpr int R = decltype(stage)::value;
-        const uint8_t* B = smem + R * CG_STAGE;
-        const uint8_t* S = B + CG_TILE;
+        const uint8_t* B = smem + R * STAGE;
+        const uint8_t* S = B + NT * CG_TILE;
+        // byte 2*half + kc of sd[ib]: the table slot of this lane's fragment
+        uint32_t sd[CG_IB];
+#pragma unroll
+        for (int ib = 0; ib < CG_IB; ++ib)
+            sd[ib] = *(const uint32_t*)(S + (CG_WROWS * wave + 32 * ib + l32) * CG_SELROW + 4 * hi);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            uint32_t sd[CG_IB];
-#pragma unroll
-            for (int ib = 0; ib < CG_IB; ++ib)
-                sd[ib] = *(const uint32_t*)(S + (CG_WROWS * wave + 32 * ib + l32) * 16 + 8 * hi + 4 * half);
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                bf16x8 hf[2];
+                bf16x8 hf[NT][2];
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const int col = 32 * nb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-                    i16x4 part[2];
+                for (int t = 0; t < NT; ++t)
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int row = 32 * half + 16 * kc + 8 * hi + 4 * t + ((lane & 15) >> 2);
-                        const int unit = (col >> 2) ^ (8 * ((row >> 1) & 1));
-                        part[t] = lds_read_tr16(B + row * 128 + unit * 8);
+                    for (int nb = 0; nb < 2; ++nb) {
+                        const int col = 32 * nb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                        i16x4 part[2];
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int row = 32 * half + 16 * kc + 8 * hi + 4 * u + ((lane & 15) >> 2);
+                            const int unit = (col >> 2) ^ (8 * ((row >> 1) & 1));
+                            part[u] = lds_read_tr16(B + t * CG_TILE + row * 128 + unit * 8);
+                        }
+                        const u32x2 w0 = __builtin_bit_cast(u32x2, part[0]);
+                        const u32x2 w1 = __builtin_bit_cast(u32x2, part[1]);
+                        hf[t][nb] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
                     }
-                    const u32x2 w0 = __builtin_bit_cast(u32x2, part[0]);
-                    const u32x2 w1 = __builtin_bit_cast(u32x2, part[1]);
-                    hf[nb] = __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
-                }
+                bf16x8 sf[CG_IB];
 #pragma unroll
-                for (int ib = 0; ib < CG_IB; ++ib) {
-                    const uint32_t off = kc ? (sd[ib] >> 16) : (sd[ib] & 0xFFFFu);
-                    const bf16x8 sf = *(const bf16x8*)(lut + off);
-                    acc[ib][0] = mfma_bf16_32x32x16(hf[0], sf, acc[ib][0]);
-                    acc[ib][1] = mfma_bf16_32x32x16(hf[1], sf, acc[ib][1]);
-                }
+                for (int ib = 0; ib < CG_IB; ++ib)
+                    sf[ib] = *(const bf16x8*)(lut + 16 * ((sd[ib] >> (8 * (2 * half + kc))) & 0xFFu));
+                // the rest tile's products after all of the high tile's, so no
+                // accumulator is the input of the next MFMA
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int ib = 0; ib < CG_IB; ++ib) {
+                        acc[ib][0] = mfma_bf16_32x32x16(hf[t][0], sf[ib], acc[ib][0]);
+                        acc[ib][1] = mfma_bf16_32x32x16(hf[t][1], sf[ib], acc[ib][1]);
+                    }
             }
         }
     };
 
-    // Pipeline over K-step pairs: stage kp % 3, two stages ahead. Each stage is
-    // 5 DMAs per wave; at the end of step kp only stage kp+2's may stay in flight.
+    // Pipeline over K-step pairs: stage kp % 3, two stages ahead. At the end of
+    // step kp only stage kp+2's DMAS per wave may stay in flight.
     issue(0, 0);
     if (nkp > 1) issue(1, 1);
-    if (nkp > 1) wait_vm<5>(); else wait_vm<0>();
+    if (nkp > 1) wait_vm<DMAS>(); else wait_vm<0>();
     __syncthreads();  // also publishes the expansion table
     auto step = [&](int kp, auto stage) {
         constexpr int R = decltype(stage)::value;
         if (kp + 2 < nkp) issue(kp + 2, (R + 2) % CG_STAGES);
         kstep(stage);
         if (kp + 1 < nkp) {
-            if (kp + 2 < nkp) wait_vm<5>(); else wait_vm<0>();
+            if (kp + 2 < nkp) wait_vm<DMAS>(); else wait_vm<0>();
             __syncthreads();
         }
     };
@@ -622,27 +651,14 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
     // that the result is base + staged, and stores it as whole 256-byte row
     // pieces: 16 lanes per row instead of 32-byte runs in 32 rows.
     constexpr int EP = CG_TN + 4;  // pitch (floats) of a staged row: 272 B
-    static_assert(4 * 32 * EP * 4 <= CG_STAGES * CG_STAGE, "the staging fits the rings");
+    static_assert(4 * 32 * EP * 4 <= CG_STAGES * STAGE, "the staging fits the rings");
     float* stg = reinterpret_cast<float*>(smem) + wave * 32 * EP;
     const float sgn = complement ? 1.f : -1.f;  // base - sum == base + (-sum) exactly
     const int rc = lane & 15;                   // the 16-byte piece of a row this lane stores
-    const f32x4 ht = *(const f32x4*)(htot + bh * HS_ROW + n0 + 4 * rc);
-    // accumulate pass: the first pass's values of a 32-row block, loaded one
-    // block ahead so that their latency overlaps the previous block's stores
-    // (rows past nqb re-read row nqb-1; they are not stored)
-    f32x4 bv[2][8];
-    auto load_base = [&](int ib, f32x4 (&v)[8]) {
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int i = min(iw + 32 * ib + 4 * rr + (lane >> 4), nqb - 1);
-            v[rr] = *(const f32x4*)(hnon + (bh * nqb + i) * (int64_t)HS_ROW + n0 + 4 * rc);
-        }
-    };
-    if (accum) load_base(0, bv[0]);
+    const f32x4 base = complement ? f32x4{} : *(const f32x4*)(htot + bh * HS_ROW + n0 + 4 * rc);
     __syncthreads();
 #pragma unroll
     for (int ib = 0; ib < CG_IB; ++ib) {
-        if (accum && ib + 1 < CG_IB) load_base(ib + 1, bv[(ib + 1) & 1]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -658,10 +674,7 @@ __global__ __launch_bounds__(256, 2) void complement_gemm_kernel(
             const int i = iw + 32 * ib + r;
             if (i >= nqb) continue;
             const f32x4 sum = *(const f32x4*)(stg + r * EP + 4 * rc);
-            f32x4* o = (f32x4*)(hnon + (bh * nqb + i) * (int64_t)HS_ROW + n0 + 4 * rc);
-            // accum: a second pass (the stack's bf16 rests) onto the first
-            const f32x4 base = accum ? bv[ib & 1][rr] : (complement ? f32x4{} : ht);
-            *o = base + sum;
+            *(f32x4*)(hnon + (bh * nqb + i) * (int64_t)HS_ROW + n0 + 4 * rc) = base + sum;
         }
         __syncthreads();
     }
@@ -712,15 +725,16 @@ hipError_t launch_complement(const int32_t* kidx, int keep, const uint16_t* hs,
     const int nkbp = (nkb + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
     // sum whichever of the kept and the non-kept sets is smaller
     const int complement = 2 * keep > nkb ? 1 : 0;
-    hipLaunchKernelGGL(msel_kernel<false>, dim3(nqb, BH), dim3(256), 0, st, kidx, keep, nullptr,
-                       nullptr, 0, nqb, nkb, nkbp / GEMM_KALIGN, complement, msel);
+    hipLaunchKernelGGL(msel_kernel<false>, dim3((nqb + 1) & ~1, BH), dim3(256), 0, st, kidx, keep,
+                       nullptr, nullptr, 0, nqb, nkb, nkbp / GEMM_KALIGN, complement, msel);
     const int64_t total = BH * complement_tiles_per_head(nqb);
     const int64_t grid = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel, hs, htot,
-                       BH, nqb, nkb, nkbp, complement, 0, hnon);
     if (hs_lo)
-        hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel,
-                           hs_lo, htot, BH, nqb, nkb, nkbp, complement, 1, hnon);
+        hipLaunchKernelGGL(complement_gemm_kernel<true>, dim3((unsigned)grid), dim3(256), 0, st,
+                           msel, hs, hs_lo, htot, BH, nqb, nkb, nkbp, complement, hnon);
+    else
+        hipLaunchKernelGGL(complement_gemm_kernel<false>, dim3((unsigned)grid), dim3(256), 0, st,
+                           msel, hs, nullptr, htot, BH, nqb, nkb, nkbp, complement, hnon);
     return hipGetLastError();
 }
 
@@ -729,15 +743,16 @@ hipError_t launch_complement_lists(const uint16_t* lists, const int32_t* counts,
                                    const uint16_t* stack_lo, const float* total, int64_t BH,
                                    uint32_t* msel, float* out, hipStream_t st) {
     const int nredp = (nred + GEMM_KALIGN - 1) / GEMM_KALIGN * GEMM_KALIGN;
-    hipLaunchKernelGGL(msel_kernel<true>, dim3(nrows, BH), dim3(256), 0, st, nullptr, 0, lists,
-                       counts, nred, nrows, nred, nredp / GEMM_KALIGN, complement, msel);
+    hipLaunchKernelGGL(msel_kernel<true>, dim3((nrows + 1) & ~1, BH), dim3(256), 0, st, nullptr, 0,
+                       lists, counts, nred, nrows, nred, nredp / GEMM_KALIGN, complement, msel);
     const int64_t tiles = BH * complement_tiles_per_head(nrows);
     const int64_t grid = (tiles + 7) / 8 * 8;
-    hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel, stack,
-                       total, BH, nrows, nred, nredp, complement, 0, out);
     if (stack_lo)
-        hipLaunchKernelGGL(complement_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, st, msel,
-                           stack_lo, total, BH, nrows, nred, nredp, complement, 1, out);
+        hipLaunchKernelGGL(complement_gemm_kernel<true>, dim3((unsigned)grid), dim3(256), 0, st,
+                           msel, stack, stack_lo, total, BH, nrows, nred, nredp, complement, out);
+    else
+        hipLaunchKernelGGL(complement_gemm_kernel<false>, dim3((unsigned)grid), dim3(256), 0, st,
+                           msel, stack, nullptr, total, BH, nrows, nred, nredp, complement, out);
     return hipGetLastError();
 }
 
