@@ -164,13 +164,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     const bool qok = tq < N;
     const int nsel = DENSE ? nkb : a.keep;
     const int32_t* krow = DENSE ? nullptr : a.kidx + (bh * a.nqb + i) * (int64_t)a.keep;
-    auto blk = [&](int jj) { return DENSE ? jj : min(max(krow[jj], 0), nkb - 1); };
-    const float sq = a.q_scale[bh * a.nqb + i];
+    // kept block indices and their K scales come through the scalar cache
+    auto blk = [&](int jj) {
+        return DENSE ? jj : min(max((int)ld_uniform(krow + jj), 0), nkb - 1);
+    };
+    const float sq = ld_uniform_f32(a.q_scale + bh * a.nqb + i);
     const float* ksc = a.k_scale + bh * nkb;
 
     // stage layout: K tile | V tile | K^T tile
-    auto issue = [&](int jj, int st) {
-        const int j = blk(jj);
+    auto issue = [&](int j, int st) {
         uint8_t* base = smem + st * DQ_STAGE;
         const int nval = min(KBLK, N - j * KBLK);
         // K: 64 rows of 128 B, chunk c of row r at slot c ^ swz8(r); rows past
@@ -221,19 +223,27 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
-    issue(0, 0);
+    // j0, sk0: the block of step jj and its scale; j1: the block of step jj+1.
+    // Each is loaded a step before its use, so its latency stays off the path.
+    int j0 = blk(0), j1 = nsel > 1 ? blk(1) : 0;
+    float sk0 = ld_uniform_f32(ksc + j0);
+    issue(j0, 0);
     for (int jj = 0; jj < nsel; ++jj) {
         const int st = jj & 1;
+        int j2 = 0;
+        float sk1 = 0.f;
         if (jj + 1 < nsel) {
-            issue(jj + 1, st ^ 1);
+            issue(j1, st ^ 1);
+            sk1 = ld_uniform_f32(ksc + j1);
+            if (jj + 2 < nsel) j2 = blk(jj + 2);
             wait_vm<DQ_DMAS>();
         } else {
             wait_vm<0>();
         }
         __syncthreads();
-        const int j = blk(jj);
+        const int j = j0;
         const int kval = min(KBLK, N - j * KBLK);
-        const float sk = ksc[j];
+        const float sk = sk0;
         const float c = (sq * sk) * a.K32;
         const uint8_t* kt = smem + st * DQ_STAGE;
         const uint8_t* vt = kt + DQ_KT;
@@ -285,6 +295,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
                 acc[dt] = mfma_bf16_32x32x16(ka, dsb[cc], acc[dt]);
             }
         __syncthreads();  // the next issue refills this stage
+        j0 = j1;
+        j1 = j2;
+        sk0 = sk1;
     }
     if (qok) {
         float* row = a.dq + (bh * N + tq) * HD;
@@ -393,11 +406,12 @@ __global__ __launch_bounds__(DK_THREADS, 2) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int cq = 0; cq < 4; ++cq) kfr[cq] = *(const i32x4*)(kp + 32 * cq + 16 * hi);
     }
-    const float sk = a.k_scale[bh * a.nkb + j];
-    const int cnt = DENSE ? nqb : a.counts[bh * a.nkb + j];
-    const uint16_t* list = DENSE ? nullptr : a.lists + (bh * a.nkb + j) * (int64_t)nqb;
+    // the block's scale, list length and list entries come through the scalar cache
+    const float sk = ld_uniform_f32(a.k_scale + bh * a.nkb + j);
+    const int cnt = DENSE ? nqb : (int)ld_uniform(a.counts + bh * a.nkb + j);
+    const int64_t lbase = (bh * a.nkb + j) * (int64_t)nqb;  // the block's list in a.lists
     // steps: (kept query block x, half f), halves entirely past N skipped
-    auto qblock = [&](int x) { return DENSE ? x : (int)list[x]; };
+    auto qblock = [&](int x) { return DENSE ? x : ld_uniform_u16(a.lists, lbase + x); };
     auto has_half = [&](int i, int f) { return i * QBLK + DK_Q * f < N; };
 
     // one step's q_i8 and dO rows (rows past N re-read row N-1: their P and
@@ -452,10 +466,13 @@ __global__ __launch_bounds__(DK_THREADS, 2) void dkdv_kernel(BwdArgs a) {
     // 16qs + 8t + 4hi + (l&15)/4 at channels col .. col+3
     const int col = 32 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const int rsub = 4 * hi + ((lane & 15) >> 2);
+    // i, sq: the query block of this step and its scale; i1: the block after
+    // it in the list. Each is loaded a step before its use.
     int x = 0, f = 0;
-    if (cnt > 0) prefetch(qblock(0) * QBLK);
+    int i = cnt > 0 ? qblock(0) : 0, i1 = cnt > 1 ? qblock(1) : 0;
+    float sq = ld_uniform_f32(a.q_scale + bh * nqb + i);
+    if (cnt > 0) prefetch(i * QBLK);
     while (x < cnt) {
-        const int i = qblock(x);
         const int q0 = i * QBLK + DK_Q * f;
         // the step after this one
         int xn = x, fn = f + 1;
@@ -463,10 +480,18 @@ __global__ __launch_bounds__(DK_THREADS, 2) void dkdv_kernel(BwdArgs a) {
             xn = x + 1;
             fn = 0;
         }
+        const int in = xn == x ? i : i1;
         stage();
         __syncthreads();  // tiles and statistics of the step visible
-        if (xn < cnt) prefetch(qblock(xn) * QBLK + DK_Q * fn);
-        const float sq = a.q_scale[bh * nqb + i];
+        int i1n = i1;
+        float sqn = sq;
+        if (xn < cnt) {
+            prefetch(in * QBLK + DK_Q * fn);
+            if (xn != x) {
+                sqn = ld_uniform_f32(a.q_scale + bh * nqb + in);
+                if (xn + 1 < cnt) i1n = qblock(xn + 1);
+            }
+        }
         const float c = (sq * sk) * a.K32;
         {
             i32x16 s = i32x16{};
@@ -544,6 +569,9 @@ __global__ __launch_bounds__(DK_THREADS, 2) void dkdv_kernel(BwdArgs a) {
         __syncthreads();  // the next step rewrites the tiles and fragments
         x = xn;
         f = fn;
+        i = in;
+        i1 = i1n;
+        sq = sqn;
     }
     // lane (key column l32 of tile h, hi) holds channels 32w + 8(r/4) + 4hi + r%4
 #pragma unroll
