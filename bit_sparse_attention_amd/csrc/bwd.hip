@@ -204,6 +204,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
         }
     };
 
+    // j0, sk0: the block of step jj and its scale; j1: the block of step jj+1.
+    // Each is loaded a step before its use, so its latency stays off the path.
+    int j0 = blk(0), j1 = nsel > 1 ? blk(1) : 0;
+    float sk0 = ld_uniform_f32(ksc + j0);
+    issue(j0, 0);
+
     // per-lane operands: Q (int8 B operand of S^T), dO (bf16 B operand of dP^T)
     i32x4 qop[4];
     bf16x8 dop[8];
@@ -218,16 +224,16 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     }
     const float mq = qok ? a.mlog[bh * N + tq] : 0.f;
     const float Dq = qok ? a.dstat[bh * N + tq] : 0.f;
+    // The compiler does not see the LDS DMAs: with these loads outstanding at
+    // the loop, it would wait for them in every step with a vmcnt that also
+    // covers part of the next stage's DMAs. Waiting here (for them and the
+    // first stage) clears them once.
+    wait_vm<0>();
 
     f32x16 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
-    // j0, sk0: the block of step jj and its scale; j1: the block of step jj+1.
-    // Each is loaded a step before its use, so its latency stays off the path.
-    int j0 = blk(0), j1 = nsel > 1 ? blk(1) : 0;
-    float sk0 = ld_uniform_f32(ksc + j0);
-    issue(j0, 0);
     for (int jj = 0; jj < nsel; ++jj) {
         const int st = jj & 1;
         int j2 = 0;
@@ -299,8 +305,17 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
         j1 = j2;
         sk0 = sk1;
     }
+    // accumulating: every value the row already holds is loaded before the
+    // first store (rows past N read row N-1 and store nothing)
+    float* row = a.dq + (bh * N + (qok ? tq : N - 1)) * HD;
+    f32x4 prev[16];
+    if (a.dq_accumulate) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) prev[4 * dt + q4] = *(const f32x4*)(row + 32 * dt + 8 * q4 + 4 * hi);
+    }
     if (qok) {
-        float* row = a.dq + (bh * N + tq) * HD;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -308,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
                 const int dv = 32 * dt + 8 * q4 + 4 * hi;
                 f32x4 g = f32x4{acc[dt][4 * q4] * a.sm, acc[dt][4 * q4 + 1] * a.sm,
                                 acc[dt][4 * q4 + 2] * a.sm, acc[dt][4 * q4 + 3] * a.sm};
-                if (a.dq_accumulate) g = g + *(const f32x4*)(row + dv);
+                if (a.dq_accumulate) g = g + prev[4 * dt + q4];
                 *(f32x4*)(row + dv) = g;
             }
     }
