@@ -387,14 +387,14 @@ constexpr int DK_QB = DK_QI + DK_Q * HD;       // bf16 Q tile [64][256 B], chunk
 constexpr int DK_GO = DK_QB + DK_Q * HD * 2;   // bf16 dO tile, same layout
 constexpr int DK_PF = DK_GO + DK_Q * HD * 2;   // P fragments
 constexpr int DK_DF = DK_PF + KV_F;            // dS fragments
-constexpr int DK_ST = DK_DF + KV_F;            // m' and D of the step's 64 queries
+constexpr int DK_ST = DK_DF + KV_F;            // m' and -D sq of the step's 64 queries
 constexpr int DK_LDS = DK_ST + 2 * DK_Q * 4;
 static_assert(2 * DK_LDS <= 160 * 1024, "two workgroups per CU");
 
 template <bool DENSE>
 __global__ __launch_bounds__(DK_THREADS, 2) void dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[DK_LDS];
-    float* stat = reinterpret_cast<float*>(smem + DK_ST);  // [m', D][query of the step]
+    float* stat = reinterpret_cast<float*>(smem + DK_ST);  // [m', -D sq][query of the step]
     const int64_t item = blockIdx.x;
     if (item >= a.BH * a.nkb) return;
     const int64_t bh = item / a.nkb;
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(DK_THREADS, 2) void dkdv_kernel(BwdArgs a) {
             spre = (tid < DK_Q ? a.mlog : a.dstat)[bh * N + t];
         }
     };
-    auto stage = [&]() {
+    auto stage = [&](float sq) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int x = tid + DK_THREADS * it, row = x >> 4, c = x & 15;
@@ -472,7 +472,8 @@ __global__ __launch_bounds__(DK_THREADS, 2) void dkdv_kernel(BwdArgs a) {
             for (int h = 0; h < 2; ++h)
                 *(bf16x8*)(smem + DK_QB + row * 256 + 16 * ((2 * c + h) ^ qswz(row))) = w[h];
         }
-        if (tid < 2 * DK_Q) stat[tid] = spre;
+        // m' as is; D as -D sq, so that dS = p (dP - D) sq is p (dP sq - D sq)
+        if (tid < 2 * DK_Q) stat[tid] = tid < DK_Q ? spre : -(spre * sq);
     };
 
     f32x16 dva[2], dka[2];  // channels 32w + ..., key tiles 0, 1
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(DK_THREADS, 2) void dkdv_kernel(BwdArgs a) {
             fn = 0;
         }
         const int in = xn == x ? i : i1;
-        stage();
+        stage(sq);
         __syncthreads();  // tiles and statistics of the step visible
         int i1n = i1;
         float sqn = sq;
@@ -530,14 +531,14 @@ __global__ __launch_bounds__(DK_THREADS, 2) void dkdv_kernel(BwdArgs a) {
                 for (int g = 0; g < 4; ++g) {
                     const int r0 = 32 * qw + 8 * g + 4 * hi;  // queries of registers 4g .. 4g+3
                     const f32x4 mq = *(const f32x4*)(stat + r0);
-                    const f32x4 Dq = *(const f32x4*)(stat + DK_Q + r0);
+                    const f32x4 nDsq = *(const f32x4*)(stat + DK_Q + r0);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * g + e;
                         float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], c, -mq[e]));
                         if constexpr (decltype(ragged)::value) p = (kok && q0 + r0 + e < N) ? p : 0.f;
                         pr[r] = p;
-                        dp[r] = p * (dp[r] - Dq[e]) * sq;
+                        dp[r] = p * __builtin_fmaf(dp[r], sq, nDsq[e]);
                     }
                 }
             };
