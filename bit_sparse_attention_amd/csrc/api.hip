@@ -753,8 +753,8 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     uint16_t* gs_lo = linear ? (uint16_t*)(base + w.gs_lo) : nullptr;
     float* dol = (linear && saved) ? (float*)(base + w.dol) : nullptr;
     if (linear) {
-        e = launch_lin_bwd_q(q, dout, (const float*)(base + w.attn.hnon), d.BH, (int)d.N, 0, dq, gf,
-                             gs, gs_lo, dol, st);
+        e = launch_lin_bwd_q(q, dout, (const float*)(base + w.attn.hnon), d.BH, (int)d.N, dq, gf, gs,
+                             gs_lo, dol, st);
         if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (linear branch)");
     }
     if (sparse) {

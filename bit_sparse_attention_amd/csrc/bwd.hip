@@ -29,6 +29,24 @@
 
 namespace ssa {
 
+// A value every lane reads at one address, from a buffer the kernel does not
+// write, through the scalar cache: a load from the constant address space,
+// which the compiler issues as s_load_dword and waits for on lgkmcnt. Loaded
+// through the vector path instead, its use would get a vmcnt wait, and the
+// compiler, which does not see the LDS DMAs, would make that vmcnt(0) and so
+// drain every DMA in flight. p must be 4-byte aligned.
+__device__ __forceinline__ uint32_t ld_uniform(const void* p) {
+    return *(const __attribute__((address_space(4))) uint32_t*)p;
+}
+__device__ __forceinline__ float ld_uniform_f32(const float* p) {
+    return __uint_as_float(ld_uniform(p));
+}
+// element e of a uint16 array whose base is 4-byte aligned (the aligned pair
+// holding it is read, so the array must extend to an even element count)
+__device__ __forceinline__ int ld_uniform_u16(const uint16_t* base, int64_t e) {
+    return (int)((ld_uniform(base + (e & ~int64_t(1))) >> (16 * (int)(e & 1))) & 0xFFFFu);
+}
+
 // Position p of a re-laid 16-token group holds token perm16(p): positions
 // 0-3 -> 0-3, 4-7 -> 8-11, 8-11 -> 4-7, 12-15 -> 12-15 (bits 2 and 3 swapped):
 // the order in which one lane of the 32x32 MFMA output holds its rows, so a
@@ -708,7 +726,7 @@ __device__ __forceinline__ float halfwave_sum16(const float (&v)[16], int lane) 
 // z[d]), a = phi(q_t), den = a . z, g = dO_t:
 //   u = H g                  (so that g . o_l = a . u / den)
 //   dden = -(a . u) / den^2
-//   dq_t (+)= (u / den + z dden) * phi'(q_t),   phi'(x) = min(phi(x), 1)
+//   dq_t = (u / den + z dden) * phi'(q_t),   phi'(x) = min(phi(x), 1)
 //   G^T[e][d] = sum_t (g[e] / den) a[d],  w[d] = sum_t a[d] dden
 // The two products run on the fp32 matrix cores (exact fp32 products, fp32
 // sums). G^T and w are written in fp32 (gf, for the total) and as bf16 plus
@@ -718,8 +736,7 @@ __device__ __forceinline__ float halfwave_sum16(const float (&v)[16], int lane) 
 __global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ dout,
                                                            const float* __restrict__ hnon, int N,
-                                                           int nqb, int accumulate,
-                                                           float* __restrict__ dq,
+                                                           int nqb, float* __restrict__ dq,
                                                            float* __restrict__ gf,
                                                            uint16_t* __restrict__ gs,
                                                            uint16_t* __restrict__ gs_lo,
@@ -796,7 +813,7 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __res
         }
         __syncthreads();
         // the row check only in a ragged last piece (one uniform branch)
-        auto store_dq = [&](auto ragged, auto acc) {
+        auto store_dq = [&](auto ragged) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const int d = 32 * (ct0 + c) + l32;
@@ -804,20 +821,15 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_q_kernel(const uint16_t* __res
                 for (int r = 0; r < 16; ++r) {
                     const int t = 32 * rt + mfma32_row(lane, r);
                     if (decltype(ragged)::value && h0 + t >= nt) continue;
-                    const float g =
+                    dq[(bh * N + i * QBLK + h0 + t) * HD + d] =
                         (u[c][r] / den_s[t] + zv[d] * dden_s[t]) * fminf(As[t * LB_P + d], 1.f);
-                    const int64_t o = (bh * N + i * QBLK + h0 + t) * HD + d;
-                    dq[o] = decltype(acc)::value ? dq[o] + g : g;
                 }
             }
         };
-        if (h0 + LB_T <= nt) {
-            if (accumulate) store_dq(std::false_type{}, std::true_type{});
-            else store_dq(std::false_type{}, std::false_type{});
-        } else {
-            if (accumulate) store_dq(std::true_type{}, std::true_type{});
-            else store_dq(std::true_type{}, std::false_type{});
-        }
+        if (h0 + LB_T <= nt)
+            store_dq(std::false_type{});
+        else
+            store_dq(std::true_type{});
         for (int x = tid; x < LB_T * HD; x += 256) {
             const int tt = x >> 7, e = x & 127;
             Gs[tt * LB_P + e] = Gs[tt * LB_P + e] / den_s[tt];
@@ -971,11 +983,11 @@ hipError_t launch_bwd_sparse(const BwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_lin_bwd_q(const uint16_t* q, const uint16_t* dout, const float* hnon, int64_t BH,
-                            int N, int accumulate, float* dq, float* gf, uint16_t* gs,
-                            uint16_t* gs_lo, float* dol, hipStream_t st) {
+                            int N, float* dq, float* gf, uint16_t* gs, uint16_t* gs_lo, float* dol,
+                            hipStream_t st) {
     const int nqb = (N + QBLK - 1) / QBLK;
-    hipLaunchKernelGGL(lin_bwd_q_kernel, dim3(nqb, BH), dim3(256), 0, st, q, dout, hnon, N, nqb,
-                       accumulate, dq, gf, gs, gs_lo, dol);
+    hipLaunchKernelGGL(lin_bwd_q_kernel, dim3(nqb, BH), dim3(256), 0, st, q, dout, hnon, N, nqb, dq,
+                       gf, gs, gs_lo, dol);
     return hipGetLastError();
 }
 

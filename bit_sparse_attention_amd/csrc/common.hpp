@@ -97,24 +97,6 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// A value every lane reads at one address, from a buffer the kernel does not
-// write, through the scalar cache: a load from the constant address space,
-// which the compiler issues as s_load_dword and waits for on lgkmcnt. Loaded
-// through the vector path instead, its use would get a vmcnt wait, and the
-// compiler, which does not see the LDS DMAs, would make that vmcnt(0) and so
-// drain every DMA in flight. p must be 4-byte aligned.
-__device__ __forceinline__ uint32_t ld_uniform(const void* p) {
-    return *(const __attribute__((address_space(4))) uint32_t*)p;
-}
-__device__ __forceinline__ float ld_uniform_f32(const float* p) {
-    return __uint_as_float(ld_uniform(p));
-}
-// element e of a uint16 array whose base is 4-byte aligned (the aligned pair
-// holding it is read, so the array must extend to an even element count)
-__device__ __forceinline__ int ld_uniform_u16(const uint16_t* base, int64_t e) {
-    return (int)((ld_uniform(base + (e & ~int64_t(1))) >> (16 * (int)(e & 1))) & 0xFFFFu);
-}
-
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

@@ -100,8 +100,8 @@ hipError_t launch_inv_lists(const int32_t* kidx, int keep, int64_t BH, int nqb, 
                             uint32_t* bits, uint16_t* lists, int32_t* counts, hipStream_t st);
 hipError_t launch_bwd_sparse(const BwdArgs& a, hipStream_t st);
 hipError_t launch_lin_bwd_q(const uint16_t* q, const uint16_t* dout, const float* hnon, int64_t BH,
-                            int N, int accumulate, float* dq, float* gf, uint16_t* gs,
-                            uint16_t* gs_lo, float* dol, hipStream_t st);
+                            int N, float* dq, float* gf, uint16_t* gs, uint16_t* gs_lo, float* dol,
+                            hipStream_t st);
 hipError_t launch_dstat(const uint16_t* dout, const float* out32, const float* dol, int64_t rows,
                         float* dstat, hipStream_t st);
 hipError_t launch_lin_bwd_k(const uint16_t* k, const uint16_t* v, const float* gc, int64_t BH,
