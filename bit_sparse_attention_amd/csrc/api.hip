@@ -222,11 +222,11 @@ StepWs ws_step(const Dims& d, bool linear) {
 }
 
 // the backward: the forward attention's workspace (V layout, and the linear
-// branch's complement states), the row statistics, the channel-first bf16
-// tiles, the inverse selection lists and the linear branch's gradient states
+// branch's complement states), the row statistics, the inverse selection
+// lists and the linear branch's gradient states
 struct BwdWs {
     AttnWs attn;
-    size_t mlog, dstat, dol, kt16, counts, lists, bits, gf, gs, gs_lo, gtot, msel, gc, total;
+    size_t mlog, dstat, dol, counts, lists, bits, gf, gs, gs_lo, gtot, msel, gc, total;
 };
 BwdWs ws_bwd(const Dims& d, bool sel, bool linear) {
     BwdWs w{};
@@ -240,7 +240,6 @@ BwdWs ws_bwd(const Dims& d, bool sel, bool linear) {
     w.mlog = take((size_t)d.BH * d.N * 4);
     w.dstat = take((size_t)d.BH * d.N * 4);
     w.dol = linear ? take((size_t)d.BH * d.N * 4) : 0;
-    w.kt16 = take((size_t)d.BH * d.nkb * HD * KBLK * 2);
     if (sel) {
         w.counts = take((size_t)d.BH * d.nkb * 4);
         w.lists = take((size_t)d.BH * d.nkb * d.nqb * 2);
@@ -797,7 +796,6 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
         b.k_scale = k_scale;
         b.v = v;
         b.dout = dout;
-        b.kt16 = (const uint16_t*)(base + w.kt16);
         b.kidx = kidx;
         b.keep = (int)keep;
         b.lists = sel ? (const uint16_t*)(base + w.lists) : nullptr;
@@ -814,8 +812,6 @@ ssa_status sage_sla_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_
         b.dq = dq;
         b.dk = dk;
         b.dv = dv;
-        if (e == hipSuccess)
-            e = launch_bwd_prep(b, (uint16_t*)(base + w.kt16), st);
         if (e == hipSuccess) e = launch_bwd_sparse(b, st);
         if (e != hipSuccess) return hip_fail(e, "sage_sla_attn_bwd launch (sparse branch)");
     }

@@ -47,64 +47,6 @@ __device__ __forceinline__ int ld_uniform_u16(const uint16_t* base, int64_t e) {
     return (int)((ld_uniform(base + (e & ~int64_t(1))) >> (16 * (int)(e & 1))) & 0xFFFFu);
 }
 
-// Position p of a re-laid 16-token group holds token perm16(p): positions
-// 0-3 -> 0-3, 4-7 -> 8-11, 8-11 -> 4-7, 12-15 -> 12-15 (bits 2 and 3 swapped):
-// the order in which one lane of the 32x32 MFMA output holds its rows, so a
-// tile computed on the matrix cores feeds the next product without shuffles.
-__device__ __forceinline__ int perm16(int p) {
-    return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
-}
-
-// ---- prep: bf16 tiles with the channel dimension first --------------------
-// y[bh][b][d][p] = bf16(x[bh][BLK*b + 16(p/16) + perm16(p%16)][d]) for the
-// BLK-token blocks b of an int8 or bf16 [BH][N][128] tensor; 0 past N.
-template <typename T, int BLK>
-__global__ __launch_bounds__(256) void transpose_tiles_kernel(const T* __restrict__ x, int N, int nb,
-                                                              uint16_t* __restrict__ y) {
-    __shared__ uint16_t t[BLK][HD + 2];
-    const int b = blockIdx.x;
-    const int64_t bh = blockIdx.y;
-    const int tid = threadIdx.x;
-    constexpr int CH = 16 / sizeof(T);  // elements per 16-byte load
-    for (int c = tid; c < BLK * HD / CH; c += 256) {
-        const int r = c / (HD / CH), d0 = (c % (HD / CH)) * CH;
-        const int tok = BLK * b + r;
-        uint16_t v[CH];
-        if (tok < N) {
-            const T* src = x + (bh * N + tok) * HD + d0;
-            if (sizeof(T) == 1) {
-                const i32x4 w = *(const i32x4*)src;
-#pragma unroll
-                for (int e = 0; e < CH; ++e) {
-                    const int8_t q = (int8_t)((w[e >> 2] >> (8 * (e & 3))) & 255);
-                    v[e] = f2bf((float)q);  // exact: |q| <= 127
-                }
-            } else {
-                const u16x8 w = *(const u16x8*)src;
-#pragma unroll
-                for (int e = 0; e < CH; ++e) v[e] = w[e];
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < CH; ++e) v[e] = 0;
-        }
-#pragma unroll
-        for (int e = 0; e < CH; ++e) t[r][d0 + e] = v[e];
-    }
-    __syncthreads();
-    uint16_t* out = y + (bh * nb + b) * (int64_t)HD * BLK;
-    for (int c = tid; c < HD * BLK / 8; c += 256) {
-        const int d = c / (BLK / 8), p0 = 8 * (c % (BLK / 8));
-        u16x8 w;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int p = p0 + e;
-            w[e] = t[16 * (p >> 4) + perm16(p & 15)][d];
-        }
-        *(u16x8*)(out + (int64_t)d * BLK + p0) = w;
-    }
-}
-
 // ---- the query blocks that kept each key block ----------------------------
 // lists[bh][j][0..counts[bh][j]) = the query blocks i (ascending) whose kept
 // list kidx[bh][i] holds j. Two passes over a bit matrix bits[bh][j][i / 32]
@@ -152,25 +94,39 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int64_
 }
 
 // ---- dq: one workgroup per (head, query block), 4 waves x 32 queries ------
-// For each kept key block: its int8 K tile (8 KB, 64 rows of 128 channels),
-// raw bf16 V tile (16 KB, 64 rows of 256 B) and bf16 K^T tile (16 KB, 128
-// channel rows of 64 re-laid keys) arrive in a double-buffered LDS ring by
-// LDS DMA. Per wave (queries 32w + l32, lane pair hi):
+// For each kept key block: its int8 K tile (8 KB, 64 rows of 128 channels)
+// and raw bf16 V tile (16 KB, 64 rows of 256 B) arrive in a double-buffered
+// LDS ring by LDS DMA; the workgroup widens the K tile to bf16 (exact) into a
+// third tile [64 keys][128 channels] (row pitch 288 B) that the dQ product
+// reads with transposing loads. Per wave (queries 32w + l32, lane pair hi):
 //   S^T = K . Q^T         (int8; lane holds query l32, keys 8(r/4)+4hi+r%4 (+32))
 //   dP^T = V . dO^T       (bf16; same layout)
 //   dS^T = P (dP - D) sk  (registers, packed as the next product's B operand)
-//   dQ^T += K^T . dS^T    (bf16, fp32 accumulation)
+//   dQ^T += K^T . dS^T    (bf16, fp32 accumulation; lane l's A fragment is
+//                          channel l%32 at 8 keys in dS's register order, two
+//                          ds_read_b64_tr_b16 of 4 consecutive keys each)
+// Each stage is refilled as soon as every wave has finished the step's S and
+// dP (the barrier that also publishes the widened tile), so two barriers per
+// step and about one and a half steps for each stage to land.
 constexpr int DQ_KT = KBLK * HD;           // int8 K tile
 constexpr int DQ_VT = KBLK * HD * 2;       // raw V tile
-constexpr int DQ_TT = HD * KBLK * 2;       // K^T tile
-constexpr int DQ_STAGE = DQ_KT + DQ_VT + DQ_TT;
+constexpr int DQ_STAGE = DQ_KT + DQ_VT;
+constexpr int DQ_KB = 2 * DQ_STAGE;        // the widened K tile, after the two stages
+constexpr int DQ_KBP = HD * 2 + 32;        // its row pitch: 288 B, so the 4 rows a transposing
+                                           // read touches fall in disjoint bank groups
+constexpr int DQ_LDS = DQ_KB + KBLK * DQ_KBP;
 constexpr int DQ_DMAS = (DQ_STAGE / 1024) / 4;  // 1 KB LDS DMAs per wave per stage
+static_assert(2 * DQ_LDS <= 160 * 1024, "two workgroups per CU");
 
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// bf16 tiles [64 rows][256 B] keep 16-byte chunk c of row r at chunk c ^ qswz(r):
+// 16 consecutive rows at one chunk (row reads) and 4 consecutive rows at 4
+// chunks (transposing reads) both cover all banks
+__device__ __forceinline__ int qswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 template <bool DENSE>
 __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * DQ_STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[DQ_LDS];
     const int64_t item = blockIdx.x;
     if (item >= a.BH * a.nqb) return;
     const int64_t bh = item / a.nqb;
@@ -189,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     const float sq = ld_uniform_f32(a.q_scale + bh * a.nqb + i);
     const float* ksc = a.k_scale + bh * nkb;
 
-    // stage layout: K tile | V tile | K^T tile
+    // stage layout: K tile | V tile
     auto issue = [&](int j, int st) {
         uint8_t* base = smem + st * DQ_STAGE;
         const int nval = min(KBLK, N - j * KBLK);
@@ -212,21 +168,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
                   rr * 256 + 16 * ((lane & 15) ^ (row & 15)),
                   lds_u32(base + DQ_KT) + (16 * wave + 4 * p) * 256);
         }
-        // K^T: 128 rows of 128 B (the V^T tile layout), zero past N
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int row = 32 * wave + 8 * p + (lane >> 3);
-            dma16(a.kt16 + (bh * nkb + j) * (int64_t)HD * KBLK,
-                  row * 128 + 16 * ((lane & 7) ^ swz8(row)),
-                  lds_u32(base + DQ_KT + DQ_VT) + (32 * wave + 8 * p) * 128);
-        }
     };
 
-    // j0, sk0: the block of step jj and its scale; j1: the block of step jj+1.
-    // Each is loaded a step before its use, so its latency stays off the path.
-    int j0 = blk(0), j1 = nsel > 1 ? blk(1) : 0;
+    // j0, sk0: the block of step jj and its scale; j1, j2: the blocks of steps
+    // jj+1, jj+2. Each is loaded ahead of its use, so its latency stays off
+    // the path.
+    int j0 = blk(0), j1 = nsel > 1 ? blk(1) : 0, j2 = nsel > 2 ? blk(2) : 0;
     float sk0 = ld_uniform_f32(ksc + j0);
     issue(j0, 0);
+    if (nsel > 1) issue(j1, 1);
 
     // per-lane operands: Q (int8 B operand of S^T), dO (bf16 B operand of dP^T)
     i32x4 qop[4];
@@ -244,34 +194,44 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     const float Dq = qok ? a.dstat[bh * N + tq] : 0.f;
     // The compiler does not see the LDS DMAs: with these loads outstanding at
     // the loop, it would wait for them in every step with a vmcnt that also
-    // covers part of the next stage's DMAs. Waiting here (for them and the
-    // first stage) clears them once.
+    // covers the DMAs in flight. Waiting here (for them and the first two
+    // stages) clears them once.
     wait_vm<0>();
 
     f32x16 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+    // transposing reads of the dQ product: lane l supplies key row
+    // 16cc + 8t + 4hi + (l&15)/4 at channels 32dt + 16((l>>4)&1) + 4(l&3) .. +3,
+    // one base address plus immediate offsets
+    const uint8_t* kbl = smem + DQ_KB + (4 * hi + ((lane & 15) >> 2)) * DQ_KBP +
+                         2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
     for (int jj = 0; jj < nsel; ++jj) {
         const int st = jj & 1;
-        int j2 = 0;
-        float sk1 = 0.f;
-        if (jj + 1 < nsel) {
-            issue(j1, st ^ 1);
-            sk1 = ld_uniform_f32(ksc + j1);
-            if (jj + 2 < nsel) j2 = blk(jj + 2);
-            wait_vm<DQ_DMAS>();
-        } else {
-            wait_vm<0>();
-        }
-        __syncthreads();
+        // stage jj must land (stage jj+1 may stay in flight)
+        if (jj + 1 < nsel) wait_vm<DQ_DMAS>(); else wait_vm<0>();
+        __syncthreads();  // stage jj visible; every wave is done with the last widened tile
         const int j = j0;
         const int kval = min(KBLK, N - j * KBLK);
         const float sk = sk0;
         const float c = (sq * sk) * a.K32;
         const uint8_t* kt = smem + st * DQ_STAGE;
         const uint8_t* vt = kt + DQ_KT;
-        const uint8_t* tt = vt + DQ_VT;
+        // widen this step's K tile: thread t converts 16 channels of two rows
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int x = tid + 256 * it, row = x >> 3, ch = x & 7;
+            const i32x4 kv = *(const i32x4*)(kt + row * 128 + 16 * (ch ^ swz8(row)));
+            bf16x8 w[2];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int b = (int)((uint32_t)kv[e >> 2] << (24 - 8 * (e & 3))) >> 24;  // signed byte e
+                w[e >> 3][e & 7] = (__bf16)(float)b;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) *(bf16x8*)(smem + DQ_KB + row * DQ_KBP + 16 * (2 * ch + h)) = w[h];
+        }
         i32x16 s[2];
         f32x16 dp[2];
         s[0] = s[1] = i32x16{};
@@ -291,6 +251,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
                 dp[h] = mfma_bf16_32x32x16(va, dop[sd], dp[h]);
             }
         }
+        // the next scale and the block two steps on (stage jj+2), loaded here
+        // and used after the barrier
+        float sk1 = 0.f;
+        int j3 = 0;
+        if (jj + 1 < nsel) sk1 = ld_uniform_f32(ksc + j1);
+        if (jj + 3 < nsel) j3 = blk(jj + 3);
+        __syncthreads();  // the widened tile is visible; every wave is done with stage jj
+        if (jj + 2 < nsel) issue(j2, st);
         // dS; in a ragged last key block the keys past N (copies of key N-1,
         // so p stays finite) are zeroed after the exp: one uniform branch per
         // block instead of a masked branch per score
@@ -314,13 +282,16 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const bf16x8 ka =
-                    *(const bf16x8*)(tt + (32 * dt + l32) * 128 + ((2 * cc + hi) ^ swz8(l32)) * 16);
+                i16x4 kp[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) kp[t] = lds_read_tr16(kbl + (16 * cc + 8 * t) * DQ_KBP + 64 * dt);
+                const u32x2 k0 = __builtin_bit_cast(u32x2, kp[0]), k1 = __builtin_bit_cast(u32x2, kp[1]);
+                const bf16x8 ka = __builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]});
                 acc[dt] = mfma_bf16_32x32x16(ka, dsb[cc], acc[dt]);
             }
-        __syncthreads();  // the next issue refills this stage
         j0 = j1;
         j1 = j2;
+        j2 = j3;
         sk0 = sk1;
     }
     // accumulating: every value the row already holds is loaded before the
@@ -394,8 +365,6 @@ __global__ __launch_bounds__(256) void dstat_kernel(const uint16_t* __restrict__
 // (the row reads) and 4 consecutive rows at 4 chunks (the transposing reads)
 // both cover all banks. 72.5 KB of LDS, so that two workgroups share a CU
 // and each runs while the other waits at a barrier.
-__device__ __forceinline__ int qswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
 constexpr int DK_THREADS = 256;
 constexpr int DK_Q = 64;                       // queries per step
 constexpr int KV_F = 4 * 2 * 64 * 16;          // one fragment set: [4 query steps][2 key tiles][64 lanes] x 16 B
@@ -947,11 +916,6 @@ __global__ __launch_bounds__(256, 1) void lin_bwd_k_kernel(const uint16_t* __res
 
 // ---------------------------------------------------------------------------
 
-hipError_t launch_bwd_prep(const BwdArgs& a, uint16_t* kt16, hipStream_t st) {
-    hipLaunchKernelGGL((transpose_tiles_kernel<int8_t, KBLK>), dim3(a.nkb, a.BH), dim3(256), 0, st,
-                       a.k_i8, a.N, a.nkb, kt16);
-    return hipGetLastError();
-}
 
 size_t keep_bits_bytes(int64_t BH, int64_t nqb, int64_t nkb) {
     return (size_t)BH * nkb * ((nqb + 31) / 32) * 4;

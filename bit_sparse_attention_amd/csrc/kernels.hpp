@@ -79,7 +79,6 @@ struct BwdArgs {
     const float* k_scale;
     const uint16_t* v;       // raw bf16 V [BH][N][128]
     const uint16_t* dout;    // bf16 dL/dO [BH][N][128]
-    const uint16_t* kt16;    // bf16 k_i8, channel-first per key block [BH][nkb][128][64]
     const int32_t* kidx;     // [BH][nqb][keep] or null (dense)
     int keep;
     const uint16_t* lists;   // [BH][nkb][nqb]: query blocks that kept each key block
@@ -93,7 +92,6 @@ struct BwdArgs {
     const float* dstat;      // [BH][N] dO . o_s
     float *dq, *dk, *dv;     // fp32 [BH][N][128]
 };
-hipError_t launch_bwd_prep(const BwdArgs& a, uint16_t* kt16, hipStream_t st);
 // bytes of the bit matrix launch_inv_lists builds the lists from
 size_t keep_bits_bytes(int64_t BH, int64_t nqb, int64_t nkb);
 hipError_t launch_inv_lists(const int32_t* kidx, int keep, int64_t BH, int nqb, int nkb,
