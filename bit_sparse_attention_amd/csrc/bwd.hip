@@ -49,22 +49,29 @@ __device__ __forceinline__ int ld_uniform_u16(const uint16_t* base, int64_t e) {
 
 // ---- the query blocks that kept each key block ----------------------------
 // lists[bh][j][0..counts[bh][j]) = the query blocks i (ascending) whose kept
-// list kidx[bh][i] holds j. Two passes over a bit matrix bits[bh][j][i / 32]
-// (cleared beforehand): one thread per kept entry sets bit i of its block's
-// row, then one thread per key block emits the set bits of its row in
-// ascending i. Entries outside [0, nkb) are ignored.
+// list kidx[bh][i] holds j. Two passes over a bit matrix bits[bh][j][i / 32]:
+// one workgroup per (head, 32 query blocks) sets the bits of its query blocks
+// for every key block in LDS and writes its word of each key block's row
+// (every word once, so nothing is cleared beforehand), then one thread per
+// key block emits the set bits of its row in ascending i. Entries outside
+// [0, nkb) are ignored.
 __global__ __launch_bounds__(256) void keep_bits_kernel(const int32_t* __restrict__ kidx, int keep,
-                                                        int nqb, int nkb, int64_t entries,
+                                                        int nqb, int nkb,
                                                         uint32_t* __restrict__ bits) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= entries) return;
-    const int64_t row = e / keep;  // bh * nqb + i
-    const int i = (int)(row % nqb);
-    const int64_t bh = row / nqb;
-    const int j = kidx[e];
-    if (j < 0 || j >= nkb) return;
+    extern __shared__ uint32_t wbits[];  // [nkb]: bit i - 32w of query block i
+    const int w = blockIdx.x;
+    const int64_t bh = blockIdx.y;
     const int words = (nqb + 31) >> 5;
-    atomicOr(bits + (bh * nkb + j) * words + (i >> 5), 1u << (i & 31));
+    for (int j = threadIdx.x; j < nkb; j += 256) wbits[j] = 0;
+    __syncthreads();
+    const int i0 = 32 * w, ni = min(32, nqb - i0);
+    const int32_t* src = kidx + (bh * nqb + i0) * (int64_t)keep;
+    for (int e = threadIdx.x; e < ni * keep; e += 256) {
+        const int j = src[e];
+        if (j >= 0 && j < nkb) atomicOr(&wbits[j], 1u << (e / keep));
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < nkb; j += 256) bits[(bh * nkb + j) * words + w] = wbits[j];
 }
 
 __global__ __launch_bounds__(256) void inv_lists_kernel(const uint32_t* __restrict__ bits,
@@ -923,12 +930,8 @@ size_t keep_bits_bytes(int64_t BH, int64_t nqb, int64_t nkb) {
 
 hipError_t launch_inv_lists(const int32_t* kidx, int keep, int64_t BH, int nqb, int nkb,
                             uint32_t* bits, uint16_t* lists, int32_t* counts, hipStream_t st) {
-    const int64_t nwords = (int64_t)BH * nkb * ((nqb + 31) / 32);
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<int64_t>((nwords + 255) / 256, 65536)),
-                       dim3(256), 0, st, (float*)bits, nwords);
-    const int64_t entries = (int64_t)BH * nqb * keep;
-    hipLaunchKernelGGL(keep_bits_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, st,
-                       kidx, keep, nqb, nkb, entries, bits);
+    hipLaunchKernelGGL(keep_bits_kernel, dim3((nqb + 31) / 32, BH), dim3(256), (size_t)nkb * 4, st,
+                       kidx, keep, nqb, nkb, bits);
     hipLaunchKernelGGL(inv_lists_kernel, dim3((nkb + 255) / 256, BH), dim3(256), 0, st, bits, nqb,
                        nkb, lists, counts);
     return hipGetLastError();
