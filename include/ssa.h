@@ -226,8 +226,9 @@ ssa_status sage_sla_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * gradient of phi(q)^T H_i / phi(q)^T z_i over the non-kept blocks (phi =
  * elu + 1 on raw Q, K). Arithmetic: int8 scores exact; P and dS rounded to
  * bf16 for the bf16 matrix-core products (fp32 accumulation); the linear
- * branch in fp32 (its states summed as the forward's, bf16 stack with an fp32
- * total). Relative L2 error against the exact gradient ~1e-3.
+ * branch in fp32 (its states summed as the forward's, from a bf16 stack and a
+ * stack of each entry's bf16 rest, with an fp32 total). Relative L2 error
+ * against the exact gradient ~1e-3.
  *   q, k, v, q_i8..k_scale, kidx, keep, branches, sm_scale: as for
  *                     sage_sla_attn_fwd (the same values the forward used)
  *   dout         in : bf16 [B,H,N,D], dL/d(out)
