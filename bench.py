@@ -509,7 +509,8 @@ def main():
     args = ap.parse_args()
     if args.pmc_summary or args.trace_summary or args.pmc_table:
         from bit_sparse_attention_amd.workloads import BENCH_WORKLOAD, LINEAR_BENCH_WORKLOAD
-        kernel = W8_KERNEL if args.w8a8 else ATTN_KERNEL
+        # --bwd: every kernel the counter files hold (the runs select them)
+        kernel = W8_KERNEL if args.w8a8 else ("" if args.bwd else ATTN_KERNEL)
         wl = args.workload or (LINEAR_BENCH_WORKLOAD if args.w8a8 else BENCH_WORKLOAD)
         if args.pmc_summary:
             print(pmc_summary(*args.pmc_summary, args.copy_calibration or 1024, wl,
