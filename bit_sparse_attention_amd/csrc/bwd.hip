@@ -225,19 +225,21 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
         const float c = (sq * sk) * a.K32;
         const uint8_t* kt = smem + st * DQ_STAGE;
         const uint8_t* vt = kt + DQ_KT;
-        // widen this step's K tile: thread t converts 16 channels of two rows
+        // widen this step's K tile: 16 threads per row, each 8 channels (an
+        // 8-byte read, a 16-byte store), so a 16-lane group reads and writes
+        // one whole row without bank conflicts
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int x = tid + 256 * it, row = x >> 3, ch = x & 7;
-            const i32x4 kv = *(const i32x4*)(kt + row * 128 + 16 * (ch ^ swz8(row)));
-            bf16x8 w[2];
+        for (int it = 0; it < 4; ++it) {
+            const int x = tid + 256 * it, row = x >> 4, c8 = x & 15;
+            const u32x2 kv =
+                *(const u32x2*)(kt + row * 128 + 16 * ((c8 >> 1) ^ swz8(row)) + 8 * (c8 & 1));
+            bf16x8 w;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
+            for (int e = 0; e < 8; ++e) {
                 const int b = (int)((uint32_t)kv[e >> 2] << (24 - 8 * (e & 3))) >> 24;  // signed byte e
-                w[e >> 3][e & 7] = (__bf16)(float)b;
+                w[e] = (__bf16)(float)b;
             }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) *(bf16x8*)(smem + DQ_KB + row * DQ_KBP + 16 * (2 * ch + h)) = w[h];
+            *(bf16x8*)(smem + DQ_KB + row * DQ_KBP + 16 * c8) = w;
         }
         i32x16 s[2];
         f32x16 dp[2];
